@@ -1,0 +1,276 @@
+/*
+ * tsg.h -- tile-signaled GEMM paths for one MI355X (gfx950).
+ *
+ * A GEMM whose tiles are linked to a concurrent producer or consumer through
+ * per-chunk or per-tile signals in device memory, run at one rank's share of
+ * a tensor-parallel or expert-parallel layer.  Peers are stood in for by
+ * buffers already resident in HBM.
+ *
+ * Pages cited:
+ *   [TL] "TileLink: Generating Efficient Compute-Communication Overlapping
+ *        Kernels using Tile-Centric Primitives" (arXiv 2503.20313).
+ *   [TD] "Triton-distributed: Programming Overlapping Kernels on Distributed
+ *        AI Systems with the Triton Compiler" (arXiv 2504.19442).
+ *   [DG] Digest page "Resource-aware Computation-Communication Overlap for
+ *        multi-GPU ML Workloads" (CTA-pipelining abstract; MoE tile-level
+ *        signaling abstract).
+ *
+ * Conventions shared by every entry point
+ *   - Matrices are dense and row-major.  "bf16" arguments hold bfloat16 bit
+ *     patterns (uint16 per element); "f32" arguments hold IEEE binary32.
+ *   - Every device pointer is caller-owned device memory of the current
+ *     device of `ctx`, 16-byte aligned, and must stay valid until the work
+ *     enqueued by the call has completed on `stream`.  Nothing is retained
+ *     after that.  Output buffers must not alias inputs.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls are asynchronous and stream-ordered: work forks from `stream` to
+ *     the context's side streams and joins back before the call returns, so
+ *     later work on `stream` sees every output.
+ *   - Return value: TSG_OK or a negative tsg_status.  Argument errors are
+ *     detected before anything is enqueued; the message is available from
+ *     tsg_last_error().  Device-side errors (a signal wait that exceeded its
+ *     bounded spin) are latched in the context and reported by tsg_check().
+ *     No C++ exception or abort crosses this interface.
+ *   - Calls that share one context must not overlap in time on different
+ *     host threads; distinct contexts are independent.
+ */
+#ifndef TSG_H_
+#define TSG_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct tsg_ctx tsg_ctx;
+
+typedef enum tsg_status {
+  TSG_OK = 0,
+  TSG_E_INVALID = -1,     /* null pointer, bad enum, bad option value        */
+  TSG_E_SHAPE = -2,       /* dimensions violate the documented constraints   */
+  TSG_E_ALIGN = -3,       /* pointer not 16-byte aligned                     */
+  TSG_E_HIP = -4,         /* a HIP runtime call failed                       */
+  TSG_E_TIMEOUT = -5,     /* a device-side signal wait exceeded its bound    */
+  TSG_E_UNSUPPORTED = -6, /* valid request this build does not implement     */
+  TSG_E_WORKSPACE = -7    /* workspace missing or smaller than required      */
+} tsg_status;
+
+/* Execution modes; all four run the same kernels.  The overlap ratio of
+ * [TL] section 7.2 is (t_compute_only + t_comm_only - t_overlap) / t_comm_only. */
+typedef enum tsg_mode {
+  TSG_MODE_OVERLAP = 0,      /* producer and consumer run concurrently, linked
+                                by tile/chunk signals                           */
+  TSG_MODE_SERIAL = 1,       /* same kernels back to back on `stream`, each
+                                with the whole GPU: communication first, then
+                                compute (AG) or compute, then reduce/combine   */
+  TSG_MODE_COMPUTE_ONLY = 2, /* the GEMM kernel(s) alone, whole GPU, every
+                                wait pre-satisfied; outputs hold valid values
+                                only if the data they read is already present  */
+  TSG_MODE_COMM_ONLY = 3     /* the copy / reduce / combine kernel alone, with
+                                the same launch shape as in overlap mode      */
+} tsg_mode;
+
+typedef enum tsg_dtype { TSG_F32 = 0, TSG_BF16 = 1 } tsg_dtype;
+
+/* Options; a zeroed struct (or NULL) selects the defaults. */
+typedef struct tsg_opts {
+  /* CU partition ([TL] section 3.1, resource binding; [TD] section 3.8,
+   * resource partition).  aux_cus = CUs reserved for the auxiliary kernel:
+   * the copy kernel of AG+GEMM, the reduce kernel of GEMM+RS, GEMM2 of the
+   * MLP, the combine kernel of MoE.  0 = the op's default; -1 = no split:
+   * both kernels may use every CU and co-reside.  main_cus = CUs for the main
+   * GEMM kernel (AG GEMM, RS producer GEMM, MLP GEMM1, MoE expert producer);
+   * 0 = every CU not given to the auxiliary kernel.  Both sides of a split
+   * must be multiples of 8 CUs (one CU per XCD per group of 8), at least 8
+   * each. */
+  int aux_cus;
+  int main_cus;
+  /* GEMM tile configuration id, 0 = the op's default (see tsg_tile_info). */
+  int tile;
+  /* Tile order knob.  AG+GEMM: 0 = start at the local chunk and follow the
+   * arrival order; 1 = plain row-major order.  GEMM+RS: 0 = local chunk
+   * first, 1 = local chunk last ([TD] section 3.7). */
+  int order;
+  /* Bound of every device-side signal wait, in milliseconds (0 = 2000). */
+  uint32_t timeout_ms;
+  /* Test hook: bit c set = the signal of chunk / row-block / tile group c
+   * is never published in this call, so its consumers time out (the call
+   * then reports TSG_E_TIMEOUT from tsg_check).  0 in normal use. */
+  uint32_t debug_skip_mask;
+  /* Nonzero: record per-tile device timestamps into the context's timeline
+   * buffer (tsg_timeline). */
+  int timeline;
+} tsg_opts;
+
+/* ------------------------------------------------------------------ ctx */
+
+/* Create a context on HIP device `device`: it owns the signal words (epoch
+ * tagged, so no reset pass is needed between calls), the error word, the
+ * side streams (CU-masked on request), events and the timeline buffer.
+ * Returns TSG_E_HIP if the device cannot be used, TSG_E_UNSUPPORTED if it is
+ * not a gfx950 device. */
+tsg_status tsg_ctx_create(int device, tsg_ctx** out);
+
+/* Destroy a context.  Waits for the context's side streams to drain. */
+void tsg_ctx_destroy(tsg_ctx* ctx);
+
+/* Message of the last error raised through `ctx` ("" if none).  The string
+ * is owned by the context and valid until the next call on it. */
+const char* tsg_last_error(const tsg_ctx* ctx);
+
+/* Synchronise `stream`, then return TSG_E_TIMEOUT if any device-side wait
+ * enqueued through `ctx` since the previous tsg_check timed out (and clear
+ * that state), TSG_E_HIP on a runtime error, else TSG_OK. */
+tsg_status tsg_check(tsg_ctx* ctx, void* stream);
+
+/* Number of CUs and of XCDs (accelerator complex dies, each with its own L2)
+ * of the context's device.  Either pointer may be NULL.  The XCD count is
+ * read from the hardware on first use (one short kernel, synchronising). */
+tsg_status tsg_device_info(tsg_ctx* ctx, int* n_cus, int* n_xcds);
+
+/* Per-kernel timing.  When enabled, every launch is bracketed by HIP events
+ * on the stream it runs on; tsg_kernel_ms returns the elapsed milliseconds of
+ * the most recent call's main GEMM kernel (which = 0) and auxiliary kernel
+ * (which = 1: copy, reduce, GEMM2 or combine), after the call has completed.  Returns TSG_E_INVALID if the last
+ * call did not run that kernel. */
+tsg_status tsg_enable_kernel_timing(tsg_ctx* ctx, int enable);
+tsg_status tsg_kernel_ms(tsg_ctx* ctx, int which, float* ms);
+
+/* Timeline of the most recent call made with opts.timeline != 0: up to
+ * `cap` records of 4 uint64 each {kind<<56 | tile, t_start, t_ready, t_end}
+ * in device wall-clock ticks (100 MHz), copied to host memory `out`;
+ * *n receives the record count.  Synchronises the device. */
+tsg_status tsg_timeline(tsg_ctx* ctx, uint64_t* out, size_t cap, size_t* n);
+
+/* ------------------------------------------------------------- AG+GEMM */
+
+/* AllGather + GEMM, one rank's share ([TL] section 2.1 and Figure 1: the
+ * activation is gathered along M, then multiplied by the local weight
+ * shard; [TD] section 3.2, Algorithm 2: pull-mode AllGather with one ready
+ * signal per source rank; [TD] section 3.7: compute tiles start at the local
+ * chunk and follow the arrival order).
+ *
+ * A copy kernel (the stand-in for peer arrival) writes chunk c of a_full
+ * (rows [c*M/R, (c+1)*M/R)) from a_local (c == rank) or from a_peers, and
+ * releases chunk c's signal; the MFMA GEMM consumer computes
+ * c = a_full * b, each tile waiting (acquire) on the signals of the chunks
+ * its rows span.
+ *
+ *   a_local  bf16 [M/R x K]            this rank's shard (input)
+ *   a_peers  bf16 [(R-1) x M/R x K]    the other ranks' shards in ascending
+ *                                      rank order, skipping `rank` (input)
+ *   a_full   bf16 [M x K]              gathered operand (output)
+ *   b        bf16 [K x N]              local weight shard (input)
+ *   c        [M x N], c_dtype          TSG_F32 or TSG_BF16 (round to nearest
+ *                                      even of the fp32 accumulator) (output)
+ *   arrival_order  host int[R-1] or NULL: order in which peer chunks arrive
+ *                  (a permutation of the ranks != rank); NULL = ring order
+ *                  rank+1, rank+2, ... (mod R)
+ * Constraints: 1 <= R <= 32, 0 <= rank < R, M % R == 0, M >= R,
+ * N % 8 == 0, K % 8 == 0, N, K >= 8 (else TSG_E_SHAPE).
+ * COMPUTE_ONLY expects a_full to hold the gathered operand already. */
+tsg_status gemm_ag_overlap(tsg_ctx* ctx, const void* a_local, const void* a_peers,
+                           void* a_full, const void* b, void* c, int c_dtype,
+                           int M, int N, int K, int R, int rank,
+                           const int* arrival_order, const tsg_opts* opts,
+                           int mode, void* stream);
+
+/* ------------------------------------------------------------- GEMM+RS */
+
+/* GEMM + ReduceScatter, one rank's share ([TL] section 2.1; [TL] Table 3
+ * producer_tile_notify / consumer_tile_wait; [TD] section 3.3, Algorithm 3:
+ * the reduction stream sums every rank's contribution to the local chunk as
+ * its signal arrives; [TD] section 3.6: the scatter is fused into the
+ * producer GEMM's epilogue).
+ *
+ * The producer GEMM computes partial = x * w (fp32, all M rows; row chunk c
+ * is the contribution destined for rank c) and releases one done signal per
+ * 128x128 tile of `partial` as soon as the tile is stored.  The reduce
+ * consumer computes, for the local chunk,
+ *     out = sum over ranks r of (r == rank ? partial[rank chunk] : peer r),
+ * summing the peers while the GEMM runs and adding each local tile once its
+ * signal is acquired.
+ *
+ *   x              bf16 [M x K]                 (input)
+ *   w              bf16 [K x N]                 (input)
+ *   partial        f32  [M x N]                 (output)
+ *   peer_partials  f32  [(R-1) x M/R x N]       other ranks' partial sums for
+ *                                               this rank's chunk, ascending
+ *                                               rank order skipping `rank`
+ *   out            f32  [M/R x N]               (output)
+ * Constraints: 1 <= R <= 32, 0 <= rank < R, M % R == 0, N % 8 == 0,
+ * K % 8 == 0, N, K >= 8.  COMM_ONLY expects `partial` to be computed already. */
+tsg_status gemm_rs_overlap(tsg_ctx* ctx, const void* x, const void* w, float* partial,
+                           const float* peer_partials, float* out,
+                           int M, int N, int K, int R, int rank,
+                           const tsg_opts* opts, int mode, void* stream);
+
+/* ---------------------------------------------------------------- MLP2 */
+
+/* CTA-pipelined two-GEMM MLP ([DG] CTA-pipelining abstract: dependent
+ * kernels run concurrently on CTA-level dependencies, shown on a 2-layer
+ * GEMM; [TL] Table 3: a consumer tile is ready when all the producer tiles
+ * it depends on are done).
+ *
+ * GEMM1 (producer, its own CU partition) computes h = bf16(GELU(x * w1))
+ * (exact erf GELU on the fp32 accumulator, rounded to nearest even) and,
+ * after each tile, releases a count on the signal of its 128-row block.
+ * GEMM2 (consumer, the other partition) computes y = h * w2 (fp32), each
+ * tile starting as soon as every GEMM1 tile of its row block is done.
+ *
+ *   x   bf16 [M x K1], w1 bf16 [K1 x N1], h bf16 [M x N1] (output),
+ *   w2  bf16 [N1 x N2], y f32 [M x N2] (output)
+ * Constraints: N1 % 8 == 0, N2 % 8 == 0, K1 % 8 == 0, all >= 8, M >= 1.
+ * Default split: 64 CUs for GEMM2, 192 for GEMM1 (opts.aux_cus / main_cus).  COMPUTE_ONLY runs GEMM1 then GEMM2 on the whole GPU
+ * without waits (identical to SERIAL for this op); COMM_ONLY is
+ * unsupported (TSG_E_UNSUPPORTED): both halves are compute. */
+tsg_status mlp2_pipelined(tsg_ctx* ctx, const void* x, const void* w1, void* h,
+                          const void* w2, float* y, int M, int K1, int N1, int N2,
+                          const tsg_opts* opts, int mode, void* stream);
+
+/* ----------------------------------------------------------------- MoE */
+
+/* MoE expert compute with overlapped gate-weighted combine ([DG] MoE
+ * tile-level signaling abstract: a persistent producer covering all local
+ * experts emits output tiles with ready signals, and a persistent consumer
+ * on a small CU partition returns them to token order as they become ready;
+ * [TL] section 4.1: dynamic mapping through lookup tables filled at run
+ * time; [TL] section 7.2: GroupGEMM + Scatter + Topk-Reduce).
+ *
+ * For every pair p = t*k + s (token t, slot s, expert e = topk_ids[t][s]):
+ *     u = x[t] * w_up[e];  hh = bf16(SiLU(u));  y_p = hh * w_down[e]  (fp32)
+ * and out[t] = fl(fl(topk_w[t][0] * y_(t,0)) + fl(topk_w[t][1] * y_(t,1)))
+ * (k == 2; the two products are rounded to fp32 and added in slot order).
+ * expert_counts[e] = number of pairs routed to e; sorted_ids = pair ids in
+ * (expert, token, slot) order.
+ *
+ *   x         bf16 [T x H]        topk_ids  int32 [T x k]   topk_w f32 [T x k]
+ *   w_up      bf16 [E x H x I]    w_down    bf16 [E x I x H]
+ *   out       f32 [T x H] (output)
+ *   expert_counts int32 [E] (output), sorted_ids int32 [T*k] (output)
+ *   workspace device memory of at least tsg_workspace_bytes(TSG_OP_MOE, dims)
+ *             bytes with dims = {T, H, I, E, k}; caller-owned, contents
+ *             undefined on entry and exit.
+ * Constraints: k == 2 (TSG_E_UNSUPPORTED otherwise), 1 <= E <= 256,
+ * T >= 1, H % 8 == 0, I % 8 == 0, H, I >= 8.  Expert ids outside [0, E) are
+ * detected on the device: the affected pairs are dropped and the call's
+ * tsg_check returns TSG_E_INVALID.  Default combine partition (aux_cus): 16 CUs. */
+tsg_status moe_expert_combine(tsg_ctx* ctx, const void* x, const int32_t* topk_ids,
+                              const float* topk_w, const void* w_up, const void* w_down,
+                              float* out, int32_t* expert_counts, int32_t* sorted_ids,
+                              void* workspace, size_t workspace_bytes,
+                              int T, int H, int I, int E, int k,
+                              const tsg_opts* opts, int mode, void* stream);
+
+enum { TSG_OP_AG = 0, TSG_OP_RS = 1, TSG_OP_MLP2 = 2, TSG_OP_MOE = 3 };
+
+/* Workspace bytes an op needs for `dims` (TSG_OP_MOE: {T, H, I, E, k});
+ * 0 for ops that need none or for invalid dims. */
+size_t tsg_workspace_bytes(int op, const int64_t* dims);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TSG_H_ */

@@ -1,0 +1,176 @@
+"""AllGather + GEMM on the GPU against the oracle.
+
+Every call runs with the gathered buffer and the output pre-filled with NaN
+patterns, so a tile that read its rows before acquiring their chunk signal, or
+a tile that was never written, shows up as a non-finite element."""
+import numpy as np
+import pytest
+
+import oracle
+from _helpers import bf16_from_dev, err_ratio, to_dev
+from synth import CONFIGS, ag_inputs
+from synth.gen import split_chunks
+
+pytestmark = pytest.mark.gpu
+
+NAN_BF16 = 0x7FC0
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    import tile_level_communication_signaled_amd as tsg
+    ctx = tsg.Context(0)
+    yield torch, tsg, ctx
+    torch.cuda.synchronize()
+    ctx.close()
+
+
+class AgCase:
+    def __init__(self, env, inp, M, N, K, R, rank, out_bf16):
+        torch, tsg, ctx = env
+        self.env, self.M, self.N, self.K, self.R, self.rank, self.out_bf16 = env, M, N, K, R, rank, out_bf16
+        loc, peers = split_chunks(inp["a"], R, rank)
+        self.loc = to_dev(loc, torch)
+        self.peers = to_dev(peers if R > 1 else np.zeros((1, 8), np.uint16), torch)
+        self.b = to_dev(inp["b"], torch)
+        self.full = torch.empty((M, K), dtype=torch.int16, device="cuda")
+        self.c = torch.empty((M, N), dtype=torch.int16 if out_bf16 else torch.float32, device="cuda")
+
+    def run(self, mode=None, order=None, opts=None, poison=True, expect=0):
+        torch, tsg, ctx = self.env
+        mode = tsg.OVERLAP if mode is None else mode
+        if poison:
+            self.full.fill_(NAN_BF16)
+            self.c.fill_(NAN_BF16 if self.out_bf16 else float("nan"))
+        tsg.gemm_ag_overlap(ctx, self.loc, self.peers, self.full, self.b, self.c,
+                            tsg.BF16 if self.out_bf16 else tsg.F32, self.M, self.N, self.K, self.R,
+                            self.rank, arrival_order=order, opts=opts, mode=mode)
+        st = ctx.check()
+        assert st == expect, (st, ctx.last_error())
+        full = bf16_from_dev(self.full)
+        if self.out_bf16:
+            c = oracle.bf16_to_f64(bf16_from_dev(self.c))
+        else:
+            c = self.c.cpu().numpy().astype(np.float64)
+        return full, c
+
+
+def _ref(inp):
+    return oracle.gemm(inp["a"], inp["b"]), oracle.gemm_abs(inp["a"], inp["b"])
+
+
+def test_tiny_ag_all_ranks_tiles_orders(env):
+    cfg = CONFIGS["tiny_ag"]
+    M, N, K, R = cfg["M"], cfg["N"], cfg["K"], cfg["R"]
+    inp = ag_inputs(M, K, N, R, seed=cfg["seed"], dist="uniform")
+    ref, scale = _ref(inp)
+    first = None
+    for rank in range(R):
+        case = AgCase(env, inp, M, N, K, R, rank, out_bf16=False)
+        peers = [r for r in range(R) if r != rank]
+        for tile in (6, 7, 3, 1):              # 64x64, 128x64 (spans two chunks), 128x128, 256x256
+            for order in (None, peers[::-1]):
+                full, c = case.run(order=order, opts={"tile": tile, "aux_cus": 8})
+                assert np.array_equal(full, inp["a"])
+                assert err_ratio(c, ref, scale) <= 1.0
+                if first is None:
+                    first = c
+                assert np.array_equal(c, first), (rank, tile, order)
+
+
+def test_tiny_ag_integer_inputs_exact(env):
+    M, N, K, R = 256, 128, 256, 4
+    rng = np.random.default_rng(5)
+    from synth import f32_to_bf16_bits
+    inp = {"a": f32_to_bf16_bits(rng.integers(-2, 3, (M, K)).astype(np.float32)),
+           "b": f32_to_bf16_bits(rng.integers(-2, 3, (K, N)).astype(np.float32))}
+    case = AgCase(env, inp, M, N, K, R, 1, out_bf16=False)
+    _, c = case.run(opts={"aux_cus": 8})
+    assert np.array_equal(c, oracle.gemm(inp["a"], inp["b"]))
+
+
+@pytest.mark.parametrize("tile", [6, 3, 1, 2])
+def test_ag_ragged_shapes(env, tile):
+    # 3 ranks of 200 rows: tiles straddle chunks; N and K are not multiples of
+    # the tile; K is not a multiple of 64
+    M, N, K, R = 600, 200, 136, 3
+    inp = ag_inputs(M, K, N, R, seed=7)
+    ref, scale = _ref(inp)
+    for rank in range(R):
+        for out_bf16 in (False, True):
+            case = AgCase(env, inp, M, N, K, R, rank, out_bf16)
+            full, c = case.run(opts={"tile": tile, "aux_cus": 16})
+            assert np.array_equal(full, inp["a"])
+            assert err_ratio(c, ref, scale, bf16_out=out_bf16) <= 1.0
+
+
+def test_ag_degenerate_single_rank_and_small(env):
+    torch, tsg, ctx = env
+    M, N, K, R = 8, 8, 8, 1
+    inp = ag_inputs(M, K, N, R, seed=8)
+    ref, scale = _ref(inp)
+    case = AgCase(env, inp, M, N, K, R, 0, out_bf16=False)
+    for mode in (tsg.OVERLAP, tsg.SERIAL):
+        full, c = case.run(mode=mode, opts={"aux_cus": 8})
+        assert np.array_equal(full, inp["a"]) and err_ratio(c, ref, scale) <= 1.0
+
+
+def test_ag_rejects_bad_arguments(env):
+    torch, tsg, ctx = env
+    inp = ag_inputs(64, 64, 64, 4, seed=9)
+    case = AgCase(env, inp, 64, 64, 64, 4, 0, out_bf16=False)
+    args = (ctx, case.loc, case.peers, case.full, case.b, case.c, tsg.F32)
+    assert tsg.gemm_ag_overlap(*args, 64, 64, 60, 4, 0, raise_on_error=False) == tsg.E_SHAPE
+    assert tsg.gemm_ag_overlap(*args, 66, 64, 64, 4, 0, raise_on_error=False) == tsg.E_SHAPE
+    assert tsg.gemm_ag_overlap(*args, 64, 64, 64, 4, 4, raise_on_error=False) == tsg.E_SHAPE
+    assert tsg.gemm_ag_overlap(*args, 64, 64, 64, 4, 0, arrival_order=[1, 1, 2],
+                               raise_on_error=False) == tsg.E_INVALID
+    assert tsg.gemm_ag_overlap(ctx, case.loc.data_ptr() + 2, case.peers, case.full, case.b, case.c, tsg.F32,
+                               64, 64, 64, 4, 0, raise_on_error=False) == tsg.E_ALIGN
+
+
+def test_ag_missing_chunk_times_out_then_recovers(env):
+    torch, tsg, ctx = env
+    M, N, K, R = 512, 256, 128, 4
+    inp = ag_inputs(M, K, N, R, seed=10)
+    ref, scale = _ref(inp)
+    case = AgCase(env, inp, M, N, K, R, 0, out_bf16=False)
+    case.run(opts={"aux_cus": 8, "debug_skip_mask": 1 << 2, "timeout_ms": 20}, expect=tsg.E_TIMEOUT)
+    full, c = case.run(opts={"aux_cus": 8})
+    assert np.array_equal(full, inp["a"]) and err_ratio(c, ref, scale) <= 1.0
+
+
+def test_ag_llama_shape_full_parity(env):
+    torch, tsg, ctx = env
+    cfg = CONFIGS["llama_ag"]
+    M, N, K, R = cfg["M"], cfg["N"], cfg["K"], cfg["R"]
+    inp = ag_inputs(M, K, N, R, seed=cfg["seed"])
+    ref, scale = _ref(inp)
+    case = AgCase(env, inp, M, N, K, R, 0, out_bf16=True)
+    full, c = case.run()
+    assert np.array_equal(full, inp["a"])
+    r = err_ratio(c, ref, scale, bf16_out=True)
+    print(f"llama_ag max err/tol = {r:.3f}")
+    assert r <= 1.0
+    _, c_serial = case.run(mode=tsg.SERIAL)
+    assert np.array_equal(c_serial, c)
+    _, c_comp = case.run(mode=tsg.COMPUTE_ONLY, poison=False)
+    assert np.array_equal(c_comp, c)
+    # another rank, another arrival order: same product, bit for bit
+    inp5 = dict(inp)
+    case5 = AgCase(env, inp5, M, N, K, R, 5, out_bf16=True)
+    full5, c5 = case5.run(order=[2, 7, 0, 4, 1, 6, 3])
+    assert np.array_equal(full5, inp["a"]) and np.array_equal(c5, c)
+
+
+@pytest.mark.parametrize("aux", [16, 32, 64, -1])
+def test_ag_llama_shape_cu_splits(env, aux):
+    torch, tsg, ctx = env
+    cfg = CONFIGS["llama_ag"]
+    M, N, K, R = cfg["M"], cfg["N"], cfg["K"], cfg["R"]
+    inp = ag_inputs(M, K, N, R, seed=cfg["seed"])
+    case = AgCase(env, inp, M, N, K, R, 3, out_bf16=True)
+    full, c = case.run(opts={"aux_cus": aux})
+    _, c_serial = case.run(mode=tsg.SERIAL)
+    assert np.array_equal(full, inp["a"]) and np.array_equal(c, c_serial)

@@ -1,0 +1,109 @@
+// Host-side internals shared by the op translation units: the context, error
+// reporting, CU-partitioned side streams and the fork/join launch helpers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
+
+#include <map>
+#include <string>
+#include <vector>
+
+#include "tsg.h"
+#include "tsg_device.hpp"
+
+struct tsg_ctx {
+  int device = 0;
+  int n_cus = 0;
+  int64_t wall_khz = 100000;
+  uint32_t epoch = 0;
+
+  uint64_t* d_sig = nullptr;   // signal words
+  size_t n_sig = 0;
+  uint32_t* d_status = nullptr;  // sticky device error bits
+  uint32_t* d_queue = nullptr;   // work-queue tickets of persistent kernels
+  uint64_t queue_base[4] = {0, 0, 0, 0};
+
+  uint64_t* d_timeline = nullptr;
+  uint32_t* d_timeline_n = nullptr;
+  uint32_t timeline_cap = 0;
+
+  // side streams keyed by CU mask (empty key: unmasked streams 0 / 1)
+  std::map<std::vector<uint32_t>, hipStream_t> masked;
+  hipStream_t side[2] = {nullptr, nullptr};
+  hipEvent_t ev_fork = nullptr;
+  hipEvent_t ev_join[2] = {nullptr, nullptr};
+  hipEvent_t ev_k[2][2] = {{nullptr, nullptr}, {nullptr, nullptr}};
+  bool timing = false;
+  bool ran[2] = {false, false};
+
+  bool probed = false;
+  int n_xcd = 0;
+
+  std::string err;
+};
+
+namespace tsgh {
+
+tsg_status fail(tsg_ctx* ctx, tsg_status st, const char* fmt, ...);
+tsg_status hip_fail(tsg_ctx* ctx, hipError_t e, const char* what);
+
+#define TSG_HIP(ctx, expr)                                   \
+  do {                                                       \
+    hipError_t e_ = (expr);                                  \
+    if (e_ != hipSuccess) return tsgh::hip_fail(ctx, e_, #expr); \
+  } while (0)
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Resolved options with defaults applied.
+struct Opts {
+  int aux_cus;   // -1 = shared (no split)
+  int main_cus;
+  int tile;
+  int order;
+  uint32_t timeout_ms;
+  uint32_t skip_mask;
+  int timeline;
+};
+Opts resolve(const tsg_opts* o, int default_aux_cus);
+
+// Producer / consumer streams for one call.  In split mode they are CU-masked
+// to disjoint CU sets (consumer CUs spread evenly over the XCDs); in shared
+// mode both are unmasked.
+struct Pair {
+  hipStream_t main;
+  hipStream_t aux;
+  int main_cus;
+  int aux_cus;
+};
+tsg_status streams(tsg_ctx* ctx, const Opts& o, Pair* out);
+
+tsg::SyncArgs sync_args(tsg_ctx* ctx, const Opts& o);
+tsg::Timeline timeline(tsg_ctx* ctx, const Opts& o);
+
+// Fork: side streams wait for everything already queued on `caller`.
+tsg_status fork(tsg_ctx* ctx, hipStream_t caller, const Pair& p);
+// Join: `caller` waits for both side streams.
+tsg_status join(tsg_ctx* ctx, hipStream_t caller, const Pair& p);
+// Kernel timing brackets (no-ops unless timing is enabled).
+void time_begin(tsg_ctx* ctx, int which, hipStream_t s);
+void time_end(tsg_ctx* ctx, int which, hipStream_t s);
+void time_reset(tsg_ctx* ctx);
+
+tsg_status check_launch(tsg_ctx* ctx, const char* what);
+
+}  // namespace tsgh
+
+// Op entry points implemented in the op translation units.
+tsg_status tsg_op_ag(tsg_ctx*, const void*, const void*, void*, const void*, void*, int, int, int,
+                     int, int, int, const int*, const tsg_opts*, int, void*);
+tsg_status tsg_op_rs(tsg_ctx*, const void*, const void*, float*, const float*, float*, int, int,
+                     int, int, int, const tsg_opts*, int, void*);
+tsg_status tsg_op_mlp2(tsg_ctx*, const void*, const void*, void*, const void*, float*, int, int,
+                       int, int, const tsg_opts*, int, void*);
+tsg_status tsg_op_moe(tsg_ctx*, const void*, const int32_t*, const float*, const void*,
+                      const void*, float*, int32_t*, int32_t*, void*, size_t, int, int, int, int,
+                      int, const tsg_opts*, int, void*);
+size_t tsg_moe_workspace(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k);
+tsg_status tsg_probe_xcd(tsg_ctx* ctx);
