@@ -35,30 +35,29 @@ __global__ void __launch_bounds__(256) ag_copy_kernel(const uint16_t* __restrict
                                                       const uint16_t* __restrict__ a_peers,
                                                       uint16_t* __restrict__ a_full,
                                                       int64_t chunk_vec, int R, int rank,
-                                                      ChunkOrder ord, uint64_t* sig, SyncArgs sa,
-                                                      uint32_t skip_mask, Timeline tl) {
+                                                      ChunkOrder ord, uint64_t* sig, uint32_t* cnt,
+                                                      SyncArgs sa, uint32_t skip_mask, Timeline tl) {
+  constexpr int U = 8;  // 16-byte vectors in flight per thread
   const int64_t nwg = gridDim.x, w = blockIdx.x;
   const int64_t lo = chunk_vec * w / nwg, hi = chunk_vec * (w + 1) / nwg;
   for (int p = 0; p < R; ++p) {
     const int c = ord.chunk[p];
-    const uint64_t t0 = wall_clock64();
+    const uint64_t t0 = tl.buf ? wall_clock64() : 0;
     const u32x4_t* __restrict__ src =
         (const u32x4_t*)(c == rank ? a_local : a_peers + (int64_t)(c < rank ? c : c - 1) * chunk_vec * 8);
     u32x4_t* __restrict__ dst = (u32x4_t*)a_full + (int64_t)c * chunk_vec;
     int64_t i = lo + threadIdx.x;
-    for (; i + 3 * 256 < hi; i += 4 * 256) {
-      const u32x4_t v0 = src[i], v1 = src[i + 256], v2 = src[i + 512], v3 = src[i + 768];
-      dst[i] = v0;
-      dst[i + 256] = v1;
-      dst[i + 512] = v2;
-      dst[i + 768] = v3;
+    for (; i + (U - 1) * 256 < hi; i += U * 256) {
+      u32x4_t v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(src + i + u * 256);
+#pragma unroll
+      for (int u = 0; u < U; ++u) dst[i + u * 256] = v[u];
     }
-    for (; i < hi; i += 256) dst[i] = src[i];
-    if (!((skip_mask >> c) & 1u)) {
-      block_release_arrive1(sig + c, sa.epoch);
-    } else {
-      __syncthreads();
-    }
+    for (; i < hi; i += 256) dst[i] = __builtin_nontemporal_load(src + i);
+    block_release_fence();
+    if (threadIdx.x == 0 && !((skip_mask >> c) & 1u))
+      sig_arrive_counted_lane(cnt + c, sig + c, (uint32_t)nwg, sa.epoch);
     if (threadIdx.x == 0 && tl.buf) timeline_put(tl, 1, (uint32_t)(c << 16 | w), t0, t0, wall_clock64());
   }
 }
@@ -76,13 +75,14 @@ struct AgGemmArgs {
   int n_tiles_n;
   int wait;               // 0: no waits (compute-only)
   uint32_t arrivals;      // arrivals that complete one chunk signal
+  int per_xcd;            // resident tiles per XCD (0 = no XCD remap)
   uint16_t mt_order[kMaxMTiles];
 };
 
-template <class Cfg, bool OUT_BF16>
+template <class Cfg, bool OUT_BF16, bool DIRECT>
 __global__ void __launch_bounds__(Cfg::NT) ag_gemm_kernel(const AgGemmArgs args) {
-  __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS];
-  const int w = blockIdx.x;
+  __shared__ __attribute__((aligned(16))) char lds[DIRECT ? Cfg::LDS_DIRECT : Cfg::LDS_REGS];
+  const int w = xcd_remap(blockIdx.x, gridDim.x, args.per_xcd);
   const int mt = args.mt_order[w / args.n_tiles_n];
   const int nt = w % args.n_tiles_n;
   const int row0 = mt * Cfg::BM, col0 = nt * Cfg::BN;
@@ -95,8 +95,11 @@ __global__ void __launch_bounds__(Cfg::NT) ag_gemm_kernel(const AgGemmArgs args)
   }
   const uint64_t t1 = args.tl.buf ? wall_clock64() : 0;
   typename GemmTile<Cfg>::Acc acc;
-  GemmTile<Cfg>::run(ARowsLinear{args.a_full, args.K, row0, args.M}, args.b, args.N, col0, args.N,
-                     args.K, lds, acc);
+  const ARowsLinear ar{args.a_full, args.K, row0, args.M};
+  if (DIRECT)
+    GemmTile<Cfg>::run_direct(ar, args.b, args.N, col0, args.N, args.K, lds, acc);
+  else
+    GemmTile<Cfg>::run_regs(ar, args.b, args.N, col0, args.N, args.K, lds, acc);
   const int M = args.M, N = args.N;
   if (OUT_BF16) {
     uint16_t* C = (uint16_t*)args.c;
@@ -143,10 +146,15 @@ TileShape shape_of(int id) {
 
 template <class Cfg>
 hipError_t launch_gemm_cfg(const AgGemmArgs& a, bool bf16, int grid, hipStream_t s) {
-  if (bf16)
-    hipLaunchKernelGGL((ag_gemm_kernel<Cfg, true>), dim3(grid), dim3(Cfg::NT), 0, s, a);
+  const bool direct = a.K % (2 * Cfg::BK) == 0;
+  if (bf16 && direct)
+    hipLaunchKernelGGL((ag_gemm_kernel<Cfg, true, true>), dim3(grid), dim3(Cfg::NT), 0, s, a);
+  else if (bf16)
+    hipLaunchKernelGGL((ag_gemm_kernel<Cfg, true, false>), dim3(grid), dim3(Cfg::NT), 0, s, a);
+  else if (direct)
+    hipLaunchKernelGGL((ag_gemm_kernel<Cfg, false, true>), dim3(grid), dim3(Cfg::NT), 0, s, a);
   else
-    hipLaunchKernelGGL((ag_gemm_kernel<Cfg, false>), dim3(grid), dim3(Cfg::NT), 0, s, a);
+    hipLaunchKernelGGL((ag_gemm_kernel<Cfg, false, false>), dim3(grid), dim3(Cfg::NT), 0, s, a);
   return hipGetLastError();
 }
 
@@ -204,7 +212,7 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
   }
   for (int p = R; p < kMaxRanks; ++p) ord.chunk[p] = 0;
 
-  const Opts o = resolve(opts, 32);
+  const Opts o = resolve(opts, -1);
   const int tile = o.tile ? o.tile : default_tile(M, N);
   const TileShape ts = shape_of(tile);
   if (!ts.bm) return fail(ctx, TSG_E_INVALID, "unknown tile id %d", tile);
@@ -251,13 +259,14 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
     time_begin(ctx, 1, s);
     hipLaunchKernelGGL(ag_copy_kernel, dim3(nwg), dim3(256), 0, s, (const uint16_t*)a_local,
                        (const uint16_t*)a_peers, (uint16_t*)a_full, chunk_vec, R, rank, ord,
-                       ctx->d_sig, ga.sa, o.skip_mask, tl);
+                       ctx->d_sig, ctx->d_cnt, ga.sa, o.skip_mask, tl);
     time_end(ctx, 1, s);
     return check_launch(ctx, "ag_copy_kernel");
   };
-  auto gemm = [&](hipStream_t s, int wait, uint32_t arrivals) -> tsg_status {
+  auto gemm = [&](hipStream_t s, int wait, uint32_t arrivals, int cus) -> tsg_status {
     ga.wait = wait;
     ga.arrivals = arrivals;
+    ga.per_xcd = cus / 8;
     time_begin(ctx, 0, s);
     hipError_t e = launch_gemm(tile, ga, c_dtype == TSG_BF16, grid_gemm, s);
     time_end(ctx, 0, s);
@@ -267,24 +276,26 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
 
   tsg_status st = TSG_OK;
   if (mode == TSG_MODE_SERIAL) {
-    const int nwg = ctx->n_cus * 4;
+    const int nwg = ctx->n_cus * 2;
     st = copy(caller, nwg);
-    if (st == TSG_OK) st = gemm(caller, 1, (uint32_t)nwg);
+    if (st == TSG_OK) st = gemm(caller, 1, (uint32_t)nwg, ctx->n_cus);
     return st;
   }
-  if (mode == TSG_MODE_COMPUTE_ONLY) return gemm(caller, 0, 0);
+  if (mode == TSG_MODE_COMPUTE_ONLY) return gemm(caller, 0, 0, ctx->n_cus);
 
   Pair pr;
   st = streams(ctx, o, &pr);
   if (st != TSG_OK) return st;
-  const int nwg = (o.aux_cus < 0 ? 64 : pr.aux_cus) * 2;
+  // Copy workgroups: each release of a chunk slice costs an L2 write-back, so
+  // a few wide workgroups (8 per XCD) rather than many.
+  const int nwg = o.aux_cus < 0 ? 64 : std::min(64, pr.aux_cus * 4);
   st = fork(ctx, caller, pr);
   if (st != TSG_OK) return st;
   // Producer (copy) first, consumer (GEMM) second: the copy never waits, so
   // even if the two kernels were serialised the GEMM's waits would all be
   // satisfied.
   st = copy(pr.aux, nwg);
-  if (st == TSG_OK && mode == TSG_MODE_OVERLAP) st = gemm(pr.main, 1, (uint32_t)nwg);
+  if (st == TSG_OK && mode == TSG_MODE_OVERLAP) st = gemm(pr.main, 1, (uint32_t)nwg, pr.main_cus);
   tsg_status sj = join(ctx, caller, pr);
   return st != TSG_OK ? st : sj;
 }

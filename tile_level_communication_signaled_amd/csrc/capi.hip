@@ -192,6 +192,8 @@ tsg_status tsg_ctx_create(int device, tsg_ctx** out) {
   if (khz > 0) c->wall_khz = khz;
   if (e == hipSuccess) e = hipMalloc(&c->d_sig, kSignals * sizeof(uint64_t));
   if (e == hipSuccess) e = hipMemset(c->d_sig, 0, kSignals * sizeof(uint64_t));
+  if (e == hipSuccess) e = hipMalloc(&c->d_cnt, kSignals * sizeof(uint32_t));
+  if (e == hipSuccess) e = hipMemset(c->d_cnt, 0, kSignals * sizeof(uint32_t));
   if (e == hipSuccess) e = hipMalloc(&c->d_status, 64);
   if (e == hipSuccess) e = hipMemset(c->d_status, 0, 64);
   if (e == hipSuccess) e = hipMalloc(&c->d_queue, 64 * sizeof(uint32_t));
@@ -229,6 +231,7 @@ void tsg_ctx_destroy(tsg_ctx* c) {
       if (c->ev_k[i][j]) (void)hipEventDestroy(c->ev_k[i][j]);
   }
   if (c->d_sig) (void)hipFree(c->d_sig);
+  if (c->d_cnt) (void)hipFree(c->d_cnt);
   if (c->d_status) (void)hipFree(c->d_status);
   if (c->d_queue) (void)hipFree(c->d_queue);
   if (c->d_timeline) (void)hipFree(c->d_timeline);
@@ -248,6 +251,9 @@ tsg_status tsg_check(tsg_ctx* ctx, void* stream) {
   uint32_t st = 0;
   TSG_HIP(ctx, hipMemcpy(&st, ctx->d_status, sizeof st, hipMemcpyDeviceToHost));
   if (st) {
+    // A timed-out call may have left arrival counters part-way: clear them.
+    TSG_HIP(ctx, hipDeviceSynchronize());
+    TSG_HIP(ctx, hipMemset(ctx->d_cnt, 0, ctx->n_sig * sizeof(uint32_t)));
     TSG_HIP(ctx, hipMemset(ctx->d_status, 0, sizeof(uint32_t)));
     if (st & tsg::ERR_TIMEOUT)
       return tsgh::fail(ctx, TSG_E_TIMEOUT, "a device-side signal wait timed out (status 0x%x)", st);

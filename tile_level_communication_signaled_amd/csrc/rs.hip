@@ -1,0 +1,312 @@
+// GEMM + ReduceScatter at one rank's share.
+//
+// Producer: the MFMA GEMM computes the full fp32 partial P = X W.  Row chunk c
+// of P (M/R rows) is the contribution destined for rank c.  As soon as a tile
+// is stored, one lane releases the done signal of every 128 x 128 sub-tile it
+// covers ("TileLink: Generating Efficient Compute-Communication Overlapping
+// Kernels using Tile-Centric Primitives", Table 3: producer_tile_notify;
+// section 5, Figure 4: the producer GEMM stores partial outputs and notifies
+// its consumer per tile).  Tiles of the local chunk come first by default
+// ("Triton-distributed: Programming Overlapping Kernels on Distributed AI
+// Systems with the Triton Compiler", section 3.7: the producer's tile order
+// follows the order its consumers need; the inter-node variant puts the local
+// chunk last, which the order knob selects).
+//
+// Consumer: the reduction stream of that page's Algorithm 3 (section 3.3):
+// for each 128 x 128 tile of the local chunk it sums the R-1 peers' partials
+// (already resident, no wait), then acquires the tile's done signal
+// (consumer_tile_wait) and adds the local partial.  Summation order: peers in
+// ascending rank order, then the local partial.
+#include "tsg_gemm.hpp"
+#include "tsg_internal.hpp"
+
+using namespace tsg;
+
+namespace {
+
+constexpr int kMaxRanks = 32;
+constexpr int kMaxMTiles = 1024;
+constexpr size_t kSigBase = 4096;      // RS signals start here in the context's pool
+constexpr int kFlagTile = 128;         // signal granularity (rows and columns)
+
+struct RsGemmArgs {
+  const uint16_t* x;
+  const uint16_t* w;
+  float* partial;
+  uint64_t* flags;
+  SyncArgs sa;
+  Timeline tl;
+  int M, N, K;
+  int n_tiles_n;
+  int n_ftn;             // 128-column signal tiles per row of signals
+  int per_xcd;
+  int chunk_rows;
+  uint32_t skip_mask;    // chunks whose signals are not published (test hook)
+  uint16_t mt_order[kMaxMTiles];
+};
+
+template <class Cfg, bool DIRECT>
+__global__ void __launch_bounds__(Cfg::NT) rs_gemm_kernel(const RsGemmArgs args) {
+  __shared__ __attribute__((aligned(16))) char lds[DIRECT ? Cfg::LDS_DIRECT : Cfg::LDS_REGS];
+  const int t = xcd_remap(blockIdx.x, gridDim.x, args.per_xcd);
+  const int mt = args.mt_order[t / args.n_tiles_n];
+  const int nt = t % args.n_tiles_n;
+  const int row0 = mt * Cfg::BM, col0 = nt * Cfg::BN;
+  const uint64_t t0 = args.tl.buf ? wall_clock64() : 0;
+  typename GemmTile<Cfg>::Acc acc;
+  const ARowsLinear ar{args.x, args.K, row0, args.M};
+  if (DIRECT)
+    GemmTile<Cfg>::run_direct(ar, args.w, args.N, col0, args.N, args.K, lds, acc);
+  else
+    GemmTile<Cfg>::run_regs(ar, args.w, args.N, col0, args.N, args.K, lds, acc);
+  const int M = args.M, N = args.N;
+  float* P = args.partial;
+  GemmTile<Cfg>::for_each(acc, [&](int r, int c, float v) {
+    const int gr = row0 + r, gc = col0 + c;
+    if (gr < M && gc < N) P[(int64_t)gr * N + gc] = v;
+  });
+  // producer_tile_notify: one release for the whole tile, then one relaxed
+  // store per covered 128 x 128 signal.
+  block_release_fence();
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");
+    const uint64_t v = sig_target(args.sa.epoch, 1);
+    for (int i = 0; i < Cfg::BM / kFlagTile; ++i) {
+      const int r = row0 + i * kFlagTile;
+      if (r >= M || ((args.skip_mask >> (r / args.chunk_rows)) & 1u)) continue;
+      for (int j = 0; j < Cfg::BN / kFlagTile; ++j) {
+        const int c = col0 + j * kFlagTile;
+        if (c >= N) continue;
+        __hip_atomic_store(args.flags + (int64_t)(r / kFlagTile) * args.n_ftn + c / kFlagTile, v,
+                           __ATOMIC_RELAXED, TSG_SIG_SCOPE);
+      }
+    }
+    if (args.tl.buf) timeline_put(args.tl, 3, (uint32_t)(mt << 16 | nt), t0, t0, wall_clock64());
+  }
+}
+
+struct RsReduceArgs {
+  const float* partial;
+  const float* peers;
+  float* out;
+  const uint64_t* flags;
+  SyncArgs sa;
+  Timeline tl;
+  int M, N, R, rank;
+  int chunk_rows;
+  int n_ftn;
+  int ftm0, n_ftm;       // signal rows covering the local chunk
+  int wait;
+};
+
+// Work unit: 16 rows x 128 columns of one 128 x 128 signal tile of the
+// local chunk; thread (ry, cx) owns rows ry and ry + 8 at float4 column cx
+// and loads both rows of four peers at a time before summing them (eight
+// 16-byte loads in flight per thread, few enough registers to share a SIMD
+// with a GEMM wave).  Workgroup g takes units g, g + G, ...;
+// the 8 units of a tile are consecutive, so they follow the producer's
+// (row-major) tile order and only the first wait on a tile can spin.
+__global__ void __launch_bounds__(256) rs_reduce_kernel(const RsReduceArgs a) {
+  const int n_units = a.n_ftm * a.n_ftn * 8;
+  const int c0 = a.rank * a.chunk_rows, c1 = c0 + a.chunk_rows;
+  const int cx = threadIdx.x & 31;
+  const int ry = threadIdx.x >> 5;
+  for (int u = blockIdx.x; u < n_units; u += gridDim.x) {
+    const int tile = u >> 3, part = u & 7;
+    const int ftm = a.ftm0 + tile / a.n_ftn, ftn = tile % a.n_ftn;
+    const int col = ftn * kFlagTile + cx * 4;
+    const int r0 = ftm * kFlagTile + part * 16 + ry, r1 = r0 + 8;
+    const bool ok0 = col < a.N && r0 >= c0 && r0 < c1;
+    const bool ok1 = col < a.N && r1 >= c0 && r1 < c1;
+    const uint64_t t0 = a.tl.buf ? wall_clock64() : 0;
+    float4 v0[4], v1[4];
+    float4 s0 = make_float4(0.f, 0.f, 0.f, 0.f), s1 = s0;
+    // peers in ascending rank order (the local rank is skipped)
+    for (int p0 = 0; p0 < a.R - 1; p0 += 4) {
+      const int np = min(4, a.R - 1 - p0);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        if (p < np) {
+          const float* pp = a.peers + (int64_t)(p0 + p) * a.chunk_rows * a.N;
+          if (ok0) v0[p] = *(const float4*)(pp + (int64_t)(r0 - c0) * a.N + col);
+          if (ok1) v1[p] = *(const float4*)(pp + (int64_t)(r1 - c0) * a.N + col);
+        }
+      }
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        if (p < np) {
+          if (ok0) { s0.x += v0[p].x; s0.y += v0[p].y; s0.z += v0[p].z; s0.w += v0[p].w; }
+          if (ok1) { s1.x += v1[p].x; s1.y += v1[p].y; s1.z += v1[p].z; s1.w += v1[p].w; }
+        }
+      }
+    }
+    if (a.wait) block_wait_ge(a.flags + (int64_t)ftm * a.n_ftn + ftn, sig_target(a.sa.epoch, 1), a.sa);
+    const uint64_t t1 = a.tl.buf ? wall_clock64() : 0;
+    if (ok0) {
+      const float4 q = *(const float4*)(a.partial + (int64_t)r0 * a.N + col);
+      *(float4*)(a.out + (int64_t)(r0 - c0) * a.N + col) = make_float4(s0.x + q.x, s0.y + q.y, s0.z + q.z, s0.w + q.w);
+    }
+    if (ok1) {
+      const float4 q = *(const float4*)(a.partial + (int64_t)r1 * a.N + col);
+      *(float4*)(a.out + (int64_t)(r1 - c0) * a.N + col) = make_float4(s1.x + q.x, s1.y + q.y, s1.z + q.z, s1.w + q.w);
+    }
+    if (a.tl.buf && threadIdx.x == 0 && part == 0)
+      timeline_put(a.tl, 4, (uint32_t)(ftm << 16 | ftn), t0, t1, wall_clock64());
+  }
+}
+
+using Cfg1 = TileCfg<256, 256, 2, 2>;
+using Cfg3 = TileCfg<128, 128, 2, 2>;
+using Cfg4 = TileCfg<256, 128, 2, 2>;
+using Cfg5 = TileCfg<128, 256, 2, 2>;
+
+struct TileShape {
+  int bm, bn;
+};
+
+TileShape shape_of(int id) {
+  switch (id) {
+    case 1: return {256, 256};
+    case 3: return {128, 128};
+    case 4: return {256, 128};
+    case 5: return {128, 256};
+    default: return {0, 0};
+  }
+}
+
+template <class Cfg>
+hipError_t launch_cfg(const RsGemmArgs& a, int grid, hipStream_t s) {
+  if (a.K % (2 * Cfg::BK) == 0)
+    hipLaunchKernelGGL((rs_gemm_kernel<Cfg, true>), dim3(grid), dim3(Cfg::NT), 0, s, a);
+  else
+    hipLaunchKernelGGL((rs_gemm_kernel<Cfg, false>), dim3(grid), dim3(Cfg::NT), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm(int id, const RsGemmArgs& a, int grid, hipStream_t s) {
+  switch (id) {
+    case 1: return launch_cfg<Cfg1>(a, grid, s);
+    case 3: return launch_cfg<Cfg3>(a, grid, s);
+    case 4: return launch_cfg<Cfg4>(a, grid, s);
+    case 5: return launch_cfg<Cfg5>(a, grid, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+tsg_status tsg_op_rs(tsg_ctx* ctx, const void* x, const void* w, float* partial,
+                     const float* peer_partials, float* out, int M, int N, int K, int R, int rank,
+                     const tsg_opts* opts, int mode, void* stream) {
+  using namespace tsgh;
+  if (!x || !w || !partial || !out || (R > 1 && !peer_partials))
+    return fail(ctx, TSG_E_INVALID, "gemm_rs_overlap: null pointer");
+  if (mode < TSG_MODE_OVERLAP || mode > TSG_MODE_COMM_ONLY) return fail(ctx, TSG_E_INVALID, "bad mode");
+  if (R < 1 || R > kMaxRanks || rank < 0 || rank >= R)
+    return fail(ctx, TSG_E_SHAPE, "need 1 <= R <= %d and 0 <= rank < R", kMaxRanks);
+  if (M < R || M % R || N < 8 || K < 8 || N % 8 || K % 8)
+    return fail(ctx, TSG_E_SHAPE, "gemm_rs_overlap: bad shape M=%d N=%d K=%d R=%d", M, N, K, R);
+  if (!aligned16(x) || !aligned16(w) || !aligned16(partial) || !aligned16(out) ||
+      (peer_partials && !aligned16(peer_partials)))
+    return fail(ctx, TSG_E_ALIGN, "gemm_rs_overlap: pointers must be 16-byte aligned");
+  if ((int64_t)M * K * 2 >= (int64_t(1) << 32) || (int64_t)K * N * 2 >= (int64_t(1) << 32))
+    return fail(ctx, TSG_E_UNSUPPORTED, "operands of 4 GiB or more are not supported");
+
+  const Opts o = resolve(opts, -1);
+  const int tile = o.tile ? o.tile : ((M >= 2048 && N >= 1024) ? 1 : 3);
+  const TileShape ts = shape_of(tile);
+  if (!ts.bm) return fail(ctx, TSG_E_INVALID, "tile id %d is not available for gemm_rs_overlap", tile);
+  const int chunk_rows = M / R;
+  const int n_mt = (M + ts.bm - 1) / ts.bm, n_nt = (N + ts.bn - 1) / ts.bn;
+  if (n_mt > kMaxMTiles) return fail(ctx, TSG_E_UNSUPPORTED, "M / BM exceeds %d", kMaxMTiles);
+  const int n_ftm = (M + kFlagTile - 1) / kFlagTile, n_ftn = (N + kFlagTile - 1) / kFlagTile;
+  if (kSigBase + (size_t)n_ftm * n_ftn > ctx->n_sig)
+    return fail(ctx, TSG_E_UNSUPPORTED, "too many 128x128 tiles for the signal pool");
+
+  TSG_HIP(ctx, hipSetDevice(ctx->device));
+  hipStream_t caller = (hipStream_t)stream;
+  ++ctx->epoch;
+  time_reset(ctx);
+
+  RsGemmArgs ga;
+  ga.x = (const uint16_t*)x;
+  ga.w = (const uint16_t*)w;
+  ga.partial = partial;
+  ga.flags = ctx->d_sig + kSigBase;
+  ga.sa = sync_args(ctx, o);
+  ga.tl = timeline(ctx, o);
+  ga.M = M;
+  ga.N = N;
+  ga.K = K;
+  ga.n_tiles_n = n_nt;
+  ga.n_ftn = n_ftn;
+  ga.chunk_rows = chunk_rows;
+  ga.skip_mask = o.skip_mask;
+  // M-tile order: by the position of the tile's first chunk in the order
+  // local, rank+1, rank+2, ... (order 0) or rank+1, ..., local last (order 1).
+  {
+    std::vector<std::pair<int, int>> key(n_mt);
+    for (int m = 0; m < n_mt; ++m) {
+      const int c = (m * ts.bm) / chunk_rows;
+      int pos = (c - rank + R) % R;
+      if (o.order == 1) pos = (pos + R - 1) % R;
+      key[m] = {pos, m};
+    }
+    std::sort(key.begin(), key.end());
+    for (int m = 0; m < n_mt; ++m) ga.mt_order[m] = (uint16_t)key[m].second;
+  }
+
+  RsReduceArgs ra;
+  ra.partial = partial;
+  ra.peers = peer_partials;
+  ra.out = out;
+  ra.flags = ga.flags;
+  ra.sa = ga.sa;
+  ra.tl = ga.tl;
+  ra.M = M;
+  ra.N = N;
+  ra.R = R;
+  ra.rank = rank;
+  ra.chunk_rows = chunk_rows;
+  ra.n_ftn = n_ftn;
+  ra.ftm0 = (rank * chunk_rows) / kFlagTile;
+  ra.n_ftm = ((rank + 1) * chunk_rows - 1) / kFlagTile - ra.ftm0 + 1;
+  const int n_red_tiles = ra.n_ftm * n_ftn;
+  if (o.timeline) TSG_HIP(ctx, hipMemsetAsync(ctx->d_timeline_n, 0, sizeof(uint32_t), caller));
+
+  auto gemm = [&](hipStream_t s, int cus) -> tsg_status {
+    ga.per_xcd = cus / 8;
+    time_begin(ctx, 0, s);
+    hipError_t e = launch_gemm(tile, ga, n_mt * n_nt, s);
+    time_end(ctx, 0, s);
+    if (e != hipSuccess) return hip_fail(ctx, e, "rs_gemm_kernel");
+    return TSG_OK;
+  };
+  auto reduce = [&](hipStream_t s, int nwg, int wait) -> tsg_status {
+    ra.wait = wait;
+    time_begin(ctx, 1, s);
+    hipLaunchKernelGGL(rs_reduce_kernel, dim3(std::max(1, std::min(nwg, 8 * n_red_tiles))), dim3(256), 0, s, ra);
+    time_end(ctx, 1, s);
+    return check_launch(ctx, "rs_reduce_kernel");
+  };
+
+  tsg_status st = TSG_OK;
+  if (mode == TSG_MODE_SERIAL) {
+    st = gemm(caller, ctx->n_cus);
+    if (st == TSG_OK) st = reduce(caller, ctx->n_cus * 2, 1);
+    return st;
+  }
+  if (mode == TSG_MODE_COMPUTE_ONLY) return gemm(caller, ctx->n_cus);
+
+  Pair pr;
+  st = streams(ctx, o, &pr);
+  if (st != TSG_OK) return st;
+  const int nwg = o.aux_cus < 0 ? ctx->n_cus : pr.aux_cus * 2;
+  st = fork(ctx, caller, pr);
+  if (st != TSG_OK) return st;
+  // Producer (GEMM) first, consumer (reduce) second: the GEMM never waits.
+  if (mode == TSG_MODE_OVERLAP) st = gemm(pr.main, pr.main_cus);
+  if (st == TSG_OK) st = reduce(pr.aux, nwg, mode == TSG_MODE_OVERLAP ? 1 : 0);
+  tsg_status sj = join(ctx, caller, pr);
+  return st != TSG_OK ? st : sj;
+}

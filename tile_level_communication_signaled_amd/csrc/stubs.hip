@@ -1,14 +1,6 @@
 // Entry points whose kernels are not built yet: they reject every call.
 #include "tsg_internal.hpp"
 
-tsg_status tsg_op_rs(tsg_ctx* ctx, const void*, const void*, float*, const float*, float*, int, int,
-                     int, int, int, const tsg_opts*, int, void*) {
-  return tsgh::fail(ctx, TSG_E_UNSUPPORTED, "gemm_rs_overlap is not available in this build");
-}
-tsg_status tsg_op_mlp2(tsg_ctx* ctx, const void*, const void*, void*, const void*, float*, int, int,
-                       int, int, const tsg_opts*, int, void*) {
-  return tsgh::fail(ctx, TSG_E_UNSUPPORTED, "mlp2_pipelined is not available in this build");
-}
 tsg_status tsg_op_moe(tsg_ctx* ctx, const void*, const int32_t*, const float*, const void*,
                       const void*, float*, int32_t*, int32_t*, void*, size_t, int, int, int, int,
                       int, const tsg_opts*, int, void*) {

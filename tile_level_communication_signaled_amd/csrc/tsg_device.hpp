@@ -7,12 +7,13 @@
 // notify carries release semantics, wait carries acquire semantics; a consumer
 // tile is ready once every producer tile it depends on is done).
 //
-// A signal is one 64-bit word {epoch:32 | count:32}.  Each call of the host API
-// draws a fresh epoch e; a producer "arrives" by moving the word to
-// {e | count+1} (or to {e | 1} if the word still carries an older epoch), with
-// release ordering.  A consumer waiting for n arrivals spins until the word is
-// >= {e | n}, then acquires.  Because epochs only grow, no reset pass is needed
-// between calls, and any number of producers may share one signal.
+// A signal is one 64-bit word {epoch:32 | n:32}.  Each call of the host API
+// draws a fresh epoch e.  A signal with one producer is published by storing
+// {e | 1} with release ordering.  A signal shared by n producers has a 32-bit
+// arrival counter beside it: every producer adds one (acquire-release), and
+// the one that completes the count resets the counter and stores {e | n}.  A
+// consumer spins until the word is >= {e | n}, then acquires.  Because epochs
+// only grow, signal words need no reset pass between calls.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -54,35 +55,33 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-// One producer arrives on signal `s` (release).  Must be called by a single
-// lane after the data it publishes is complete and visible (see
-// block_release_arrive).
-__device__ __forceinline__ void sig_arrive_lane(uint64_t* s, uint32_t epoch) {
-  uint64_t old = __hip_atomic_load(s, __ATOMIC_RELAXED, TSG_SIG_SCOPE);
-  for (;;) {
-    const uint64_t nv = ((uint32_t)(old >> 32) == epoch) ? old + 1 : sig_target(epoch, 1);
-    if (__hip_atomic_compare_exchange_strong(s, &old, nv, __ATOMIC_RELEASE, __ATOMIC_RELAXED,
-                                             TSG_SIG_SCOPE))
-      return;
+// Single producer: publish {epoch | n} with release ordering (one lane).
+__device__ __forceinline__ void sig_publish_lane(uint64_t* s, uint32_t epoch, uint32_t n) {
+  __hip_atomic_store(s, sig_target(epoch, n), __ATOMIC_RELEASE, TSG_SIG_SCOPE);
+}
+
+// n producers share one signal: each arrives once on the 32-bit arrival
+// counter `cnt` (acquire-release fetch-add, so the last arriver has acquired
+// every other arriver's release); the last one resets the counter for the
+// next call and publishes {epoch | n} with release ordering.  One lane.
+__device__ __forceinline__ void sig_arrive_counted_lane(uint32_t* cnt, uint64_t* s, uint32_t n,
+                                                        uint32_t epoch) {
+  const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_ACQ_REL, TSG_SIG_SCOPE);
+  if (old == n - 1) {
+    __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, TSG_SIG_SCOPE);
+    __hip_atomic_store(s, sig_target(epoch, n), __ATOMIC_RELEASE, TSG_SIG_SCOPE);
   }
 }
 
-// Whole workgroup: make this block's prior global stores visible device-wide
-// (each wave waits for its stores and writes back its XCD's L2 through the
-// release fence), then one lane arrives on each of `n` signals.
-__device__ __forceinline__ void block_release_arrive(uint64_t* sigs, const int* idx, int n,
-                                                     uint32_t epoch) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+// Whole workgroup, before one lane publishes or arrives: every wave waits
+// until its global stores have been acknowledged by its XCD's L2, then the
+// barrier orders all waves before the publishing lane, whose release at
+// system scope writes that L2 back.  One write-back per workgroup instead of
+// one per wave.
+__device__ __forceinline__ void block_release_fence() {
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int i = 0; i < n; ++i) sig_arrive_lane(sigs + idx[i], epoch);
-  }
-}
-
-__device__ __forceinline__ void block_release_arrive1(uint64_t* s, uint32_t epoch) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  __syncthreads();
-  if (threadIdx.x == 0) sig_arrive_lane(s, epoch);
 }
 
 // Wave-level wait: every lane of the calling wave executes this with the same
@@ -129,6 +128,20 @@ __device__ __forceinline__ void block_wait_ge(const uint64_t* s, uint64_t target
   if (threadIdx.x < 64) wave_wait_ge(s, target, sa);
   __syncthreads();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs, each with its own
+// L2.  Map launch index w to a logical tile index so that every XCD runs a
+// contiguous block of `per_xcd` logical tiles out of each wave of
+// 8 * per_xcd (neighbouring tiles share operand rows or columns, which then
+// stay in one L2).  A final partial wave keeps the identity mapping, so the
+// map is a bijection on [0, G).
+__device__ __forceinline__ int xcd_remap(int w, int G, int per_xcd) {
+  const int wave = 8 * per_xcd;
+  const int v = w / wave;
+  if (per_xcd <= 0 || (v + 1) * wave > G) return w;
+  const int r = w - v * wave;
+  return v * wave + (r & 7) * per_xcd + (r >> 3);
 }
 
 // Timeline record: {kind<<56 | id, t_start, t_ready, t_end}.

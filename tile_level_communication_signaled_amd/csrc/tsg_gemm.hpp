@@ -3,16 +3,21 @@
 // One workgroup computes a BM x BN tile of C = A * B with A [M x K] and
 // B [K x N] both row-major bf16, accumulating in fp32 with
 // v_mfma_f32_32x32x16_bf16.  The K loop moves BK = 64 columns of A and rows of
-// B per step through a two-stage LDS ring:
+// B per step through LDS:
 //
-//   * A is staged as BM rows x 8 chunks of 16 bytes (8 bf16 along k).
+//   * A is staged as BM rows x 8 chunks of 16 bytes (8 bf16 along k).  On the
+//     main path A goes straight from global memory to LDS (16-byte
+//     global_load_lds), through a three-stage ring, so it costs no registers.
 //   * B is staged transposed, as BN rows (one per output column n) x 8 chunks
 //     of 8 consecutive k, so that both MFMA operands are read as one 16-byte
-//     LDS load per lane.  The transpose happens in registers while staging:
-//     each thread loads an 8 (k) x 8 (n) block with eight coalesced 16-byte
-//     row loads and repacks it with byte permutes.
-//   * Chunk c of LDS row r is stored at chunk position c ^ (r & 7), so the
-//     16-byte reads of 8 consecutive rows hit 8 distinct bank groups.
+//     LDS load per lane.  The transpose happens in registers: each thread
+//     loads an 8 (k) x 8 (n) block with eight coalesced 16-byte row loads and
+//     repacks it with byte permutes.  Two register sets and a two-stage LDS
+//     ring keep the loads of step kt + 2 in flight while step kt is computed.
+//   * Chunk c of LDS row r is stored at chunk position c ^ ((r / 2) mod 8), so
+//     the 16-byte reads of 16 consecutive rows (and the transposed B writes,
+//     issued in an order that alternates row parity across lanes) hit
+//     distinct bank groups.
 //
 // Waves are arranged WM x WN; a wave owns a (BM/WM) x (BN/WN) sub-tile made of
 // 32x32 MFMA fragments.  Operand layout of the 32x32x16 bf16 MFMA: lane l
@@ -21,11 +26,13 @@
 // fragment gives lane l column (l mod 32) and, in register v, row
 // 8*(v / 4) + 4*(l / 32) + (v mod 4).
 //
-// Loads of rows beyond M, columns beyond N and k beyond K read zeros (N and K
-// must be multiples of 8), so ragged tiles need no special path.  The pages
-// ask tile-level single-device kernels to coalesce global accesses, keep LDS
-// free of bank conflicts, pipeline loads against compute and use the matrix
-// units ([TL] section 4.3).
+// Rows beyond M read a valid row instead (their results are never stored);
+// columns beyond N read zeros (N must be a multiple of 8).  The main path
+// needs K to be a multiple of 128; the fallback path (A staged through
+// registers too, one step of prefetch) zero-fills k beyond K (K a multiple of
+// 8).  The pages ask tile-level single-device kernels to coalesce global
+// accesses, keep LDS free of bank conflicts, pipeline loads against compute
+// and use the matrix units ([TL] section 4.3).
 #pragma once
 
 #include "tsg_device.hpp"
@@ -36,24 +43,35 @@ template <int BM_, int BN_, int WM_, int WN_>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
   static constexpr int BK = 64;
-  static constexpr int NT = 64 * WM * WN;
+  static constexpr int NW = WM * WN;
+  static constexpr int NT = 64 * NW;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int FM = WTM / 32, FN = WTN / 32;
   static constexpr int A_STAGE = BM * BK * 2;
   static constexpr int B_STAGE = BN * BK * 2;
-  static constexpr int STAGE = A_STAGE + B_STAGE;
-  static constexpr int LDS = 2 * STAGE;
+  static constexpr int LDS_DIRECT = 3 * A_STAGE + 2 * B_STAGE;
+  static constexpr int LDS_REGS = 2 * (A_STAGE + B_STAGE);
   static constexpr int A_CH = BM * 8;               // 16-byte chunks per A stage
-  static constexpr int A_PT = (A_CH + NT - 1) / NT; // chunks per thread
+  static constexpr int A_PT = (A_CH + NT - 1) / NT; // chunks per thread (register path)
+  static constexpr int A_BLK = BM / 8;              // 1 KB blocks of 8 rows per A stage
+  static constexpr int A_BPW = (A_BLK + NW - 1) / NW;  // blocks per wave (direct path)
   static constexpr int B_BL = BN;                   // 8x8 blocks per B stage
   static constexpr int B_PT = (B_BL + NT - 1) / NT; // blocks per thread
+  static constexpr int VM_PER_STEP = A_BPW + 8 * B_PT;  // VMEM ops per thread per step
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
-  static_assert(BN % 8 == 0, "BN must be a multiple of 8");
-  static_assert(LDS <= 160 * 1024, "LDS budget of one CU exceeded");
+  static_assert(BN % 8 == 0 && BM % 8 == 0, "BM and BN must be multiples of 8");
+  static_assert(LDS_REGS <= 160 * 1024, "LDS budget of one CU exceeded");
+  static_assert(VM_PER_STEP < 64, "too many loads per step for one wait count");
 };
 
+// Physical 16-byte position of logical chunk `chunk` of LDS row `row`.  A
+// row is 128 bytes; with 64 banks of 4 bytes, the 16 lanes served together by
+// a 16-byte access hit distinct banks iff their (row parity, position) pairs
+// are distinct.  The MFMA fragment reads touch 16 consecutive rows at one
+// logical chunk, so the position is XORed with (row / 2) mod 8.
+__device__ __forceinline__ int lds_pos(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 __device__ __forceinline__ uint32_t lds_swz(int row, int chunk) {
-  return (uint32_t)(((row << 3) | (chunk ^ (row & 7))) << 4);
+  return (uint32_t)(((row << 3) | lds_pos(row, chunk)) << 4);
 }
 
 // lo = a.lo16, hi = b.lo16
@@ -65,8 +83,16 @@ __device__ __forceinline__ uint32_t pack_hi16(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
 
+// s_waitcnt with vmcnt <= n and no wait on the other counters (gfx9 encoding:
+// vmcnt in bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
 // Source rows of the A operand of one tile.  row(r) gives the element offset
-// of tile row r in `base`, or -1 for a row that reads as zeros.
+// of tile row r in `base`, or -1 for a row outside the operand.
 struct ARowsLinear {
   const uint16_t* base;
   int64_t ld;
@@ -78,7 +104,7 @@ struct ARowsLinear {
   }
 };
 
-// Gathered rows: idx[r] is the source row index (or < 0 for a zero row).
+// Gathered rows: idx[r] is the source row index (or < 0 for no row).
 struct ARowsGather {
   const uint16_t* base;
   int64_t ld;
@@ -93,124 +119,242 @@ template <class Cfg>
 struct GemmTile {
   using Acc = f32x16_t[Cfg::FM][Cfg::FN];
 
-  // A source of this tile, B source, sizes.
-  template <class ARows>
-  __device__ __forceinline__ static void run(const ARows& ar, const uint16_t* __restrict__ B,
-                                             int64_t ldb, int col0, int N, int K, char* lds,
-                                             Acc& acc) {
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm0 = (wave / Cfg::WN) * Cfg::WTM;
-    const int wn0 = (wave % Cfg::WN) * Cfg::WTN;
+  struct BRegs {
+    u32x4_t b[Cfg::B_PT][8];
+  };
 
+  __device__ __forceinline__ static void zero(Acc& acc) {
 #pragma unroll
     for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
       for (int j = 0; j < Cfg::FN; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  }
 
-    // Per-thread A chunks: fixed row and chunk column for the whole K loop.
-    int64_t a_off[Cfg::A_PT];
-    int a_c[Cfg::A_PT];
-#pragma unroll
-    for (int i = 0; i < Cfg::A_PT; ++i) {
-      const int q = tid + i * Cfg::NT;
-      const int r = q >> 3;
-      a_c[i] = q & 7;
-      a_off[i] = (q < Cfg::A_CH) ? ar.row(r) : (int64_t)-1;
-    }
-    // Per-thread B blocks: k block kb (8 rows) and n block nb (8 columns).
-    int b_kb[Cfg::B_PT], b_n[Cfg::B_PT];
-    bool b_ok[Cfg::B_PT];
+  // Thread q of a B stage moves the 8 x 8 block at k block (q mod 8) and n
+  // block (q / 8): each of its 8 row loads is one 16-byte piece of a 128-byte
+  // run that 8 consecutive lanes cover.  boff = byte offset of the block's
+  // first element relative to row k0 of B (fixed for the whole K loop).
+  struct BAddr {
+    uint32_t boff[Cfg::B_PT];
+    bool ok[Cfg::B_PT];
+    int kb[Cfg::B_PT];
+  };
+
+  __device__ __forceinline__ static void b_addr(BAddr& ba, int64_t ldb, int col0, int N) {
+    const int tid = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < Cfg::B_PT; ++i) {
       const int q = tid + i * Cfg::NT;
-      b_kb[i] = q / (Cfg::BN / 8);
-      b_n[i] = (q % (Cfg::BN / 8)) * 8;
-      b_ok[i] = (q < Cfg::B_BL) && (col0 + b_n[i] < N);
+      const int kb = q & 7;
+      const int n = (q >> 3) * 8;
+      ba.kb[i] = kb;
+      ba.ok[i] = (q < Cfg::B_BL) && (col0 + n < N);
+      ba.boff[i] = (uint32_t)(((int64_t)kb * 8 * ldb + col0 + n) * 2);
     }
+  }
 
+  // Global loads of one 64 x BN step of B into registers.  CHECK_K: zero the
+  // rows at or beyond K.
+  template <bool CHECK_K>
+  __device__ __forceinline__ static void load_b(BRegs& rg, const BAddr& ba,
+                                                const uint16_t* __restrict__ B, int64_t ldb, int K,
+                                                int k0) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const char* row = (const char*)B + (int64_t)(k0 + j) * ldb * 2;  // uniform
+#pragma unroll
+      for (int i = 0; i < Cfg::B_PT; ++i) {
+        const bool ok = ba.ok[i] && (!CHECK_K || k0 + ba.kb[i] * 8 + j < K);
+        if (ok)
+          rg.b[i][j] = *(const u32x4_t*)(row + ba.boff[i]);
+        else
+          rg.b[i][j] = u32x4_t{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+
+  // Transpose the 8x8 blocks in registers and write them to a B stage.  LDS
+  // row n + s holds output column n + s.  Lanes whose n block is odd write
+  // their rows in the order 1,0,3,2,... instead of 0,1,2,3,..., so that each
+  // write instruction covers both row parities (see lds_swz).
+  __device__ __forceinline__ static void store_b(const BRegs& rg, char* lb) {
+    const int tid = threadIdx.x;
+    constexpr uint32_t LO = 0x05040100u, HI = 0x07060302u;
+#pragma unroll
+    for (int i = 0; i < Cfg::B_PT; ++i) {
+      const int q = tid + i * Cfg::NT;
+      if (q < Cfg::B_BL) {
+        const int kb = q & 7;
+        const int n = (q >> 3) * 8;
+        const int par = (q >> 3) & 1;
+        const uint32_t s0 = par ? HI : LO, s1 = par ? LO : HI;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          u32x4_t v0, v1;
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            v0[p] = __builtin_amdgcn_perm(rg.b[i][2 * p + 1][m], rg.b[i][2 * p][m], s0);
+            v1[p] = __builtin_amdgcn_perm(rg.b[i][2 * p + 1][m], rg.b[i][2 * p][m], s1);
+          }
+          *(u32x4_t*)(lb + lds_swz(n + 2 * m + par, kb)) = v0;
+          *(u32x4_t*)(lb + lds_swz(n + 2 * m + (par ^ 1), kb)) = v1;
+        }
+      }
+    }
+  }
+
+  // One BK step from LDS: 4 k sub-steps of 16.  The fragments of sub-step
+  // ks + 1 are read before the MFMAs of sub-step ks are issued.
+  __device__ __forceinline__ static void compute(const char* la, const char* lb, Acc& acc) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wm0 = (wave / Cfg::WN) * Cfg::WTM;
+    const int wn0 = (wave % Cfg::WN) * Cfg::WTN;
+    const int l32 = lane & 31;
+    const int hi = lane >> 5;
+    bf16x8_t af[2][Cfg::FM], bfr[2][Cfg::FN];
+    auto rd = [&](int buf, int ks) {
+#pragma unroll
+      for (int i = 0; i < Cfg::FM; ++i)
+        af[buf][i] = *(const bf16x8_t*)(la + lds_swz(wm0 + i * 32 + l32, 2 * ks + hi));
+#pragma unroll
+      for (int j = 0; j < Cfg::FN; ++j)
+        bfr[buf][j] = *(const bf16x8_t*)(lb + lds_swz(wn0 + j * 32 + l32, 2 * ks + hi));
+    };
+    rd(0, 0);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (ks + 1 < 4) rd((ks + 1) & 1, ks + 1);
+#pragma unroll
+      for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < Cfg::FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][i], bfr[ks & 1][j],
+                                                               acc[i][j], 0, 0, 0);
+    }
+  }
+
+  // Main path (K % 128 == 0, so the step count is even and the loop below,
+  // unrolled by two, has no exit in its middle): A global -> LDS directly,
+  // three A stages.
+  // LDS layout: [A0 A1 A2 B0 B1], Cfg::LDS_DIRECT bytes.
+  template <class ARows>
+  __device__ __forceinline__ static void run_direct(const ARows& ar,
+                                                    const uint16_t* __restrict__ B, int64_t ldb,
+                                                    int col0, int N, int K, char* lds, Acc& acc) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    char* const lds_a = lds;
+    char* const lds_b = lds + 3 * Cfg::A_STAGE;
+    zero(acc);
+
+    // Byte offsets of the A rows this lane moves: block b = wave + t*NW covers
+    // tile rows 8b .. 8b + 7; lane l fills LDS slot l of the block, i.e. row
+    // r = 8b + l/8 at position l mod 8, which holds logical chunk
+    // (l mod 8) ^ ((r / 2) mod 8) (lds_pos is its own inverse in the chunk).
+    uint32_t a_off[Cfg::A_BPW];
+#pragma unroll
+    for (int t = 0; t < Cfg::A_BPW; ++t) {
+      const int b = wave + t * Cfg::NW;
+      const int r = b * 8 + (lane >> 3);
+      int64_t off = (b < Cfg::A_BLK) ? ar.row(r) : (int64_t)0;
+      if (off < 0) off = 0;  // outside the operand: read a valid row, result never stored
+      a_off[t] = (uint32_t)((off + lds_pos(r, lane & 7) * 8) * 2);
+    }
+    auto issue_a = [&](int stage, int k0) {
+      char* la = lds_a + stage * Cfg::A_STAGE;
+      const char* base = (const char*)ar.base + (int64_t)k0 * 2;  // uniform
+#pragma unroll
+      for (int t = 0; t < Cfg::A_BPW; ++t) {
+        const int b = wave + t * Cfg::NW;
+        if (b < Cfg::A_BLK)
+          __builtin_amdgcn_global_load_lds((const void*)(base + a_off[t]),
+                                           (__attribute__((address_space(3))) void*)(la + b * 1024),
+                                           16, 0, 0);
+      }
+    };
+    BAddr ba;
+    b_addr(ba, ldb, col0, N);
+
+    const int nk = K / Cfg::BK;
+    BRegs r0, r1;
+    issue_a(0, 0);
+    load_b<false>(r0, ba, B, ldb, K, 0);
+    if (nk > 1) {
+      issue_a(1, Cfg::BK);
+      load_b<false>(r1, ba, B, ldb, K, Cfg::BK);
+    }
+    store_b(r0, lds_b);
+    if (nk > 1) wait_vmcnt<Cfg::VM_PER_STEP>(); else wait_vmcnt<0>();
+    __syncthreads();
+    // Step kt: A in stage kt % 3, B in stage kt % 2.  Loads of step kt + 2
+    // are issued first (A into the stage step kt - 1 vacated, B into the
+    // register set whose contents were stored last step); then step kt is
+    // computed; then step kt + 1's B is written to LDS; the wait leaves only
+    // this step's loads outstanding, so step kt + 1's A has landed before the
+    // barrier.
+    int sa = 0;
+    for (int kt = 0; kt < nk; kt += 2) {
+      const int sa2 = sa >= 1 ? sa - 1 : 2;   // (kt + 2) % 3
+      if (kt + 2 < nk) {
+        issue_a(sa2, (kt + 2) * Cfg::BK);
+        load_b<false>(r0, ba, B, ldb, K, (kt + 2) * Cfg::BK);
+      }
+      compute(lds_a + sa * Cfg::A_STAGE, lds_b, acc);
+      if (kt + 1 < nk) store_b(r1, lds_b + Cfg::B_STAGE);
+      if (kt + 2 < nk) wait_vmcnt<Cfg::VM_PER_STEP>(); else wait_vmcnt<0>();
+      __syncthreads();
+      const int sa1 = sa == 2 ? 0 : sa + 1;   // (kt + 1) % 3
+      if (kt + 3 < nk) {
+        issue_a(sa, (kt + 3) * Cfg::BK);       // (kt + 3) % 3 == kt % 3
+        load_b<false>(r1, ba, B, ldb, K, (kt + 3) * Cfg::BK);
+      }
+      compute(lds_a + sa1 * Cfg::A_STAGE, lds_b + Cfg::B_STAGE, acc);
+      if (kt + 2 < nk) store_b(r0, lds_b);
+      if (kt + 3 < nk) wait_vmcnt<Cfg::VM_PER_STEP>(); else wait_vmcnt<0>();
+      __syncthreads();
+      sa = sa2;                                 // (kt + 2) % 3
+    }
+  }
+
+  // Fallback path (any K multiple of 8): A and B staged through registers,
+  // one step of prefetch, two LDS stages.  LDS layout: [A0 B0 A1 B1].
+  template <class ARows>
+  __device__ __forceinline__ static void run_regs(const ARows& ar, const uint16_t* __restrict__ B,
+                                                  int64_t ldb, int col0, int N, int K, char* lds,
+                                                  Acc& acc) {
+    const int tid = threadIdx.x;
+    zero(acc);
+    constexpr int STAGE = Cfg::A_STAGE + Cfg::B_STAGE;
     u32x4_t ra[Cfg::A_PT];
-    u32x4_t rb[Cfg::B_PT][8];
-
+    BRegs rb;
+    BAddr ba;
+    b_addr(ba, ldb, col0, N);
+    const int a_c = tid & 7;
     auto load = [&](int k0) {
+      const int kc = k0 + a_c * 8;
 #pragma unroll
       for (int i = 0; i < Cfg::A_PT; ++i) {
-        const int kc = k0 + a_c[i] * 8;
-        if (a_off[i] >= 0 && kc < K)
-          ra[i] = *(const u32x4_t*)(ar.base + a_off[i] + kc);
+        const int q = tid + i * Cfg::NT;
+        const int64_t off = (q < Cfg::A_CH) ? ar.row(q >> 3) : (int64_t)-1;
+        if (off >= 0 && kc < K)
+          ra[i] = *(const u32x4_t*)(ar.base + off + kc);
         else
           ra[i] = u32x4_t{0u, 0u, 0u, 0u};
       }
-#pragma unroll
-      for (int i = 0; i < Cfg::B_PT; ++i) {
-        const int kr = k0 + b_kb[i] * 8;
-        const uint16_t* p = B + (int64_t)kr * ldb + col0 + b_n[i];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          if (b_ok[i] && kr + j < K)
-            rb[i][j] = *(const u32x4_t*)(p + (int64_t)j * ldb);
-          else
-            rb[i][j] = u32x4_t{0u, 0u, 0u, 0u};
-        }
-      }
+      load_b<true>(rb, ba, B, ldb, K, k0);
     };
-
     auto store = [&](int stage) {
-      char* la = lds + stage * Cfg::STAGE;
-      char* lb = la + Cfg::A_STAGE;
+      char* la = lds + stage * STAGE;
 #pragma unroll
       for (int i = 0; i < Cfg::A_PT; ++i) {
         const int q = tid + i * Cfg::NT;
         if (q < Cfg::A_CH) *(u32x4_t*)(la + lds_swz(q >> 3, q & 7)) = ra[i];
       }
-#pragma unroll
-      for (int i = 0; i < Cfg::B_PT; ++i) {
-        const int q = tid + i * Cfg::NT;
-        if (q < Cfg::B_BL) {
-#pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            // columns n = 2m (low halves) and 2m + 1 (high halves)
-            u32x4_t lo, hi;
-            lo[0] = pack_lo16(rb[i][0][m], rb[i][1][m]);
-            lo[1] = pack_lo16(rb[i][2][m], rb[i][3][m]);
-            lo[2] = pack_lo16(rb[i][4][m], rb[i][5][m]);
-            lo[3] = pack_lo16(rb[i][6][m], rb[i][7][m]);
-            hi[0] = pack_hi16(rb[i][0][m], rb[i][1][m]);
-            hi[1] = pack_hi16(rb[i][2][m], rb[i][3][m]);
-            hi[2] = pack_hi16(rb[i][4][m], rb[i][5][m]);
-            hi[3] = pack_hi16(rb[i][6][m], rb[i][7][m]);
-            *(u32x4_t*)(lb + lds_swz(b_n[i] + 2 * m, b_kb[i])) = lo;
-            *(u32x4_t*)(lb + lds_swz(b_n[i] + 2 * m + 1, b_kb[i])) = hi;
-          }
-        }
-      }
+      store_b(rb, la + Cfg::A_STAGE);
     };
-
-    auto compute = [&](int stage) {
-      const char* la = lds + stage * Cfg::STAGE;
-      const char* lb = la + Cfg::A_STAGE;
-      const int l32 = lane & 31;
-      const int hi = lane >> 5;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        bf16x8_t af[Cfg::FM], bfr[Cfg::FN];
-#pragma unroll
-        for (int i = 0; i < Cfg::FM; ++i)
-          af[i] = *(const bf16x8_t*)(la + lds_swz(wm0 + i * 32 + l32, 2 * ks + hi));
-#pragma unroll
-        for (int j = 0; j < Cfg::FN; ++j)
-          bfr[j] = *(const bf16x8_t*)(lb + lds_swz(wn0 + j * 32 + l32, 2 * ks + hi));
-#pragma unroll
-        for (int i = 0; i < Cfg::FM; ++i)
-#pragma unroll
-          for (int j = 0; j < Cfg::FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-      }
-    };
-
     const int nk = (K + Cfg::BK - 1) / Cfg::BK;
     load(0);
     store(0);
@@ -218,7 +362,7 @@ struct GemmTile {
     for (int kt = 0; kt < nk; ++kt) {
       const int cur = kt & 1;
       if (kt + 1 < nk) load((kt + 1) * Cfg::BK);
-      compute(cur);
+      compute(lds + cur * STAGE, lds + cur * STAGE + Cfg::A_STAGE, acc);
       if (kt + 1 < nk) store(cur ^ 1);
       __syncthreads();
     }

@@ -19,6 +19,7 @@ struct tsg_ctx {
   uint32_t epoch = 0;
 
   uint64_t* d_sig = nullptr;   // signal words
+  uint32_t* d_cnt = nullptr;   // arrival counters, one per signal word (zero between calls)
   size_t n_sig = 0;
   uint32_t* d_status = nullptr;  // sticky device error bits
   uint32_t* d_queue = nullptr;   // work-queue tickets of persistent kernels
