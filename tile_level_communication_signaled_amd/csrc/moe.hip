@@ -1,0 +1,512 @@
+// MoE expert compute with the gate-weighted combine overlapped through
+// tile-level signals.
+//
+// Digest page "Resource-aware Computation-Communication Overlap for
+// multi-GPU ML Workloads", abstract on MoE expert compute overlapped with the
+// return all-to-all: a persistent per-rank producer covers all local experts
+// and emits output tiles with ready signals; a persistent consumer on a small
+// CU partition moves them back towards token order as they become ready.
+// "TileLink: Generating Efficient Compute-Communication Overlapping Kernels
+// using Tile-Centric Primitives", section 4.1 (dynamic mapping: lookup tables
+// filled at run time by the routing) and section 7.2 (GroupGEMM + Scatter +
+// Topk-Reduce).
+//
+// Kernels (one call):
+//   1. moe_route_kernel (one workgroup): expert_counts, a stable counting sort
+//      of the pairs p = t*k + s by expert (sorted_ids, order (expert, t, s)),
+//      and the lookup tables of the padded layout: every expert's rows are
+//      padded to a multiple of BM = 128, row block rb belongs to one expert,
+//      row_pair[row] = pair id or -1, row_token[row] = token or -1,
+//      pair_row[p] = padded row of pair p.
+//   2. moe_producer_kernel (persistent, atomic work queue): first every "up"
+//      tile (row block rb, 128 columns of I): gather x rows through row_token,
+//      multiply by w_up[e], h = bf16(SiLU(u)); each arrives on the signal of
+//      its row block.  Then every "down" tile (rb, 256 columns of H): acquire
+//      the row block's signal (all up tiles of rb done), y = h w_down[e] in
+//      fp32 into the staging buffer, release the tile's ready signal.
+//   3. moe_combine_kernel (persistent, consumer partition): walks the down
+//      tiles in queue order, acquires each ready signal, and for every token
+//      whose other routed row lies in an earlier tile (acquiring that tile's
+//      signal too) writes out[t] = fl(fl(g0 y0) + fl(g1 y1)) in slot order.
+//      Every token is written exactly once, by the later of its two tiles:
+//      no atomics and no zero-fill of out.
+#include "tsg_gemm.hpp"
+#include "tsg_internal.hpp"
+
+using namespace tsg;
+
+namespace {
+
+constexpr int BM = 128;                 // row padding unit and tile rows
+constexpr int BN_UP = 128;
+constexpr int BN_DN = 256;
+constexpr int kRouteThreads = 256;
+constexpr int kMaxExperts = 256;
+constexpr size_t kSigH = size_t(1) << 19;          // h row-block signals
+constexpr size_t kSigReady = kSigH + 65536;         // ready signals of down tiles
+constexpr size_t kSigEnd = kSigReady + 262144;
+
+using CfgUp = TileCfg<BM, BN_UP, 2, 2>;
+using CfgDn = TileCfg<BM, BN_DN, 2, 2>;
+
+// Workspace layout (byte offsets, 256-aligned).
+struct Layout {
+  size_t meta, offs, poffs, rb_expert, row_pair, row_token, pair_row, h, y, total;
+  int64_t n_rb_max, rows_max;
+};
+
+inline size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
+
+Layout layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k) {
+  Layout L;
+  const int64_t pairs = T * k;
+  L.n_rb_max = (pairs + E * (BM - 1) + BM - 1) / BM;
+  L.rows_max = L.n_rb_max * BM;
+  size_t o = 0;
+  L.meta = o;      o += up256(64 * 4);
+  L.offs = o;      o += up256((E + 1) * 4);
+  L.poffs = o;     o += up256((E + 1) * 4);
+  L.rb_expert = o; o += up256(L.n_rb_max * 4);
+  L.row_pair = o;  o += up256(L.rows_max * 4);
+  L.row_token = o; o += up256(L.rows_max * 4);
+  L.pair_row = o;  o += up256(pairs * 4);
+  L.h = o;         o += up256(L.rows_max * I * 2);
+  L.y = o;         o += up256(L.rows_max * H * 4);
+  L.total = o;
+  return L;
+}
+
+struct Ws {
+  int* meta;        // [0] = number of row blocks in use, [1] = valid pairs
+  int* offs;
+  int* poffs;
+  int* rb_expert;
+  int* row_pair;
+  int* row_token;
+  int* pair_row;
+  uint16_t* h;
+  float* y;
+};
+
+Ws bind(char* base, const Layout& L) {
+  Ws w;
+  w.meta = (int*)(base + L.meta);
+  w.offs = (int*)(base + L.offs);
+  w.poffs = (int*)(base + L.poffs);
+  w.rb_expert = (int*)(base + L.rb_expert);
+  w.row_pair = (int*)(base + L.row_pair);
+  w.row_token = (int*)(base + L.row_token);
+  w.pair_row = (int*)(base + L.pair_row);
+  w.h = (uint16_t*)(base + L.h);
+  w.y = (float*)(base + L.y);
+  return w;
+}
+
+// ------------------------------------------------------------------ route
+// One workgroup.  Thread j owns the contiguous pair block
+// [j*PB, (j+1)*PB); per-thread, per-expert counts live in LDS (uint16).
+// Stable: the position of pair p is offs[e] + (pairs of e in earlier blocks)
+// + (pairs of e earlier in p's own block).
+struct RouteArgs {
+  const int32_t* ids;
+  int32_t* counts;
+  int32_t* sorted_ids;
+  Ws ws;
+  uint32_t* status;
+  int T, E, k;
+  int64_t rows_max, n_rb_max;
+};
+
+__global__ void __launch_bounds__(kRouteThreads) moe_route_kernel(const RouteArgs a) {
+  __shared__ uint16_t cnt[kMaxExperts][kRouteThreads];
+  __shared__ int s_offs[kMaxExperts + 1], s_poffs[kMaxExperts + 1];
+  __shared__ int s_bad;
+  const int j = threadIdx.x;
+  const int P = a.T * a.k, E = a.E;
+  const int PB = (P + kRouteThreads - 1) / kRouteThreads;
+  const int p0 = min(P, j * PB), p1 = min(P, p0 + PB);
+  for (int e = 0; e < E; ++e) cnt[e][j] = 0;
+  if (j == 0) s_bad = 0;
+  __syncthreads();
+  int bad = 0;
+  for (int p = p0; p < p1; ++p) {
+    const int e = a.ids[p];
+    if (e >= 0 && e < E) cnt[e][j]++;
+    else bad = 1;
+  }
+  if (bad) atomicOr(&s_bad, 1);
+  __syncthreads();
+  // exclusive scan over threads, one expert per thread (E <= 256 threads)
+  for (int e = j; e < E; e += kRouteThreads) {
+    int run = 0;
+    for (int i = 0; i < kRouteThreads; ++i) {
+      const int c = cnt[e][i];
+      cnt[e][i] = (uint16_t)run;
+      run += c;
+    }
+    s_offs[e + 1] = run;  // count of expert e, scanned below
+  }
+  __syncthreads();
+  if (j == 0) {
+    int o = 0, po = 0;
+    for (int e = 0; e < E; ++e) {
+      const int c = s_offs[e + 1];
+      a.counts[e] = c;
+      s_offs[e] = o;
+      s_poffs[e] = po;
+      o += c;
+      po += (c + BM - 1) / BM * BM;
+    }
+    s_offs[E] = o;
+    s_poffs[E] = po;
+    a.ws.meta[0] = po / BM;
+    a.ws.meta[1] = o;
+    for (int e = 0; e <= E; ++e) {
+      a.ws.offs[e] = s_offs[e];
+      a.ws.poffs[e] = s_poffs[e];
+    }
+    if (s_bad) __hip_atomic_fetch_or(a.status, ERR_BAD_EXPERT, __ATOMIC_RELAXED, TSG_SIG_SCOPE);
+  }
+  __syncthreads();
+  // row tables default to "no pair"; pairs dropped for a bad id keep -1
+  for (int64_t r = j; r < a.rows_max; r += kRouteThreads) {
+    a.ws.row_pair[r] = -1;
+    a.ws.row_token[r] = -1;
+  }
+  for (int p = j; p < P; p += kRouteThreads) {
+    a.sorted_ids[p] = -1;
+    a.ws.pair_row[p] = -1;
+  }
+  for (int64_t rb = j; rb < a.n_rb_max; rb += kRouteThreads) a.ws.rb_expert[rb] = -1;
+  __syncthreads();
+  for (int e = 0; e < E; ++e)
+    for (int rb = s_poffs[e] / BM + j; rb < s_poffs[e + 1] / BM; rb += kRouteThreads) a.ws.rb_expert[rb] = e;
+  for (int p = p0; p < p1; ++p) {
+    const int e = a.ids[p];
+    if (e < 0 || e >= E) continue;
+    const int rank = cnt[e][j]++;
+    const int pos = s_offs[e] + rank;
+    const int row = s_poffs[e] + rank;
+    a.sorted_ids[pos] = p;
+    a.ws.pair_row[p] = row;
+    a.ws.row_pair[row] = p;
+    a.ws.row_token[row] = p / a.k;
+  }
+}
+
+// --------------------------------------------------------------- producer
+struct ProdArgs {
+  const uint16_t* x;
+  const uint16_t* w_up;
+  const uint16_t* w_down;
+  Ws ws;
+  uint64_t* sig_h;
+  uint32_t* cnt_h;
+  uint64_t* sig_ready;
+  uint32_t* queue;
+  uint32_t queue_base;
+  SyncArgs sa;
+  Timeline tl;
+  int T, H, I;
+  int n_up_nt, n_dn_nt;
+  int n_rb_max;
+  int n_items;
+  uint32_t skip_mask;     // row blocks (mod 32) whose up tiles never arrive (test hook)
+};
+
+template <bool DIRECT_UP, bool DIRECT_DN>
+__global__ void __launch_bounds__(256) moe_producer_kernel(const ProdArgs a) {
+  constexpr int LUP = DIRECT_UP ? CfgUp::LDS_DIRECT : CfgUp::LDS_REGS;
+  constexpr int LDN = DIRECT_DN ? CfgDn::LDS_DIRECT : CfgDn::LDS_REGS;
+  __shared__ __attribute__((aligned(16))) char lds[LUP > LDN ? LUP : LDN];
+  __shared__ int s_item;
+  // Every value that steers a loop or branch around a barrier is made
+  // wave-uniform (readfirstlane): values read from memory are otherwise
+  // treated as divergent, and a divergent loop around barriers is
+  // restructured by the compiler into a form whose `continue` edge skipped
+  // the fetch of the next item (an endless loop).
+  const int n_rb = __builtin_amdgcn_readfirstlane(a.ws.meta[0]);
+  const int n_up = a.n_rb_max * a.n_up_nt;
+  // Next queue item, identical in every thread.  The loop below has a single
+  // back edge that always passes through this fetch (no `continue`).
+  auto fetch = [&]() -> int {
+    if (threadIdx.x == 0) s_item = (int)(atomicAdd(a.queue, 1u) - a.queue_base);
+    __syncthreads();
+    const int v = __builtin_amdgcn_readfirstlane(s_item);
+    __syncthreads();
+    return v;
+  };
+  for (int item = fetch(); item < a.n_items; item = fetch()) {
+    const uint64_t t0 = a.tl.buf ? wall_clock64() : 0;
+    const bool up = item < n_up;
+    const int rb = up ? item / a.n_up_nt : (item - n_up) / a.n_dn_nt;
+    const int nt = up ? item % a.n_up_nt : (item - n_up) % a.n_dn_nt;
+    if (rb < n_rb && up) {
+      const int e = __builtin_amdgcn_readfirstlane(a.ws.rb_expert[rb]);
+      const int col0 = nt * BN_UP;
+      typename GemmTile<CfgUp>::Acc acc;
+      const ARowsGather ar{a.x, a.H, a.ws.row_token + (int64_t)rb * BM};
+      const uint16_t* B = a.w_up + (int64_t)e * a.H * a.I;
+      if (DIRECT_UP)
+        GemmTile<CfgUp>::run_direct(ar, B, a.I, col0, a.I, a.H, lds, acc);
+      else
+        GemmTile<CfgUp>::run_regs(ar, B, a.I, col0, a.I, a.H, lds, acc);
+      const int I = a.I;
+      uint16_t* hrow = a.ws.h + (int64_t)rb * BM * I;
+      GemmTile<CfgUp>::for_each(acc, [&](int r, int c, float u) {
+        const int gc = col0 + c;
+        if (gc < I) hrow[(int64_t)r * I + gc] = (uint16_t)f32_to_bf16(u / (1.0f + expf(-u)));
+      });
+      block_release_fence();
+      if (threadIdx.x == 0) {
+        if (!((a.skip_mask >> (rb & 31)) & 1u))
+          sig_arrive_counted_lane(a.cnt_h + rb, a.sig_h + rb, (uint32_t)a.n_up_nt, a.sa.epoch);
+        if (a.tl.buf) timeline_put(a.tl, 7, (uint32_t)(rb << 16 | nt), t0, t0, wall_clock64());
+      }
+    } else if (rb < n_rb) {
+      const int e = __builtin_amdgcn_readfirstlane(a.ws.rb_expert[rb]);
+      const int col0 = nt * BN_DN;
+      block_wait_ge(a.sig_h + rb, sig_target(a.sa.epoch, (uint32_t)a.n_up_nt), a.sa);
+      const uint64_t t1 = a.tl.buf ? wall_clock64() : 0;
+      typename GemmTile<CfgDn>::Acc acc;
+      const ARowsLinear ar{a.ws.h, a.I, rb * BM, a.n_rb_max * BM};
+      const uint16_t* B = a.w_down + (int64_t)e * a.I * a.H;
+      if (DIRECT_DN)
+        GemmTile<CfgDn>::run_direct(ar, B, a.H, col0, a.H, a.I, lds, acc);
+      else
+        GemmTile<CfgDn>::run_regs(ar, B, a.H, col0, a.H, a.I, lds, acc);
+      // rows past the expert's last pair are padding: not stored
+      const int valid = __builtin_amdgcn_readfirstlane(
+          min(BM, a.ws.offs[e + 1] - a.ws.offs[e] - (rb * BM - a.ws.poffs[e])));
+      const int H = a.H;
+      float* yrow = a.ws.y + (int64_t)rb * BM * H;
+      GemmTile<CfgDn>::for_each(acc, [&](int r, int c, float v) {
+        const int gc = col0 + c;
+        if (r < valid && gc < H) yrow[(int64_t)r * H + gc] = v;
+      });
+      block_release_fence();
+      if (threadIdx.x == 0) {
+        sig_publish_lane(a.sig_ready + (int64_t)rb * a.n_dn_nt + nt, a.sa.epoch, 1);
+        if (a.tl.buf) timeline_put(a.tl, 8, (uint32_t)(rb << 16 | nt), t0, t1, wall_clock64());
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- combine
+struct CombArgs {
+  const float* topk_w;
+  float* out;
+  Ws ws;
+  const uint64_t* sig_ready;
+  SyncArgs sa;
+  Timeline tl;
+  int H, k;
+  int n_dn_nt, n_rb_max;
+  int wait;
+};
+
+// Each wave takes 32 rows of the tile, 8 at a time: resolve the 8 rows'
+// pairs and partners, acquire the partners' tiles, issue all loads, then
+// combine and store (lane l owns float4 column l of the 256-column tile).
+__global__ void __launch_bounds__(256) moe_combine_kernel(const CombArgs a) {
+  // uniform (see the producer): the unit loop contains a barrier
+  const int n_rb = __builtin_amdgcn_readfirstlane(a.ws.meta[0]);
+  const int n_units = a.n_rb_max * a.n_dn_nt;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int u = blockIdx.x; u < n_units; u += gridDim.x) {
+    const int rb = u / a.n_dn_nt, nt = u % a.n_dn_nt;
+    if (rb >= n_rb) break;                   // units are rb-major: the rest are empty too
+    const uint64_t t0 = a.tl.buf ? wall_clock64() : 0;
+    if (a.wait) block_wait_ge(a.sig_ready + (int64_t)rb * a.n_dn_nt + nt, sig_target(a.sa.epoch, 1), a.sa);
+    const uint64_t t1 = a.tl.buf ? wall_clock64() : 0;
+    const int col = nt * BN_DN + lane * 4;
+    const bool col_ok = col < a.H;
+    for (int g = 0; g < 4; ++g) {
+      const int r0 = rb * BM + wave * 32 + g * 8;
+      int tok[8], own[8], oth[8];
+      bool act[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int p = __builtin_amdgcn_readfirstlane(a.ws.row_pair[r0 + j]);
+        act[j] = false;
+        tok[j] = -1;
+        if (p < 0) continue;
+        const int q = p ^ 1;                 // the token's other slot (k == 2)
+        const int pr = __builtin_amdgcn_readfirstlane(a.ws.pair_row[q]);
+        const int prb = pr >= 0 ? pr / BM : -1;
+        if (prb > rb) continue;              // the later tile combines this token
+        if (prb >= 0 && a.wait)
+          wave_wait_ge(a.sig_ready + (int64_t)prb * a.n_dn_nt + nt, sig_target(a.sa.epoch, 1), a.sa);
+        act[j] = true;
+        tok[j] = p / a.k;
+        // own = row of slot 0, oth = row of slot 1 (-1: that slot was dropped)
+        own[j] = (p & 1) ? pr : r0 + j;
+        oth[j] = (p & 1) ? r0 + j : pr;
+      }
+      float4 v0[8], v1[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        v0[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+        v1[j] = v0[j];
+        if (act[j] && col_ok) {
+          if (own[j] >= 0) v0[j] = *(const float4*)(a.ws.y + (int64_t)own[j] * a.H + col);
+          if (oth[j] >= 0) v1[j] = *(const float4*)(a.ws.y + (int64_t)oth[j] * a.H + col);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (act[j] && col_ok) {
+          const float g0 = a.topk_w[(int64_t)tok[j] * a.k], g1 = a.topk_w[(int64_t)tok[j] * a.k + 1];
+          float4 o;
+          o.x = __fadd_rn(__fmul_rn(g0, v0[j].x), __fmul_rn(g1, v1[j].x));
+          o.y = __fadd_rn(__fmul_rn(g0, v0[j].y), __fmul_rn(g1, v1[j].y));
+          o.z = __fadd_rn(__fmul_rn(g0, v0[j].z), __fmul_rn(g1, v1[j].z));
+          o.w = __fadd_rn(__fmul_rn(g0, v0[j].w), __fmul_rn(g1, v1[j].w));
+          *(float4*)(a.out + (int64_t)tok[j] * a.H + col) = o;
+        }
+      }
+    }
+    if (a.tl.buf && threadIdx.x == 0) timeline_put(a.tl, 9, (uint32_t)(rb << 16 | nt), t0, t1, wall_clock64());
+  }
+}
+
+template <bool U, bool D>
+void launch_prod(const ProdArgs& a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((moe_producer_kernel<U, D>), dim3(grid), dim3(256), 0, s, a);
+}
+
+}  // namespace
+
+size_t tsg_moe_workspace(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k) {
+  if (T < 1 || H < 8 || I < 8 || E < 1 || E > kMaxExperts || k != 2) return 0;
+  return layout(T, H, I, E, k).total;
+}
+
+tsg_status tsg_op_moe(tsg_ctx* ctx, const void* x, const int32_t* topk_ids, const float* topk_w,
+                      const void* w_up, const void* w_down, float* out, int32_t* expert_counts,
+                      int32_t* sorted_ids, void* workspace, size_t workspace_bytes, int T, int H,
+                      int I, int E, int k, const tsg_opts* opts, int mode, void* stream) {
+  using namespace tsgh;
+  if (!x || !topk_ids || !topk_w || !w_up || !w_down || !out || !expert_counts || !sorted_ids)
+    return fail(ctx, TSG_E_INVALID, "moe_expert_combine: null pointer");
+  if (mode < TSG_MODE_OVERLAP || mode > TSG_MODE_COMM_ONLY) return fail(ctx, TSG_E_INVALID, "bad mode");
+  if (k != 2) return fail(ctx, TSG_E_UNSUPPORTED, "moe_expert_combine supports k == 2 only");
+  if (T < 1 || E < 1 || E > kMaxExperts || H < 8 || I < 8 || H % 8 || I % 8)
+    return fail(ctx, TSG_E_SHAPE, "moe_expert_combine: bad shape T=%d H=%d I=%d E=%d", T, H, I, E);
+  if ((int64_t)T * k > 65535 * kRouteThreads)
+    return fail(ctx, TSG_E_UNSUPPORTED, "too many routed pairs");
+  if (!aligned16(x) || !aligned16(w_up) || !aligned16(w_down) || !aligned16(out) || !aligned16(workspace))
+    return fail(ctx, TSG_E_ALIGN, "moe_expert_combine: pointers must be 16-byte aligned");
+  const Layout L = layout(T, H, I, E, k);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(ctx, TSG_E_WORKSPACE, "workspace of %zu bytes needed", L.total);
+  if ((int64_t)T * H * 2 >= (int64_t(1) << 32) || (int64_t)H * I * 2 >= (int64_t(1) << 32) ||
+      L.rows_max * I * 2 >= (int64_t(1) << 32))
+    return fail(ctx, TSG_E_UNSUPPORTED, "operands of 4 GiB or more are not supported");
+  const int n_up_nt = (I + BN_UP - 1) / BN_UP, n_dn_nt = (H + BN_DN - 1) / BN_DN;
+  if ((size_t)L.n_rb_max > kSigReady - kSigH || (size_t)L.n_rb_max * n_dn_nt > kSigEnd - kSigReady ||
+      kSigEnd > ctx->n_sig)
+    return fail(ctx, TSG_E_UNSUPPORTED, "too many tiles for the signal pool");
+
+  const Opts o = resolve(opts, 16);
+  TSG_HIP(ctx, hipSetDevice(ctx->device));
+  hipStream_t caller = (hipStream_t)stream;
+  ++ctx->epoch;
+  time_reset(ctx);
+  const Ws ws = bind((char*)workspace, L);
+  const SyncArgs sa = sync_args(ctx, o);
+  const Timeline tl = timeline(ctx, o);
+  if (o.timeline) TSG_HIP(ctx, hipMemsetAsync(ctx->d_timeline_n, 0, sizeof(uint32_t), caller));
+
+  RouteArgs ra;
+  ra.ids = topk_ids;
+  ra.counts = expert_counts;
+  ra.sorted_ids = sorted_ids;
+  ra.ws = ws;
+  ra.status = ctx->d_status;
+  ra.T = T;
+  ra.E = E;
+  ra.k = k;
+  ra.rows_max = L.rows_max;
+  ra.n_rb_max = L.n_rb_max;
+
+  ProdArgs pa;
+  pa.x = (const uint16_t*)x;
+  pa.w_up = (const uint16_t*)w_up;
+  pa.w_down = (const uint16_t*)w_down;
+  pa.ws = ws;
+  pa.sig_h = ctx->d_sig + kSigH;
+  pa.cnt_h = ctx->d_cnt + kSigH;
+  pa.sig_ready = ctx->d_sig + kSigReady;
+  pa.queue = ctx->d_queue;
+  pa.sa = sa;
+  pa.tl = tl;
+  pa.T = T;
+  pa.H = H;
+  pa.I = I;
+  pa.n_up_nt = n_up_nt;
+  pa.n_dn_nt = n_dn_nt;
+  pa.n_rb_max = (int)L.n_rb_max;
+  pa.n_items = (int)(L.n_rb_max * (n_up_nt + n_dn_nt));
+  pa.skip_mask = o.skip_mask;
+
+  CombArgs ca;
+  ca.topk_w = topk_w;
+  ca.out = out;
+  ca.ws = ws;
+  ca.sig_ready = pa.sig_ready;
+  ca.sa = sa;
+  ca.tl = tl;
+  ca.H = H;
+  ca.k = k;
+  ca.n_dn_nt = n_dn_nt;
+  ca.n_rb_max = (int)L.n_rb_max;
+
+  auto route = [&]() -> tsg_status {
+    hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(kRouteThreads), 0, caller, ra);
+    return check_launch(ctx, "moe_route_kernel");
+  };
+  auto produce = [&](hipStream_t s, int nwg) -> tsg_status {
+    // every producer workgroup ends with one failing ticket: the queue moves
+    // by n_items + nwg per call, tracked here so no reset pass is needed
+    pa.queue_base = (uint32_t)ctx->queue_base[0];
+    ctx->queue_base[0] += (uint64_t)pa.n_items + (uint64_t)nwg;
+    const bool du = H % (2 * CfgUp::BK) == 0, dd = I % (2 * CfgDn::BK) == 0;
+    time_begin(ctx, 0, s);
+    if (du && dd) launch_prod<true, true>(pa, nwg, s);
+    else if (du) launch_prod<true, false>(pa, nwg, s);
+    else if (dd) launch_prod<false, true>(pa, nwg, s);
+    else launch_prod<false, false>(pa, nwg, s);
+    time_end(ctx, 0, s);
+    return check_launch(ctx, "moe_producer_kernel");
+  };
+  auto combine = [&](hipStream_t s, int nwg, int wait) -> tsg_status {
+    ca.wait = wait;
+    time_begin(ctx, 1, s);
+    hipLaunchKernelGGL(moe_combine_kernel, dim3(nwg), dim3(256), 0, s, ca);
+    time_end(ctx, 1, s);
+    return check_launch(ctx, "moe_combine_kernel");
+  };
+
+  tsg_status st = TSG_OK;
+  if (mode != TSG_MODE_COMM_ONLY) st = route();
+  if (st != TSG_OK) return st;
+  if (mode == TSG_MODE_SERIAL || mode == TSG_MODE_COMPUTE_ONLY) {
+    st = produce(caller, ctx->n_cus);
+    if (st == TSG_OK && mode == TSG_MODE_SERIAL) st = combine(caller, ctx->n_cus * 2, 1);
+    return st;
+  }
+  Pair pr;
+  st = streams(ctx, o, &pr);
+  if (st != TSG_OK) return st;
+  const int nwg_c = o.aux_cus < 0 ? 64 : pr.aux_cus * 2;
+  st = fork(ctx, caller, pr);
+  if (st != TSG_OK) return st;
+  // Producer first, consumer second: the producer's only waits are on its own
+  // earlier queue items, which are already running.
+  if (mode == TSG_MODE_OVERLAP) st = produce(pr.main, pr.main_cus);
+  if (st == TSG_OK) st = combine(pr.aux, nwg_c, mode == TSG_MODE_OVERLAP ? 1 : 0);
+  tsg_status sj = join(ctx, caller, pr);
+  return st != TSG_OK ? st : sj;
+}
