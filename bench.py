@@ -1,19 +1,27 @@
 #!/usr/bin/env python3
 """Benchmark of the tile-signaled GEMM paths on one MI355X.
 
-Default workload: AllGather + GEMM at one rank's TP=8 share of a Llama-style
-MLP up-projection (A 8192x4096 bf16 gathered from 8 row chunks of 1024, one
-local and seven written by the concurrent copy kernel; B 4096x1792 bf16;
-fp32 accumulate, bf16 out).  One step = one gemm_ag_overlap call in overlap
-mode with its inputs already resident in HBM.  The same kernels are also timed
-serialized (copy, then GEMM), GEMM-only and copy-only, for the speedup, the
-"within 10% of GEMM-only" ratio and the overlap ratio.
+Headline workload (the JSON line's `value`): AllGather + GEMM at one rank's
+TP=8 share of a Llama-style MLP up-projection -- A 8192x4096 bf16 gathered
+from 8 row chunks of 1024 (the local one and seven written by the concurrent
+copy kernel), B 4096x1792 bf16, fp32 accumulate, bf16 out.  One step = one
+gemm_ag_overlap call in overlap mode with every input already resident in
+HBM; K steps are timed with the wall clock between two device
+synchronisations.  The same kernels are also timed serialized (copy, then
+GEMM), GEMM-only and copy-only, giving the speedup over serial, the ratio to
+GEMM-only and the overlap ratio (comp + comm - overlap) / comm.
 
-Prints one JSON line (see --help for options).  Only one GPU is supported.
+`paths` reports the same four modes for every path at its full-size
+workload: AG+GEMM, GEMM+RS (8192x1792 @ 1792x4096, 7 fp32 peer partials),
+the CTA-pipelined MLP (2048x8192 @ 8192x4096, GELU, @ 4096x8192) and MoE
+(4096 tokens, hidden 4096, 8 experts of 4096x1408 / 1408x4096, top-2 Zipf).
+
+Prints one JSON line.  Only one GPU is supported.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -25,6 +33,8 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "overlapped TFLOP/s, % bf16 MFMA peak, speedup vs serialized copy+GEMM"
+CSRC = os.path.join(ROOT, "tile_level_communication_signaled_amd", "csrc")
+TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def _parse():
@@ -32,12 +42,83 @@ def _parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="llama_ag", choices=["llama_ag"])
-    p.add_argument("--aux-cus", type=int, default=0, help="copy-kernel CUs (0 = default, -1 = shared)")
+    p.add_argument("--aux-cus", type=int, default=0, help="copy-kernel CUs of the headline (0 = default, -1 = shared)")
     p.add_argument("--tile", type=int, default=0)
+    p.add_argument("--paths", default="all", choices=["all", "ag"], help="also time the other three paths")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    p.add_argument("--sweep", action="store_true", help="also print per-configuration timings to stderr")
+    p.add_argument("--headline-only", action="store_true",
+                   help="time only the headline overlap steps (for kernel traces)")
+    p.add_argument("--counters", action="store_true",
+                   help="counter-collection run: the profiler serialises kernels, so the GEMM runs in "
+                        "compute-only mode and the copy in comm-only mode (K steps each), then one plain "
+                        "1 GiB device copy of known size calibrates the byte counters; prints nothing")
+    p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="no GPU: turn the counter_collection.csv files of two rocprofv3 --pmc runs of "
+                        "--counters (FETCH_SIZE, then WRITE_SIZE) into the traffic record and exit")
     return p.parse_args()
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel: str):
+    """HBM bytes per launch of `kernel` measured with rocprofv3 counters, or
+    None when the record is missing or older than the current sources."""
+    try:
+        rec = json.load(open(TRAFFIC))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != source_hash():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else int(k["bytes_per_launch"])
+
+
+CALIB_BYTES = 1 << 30   # the plain device copy that --counters runs: 1 GiB read, 1 GiB written
+
+
+def summarize_counters(fetch_csv: str, write_csv: str, out_path: str = TRAFFIC) -> dict:
+    """Per-launch HBM bytes of the AG kernels from two rocprofv3 --pmc runs.
+
+    FETCH_SIZE and WRITE_SIZE are read in KiB per dispatch and averaged per
+    kernel.  Each counter is scaled by the factor that makes it read exactly
+    1 GiB on the plain 1 GiB device copy (the largest __amd_rocclr_copyBuffer
+    dispatch) of the same run."""
+    import csv
+
+    def per_kernel(path, counter):
+        acc = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return acc
+
+    rec = {"source_hash": source_hash(), "calibration_bytes": CALIB_BYTES, "kernels": {}}
+    totals = {}
+    for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        acc = per_kernel(path, name)
+        calib = max(v for k, vs in acc.items() if k.startswith("__amd_rocclr_copyBuffer") for v in vs)
+        scale = CALIB_BYTES / (calib * 1024.0)
+        rec[name + "_scale"] = round(scale, 5)
+        for short in ("ag_gemm_kernel", "ag_copy_kernel"):
+            vs = [v for k, lst in acc.items() if short in k for v in lst]
+            if vs:
+                totals.setdefault(short, {})[name] = sum(vs) / len(vs) * 1024.0 * scale
+                totals[short]["launches_" + name] = len(vs)
+    for short, t in totals.items():
+        rec["kernels"][short] = {"fetch_bytes": int(t["FETCH_SIZE"]), "write_bytes": int(t["WRITE_SIZE"]),
+                                 "bytes_per_launch": int(t["FETCH_SIZE"] + t["WRITE_SIZE"]),
+                                 "launches": t["launches_FETCH_SIZE"]}
+    with open(out_path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    return rec
 
 
 def _cpu_baseline(inp, M, N, K, R):
@@ -58,13 +139,93 @@ def _cpu_baseline(inp, M, N, K, R):
         oracle.ag_gemm(loc, peers, inp["b"], R, 0)
         times.append(time.perf_counter() - t0)
     t = float(np.median(times))
-    return {"value": 2.0 * M * N * K / t / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"the full workload (AllGather + {M}x{N}x{K} GEMM, float64 numpy), "
-                      f"median of {len(times)} runs, {t:.2f} s each"}
+    return {"value": round(2.0 * M * N * K / t / 1e12, 4), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"the full workload (AllGather + {M}x{N}x{K} GEMM, float64 numpy on the host), "
+                      f"median of {len(times)} runs of {t:.2f} s"}
+
+
+class Timer:
+    """Times calls of one path in each mode: whole-call milliseconds from
+    events on the caller stream, plus the main/aux kernel durations that the
+    library measures with events on the kernels' own streams."""
+
+    def __init__(self, torch, tsg, ctx, fn):
+        self.torch, self.tsg, self.ctx, self.fn = torch, tsg, ctx, fn
+
+    def run(self, mode, n, warmup=2, kernels=()):
+        torch, tsg, ctx = self.torch, self.tsg, self.ctx
+        for i in range(warmup):
+            self.fn(i, mode)
+        if ctx.check() != tsg.OK:
+            raise RuntimeError(ctx.last_error())
+        ctx.enable_kernel_timing(bool(kernels))
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        kms = {k: [] for k in kernels}
+        for i in range(n):
+            ev[i][0].record()
+            self.fn(i, mode)
+            ev[i][1].record()
+            for k in kernels:
+                kms[k].append(ctx.kernel_ms(k))
+        torch.cuda.synchronize()
+        ctx.enable_kernel_timing(False)
+        if ctx.check() != tsg.OK:
+            raise RuntimeError(ctx.last_error())
+        ms = sorted(a.elapsed_time(b) for a, b in ev)
+        med = ms[len(ms) // 2]
+        return med, {k: sorted(v)[len(v) // 2] for k, v in kms.items()}
+
+
+def _summary(flops, hbm_bytes, t):
+    """t: dict mode -> median ms (None when the mode does not apply)."""
+    ov, se, co, cm = t["overlap"], t["serial"], t["compute_only"], t.get("comm_only")
+    out = {
+        "ms": {k: (None if v is None else round(v, 5)) for k, v in t.items()},
+        "tflops": round(flops / (ov * 1e-3) / 1e12, 2),
+        "pct_bf16_peak": round(100.0 * flops / (ov * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "hbm_GBps_algorithmic": round(hbm_bytes / (ov * 1e-3) / 1e9, 1),
+        "pct_hbm_peak": round(100.0 * hbm_bytes / (ov * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+        "speedup_vs_serial": round(se / ov, 4),
+        "overlap_vs_compute_only": round(ov / co, 4),
+        "flops": int(flops),
+        "hbm_bytes_algorithmic": int(hbm_bytes),
+    }
+    if cm:
+        out["overlap_ratio"] = round((co + cm - ov) / cm, 4)
+    return out
+
+
+def _path_ag(torch, tsg, ctx, cfg, n, opts, seed_sets=2):
+    import numpy as np
+    from synth import ag_inputs
+    from synth.gen import split_chunks
+    M, N, K, R = cfg["M"], cfg["N"], cfg["K"], cfg["R"]
+    sets, host = [], None
+    for s in range(seed_sets):
+        inp = ag_inputs(M, K, N, R, rank=0, seed=cfg["seed"] + 100 * s)
+        host = host or inp
+        loc, peers = split_chunks(inp["a"], R, 0)
+        sets.append({"loc": torch.from_numpy(loc.view(np.int16)).cuda(),
+                     "peers": torch.from_numpy(peers.view(np.int16)).cuda(),
+                     "b": torch.from_numpy(inp["b"].view(np.int16)).cuda(),
+                     "full": torch.empty((M, K), dtype=torch.int16, device="cuda"),
+                     "c": torch.empty((M, N), dtype=torch.int16, device="cuda")})
+
+    def fn(i, mode):
+        d = sets[i % len(sets)]
+        tsg.gemm_ag_overlap(ctx, d["loc"], d["peers"], d["full"], d["b"], d["c"], tsg.BF16, M, N, K, R, 0,
+                            opts=opts, mode=mode)
+    flops = 2.0 * M * N * K
+    gemm_bytes = M * K * 2 + K * N * 2 + M * N * 2
+    copy_bytes = 2 * M * K * 2
+    return fn, flops, gemm_bytes, copy_bytes, host
 
 
 def main():
     args = _parse()
+    if args.summarize_counters:
+        print(json.dumps(summarize_counters(*args.summarize_counters)))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this library has no multi-GPU path "
               "(peers are stood in for by buffers in local HBM).", file=sys.stderr)
@@ -73,86 +234,120 @@ def main():
     import numpy as np
     import torch
     import tile_level_communication_signaled_amd as tsg
-    from synth import CONFIGS, ag_inputs
-    from synth.gen import split_chunks
-
-    cfg = CONFIGS[args.workload]
-    M, N, K, R = cfg["M"], cfg["N"], cfg["K"], cfg["R"]
-    rank = 0
-    flops = 2.0 * M * N * K
-
-    # Two resident input sets, used alternately, so that back-to-back steps do
-    # not find their operands in the 256 MB Infinity Cache.
-    sets = []
-    host_inp = None
-    for s in range(2):
-        inp = ag_inputs(M, K, N, R, rank=rank, seed=cfg["seed"] + 100 * s)
-        if s == 0:
-            host_inp = inp
-        loc, peers = split_chunks(inp["a"], R, rank)
-        d = {
-            "loc": torch.from_numpy(loc.view(np.int16)).cuda(),
-            "peers": torch.from_numpy(peers.view(np.int16)).cuda(),
-            "b": torch.from_numpy(inp["b"].view(np.int16)).cuda(),
-            "full": torch.empty((M, K), dtype=torch.int16, device="cuda"),
-            "c": torch.empty((M, N), dtype=torch.int16, device="cuda"),
-        }
-        sets.append(d)
-    torch.cuda.synchronize()
+    from synth import CONFIGS, mlp2_inputs, moe_inputs, rs_inputs
 
     ctx = tsg.Context(0)
-    opts = tsg.Opts(aux_cus=args.aux_cus, tile=args.tile)
+    hopts = tsg.Opts(aux_cus=args.aux_cus, tile=args.tile)
+    cfg = CONFIGS["llama_ag"]
+    M, N, K, R = cfg["M"], cfg["N"], cfg["K"], cfg["R"]
+    ag_fn, ag_flops, ag_gemm_bytes, ag_copy_bytes, ag_host = _path_ag(torch, tsg, ctx, cfg, args.steps, hopts)
 
-    def call(i, mode):
-        d = sets[i % 2]
-        tsg.gemm_ag_overlap(ctx, d["loc"], d["peers"], d["full"], d["b"], d["c"], tsg.BF16, M, N, K, R, rank,
-                            opts=opts, mode=mode)
-
-    def timed(mode, steps, warmup, kernel=None):
-        for i in range(warmup):
-            call(i, mode)
+    if args.counters:
+        for i in range(args.steps):
+            ag_fn(i, tsg.COMPUTE_ONLY)
+        for i in range(args.steps):
+            ag_fn(i, tsg.COMM_ONLY)
+        torch.cuda.synchronize()
+        src = torch.empty(1 << 29, dtype=torch.int16, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
         if ctx.check() != tsg.OK:
             raise RuntimeError(ctx.last_error())
-        ctx.enable_kernel_timing(kernel is not None)
-        kms = []
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(steps):
-            call(i, mode)
-            if kernel is not None:
-                kms.append(ctx.kernel_ms(kernel))   # waits for this step's kernel event
-        torch.cuda.synchronize()
-        dt = (time.perf_counter() - t0) / steps
-        ctx.enable_kernel_timing(False)
-        st = ctx.check()
-        if st != tsg.OK:
-            raise RuntimeError(ctx.last_error())
-        return dt * 1e3, (float(np.mean(kms)) if kms else None)
+        ctx.close()
+        return
 
-    # Timed region of the headline number: K overlap steps, nothing else.
+    # ---- headline: K overlap steps between two synchronisations, nothing else
     for i in range(args.warmup):
-        call(i, tsg.OVERLAP)
+        ag_fn(i, tsg.OVERLAP)
     if ctx.check() != tsg.OK:
         raise RuntimeError(ctx.last_error())
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        call(i, tsg.OVERLAP)
+        ag_fn(i, tsg.OVERLAP)
     torch.cuda.synchronize()
-    ms_overlap = (time.perf_counter() - t0) / args.steps * 1e3
+    ms_step = (time.perf_counter() - t0) / args.steps * 1e3
     if ctx.check() != tsg.OK:
         raise RuntimeError(ctx.last_error())
 
-    # Reference modes and per-kernel durations (HIP events on the kernels' own streams).
-    _, gemm_ms_in_overlap = timed(tsg.OVERLAP, args.steps, 2, kernel=0)
-    ms_serial, _ = timed(tsg.SERIAL, args.steps, 2)
-    ms_compute, gemm_ms_alone = timed(tsg.COMPUTE_ONLY, args.steps, 2, kernel=0)
-    ms_comm, copy_ms = timed(tsg.COMM_ONLY, args.steps, 2, kernel=1)
+    if args.headline_only:
+        print(json.dumps({"metric": METRIC, "value": round(ag_flops / (ms_step * 1e-3) / 1e12, 2),
+                          "unit": "TFLOP/s", "ms_per_step": round(ms_step, 5), "steps": args.steps}), flush=True)
+        ctx.close()
+        return
 
-    tflops = flops / (ms_overlap * 1e-3) / 1e12
-    achieved = flops / (gemm_ms_in_overlap * 1e-3) / 1e12
-    copy_bytes = 2 * (M * K * 2)   # every chunk (local included) read once and written once
-    gemm_bytes = M * K * 2 + K * N * 2 + M * N * 2
+    timer = Timer(torch, tsg, ctx, ag_fn)
+    n = max(5, min(args.steps, 30))
+    t_ov, k_ov = timer.run(tsg.OVERLAP, n, kernels=(0, 1))
+    t_se, _ = timer.run(tsg.SERIAL, n)
+    t_co, k_co = timer.run(tsg.COMPUTE_ONLY, n, kernels=(0,))
+    t_cm, k_cm = timer.run(tsg.COMM_ONLY, n, kernels=(1,))
+    ag = _summary(ag_flops, ag_gemm_bytes + ag_copy_bytes,
+                  {"overlap": t_ov, "serial": t_se, "compute_only": t_co, "comm_only": t_cm})
+    ag["kernel_ms"] = {"gemm_in_overlap": round(k_ov[0], 5), "copy_in_overlap": round(k_ov[1], 5),
+                       "gemm_alone": round(k_co[0], 5), "copy_alone": round(k_cm[1], 5)}
+    paths = {"ag_gemm": ag}
+
+    if args.paths == "all":
+        c3 = CONFIGS["gemm_rs"]
+        inp = rs_inputs(c3["M"], c3["K"], c3["N"], c3["R"], rank=0, seed=c3["seed"])
+        x = torch.from_numpy(inp["x"].view(np.int16)).cuda()
+        w = torch.from_numpy(inp["w"].view(np.int16)).cuda()
+        pp = torch.from_numpy(inp["peer_partials"]).cuda()
+        P = torch.empty((c3["M"], c3["N"]), dtype=torch.float32, device="cuda")
+        o = torch.empty((c3["M"] // c3["R"], c3["N"]), dtype=torch.float32, device="cuda")
+        rs_fn = lambda i, mode: tsg.gemm_rs_overlap(ctx, x, w, P, pp, o, c3["M"], c3["N"], c3["K"], c3["R"], 0,
+                                                    mode=mode)
+        t = Timer(torch, tsg, ctx, rs_fn)
+        mr = c3["M"] // c3["R"]
+        rs_bytes = (c3["M"] * c3["K"] * 2 + c3["K"] * c3["N"] * 2 + c3["M"] * c3["N"] * 4
+                    + (c3["R"] - 1) * mr * c3["N"] * 4 + 2 * mr * c3["N"] * 4)
+        paths["gemm_rs"] = _summary(2.0 * c3["M"] * c3["N"] * c3["K"], rs_bytes,
+                                    {"overlap": t.run(tsg.OVERLAP, n)[0], "serial": t.run(tsg.SERIAL, n)[0],
+                                     "compute_only": t.run(tsg.COMPUTE_ONLY, n)[0],
+                                     "comm_only": t.run(tsg.COMM_ONLY, n)[0]})
+        del x, w, pp, P, o
+
+        c4 = CONFIGS["mlp2"]
+        inp = mlp2_inputs(c4["M"], c4["K1"], c4["N1"], c4["N2"], seed=c4["seed"])
+        dx, d1, d2 = (torch.from_numpy(inp[k].view(np.int16)).cuda() for k in ("x", "w1", "w2"))
+        h = torch.empty((c4["M"], c4["N1"]), dtype=torch.int16, device="cuda")
+        y = torch.empty((c4["M"], c4["N2"]), dtype=torch.float32, device="cuda")
+        mlp_fn = lambda i, mode: tsg.mlp2_pipelined(ctx, dx, d1, h, d2, y, c4["M"], c4["K1"], c4["N1"], c4["N2"],
+                                                    mode=mode)
+        t = Timer(torch, tsg, ctx, mlp_fn)
+        mlp_flops = 2.0 * c4["M"] * c4["N1"] * c4["K1"] + 2.0 * c4["M"] * c4["N2"] * c4["N1"]
+        mlp_bytes = (c4["M"] * c4["K1"] * 2 + c4["K1"] * c4["N1"] * 2 + 2 * c4["M"] * c4["N1"] * 2
+                     + c4["N1"] * c4["N2"] * 2 + c4["M"] * c4["N2"] * 4)
+        paths["mlp2"] = _summary(mlp_flops, mlp_bytes,
+                                 {"overlap": t.run(tsg.OVERLAP, n)[0], "serial": t.run(tsg.SERIAL, n)[0],
+                                  "compute_only": t.run(tsg.COMPUTE_ONLY, n)[0], "comm_only": None})
+        del dx, d1, d2, h, y
+
+        c5 = CONFIGS["moe"]
+        T, Hh, I, E, k = c5["T"], c5["H"], c5["I"], c5["E"], c5["k"]
+        inp = moe_inputs(T, Hh, I, E, k=k, seed=c5["seed"], zipf=c5["zipf"])
+        dv = lambda a: torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).cuda()
+        mx, ids, g, wu, wd = dv(inp["x"]), dv(inp["topk_ids"]), dv(inp["topk_w"]), dv(inp["w_up"]), dv(inp["w_down"])
+        out = torch.empty((T, Hh), dtype=torch.float32, device="cuda")
+        cnt = torch.empty((E,), dtype=torch.int32, device="cuda")
+        srt = torch.empty((T * k,), dtype=torch.int32, device="cuda")
+        wsb = tsg.workspace_bytes(tsg.OP_MOE, [T, Hh, I, E, k])
+        ws = torch.empty((wsb,), dtype=torch.uint8, device="cuda")
+        moe_fn = lambda i, mode: tsg.moe_expert_combine(ctx, mx, ids, g, wu, wd, out, cnt, srt, ws, wsb,
+                                                        T, Hh, I, E, k, mode=mode)
+        t = Timer(torch, tsg, ctx, moe_fn)
+        moe_flops = 4.0 * T * k * Hh * I
+        moe_bytes = (T * k * Hh * 2 + 2 * E * Hh * I * 2 + 2 * T * k * I * 2 + 2 * T * k * Hh * 4
+                     + T * Hh * 4)
+        paths["moe"] = _summary(moe_flops, moe_bytes,
+                                {"overlap": t.run(tsg.OVERLAP, n)[0], "serial": t.run(tsg.SERIAL, n)[0],
+                                 "compute_only": t.run(tsg.COMPUTE_ONLY, n)[0],
+                                 "comm_only": t.run(tsg.COMM_ONLY, n)[0]})
+
+    tflops = ag_flops / (ms_step * 1e-3) / 1e12
+    achieved = ag_flops / (k_ov[0] * 1e-3) / 1e12
     out = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -160,31 +355,28 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_overlap, 5),
+        "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1)/64 bf16 operands, two resident input sets used alternately)",
-        "config": {"workload": f"{args.workload}: AllGather+GEMM, A {M}x{K} bf16 in {R} row chunks of {M // R} "
-                               f"(rank {rank} local, {R - 1} copied in by the concurrent copy kernel), "
+        "data": "synthetic (seeded N(0,1)/64 bf16 operands; two resident input sets used alternately)",
+        "config": {"workload": f"AllGather+GEMM, A {M}x{K} bf16 in {R} row chunks of {M // R} "
+                               f"(rank 0 local, {R - 1} copied in by the concurrent copy kernel), "
                                f"B {K}x{N} bf16, fp32 accumulate, bf16 out",
                    "M": M, "N": N, "K": K, "R": R, "aux_cus": args.aux_cus, "tile": args.tile},
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
-        "speedup_vs_serial": round(ms_serial / ms_overlap, 4),
-        "overlap_vs_compute_only": round(ms_overlap / ms_compute, 4),
-        "overlap_ratio": round((ms_compute + ms_comm - ms_overlap) / ms_comm, 4),
-        "ms": {"overlap": round(ms_overlap, 5), "serial": round(ms_serial, 5),
-               "compute_only": round(ms_compute, 5), "comm_only": round(ms_comm, 5),
-               "gemm_kernel_in_overlap": round(gemm_ms_in_overlap, 5),
-               "gemm_kernel_alone": round(gemm_ms_alone, 5), "copy_kernel": round(copy_ms, 5)},
-        "copy_GBps": round(copy_bytes / (copy_ms * 1e-3) / 1e9, 1),
+        "speedup_vs_serial": ag["speedup_vs_serial"],
+        "overlap_vs_compute_only": ag["overlap_vs_compute_only"],
+        "overlap_ratio": ag.get("overlap_ratio"),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "kernel": "ag_gemm_kernel", "algorithmic_bytes": gemm_bytes},
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": _traffic("ag_gemm_kernel"), "kernel": "ag_gemm_kernel (in overlap mode)",
+                     "algorithmic_bytes": ag_gemm_bytes, "source_hash": source_hash()},
+        "paths": paths,
     }
     if not args.no_cpu:
-        out["cpu_baseline"] = _cpu_baseline(host_inp, M, N, K, R)
+        out["cpu_baseline"] = _cpu_baseline(ag_host, M, N, K, R)
     print(json.dumps(out), flush=True)
     ctx.close()
 

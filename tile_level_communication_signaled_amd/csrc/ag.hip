@@ -172,7 +172,8 @@ hipError_t launch_gemm(int id, const AgGemmArgs& a, bool bf16, int grid, hipStre
 }
 
 int default_tile(int M, int N) {
-  if (N % 224 == 0 && N % 256 != 0 && M >= 2048) return 2;
+  // 256 x 224 when it gives whole waves of 256 tiles (e.g. 8192 x 1792)
+  if (N % 224 == 0 && M % 256 == 0 && ((M / 256) * (N / 224)) % 256 == 0) return 2;
   if (M >= 2048 && N >= 1024) return 1;
   if (M >= 512 && N >= 256) return 3;
   return 6;
