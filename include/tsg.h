@@ -102,6 +102,17 @@ typedef struct tsg_opts {
   /* Nonzero: record per-tile device timestamps into the context's timeline
    * buffer (tsg_timeline). */
   int timeline;
+  /* Workgroups of the auxiliary kernel (AG copy, RS reduce, MLP GEMM2, MoE
+   * combine); 0 = the op's default. */
+  int aux_wgs;
+  /* AG+GEMM: width in K columns of one communication tile.  Each chunk of A
+   * is moved and signalled as ceil(K / comm_tile) column slabs, and a GEMM
+   * tile waits for slab s of its rows just before it loads them, so compute
+   * starts on the first slab instead of the whole chunk ([TL] section 3.1:
+   * communication and computation tiles are sized independently).  A power
+   * of two, at least 64; 0 = 512.  Capped at 2048 and at K rounded up to a
+   * power of two (one signal per chunk when K <= 2048). */
+  int comm_tile;
 } tsg_opts;
 
 /* ------------------------------------------------------------------ ctx */
@@ -139,9 +150,14 @@ tsg_status tsg_enable_kernel_timing(tsg_ctx* ctx, int enable);
 tsg_status tsg_kernel_ms(tsg_ctx* ctx, int which, float* ms);
 
 /* Timeline of the most recent call made with opts.timeline != 0: up to
- * `cap` records of 4 uint64 each {kind<<56 | tile, t_start, t_ready, t_end}
- * in device wall-clock ticks (100 MHz), copied to host memory `out`;
- * *n receives the record count.  Synchronises the device. */
+ * `cap` records of 4 uint64 each {kind<<56 | where<<32 | id, t_start,
+ * t_start + ticks spent waiting for signals, t_end} in device wall-clock
+ * ticks (100 MHz), copied to host memory `out`; *n receives the record
+ * count.  Synchronises the device.  where = XCD<<8 | shader engine<<4 | CU
+ * of the workgroup.  kind / id: 1 AG copy unit (chunk<<24 | slab<<12 |
+ * piece), 2 AG GEMM tile, 3 RS GEMM tile, 4 RS reduce tile, 5 MLP GEMM1
+ * tile, 6 MLP GEMM2 tile (m_tile<<16 | n_tile for tiles), 7 MoE up tile,
+ * 8 MoE down tile, 9 MoE combine unit (row_block<<16 | n_tile). */
 tsg_status tsg_timeline(tsg_ctx* ctx, uint64_t* out, size_t cap, size_t* n);
 
 /* ------------------------------------------------------------- AG+GEMM */

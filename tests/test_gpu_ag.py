@@ -93,16 +93,84 @@ def test_tiny_ag_integer_inputs_exact(env):
 @pytest.mark.parametrize("tile", [6, 3, 1, 2])
 def test_ag_ragged_shapes(env, tile):
     # 3 ranks of 200 rows: tiles straddle chunks; N and K are not multiples of
-    # the tile; K is not a multiple of 64
+    # the tile; K is not a multiple of 64 (communication slabs of 64 columns:
+    # 64, 64 and a last slab of 8)
     M, N, K, R = 600, 200, 136, 3
     inp = ag_inputs(M, K, N, R, seed=7)
     ref, scale = _ref(inp)
     for rank in range(R):
         for out_bf16 in (False, True):
             case = AgCase(env, inp, M, N, K, R, rank, out_bf16)
-            full, c = case.run(opts={"tile": tile, "aux_cus": 16})
-            assert np.array_equal(full, inp["a"])
-            assert err_ratio(c, ref, scale, bf16_out=out_bf16) <= 1.0
+            for ct in (0, 64):
+                full, c = case.run(opts={"tile": tile, "aux_cus": 16, "comm_tile": ct})
+                assert np.array_equal(full, inp["a"])
+                assert err_ratio(c, ref, scale, bf16_out=out_bf16) <= 1.0
+
+
+@pytest.mark.parametrize("K", [512, 320])
+def test_ag_comm_tile_slabs(env, K):
+    # Chunks move as column slabs; tiles wait slab by slab inside the K loop.
+    # K = 512 runs the direct-to-LDS main loop, K = 320 the register path with
+    # a partial last slab (128, 128, 64).  Few copy workgroups so that tiles
+    # really do wait on later slabs.  Every combination gives the same bits.
+    M, N, R = 512, 256, 4
+    inp = ag_inputs(M, K, N, R, seed=11)
+    ref, scale = _ref(inp)
+    first = None
+    for rank in (0, 3):
+        case = AgCase(env, inp, M, N, K, R, rank, out_bf16=False)
+        for tile in (6, 3, 1):                 # 256-row tiles span two 128-row chunks
+            for ct in (64, 128, 1024):
+                for wgs in (3, 64):
+                    full, c = case.run(opts={"tile": tile, "aux_cus": -1, "comm_tile": ct, "aux_wgs": wgs})
+                    assert np.array_equal(full, inp["a"]), (rank, tile, ct, wgs)
+                    assert err_ratio(c, ref, scale) <= 1.0
+                    if first is None:
+                        first = c
+                    assert np.array_equal(c, first), (rank, tile, ct, wgs)
+
+
+def test_ag_comm_tile_ragged_rows_and_unaligned_buffer(env):
+    # 3 chunks of 200 rows, K a multiple of 64: the last 128-row tile has rows
+    # beyond M (read as a stand-in row of the tile); then the same with the
+    # gathered buffer 16 bytes off a 128-byte boundary, where slabs share
+    # cache lines and the waits take the general acquire.
+    torch, tsg, ctx = env
+    M, N, K, R = 600, 192, 512, 3
+    inp = ag_inputs(M, K, N, R, seed=13)
+    ref, scale = _ref(inp)
+    case = AgCase(env, inp, M, N, K, R, 2, out_bf16=False)
+    for tile in (3, 6):
+        full, c = case.run(opts={"tile": tile, "comm_tile": 64, "aux_wgs": 4})
+        assert np.array_equal(full, inp["a"]) and err_ratio(c, ref, scale) <= 1.0
+    store = torch.empty((M * K + 64,), dtype=torch.int16, device="cuda")
+    case.full = store[8:8 + M * K].view(M, K)
+    assert case.full.data_ptr() % 128 == 16
+    for tile in (3, 6):
+        full, c = case.run(opts={"tile": tile, "comm_tile": 64, "aux_wgs": 4})
+        assert np.array_equal(full, inp["a"]) and err_ratio(c, ref, scale) <= 1.0
+
+
+def test_ag_comm_only_and_serial_fill_gathered_buffer(env):
+    torch, tsg, ctx = env
+    M, N, K, R = 512, 128, 256, 8
+    inp = ag_inputs(M, K, N, R, seed=12)
+    ref, scale = _ref(inp)
+    case = AgCase(env, inp, M, N, K, R, 6, out_bf16=False)
+    full, _ = case.run(mode=tsg.COMM_ONLY, opts={"comm_tile": 64})
+    assert np.array_equal(full, inp["a"])
+    full, c = case.run(mode=tsg.SERIAL, opts={"comm_tile": 64, "aux_wgs": 5})
+    assert np.array_equal(full, inp["a"]) and err_ratio(c, ref, scale) <= 1.0
+
+
+def test_ag_rejects_bad_comm_tile(env):
+    torch, tsg, ctx = env
+    inp = ag_inputs(64, 64, 64, 4, seed=9)
+    case = AgCase(env, inp, 64, 64, 64, 4, 0, out_bf16=False)
+    for ct in (32, 96, -64):
+        st = tsg.gemm_ag_overlap(ctx, case.loc, case.peers, case.full, case.b, case.c, tsg.F32, 64, 64, 64, 4, 0,
+                                 opts={"comm_tile": ct}, raise_on_error=False)
+        assert st == tsg.E_INVALID, ct
 
 
 def test_ag_degenerate_single_rank_and_small(env):
@@ -138,6 +206,11 @@ def test_ag_missing_chunk_times_out_then_recovers(env):
     case = AgCase(env, inp, M, N, K, R, 0, out_bf16=False)
     case.run(opts={"aux_cus": 8, "debug_skip_mask": 1 << 2, "timeout_ms": 20}, expect=tsg.E_TIMEOUT)
     full, c = case.run(opts={"aux_cus": 8})
+    assert np.array_equal(full, inp["a"]) and err_ratio(c, ref, scale) <= 1.0
+    # the same with two slabs per chunk: the waits inside the K loop time out too
+    case.run(opts={"aux_cus": 8, "debug_skip_mask": 1 << 1, "timeout_ms": 20, "comm_tile": 64},
+             expect=tsg.E_TIMEOUT)
+    full, c = case.run(opts={"aux_cus": 8, "comm_tile": 64})
     assert np.array_equal(full, inp["a"]) and err_ratio(c, ref, scale) <= 1.0
 
 

@@ -48,6 +48,8 @@ class Opts(ctypes.Structure):
         ("timeout_ms", ctypes.c_uint32),
         ("debug_skip_mask", ctypes.c_uint32),
         ("timeline", ctypes.c_int),
+        ("aux_wgs", ctypes.c_int),
+        ("comm_tile", ctypes.c_int),
     ]
 
 

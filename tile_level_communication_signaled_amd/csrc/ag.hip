@@ -1,21 +1,30 @@
 // AllGather + GEMM at one rank's share.
 //
 // Producer: a copy kernel standing in for the peers' arrival.  It moves the
-// shards chunk by chunk in arrival order (the local shard first) into the
-// gathered buffer and releases each chunk's signal once every copy workgroup
-// has finished its slice of that chunk ("Triton-distributed: Programming
+// shards into the gathered buffer in arrival order (the local shard first)
+// and signals what it has moved ("Triton-distributed: Programming
 // Overlapping Kernels on Distributed AI Systems with the Triton Compiler",
 // section 3.2, Algorithm 2, pull mode: local copy and signal, then one copy
-// and one signal per peer).
+// and one signal per peer).  The unit of communication is not the whole chunk
+// but a column slab of it: chunk c, K columns [s * W, (s + 1) * W).  The
+// communication tile is sized independently of the compute tile ("TileLink:
+// Generating Efficient Compute-Communication Overlapping Kernels using
+// Tile-Centric Primitives", section 3.1, decoupled tile sizes; section 4.1,
+// the static mapping from a compute tile to the communication tiles it
+// needs).  Slabs are moved slab-major: slab 0 of every chunk in arrival
+// order, then slab 1, and so on, each slab in pieces of rows; the last piece
+// of a slab to finish publishes its signal (counted arrivals).
 //
 // Consumer: the MFMA GEMM.  Workgroup w takes the w-th tile of a swizzled
-// order that starts at the local chunk and follows the arrival order (same
-// page, section 3.7: the compute tile order is aligned with the arrival order
-// of the communication tiles), waits (acquire) on the signals of every chunk
-// its rows span, then runs its K loop.  The chunk a row belongs to is the
-// static rank mapping of "TileLink: Generating Efficient Compute-
-// Communication Overlapping Kernels using Tile-Centric Primitives", section
-// 4.1 (rank = floor(row / M_per_rank)) with one channel per rank.
+// order that starts at the local chunk and follows the arrival order (the
+// Triton-distributed page, section 3.7: the compute tile order follows the
+// arrival order of the communication tiles).  It waits (acquire) for slab 0
+// of every chunk its rows span, and then, just before it issues the loads of
+// the first K step of slab s, for slab s.  The signal of slab s + 1 is read
+// as soon as slab s has been passed, so when the copy runs ahead the wait
+// costs no round trip.  The chunk a row belongs to is the static rank mapping
+// of the TileLink page, section 4.1 (rank = floor(row / M_per_rank)), with
+// one channel per rank.
 #include "tsg_gemm.hpp"
 #include "tsg_internal.hpp"
 
@@ -25,40 +34,103 @@ namespace {
 
 constexpr int kMaxRanks = 32;
 constexpr int kMaxMTiles = 1024;
+constexpr size_t kSigBase = size_t(1) << 18;  // AG slab signals in the context's pool
+constexpr size_t kSigCap = size_t(1) << 18;   // slots up to the next op's region
 
 struct ChunkOrder {
   int8_t chunk[kMaxRanks];  // chunk copied at arrival position p (p = 0: local)
 };
 
 // ---------------------------------------------------------------- copy
-__global__ void __launch_bounds__(256) ag_copy_kernel(const uint16_t* __restrict__ a_local,
-                                                      const uint16_t* __restrict__ a_peers,
-                                                      uint16_t* __restrict__ a_full,
-                                                      int64_t chunk_vec, int R, int rank,
-                                                      ChunkOrder ord, uint64_t* sig, uint32_t* cnt,
-                                                      SyncArgs sa, uint32_t skip_mask, Timeline tl) {
+constexpr int kHead = 4;  // leading slabs with their own piece counts
+
+struct CopyArgs {
+  const u32x4_t* a_local;  // [chunk_rows x K] bf16, as 16-byte vectors
+  const u32x4_t* a_peers;  // [(R - 1) x chunk_rows x K], ascending rank without `rank`
+  u32x4_t* a_full;         // [M x K]
+  uint64_t* sig;           // signal of (chunk c, slab s) at c * n_slab + s
+  uint32_t* cnt;           // arrival counters, same indexing
+  SyncArgs sa;
+  Timeline tl;
+  ChunkOrder ord;
+  int64_t k8;              // vectors per row (K / 8)
+  int chunk_rows, R, rank;
+  int n_slab;              // slabs per chunk
+  int vpr_log2;            // log2(vectors per slab row), <= 8: slab width W = 8 << vpr_log2
+  // Pieces per chunk of slab s: np[s] for s < kHead, np[kHead] for the rest;
+  // the units of slab s < kHead start at ustart[s], those of the rest at
+  // ustart[kHead].
+  int np[kHead + 1];
+  int ustart[kHead + 1];
+  int n_units;
+  uint32_t skip_mask;
+};
+
+// Work unit u -> (slab s, arrival position p, piece j), slab-major.  One unit
+// copies piece j (np[s] pieces of about equal rows) of slab s of chunk
+// ord[p], then arrives on that slab's signal.  The first slabs are cut into
+// more pieces so that many workgroups share them: every GEMM tile needs
+// slab 0 before it can start, slab 1 soon after, and so on, while later
+// slabs have time to arrive in larger pieces, which need fewer releases.
+__global__ void __launch_bounds__(256) ag_copy_kernel(const CopyArgs a) {
   constexpr int U = 8;  // 16-byte vectors in flight per thread
-  const int64_t nwg = gridDim.x, w = blockIdx.x;
-  const int64_t lo = chunk_vec * w / nwg, hi = chunk_vec * (w + 1) / nwg;
-  for (int p = 0; p < R; ++p) {
-    const int c = ord.chunk[p];
-    const uint64_t t0 = tl.buf ? wall_clock64() : 0;
-    const u32x4_t* __restrict__ src =
-        (const u32x4_t*)(c == rank ? a_local : a_peers + (int64_t)(c < rank ? c : c - 1) * chunk_vec * 8);
-    u32x4_t* __restrict__ dst = (u32x4_t*)a_full + (int64_t)c * chunk_vec;
-    int64_t i = lo + threadIdx.x;
-    for (; i + (U - 1) * 256 < hi; i += U * 256) {
-      u32x4_t v[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(src + i + u * 256);
-#pragma unroll
-      for (int u = 0; u < U; ++u) dst[i + u * 256] = v[u];
+  const int vpr = 1 << a.vpr_log2;
+  for (int u = blockIdx.x; u < a.n_units; u += gridDim.x) {
+    const uint64_t t0 = a.tl.buf ? wall_clock64() : 0;
+    int s, rem, npc;
+    if (u >= a.ustart[kHead]) {
+      npc = a.np[kHead];
+      const int v = u - a.ustart[kHead];
+      const int per = a.R * npc;
+      s = kHead + v / per;
+      rem = v - (s - kHead) * per;
+    } else {
+      s = 0;
+      while (u >= a.ustart[s + 1]) ++s;
+      npc = a.np[s];
+      rem = u - a.ustart[s];
     }
-    for (; i < hi; i += 256) dst[i] = __builtin_nontemporal_load(src + i);
+    const int p = rem / npc;
+    const int j = rem - p * npc;
+    const int c = a.ord.chunk[p];
+    const int rp = (a.chunk_rows + npc - 1) / npc;
+    const int r0 = j * rp;
+    const int nr = min(rp, a.chunk_rows - r0);
+    const int64_t col0 = (int64_t)s * vpr;
+    const int width = (int)min((int64_t)vpr, a.k8 - col0);
+    const int64_t chunk_vec = (int64_t)a.chunk_rows * a.k8;
+    const u32x4_t* __restrict__ src =
+        (c == a.rank ? a.a_local : a.a_peers + (int64_t)(c < a.rank ? c : c - 1) * chunk_vec) +
+        (int64_t)r0 * a.k8 + col0;
+    u32x4_t* __restrict__ dst = a.a_full + ((int64_t)c * a.chunk_rows + r0) * a.k8 + col0;
+    // Slab rows are at most 256 vectors wide, so thread t always moves column
+    // t mod vpr of rows t / vpr, t / vpr + 256 / vpr, ...  Addresses are a
+    // uniform base plus a 32-bit byte offset (one register per access).
+    const int rows_q = 256 >> a.vpr_log2;
+    const int cc = threadIdx.x & (vpr - 1);
+    const int rr = threadIdx.x >> a.vpr_log2;
+    if (cc < width) {
+      const char* sb = (const char*)src;
+      char* db = (char*)dst;
+      const uint32_t step = (uint32_t)(rows_q * a.k8 * 16);
+      uint32_t off = (uint32_t)((rr * a.k8 + cc) * 16);
+      int r = rr;
+      for (; r + (U - 1) * rows_q < nr; r += U * rows_q, off += U * step) {
+        u32x4_t v[U];
+#pragma unroll
+        for (int q = 0; q < U; ++q) v[q] = *(const u32x4_t*)(sb + (off + q * step));
+#pragma unroll
+        for (int q = 0; q < U; ++q) *(u32x4_t*)(db + (off + q * step)) = v[q];
+      }
+      for (; r < nr; r += rows_q, off += step)
+        *(u32x4_t*)(db + off) = *(const u32x4_t*)(sb + off);
+    }
     block_release_fence();
-    if (threadIdx.x == 0 && !((skip_mask >> c) & 1u))
-      sig_arrive_counted_lane(cnt + c, sig + c, (uint32_t)nwg, sa.epoch);
-    if (threadIdx.x == 0 && tl.buf) timeline_put(tl, 1, (uint32_t)(c << 16 | w), t0, t0, wall_clock64());
+    const size_t si = (size_t)c * a.n_slab + s;
+    if (threadIdx.x == 0 && !((a.skip_mask >> c) & 1u))
+      sig_arrive_counted_lane(a.cnt + si, a.sig + si, (uint32_t)npc, a.sa.epoch);
+    if (threadIdx.x == 0 && a.tl.buf)
+      timeline_put(a.tl, 1, (uint32_t)(c << 24 | s << 12 | (j & 0xfff)), t0, t0, wall_clock64());
   }
 }
 
@@ -67,16 +139,80 @@ struct AgGemmArgs {
   const uint16_t* a_full;
   const uint16_t* b;
   void* c;
-  uint64_t* sig;
+  uint64_t* sig;          // slab signals, c * n_slab + s
   SyncArgs sa;
   Timeline tl;
   int M, N, K;
   int chunk_rows;
   int n_tiles_n;
   int wait;               // 0: no waits (compute-only)
-  uint32_t arrivals;      // arrivals that complete one chunk signal
+  uint32_t arrivals;      // arrivals that complete one slab signal
+  int n_slab;
+  int slab_log2;          // log2 of the slab width in K columns
+  int l1_only;            // slabs never share a 128-byte line
   int per_xcd;            // resident tiles per XCD (0 = no XCD remap)
   uint16_t mt_order[kMaxMTiles];
+};
+
+// Slab waits inside the K loop, per wave.  Slabs below `ready_until` are
+// known complete and already acquired.  Reaching slab s >= ready_until, the
+// wave polls a window of signals in one load: lane l reads chunk
+// c_lo + l mod n_span at slab s + l / n_span.  The window's complete prefix
+// becomes ready; if slab s itself is incomplete the wave polls it until it
+// is.  One acquire then covers every slab of the prefix.  As the copy runs
+// ahead of the GEMM, a tile polls a few times instead of once per slab.
+//
+// The general acquire invalidates the wave's L1 and its XCD's L2, which also
+// drops the L2's copy of the B panel that all tiles of the XCD share.  When
+// no 128-byte line of the gathered buffer holds bytes of two slabs (a
+// 128-byte aligned buffer, rows of a multiple of 128 bytes, slabs of at least
+// 64 columns) nothing on this XCD can have read a line of slab s before slab
+// s was complete: tiles load a slab only after its wait, rows outside the
+// operand are read as its last row, and the L2 was invalidated when the tile
+// started.  Then invalidating L1 alone is enough.  The flag loads have
+// returned before the invalidate (their values decided the branch), so loads
+// issued after it see the producer's released data.
+struct SlabWait {
+  const uint64_t* sig;
+  SyncArgs sa;
+  uint64_t target;
+  uint64_t waited;  // ticks spent polling inside the K loop (timeline only)
+  int n_slab, slab_log2, c_lo, n_span;
+  int ready_until;
+  bool active;
+  bool l1_only;     // slabs are line-aligned: the acquire only invalidates L1
+
+  __device__ __forceinline__ void before_a(int k0) {
+    if (!active || (k0 & ((1 << slab_log2) - 1))) return;
+    const int s = k0 >> slab_log2;
+    if (s < ready_until) return;
+    const int lane = __lane_id();
+    const int win = 64 / n_span;                 // slabs per window
+    const int ls = s + lane / n_span;            // this lane's slab
+    const bool valid = lane < win * n_span && ls < n_slab;
+    uint64_t v = ~0ull;
+    if (valid)
+      v = __hip_atomic_load(sig + (size_t)(c_lo + lane % n_span) * n_slab + ls, __ATOMIC_RELAXED,
+                            TSG_SIG_SCOPE);
+    const uint64_t bad = __builtin_amdgcn_ballot_w64(v < target);
+    if (bad == 0) {
+      ready_until = min(s + win, n_slab);
+    } else {
+      const int f = (int)__builtin_ctzll(bad);   // first incomplete lane, slab-major
+      if (f >= n_span) {
+        ready_until = s + f / n_span;
+      } else {
+        const uint64_t t = wall_clock64();
+        for (int i = 0; i < n_span; ++i) wave_poll_ge(sig + (size_t)(c_lo + i) * n_slab + s, target, sa);
+        waited += wall_clock64() - t;
+        ready_until = s + 1;
+      }
+    }
+    if (l1_only)
+      asm volatile("buffer_inv sc0" ::: "memory");
+    else
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
 };
 
 template <class Cfg, bool OUT_BF16, bool DIRECT>
@@ -87,19 +223,31 @@ __global__ void __launch_bounds__(Cfg::NT) ag_gemm_kernel(const AgGemmArgs args)
   const int nt = w % args.n_tiles_n;
   const int row0 = mt * Cfg::BM, col0 = nt * Cfg::BN;
   const uint64_t t0 = args.tl.buf ? wall_clock64() : 0;
+  SlabWait hook;
+  hook.active = false;
+  hook.waited = 0;
   if (args.wait) {
     const int last = min(row0 + Cfg::BM, args.M) - 1;
-    const uint64_t target = sig_target(args.sa.epoch, args.arrivals);
-    for (int c = row0 / args.chunk_rows; c <= last / args.chunk_rows; ++c)
-      block_wait_ge(args.sig + c, target, args.sa);
+    const int c_lo = row0 / args.chunk_rows, c_hi = last / args.chunk_rows;
+    hook.sig = args.sig;
+    hook.sa = args.sa;
+    hook.target = sig_target(args.sa.epoch, args.arrivals);
+    hook.n_slab = args.n_slab;
+    hook.slab_log2 = args.slab_log2;
+    hook.c_lo = c_lo;
+    hook.n_span = c_hi - c_lo + 1;
+    hook.active = args.n_slab > 1;
+    hook.l1_only = args.l1_only != 0;
+    hook.ready_until = 1;
+    for (int c = c_lo; c <= c_hi; ++c) block_wait_ge(args.sig + (size_t)c * args.n_slab, hook.target, args.sa);
   }
   const uint64_t t1 = args.tl.buf ? wall_clock64() : 0;
   typename GemmTile<Cfg>::Acc acc;
   const ARowsLinear ar{args.a_full, args.K, row0, args.M};
   if (DIRECT)
-    GemmTile<Cfg>::run_direct(ar, args.b, args.N, col0, args.N, args.K, lds, acc);
+    GemmTile<Cfg>::run_direct(ar, args.b, args.N, col0, args.N, args.K, lds, acc, hook);
   else
-    GemmTile<Cfg>::run_regs(ar, args.b, args.N, col0, args.N, args.K, lds, acc);
+    GemmTile<Cfg>::run_regs(ar, args.b, args.N, col0, args.N, args.K, lds, acc, hook);
   const int M = args.M, N = args.N;
   if (OUT_BF16) {
     uint16_t* C = (uint16_t*)args.c;
@@ -115,7 +263,7 @@ __global__ void __launch_bounds__(Cfg::NT) ag_gemm_kernel(const AgGemmArgs args)
     });
   }
   if (args.tl.buf && threadIdx.x == 0)
-    timeline_put(args.tl, 2, (uint32_t)(mt << 16 | nt), t0, t1, wall_clock64());
+    timeline_put(args.tl, 2, (uint32_t)(mt << 16 | nt), t0, t1 + hook.waited, wall_clock64());
 }
 
 // Tile configurations (id -> BM x BN, waves).
@@ -156,6 +304,33 @@ hipError_t launch_gemm_cfg(const AgGemmArgs& a, bool bf16, int grid, hipStream_t
   else
     hipLaunchKernelGGL((ag_gemm_kernel<Cfg, false, false>), dim3(grid), dim3(Cfg::NT), 0, s, a);
   return hipGetLastError();
+}
+
+template <class Cfg>
+const void* gemm_fn_cfg(bool bf16, bool direct) {
+  if (bf16 && direct) return (const void*)&ag_gemm_kernel<Cfg, true, true>;
+  if (bf16) return (const void*)&ag_gemm_kernel<Cfg, true, false>;
+  if (direct) return (const void*)&ag_gemm_kernel<Cfg, false, true>;
+  return (const void*)&ag_gemm_kernel<Cfg, false, false>;
+}
+
+// The GEMM kernel a launch uses, and its workgroup size.
+const void* gemm_fn(int id, bool bf16, int K, int* nt) {
+  switch (id) {
+#define TSG_AG_CFG(i, C)                                     \
+  case i:                                                    \
+    *nt = C::NT;                                             \
+    return gemm_fn_cfg<C>(bf16, K % (2 * C::BK) == 0);
+    TSG_AG_CFG(1, Cfg1)
+    TSG_AG_CFG(2, Cfg2)
+    TSG_AG_CFG(3, Cfg3)
+    TSG_AG_CFG(4, Cfg4)
+    TSG_AG_CFG(5, Cfg5)
+    TSG_AG_CFG(6, Cfg6)
+    TSG_AG_CFG(7, Cfg7)
+#undef TSG_AG_CFG
+    default: *nt = 0; return nullptr;
+  }
 }
 
 hipError_t launch_gemm(int id, const AgGemmArgs& a, bool bf16, int grid, hipStream_t s) {
@@ -221,7 +396,83 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
   const int n_mt = (M + ts.bm - 1) / ts.bm, n_nt = (N + ts.bn - 1) / ts.bn;
   if (n_mt > kMaxMTiles) return fail(ctx, TSG_E_UNSUPPORTED, "M / BM exceeds %d", kMaxMTiles);
 
+  // Communication tile: slab width W (power of two, >= 64; capped at 2048
+  // columns and at the first power of two >= K, which is one slab per chunk).
+  int slab = o.comm_tile ? o.comm_tile : 512;
+  if (slab < 64 || (slab & (slab - 1)))
+    return fail(ctx, TSG_E_INVALID, "comm_tile must be a power of two >= 64 (got %d)", slab);
+  int k_pow2 = 64;
+  while (k_pow2 < K) k_pow2 *= 2;
+  slab = std::min(std::min(slab, k_pow2), 2048);
+  int slab_log2 = 0;
+  while ((1 << slab_log2) < slab) ++slab_log2;
+  const int n_slab = (K + slab - 1) / slab;
+  if ((size_t)R * n_slab > kSigCap)
+    return fail(ctx, TSG_E_UNSUPPORTED, "R * ceil(K / comm_tile) exceeds %zu signals", kSigCap);
+  const int vpr_log2 = slab_log2 - 3;
   TSG_HIP(ctx, hipSetDevice(ctx->device));
+
+  // Copy workgroups and streams.  Overlap: in shared mode one workgroup per
+  // two CUs, resident beside the GEMM's workgroups (the copy needs few
+  // registers and no LDS); in split mode four per copy CU.  Serial: two per
+  // CU.
+  // In shared mode the GEMM runs on the caller's stream and the copy on a
+  // side stream; their workgroups must be able to share a CU, or a GEMM that
+  // fills every CU first would leave the copy no room while it waits for the
+  // copy.  Otherwise the two run back to back.
+  Pair pr{(hipStream_t)stream, (hipStream_t)stream, ctx->n_cus, 0};
+  int nwg = o.aux_wgs > 0 ? o.aux_wgs : ctx->n_cus * 2;
+  bool back_to_back = mode == TSG_MODE_SERIAL;
+  if (mode == TSG_MODE_OVERLAP || mode == TSG_MODE_COMM_ONLY) {
+    const tsg_status ss = streams(ctx, o, &pr, (hipStream_t)stream);
+    if (ss != TSG_OK) return ss;
+    if (o.aux_wgs <= 0) nwg = o.aux_cus < 0 ? ctx->n_cus / 2 : pr.aux_cus * 4;
+    if (mode == TSG_MODE_OVERLAP && o.aux_cus < 0) {
+      int nt = 0;
+      const void* fn = gemm_fn(tile, c_dtype == TSG_BF16, K, &nt);
+      back_to_back = !co_resident(ctx, fn, nt, (const void*)&ag_copy_kernel, 256);
+    }
+  }
+  // Pieces: every piece ends in a release, whose L2 write-back of the dirty
+  // copy data costs tens of nanoseconds and stalls the XCD's other traffic, so
+  // body pieces are as large as the workgroup count allows (about the copy
+  // volume over the workgroups, between 32 KB and 128 KB).  Slab 0, which
+  // every tile waits for first, is cut so that all workgroups share it; each
+  // following head slab gets half as many pieces, down to the body size.
+  const int64_t total_vec = (int64_t)R * chunk_rows * (K / 8);
+  int64_t unit_vec = 2048;
+  while (unit_vec < 8192 && unit_vec * 2 * nwg <= total_vec) unit_vec *= 2;
+  const int rows_q = 256 >> vpr_log2;  // rows one pass of the workgroup moves
+  auto pieces_for_rows = [&](int64_t rows) {
+    rows = std::max<int64_t>(rows, std::min(rows_q, chunk_rows));
+    return (int)std::max<int64_t>(1, (chunk_rows + rows - 1) / rows);
+  };
+  const int np_body = pieces_for_rows(unit_vec >> vpr_log2);
+  int np[kHead + 1];
+  int np_head = std::max(np_body, pieces_for_rows(std::max<int64_t>(1, (int64_t)chunk_rows * R / nwg)));
+  for (int h = 0; h < kHead; ++h) {
+    np[h] = std::max(np_body, np_head);
+    np_head /= 2;
+  }
+  np[kHead] = np_body;
+  for (int h = 0; h <= kHead; ++h) {  // no empty piece: every piece arrives once
+    const int rp = (chunk_rows + np[h] - 1) / np[h];
+    np[h] = (chunk_rows + rp - 1) / rp;
+  }
+  int64_t rows_max = 0;
+  for (int h = 0; h <= kHead; ++h) rows_max = std::max<int64_t>(rows_max, (chunk_rows + np[h] - 1) / np[h]);
+  if (rows_max * K * 2 >= (int64_t)1 << 31)
+    return fail(ctx, TSG_E_UNSUPPORTED, "gemm_ag_overlap: K too large for the copy's 32-bit offsets");
+  int ustart[kHead + 1];
+  int64_t n_units = 0;
+  for (int h = 0; h < kHead; ++h) {
+    ustart[h] = (int)n_units;
+    if (h < n_slab) n_units += (int64_t)R * np[h];
+  }
+  ustart[kHead] = (int)n_units;
+  n_units += (int64_t)std::max(0, n_slab - kHead) * R * np[kHead];
+  if (n_units >= ((int64_t)1 << 30)) return fail(ctx, TSG_E_UNSUPPORTED, "gemm_ag_overlap: too many copy units");
+
   hipStream_t caller = (hipStream_t)stream;
   ++ctx->epoch;
   time_reset(ctx);
@@ -230,7 +481,7 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
   ga.a_full = (const uint16_t*)a_full;
   ga.b = (const uint16_t*)b;
   ga.c = c;
-  ga.sig = ctx->d_sig;  // chunk signals 0 .. R-1
+  ga.sig = ctx->d_sig + kSigBase;
   ga.sa = sync_args(ctx, o);
   ga.tl = timeline(ctx, o);
   ga.M = M;
@@ -238,6 +489,10 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
   ga.K = K;
   ga.chunk_rows = chunk_rows;
   ga.n_tiles_n = n_nt;
+  ga.arrivals = 1;  // any completed count: a slab signal is only published once complete
+  ga.n_slab = n_slab;
+  ga.slab_log2 = slab_log2;
+  ga.l1_only = ((uintptr_t)a_full % 128 == 0 && K % 64 == 0) ? 1 : 0;
   // M-tile order: by the arrival position of the last chunk a tile spans,
   // ties by row (order knob 1 = plain row order).
   {
@@ -251,22 +506,39 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
     std::sort(key.begin(), key.end());
     for (int m = 0; m < n_mt; ++m) ga.mt_order[m] = (uint16_t)key[m].second;
   }
-  const int64_t chunk_vec = (int64_t)chunk_rows * K / 8;
   const int grid_gemm = n_mt * n_nt;
-  const Timeline tl = timeline(ctx, o);
   if (o.timeline) TSG_HIP(ctx, hipMemsetAsync(ctx->d_timeline_n, 0, sizeof(uint32_t), caller));
+
+  CopyArgs ca;
+  ca.a_local = (const u32x4_t*)a_local;
+  ca.a_peers = (const u32x4_t*)a_peers;
+  ca.a_full = (u32x4_t*)a_full;
+  ca.sig = ctx->d_sig + kSigBase;
+  ca.cnt = ctx->d_cnt + kSigBase;
+  ca.sa = ga.sa;
+  ca.tl = ga.tl;
+  ca.ord = ord;
+  ca.k8 = K / 8;
+  ca.chunk_rows = chunk_rows;
+  ca.R = R;
+  ca.rank = rank;
+  ca.n_slab = n_slab;
+  ca.vpr_log2 = vpr_log2;
+  for (int h = 0; h <= kHead; ++h) {
+    ca.np[h] = np[h];
+    ca.ustart[h] = ustart[h];
+  }
+  ca.n_units = (int)n_units;
+  ca.skip_mask = o.skip_mask;
 
   auto copy = [&](hipStream_t s, int nwg) -> tsg_status {
     time_begin(ctx, 1, s);
-    hipLaunchKernelGGL(ag_copy_kernel, dim3(nwg), dim3(256), 0, s, (const uint16_t*)a_local,
-                       (const uint16_t*)a_peers, (uint16_t*)a_full, chunk_vec, R, rank, ord,
-                       ctx->d_sig, ctx->d_cnt, ga.sa, o.skip_mask, tl);
+    hipLaunchKernelGGL(ag_copy_kernel, dim3((int)std::min<int64_t>(nwg, n_units)), dim3(256), 0, s, ca);
     time_end(ctx, 1, s);
     return check_launch(ctx, "ag_copy_kernel");
   };
-  auto gemm = [&](hipStream_t s, int wait, uint32_t arrivals, int cus) -> tsg_status {
+  auto gemm = [&](hipStream_t s, int wait, int cus) -> tsg_status {
     ga.wait = wait;
-    ga.arrivals = arrivals;
     ga.per_xcd = cus / 8;
     time_begin(ctx, 0, s);
     hipError_t e = launch_gemm(tile, ga, c_dtype == TSG_BF16, grid_gemm, s);
@@ -276,27 +548,29 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
   };
 
   tsg_status st = TSG_OK;
-  if (mode == TSG_MODE_SERIAL) {
-    const int nwg = ctx->n_cus * 2;
+  if (back_to_back) {
     st = copy(caller, nwg);
-    if (st == TSG_OK) st = gemm(caller, 1, (uint32_t)nwg, ctx->n_cus);
+    if (st == TSG_OK) st = gemm(caller, 1, ctx->n_cus);
     return st;
   }
-  if (mode == TSG_MODE_COMPUTE_ONLY) return gemm(caller, 0, 0, ctx->n_cus);
+  if (mode == TSG_MODE_COMPUTE_ONLY) return gemm(caller, 0, ctx->n_cus);
 
-  Pair pr;
-  st = streams(ctx, o, &pr);
-  if (st != TSG_OK) return st;
-  // Copy workgroups: each release of a chunk slice costs an L2 write-back, so
-  // a few wide workgroups (8 per XCD) rather than many.
-  const int nwg = o.aux_cus < 0 ? 64 : std::min(64, pr.aux_cus * 4);
   st = fork(ctx, caller, pr);
   if (st != TSG_OK) return st;
-  // Producer (copy) first, consumer (GEMM) second: the copy never waits, so
-  // even if the two kernels were serialised the GEMM's waits would all be
-  // satisfied.
-  st = copy(pr.aux, nwg);
-  if (st == TSG_OK && mode == TSG_MODE_OVERLAP) st = gemm(pr.main, 1, (uint32_t)nwg, pr.main_cus);
+  // Producer (copy) first, consumer (GEMM) second.  The copy never waits and
+  // can always find room (split CUs, or a CU shared with a GEMM workgroup);
+  // the GEMM's waits are bounded, so a consumer dispatched ahead of a producer
+  // that cannot run (as under a profiler that serialises kernels) ends in a
+  // reported timeout rather than a hang.
+  if (mode == TSG_MODE_OVERLAP && pr.main == caller) {
+    // The GEMM needs no fork: launched first it is dispatched at once, and the
+    // copy's workgroups join it on the same CUs.
+    st = gemm(pr.main, 1, pr.main_cus);
+    if (st == TSG_OK) st = copy(pr.aux, nwg);
+  } else {
+    st = copy(pr.aux, nwg);
+    if (st == TSG_OK && mode == TSG_MODE_OVERLAP) st = gemm(pr.main, 1, pr.main_cus);
+  }
   tsg_status sj = join(ctx, caller, pr);
   return st != TSG_OK ? st : sj;
 }

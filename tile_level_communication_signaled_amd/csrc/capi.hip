@@ -48,6 +48,8 @@ Opts resolve(const tsg_opts* o, int default_aux_cus) {
   r.timeout_ms = o && o->timeout_ms ? o->timeout_ms : 2000u;
   r.skip_mask = o ? o->debug_skip_mask : 0u;
   r.timeline = o ? o->timeline : 0;
+  r.aux_wgs = o ? o->aux_wgs : 0;
+  r.comm_tile = o ? o->comm_tile : 0;
   return r;
 }
 
@@ -70,10 +72,14 @@ static tsg_status masked(tsg_ctx* ctx, const std::vector<uint32_t>& mask, hipStr
   return TSG_OK;
 }
 
-tsg_status streams(tsg_ctx* ctx, const Opts& o, Pair* out) {
+tsg_status streams(tsg_ctx* ctx, const Opts& o, Pair* out, hipStream_t caller) {
   const int n = ctx->n_cus;
   if (o.aux_cus < 0) {
-    tsg_status st = unmasked(ctx, 0, &out->main);
+    tsg_status st = TSG_OK;
+    if (caller)
+      out->main = caller;
+    else
+      st = unmasked(ctx, 0, &out->main);
     if (st != TSG_OK) return st;
     st = unmasked(ctx, 1, &out->aux);
     out->main_cus = n;
@@ -119,19 +125,42 @@ tsg::Timeline timeline(tsg_ctx* ctx, const Opts& o) {
 
 tsg_status fork(tsg_ctx* ctx, hipStream_t caller, const Pair& p) {
   TSG_HIP(ctx, hipEventRecord(ctx->ev_fork, caller));
-  TSG_HIP(ctx, hipStreamWaitEvent(p.main, ctx->ev_fork, 0));
-  if (p.aux != p.main) TSG_HIP(ctx, hipStreamWaitEvent(p.aux, ctx->ev_fork, 0));
+  if (p.main != caller) TSG_HIP(ctx, hipStreamWaitEvent(p.main, ctx->ev_fork, 0));
+  if (p.aux != p.main && p.aux != caller) TSG_HIP(ctx, hipStreamWaitEvent(p.aux, ctx->ev_fork, 0));
   return TSG_OK;
 }
 
 tsg_status join(tsg_ctx* ctx, hipStream_t caller, const Pair& p) {
-  TSG_HIP(ctx, hipEventRecord(ctx->ev_join[0], p.main));
-  TSG_HIP(ctx, hipStreamWaitEvent(caller, ctx->ev_join[0], 0));
-  if (p.aux != p.main) {
+  if (p.main != caller) {
+    TSG_HIP(ctx, hipEventRecord(ctx->ev_join[0], p.main));
+    TSG_HIP(ctx, hipStreamWaitEvent(caller, ctx->ev_join[0], 0));
+  }
+  if (p.aux != p.main && p.aux != caller) {
     TSG_HIP(ctx, hipEventRecord(ctx->ev_join[1], p.aux));
     TSG_HIP(ctx, hipStreamWaitEvent(caller, ctx->ev_join[1], 0));
   }
   return TSG_OK;
+}
+
+bool co_resident(tsg_ctx* ctx, const void* a, int nt_a, const void* b, int nt_b) {
+  const auto key = std::make_pair(a, b);
+  auto it = ctx->co_res.find(key);
+  if (it != ctx->co_res.end()) return it->second;
+  hipFuncAttributes fa, fb;
+  bool ok = hipFuncGetAttributes(&fa, a) == hipSuccess && hipFuncGetAttributes(&fb, b) == hipSuccess;
+  if (ok) {
+    // Registers: a workgroup's waves are spread over the CU's 4 SIMDs; each
+    // SIMD holds 512 registers per lane, allocated in granules of 8.
+    auto regs = [](const hipFuncAttributes& f, int nt) {
+      const int waves_per_simd = ((nt + 63) / 64 + 3) / 4;
+      return ((f.numRegs + 7) / 8) * 8 * waves_per_simd;
+    };
+    ok = regs(fa, nt_a) + regs(fb, nt_b) <= 512 &&
+         fa.sharedSizeBytes + fb.sharedSizeBytes <= (size_t)160 * 1024;
+  }
+  (void)hipGetLastError();
+  ctx->co_res[key] = ok;
+  return ok;
 }
 
 void time_reset(tsg_ctx* ctx) { ctx->ran[0] = ctx->ran[1] = false; }

@@ -61,13 +61,16 @@ __device__ __forceinline__ void sig_publish_lane(uint64_t* s, uint32_t epoch, ui
 }
 
 // n producers share one signal: each arrives once on the 32-bit arrival
-// counter `cnt` (acquire-release fetch-add, so the last arriver has acquired
-// every other arriver's release); the last one resets the counter for the
-// next call and publishes {epoch | n} with release ordering.  One lane.
+// counter `cnt` with a release fetch-add; the last one to arrive acquires
+// (a fence after reading the count of n - 1, which synchronises with every
+// earlier arriver's release), resets the counter for the next call and
+// publishes {epoch | n} with release ordering.  Only the last arriver pays
+// for the acquire, which invalidates its XCD's caches.  One lane.
 __device__ __forceinline__ void sig_arrive_counted_lane(uint32_t* cnt, uint64_t* s, uint32_t n,
                                                         uint32_t epoch) {
-  const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_ACQ_REL, TSG_SIG_SCOPE);
+  const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELEASE, TSG_SIG_SCOPE);
   if (old == n - 1) {
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
     __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, TSG_SIG_SCOPE);
     __hip_atomic_store(s, sig_target(epoch, n), __ATOMIC_RELEASE, TSG_SIG_SCOPE);
   }
@@ -84,13 +87,14 @@ __device__ __forceinline__ void block_release_fence() {
   __syncthreads();
 }
 
-// Wave-level wait: every lane of the calling wave executes this with the same
+// Wave-level poll: every lane of the calling wave executes this with the same
 // arguments.  Lane 0 polls the signal (system-scope atomic load) and the value
 // is broadcast to the wave with readfirstlane, so the loop stays uniform.
-// Bounded: after sa.spin_ticks the error word gets ERR_TIMEOUT and the wait
-// returns; once that bit is set, later waits return immediately, so a missing
-// producer turns into an error instead of a hang.
-__device__ __forceinline__ void wave_wait_ge(const uint64_t* s, uint64_t target,
+// Bounded: after sa.spin_ticks the error word gets ERR_TIMEOUT and the poll
+// returns; once that bit is set, later polls return immediately, so a missing
+// producer turns into an error instead of a hang.  No acquire: the caller
+// follows it with the fence its data needs (wave_wait_ge below).
+__device__ __forceinline__ void wave_poll_ge(const uint64_t* s, uint64_t target,
                                              const SyncArgs& sa) {
   const int lane = __lane_id();
   uint64_t v = 0;
@@ -117,6 +121,12 @@ __device__ __forceinline__ void wave_wait_ge(const uint64_t* s, uint64_t target,
       }
     }
   }
+}
+
+// Wave-level wait: poll, then acquire at agent scope.
+__device__ __forceinline__ void wave_wait_ge(const uint64_t* s, uint64_t target,
+                                             const SyncArgs& sa) {
+  wave_poll_ge(s, target, sa);
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
@@ -144,7 +154,16 @@ __device__ __forceinline__ int xcd_remap(int w, int G, int per_xcd) {
   return v * wave + (r & 7) * per_xcd + (r >> 3);
 }
 
-// Timeline record: {kind<<56 | id, t_start, t_ready, t_end}.
+// Where the calling wave runs: XCD (bits 8..11), shader engine (4..6) and
+// CU within it (0..3), from the HW_ID and XCC_ID hardware registers.
+__device__ __forceinline__ uint32_t hw_where() {
+  const uint32_t hw = __builtin_amdgcn_s_getreg((31 << 11) | 4);   // HW_ID, all 32 bits
+  const uint32_t xcc = __builtin_amdgcn_s_getreg((3 << 11) | 20);  // XCC_ID, bits 0..3
+  return (xcc & 0xFu) << 8 | ((hw >> 13) & 0x7u) << 4 | ((hw >> 8) & 0xFu);
+}
+
+// Timeline record: {kind<<56 | where<<32 | id, t_start, t_start + ticks spent
+// in signal waits, t_end}.
 struct Timeline {
   uint64_t* buf;     // 4 x cap words, or null
   uint32_t* count;   // number of records written
@@ -157,7 +176,7 @@ __device__ __forceinline__ void timeline_put(const Timeline& tl, uint32_t kind, 
   const uint32_t i = atomicAdd(tl.count, 1u);
   if (i < tl.cap) {
     uint64_t* r = tl.buf + 4ull * i;
-    r[0] = ((uint64_t)kind << 56) | id;
+    r[0] = ((uint64_t)kind << 56) | ((uint64_t)hw_where() << 32) | id;
     r[1] = t0;
     r[2] = t1;
     r[3] = t2;

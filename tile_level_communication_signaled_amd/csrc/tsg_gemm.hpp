@@ -26,7 +26,8 @@
 // fragment gives lane l column (l mod 32) and, in register v, row
 // 8*(v / 4) + 4*(l / 32) + (v mod 4).
 //
-// Rows beyond M read a valid row instead (their results are never stored);
+// Rows beyond M read a stand-in row of the operand instead (their results are
+// never stored);
 // columns beyond N read zeros (N must be a multiple of 8).  The main path
 // needs K to be a multiple of 128; the fallback path (A staged through
 // registers too, one step of prefetch) zero-fills k beyond K (K a multiple of
@@ -102,6 +103,10 @@ struct ARowsLinear {
     const int g = row0 + r;
     return g < M ? (int64_t)g * ld : (int64_t)-1;
   }
+  // Row read in place of rows outside the operand: the operand's last row,
+  // which belongs to the tile, so it is covered by whatever the tile waited
+  // for before loading.
+  __device__ __forceinline__ int64_t stand_in() const { return (int64_t)(M - 1) * ld; }
 };
 
 // Gathered rows: idx[r] is the source row index (or < 0 for no row).
@@ -113,6 +118,14 @@ struct ARowsGather {
     const int g = idx[r];
     return g >= 0 ? (int64_t)g * ld : (int64_t)-1;
   }
+  __device__ __forceinline__ int64_t stand_in() const { return 0; }
+};
+
+// Called with the first K column k0 of every step, in increasing order, just
+// before that step's A loads are issued: a consumer whose A arrives in column
+// slabs waits there for the slab's signal.
+struct NoHook {
+  __device__ __forceinline__ void before_a(int) {}
 };
 
 template <class Cfg>
@@ -240,10 +253,11 @@ struct GemmTile {
   // unrolled by two, has no exit in its middle): A global -> LDS directly,
   // three A stages.
   // LDS layout: [A0 A1 A2 B0 B1], Cfg::LDS_DIRECT bytes.
-  template <class ARows>
+  template <class ARows, class Hook = NoHook>
   __device__ __forceinline__ static void run_direct(const ARows& ar,
                                                     const uint16_t* __restrict__ B, int64_t ldb,
-                                                    int col0, int N, int K, char* lds, Acc& acc) {
+                                                    int col0, int N, int K, char* lds, Acc& acc,
+                                                    Hook hook = Hook()) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     char* const lds_a = lds;
@@ -260,7 +274,7 @@ struct GemmTile {
       const int b = wave + t * Cfg::NW;
       const int r = b * 8 + (lane >> 3);
       int64_t off = (b < Cfg::A_BLK) ? ar.row(r) : (int64_t)0;
-      if (off < 0) off = 0;  // outside the operand: read a valid row, result never stored
+      if (off < 0) off = ar.stand_in();  // outside the operand: result never stored
       a_off[t] = (uint32_t)((off + lds_pos(r, lane & 7) * 8) * 2);
     }
     auto issue_a = [&](int stage, int k0) {
@@ -280,9 +294,11 @@ struct GemmTile {
 
     const int nk = K / Cfg::BK;
     BRegs r0, r1;
+    hook.before_a(0);
     issue_a(0, 0);
     load_b<false>(r0, ba, B, ldb, K, 0);
     if (nk > 1) {
+      hook.before_a(Cfg::BK);
       issue_a(1, Cfg::BK);
       load_b<false>(r1, ba, B, ldb, K, Cfg::BK);
     }
@@ -299,6 +315,7 @@ struct GemmTile {
     for (int kt = 0; kt < nk; kt += 2) {
       const int sa2 = sa >= 1 ? sa - 1 : 2;   // (kt + 2) % 3
       if (kt + 2 < nk) {
+        hook.before_a((kt + 2) * Cfg::BK);
         issue_a(sa2, (kt + 2) * Cfg::BK);
         load_b<false>(r0, ba, B, ldb, K, (kt + 2) * Cfg::BK);
       }
@@ -308,6 +325,7 @@ struct GemmTile {
       __syncthreads();
       const int sa1 = sa == 2 ? 0 : sa + 1;   // (kt + 1) % 3
       if (kt + 3 < nk) {
+        hook.before_a((kt + 3) * Cfg::BK);
         issue_a(sa, (kt + 3) * Cfg::BK);       // (kt + 3) % 3 == kt % 3
         load_b<false>(r1, ba, B, ldb, K, (kt + 3) * Cfg::BK);
       }
@@ -321,10 +339,10 @@ struct GemmTile {
 
   // Fallback path (any K multiple of 8): A and B staged through registers,
   // one step of prefetch, two LDS stages.  LDS layout: [A0 B0 A1 B1].
-  template <class ARows>
+  template <class ARows, class Hook = NoHook>
   __device__ __forceinline__ static void run_regs(const ARows& ar, const uint16_t* __restrict__ B,
                                                   int64_t ldb, int col0, int N, int K, char* lds,
-                                                  Acc& acc) {
+                                                  Acc& acc, Hook hook = Hook()) {
     const int tid = threadIdx.x;
     zero(acc);
     constexpr int STAGE = Cfg::A_STAGE + Cfg::B_STAGE;
@@ -356,12 +374,16 @@ struct GemmTile {
       store_b(rb, la + Cfg::A_STAGE);
     };
     const int nk = (K + Cfg::BK - 1) / Cfg::BK;
+    hook.before_a(0);
     load(0);
     store(0);
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
       const int cur = kt & 1;
-      if (kt + 1 < nk) load((kt + 1) * Cfg::BK);
+      if (kt + 1 < nk) {
+        hook.before_a((kt + 1) * Cfg::BK);
+        load((kt + 1) * Cfg::BK);
+      }
       compute(lds + cur * STAGE, lds + cur * STAGE + Cfg::A_STAGE, acc);
       if (kt + 1 < nk) store(cur ^ 1);
       __syncthreads();

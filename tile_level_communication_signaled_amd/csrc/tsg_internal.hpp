@@ -40,6 +40,7 @@ struct tsg_ctx {
 
   bool probed = false;
   int n_xcd = 0;
+  std::map<std::pair<const void*, const void*>, bool> co_res;  // co_resident() cache
 
   std::string err;
 };
@@ -66,19 +67,28 @@ struct Opts {
   uint32_t timeout_ms;
   uint32_t skip_mask;
   int timeline;
+  int aux_wgs;   // 0 = the op's default
+  int comm_tile; // 0 = the op's default
 };
 Opts resolve(const tsg_opts* o, int default_aux_cus);
 
 // Producer / consumer streams for one call.  In split mode they are CU-masked
 // to disjoint CU sets (consumer CUs spread evenly over the XCDs); in shared
-// mode both are unmasked.
+// mode both are unmasked, and when `caller` is given the main kernel runs on
+// the caller's stream itself (no fork or join for it).
 struct Pair {
   hipStream_t main;
   hipStream_t aux;
   int main_cus;
   int aux_cus;
 };
-tsg_status streams(tsg_ctx* ctx, const Opts& o, Pair* out);
+tsg_status streams(tsg_ctx* ctx, const Opts& o, Pair* out, hipStream_t caller = nullptr);
+
+// True when one workgroup of kernel `a` (nt_a threads) and one of kernel `b`
+// fit on one CU together: registers of their waves on each SIMD and LDS.
+// Kernels whose workgroups cannot share a CU must not be relied on to run
+// concurrently.
+bool co_resident(tsg_ctx* ctx, const void* a, int nt_a, const void* b, int nt_b);
 
 tsg::SyncArgs sync_args(tsg_ctx* ctx, const Opts& o);
 tsg::Timeline timeline(tsg_ctx* ctx, const Opts& o);
