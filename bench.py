@@ -153,22 +153,29 @@ class Timer:
         self.torch, self.tsg, self.ctx, self.fn = torch, tsg, ctx, fn
 
     def run(self, mode, n, warmup=2, kernels=()):
+        """Median call ms over n calls (no per-kernel events in these calls),
+        then, if asked, median kernel ms over n further calls that record the
+        library's per-kernel events."""
         torch, tsg, ctx = self.torch, self.tsg, self.ctx
         for i in range(warmup):
             self.fn(i, mode)
         if ctx.check() != tsg.OK:
             raise RuntimeError(ctx.last_error())
-        ctx.enable_kernel_timing(bool(kernels))
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-        kms = {k: [] for k in kernels}
         for i in range(n):
             ev[i][0].record()
             self.fn(i, mode)
             ev[i][1].record()
-            for k in kernels:
-                kms[k].append(ctx.kernel_ms(k))
         torch.cuda.synchronize()
-        ctx.enable_kernel_timing(False)
+        kms = {k: [] for k in kernels}
+        if kernels:
+            ctx.enable_kernel_timing(True)
+            for i in range(n):
+                self.fn(i, mode)
+                for k in kernels:
+                    kms[k].append(ctx.kernel_ms(k))
+            torch.cuda.synchronize()
+            ctx.enable_kernel_timing(False)
         if ctx.check() != tsg.OK:
             raise RuntimeError(ctx.last_error())
         ms = sorted(a.elapsed_time(b) for a, b in ev)

@@ -17,9 +17,10 @@
 //
 // GELU is the exact form 0.5 z (1 + erf(z / sqrt 2)) on the fp32 accumulator
 // (erff of the device math library), rounded to bf16 (nearest even): H is the
-// bf16 operand of GEMM2.  The two kernels sit on a CU split (default 192 / 64)
-// or share every CU, with the persistent consumer bounded to 64 workgroups so
-// that the producer always keeps most of the GPU.
+// bf16 operand of GEMM2.  By default (shared CUs) both layers run in one
+// persistent kernel fed by a ticket queue (mlp_fused_kernel); with a CU
+// split the two kernels run concurrently on disjoint CU sets, GEMM2 as a
+// persistent consumer.
 #include "tsg_gemm.hpp"
 #include "tsg_internal.hpp"
 
@@ -40,7 +41,8 @@ struct Mlp1Args {
   SyncArgs sa;
   Timeline tl;
   int M, K1, N1;
-  int n_tiles_n;
+  int n_tiles_n, n_tiles_m;
+  int group;              // tile rows per group of the grouped order
   int per_xcd;
   uint32_t arrivals;      // GEMM1 tiles per row block (= n_tiles_n)
   uint32_t skip_mask;     // row blocks whose signal is never completed (test hook)
@@ -50,7 +52,8 @@ template <class Cfg, bool DIRECT>
 __global__ void __launch_bounds__(Cfg::NT) mlp_gemm1_kernel(const Mlp1Args a) {
   __shared__ __attribute__((aligned(16))) char lds[DIRECT ? Cfg::LDS_DIRECT : Cfg::LDS_REGS];
   const int t = xcd_remap(blockIdx.x, gridDim.x, a.per_xcd);
-  const int mt = t / a.n_tiles_n, nt = t % a.n_tiles_n;
+  int mt, nt;
+  grouped_tile(t, a.n_tiles_m, a.n_tiles_n, a.group, mt, nt);
   const int row0 = mt * Cfg::BM, col0 = nt * Cfg::BN;
   const uint64_t t0 = a.tl.buf ? wall_clock64() : 0;
   typename GemmTile<Cfg>::Acc acc;
@@ -87,6 +90,8 @@ struct Mlp2Args {
   Timeline tl;
   int M, N1, N2;
   int n_tiles_n, n_tiles;
+  int group;              // tile rows per group of the grouped order
+  int per_xcd;            // consecutive tiles per XCD (0: no remap)
   int wait;
   uint32_t arrivals;
 };
@@ -96,8 +101,11 @@ struct Mlp2Args {
 template <class Cfg, bool DIRECT>
 __global__ void __launch_bounds__(Cfg::NT) mlp_gemm2_kernel(const Mlp2Args a) {
   __shared__ __attribute__((aligned(16))) char lds[DIRECT ? Cfg::LDS_DIRECT : Cfg::LDS_REGS];
-  for (int t = blockIdx.x; t < a.n_tiles; t += gridDim.x) {
-    const int mt = t / a.n_tiles_n, nt = t % a.n_tiles_n;
+  for (int tp = blockIdx.x; tp < a.n_tiles; tp += gridDim.x) {
+    // with a grid that is a multiple of 8, index tp runs on XCD tp mod 8
+    const int t = xcd_remap(tp, a.n_tiles, a.per_xcd);
+    int mt, nt;
+    grouped_tile(t, a.n_tiles / a.n_tiles_n, a.n_tiles_n, a.group, mt, nt);
     const int row0 = mt * Cfg::BM, col0 = nt * Cfg::BN;
     const uint64_t t0 = a.tl.buf ? wall_clock64() : 0;
     if (a.wait) {
@@ -123,10 +131,148 @@ __global__ void __launch_bounds__(Cfg::NT) mlp_gemm2_kernel(const Mlp2Args a) {
   }
 }
 
+// Both GEMMs in one persistent kernel (overlap mode on shared CUs).
+// Items are GEMM1 tiles (phase 1), then GEMM2 tiles (phase 2), each set in
+// grouped tile order and cut into 8 contiguous shares, one per XCD, so that
+// the tiles an XCD runs form a compact block of the tile grid whose operands
+// its L2 can reuse.  A workgroup reads its XCD (XCC_ID) and takes tickets
+// from its XCD's phase-1 queue, then from the other XCDs' phase-1 queues,
+// and only then from the phase-2 queues, its own first.  A GEMM2 tile
+// acquires the signals of its row blocks before its K loop.  No item waits
+// for a later one, and a workgroup takes a phase-2 item only once every
+// phase-1 item has been taken by a running workgroup that never waits, so the
+// queues always drain.  The last workgroup to leave resets the counters.
+struct MlpFusedArgs {
+  Mlp1Args g1;
+  Mlp2Args g2;
+  uint32_t* queues;  // 2 phases x 8 XCD ticket counters, then an exit counter
+  int n_items1;      // GEMM1 tiles
+  int n_items2;      // GEMM2 tiles
+  int n_mt2;         // GEMM2 tile rows
+};
+
+template <class C1, bool D1, class C2, bool D2>
+__global__ void __launch_bounds__(256) mlp_fused_kernel(const MlpFusedArgs f) {
+  static_assert(C1::NT == 256 && C2::NT == 256, "both tiles use 2 x 2 waves");
+  constexpr int L1 = D1 ? C1::LDS_DIRECT : C1::LDS_REGS;
+  constexpr int L2 = D2 ? C2::LDS_DIRECT : C2::LDS_REGS;
+  __shared__ __attribute__((aligned(16))) char lds[L1 > L2 ? L1 : L2];
+  const int my_xcd = (int)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & 7);  // XCC_ID
+  // The ticket goes through the first word of the tile buffer, which is free
+  // between items (a tile's last LDS read precedes its pipeline's final
+  // barrier; the next tile writes LDS only after the second barrier here).
+  // The item is made wave-uniform (readfirstlane) and the loop has a single
+  // back edge through the fetch, so its barriers stay uniform.
+  auto fetch = [&]() -> int {
+    volatile int* s_item = (volatile int*)lds;
+    if (threadIdx.x == 0) {
+      int item = -1;
+      for (int ph = 0; ph < 2 && item < 0; ++ph) {
+        const int n = ph == 0 ? f.n_items1 : f.n_items2;
+        for (int d = 0; d < 8 && item < 0; ++d) {
+          const int x = (my_xcd + d) & 7;
+          const int lo = (int)((int64_t)n * x / 8), hi = (int)((int64_t)n * (x + 1) / 8);
+          if (hi == lo) continue;
+          const uint32_t t = atomicAdd(f.queues + ph * 8 + x, 1u);
+          if (t < (uint32_t)(hi - lo)) item = (ph == 0 ? 0 : f.n_items1) + lo + (int)t;
+        }
+      }
+      *s_item = item;
+    }
+    __syncthreads();
+    const int v = __builtin_amdgcn_readfirstlane(*s_item);
+    __syncthreads();
+    return v;
+  };
+  const Mlp1Args& a = f.g1;
+  const Mlp2Args& b = f.g2;
+  for (int item = fetch(); item >= 0; item = fetch()) {
+    const uint64_t t0 = a.tl.buf ? wall_clock64() : 0;
+    if (item < f.n_items1) {
+      int mt, nt;
+      grouped_tile(item, a.n_tiles_m, a.n_tiles_n, a.group, mt, nt);
+      const int row0 = mt * C1::BM, col0 = nt * C1::BN;
+      typename GemmTile<C1>::Acc acc;
+      const ARowsLinear ar{a.x, a.K1, row0, a.M};
+      if (D1)
+        GemmTile<C1>::run_direct(ar, a.w1, a.N1, col0, a.N1, a.K1, lds, acc);
+      else
+        GemmTile<C1>::run_regs(ar, a.w1, a.N1, col0, a.N1, a.K1, lds, acc);
+      const int M = a.M, N1 = a.N1;
+      uint16_t* H = a.h;
+      GemmTile<C1>::for_each(acc, [&](int r, int c, float z) {
+        const int gr = row0 + r, gc = col0 + c;
+        if (gr < M && gc < N1) {
+          const float g = 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
+          H[(int64_t)gr * N1 + gc] = (uint16_t)f32_to_bf16(g);
+        }
+      });
+      block_release_fence();
+      if (threadIdx.x == 0) {
+        for (int rb = row0 / kRowBlock; rb * kRowBlock < min(row0 + C1::BM, a.M); ++rb) {
+          if ((a.skip_mask >> (rb & 31)) & 1u) continue;
+          sig_arrive_counted_lane(a.cnt + rb, a.sig + rb, a.arrivals, a.sa.epoch);
+        }
+        if (a.tl.buf) timeline_put(a.tl, 5, (uint32_t)(mt << 16 | nt), t0, t0, wall_clock64());
+      }
+    } else {
+      int mt, nt;
+      grouped_tile(item - f.n_items1, f.n_mt2, b.n_tiles_n, b.group, mt, nt);
+      const int row0 = mt * C2::BM, col0 = nt * C2::BN;
+      const uint64_t target = sig_target(b.sa.epoch, b.arrivals);
+      for (int rb = row0 / kRowBlock; rb * kRowBlock < min(row0 + C2::BM, b.M); ++rb)
+        block_wait_ge(b.sig + rb, target, b.sa);
+      const uint64_t t1 = b.tl.buf ? wall_clock64() : 0;
+      typename GemmTile<C2>::Acc acc;
+      const ARowsLinear ar{b.h, b.N1, row0, b.M};
+      if (D2)
+        GemmTile<C2>::run_direct(ar, b.w2, b.N2, col0, b.N2, b.N1, lds, acc);
+      else
+        GemmTile<C2>::run_regs(ar, b.w2, b.N2, col0, b.N2, b.N1, lds, acc);
+      const int M = b.M, N2 = b.N2;
+      float* Y = b.y;
+      GemmTile<C2>::for_each(acc, [&](int r, int c, float v) {
+        const int gr = row0 + r, gc = col0 + c;
+        if (gr < M && gc < N2) Y[(int64_t)gr * N2 + gc] = v;
+      });
+      if (b.tl.buf && threadIdx.x == 0) timeline_put(b.tl, 6, (uint32_t)(mt << 16 | nt), t0, t1, wall_clock64());
+    }
+  }
+  // last one out resets the ticket counters for the next call
+  if (threadIdx.x == 0 && atomicAdd(f.queues + 16, 1u) == gridDim.x - 1)
+    for (int i = 0; i <= 16; ++i) __hip_atomic_store(f.queues + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 using Cfg1 = TileCfg<256, 256, 2, 2>;
 using Cfg3 = TileCfg<128, 128, 2, 2>;
 using Cfg4 = TileCfg<256, 128, 2, 2>;
 using Cfg5 = TileCfg<128, 256, 2, 2>;
+
+template <class C1, class C2>
+hipError_t launch_fused_cfg(const MlpFusedArgs& f, int grid, hipStream_t s) {
+  const bool d1 = f.g1.K1 % (2 * C1::BK) == 0, d2 = f.g2.N1 % (2 * C2::BK) == 0;
+  if (d1 && d2)
+    hipLaunchKernelGGL((mlp_fused_kernel<C1, true, C2, true>), dim3(grid), dim3(256), 0, s, f);
+  else if (d1)
+    hipLaunchKernelGGL((mlp_fused_kernel<C1, true, C2, false>), dim3(grid), dim3(256), 0, s, f);
+  else if (d2)
+    hipLaunchKernelGGL((mlp_fused_kernel<C1, false, C2, true>), dim3(grid), dim3(256), 0, s, f);
+  else
+    hipLaunchKernelGGL((mlp_fused_kernel<C1, false, C2, false>), dim3(grid), dim3(256), 0, s, f);
+  return hipGetLastError();
+}
+
+// Tile pairs the fused kernel is built for: (GEMM1 tile, GEMM2 tile).
+bool fused_supported(int t1, int t2) {
+  return (t1 == 5 && t2 == 1) || (t1 == 5 && t2 == 5) || (t1 == 3 && t2 == 3);
+}
+
+hipError_t launch_fused(int t1, int t2, const MlpFusedArgs& f, int grid, hipStream_t s) {
+  if (t1 == 5 && t2 == 1) return launch_fused_cfg<Cfg5, Cfg1>(f, grid, s);
+  if (t1 == 5 && t2 == 5) return launch_fused_cfg<Cfg5, Cfg5>(f, grid, s);
+  if (t1 == 3 && t2 == 3) return launch_fused_cfg<Cfg3, Cfg3>(f, grid, s);
+  return hipErrorInvalidValue;
+}
 
 struct TileShape {
   int bm, bn;
@@ -200,9 +346,10 @@ tsg_status tsg_op_mlp2(tsg_ctx* ctx, const void* x, const void* w1, void* h, con
   const int n_rb = (M + kRowBlock - 1) / kRowBlock;
   if (n_rb > kMaxRowBlocks) return fail(ctx, TSG_E_UNSUPPORTED, "M exceeds %d rows", kMaxRowBlocks * kRowBlock);
 
-  const Opts o = resolve(opts, 64);
-  const int tile1 = o.tile ? o.tile : 5;  // 128 x 256 for GEMM1
-  const int tile2 = o.tile ? o.tile : 1;  // 256 x 256 for GEMM2
+  const Opts o = resolve(opts, -1);
+  const bool small = M < 1024 || N1 < 1024 || N2 < 1024;
+  const int tile1 = o.tile ? o.tile : (small ? 3 : 5);  // 128 x 256 for GEMM1
+  const int tile2 = o.tile ? o.tile : (small ? 3 : (o.order == 5 ? 5 : 1));  // 256 x 256 for GEMM2
   const TileShape s1 = shape_of(tile1), s2 = shape_of(tile2);
   if (!s1.bm || !s2.bm) return fail(ctx, TSG_E_INVALID, "tile id %d is not available for mlp2_pipelined", o.tile);
 
@@ -225,6 +372,8 @@ tsg_status tsg_op_mlp2(tsg_ctx* ctx, const void* x, const void* w1, void* h, con
   a1.K1 = K1;
   a1.N1 = N1;
   a1.n_tiles_n = n_nt1;
+  a1.n_tiles_m = n_mt1;
+  a1.group = 8;
   a1.arrivals = (uint32_t)n_nt1;
   a1.skip_mask = o.skip_mask;
   Mlp2Args a2;
@@ -239,6 +388,7 @@ tsg_status tsg_op_mlp2(tsg_ctx* ctx, const void* x, const void* w1, void* h, con
   a2.N2 = N2;
   a2.n_tiles_n = n_nt2;
   a2.n_tiles = n_mt2 * n_nt2;
+  a2.group = 8;
   a2.arrivals = (uint32_t)n_nt1;
   if (o.timeline) TSG_HIP(ctx, hipMemsetAsync(ctx->d_timeline_n, 0, sizeof(uint32_t), caller));
 
@@ -251,8 +401,10 @@ tsg_status tsg_op_mlp2(tsg_ctx* ctx, const void* x, const void* w1, void* h, con
   };
   auto gemm2 = [&](hipStream_t s, int nwg, int wait) -> tsg_status {
     a2.wait = wait;
+    nwg = std::max(1, std::min(nwg, a2.n_tiles));
+    a2.per_xcd = nwg % 8 == 0 ? nwg / 8 : 0;
     time_begin(ctx, 1, s);
-    hipError_t e = launch2(tile2, a2, std::max(1, std::min(nwg, a2.n_tiles)), s);
+    hipError_t e = launch2(tile2, a2, nwg, s);
     time_end(ctx, 1, s);
     return e == hipSuccess ? TSG_OK : hip_fail(ctx, e, "mlp_gemm2_kernel");
   };
@@ -263,13 +415,31 @@ tsg_status tsg_op_mlp2(tsg_ctx* ctx, const void* x, const void* w1, void* h, con
     if (st == TSG_OK) st = gemm2(caller, a2.n_tiles, mode == TSG_MODE_SERIAL ? 1 : 0);
     return st;
   }
+  if (o.aux_cus < 0 && fused_supported(tile1, tile2)) {
+    // Shared CUs: both layers in one persistent kernel on the caller's stream.
+    MlpFusedArgs f;
+    f.g1 = a1;
+    f.g2 = a2;
+    f.g2.wait = 1;
+    f.g2.per_xcd = 0;
+    f.g1.per_xcd = 0;
+    f.n_items1 = n_mt1 * n_nt1;
+    f.n_items2 = a2.n_tiles;
+    f.n_mt2 = n_mt2;
+    const int nwg = o.aux_wgs > 0 ? o.aux_wgs : ctx->n_cus;
+    f.queues = ctx->d_queue + 16;
+    time_begin(ctx, 0, caller);
+    hipError_t e = launch_fused(tile1, tile2, f, nwg, caller);
+    time_end(ctx, 0, caller);
+    return e == hipSuccess ? TSG_OK : hip_fail(ctx, e, "mlp_fused_kernel");
+  }
   Pair pr;
   st = streams(ctx, o, &pr);
   if (st != TSG_OK) return st;
   // The consumer is persistent with one workgroup per CU of its partition
   // (64 in shared mode), so waiting consumer workgroups can never occupy the
   // whole GPU.
-  const int nwg2 = o.aux_cus < 0 ? 64 : pr.aux_cus;
+  const int nwg2 = o.aux_wgs > 0 ? o.aux_wgs : (o.aux_cus < 0 ? 64 : pr.aux_cus);
   st = fork(ctx, caller, pr);
   if (st != TSG_OK) return st;
   st = gemm1(pr.main, pr.main_cus);

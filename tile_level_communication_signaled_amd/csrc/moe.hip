@@ -24,12 +24,15 @@
 //      its row block.  Then every "down" tile (rb, 256 columns of H): acquire
 //      the row block's signal (all up tiles of rb done), y = h w_down[e] in
 //      fp32 into the staging buffer, release the tile's ready signal.
-//   3. moe_combine_kernel (persistent, consumer partition): walks the down
-//      tiles in queue order, acquires each ready signal, and for every token
-//      whose other routed row lies in an earlier tile (acquiring that tile's
-//      signal too) writes out[t] = fl(fl(g0 y0) + fl(g1 y1)) in slot order.
-//      Every token is written exactly once, by the later of its two tiles:
-//      no atomics and no zero-fill of out.
+//   3. The combine (combine_unit), per down tile in queue order: acquire
+//      its ready signal, and for every token whose other routed row lies in
+//      this or an earlier tile (acquiring that tile's signal too) write
+//      out[t] = fl(fl(g0 y0) + fl(g1 y1)) in slot order.  Every token is
+//      written exactly once, by the later of its two tiles: no atomics and no
+//      zero-fill of out.  In overlap mode on shared CUs the combine units are
+//      queue items of the producer itself, after the down tiles, so they run
+//      on any CU as soon as their tiles are ready; with a CU split they run
+//      in moe_combine_kernel, a persistent consumer on its own partition.
 #include "tsg_gemm.hpp"
 #include "tsg_internal.hpp"
 
@@ -40,6 +43,7 @@ namespace {
 constexpr int BM = 128;                 // row padding unit and tile rows
 constexpr int BN_UP = 128;
 constexpr int BN_DN = 256;
+constexpr int kCombMaxRb = 4096;         // row blocks the combine's partner list can name
 constexpr int kRouteThreads = 256;
 constexpr int kMaxExperts = 256;
 constexpr size_t kSigH = size_t(1) << 19;          // h row-block signals
@@ -195,6 +199,18 @@ __global__ void __launch_bounds__(kRouteThreads) moe_route_kernel(const RouteArg
 }
 
 // --------------------------------------------------------------- producer
+struct CombArgs {
+  const float* topk_w;
+  float* out;
+  Ws ws;
+  const uint64_t* sig_ready;
+  SyncArgs sa;
+  Timeline tl;
+  int H, k;
+  int n_dn_nt, n_rb_max;
+  int wait;
+};
+
 struct ProdArgs {
   const uint16_t* x;
   const uint16_t* w_up;
@@ -210,10 +226,150 @@ struct ProdArgs {
   int T, H, I;
   int n_up_nt, n_dn_nt;
   int n_rb_max;
-  int n_items;
+  int n_items;            // up + down tiles, then (fused mode) combine units
+  int n_prod_items;       // up + down tiles
+  CombArgs comb;          // combine units run as queue items after the down tiles
   uint32_t skip_mask;     // row blocks (mod 32) whose up tiles never arrive (test hook)
 };
 
+
+// ---------------------------------------------------------------- combine
+
+// Combine consumer.  Unit = one down tile (128 rows x BN_DN columns of y),
+// in the producer's order (row block major).  A token is combined by the
+// later of the two row blocks holding its slots, so every token is written
+// exactly once: out[t] = g0 * y(slot 0) + g1 * y(slot 1), products and sum
+// rounded in that order (an absent slot contributes 0).
+//   1. Threads 0..127 read the routing of the unit's rows (pair, partner
+//      row, token, gates) into LDS, and list the partner row blocks that
+//      precede this one (their tiles must be ready too), once each.
+//   2. Wave 0 reads every listed partner tile's signal in one load per 64,
+//      polls only those not yet published, and the workgroup acquires.
+//   3. Each wave takes 32 rows: eight rows at a time it issues all sixteen
+//      16-byte loads of y (both slots, this lane's 4 columns), then combines
+//      and stores them.
+// Called by every thread of the workgroup with uniform (rb, nt); `scratch`
+// is kCombScratch bytes of LDS owned by the caller for the call.
+constexpr int kCombScratch = 8 * BM * 4 + 16;
+
+__device__ __forceinline__ void combine_unit(const CombArgs& a, int rb, int nt, char* scratch) {
+  int* s_tok = (int*)scratch;
+  int* s_own = s_tok + BM;
+  int* s_oth = s_own + BM;
+  float* s_g0 = (float*)(s_oth + BM);
+  float* s_g1 = s_g0 + BM;
+  uint32_t* s_seen = (uint32_t*)(s_g1 + BM);   // kCombMaxRb bits
+  int* s_list = (int*)(s_seen + BM);
+  int* s_nlist = s_list + BM;
+  static_assert(kCombMaxRb / 32 <= BM, "partner bitmap must fit its LDS slot");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint64_t t0 = a.tl.buf ? wall_clock64() : 0;
+  const uint64_t target = sig_target(a.sa.epoch, 1);
+  if (a.wait && threadIdx.x < 64) wave_poll_ge(a.sig_ready + (int64_t)rb * a.n_dn_nt + nt, target, a.sa);
+  for (int i = threadIdx.x; i < kCombMaxRb / 32; i += blockDim.x) s_seen[i] = 0u;
+  if (threadIdx.x == 0) *s_nlist = 0;
+  __syncthreads();
+  if (threadIdx.x < BM) {
+    const int row = rb * BM + threadIdx.x;
+    const int p = a.ws.row_pair[row];
+    int tok = -1, own = -1, oth = -1;
+    float g0 = 0.f, g1 = 0.f;
+    if (p >= 0) {
+      const int pr = a.ws.pair_row[p ^ 1];   // the token's other slot (k == 2)
+      const int prb = pr >= 0 ? pr / BM : -1;
+      if (prb <= rb) {                       // else the later tile combines this token
+        tok = p / a.k;
+        own = (p & 1) ? pr : row;            // row of slot 0 (-1: slot dropped)
+        oth = (p & 1) ? row : pr;            // row of slot 1
+        g0 = a.topk_w[(int64_t)tok * a.k];
+        g1 = a.topk_w[(int64_t)tok * a.k + 1];
+        if (prb >= 0 && prb < rb) {
+          const uint32_t bit = 1u << (prb & 31);
+          if (!(atomicOr(&s_seen[prb >> 5], bit) & bit)) s_list[atomicAdd(s_nlist, 1)] = prb;
+        }
+      }
+    }
+    s_tok[threadIdx.x] = tok;
+    s_own[threadIdx.x] = own;
+    s_oth[threadIdx.x] = oth;
+    s_g0[threadIdx.x] = g0;
+    s_g1[threadIdx.x] = g1;
+  }
+  __syncthreads();
+  if (a.wait && threadIdx.x < 64) {
+    const int nl = __builtin_amdgcn_readfirstlane(*s_nlist);
+    for (int i0 = 0; i0 < nl; i0 += 64) {
+      const int i = i0 + lane;
+      uint64_t v = ~0ull;
+      int prb = 0;
+      if (i < nl) {
+        prb = s_list[i];
+        v = __hip_atomic_load(a.sig_ready + (int64_t)prb * a.n_dn_nt + nt, __ATOMIC_RELAXED, TSG_SIG_SCOPE);
+      }
+      uint64_t pending = __builtin_amdgcn_ballot_w64(v < target);
+      while (pending) {
+        const int l = (int)__builtin_ctzll(pending);
+        pending &= pending - 1;
+        const int q = __builtin_amdgcn_readlane(prb, l);
+        wave_poll_ge(a.sig_ready + (int64_t)q * a.n_dn_nt + nt, target, a.sa);
+      }
+    }
+  }
+  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  const uint64_t t1 = a.tl.buf ? wall_clock64() : 0;
+  const int col = nt * BN_DN + lane * 4;
+  const bool col_ok = col < a.H;
+#pragma unroll 1
+  for (int g = 0; g < 4; ++g) {
+    const int j0 = wave * 32 + g * 8;
+    float4 v0[8], v1[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int own = s_own[j0 + j], oth = s_oth[j0 + j];
+      v0[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      v1[j] = v0[j];
+      if (s_tok[j0 + j] >= 0 && col_ok) {
+        if (own >= 0) v0[j] = *(const float4*)(a.ws.y + (int64_t)own * a.H + col);
+        if (oth >= 0) v1[j] = *(const float4*)(a.ws.y + (int64_t)oth * a.H + col);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int tok = s_tok[j0 + j];
+      if (tok >= 0 && col_ok) {
+        const float g0 = s_g0[j0 + j], g1 = s_g1[j0 + j];
+        float4 o;
+        o.x = __fadd_rn(__fmul_rn(g0, v0[j].x), __fmul_rn(g1, v1[j].x));
+        o.y = __fadd_rn(__fmul_rn(g0, v0[j].y), __fmul_rn(g1, v1[j].y));
+        o.z = __fadd_rn(__fmul_rn(g0, v0[j].z), __fmul_rn(g1, v1[j].z));
+        o.w = __fadd_rn(__fmul_rn(g0, v0[j].w), __fmul_rn(g1, v1[j].w));
+        *(float4*)(a.out + (int64_t)tok * a.H + col) = o;
+      }
+    }
+  }
+  if (a.tl.buf && threadIdx.x == 0) timeline_put(a.tl, 9, (uint32_t)(rb << 16 | nt), t0, t1, wall_clock64());
+  __syncthreads();  // LDS routing of this unit fully read before the caller reuses it
+}
+
+// Combine kernel (serial, combine-only and CU-split modes).  The unit loop is
+// uniform: its trip values come from kernel arguments or are read first-lane.
+__global__ void __launch_bounds__(256) moe_combine_kernel(const CombArgs a) {
+  __shared__ __attribute__((aligned(16))) char scratch[kCombScratch];
+  const int n_rb = __builtin_amdgcn_readfirstlane(a.ws.meta[0]);
+  const int n_units = a.n_rb_max * a.n_dn_nt;
+  for (int u = blockIdx.x; u < n_units; u += gridDim.x) {
+    const int rb = u / a.n_dn_nt, nt = u % a.n_dn_nt;
+    if (rb >= n_rb) break;                   // units are rb-major: the rest are empty too
+    combine_unit(a, rb, nt, scratch);
+  }
+}
+
+// Persistent producer: up tiles, then down tiles, then (fused mode) the
+// combine units, all from one ticket queue.  Every item waits only for
+// earlier items (down tiles for their row block's up tiles, combine units for
+// down tiles), which running workgroups took before it and complete without
+// waiting on later ones.
 template <bool DIRECT_UP, bool DIRECT_DN>
 __global__ void __launch_bounds__(256) moe_producer_kernel(const ProdArgs a) {
   constexpr int LUP = DIRECT_UP ? CfgUp::LDS_DIRECT : CfgUp::LDS_REGS;
@@ -238,136 +394,65 @@ __global__ void __launch_bounds__(256) moe_producer_kernel(const ProdArgs a) {
   };
   for (int item = fetch(); item < a.n_items; item = fetch()) {
     const uint64_t t0 = a.tl.buf ? wall_clock64() : 0;
-    const bool up = item < n_up;
-    const int rb = up ? item / a.n_up_nt : (item - n_up) / a.n_dn_nt;
-    const int nt = up ? item % a.n_up_nt : (item - n_up) % a.n_dn_nt;
-    if (rb < n_rb && up) {
-      const int e = __builtin_amdgcn_readfirstlane(a.ws.rb_expert[rb]);
-      const int col0 = nt * BN_UP;
-      typename GemmTile<CfgUp>::Acc acc;
-      const ARowsGather ar{a.x, a.H, a.ws.row_token + (int64_t)rb * BM};
-      const uint16_t* B = a.w_up + (int64_t)e * a.H * a.I;
-      if (DIRECT_UP)
-        GemmTile<CfgUp>::run_direct(ar, B, a.I, col0, a.I, a.H, lds, acc);
-      else
-        GemmTile<CfgUp>::run_regs(ar, B, a.I, col0, a.I, a.H, lds, acc);
-      const int I = a.I;
-      uint16_t* hrow = a.ws.h + (int64_t)rb * BM * I;
-      GemmTile<CfgUp>::for_each(acc, [&](int r, int c, float u) {
-        const int gc = col0 + c;
-        if (gc < I) hrow[(int64_t)r * I + gc] = (uint16_t)f32_to_bf16(u / (1.0f + expf(-u)));
-      });
-      block_release_fence();
-      if (threadIdx.x == 0) {
-        if (!((a.skip_mask >> (rb & 31)) & 1u))
-          sig_arrive_counted_lane(a.cnt_h + rb, a.sig_h + rb, (uint32_t)a.n_up_nt, a.sa.epoch);
-        if (a.tl.buf) timeline_put(a.tl, 7, (uint32_t)(rb << 16 | nt), t0, t0, wall_clock64());
-      }
-    } else if (rb < n_rb) {
-      const int e = __builtin_amdgcn_readfirstlane(a.ws.rb_expert[rb]);
-      const int col0 = nt * BN_DN;
-      block_wait_ge(a.sig_h + rb, sig_target(a.sa.epoch, (uint32_t)a.n_up_nt), a.sa);
-      const uint64_t t1 = a.tl.buf ? wall_clock64() : 0;
-      typename GemmTile<CfgDn>::Acc acc;
-      const ARowsLinear ar{a.ws.h, a.I, rb * BM, a.n_rb_max * BM};
-      const uint16_t* B = a.w_down + (int64_t)e * a.I * a.H;
-      if (DIRECT_DN)
-        GemmTile<CfgDn>::run_direct(ar, B, a.H, col0, a.H, a.I, lds, acc);
-      else
-        GemmTile<CfgDn>::run_regs(ar, B, a.H, col0, a.H, a.I, lds, acc);
-      // rows past the expert's last pair are padding: not stored
-      const int valid = __builtin_amdgcn_readfirstlane(
-          min(BM, a.ws.offs[e + 1] - a.ws.offs[e] - (rb * BM - a.ws.poffs[e])));
-      const int H = a.H;
-      float* yrow = a.ws.y + (int64_t)rb * BM * H;
-      GemmTile<CfgDn>::for_each(acc, [&](int r, int c, float v) {
-        const int gc = col0 + c;
-        if (r < valid && gc < H) yrow[(int64_t)r * H + gc] = v;
-      });
-      block_release_fence();
-      if (threadIdx.x == 0) {
-        sig_publish_lane(a.sig_ready + (int64_t)rb * a.n_dn_nt + nt, a.sa.epoch, 1);
-        if (a.tl.buf) timeline_put(a.tl, 8, (uint32_t)(rb << 16 | nt), t0, t1, wall_clock64());
-      }
-    }
-  }
-}
-
-// ---------------------------------------------------------------- combine
-struct CombArgs {
-  const float* topk_w;
-  float* out;
-  Ws ws;
-  const uint64_t* sig_ready;
-  SyncArgs sa;
-  Timeline tl;
-  int H, k;
-  int n_dn_nt, n_rb_max;
-  int wait;
-};
-
-// Each wave takes 32 rows of the tile, 8 at a time: resolve the 8 rows'
-// pairs and partners, acquire the partners' tiles, issue all loads, then
-// combine and store (lane l owns float4 column l of the 256-column tile).
-__global__ void __launch_bounds__(256) moe_combine_kernel(const CombArgs a) {
-  // uniform (see the producer): the unit loop contains a barrier
-  const int n_rb = __builtin_amdgcn_readfirstlane(a.ws.meta[0]);
-  const int n_units = a.n_rb_max * a.n_dn_nt;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int u = blockIdx.x; u < n_units; u += gridDim.x) {
-    const int rb = u / a.n_dn_nt, nt = u % a.n_dn_nt;
-    if (rb >= n_rb) break;                   // units are rb-major: the rest are empty too
-    const uint64_t t0 = a.tl.buf ? wall_clock64() : 0;
-    if (a.wait) block_wait_ge(a.sig_ready + (int64_t)rb * a.n_dn_nt + nt, sig_target(a.sa.epoch, 1), a.sa);
-    const uint64_t t1 = a.tl.buf ? wall_clock64() : 0;
-    const int col = nt * BN_DN + lane * 4;
-    const bool col_ok = col < a.H;
-    for (int g = 0; g < 4; ++g) {
-      const int r0 = rb * BM + wave * 32 + g * 8;
-      int tok[8], own[8], oth[8];
-      bool act[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int p = __builtin_amdgcn_readfirstlane(a.ws.row_pair[r0 + j]);
-        act[j] = false;
-        tok[j] = -1;
-        if (p < 0) continue;
-        const int q = p ^ 1;                 // the token's other slot (k == 2)
-        const int pr = __builtin_amdgcn_readfirstlane(a.ws.pair_row[q]);
-        const int prb = pr >= 0 ? pr / BM : -1;
-        if (prb > rb) continue;              // the later tile combines this token
-        if (prb >= 0 && a.wait)
-          wave_wait_ge(a.sig_ready + (int64_t)prb * a.n_dn_nt + nt, sig_target(a.sa.epoch, 1), a.sa);
-        act[j] = true;
-        tok[j] = p / a.k;
-        // own = row of slot 0, oth = row of slot 1 (-1: that slot was dropped)
-        own[j] = (p & 1) ? pr : r0 + j;
-        oth[j] = (p & 1) ? r0 + j : pr;
-      }
-      float4 v0[8], v1[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        v0[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-        v1[j] = v0[j];
-        if (act[j] && col_ok) {
-          if (own[j] >= 0) v0[j] = *(const float4*)(a.ws.y + (int64_t)own[j] * a.H + col);
-          if (oth[j] >= 0) v1[j] = *(const float4*)(a.ws.y + (int64_t)oth[j] * a.H + col);
+    // no `continue`: the loop keeps a single back edge through the fetch
+    if (item >= a.n_prod_items) {            // combine unit (fused mode)
+      const int cu = item - a.n_prod_items;
+      const int rb = cu / a.n_dn_nt, nt = cu % a.n_dn_nt;
+      if (rb < n_rb) combine_unit(a.comb, rb, nt, lds);
+    } else {
+      const bool up = item < n_up;
+      const int rb = up ? item / a.n_up_nt : (item - n_up) / a.n_dn_nt;
+      const int nt = up ? item % a.n_up_nt : (item - n_up) % a.n_dn_nt;
+      if (rb < n_rb && up) {
+        const int e = __builtin_amdgcn_readfirstlane(a.ws.rb_expert[rb]);
+        const int col0 = nt * BN_UP;
+        typename GemmTile<CfgUp>::Acc acc;
+        const ARowsGather ar{a.x, a.H, a.ws.row_token + (int64_t)rb * BM};
+        const uint16_t* B = a.w_up + (int64_t)e * a.H * a.I;
+        if (DIRECT_UP)
+          GemmTile<CfgUp>::run_direct(ar, B, a.I, col0, a.I, a.H, lds, acc);
+        else
+          GemmTile<CfgUp>::run_regs(ar, B, a.I, col0, a.I, a.H, lds, acc);
+        const int I = a.I;
+        uint16_t* hrow = a.ws.h + (int64_t)rb * BM * I;
+        GemmTile<CfgUp>::for_each(acc, [&](int r, int c, float u) {
+          const int gc = col0 + c;
+          if (gc < I) hrow[(int64_t)r * I + gc] = (uint16_t)f32_to_bf16(u / (1.0f + expf(-u)));
+        });
+        block_release_fence();
+        if (threadIdx.x == 0) {
+          if (!((a.skip_mask >> (rb & 31)) & 1u))
+            sig_arrive_counted_lane(a.cnt_h + rb, a.sig_h + rb, (uint32_t)a.n_up_nt, a.sa.epoch);
+          if (a.tl.buf) timeline_put(a.tl, 7, (uint32_t)(rb << 16 | nt), t0, t0, wall_clock64());
         }
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (act[j] && col_ok) {
-          const float g0 = a.topk_w[(int64_t)tok[j] * a.k], g1 = a.topk_w[(int64_t)tok[j] * a.k + 1];
-          float4 o;
-          o.x = __fadd_rn(__fmul_rn(g0, v0[j].x), __fmul_rn(g1, v1[j].x));
-          o.y = __fadd_rn(__fmul_rn(g0, v0[j].y), __fmul_rn(g1, v1[j].y));
-          o.z = __fadd_rn(__fmul_rn(g0, v0[j].z), __fmul_rn(g1, v1[j].z));
-          o.w = __fadd_rn(__fmul_rn(g0, v0[j].w), __fmul_rn(g1, v1[j].w));
-          *(float4*)(a.out + (int64_t)tok[j] * a.H + col) = o;
+      } else if (rb < n_rb) {
+        const int e = __builtin_amdgcn_readfirstlane(a.ws.rb_expert[rb]);
+        const int col0 = nt * BN_DN;
+        block_wait_ge(a.sig_h + rb, sig_target(a.sa.epoch, (uint32_t)a.n_up_nt), a.sa);
+        const uint64_t t1 = a.tl.buf ? wall_clock64() : 0;
+        typename GemmTile<CfgDn>::Acc acc;
+        const ARowsLinear ar{a.ws.h, a.I, rb * BM, a.n_rb_max * BM};
+        const uint16_t* B = a.w_down + (int64_t)e * a.I * a.H;
+        if (DIRECT_DN)
+          GemmTile<CfgDn>::run_direct(ar, B, a.H, col0, a.H, a.I, lds, acc);
+        else
+          GemmTile<CfgDn>::run_regs(ar, B, a.H, col0, a.H, a.I, lds, acc);
+        // rows past the expert's last pair are padding: not stored
+        const int valid = __builtin_amdgcn_readfirstlane(
+            min(BM, a.ws.offs[e + 1] - a.ws.offs[e] - (rb * BM - a.ws.poffs[e])));
+        const int H = a.H;
+        float* yrow = a.ws.y + (int64_t)rb * BM * H;
+        GemmTile<CfgDn>::for_each(acc, [&](int r, int c, float v) {
+          const int gc = col0 + c;
+          if (r < valid && gc < H) yrow[(int64_t)r * H + gc] = v;
+        });
+        block_release_fence();
+        if (threadIdx.x == 0) {
+          sig_publish_lane(a.sig_ready + (int64_t)rb * a.n_dn_nt + nt, a.sa.epoch, 1);
+          if (a.tl.buf) timeline_put(a.tl, 8, (uint32_t)(rb << 16 | nt), t0, t1, wall_clock64());
         }
       }
     }
-    if (a.tl.buf && threadIdx.x == 0) timeline_put(a.tl, 9, (uint32_t)(rb << 16 | nt), t0, t1, wall_clock64());
   }
 }
 
@@ -405,11 +490,13 @@ tsg_status tsg_op_moe(tsg_ctx* ctx, const void* x, const int32_t* topk_ids, cons
       L.rows_max * I * 2 >= (int64_t(1) << 32))
     return fail(ctx, TSG_E_UNSUPPORTED, "operands of 4 GiB or more are not supported");
   const int n_up_nt = (I + BN_UP - 1) / BN_UP, n_dn_nt = (H + BN_DN - 1) / BN_DN;
+  if (L.n_rb_max > kCombMaxRb)
+    return fail(ctx, TSG_E_UNSUPPORTED, "moe_expert_combine: more than %d row blocks", kCombMaxRb);
   if ((size_t)L.n_rb_max > kSigReady - kSigH || (size_t)L.n_rb_max * n_dn_nt > kSigEnd - kSigReady ||
       kSigEnd > ctx->n_sig)
     return fail(ctx, TSG_E_UNSUPPORTED, "too many tiles for the signal pool");
 
-  const Opts o = resolve(opts, 16);
+  const Opts o = resolve(opts, -1);
   TSG_HIP(ctx, hipSetDevice(ctx->device));
   hipStream_t caller = (hipStream_t)stream;
   ++ctx->epoch;
@@ -448,7 +535,8 @@ tsg_status tsg_op_moe(tsg_ctx* ctx, const void* x, const int32_t* topk_ids, cons
   pa.n_up_nt = n_up_nt;
   pa.n_dn_nt = n_dn_nt;
   pa.n_rb_max = (int)L.n_rb_max;
-  pa.n_items = (int)(L.n_rb_max * (n_up_nt + n_dn_nt));
+  pa.n_prod_items = (int)(L.n_rb_max * (n_up_nt + n_dn_nt));
+  pa.n_items = pa.n_prod_items;
   pa.skip_mask = o.skip_mask;
 
   CombArgs ca;
@@ -492,6 +580,13 @@ tsg_status tsg_op_moe(tsg_ctx* ctx, const void* x, const int32_t* topk_ids, cons
   tsg_status st = TSG_OK;
   if (mode != TSG_MODE_COMM_ONLY) st = route();
   if (st != TSG_OK) return st;
+  if (mode == TSG_MODE_OVERLAP && o.aux_cus < 0) {
+    // Shared CUs: the combine units are queue items of the producer itself.
+    ca.wait = 1;
+    pa.comb = ca;
+    pa.n_items = pa.n_prod_items + (int)(L.n_rb_max * n_dn_nt);
+    return produce(caller, o.aux_wgs > 0 ? o.aux_wgs : ctx->n_cus);
+  }
   if (mode == TSG_MODE_SERIAL || mode == TSG_MODE_COMPUTE_ONLY) {
     st = produce(caller, ctx->n_cus);
     if (st == TSG_OK && mode == TSG_MODE_SERIAL) st = combine(caller, ctx->n_cus * 2, 1);
@@ -500,7 +595,7 @@ tsg_status tsg_op_moe(tsg_ctx* ctx, const void* x, const int32_t* topk_ids, cons
   Pair pr;
   st = streams(ctx, o, &pr);
   if (st != TSG_OK) return st;
-  const int nwg_c = o.aux_cus < 0 ? 64 : pr.aux_cus * 2;
+  const int nwg_c = o.aux_wgs > 0 ? o.aux_wgs : (o.aux_cus < 0 ? 64 : pr.aux_cus * 4);
   st = fork(ctx, caller, pr);
   if (st != TSG_OK) return st;
   // Producer first, consumer second: the producer's only waits are on its own

@@ -37,7 +37,8 @@ struct RsGemmArgs {
   SyncArgs sa;
   Timeline tl;
   int M, N, K;
-  int n_tiles_n;
+  int n_tiles_n, n_tiles_m;
+  int group;              // tile rows per group of the grouped order
   int n_ftn;             // 128-column signal tiles per row of signals
   int per_xcd;
   int chunk_rows;
@@ -49,8 +50,9 @@ template <class Cfg, bool DIRECT>
 __global__ void __launch_bounds__(Cfg::NT) rs_gemm_kernel(const RsGemmArgs args) {
   __shared__ __attribute__((aligned(16))) char lds[DIRECT ? Cfg::LDS_DIRECT : Cfg::LDS_REGS];
   const int t = xcd_remap(blockIdx.x, gridDim.x, args.per_xcd);
-  const int mt = args.mt_order[t / args.n_tiles_n];
-  const int nt = t % args.n_tiles_n;
+  int ml, nt;
+  grouped_tile(t, args.n_tiles_m, args.n_tiles_n, args.group, ml, nt);
+  const int mt = args.mt_order[ml];
   const int row0 = mt * Cfg::BM, col0 = nt * Cfg::BN;
   const uint64_t t0 = args.tl.buf ? wall_clock64() : 0;
   typename GemmTile<Cfg>::Acc acc;
@@ -100,57 +102,78 @@ struct RsReduceArgs {
 };
 
 // Work unit: 16 rows x 128 columns of one 128 x 128 signal tile of the
-// local chunk; thread (ry, cx) owns rows ry and ry + 8 at float4 column cx
-// and loads both rows of four peers at a time before summing them (eight
-// 16-byte loads in flight per thread, few enough registers to share a SIMD
-// with a GEMM wave).  Workgroup g takes units g, g + G, ...;
-// the 8 units of a tile are consecutive, so they follow the producer's
-// (row-major) tile order and only the first wait on a tile can spin.
+// local chunk; thread (ry, cx) owns rows ry and ry + 8 at float4 column cx.
+// Workgroup g owns units g, g + G, ... and runs two phases over them.
+//   Phase 1 (no wait): out = sum of the R - 1 peers' partials, ascending
+//   rank, four peers (eight 16-byte loads) in flight at a time.
+//   Phase 2 (in unit order, which follows the producer's tile order):
+//   acquire the tile's done signal, then out += the local partial.
+// Phase 1 depends on nothing the GEMM computes, so it runs beside the
+// GEMM's first tiles; only the last third of the traffic waits for them.
+// Every thread re-reads exactly the elements it stored, so the two phases
+// need no synchronisation between threads.  Summation order per element:
+// peers in ascending rank order, then the local partial.
 __global__ void __launch_bounds__(256) rs_reduce_kernel(const RsReduceArgs a) {
+  constexpr int P_MAX = 4;  // peers per load batch (eight 16-byte loads in flight)
   const int n_units = a.n_ftm * a.n_ftn * 8;
   const int c0 = a.rank * a.chunk_rows, c1 = c0 + a.chunk_rows;
   const int cx = threadIdx.x & 31;
   const int ry = threadIdx.x >> 5;
-  for (int u = blockIdx.x; u < n_units; u += gridDim.x) {
+  auto where = [&](int u, int& ftm, int& ftn, int& r0, int& col) {
     const int tile = u >> 3, part = u & 7;
-    const int ftm = a.ftm0 + tile / a.n_ftn, ftn = tile % a.n_ftn;
-    const int col = ftn * kFlagTile + cx * 4;
-    const int r0 = ftm * kFlagTile + part * 16 + ry, r1 = r0 + 8;
+    ftm = a.ftm0 + tile / a.n_ftn;
+    ftn = tile % a.n_ftn;
+    col = ftn * kFlagTile + cx * 4;
+    r0 = ftm * kFlagTile + part * 16 + ry;
+  };
+  for (int u = blockIdx.x; u < n_units; u += gridDim.x) {
+    int ftm, ftn, r0, col;
+    where(u, ftm, ftn, r0, col);
+    const int r1 = r0 + 8;
     const bool ok0 = col < a.N && r0 >= c0 && r0 < c1;
     const bool ok1 = col < a.N && r1 >= c0 && r1 < c1;
-    const uint64_t t0 = a.tl.buf ? wall_clock64() : 0;
-    float4 v0[4], v1[4];
     float4 s0 = make_float4(0.f, 0.f, 0.f, 0.f), s1 = s0;
-    // peers in ascending rank order (the local rank is skipped)
-    for (int p0 = 0; p0 < a.R - 1; p0 += 4) {
-      const int np = min(4, a.R - 1 - p0);
+    for (int p0 = 0; p0 < a.R - 1; p0 += P_MAX) {
+      const int np = min(P_MAX, a.R - 1 - p0);
+      float4 v0[P_MAX], v1[P_MAX];
+      // uniform peer base + 32-bit element offsets (a chunk is < 2^31 elements)
+      const uint32_t o0 = (uint32_t)((r0 - c0) * a.N + col), o1 = o0 + 8u * (uint32_t)a.N;
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
+      for (int p = 0; p < P_MAX; ++p) {
         if (p < np) {
           const float* pp = a.peers + (int64_t)(p0 + p) * a.chunk_rows * a.N;
-          if (ok0) v0[p] = *(const float4*)(pp + (int64_t)(r0 - c0) * a.N + col);
-          if (ok1) v1[p] = *(const float4*)(pp + (int64_t)(r1 - c0) * a.N + col);
+          if (ok0) v0[p] = *(const float4*)(pp + o0);
+          if (ok1) v1[p] = *(const float4*)(pp + o1);
         }
       }
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
+      for (int p = 0; p < P_MAX; ++p) {
         if (p < np) {
           if (ok0) { s0.x += v0[p].x; s0.y += v0[p].y; s0.z += v0[p].z; s0.w += v0[p].w; }
           if (ok1) { s1.x += v1[p].x; s1.y += v1[p].y; s1.z += v1[p].z; s1.w += v1[p].w; }
         }
       }
     }
+    if (ok0) *(float4*)(a.out + (int64_t)(r0 - c0) * a.N + col) = s0;
+    if (ok1) *(float4*)(a.out + (int64_t)(r1 - c0) * a.N + col) = s1;
+  }
+  for (int u = blockIdx.x; u < n_units; u += gridDim.x) {
+    int ftm, ftn, r0, col;
+    where(u, ftm, ftn, r0, col);
+    const int r1 = r0 + 8;
+    const bool ok0 = col < a.N && r0 >= c0 && r0 < c1;
+    const bool ok1 = col < a.N && r1 >= c0 && r1 < c1;
+    const uint64_t t0 = a.tl.buf ? wall_clock64() : 0;
     if (a.wait) block_wait_ge(a.flags + (int64_t)ftm * a.n_ftn + ftn, sig_target(a.sa.epoch, 1), a.sa);
     const uint64_t t1 = a.tl.buf ? wall_clock64() : 0;
-    if (ok0) {
-      const float4 q = *(const float4*)(a.partial + (int64_t)r0 * a.N + col);
-      *(float4*)(a.out + (int64_t)(r0 - c0) * a.N + col) = make_float4(s0.x + q.x, s0.y + q.y, s0.z + q.z, s0.w + q.w);
-    }
-    if (ok1) {
-      const float4 q = *(const float4*)(a.partial + (int64_t)r1 * a.N + col);
-      *(float4*)(a.out + (int64_t)(r1 - c0) * a.N + col) = make_float4(s1.x + q.x, s1.y + q.y, s1.z + q.z, s1.w + q.w);
-    }
-    if (a.tl.buf && threadIdx.x == 0 && part == 0)
+    float4 q0, q1, o0, o1;
+    float* d0 = a.out + (int64_t)(r0 - c0) * a.N + col;
+    float* d1 = a.out + (int64_t)(r1 - c0) * a.N + col;
+    if (ok0) { q0 = *(const float4*)(a.partial + (int64_t)r0 * a.N + col); o0 = *(const float4*)d0; }
+    if (ok1) { q1 = *(const float4*)(a.partial + (int64_t)r1 * a.N + col); o1 = *(const float4*)d1; }
+    if (ok0) *(float4*)d0 = make_float4(o0.x + q0.x, o0.y + q0.y, o0.z + q0.z, o0.w + q0.w);
+    if (ok1) *(float4*)d1 = make_float4(o1.x + q1.x, o1.y + q1.y, o1.z + q1.z, o1.w + q1.w);
+    if (a.tl.buf && threadIdx.x == 0 && (u & 7) == 0)
       timeline_put(a.tl, 4, (uint32_t)(ftm << 16 | ftn), t0, t1, wall_clock64());
   }
 }
@@ -183,6 +206,21 @@ hipError_t launch_cfg(const RsGemmArgs& a, int grid, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <class Cfg>
+const void* fn_cfg(bool direct) {
+  return direct ? (const void*)&rs_gemm_kernel<Cfg, true> : (const void*)&rs_gemm_kernel<Cfg, false>;
+}
+
+const void* gemm_fn(int id, bool direct) {
+  switch (id) {
+    case 1: return fn_cfg<Cfg1>(direct);
+    case 3: return fn_cfg<Cfg3>(direct);
+    case 4: return fn_cfg<Cfg4>(direct);
+    case 5: return fn_cfg<Cfg5>(direct);
+    default: return nullptr;
+  }
+}
+
 hipError_t launch_gemm(int id, const RsGemmArgs& a, int grid, hipStream_t s) {
   switch (id) {
     case 1: return launch_cfg<Cfg1>(a, grid, s);
@@ -209,6 +247,8 @@ tsg_status tsg_op_rs(tsg_ctx* ctx, const void* x, const void* w, float* partial,
   if (!aligned16(x) || !aligned16(w) || !aligned16(partial) || !aligned16(out) ||
       (peer_partials && !aligned16(peer_partials)))
     return fail(ctx, TSG_E_ALIGN, "gemm_rs_overlap: pointers must be 16-byte aligned");
+  if ((int64_t)(M / R) * N >= (int64_t(1) << 31))
+    return fail(ctx, TSG_E_UNSUPPORTED, "gemm_rs_overlap: a chunk of 2^31 elements or more is not supported");
   if ((int64_t)M * K * 2 >= (int64_t(1) << 32) || (int64_t)K * N * 2 >= (int64_t(1) << 32))
     return fail(ctx, TSG_E_UNSUPPORTED, "operands of 4 GiB or more are not supported");
 
@@ -239,6 +279,8 @@ tsg_status tsg_op_rs(tsg_ctx* ctx, const void* x, const void* w, float* partial,
   ga.N = N;
   ga.K = K;
   ga.n_tiles_n = n_nt;
+  ga.n_tiles_m = n_mt;
+  ga.group = 8;
   ga.n_ftn = n_ftn;
   ga.chunk_rows = chunk_rows;
   ga.skip_mask = o.skip_mask;
@@ -291,17 +333,25 @@ tsg_status tsg_op_rs(tsg_ctx* ctx, const void* x, const void* w, float* partial,
   };
 
   tsg_status st = TSG_OK;
-  if (mode == TSG_MODE_SERIAL) {
+  if (mode == TSG_MODE_COMPUTE_ONLY) return gemm(caller, ctx->n_cus);
+  // In shared mode the GEMM runs on the caller's stream and the reduce on a
+  // side stream, one workgroup per CU beside the GEMM's; when the two cannot
+  // share a CU they run back to back instead.
+  bool back_to_back = mode == TSG_MODE_SERIAL;
+  if (mode == TSG_MODE_OVERLAP && o.aux_cus < 0) {
+    const bool direct = K % 128 == 0;
+    back_to_back = !co_resident(ctx, gemm_fn(tile, direct), 256 /* 2 x 2 waves */, (const void*)&rs_reduce_kernel, 256);
+  }
+  if (back_to_back) {
     st = gemm(caller, ctx->n_cus);
-    if (st == TSG_OK) st = reduce(caller, ctx->n_cus * 2, 1);
+    if (st == TSG_OK) st = reduce(caller, o.aux_wgs > 0 ? o.aux_wgs : ctx->n_cus * 2, 1);
     return st;
   }
-  if (mode == TSG_MODE_COMPUTE_ONLY) return gemm(caller, ctx->n_cus);
 
   Pair pr;
-  st = streams(ctx, o, &pr);
+  st = streams(ctx, o, &pr, caller);
   if (st != TSG_OK) return st;
-  const int nwg = o.aux_cus < 0 ? ctx->n_cus : pr.aux_cus * 2;
+  const int nwg = o.aux_wgs > 0 ? o.aux_wgs : (o.aux_cus < 0 ? ctx->n_cus : pr.aux_cus * 2);
   st = fork(ctx, caller, pr);
   if (st != TSG_OK) return st;
   // Producer (GEMM) first, consumer (reduce) second: the GEMM never waits.

@@ -162,6 +162,21 @@ __device__ __forceinline__ uint32_t hw_where() {
   return (xcc & 0xFu) << 8 | ((hw >> 13) & 0x7u) << 4 | ((hw >> 8) & 0xFu);
 }
 
+// Grouped tile order: logical tile t -> tile (m, n), walking groups of G
+// tile rows column by column.  A run of consecutive logical tiles (one XCD's
+// share after xcd_remap) then forms a near-square block of the tile grid, so
+// the operand rows and columns it reads are reused by more of the XCD's
+// tiles in its L2.  A bijection on [0, n_m * n_n) for any G >= 1.
+__device__ __forceinline__ void grouped_tile(int t, int n_m, int n_n, int G, int& m, int& n) {
+  const int per_group = G * n_n;
+  const int g = t / per_group;
+  const int first = g * G;
+  const int rows = min(G, n_m - first);
+  const int r = t - g * per_group;
+  m = first + r % rows;
+  n = r / rows;
+}
+
 // Timeline record: {kind<<56 | where<<32 | id, t_start, t_start + ticks spent
 // in signal waits, t_end}.
 struct Timeline {

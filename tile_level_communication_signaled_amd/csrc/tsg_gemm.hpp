@@ -92,6 +92,16 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// Workgroup barrier of the K pipeline.  It waits for this wave's LDS
+// accesses only, so global loads still in flight (the prefetch of later
+// steps) are not drained, as __syncthreads() (whose fence also covers the
+// direct-to-LDS loads, counted with global loads) would do.  Direct-to-LDS
+// loads a step depends on are waited for explicitly (wait_vmcnt) before it.
+// The memory clobber keeps the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Source rows of the A operand of one tile.  row(r) gives the element offset
 // of tile row r in `base`, or -1 for a row outside the operand.
 struct ARowsLinear {
@@ -247,6 +257,22 @@ struct GemmTile {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][i], bfr[ks & 1][j],
                                                                acc[i][j], 0, 0, 0);
     }
+    // Instruction order: the fragment reads of sub-step ks + 1 are spread
+    // between the MFMAs of sub-step ks, so that the LDS latency is covered by
+    // matrix work instead of being waited out before it (one wave per SIMD
+    // leaves no other wave to cover it).
+    constexpr int NR = Cfg::FM + Cfg::FN, NM = Cfg::FM * Cfg::FN;
+    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);  // reads of sub-step 0
+#pragma unroll
+    for (int ks = 0; ks < 3; ++ks) {
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      if (NM > NR) __builtin_amdgcn_sched_group_barrier(0x008, NM > NR ? NM - NR : 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
   }
 
   // Main path (K % 128 == 0, so the step count is even and the loop below,
@@ -304,7 +330,7 @@ struct GemmTile {
     }
     store_b(r0, lds_b);
     if (nk > 1) wait_vmcnt<Cfg::VM_PER_STEP>(); else wait_vmcnt<0>();
-    __syncthreads();
+    lds_barrier();
     // Step kt: A in stage kt % 3, B in stage kt % 2.  Loads of step kt + 2
     // are issued first (A into the stage step kt - 1 vacated, B into the
     // register set whose contents were stored last step); then step kt is
@@ -322,7 +348,7 @@ struct GemmTile {
       compute(lds_a + sa * Cfg::A_STAGE, lds_b, acc);
       if (kt + 1 < nk) store_b(r1, lds_b + Cfg::B_STAGE);
       if (kt + 2 < nk) wait_vmcnt<Cfg::VM_PER_STEP>(); else wait_vmcnt<0>();
-      __syncthreads();
+      lds_barrier();
       const int sa1 = sa == 2 ? 0 : sa + 1;   // (kt + 1) % 3
       if (kt + 3 < nk) {
         hook.before_a((kt + 3) * Cfg::BK);
@@ -332,7 +358,7 @@ struct GemmTile {
       compute(lds_a + sa1 * Cfg::A_STAGE, lds_b + Cfg::B_STAGE, acc);
       if (kt + 2 < nk) store_b(r0, lds_b);
       if (kt + 3 < nk) wait_vmcnt<Cfg::VM_PER_STEP>(); else wait_vmcnt<0>();
-      __syncthreads();
+      lds_barrier();
       sa = sa2;                                 // (kt + 2) % 3
     }
   }
@@ -377,7 +403,7 @@ struct GemmTile {
     hook.before_a(0);
     load(0);
     store(0);
-    __syncthreads();
+    lds_barrier();
     for (int kt = 0; kt < nk; ++kt) {
       const int cur = kt & 1;
       if (kt + 1 < nk) {
@@ -386,7 +412,7 @@ struct GemmTile {
       }
       compute(lds + cur * STAGE, lds + cur * STAGE + Cfg::A_STAGE, acc);
       if (kt + 1 < nk) store(cur ^ 1);
-      __syncthreads();
+      lds_barrier();
     }
   }
 
