@@ -351,7 +351,7 @@ tsg_status tsg_op_rs(tsg_ctx* ctx, const void* x, const void* w, float* partial,
   Pair pr;
   st = streams(ctx, o, &pr, caller);
   if (st != TSG_OK) return st;
-  const int nwg = o.aux_wgs > 0 ? o.aux_wgs : (o.aux_cus < 0 ? ctx->n_cus : pr.aux_cus * 2);
+  const int nwg = o.aux_wgs > 0 ? o.aux_wgs : (o.aux_cus < 0 ? 2 * ctx->n_cus : pr.aux_cus * 2);
   st = fork(ctx, caller, pr);
   if (st != TSG_OK) return st;
   // Producer (GEMM) first, consumer (reduce) second: the GEMM never waits.
