@@ -169,10 +169,13 @@ tsg_status tsg_timeline(tsg_ctx* ctx, uint64_t* out, size_t cap, size_t* n);
  * chunk and follow the arrival order).
  *
  * A copy kernel (the stand-in for peer arrival) writes chunk c of a_full
- * (rows [c*M/R, (c+1)*M/R)) from a_local (c == rank) or from a_peers, and
- * releases chunk c's signal; the MFMA GEMM consumer computes
- * c = a_full * b, each tile waiting (acquire) on the signals of the chunks
- * its rows span.
+ * (rows [c*M/R, (c+1)*M/R)) from a_peers in arrival order, then the local
+ * chunk from a_local, column slab by column slab (opts.comm_tile), releasing
+ * each slab's signal; the MFMA GEMM consumer computes c = a_full * b.  A tile
+ * inside the local chunk reads a_local in place and never waits; every other
+ * tile waits (acquire) for slab s of the chunks its rows span just before it
+ * loads slab s ([TL] section 3.1: communication tiles sized independently of
+ * compute tiles).
  *
  *   a_local  bf16 [M/R x K]            this rank's shard (input)
  *   a_peers  bf16 [(R-1) x M/R x K]    the other ranks' shards in ascending
@@ -186,7 +189,7 @@ tsg_status tsg_timeline(tsg_ctx* ctx, uint64_t* out, size_t cap, size_t* n);
  *                  rank+1, rank+2, ... (mod R)
  * Constraints: 1 <= R <= 32, 0 <= rank < R, M % R == 0, M >= R,
  * N % 8 == 0, K % 8 == 0, N, K >= 8 (else TSG_E_SHAPE).
- * COMPUTE_ONLY expects a_full to hold the gathered operand already. */
+ * COMPUTE_ONLY expects a_full to hold the gathered peer chunks already. */
 tsg_status gemm_ag_overlap(tsg_ctx* ctx, const void* a_local, const void* a_peers,
                            void* a_full, const void* b, void* c, int c_dtype,
                            int M, int N, int K, int R, int rank,

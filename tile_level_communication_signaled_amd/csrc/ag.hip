@@ -1,7 +1,8 @@
 // AllGather + GEMM at one rank's share.
 //
 // Producer: a copy kernel standing in for the peers' arrival.  It moves the
-// shards into the gathered buffer in arrival order (the local shard first)
+// peers' shards into the gathered buffer in arrival order, then the local
+// shard (GEMM tiles inside the local chunk read it in place and never wait),
 // and signals what it has moved ("Triton-distributed: Programming
 // Overlapping Kernels on Distributed AI Systems with the Triton Compiler",
 // section 3.2, Algorithm 2, pull mode: local copy and signal, then one copy
@@ -137,6 +138,7 @@ __global__ void __launch_bounds__(256) ag_copy_kernel(const CopyArgs a) {
 // ---------------------------------------------------------------- GEMM
 struct AgGemmArgs {
   const uint16_t* a_full;
+  const uint16_t* a_local;  // the local chunk, read in place by tiles inside it
   const uint16_t* b;
   void* c;
   uint64_t* sig;          // slab signals, c * n_slab + s
@@ -144,6 +146,7 @@ struct AgGemmArgs {
   Timeline tl;
   int M, N, K;
   int chunk_rows;
+  int rank;
   int n_tiles_n;
   int wait;               // 0: no waits (compute-only)
   uint32_t arrivals;      // arrivals that complete one slab signal
@@ -226,9 +229,12 @@ __global__ void __launch_bounds__(Cfg::NT) ag_gemm_kernel(const AgGemmArgs args)
   SlabWait hook;
   hook.active = false;
   hook.waited = 0;
-  if (args.wait) {
-    const int last = min(row0 + Cfg::BM, args.M) - 1;
-    const int c_lo = row0 / args.chunk_rows, c_hi = last / args.chunk_rows;
+  const int last = min(row0 + Cfg::BM, args.M) - 1;
+  const int c_lo = row0 / args.chunk_rows, c_hi = last / args.chunk_rows;
+  // A tile inside the local chunk reads it where it already is and waits for
+  // nothing; every other tile reads the gathered buffer behind its signals.
+  const bool local = c_lo == args.rank && c_hi == args.rank;
+  if (args.wait && !local) {
     hook.sig = args.sig;
     hook.sa = args.sa;
     hook.target = sig_target(args.sa.epoch, args.arrivals);
@@ -243,7 +249,9 @@ __global__ void __launch_bounds__(Cfg::NT) ag_gemm_kernel(const AgGemmArgs args)
   }
   const uint64_t t1 = args.tl.buf ? wall_clock64() : 0;
   typename GemmTile<Cfg>::Acc acc;
-  const ARowsLinear ar{args.a_full, args.K, row0, args.M};
+  const ARowsLinear ar = local ? ARowsLinear{args.a_local, args.K, row0 - args.rank * args.chunk_rows,
+                                             args.chunk_rows}
+                               : ARowsLinear{args.a_full, args.K, row0, args.M};
   if (DIRECT)
     GemmTile<Cfg>::run_direct(ar, args.b, args.N, col0, args.N, args.K, lds, acc, hook);
   else
@@ -479,6 +487,8 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
 
   AgGemmArgs ga;
   ga.a_full = (const uint16_t*)a_full;
+  ga.a_local = (const uint16_t*)a_local;
+  ga.rank = rank;
   ga.b = (const uint16_t*)b;
   ga.c = c;
   ga.sig = ctx->d_sig + kSigBase;
@@ -517,7 +527,16 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
   ca.cnt = ctx->d_cnt + kSigBase;
   ca.sa = ga.sa;
   ca.tl = ga.tl;
-  ca.ord = ord;
+  // The copy moves the peers' chunks in arrival order and the local chunk
+  // last: tiles inside the local chunk read it in place, so only the
+  // gathered buffer's own content (and tiles straddling it) waits for it.
+  {
+    ChunkOrder co;
+    for (int p = 0; p < kMaxRanks; ++p) co.chunk[p] = 0;
+    for (int p = 1; p < R; ++p) co.chunk[p - 1] = ord.chunk[p];
+    co.chunk[R - 1] = (int8_t)rank;
+    ca.ord = co;
+  }
   ca.k8 = K / 8;
   ca.chunk_rows = chunk_rows;
   ca.R = R;
