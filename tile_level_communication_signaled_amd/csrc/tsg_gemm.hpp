@@ -8,12 +8,13 @@
 //   * A is staged as BM rows x 8 chunks of 16 bytes (8 bf16 along k).  On the
 //     main path A goes straight from global memory to LDS (16-byte
 //     global_load_lds), through a three-stage ring, so it costs no registers.
-//   * B is staged transposed, as BN rows (one per output column n) x 8 chunks
-//     of 8 consecutive k, so that both MFMA operands are read as one 16-byte
-//     LDS load per lane.  The transpose happens in registers: each thread
-//     loads an 8 (k) x 8 (n) block with eight coalesced 16-byte row loads and
-//     repacks it with byte permutes.  Two register sets and a two-stage LDS
-//     ring keep the loads of step kt + 2 in flight while step kt is computed.
+//   * On the main path B also goes straight to LDS, row-major (64 rows of k x
+//     BN columns), through a two-stage ring, and the MFMA B fragments are read
+//     with the LDS transpose read (ds_read_b64_tr_b16), two per fragment.
+//   * On the fallback path B is staged transposed, as BN rows (one per output
+//     column n) x 8 chunks of 8 consecutive k: each thread loads an 8 (k) x
+//     8 (n) block with eight coalesced 16-byte row loads and repacks it with
+//     byte permutes.
 //   * Chunk c of LDS row r is stored at chunk position c ^ ((r / 2) mod 8), so
 //     the 16-byte reads of 16 consecutive rows (and the transposed B writes,
 //     issued in an order that alternates row parity across lanes) hit
@@ -26,9 +27,9 @@
 // fragment gives lane l column (l mod 32) and, in register v, row
 // 8*(v / 4) + 4*(l / 32) + (v mod 4).
 //
-// Rows beyond M read a stand-in row of the operand instead (their results are
-// never stored);
-// columns beyond N read zeros (N must be a multiple of 8).  The main path
+// Rows beyond M read a stand-in row of the operand instead, and columns beyond
+// N read the operand's last 8 columns (main path) or zeros (fallback path);
+// their results are never stored (N must be a multiple of 8).  The main path
 // needs K to be a multiple of 128; the fallback path (A staged through
 // registers too, one step of prefetch) zero-fills k beyond K (K a multiple of
 // 8).  The pages ask tile-level single-device kernels to coalesce global
@@ -275,15 +276,76 @@ struct GemmTile {
     __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
   }
 
-  // Main path (K % 128 == 0, so the step count is even and the loop below,
-  // unrolled by two, has no exit in its middle): A global -> LDS directly,
-  // three A stages.
+  // Fragment reads of a B stage laid out row-major, [BK rows (k)] x [BN
+  // columns (n)], with the LDS transpose read: one ds_read_b64_tr_b16 gives a
+  // lane four consecutive k of one column.  In each group of 16 lanes, lane
+  // 4i + q points at row i, columns 4q..4q+3 of a 4 x 16 block, and lane
+  // 4q + e receives column 4q + e of rows 0..3.  With the block's rows at
+  // k = 16 ks + 8 (l / 32) + 4 t and its columns at n = 16 ((l / 16) mod 2)
+  // of the fragment, lane l ends up with column (l mod 32) and k values
+  // 8 (l / 32) .. + 7 of sub-step ks (t = 0, 1): the MFMA B operand layout.
+  __device__ __forceinline__ static uint32_t tr_lane_offset(int wn0) {
+    const int lane = threadIdx.x & 63;
+    const int hi = lane >> 5, g = lane >> 4, sl = lane & 15;
+    return (uint32_t)(((8 * hi + (sl >> 2)) * Cfg::BN + wn0 + 16 * (g & 1) + 4 * (sl & 3)) * 2);
+  }
+
+  __device__ __forceinline__ static bf16x8_t read_b_tr(const char* lb, uint32_t lane_off, int ks, int j) {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    typedef short v8i16 __attribute__((ext_vector_type(8)));
+    const char* p = lb + lane_off + (ks * 16 * Cfg::BN + j * 32) * 2;
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p);
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16*)(p + 4 * Cfg::BN * 2));
+    const v8i16 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8_t, w);
+  }
+
+  // One BK step: A from a swizzled stage, B from a row-major stage.
+  __device__ __forceinline__ static void compute_tr(const char* la, const char* lb, uint32_t tr_off,
+                                                    Acc& acc) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wm0 = (wave / Cfg::WN) * Cfg::WTM;
+    const int l32 = lane & 31;
+    const int hi = lane >> 5;
+    bf16x8_t af[2][Cfg::FM], bfr[2][Cfg::FN];
+    auto rd = [&](int buf, int ks) {
+#pragma unroll
+      for (int i = 0; i < Cfg::FM; ++i)
+        af[buf][i] = *(const bf16x8_t*)(la + lds_swz(wm0 + i * 32 + l32, 2 * ks + hi));
+#pragma unroll
+      for (int j = 0; j < Cfg::FN; ++j) bfr[buf][j] = read_b_tr(lb, tr_off, ks, j);
+    };
+    rd(0, 0);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (ks + 1 < 4) rd((ks + 1) & 1, ks + 1);
+#pragma unroll
+      for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < Cfg::FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][i], bfr[ks & 1][j],
+                                                               acc[i][j], 0, 0, 0);
+    }
+  }
+
+  // Main path (K % 128 == 0): both operands go from global memory straight
+  // to LDS (16-byte global_load_lds, no registers).  A uses three stages in
+  // the swizzled layout; B two stages, row-major, read with transpose reads.
+  // Step kt: the loads of B for step kt + 1 and of A for step kt + 2 are
+  // issued first (into the stages step kt - 1 vacated), then step kt is
+  // computed; the wait then leaves only the A loads just issued in flight, so
+  // everything step kt + 1 reads has landed before the barrier.
   // LDS layout: [A0 A1 A2 B0 B1], Cfg::LDS_DIRECT bytes.
   template <class ARows, class Hook = NoHook>
   __device__ __forceinline__ static void run_direct(const ARows& ar,
                                                     const uint16_t* __restrict__ B, int64_t ldb,
                                                     int col0, int N, int K, char* lds, Acc& acc,
                                                     Hook hook = Hook()) {
+    static_assert(Cfg::B_STAGE % 1024 == 0, "a B stage must be whole 1 KB load blocks");
+    constexpr int B_BLK = Cfg::B_STAGE / 1024;
+    constexpr int B_BPW = (B_BLK + Cfg::NW - 1) / Cfg::NW;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     char* const lds_a = lds;
@@ -303,6 +365,18 @@ struct GemmTile {
       if (off < 0) off = ar.stand_in();  // outside the operand: result never stored
       a_off[t] = (uint32_t)((off + lds_pos(r, lane & 7) * 8) * 2);
     }
+    // B: 16-byte chunk c = 64 blk + lane of a stage is row c / (BN/8), column
+    // 8 (c mod (BN/8)); columns at or beyond N read the operand's last 8
+    // columns instead (their results are never stored).
+    uint32_t b_off[B_BPW];
+#pragma unroll
+    for (int t = 0; t < B_BPW; ++t) {
+      const int c = (wave + t * Cfg::NW) * 64 + lane;
+      const int row = c / (Cfg::BN / 8);
+      int col = col0 + (c % (Cfg::BN / 8)) * 8;
+      if (col >= N) col = N - 8;
+      b_off[t] = (uint32_t)(((int64_t)row * ldb + col) * 2);
+    }
     auto issue_a = [&](int stage, int k0) {
       char* la = lds_a + stage * Cfg::A_STAGE;
       const char* base = (const char*)ar.base + (int64_t)k0 * 2;  // uniform
@@ -315,51 +389,45 @@ struct GemmTile {
                                            16, 0, 0);
       }
     };
-    BAddr ba;
-    b_addr(ba, ldb, col0, N);
+    auto issue_b = [&](int stage, int k0) {
+      char* lb = lds_b + stage * Cfg::B_STAGE;
+      const char* base = (const char*)B + (int64_t)k0 * ldb * 2;  // uniform
+#pragma unroll
+      for (int t = 0; t < B_BPW; ++t) {
+        const int blk = wave + t * Cfg::NW;
+        if (blk < B_BLK)
+          __builtin_amdgcn_global_load_lds((const void*)(base + b_off[t]),
+                                           (__attribute__((address_space(3))) void*)(lb + blk * 1024),
+                                           16, 0, 0);
+      }
+    };
+    const int wn0 = (wave % Cfg::WN) * Cfg::WTN;
+    const uint32_t tr_off = tr_lane_offset(wn0);
 
     const int nk = K / Cfg::BK;
-    BRegs r0, r1;
     hook.before_a(0);
+    issue_b(0, 0);
     issue_a(0, 0);
-    load_b<false>(r0, ba, B, ldb, K, 0);
     if (nk > 1) {
       hook.before_a(Cfg::BK);
       issue_a(1, Cfg::BK);
-      load_b<false>(r1, ba, B, ldb, K, Cfg::BK);
+      wait_vmcnt<Cfg::A_BPW>();
+    } else {
+      wait_vmcnt<0>();
     }
-    store_b(r0, lds_b);
-    if (nk > 1) wait_vmcnt<Cfg::VM_PER_STEP>(); else wait_vmcnt<0>();
     lds_barrier();
-    // Step kt: A in stage kt % 3, B in stage kt % 2.  Loads of step kt + 2
-    // are issued first (A into the stage step kt - 1 vacated, B into the
-    // register set whose contents were stored last step); then step kt is
-    // computed; then step kt + 1's B is written to LDS; the wait leaves only
-    // this step's loads outstanding, so step kt + 1's A has landed before the
-    // barrier.
-    int sa = 0;
-    for (int kt = 0; kt < nk; kt += 2) {
+    int sa = 0;  // kt % 3
+    for (int kt = 0; kt < nk; ++kt) {
       const int sa2 = sa >= 1 ? sa - 1 : 2;   // (kt + 2) % 3
+      if (kt + 1 < nk) issue_b((kt + 1) & 1, (kt + 1) * Cfg::BK);
       if (kt + 2 < nk) {
         hook.before_a((kt + 2) * Cfg::BK);
         issue_a(sa2, (kt + 2) * Cfg::BK);
-        load_b<false>(r0, ba, B, ldb, K, (kt + 2) * Cfg::BK);
       }
-      compute(lds_a + sa * Cfg::A_STAGE, lds_b, acc);
-      if (kt + 1 < nk) store_b(r1, lds_b + Cfg::B_STAGE);
-      if (kt + 2 < nk) wait_vmcnt<Cfg::VM_PER_STEP>(); else wait_vmcnt<0>();
+      compute_tr(lds_a + sa * Cfg::A_STAGE, lds_b + (kt & 1) * Cfg::B_STAGE, tr_off, acc);
+      if (kt + 2 < nk) wait_vmcnt<Cfg::A_BPW>(); else wait_vmcnt<0>();
       lds_barrier();
-      const int sa1 = sa == 2 ? 0 : sa + 1;   // (kt + 1) % 3
-      if (kt + 3 < nk) {
-        hook.before_a((kt + 3) * Cfg::BK);
-        issue_a(sa, (kt + 3) * Cfg::BK);       // (kt + 3) % 3 == kt % 3
-        load_b<false>(r1, ba, B, ldb, K, (kt + 3) * Cfg::BK);
-      }
-      compute(lds_a + sa1 * Cfg::A_STAGE, lds_b + Cfg::B_STAGE, acc);
-      if (kt + 2 < nk) store_b(r0, lds_b);
-      if (kt + 3 < nk) wait_vmcnt<Cfg::VM_PER_STEP>(); else wait_vmcnt<0>();
-      lds_barrier();
-      sa = sa2;                                 // (kt + 2) % 3
+      sa = sa == 2 ? 0 : sa + 1;
     }
   }
 
