@@ -72,7 +72,7 @@ struct CopyArgs {
 // ord[p], then arrives on that slab's signal.  The first slabs are cut into
 // more pieces so that many workgroups share them: every GEMM tile needs
 // slab 0 before it can start, slab 1 soon after, and so on, while later
-// slabs have time to arrive in larger pieces, which need fewer releases.
+// slabs have time to arrive in larger pieces, which need fewer store drains and arrivals.
 __global__ void __launch_bounds__(256) ag_copy_kernel(const CopyArgs a) {
   constexpr int U = 8;  // 16-byte vectors in flight per thread
   const int vpr = 1 << a.vpr_log2;
@@ -121,15 +121,17 @@ __global__ void __launch_bounds__(256) ag_copy_kernel(const CopyArgs a) {
 #pragma unroll
         for (int q = 0; q < U; ++q) v[q] = *(const u32x4_t*)(sb + (off + q * step));
 #pragma unroll
-        for (int q = 0; q < U; ++q) *(u32x4_t*)(db + (off + q * step)) = v[q];
+        for (int q = 0; q < U; ++q) store_coherent((u32x4_t*)(db + (off + q * step)), v[q]);
       }
       for (; r < nr; r += rows_q, off += step)
-        *(u32x4_t*)(db + off) = *(const u32x4_t*)(sb + off);
+        store_coherent((u32x4_t*)(db + off), *(const u32x4_t*)(sb + off));
     }
-    block_release_fence();
+    // The piece is published without an L2 write-back: its stores went
+    // through to the coherence point (store_coherent).
+    block_coherent_complete();
     const size_t si = (size_t)c * a.n_slab + s;
     if (threadIdx.x == 0 && !((a.skip_mask >> c) & 1u))
-      sig_arrive_counted_lane(a.cnt + si, a.sig + si, (uint32_t)npc, a.sa.epoch);
+      sig_arrive_counted_coherent(a.cnt + si, a.sig + si, (uint32_t)npc, a.sa.epoch);
     if (threadIdx.x == 0 && a.tl.buf)
       timeline_put(a.tl, 1, (uint32_t)(c << 24 | s << 12 | (j & 0xfff)), t0, t0, wall_clock64());
   }
@@ -441,9 +443,9 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
       back_to_back = !co_resident(ctx, fn, nt, (const void*)&ag_copy_kernel, 256);
     }
   }
-  // Pieces: every piece ends in a release, whose L2 write-back of the dirty
-  // copy data costs tens of nanoseconds and stalls the XCD's other traffic, so
-  // body pieces are as large as the workgroup count allows (about the copy
+  // Pieces: every piece ends with the workgroup draining its stores to the
+  // coherence point before it arrives, which idles it for a memory round trip,
+  // so body pieces are as large as the workgroup count allows (about the copy
   // volume over the workgroups, between 32 KB and 128 KB).  Slab 0, which
   // every tile waits for first, is cut so that all workgroups share it; each
   // following head slab gets half as many pieces, down to the body size.

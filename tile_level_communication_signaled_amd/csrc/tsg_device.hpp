@@ -76,6 +76,41 @@ __device__ __forceinline__ void sig_arrive_counted_lane(uint32_t* cnt, uint64_t*
   }
 }
 
+// Coherent-store publication.  A store issued at signal scope writes through
+// the XCD's L2 to the device's coherence point, and the wave's store counter
+// drops only once the write is acknowledged there.  A producer whose data
+// stores are all of this kind needs no L2 write-back before its signal: once
+// every wave has waited for its stores, the data is visible to every XCD, and
+// the signal (also a signal-scope store) is ordered after it.  This avoids the
+// release's write-back of the whole L2, which serialises on the XCD and stalls
+// its other traffic, at the price of 8-byte store instructions.
+__device__ __forceinline__ void store_coherent(u32x4_t* p, u32x4_t v) {
+  uint64_t* q = (uint64_t*)p;
+  __hip_atomic_store(q, (uint64_t)v[0] | ((uint64_t)v[1] << 32), __ATOMIC_RELAXED, TSG_SIG_SCOPE);
+  __hip_atomic_store(q + 1, (uint64_t)v[2] | ((uint64_t)v[3] << 32), __ATOMIC_RELAXED, TSG_SIG_SCOPE);
+}
+
+// Whole workgroup, after its coherent stores: every wave waits until they are
+// acknowledged, then the barrier orders all waves before the lane that
+// arrives.
+__device__ __forceinline__ void block_coherent_complete() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+}
+
+// Counted arrival after block_coherent_complete(): no fence is needed, as the
+// data each arriver made visible is complete before its fetch-add, and the
+// last arriver's signal store follows its fetch-add.  One lane.
+__device__ __forceinline__ void sig_arrive_counted_coherent(uint32_t* cnt, uint64_t* s, uint32_t n,
+                                                            uint32_t epoch) {
+  const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, TSG_SIG_SCOPE);
+  if (old == n - 1) {
+    __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, TSG_SIG_SCOPE);
+    __hip_atomic_store(s, sig_target(epoch, n), __ATOMIC_RELAXED, TSG_SIG_SCOPE);
+  }
+}
+
 // Whole workgroup, before one lane publishes or arrives: every wave waits
 // until its global stores have been acknowledged by its XCD's L2, then the
 // barrier orders all waves before the publishing lane, whose release at
