@@ -213,10 +213,7 @@ struct SlabWait {
         ready_until = s + 1;
       }
     }
-    if (l1_only)
-      asm volatile("buffer_inv sc0" ::: "memory");
-    else
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    acquire_lines(l1_only);
   }
 };
 
@@ -247,7 +244,8 @@ __global__ void __launch_bounds__(Cfg::NT) ag_gemm_kernel(const AgGemmArgs args)
     hook.active = args.n_slab > 1;
     hook.l1_only = args.l1_only != 0;
     hook.ready_until = 1;
-    for (int c = c_lo; c <= c_hi; ++c) block_wait_ge(args.sig + (size_t)c * args.n_slab, hook.target, args.sa);
+    for (int c = c_lo; c <= c_hi; ++c) block_poll_ge(args.sig + (size_t)c * args.n_slab, hook.target, args.sa);
+    acquire_lines(hook.l1_only);
   }
   const uint64_t t1 = args.tl.buf ? wall_clock64() : 0;
   typename GemmTile<Cfg>::Acc acc;

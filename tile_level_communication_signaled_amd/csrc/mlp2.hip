@@ -68,14 +68,14 @@ __global__ void __launch_bounds__(Cfg::NT) mlp_gemm1_kernel(const Mlp1Args a) {
     const int gr = row0 + r, gc = col0 + c;
     if (gr < M && gc < N1) {
       const float g = 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
-      H[(int64_t)gr * N1 + gc] = (uint16_t)f32_to_bf16(g);
+      store_coherent(H + (int64_t)gr * N1 + gc, (uint16_t)f32_to_bf16(g));
     }
   });
-  block_release_fence();
+  block_coherent_complete();
   if (threadIdx.x == 0) {
     for (int b = row0 / kRowBlock; b * kRowBlock < min(row0 + Cfg::BM, M); ++b) {
       if ((a.skip_mask >> (b & 31)) & 1u) continue;
-      sig_arrive_counted_lane(a.cnt + b, a.sig + b, a.arrivals, a.sa.epoch);
+      sig_arrive_counted_coherent(a.cnt + b, a.sig + b, a.arrivals, a.sa.epoch);
     }
     if (a.tl.buf) timeline_put(a.tl, 5, (uint32_t)(mt << 16 | nt), t0, t0, wall_clock64());
   }
@@ -93,6 +93,7 @@ struct Mlp2Args {
   int group;              // tile rows per group of the grouped order
   int per_xcd;            // consecutive tiles per XCD (0: no remap)
   int wait;
+  int l1_only;            // H rows are whole 128-byte lines: acquire invalidates L1 only
   uint32_t arrivals;
 };
 
@@ -111,7 +112,8 @@ __global__ void __launch_bounds__(Cfg::NT) mlp_gemm2_kernel(const Mlp2Args a) {
     if (a.wait) {
       const uint64_t target = sig_target(a.sa.epoch, a.arrivals);
       for (int b = row0 / kRowBlock; b * kRowBlock < min(row0 + Cfg::BM, a.M); ++b)
-        block_wait_ge(a.sig + b, target, a.sa);
+        block_poll_ge(a.sig + b, target, a.sa);
+      acquire_lines(a.l1_only);
     }
     const uint64_t t1 = a.tl.buf ? wall_clock64() : 0;
     typename GemmTile<Cfg>::Acc acc;
@@ -165,19 +167,41 @@ __global__ void __launch_bounds__(256) mlp_fused_kernel(const MlpFusedArgs f) {
   // back edge through the fetch, so its barriers stay uniform.
   auto fetch = [&]() -> int {
     volatile int* s_item = (volatile int*)lds;
-    if (threadIdx.x == 0) {
+    if (threadIdx.x < 64) {
+      // Wave 0 claims the item.  Each phase: the own XCD's queue first; if
+      // that is used up, one load per queue shows which still have tickets,
+      // and only those are tried.  A failed claim proves its queue used up,
+      // so a phase is left only once all its items are taken.
+      const int lane = threadIdx.x;
       int item = -1;
       for (int ph = 0; ph < 2 && item < 0; ++ph) {
         const int n = ph == 0 ? f.n_items1 : f.n_items2;
-        for (int d = 0; d < 8 && item < 0; ++d) {
-          const int x = (my_xcd + d) & 7;
+        const int base = ph == 0 ? 0 : f.n_items1;
+        auto claim = [&](int x) {
           const int lo = (int)((int64_t)n * x / 8), hi = (int)((int64_t)n * (x + 1) / 8);
-          if (hi == lo) continue;
-          const uint32_t t = atomicAdd(f.queues + ph * 8 + x, 1u);
-          if (t < (uint32_t)(hi - lo)) item = (ph == 0 ? 0 : f.n_items1) + lo + (int)t;
+          if (hi == lo) return;
+          uint32_t t = 0;
+          if (lane == 0) t = atomicAdd(f.queues + ph * 8 + x, 1u);
+          t = __builtin_amdgcn_readfirstlane(t);
+          if (t < (uint32_t)(hi - lo)) item = base + lo + (int)t;
+        };
+        claim(my_xcd);
+        if (item < 0) {
+          bool open = false;
+          if (lane < 8 && lane != my_xcd) {
+            const int lo = (int)((int64_t)n * lane / 8), hi = (int)((int64_t)n * (lane + 1) / 8);
+            const uint32_t c = __hip_atomic_load(f.queues + ph * 8 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            open = c < (uint32_t)(hi - lo);
+          }
+          uint64_t cand = __builtin_amdgcn_ballot_w64(open);
+          while (cand != 0 && item < 0) {
+            const int x = (int)__builtin_ctzll(cand);
+            cand &= cand - 1;
+            claim(x);
+          }
         }
       }
-      *s_item = item;
+      if (lane == 0) *s_item = item;
     }
     __syncthreads();
     const int v = __builtin_amdgcn_readfirstlane(*s_item);
@@ -204,14 +228,14 @@ __global__ void __launch_bounds__(256) mlp_fused_kernel(const MlpFusedArgs f) {
         const int gr = row0 + r, gc = col0 + c;
         if (gr < M && gc < N1) {
           const float g = 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
-          H[(int64_t)gr * N1 + gc] = (uint16_t)f32_to_bf16(g);
+          store_coherent(H + (int64_t)gr * N1 + gc, (uint16_t)f32_to_bf16(g));
         }
       });
-      block_release_fence();
+      block_coherent_complete();
       if (threadIdx.x == 0) {
         for (int rb = row0 / kRowBlock; rb * kRowBlock < min(row0 + C1::BM, a.M); ++rb) {
           if ((a.skip_mask >> (rb & 31)) & 1u) continue;
-          sig_arrive_counted_lane(a.cnt + rb, a.sig + rb, a.arrivals, a.sa.epoch);
+          sig_arrive_counted_coherent(a.cnt + rb, a.sig + rb, a.arrivals, a.sa.epoch);
         }
         if (a.tl.buf) timeline_put(a.tl, 5, (uint32_t)(mt << 16 | nt), t0, t0, wall_clock64());
       }
@@ -221,7 +245,8 @@ __global__ void __launch_bounds__(256) mlp_fused_kernel(const MlpFusedArgs f) {
       const int row0 = mt * C2::BM, col0 = nt * C2::BN;
       const uint64_t target = sig_target(b.sa.epoch, b.arrivals);
       for (int rb = row0 / kRowBlock; rb * kRowBlock < min(row0 + C2::BM, b.M); ++rb)
-        block_wait_ge(b.sig + rb, target, b.sa);
+        block_poll_ge(b.sig + rb, target, b.sa);
+      acquire_lines(b.l1_only);
       const uint64_t t1 = b.tl.buf ? wall_clock64() : 0;
       typename GemmTile<C2>::Acc acc;
       const ARowsLinear ar{b.h, b.N1, row0, b.M};
@@ -390,6 +415,7 @@ tsg_status tsg_op_mlp2(tsg_ctx* ctx, const void* x, const void* w1, void* h, con
   a2.n_tiles = n_mt2 * n_nt2;
   a2.group = 8;
   a2.arrivals = (uint32_t)n_nt1;
+  a2.l1_only = ((uintptr_t)h % 128 == 0 && ((int64_t)N1 * 2) % 128 == 0) ? 1 : 0;
   if (o.timeline) TSG_HIP(ctx, hipMemsetAsync(ctx->d_timeline_n, 0, sizeof(uint32_t), caller));
 
   auto gemm1 = [&](hipStream_t s, int cus) -> tsg_status {

@@ -230,6 +230,7 @@ struct ProdArgs {
   int n_prod_items;       // up + down tiles
   CombArgs comb;          // combine units run as queue items after the down tiles
   uint32_t skip_mask;     // row blocks (mod 32) whose up tiles never arrive (test hook)
+  int h_l1_only;          // h rows are whole 128-byte lines: acquire invalidates L1 only
 };
 
 
@@ -315,8 +316,7 @@ __device__ __forceinline__ void combine_unit(const CombArgs& a, int rb, int nt, 
       }
     }
   }
-  __syncthreads();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  __syncthreads();  // y is read with coherent loads: no cache invalidation
   const uint64_t t1 = a.tl.buf ? wall_clock64() : 0;
   const int col = nt * BN_DN + lane * 4;
   const bool col_ok = col < a.H;
@@ -330,8 +330,8 @@ __device__ __forceinline__ void combine_unit(const CombArgs& a, int rb, int nt, 
       v0[j] = make_float4(0.f, 0.f, 0.f, 0.f);
       v1[j] = v0[j];
       if (s_tok[j0 + j] >= 0 && col_ok) {
-        if (own >= 0) v0[j] = *(const float4*)(a.ws.y + (int64_t)own * a.H + col);
-        if (oth >= 0) v1[j] = *(const float4*)(a.ws.y + (int64_t)oth * a.H + col);
+        if (own >= 0) v0[j] = load_coherent((const float4*)(a.ws.y + (int64_t)own * a.H + col));
+        if (oth >= 0) v1[j] = load_coherent((const float4*)(a.ws.y + (int64_t)oth * a.H + col));
       }
     }
 #pragma unroll
@@ -417,18 +417,18 @@ __global__ void __launch_bounds__(256) moe_producer_kernel(const ProdArgs a) {
         uint16_t* hrow = a.ws.h + (int64_t)rb * BM * I;
         GemmTile<CfgUp>::for_each(acc, [&](int r, int c, float u) {
           const int gc = col0 + c;
-          if (gc < I) hrow[(int64_t)r * I + gc] = (uint16_t)f32_to_bf16(u / (1.0f + expf(-u)));
+          if (gc < I) store_coherent(hrow + (int64_t)r * I + gc, (uint16_t)f32_to_bf16(u / (1.0f + expf(-u))));
         });
-        block_release_fence();
+        block_coherent_complete();
         if (threadIdx.x == 0) {
           if (!((a.skip_mask >> (rb & 31)) & 1u))
-            sig_arrive_counted_lane(a.cnt_h + rb, a.sig_h + rb, (uint32_t)a.n_up_nt, a.sa.epoch);
+            sig_arrive_counted_coherent(a.cnt_h + rb, a.sig_h + rb, (uint32_t)a.n_up_nt, a.sa.epoch);
           if (a.tl.buf) timeline_put(a.tl, 7, (uint32_t)(rb << 16 | nt), t0, t0, wall_clock64());
         }
       } else if (rb < n_rb) {
         const int e = __builtin_amdgcn_readfirstlane(a.ws.rb_expert[rb]);
         const int col0 = nt * BN_DN;
-        block_wait_ge(a.sig_h + rb, sig_target(a.sa.epoch, (uint32_t)a.n_up_nt), a.sa);
+        block_wait_lines(a.sig_h + rb, sig_target(a.sa.epoch, (uint32_t)a.n_up_nt), a.sa, a.h_l1_only != 0);
         const uint64_t t1 = a.tl.buf ? wall_clock64() : 0;
         typename GemmTile<CfgDn>::Acc acc;
         const ARowsLinear ar{a.ws.h, a.I, rb * BM, a.n_rb_max * BM};
@@ -444,11 +444,11 @@ __global__ void __launch_bounds__(256) moe_producer_kernel(const ProdArgs a) {
         float* yrow = a.ws.y + (int64_t)rb * BM * H;
         GemmTile<CfgDn>::for_each(acc, [&](int r, int c, float v) {
           const int gc = col0 + c;
-          if (r < valid && gc < H) yrow[(int64_t)r * H + gc] = v;
+          if (r < valid && gc < H) store_coherent(yrow + (int64_t)r * H + gc, v);
         });
-        block_release_fence();
+        block_coherent_complete();
         if (threadIdx.x == 0) {
-          sig_publish_lane(a.sig_ready + (int64_t)rb * a.n_dn_nt + nt, a.sa.epoch, 1);
+          sig_publish_coherent(a.sig_ready + (int64_t)rb * a.n_dn_nt + nt, a.sa.epoch, 1);
           if (a.tl.buf) timeline_put(a.tl, 8, (uint32_t)(rb << 16 | nt), t0, t1, wall_clock64());
         }
       }
@@ -538,6 +538,7 @@ tsg_status tsg_op_moe(tsg_ctx* ctx, const void* x, const int32_t* topk_ids, cons
   pa.n_prod_items = (int)(L.n_rb_max * (n_up_nt + n_dn_nt));
   pa.n_items = pa.n_prod_items;
   pa.skip_mask = o.skip_mask;
+  pa.h_l1_only = ((uintptr_t)ws.h % 128 == 0 && ((int64_t)I * 2) % 128 == 0) ? 1 : 0;
 
   CombArgs ca;
   ca.topk_w = topk_w;

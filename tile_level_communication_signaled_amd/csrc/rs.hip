@@ -65,13 +65,13 @@ __global__ void __launch_bounds__(Cfg::NT) rs_gemm_kernel(const RsGemmArgs args)
   float* P = args.partial;
   GemmTile<Cfg>::for_each(acc, [&](int r, int c, float v) {
     const int gr = row0 + r, gc = col0 + c;
-    if (gr < M && gc < N) P[(int64_t)gr * N + gc] = v;
+    if (gr < M && gc < N) store_coherent(P + (int64_t)gr * N + gc, v);
   });
-  // producer_tile_notify: one release for the whole tile, then one relaxed
-  // store per covered 128 x 128 signal.
-  block_release_fence();
+  // producer_tile_notify: the tile's stores went through to the coherence
+  // point; once every wave has them acknowledged, one store per covered
+  // 128 x 128 signal publishes it (no L2 write-back).
+  block_coherent_complete();
   if (threadIdx.x == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");
     const uint64_t v = sig_target(args.sa.epoch, 1);
     for (int i = 0; i < Cfg::BM / kFlagTile; ++i) {
       const int r = row0 + i * kFlagTile;
@@ -164,13 +164,16 @@ __global__ void __launch_bounds__(256) rs_reduce_kernel(const RsReduceArgs a) {
     const bool ok0 = col < a.N && r0 >= c0 && r0 < c1;
     const bool ok1 = col < a.N && r1 >= c0 && r1 < c1;
     const uint64_t t0 = a.tl.buf ? wall_clock64() : 0;
-    if (a.wait) block_wait_ge(a.flags + (int64_t)ftm * a.n_ftn + ftn, sig_target(a.sa.epoch, 1), a.sa);
+    // consumer_tile_wait; the partial is then read with coherent loads, so the
+    // wait needs no cache invalidation (which would also drop the L2 data of
+    // the GEMM running beside the reduce).
+    if (a.wait) block_poll_ge(a.flags + (int64_t)ftm * a.n_ftn + ftn, sig_target(a.sa.epoch, 1), a.sa);
     const uint64_t t1 = a.tl.buf ? wall_clock64() : 0;
     float4 q0, q1, o0, o1;
     float* d0 = a.out + (int64_t)(r0 - c0) * a.N + col;
     float* d1 = a.out + (int64_t)(r1 - c0) * a.N + col;
-    if (ok0) { q0 = *(const float4*)(a.partial + (int64_t)r0 * a.N + col); o0 = *(const float4*)d0; }
-    if (ok1) { q1 = *(const float4*)(a.partial + (int64_t)r1 * a.N + col); o1 = *(const float4*)d1; }
+    if (ok0) { q0 = load_coherent((const float4*)(a.partial + (int64_t)r0 * a.N + col)); o0 = *(const float4*)d0; }
+    if (ok1) { q1 = load_coherent((const float4*)(a.partial + (int64_t)r1 * a.N + col)); o1 = *(const float4*)d1; }
     if (ok0) *(float4*)d0 = make_float4(o0.x + q0.x, o0.y + q0.y, o0.z + q0.z, o0.w + q0.w);
     if (ok1) *(float4*)d1 = make_float4(o1.x + q1.x, o1.y + q1.y, o1.z + q1.z, o1.w + q1.w);
     if (a.tl.buf && threadIdx.x == 0 && (u & 7) == 0)

@@ -90,6 +90,25 @@ __device__ __forceinline__ void store_coherent(u32x4_t* p, u32x4_t v) {
   __hip_atomic_store(q + 1, (uint64_t)v[2] | ((uint64_t)v[3] << 32), __ATOMIC_RELAXED, TSG_SIG_SCOPE);
 }
 
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store((uint32_t*)p, __float_as_uint(v), __ATOMIC_RELAXED, TSG_SIG_SCOPE);
+}
+
+__device__ __forceinline__ void store_coherent(uint16_t* p, uint16_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, TSG_SIG_SCOPE);
+}
+
+// Coherent load of 16 bytes (two 64-bit relaxed atomic loads at signal
+// scope): it bypasses the caches that may hold an older copy of the line, so
+// a consumer that reads data once after a signal needs no cache invalidation.
+__device__ __forceinline__ float4 load_coherent(const float4* p) {
+  const uint64_t* q = (const uint64_t*)p;
+  const uint64_t a = __hip_atomic_load(q, __ATOMIC_RELAXED, TSG_SIG_SCOPE);
+  const uint64_t b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, TSG_SIG_SCOPE);
+  return make_float4(__uint_as_float((uint32_t)a), __uint_as_float((uint32_t)(a >> 32)),
+                     __uint_as_float((uint32_t)b), __uint_as_float((uint32_t)(b >> 32)));
+}
+
 // Whole workgroup, after its coherent stores: every wave waits until they are
 // acknowledged, then the barrier orders all waves before the lane that
 // arrives.
@@ -109,6 +128,11 @@ __device__ __forceinline__ void sig_arrive_counted_coherent(uint32_t* cnt, uint6
     __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, TSG_SIG_SCOPE);
     __hip_atomic_store(s, sig_target(epoch, n), __ATOMIC_RELAXED, TSG_SIG_SCOPE);
   }
+}
+
+// Single producer after block_coherent_complete(): publish {epoch | n}.
+__device__ __forceinline__ void sig_publish_coherent(uint64_t* s, uint32_t epoch, uint32_t n) {
+  __hip_atomic_store(s, sig_target(epoch, n), __ATOMIC_RELAXED, TSG_SIG_SCOPE);
 }
 
 // Whole workgroup, before one lane publishes or arrives: every wave waits
@@ -173,6 +197,38 @@ __device__ __forceinline__ void block_wait_ge(const uint64_t* s, uint64_t target
   if (threadIdx.x < 64) wave_wait_ge(s, target, sa);
   __syncthreads();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
+// Workgroup-level wait without an acquire: for consumers that read the
+// guarded data only with coherent loads (load_coherent), issued after the
+// barrier and therefore after the signal was seen.
+__device__ __forceinline__ void block_poll_ge(const uint64_t* s, uint64_t target,
+                                              const SyncArgs& sa) {
+  if (threadIdx.x < 64) wave_poll_ge(s, target, sa);
+  __syncthreads();
+}
+
+// Acquire for a consumer that reads guarded data with ordinary loads, per
+// wave, after the signal was seen.  Every kernel starts with caches that hold
+// no stale device data (the dispatch's acquire invalidates them), so an
+// XCD's L2 can hold an old copy of a guarded line only if something on that
+// XCD read the line earlier in the same kernel.  When the guarded regions
+// are whole 128-byte lines that nothing reads before their signal
+// (`line_exclusive`), only this CU's L1 can be stale and invalidating it is
+// enough; the L2, and with it the operands of every other workgroup on the
+// XCD, is kept.  Otherwise the acquire invalidates both.
+__device__ __forceinline__ void acquire_lines(bool line_exclusive) {
+  if (line_exclusive)
+    asm volatile("buffer_inv sc0" ::: "memory");
+  else
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
+// Workgroup-level wait followed by acquire_lines in every wave.
+__device__ __forceinline__ void block_wait_lines(const uint64_t* s, uint64_t target,
+                                                 const SyncArgs& sa, bool line_exclusive) {
+  block_poll_ge(s, target, sa);
+  acquire_lines(line_exclusive);
 }
 
 // Workgroups are dispatched round-robin over the 8 XCDs, each with its own
