@@ -40,8 +40,8 @@ TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 def _parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=500)
     p.add_argument("--aux-cus", type=int, default=0, help="copy-kernel CUs of the headline (0 = default, -1 = shared)")
     p.add_argument("--tile", type=int, default=0)
     p.add_argument("--paths", default="all", choices=["all", "ag"], help="also time the other three paths")
@@ -150,46 +150,56 @@ def _cpu_baseline(inp, M, N, K, R):
 
 
 class Timer:
-    """Times calls of one path in each mode: whole-call milliseconds from
-    events on the caller stream, plus the main/aux kernel durations that the
-    library measures with events on the kernels' own streams."""
+    """Times calls of one path in each mode: milliseconds per call over
+    back-to-back calls (stream-ordered throughput, as in the headline), plus
+    the main/aux kernel durations that the library measures with events on
+    the kernels' own streams."""
 
     def __init__(self, torch, tsg, ctx, fn):
         self.torch, self.tsg, self.ctx, self.fn = torch, tsg, ctx, fn
 
-    def run(self, mode, n, warmup=2, kernels=()):
-        """Median call ms over n calls (no per-kernel events in these calls),
-        then, if asked, median kernel ms over n further calls that record the
-        library's per-kernel events."""
-        torch, tsg, ctx = self.torch, self.tsg, self.ctx
-        for i in range(warmup):
-            self.fn(i, mode)
-        if ctx.check() != tsg.OK:
-            raise RuntimeError(ctx.last_error())
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    def _check(self):
+        if self.ctx.check() != self.tsg.OK:
+            raise RuntimeError(self.ctx.last_error())
+
+    def modes(self, modes, n, rounds=3, warmup=3):
+        """ms per call for each mode: the modes are interleaved over `rounds`
+        rounds of n back-to-back calls each (so a clock change between modes
+        does not bias one of them) and the median round is kept."""
+        torch = self.torch
+        for m in modes:
+            for i in range(warmup):
+                self.fn(i, m)
+        self._check()
+        got = {m: [] for m in modes}
+        for _ in range(rounds):
+            for m in modes:
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                for i in range(n):
+                    self.fn(i, m)
+                torch.cuda.synchronize()
+                got[m].append((time.perf_counter() - t0) / n * 1e3)
+        self._check()
+        return {m: sorted(v)[len(v) // 2] for m, v in got.items()}
+
+    def kernels(self, mode, n, which):
+        """Median kernel ms (library events) over n calls, per kernel slot."""
+        torch, ctx = self.torch, self.ctx
+        kms = {k: [] for k in which}
+        ctx.enable_kernel_timing(True)
         for i in range(n):
-            ev[i][0].record()
             self.fn(i, mode)
-            ev[i][1].record()
+            for k in which:
+                kms[k].append(ctx.kernel_ms(k))
         torch.cuda.synchronize()
-        kms = {k: [] for k in kernels}
-        if kernels:
-            ctx.enable_kernel_timing(True)
-            for i in range(n):
-                self.fn(i, mode)
-                for k in kernels:
-                    kms[k].append(ctx.kernel_ms(k))
-            torch.cuda.synchronize()
-            ctx.enable_kernel_timing(False)
-        if ctx.check() != tsg.OK:
-            raise RuntimeError(ctx.last_error())
-        ms = sorted(a.elapsed_time(b) for a, b in ev)
-        med = ms[len(ms) // 2]
-        return med, {k: sorted(v)[len(v) // 2] for k, v in kms.items()}
+        ctx.enable_kernel_timing(False)
+        self._check()
+        return {k: sorted(v)[len(v) // 2] for k, v in kms.items()}
 
 
 def _summary(flops, hbm_bytes, t):
-    """t: dict mode -> median ms (None when the mode does not apply)."""
+    """t: dict mode -> ms per call, back to back (None when the mode does not apply)."""
     ov, se, co, cm = t["overlap"], t["serial"], t["compute_only"], t.get("comm_only")
     out = {
         "ms": {k: (None if v is None else round(v, 5)) for k, v in t.items()},
@@ -295,12 +305,13 @@ def main():
 
     timer = Timer(torch, tsg, ctx, ag_fn)
     n = max(5, min(args.steps, 30))
-    t_ov, k_ov = timer.run(tsg.OVERLAP, n, kernels=(0, 1))
-    t_se, _ = timer.run(tsg.SERIAL, n)
-    t_co, k_co = timer.run(tsg.COMPUTE_ONLY, n, kernels=(0,))
-    t_cm, k_cm = timer.run(tsg.COMM_ONLY, n, kernels=(1,))
+    tm = timer.modes((tsg.OVERLAP, tsg.SERIAL, tsg.COMPUTE_ONLY, tsg.COMM_ONLY), n)
+    k_ov = timer.kernels(tsg.OVERLAP, n, (0, 1))
+    k_co = timer.kernels(tsg.COMPUTE_ONLY, n, (0,))
+    k_cm = timer.kernels(tsg.COMM_ONLY, n, (1,))
     ag = _summary(ag_flops, ag_gemm_bytes + ag_copy_bytes,
-                  {"overlap": t_ov, "serial": t_se, "compute_only": t_co, "comm_only": t_cm})
+                  {"overlap": tm[tsg.OVERLAP], "serial": tm[tsg.SERIAL],
+                   "compute_only": tm[tsg.COMPUTE_ONLY], "comm_only": tm[tsg.COMM_ONLY]})
     ag["kernel_ms"] = {"gemm_in_overlap": round(k_ov[0], 5), "copy_in_overlap": round(k_ov[1], 5),
                        "gemm_alone": round(k_co[0], 5), "copy_alone": round(k_cm[1], 5)}
     paths = {"ag_gemm": ag}
@@ -319,10 +330,10 @@ def main():
         mr = c3["M"] // c3["R"]
         rs_bytes = (c3["M"] * c3["K"] * 2 + c3["K"] * c3["N"] * 2 + c3["M"] * c3["N"] * 4
                     + (c3["R"] - 1) * mr * c3["N"] * 4 + 2 * mr * c3["N"] * 4)
+        tm = t.modes((tsg.OVERLAP, tsg.SERIAL, tsg.COMPUTE_ONLY, tsg.COMM_ONLY), n)
         paths["gemm_rs"] = _summary(2.0 * c3["M"] * c3["N"] * c3["K"], rs_bytes,
-                                    {"overlap": t.run(tsg.OVERLAP, n)[0], "serial": t.run(tsg.SERIAL, n)[0],
-                                     "compute_only": t.run(tsg.COMPUTE_ONLY, n)[0],
-                                     "comm_only": t.run(tsg.COMM_ONLY, n)[0]})
+                                    {"overlap": tm[tsg.OVERLAP], "serial": tm[tsg.SERIAL],
+                                     "compute_only": tm[tsg.COMPUTE_ONLY], "comm_only": tm[tsg.COMM_ONLY]})
         del x, w, pp, P, o
 
         c4 = CONFIGS["mlp2"]
@@ -336,9 +347,10 @@ def main():
         mlp_flops = 2.0 * c4["M"] * c4["N1"] * c4["K1"] + 2.0 * c4["M"] * c4["N2"] * c4["N1"]
         mlp_bytes = (c4["M"] * c4["K1"] * 2 + c4["K1"] * c4["N1"] * 2 + 2 * c4["M"] * c4["N1"] * 2
                      + c4["N1"] * c4["N2"] * 2 + c4["M"] * c4["N2"] * 4)
+        tm = t.modes((tsg.OVERLAP, tsg.SERIAL, tsg.COMPUTE_ONLY), n)
         paths["mlp2"] = _summary(mlp_flops, mlp_bytes,
-                                 {"overlap": t.run(tsg.OVERLAP, n)[0], "serial": t.run(tsg.SERIAL, n)[0],
-                                  "compute_only": t.run(tsg.COMPUTE_ONLY, n)[0], "comm_only": None})
+                                 {"overlap": tm[tsg.OVERLAP], "serial": tm[tsg.SERIAL],
+                                  "compute_only": tm[tsg.COMPUTE_ONLY], "comm_only": None})
         del dx, d1, d2, h, y
 
         c5 = CONFIGS["moe"]
@@ -357,10 +369,10 @@ def main():
         moe_flops = 4.0 * T * k * Hh * I
         moe_bytes = (T * k * Hh * 2 + 2 * E * Hh * I * 2 + 2 * T * k * I * 2 + 2 * T * k * Hh * 4
                      + T * Hh * 4)
+        tm = t.modes((tsg.OVERLAP, tsg.SERIAL, tsg.COMPUTE_ONLY, tsg.COMM_ONLY), n)
         paths["moe"] = _summary(moe_flops, moe_bytes,
-                                {"overlap": t.run(tsg.OVERLAP, n)[0], "serial": t.run(tsg.SERIAL, n)[0],
-                                 "compute_only": t.run(tsg.COMPUTE_ONLY, n)[0],
-                                 "comm_only": t.run(tsg.COMM_ONLY, n)[0]})
+                                {"overlap": tm[tsg.OVERLAP], "serial": tm[tsg.SERIAL],
+                                 "compute_only": tm[tsg.COMPUTE_ONLY], "comm_only": tm[tsg.COMM_ONLY]})
 
     tflops = ag_flops / (ms_step * 1e-3) / 1e12
     achieved = ag_flops / (k_ov[0] * 1e-3) / 1e12

@@ -259,10 +259,8 @@ __global__ void __launch_bounds__(Cfg::NT) ag_gemm_kernel(const AgGemmArgs args)
   const int M = args.M, N = args.N;
   if (OUT_BF16) {
     uint16_t* C = (uint16_t*)args.c;
-    GemmTile<Cfg>::for_each(acc, [&](int r, int c, float v) {
-      const int gr = row0 + r, gc = col0 + c;
-      if (gr < M && gc < N) C[(int64_t)gr * N + gc] = (uint16_t)f32_to_bf16(v);
-    });
+    GemmTile<Cfg>::template store_bf16_staged<sizeof(lds), false>(
+        acc, lds, C + (int64_t)row0 * N + col0, N, M - row0, N - col0, [](float v) { return v; });
   } else {
     float* C = (float*)args.c;
     GemmTile<Cfg>::for_each(acc, [&](int r, int c, float v) {

@@ -32,6 +32,9 @@ constexpr size_t kSigBase = 64;     // row-block signals of MLP2 in the context'
 constexpr int kRowBlock = 128;
 constexpr int kMaxRowBlocks = 4000;
 
+// GELU, exact form, on the fp32 accumulator: 0.5 z (1 + erf(z / sqrt 2)).
+__device__ __forceinline__ float gelu_erf(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
+
 struct Mlp1Args {
   const uint16_t* x;
   const uint16_t* w1;
@@ -62,18 +65,11 @@ __global__ void __launch_bounds__(Cfg::NT) mlp_gemm1_kernel(const Mlp1Args a) {
     GemmTile<Cfg>::run_direct(ar, a.w1, a.N1, col0, a.N1, a.K1, lds, acc);
   else
     GemmTile<Cfg>::run_regs(ar, a.w1, a.N1, col0, a.N1, a.K1, lds, acc);
-  const int M = a.M, N1 = a.N1;
-  uint16_t* H = a.h;
-  GemmTile<Cfg>::for_each(acc, [&](int r, int c, float z) {
-    const int gr = row0 + r, gc = col0 + c;
-    if (gr < M && gc < N1) {
-      const float g = 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
-      store_coherent(H + (int64_t)gr * N1 + gc, (uint16_t)f32_to_bf16(g));
-    }
-  });
+  GemmTile<Cfg>::template store_bf16_staged<sizeof(lds), true>(
+      acc, lds, a.h + (int64_t)row0 * a.N1 + col0, a.N1, a.M - row0, a.N1 - col0, gelu_erf);
   block_coherent_complete();
   if (threadIdx.x == 0) {
-    for (int b = row0 / kRowBlock; b * kRowBlock < min(row0 + Cfg::BM, M); ++b) {
+    for (int b = row0 / kRowBlock; b * kRowBlock < min(row0 + Cfg::BM, a.M); ++b) {
       if ((a.skip_mask >> (b & 31)) & 1u) continue;
       sig_arrive_counted_coherent(a.cnt + b, a.sig + b, a.arrivals, a.sa.epoch);
     }
@@ -222,15 +218,8 @@ __global__ void __launch_bounds__(256) mlp_fused_kernel(const MlpFusedArgs f) {
         GemmTile<C1>::run_direct(ar, a.w1, a.N1, col0, a.N1, a.K1, lds, acc);
       else
         GemmTile<C1>::run_regs(ar, a.w1, a.N1, col0, a.N1, a.K1, lds, acc);
-      const int M = a.M, N1 = a.N1;
-      uint16_t* H = a.h;
-      GemmTile<C1>::for_each(acc, [&](int r, int c, float z) {
-        const int gr = row0 + r, gc = col0 + c;
-        if (gr < M && gc < N1) {
-          const float g = 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
-          store_coherent(H + (int64_t)gr * N1 + gc, (uint16_t)f32_to_bf16(g));
-        }
-      });
+      GemmTile<C1>::template store_bf16_staged<sizeof(lds), true>(
+          acc, lds, a.h + (int64_t)row0 * a.N1 + col0, a.N1, a.M - row0, a.N1 - col0, gelu_erf);
       block_coherent_complete();
       if (threadIdx.x == 0) {
         for (int rb = row0 / kRowBlock; rb * kRowBlock < min(row0 + C1::BM, a.M); ++rb) {

@@ -413,12 +413,10 @@ __global__ void __launch_bounds__(256) moe_producer_kernel(const ProdArgs a) {
           GemmTile<CfgUp>::run_direct(ar, B, a.I, col0, a.I, a.H, lds, acc);
         else
           GemmTile<CfgUp>::run_regs(ar, B, a.I, col0, a.I, a.H, lds, acc);
-        const int I = a.I;
-        uint16_t* hrow = a.ws.h + (int64_t)rb * BM * I;
-        GemmTile<CfgUp>::for_each(acc, [&](int r, int c, float u) {
-          const int gc = col0 + c;
-          if (gc < I) store_coherent(hrow + (int64_t)r * I + gc, (uint16_t)f32_to_bf16(u / (1.0f + expf(-u))));
-        });
+        // h = bf16(SiLU(u)), SiLU(u) = u / (1 + e^-u)
+        GemmTile<CfgUp>::template store_bf16_staged<sizeof(lds), true>(
+            acc, lds, a.ws.h + (int64_t)rb * BM * a.I + col0, a.I, BM, a.I - col0,
+            [](float u) { return u / (1.0f + expf(-u)); });
         block_coherent_complete();
         if (threadIdx.x == 0) {
           if (!((a.skip_mask >> (rb & 31)) & 1u))

@@ -503,6 +503,68 @@ struct GemmTile {
           f(r, c, acc[i][j][v]);
         }
   }
+
+  // bf16 epilogue through LDS.  C points at the tile's first element, with
+  // ldc elements per row; ldc and the address are multiples of 8 elements,
+  // and only the first `rows` rows and `cols` columns of the tile are stored
+  // (cols a multiple of 8).  Each wave rounds f(value) of its results to
+  // bf16 (nearest even) into its own region of LDS, row-major, then reads
+  // the region back in 16-byte row pieces and stores those: a wave writes
+  // whole 16-byte vectors instead of one 2-byte element per lane and value.
+  // Rows are padded by 32 bytes when the LDS allows it, so that the two row
+  // groups of a fragment (rows r and r + 4) write different banks.  Called by
+  // every thread after the K loop, whose last barrier freed the LDS;
+  // LDS_BYTES is the size of the caller's LDS array.  COHERENT: the stores go
+  // through to the coherence point (store_coherent), for data a consumer in
+  // the same kernel reads after a signal.
+  template <int LDS_BYTES, bool COHERENT, class F>
+  __device__ __forceinline__ static void store_bf16_staged(const Acc& acc, char* lds, uint16_t* C,
+                                                          int64_t ldc, int rows, int cols, F&& f) {
+    constexpr int PAD = Cfg::NW * Cfg::WTM * (Cfg::WTN * 2 + 32) <= LDS_BYTES ? 32 : 0;
+    constexpr int STRIDE = Cfg::WTN * 2 + PAD;
+    static_assert(Cfg::NW * Cfg::WTM * STRIDE <= LDS_BYTES, "staged tile does not fit the LDS");
+    constexpr int VPR = Cfg::WTN / 8;          // 16-byte pieces per row
+    constexpr int TOT = Cfg::WTM * VPR;
+    static_assert(TOT % 64 == 0, "pieces must fill whole wave passes");
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm0 = (wave / Cfg::WN) * Cfg::WTM;
+    const int wn0 = (wave % Cfg::WN) * Cfg::WTN;
+    char* reg = lds + wave * (Cfg::WTM * STRIDE);
+    char* wr = reg + ((lane >> 5) * 4) * STRIDE + (lane & 31) * 2;
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < Cfg::FN; ++j)
+      {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = i * 32 + (v >> 2) * 8 + (v & 3);
+          *(uint16_t*)(wr + r * STRIDE + j * 64) = (uint16_t)f32_to_bf16(f(acc[i][j][v]));
+        }
+        // one fragment at a time: keeps the compiler from moving every
+        // accumulator into vector registers at once
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    // The region is this wave's alone: its LDS writes complete before its
+    // reads, and the clobber keeps the compiler from reordering them.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    uint16_t* dst0 = C + (int64_t)wm0 * ldc + wn0;
+#pragma unroll 4
+    for (int it = 0; it < TOT / 64; ++it) {
+      const int idx = it * 64 + lane;
+      const int r = idx / VPR, q = idx - r * VPR;
+      const u32x4_t v = *(const u32x4_t*)(reg + r * STRIDE + q * 16);
+      u32x4_t* d = (u32x4_t*)(dst0 + (int64_t)r * ldc + q * 8);
+      if (wm0 + r < rows && wn0 + q * 8 < cols) {
+        if (COHERENT)
+          store_coherent(d, v);
+        else
+          *d = v;
+      }
+    }
+  }
 };
 
 }  // namespace tsg
