@@ -113,6 +113,15 @@ typedef struct tsg_opts {
    * of two, at least 64; 0 = 512.  Capped at 2048 and at K rounded up to a
    * power of two (one signal per chunk when K <= 2048). */
   int comm_tile;
+  /* AG+GEMM, shared CUs: copy units (pieces of the first column slabs, in
+   * the copy's order) that the GEMM's first workgroups take from the copy's
+   * work queue and move themselves at their start, before their first wait:
+   * the consumer pulls the head of the data ([TL] Table 3, tile_pull_data),
+   * so compute need not wait for the copy kernel to be scheduled.  Units not
+   * taken by the GEMM are moved by the copy kernel from the same queue.
+   * 0 = the op's default (one unit per CU, at most the first slab's units),
+   * -1 = none. */
+  int pull_units;
 } tsg_opts;
 
 /* ------------------------------------------------------------------ ctx */

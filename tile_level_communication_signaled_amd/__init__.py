@@ -50,6 +50,7 @@ class Opts(ctypes.Structure):
         ("timeline", ctypes.c_int),
         ("aux_wgs", ctypes.c_int),
         ("comm_tile", ctypes.c_int),
+        ("pull_units", ctypes.c_int),
     ]
 
 

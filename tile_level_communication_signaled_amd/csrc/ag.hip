@@ -37,6 +37,7 @@ constexpr int kMaxRanks = 32;
 constexpr int kMaxMTiles = 1024;
 constexpr size_t kSigBase = size_t(1) << 18;  // AG slab signals in the context's pool
 constexpr size_t kSigCap = size_t(1) << 18;   // slots up to the next op's region
+constexpr int kQueueSlot = 40;                // copy work queue in the context's ticket words
 
 struct ChunkOrder {
   int8_t chunk[kMaxRanks];  // chunk copied at arrival position p (p = 0: local)
@@ -65,6 +66,11 @@ struct CopyArgs {
   int ustart[kHead + 1];
   int n_units;
   uint32_t skip_mask;
+  // Work queue shared by the copy kernel's workgroups and the GEMM
+  // workgroups that pull units: a ticket counter and an exit counter; the
+  // last of the n_workers claimers to leave resets both for the next call.
+  uint32_t* queue;
+  uint32_t n_workers;
 };
 
 // Work unit u -> (slab s, arrival position p, piece j), slab-major.  One unit
@@ -73,68 +79,94 @@ struct CopyArgs {
 // more pieces so that many workgroups share them: every GEMM tile needs
 // slab 0 before it can start, slab 1 soon after, and so on, while later
 // slabs have time to arrive in larger pieces, which need fewer store drains and arrivals.
-__global__ void __launch_bounds__(256) ag_copy_kernel(const CopyArgs a) {
+// Moves unit u and arrives on its slab's signal.  Called by every thread of
+// the workgroup with the same u.
+__device__ __forceinline__ void copy_unit(const CopyArgs& a, int u) {
   constexpr int U = 8;  // 16-byte vectors in flight per thread
   const int vpr = 1 << a.vpr_log2;
-  for (int u = blockIdx.x; u < a.n_units; u += gridDim.x) {
-    const uint64_t t0 = a.tl.buf ? wall_clock64() : 0;
-    int s, rem, npc;
-    if (u >= a.ustart[kHead]) {
-      npc = a.np[kHead];
-      const int v = u - a.ustart[kHead];
-      const int per = a.R * npc;
-      s = kHead + v / per;
-      rem = v - (s - kHead) * per;
-    } else {
-      s = 0;
-      while (u >= a.ustart[s + 1]) ++s;
-      npc = a.np[s];
-      rem = u - a.ustart[s];
-    }
-    const int p = rem / npc;
-    const int j = rem - p * npc;
-    const int c = a.ord.chunk[p];
-    const int rp = (a.chunk_rows + npc - 1) / npc;
-    const int r0 = j * rp;
-    const int nr = min(rp, a.chunk_rows - r0);
-    const int64_t col0 = (int64_t)s * vpr;
-    const int width = (int)min((int64_t)vpr, a.k8 - col0);
-    const int64_t chunk_vec = (int64_t)a.chunk_rows * a.k8;
-    const u32x4_t* __restrict__ src =
-        (c == a.rank ? a.a_local : a.a_peers + (int64_t)(c < a.rank ? c : c - 1) * chunk_vec) +
-        (int64_t)r0 * a.k8 + col0;
-    u32x4_t* __restrict__ dst = a.a_full + ((int64_t)c * a.chunk_rows + r0) * a.k8 + col0;
-    // Slab rows are at most 256 vectors wide, so thread t always moves column
-    // t mod vpr of rows t / vpr, t / vpr + 256 / vpr, ...  Addresses are a
-    // uniform base plus a 32-bit byte offset (one register per access).
-    const int rows_q = 256 >> a.vpr_log2;
-    const int cc = threadIdx.x & (vpr - 1);
-    const int rr = threadIdx.x >> a.vpr_log2;
-    if (cc < width) {
-      const char* sb = (const char*)src;
-      char* db = (char*)dst;
-      const uint32_t step = (uint32_t)(rows_q * a.k8 * 16);
-      uint32_t off = (uint32_t)((rr * a.k8 + cc) * 16);
-      int r = rr;
-      for (; r + (U - 1) * rows_q < nr; r += U * rows_q, off += U * step) {
-        u32x4_t v[U];
-#pragma unroll
-        for (int q = 0; q < U; ++q) v[q] = *(const u32x4_t*)(sb + (off + q * step));
-#pragma unroll
-        for (int q = 0; q < U; ++q) store_coherent((u32x4_t*)(db + (off + q * step)), v[q]);
-      }
-      for (; r < nr; r += rows_q, off += step)
-        store_coherent((u32x4_t*)(db + off), *(const u32x4_t*)(sb + off));
-    }
-    // The piece is published without an L2 write-back: its stores went
-    // through to the coherence point (store_coherent).
-    block_coherent_complete();
-    const size_t si = (size_t)c * a.n_slab + s;
-    if (threadIdx.x == 0 && !((a.skip_mask >> c) & 1u))
-      sig_arrive_counted_coherent(a.cnt + si, a.sig + si, (uint32_t)npc, a.sa.epoch);
-    if (threadIdx.x == 0 && a.tl.buf)
-      timeline_put(a.tl, 1, (uint32_t)(c << 24 | s << 12 | (j & 0xfff)), t0, t0, wall_clock64());
+  const uint64_t t0 = a.tl.buf ? wall_clock64() : 0;
+  int s, rem, npc;
+  if (u >= a.ustart[kHead]) {
+    npc = a.np[kHead];
+    const int v = u - a.ustart[kHead];
+    const int per = a.R * npc;
+    s = kHead + v / per;
+    rem = v - (s - kHead) * per;
+  } else {
+    s = 0;
+    while (u >= a.ustart[s + 1]) ++s;
+    npc = a.np[s];
+    rem = u - a.ustart[s];
   }
+  const int p = rem / npc;
+  const int j = rem - p * npc;
+  const int c = a.ord.chunk[p];
+  const int rp = (a.chunk_rows + npc - 1) / npc;
+  const int r0 = j * rp;
+  const int nr = min(rp, a.chunk_rows - r0);
+  const int64_t col0 = (int64_t)s * vpr;
+  const int width = (int)min((int64_t)vpr, a.k8 - col0);
+  const int64_t chunk_vec = (int64_t)a.chunk_rows * a.k8;
+  const u32x4_t* __restrict__ src =
+      (c == a.rank ? a.a_local : a.a_peers + (int64_t)(c < a.rank ? c : c - 1) * chunk_vec) +
+      (int64_t)r0 * a.k8 + col0;
+  u32x4_t* __restrict__ dst = a.a_full + ((int64_t)c * a.chunk_rows + r0) * a.k8 + col0;
+  // Slab rows are at most 256 vectors wide, so thread t always moves column
+  // t mod vpr of rows t / vpr, t / vpr + 256 / vpr, ...  Addresses are a
+  // uniform base plus a 32-bit byte offset (one register per access).
+  const int rows_q = 256 >> a.vpr_log2;
+  const int cc = threadIdx.x & (vpr - 1);
+  const int rr = threadIdx.x >> a.vpr_log2;
+  if (cc < width) {
+    const char* sb = (const char*)src;
+    char* db = (char*)dst;
+    const uint32_t step = (uint32_t)(rows_q * a.k8 * 16);
+    uint32_t off = (uint32_t)((rr * a.k8 + cc) * 16);
+    int r = rr;
+    for (; r + (U - 1) * rows_q < nr; r += U * rows_q, off += U * step) {
+      u32x4_t v[U];
+#pragma unroll
+      for (int q = 0; q < U; ++q) v[q] = *(const u32x4_t*)(sb + (off + q * step));
+#pragma unroll
+      for (int q = 0; q < U; ++q) store_coherent((u32x4_t*)(db + (off + q * step)), v[q]);
+    }
+    for (; r < nr; r += rows_q, off += step)
+      store_coherent((u32x4_t*)(db + off), *(const u32x4_t*)(sb + off));
+  }
+  // The piece is published without an L2 write-back: its stores went
+  // through to the coherence point (store_coherent).
+  block_coherent_complete();
+  const size_t si = (size_t)c * a.n_slab + s;
+  if (threadIdx.x == 0 && !((a.skip_mask >> c) & 1u))
+    sig_arrive_counted_coherent(a.cnt + si, a.sig + si, (uint32_t)npc, a.sa.epoch);
+  if (threadIdx.x == 0 && a.tl.buf)
+    timeline_put(a.tl, 1, (uint32_t)(c << 24 | s << 12 | (j & 0xfff)), t0, t0, wall_clock64());
+}
+
+// Next unit from the queue, identical in every thread (`slot` is one int of
+// LDS owned by the caller).
+__device__ __forceinline__ int claim_unit(const CopyArgs& a, volatile int* slot) {
+  if (threadIdx.x == 0) *slot = (int)atomicAdd(a.queue, 1u);
+  __syncthreads();
+  const int u = __builtin_amdgcn_readfirstlane(*slot);
+  __syncthreads();
+  return u;
+}
+
+// A claimer is done with the queue; the last one resets it.  One lane.
+__device__ __forceinline__ void leave_queue(const CopyArgs& a) {
+  if (atomicAdd(a.queue + 1, 1u) == a.n_workers - 1) {
+    __hip_atomic_store(a.queue, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(a.queue + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Copy kernel: takes units from the queue in order (slab-major) until none
+// is left.  It never waits, so it always drains the queue.
+__global__ void __launch_bounds__(256) ag_copy_kernel(const CopyArgs a) {
+  __shared__ int slot;
+  for (int u = claim_unit(a, &slot); u < a.n_units; u = claim_unit(a, &slot)) copy_unit(a, u);
+  if (threadIdx.x == 0) leave_queue(a);
 }
 
 // ---------------------------------------------------------------- GEMM
@@ -156,6 +188,8 @@ struct AgGemmArgs {
   int slab_log2;          // log2 of the slab width in K columns
   int l1_only;            // slabs never share a 128-byte line
   int per_xcd;            // resident tiles per XCD (0 = no XCD remap)
+  int pull_wgs;           // workgroups 0 .. pull_wgs - 1 first move one copy unit each
+  CopyArgs copy;
   uint16_t mt_order[kMaxMTiles];
 };
 
@@ -225,6 +259,13 @@ __global__ void __launch_bounds__(Cfg::NT) ag_gemm_kernel(const AgGemmArgs args)
   const int nt = w % args.n_tiles_n;
   const int row0 = mt * Cfg::BM, col0 = nt * Cfg::BN;
   const uint64_t t0 = args.tl.buf ? wall_clock64() : 0;
+  if (Cfg::NT == 256 && (int)blockIdx.x < args.pull_wgs) {
+    // tile_pull_data: move one unit of the copy's queue before any wait (the
+    // LDS is not in use yet, so its first word carries the ticket)
+    const int u = claim_unit(args.copy, (volatile int*)lds);
+    if (u < args.copy.n_units) copy_unit(args.copy, u);
+    if (threadIdx.x == 0) leave_queue(args.copy);
+  }
   SlabWait hook;
   hook.active = false;
   hook.waited = 0;
@@ -547,15 +588,31 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
   }
   ca.n_units = (int)n_units;
   ca.skip_mask = o.skip_mask;
+  ca.queue = ctx->d_queue + kQueueSlot;
+  // Units the GEMM pulls itself (overlap on shared CUs, tiles of 256 threads,
+  // whose workgroups move a unit the way the copy's do): by default one per
+  // workgroup of the first wave of tiles, at most the first slab's units.
+  const int copy_grid = (int)std::min<int64_t>(nwg, n_units);
+  int pull = 0;
+  int gemm_nt = 0;
+  (void)gemm_fn(tile, c_dtype == TSG_BF16, K, &gemm_nt);
+  if (mode == TSG_MODE_OVERLAP && !back_to_back && o.aux_cus < 0 && o.pull_units >= 0 && gemm_nt == 256) {
+    pull = o.pull_units > 0 ? o.pull_units : std::min(ctx->n_cus, ustart[1]);
+    pull = (int)std::min<int64_t>(std::min(pull, grid_gemm), n_units);
+  }
+  ca.n_workers = (uint32_t)(copy_grid + pull);
+  ga.pull_wgs = 0;
+  ga.copy = ca;
 
-  auto copy = [&](hipStream_t s, int nwg) -> tsg_status {
+  auto copy = [&](hipStream_t s) -> tsg_status {
     time_begin(ctx, 1, s);
-    hipLaunchKernelGGL(ag_copy_kernel, dim3((int)std::min<int64_t>(nwg, n_units)), dim3(256), 0, s, ca);
+    hipLaunchKernelGGL(ag_copy_kernel, dim3(copy_grid), dim3(256), 0, s, ca);
     time_end(ctx, 1, s);
     return check_launch(ctx, "ag_copy_kernel");
   };
   auto gemm = [&](hipStream_t s, int wait, int cus) -> tsg_status {
     ga.wait = wait;
+    ga.pull_wgs = wait ? pull : 0;
     ga.per_xcd = cus / 8;
     time_begin(ctx, 0, s);
     hipError_t e = launch_gemm(tile, ga, c_dtype == TSG_BF16, grid_gemm, s);
@@ -566,7 +623,7 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
 
   tsg_status st = TSG_OK;
   if (back_to_back) {
-    st = copy(caller, nwg);
+    st = copy(caller);
     if (st == TSG_OK) st = gemm(caller, 1, ctx->n_cus);
     return st;
   }
@@ -583,9 +640,9 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
     // The GEMM needs no fork: launched first it is dispatched at once, and the
     // copy's workgroups join it on the same CUs.
     st = gemm(pr.main, 1, pr.main_cus);
-    if (st == TSG_OK) st = copy(pr.aux, nwg);
+    if (st == TSG_OK) st = copy(pr.aux);
   } else {
-    st = copy(pr.aux, nwg);
+    st = copy(pr.aux);
     if (st == TSG_OK && mode == TSG_MODE_OVERLAP) st = gemm(pr.main, 1, pr.main_cus);
   }
   tsg_status sj = join(ctx, caller, pr);

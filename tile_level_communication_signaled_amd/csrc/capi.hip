@@ -50,6 +50,7 @@ Opts resolve(const tsg_opts* o, int default_aux_cus) {
   r.timeline = o ? o->timeline : 0;
   r.aux_wgs = o ? o->aux_wgs : 0;
   r.comm_tile = o ? o->comm_tile : 0;
+  r.pull_units = o ? o->pull_units : 0;
   return r;
 }
 

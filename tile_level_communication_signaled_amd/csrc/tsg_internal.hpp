@@ -69,6 +69,7 @@ struct Opts {
   int timeline;
   int aux_wgs;   // 0 = the op's default
   int comm_tile; // 0 = the op's default
+  int pull_units; // 0 = the op's default, -1 = none
 };
 Opts resolve(const tsg_opts* o, int default_aux_cus);
 
