@@ -82,7 +82,7 @@ struct CopyArgs {
 // Moves unit u and arrives on its slab's signal.  Called by every thread of
 // the workgroup with the same u.
 __device__ __forceinline__ void copy_unit(const CopyArgs& a, int u) {
-  constexpr int U = 8;  // 16-byte vectors in flight per thread
+  constexpr int U = 8;  // 8-byte words in flight per thread
   const int vpr = 1 << a.vpr_log2;
   const uint64_t t0 = a.tl.buf ? wall_clock64() : 0;
   int s, rem, npc;
@@ -111,27 +111,41 @@ __device__ __forceinline__ void copy_unit(const CopyArgs& a, int u) {
       (c == a.rank ? a.a_local : a.a_peers + (int64_t)(c < a.rank ? c : c - 1) * chunk_vec) +
       (int64_t)r0 * a.k8 + col0;
   u32x4_t* __restrict__ dst = a.a_full + ((int64_t)c * a.chunk_rows + r0) * a.k8 + col0;
-  // Slab rows are at most 256 vectors wide, so thread t always moves column
-  // t mod vpr of rows t / vpr, t / vpr + 256 / vpr, ...  Addresses are a
-  // uniform base plus a 32-bit byte offset (one register per access).
-  const int rows_q = 256 >> a.vpr_log2;
-  const int cc = threadIdx.x & (vpr - 1);
-  const int rr = threadIdx.x >> a.vpr_log2;
-  if (cc < width) {
-    const char* sb = (const char*)src;
-    char* db = (char*)dst;
-    const uint32_t step = (uint32_t)(rows_q * a.k8 * 16);
-    uint32_t off = (uint32_t)((rr * a.k8 + cc) * 16);
-    int r = rr;
-    for (; r + (U - 1) * rows_q < nr; r += U * rows_q, off += U * step) {
-      u32x4_t v[U];
+  // The piece moves in 8-byte words, so that each coherent store instruction
+  // of a wave covers 64 consecutive words of a row (512 contiguous bytes, or
+  // whole rows of a narrow slab) and writes whole lines: stores of 16 bytes
+  // per lane would go out as two 8-byte halves, each instruction writing
+  // every other 8 bytes.  A slab row is wpr <= 512 words; thread t moves word
+  // t mod tpr (+ 256 when the row is wider than the workgroup) of rows
+  // t / tpr, t / tpr + rows_p, ...  Addresses are a uniform base plus a
+  // 32-bit byte offset (one register per access).
+  const int wpr = 2 * vpr;
+  const int tpr_log2 = min(a.vpr_log2 + 1, 8);
+  const int tpr = 1 << tpr_log2;
+  const int rows_p = 256 >> tpr_log2;
+  const int rr = threadIdx.x >> tpr_log2;
+  const int wwidth = 2 * width;
+  const char* sb = (const char*)src;
+  char* db = (char*)dst;
+  const uint32_t row_bytes = (uint32_t)(a.k8 * 16);
+  const uint32_t step = (uint32_t)rows_p * row_bytes;
+  const int cw = threadIdx.x & (tpr - 1);
+  for (int k = 0; k < wpr; k += 256) {  // a second pass only for rows of 512 words
+    if (cw + k < wwidth) {
+      const char* sk = sb + k * 8;
+      char* dk = db + k * 8;
+      uint32_t off = (uint32_t)rr * row_bytes + (uint32_t)cw * 8u;
+      int r = rr;
+      for (; r + (U - 1) * rows_p < nr; r += U * rows_p, off += U * step) {
+        uint64_t v[U];
 #pragma unroll
-      for (int q = 0; q < U; ++q) v[q] = *(const u32x4_t*)(sb + (off + q * step));
+        for (int q = 0; q < U; ++q) v[q] = *(const uint64_t*)(sk + (off + q * step));
 #pragma unroll
-      for (int q = 0; q < U; ++q) store_coherent((u32x4_t*)(db + (off + q * step)), v[q]);
+        for (int q = 0; q < U; ++q) store_coherent((uint64_t*)(dk + (off + q * step)), v[q]);
+      }
+      for (; r < nr; r += rows_p, off += step)
+        store_coherent((uint64_t*)(dk + off), *(const uint64_t*)(sk + off));
     }
-    for (; r < nr; r += rows_q, off += step)
-      store_coherent((u32x4_t*)(db + off), *(const u32x4_t*)(sb + off));
   }
   // The piece is published without an L2 write-back: its stores went
   // through to the coherence point (store_coherent).
@@ -460,7 +474,7 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
   TSG_HIP(ctx, hipSetDevice(ctx->device));
 
   // Copy workgroups and streams.  Overlap: in shared mode one workgroup per
-  // two CUs, resident beside the GEMM's workgroups (the copy needs few
+  // CU, resident beside the GEMM's workgroups (the copy needs few
   // registers and no LDS); in split mode four per copy CU.  Serial: two per
   // CU.
   // In shared mode the GEMM runs on the caller's stream and the copy on a
@@ -473,7 +487,7 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
   if (mode == TSG_MODE_OVERLAP || mode == TSG_MODE_COMM_ONLY) {
     const tsg_status ss = streams(ctx, o, &pr, (hipStream_t)stream);
     if (ss != TSG_OK) return ss;
-    if (o.aux_wgs <= 0) nwg = o.aux_cus < 0 ? ctx->n_cus / 2 : pr.aux_cus * 4;
+    if (o.aux_wgs <= 0) nwg = o.aux_cus < 0 ? ctx->n_cus : pr.aux_cus * 4;
     if (mode == TSG_MODE_OVERLAP && o.aux_cus < 0) {
       int nt = 0;
       const void* fn = gemm_fn(tile, c_dtype == TSG_BF16, K, &nt);

@@ -90,6 +90,10 @@ __device__ __forceinline__ void store_coherent(u32x4_t* p, u32x4_t v) {
   __hip_atomic_store(q + 1, (uint64_t)v[2] | ((uint64_t)v[3] << 32), __ATOMIC_RELAXED, TSG_SIG_SCOPE);
 }
 
+__device__ __forceinline__ void store_coherent(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, TSG_SIG_SCOPE);
+}
+
 __device__ __forceinline__ void store_coherent(float* p, float v) {
   __hip_atomic_store((uint32_t*)p, __float_as_uint(v), __ATOMIC_RELAXED, TSG_SIG_SCOPE);
 }

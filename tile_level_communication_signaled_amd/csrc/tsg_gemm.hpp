@@ -551,17 +551,28 @@ struct GemmTile {
     // reads, and the clobber keeps the compiler from reordering them.
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     uint16_t* dst0 = C + (int64_t)wm0 * ldc + wn0;
+    if (COHERENT) {
+      // 8-byte pieces: each store instruction of the wave then writes
+      // consecutive bytes of a row, whole lines at a time (16-byte coherent
+      // stores go out as two 8-byte halves, each instruction writing every
+      // other 8 bytes)
+      constexpr int WPR = Cfg::WTN / 4;
+      constexpr int TOT8 = Cfg::WTM * WPR;
+      static_assert(TOT8 % 64 == 0, "pieces must fill whole wave passes");
 #pragma unroll 4
-    for (int it = 0; it < TOT / 64; ++it) {
-      const int idx = it * 64 + lane;
-      const int r = idx / VPR, q = idx - r * VPR;
-      const u32x4_t v = *(const u32x4_t*)(reg + r * STRIDE + q * 16);
-      u32x4_t* d = (u32x4_t*)(dst0 + (int64_t)r * ldc + q * 8);
-      if (wm0 + r < rows && wn0 + q * 8 < cols) {
-        if (COHERENT)
-          store_coherent(d, v);
-        else
-          *d = v;
+      for (int it = 0; it < TOT8 / 64; ++it) {
+        const int idx = it * 64 + lane;
+        const int r = idx / WPR, q = idx - r * WPR;
+        const uint64_t v = *(const uint64_t*)(reg + r * STRIDE + q * 8);
+        if (wm0 + r < rows && wn0 + q * 4 < cols) store_coherent((uint64_t*)(dst0 + (int64_t)r * ldc + q * 4), v);
+      }
+    } else {
+#pragma unroll 4
+      for (int it = 0; it < TOT / 64; ++it) {
+        const int idx = it * 64 + lane;
+        const int r = idx / VPR, q = idx - r * VPR;
+        const u32x4_t v = *(const u32x4_t*)(reg + r * STRIDE + q * 16);
+        if (wm0 + r < rows && wn0 + q * 8 < cols) *(u32x4_t*)(dst0 + (int64_t)r * ldc + q * 8) = v;
       }
     }
   }
