@@ -151,6 +151,28 @@ def test_ag_comm_tile_ragged_rows_and_unaligned_buffer(env):
         assert np.array_equal(full, inp["a"]) and err_ratio(c, ref, scale) <= 1.0
 
 
+def test_ag_pull_units_variants(env):
+    # The GEMM's first workgroups may pull any number of the copy's units from
+    # the shared work queue (none, the default, a few, more than there are):
+    # every variant gathers the same buffer and computes the same bits, and
+    # calls alternating between variants keep the queue's reset consistent.
+    M, N, K, R = 1024, 512, 512, 4
+    inp = ag_inputs(M, K, N, R, seed=21)
+    ref, scale = _ref(inp)
+    first = None
+    for rank, tile in ((1, 3), (2, 1)):
+        case = AgCase(env, inp, M, N, K, R, rank, out_bf16=False)
+        for pull in (-1, 0, 1, 5, 100000):
+            for ct, wgs in ((64, 4), (256, 0)):
+                full, c = case.run(opts={"tile": tile, "aux_cus": -1, "pull_units": pull, "comm_tile": ct,
+                                         "aux_wgs": wgs})
+                assert np.array_equal(full, inp["a"]), (rank, tile, pull, ct)
+                assert err_ratio(c, ref, scale) <= 1.0
+                if first is None:
+                    first = c
+                assert np.array_equal(c, first), (rank, tile, pull, ct)
+
+
 def test_ag_comm_only_and_serial_fill_gathered_buffer(env):
     torch, tsg, ctx = env
     M, N, K, R = 512, 128, 256, 8

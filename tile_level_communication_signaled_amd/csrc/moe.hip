@@ -594,7 +594,11 @@ tsg_status tsg_op_moe(tsg_ctx* ctx, const void* x, const int32_t* topk_ids, cons
   Pair pr;
   st = streams(ctx, o, &pr);
   if (st != TSG_OK) return st;
-  const int nwg_c = o.aux_wgs > 0 ? o.aux_wgs : (o.aux_cus < 0 ? 64 : pr.aux_cus * 4);
+  // Combine workgroups: overlap on shared CUs keeps the consumer small (64);
+  // the combine alone uses the whole GPU, as in serial mode.
+  const int nwg_c = o.aux_wgs > 0 ? o.aux_wgs
+                    : mode == TSG_MODE_COMM_ONLY ? (o.aux_cus < 0 ? ctx->n_cus * 2 : pr.aux_cus * 4)
+                    : (o.aux_cus < 0 ? 64 : pr.aux_cus * 4);
   st = fork(ctx, caller, pr);
   if (st != TSG_OK) return st;
   // Producer first, consumer second: the producer's only waits are on its own
