@@ -49,9 +49,13 @@ def _parse():
     p.add_argument("--headline-only", action="store_true",
                    help="time only the headline overlap steps (for kernel traces)")
     p.add_argument("--counters", action="store_true",
-                   help="counter-collection run: the profiler serialises kernels, so the GEMM runs in "
-                        "compute-only mode and the copy in comm-only mode (K steps each), then one plain "
-                        "1 GiB device copy of known size calibrates the byte counters; prints nothing")
+                   help="counter-collection run: the profiler serialises kernels, so every path runs in "
+                        "compute-only mode and in comm-only mode (K steps each) instead of overlapped, then "
+                        "one plain 1 GiB device copy of known size calibrates the byte counters; prints "
+                        "nothing")
+    p.add_argument("--timeline", action="store_true",
+                   help="print each path's device timeline of one overlapped call (units active and "
+                        "waiting per time bin) as markdown, and exit")
     p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="no GPU: turn the counter_collection.csv files of two rocprofv3 --pmc runs of "
                         "--counters (FETCH_SIZE, then WRITE_SIZE) into the traffic record and exit")
@@ -87,8 +91,13 @@ def _traffic(kernel: str):
 CALIB_BYTES = 1 << 30   # the plain device copy that --counters runs: 1 GiB read, 1 GiB written
 
 
+KERNELS = ("ag_gemm_kernel", "ag_copy_kernel", "rs_gemm_kernel", "rs_reduce_kernel", "mlp_gemm1_kernel",
+           "mlp_gemm2_kernel", "moe_route_kernel", "moe_producer_kernel", "moe_combine_kernel")
+
+
 def summarize_counters(fetch_csv: str, write_csv: str, out_path: str = TRAFFIC) -> dict:
-    """Per-launch HBM bytes of the AG kernels from two rocprofv3 --pmc runs.
+    """Per-launch HBM bytes of the library's kernels from two rocprofv3 --pmc
+    runs of --counters.
 
     FETCH_SIZE and WRITE_SIZE are read in KiB per dispatch and averaged per
     kernel.  Each counter is scaled by the factor that makes it read exactly
@@ -111,7 +120,7 @@ def summarize_counters(fetch_csv: str, write_csv: str, out_path: str = TRAFFIC) 
         calib = max(v for k, vs in acc.items() if k.startswith("__amd_rocclr_copyBuffer") for v in vs)
         scale = CALIB_BYTES / (calib * 1024.0)
         rec[name + "_scale"] = round(scale, 5)
-        for short in ("ag_gemm_kernel", "ag_copy_kernel"):
+        for short in KERNELS:
             vs = [v for k, lst in acc.items() if short in k for v in lst]
             if vs:
                 totals.setdefault(short, {})[name] = sum(vs) / len(vs) * 1024.0 * scale
@@ -233,14 +242,95 @@ def _path_ag(torch, tsg, ctx, cfg, n, opts, seed_sets=2):
                      "full": torch.empty((M, K), dtype=torch.int16, device="cuda"),
                      "c": torch.empty((M, N), dtype=torch.int16, device="cuda")})
 
-    def fn(i, mode):
+    def fn(i, mode, o=None):
         d = sets[i % len(sets)]
         tsg.gemm_ag_overlap(ctx, d["loc"], d["peers"], d["full"], d["b"], d["c"], tsg.BF16, M, N, K, R, 0,
-                            opts=opts, mode=mode)
+                            opts=o if o is not None else opts, mode=mode)
     flops = 2.0 * M * N * K
     gemm_bytes = M * K * 2 + K * N * 2 + M * N * 2
     copy_bytes = 2 * M * K * 2
     return fn, flops, gemm_bytes, copy_bytes, host
+
+
+def _other_paths(torch, tsg, ctx):
+    """The GEMM+RS, MLP and MoE paths at full size: name -> (fn(i, mode,
+    opts=None), flops, algorithmic HBM bytes, modes the path has)."""
+    import numpy as np
+    from synth import CONFIGS, mlp2_inputs, moe_inputs, rs_inputs
+    dv = lambda a: torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).cuda()
+    out = {}
+
+    c3 = CONFIGS["gemm_rs"]
+    M, N, K, R = c3["M"], c3["N"], c3["K"], c3["R"]
+    inp = rs_inputs(M, K, N, R, rank=0, seed=c3["seed"])
+    x, w, pp = dv(inp["x"]), dv(inp["w"]), dv(inp["peer_partials"])
+    P = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    o = torch.empty((M // R, N), dtype=torch.float32, device="cuda")
+    rs_fn = lambda i, mode, opts=None: tsg.gemm_rs_overlap(ctx, x, w, P, pp, o, M, N, K, R, 0, opts=opts, mode=mode)
+    mr = M // R
+    rs_bytes = M * K * 2 + K * N * 2 + M * N * 4 + (R - 1) * mr * N * 4 + 2 * mr * N * 4
+    out["gemm_rs"] = (rs_fn, 2.0 * M * N * K, rs_bytes,
+                      (tsg.OVERLAP, tsg.SERIAL, tsg.COMPUTE_ONLY, tsg.COMM_ONLY))
+
+    c4 = CONFIGS["mlp2"]
+    M4, K1, N1, N2 = c4["M"], c4["K1"], c4["N1"], c4["N2"]
+    inp = mlp2_inputs(M4, K1, N1, N2, seed=c4["seed"])
+    dx, d1, d2 = dv(inp["x"]), dv(inp["w1"]), dv(inp["w2"])
+    h = torch.empty((M4, N1), dtype=torch.int16, device="cuda")
+    y = torch.empty((M4, N2), dtype=torch.float32, device="cuda")
+    mlp_fn = lambda i, mode, opts=None: tsg.mlp2_pipelined(ctx, dx, d1, h, d2, y, M4, K1, N1, N2, opts=opts,
+                                                          mode=mode)
+    mlp_flops = 2.0 * M4 * N1 * K1 + 2.0 * M4 * N2 * N1
+    mlp_bytes = M4 * K1 * 2 + K1 * N1 * 2 + 2 * M4 * N1 * 2 + N1 * N2 * 2 + M4 * N2 * 4
+    out["mlp2"] = (mlp_fn, mlp_flops, mlp_bytes, (tsg.OVERLAP, tsg.SERIAL, tsg.COMPUTE_ONLY))
+
+    c5 = CONFIGS["moe"]
+    T, Hh, I, E, k = c5["T"], c5["H"], c5["I"], c5["E"], c5["k"]
+    inp = moe_inputs(T, Hh, I, E, k=k, seed=c5["seed"], zipf=c5["zipf"])
+    mx, ids, g, wu, wd = dv(inp["x"]), dv(inp["topk_ids"]), dv(inp["topk_w"]), dv(inp["w_up"]), dv(inp["w_down"])
+    mo = torch.empty((T, Hh), dtype=torch.float32, device="cuda")
+    cnt = torch.empty((E,), dtype=torch.int32, device="cuda")
+    srt = torch.empty((T * k,), dtype=torch.int32, device="cuda")
+    wsb = tsg.workspace_bytes(tsg.OP_MOE, [T, Hh, I, E, k])
+    ws = torch.empty((wsb,), dtype=torch.uint8, device="cuda")
+    moe_fn = lambda i, mode, opts=None: tsg.moe_expert_combine(ctx, mx, ids, g, wu, wd, mo, cnt, srt, ws, wsb,
+                                                               T, Hh, I, E, k, opts=opts, mode=mode)
+    moe_flops = 4.0 * T * k * Hh * I
+    moe_bytes = T * k * Hh * 2 + 2 * E * Hh * I * 2 + 2 * T * k * I * 2 + 2 * T * k * Hh * 4 + T * Hh * 4
+    out["moe"] = (moe_fn, moe_flops, moe_bytes, (tsg.OVERLAP, tsg.SERIAL, tsg.COMPUTE_ONLY, tsg.COMM_ONLY))
+    return out
+
+
+# Timeline record kinds (tsg_timeline): producer / consumer units of each path.
+TL_KINDS = {"ag_gemm": ((1, "copy units"), (2, "GEMM tiles")),
+            "gemm_rs": ((3, "GEMM tiles"), (4, "reduce units")),
+            "mlp2": ((5, "GEMM1 tiles"), (6, "GEMM2 tiles")),
+            "moe": ((7, "up tiles"), (8, "down tiles"), (9, "combine units"))}
+
+
+def _timeline_text(name, recs, bins=24):
+    """Markdown table of one overlapped call's device timeline: per time bin,
+    the units of each kind that are active, and how many of them are waiting
+    for a signal (records: {kind<<56 | where<<32 | id, start, start + wait,
+    end}, 100 MHz wall clock)."""
+    kinds = TL_KINDS[name]
+    rows = [(int(r[0]) >> 56, r[1], r[2], r[3]) for r in recs]
+    t0 = min(r[1] for r in rows)
+    t1 = max(r[3] for r in rows)
+    span = max(1, t1 - t0)
+    head = f"**{name}**: one overlapped call, span {span / 100:.1f} us.  Per bin of {span / bins / 100:.1f} us: " \
+           "units active (of which waiting for a signal)."
+    lines = [head, "", "| t (us) | " + " | ".join(k[1] for k in kinds) + " |",
+             "|---|" + "---|" * len(kinds)]
+    for b in range(bins):
+        lo, hi = t0 + span * b / bins, t0 + span * (b + 1) / bins
+        cells = []
+        for kind, _ in kinds:
+            act = sum(1 for r in rows if r[0] == kind and r[1] < hi and r[3] >= lo)
+            wt = sum(1 for r in rows if r[0] == kind and r[1] < hi and r[2] >= lo and r[2] > r[1])
+            cells.append(f"{act} ({wt})" if wt else f"{act}")
+        lines.append(f"| {(lo - t0) / 100:.1f} | " + " | ".join(cells) + " |")
+    return "\n".join(lines)
 
 
 def main():
@@ -268,11 +358,39 @@ def main():
     M, N, K, R = cfg["M"], cfg["N"], cfg["K"], cfg["R"]
     ag_fn, ag_flops, ag_gemm_bytes, ag_copy_bytes, ag_host = _path_ag(torch, tsg, ctx, cfg, args.steps, hopts)
 
+    if args.timeline:
+        # One overlapped call per path with device timestamps (after warm-up);
+        # AG also serialized, for comparison.
+        out = ["Device timelines (`python3 bench.py --timeline`), one call each.", ""]
+        runs = [("ag_gemm", ag_fn, tsg.OVERLAP), ("ag_gemm", ag_fn, tsg.SERIAL)]
+        if args.paths == "all":
+            for name, (fn, *_rest) in _other_paths(torch, tsg, ctx).items():
+                runs.append((name, fn, tsg.OVERLAP))
+        for name, fn, mode in runs:
+            for i in range(20):
+                fn(i, mode)
+            torch.cuda.synchronize()
+            fn(0, mode, tsg.Opts(aux_cus=args.aux_cus, tile=args.tile, timeline=1))
+            torch.cuda.synchronize()
+            if ctx.check() != tsg.OK:
+                raise RuntimeError(ctx.last_error())
+            label = {tsg.OVERLAP: "overlap", tsg.SERIAL: "serial"}[mode]
+            out += [f"### {name}, {label}", "", _timeline_text(name, ctx.timeline()), ""]
+        print("\n".join(out), flush=True)
+        ctx.close()
+        return
+
     if args.counters:
         for i in range(args.steps):
             ag_fn(i, tsg.COMPUTE_ONLY)
         for i in range(args.steps):
             ag_fn(i, tsg.COMM_ONLY)
+        if args.paths == "all":
+            for name, (fn, _f, _b, modes) in _other_paths(torch, tsg, ctx).items():
+                for mode in (tsg.COMPUTE_ONLY, tsg.COMM_ONLY):
+                    if mode in modes:
+                        for i in range(args.steps):
+                            fn(i, mode)
         torch.cuda.synchronize()
         src = torch.empty(1 << 29, dtype=torch.int16, device="cuda")
         dst = torch.empty_like(src)
@@ -317,62 +435,11 @@ def main():
     paths = {"ag_gemm": ag}
 
     if args.paths == "all":
-        c3 = CONFIGS["gemm_rs"]
-        inp = rs_inputs(c3["M"], c3["K"], c3["N"], c3["R"], rank=0, seed=c3["seed"])
-        x = torch.from_numpy(inp["x"].view(np.int16)).cuda()
-        w = torch.from_numpy(inp["w"].view(np.int16)).cuda()
-        pp = torch.from_numpy(inp["peer_partials"]).cuda()
-        P = torch.empty((c3["M"], c3["N"]), dtype=torch.float32, device="cuda")
-        o = torch.empty((c3["M"] // c3["R"], c3["N"]), dtype=torch.float32, device="cuda")
-        rs_fn = lambda i, mode: tsg.gemm_rs_overlap(ctx, x, w, P, pp, o, c3["M"], c3["N"], c3["K"], c3["R"], 0,
-                                                    mode=mode)
-        t = Timer(torch, tsg, ctx, rs_fn)
-        mr = c3["M"] // c3["R"]
-        rs_bytes = (c3["M"] * c3["K"] * 2 + c3["K"] * c3["N"] * 2 + c3["M"] * c3["N"] * 4
-                    + (c3["R"] - 1) * mr * c3["N"] * 4 + 2 * mr * c3["N"] * 4)
-        tm = t.modes((tsg.OVERLAP, tsg.SERIAL, tsg.COMPUTE_ONLY, tsg.COMM_ONLY), n)
-        paths["gemm_rs"] = _summary(2.0 * c3["M"] * c3["N"] * c3["K"], rs_bytes,
-                                    {"overlap": tm[tsg.OVERLAP], "serial": tm[tsg.SERIAL],
-                                     "compute_only": tm[tsg.COMPUTE_ONLY], "comm_only": tm[tsg.COMM_ONLY]})
-        del x, w, pp, P, o
-
-        c4 = CONFIGS["mlp2"]
-        inp = mlp2_inputs(c4["M"], c4["K1"], c4["N1"], c4["N2"], seed=c4["seed"])
-        dx, d1, d2 = (torch.from_numpy(inp[k].view(np.int16)).cuda() for k in ("x", "w1", "w2"))
-        h = torch.empty((c4["M"], c4["N1"]), dtype=torch.int16, device="cuda")
-        y = torch.empty((c4["M"], c4["N2"]), dtype=torch.float32, device="cuda")
-        mlp_fn = lambda i, mode: tsg.mlp2_pipelined(ctx, dx, d1, h, d2, y, c4["M"], c4["K1"], c4["N1"], c4["N2"],
-                                                    mode=mode)
-        t = Timer(torch, tsg, ctx, mlp_fn)
-        mlp_flops = 2.0 * c4["M"] * c4["N1"] * c4["K1"] + 2.0 * c4["M"] * c4["N2"] * c4["N1"]
-        mlp_bytes = (c4["M"] * c4["K1"] * 2 + c4["K1"] * c4["N1"] * 2 + 2 * c4["M"] * c4["N1"] * 2
-                     + c4["N1"] * c4["N2"] * 2 + c4["M"] * c4["N2"] * 4)
-        tm = t.modes((tsg.OVERLAP, tsg.SERIAL, tsg.COMPUTE_ONLY), n)
-        paths["mlp2"] = _summary(mlp_flops, mlp_bytes,
-                                 {"overlap": tm[tsg.OVERLAP], "serial": tm[tsg.SERIAL],
-                                  "compute_only": tm[tsg.COMPUTE_ONLY], "comm_only": None})
-        del dx, d1, d2, h, y
-
-        c5 = CONFIGS["moe"]
-        T, Hh, I, E, k = c5["T"], c5["H"], c5["I"], c5["E"], c5["k"]
-        inp = moe_inputs(T, Hh, I, E, k=k, seed=c5["seed"], zipf=c5["zipf"])
-        dv = lambda a: torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).cuda()
-        mx, ids, g, wu, wd = dv(inp["x"]), dv(inp["topk_ids"]), dv(inp["topk_w"]), dv(inp["w_up"]), dv(inp["w_down"])
-        out = torch.empty((T, Hh), dtype=torch.float32, device="cuda")
-        cnt = torch.empty((E,), dtype=torch.int32, device="cuda")
-        srt = torch.empty((T * k,), dtype=torch.int32, device="cuda")
-        wsb = tsg.workspace_bytes(tsg.OP_MOE, [T, Hh, I, E, k])
-        ws = torch.empty((wsb,), dtype=torch.uint8, device="cuda")
-        moe_fn = lambda i, mode: tsg.moe_expert_combine(ctx, mx, ids, g, wu, wd, out, cnt, srt, ws, wsb,
-                                                        T, Hh, I, E, k, mode=mode)
-        t = Timer(torch, tsg, ctx, moe_fn)
-        moe_flops = 4.0 * T * k * Hh * I
-        moe_bytes = (T * k * Hh * 2 + 2 * E * Hh * I * 2 + 2 * T * k * I * 2 + 2 * T * k * Hh * 4
-                     + T * Hh * 4)
-        tm = t.modes((tsg.OVERLAP, tsg.SERIAL, tsg.COMPUTE_ONLY, tsg.COMM_ONLY), n)
-        paths["moe"] = _summary(moe_flops, moe_bytes,
-                                {"overlap": tm[tsg.OVERLAP], "serial": tm[tsg.SERIAL],
-                                 "compute_only": tm[tsg.COMPUTE_ONLY], "comm_only": tm[tsg.COMM_ONLY]})
+        for name, (fn, flops, nbytes, modes) in _other_paths(torch, tsg, ctx).items():
+            tm = Timer(torch, tsg, ctx, fn).modes(modes, n)
+            paths[name] = _summary(flops, nbytes,
+                                   {"overlap": tm[tsg.OVERLAP], "serial": tm[tsg.SERIAL],
+                                    "compute_only": tm[tsg.COMPUTE_ONLY], "comm_only": tm.get(tsg.COMM_ONLY)})
 
     tflops = ag_flops / (ms_step * 1e-3) / 1e12
     achieved = ag_flops / (k_ov[0] * 1e-3) / 1e12

@@ -284,16 +284,39 @@ struct GemmTile {
   // k = 16 ks + 8 (l / 32) + 4 t and its columns at n = 16 ((l / 16) mod 2)
   // of the fragment, lane l ends up with column (l mod 32) and k values
   // 8 (l / 32) .. + 7 of sub-step ks (t = 0, 1): the MFMA B operand layout.
-  __device__ __forceinline__ static uint32_t tr_lane_offset(int wn0) {
+  // B stages are row-major with BN columns.  When a row is a multiple of 128
+  // bytes every row starts at the same bank, and the four rows that one
+  // transpose read touches collide: half a wave reads 64 bytes of each of
+  // four rows, which fill the 64 banks only if the rows' pieces land on
+  // different banks.  The 16-byte chunk c of row r is then stored at
+  // position c ^ (4 (r mod 4)) (rows of a multiple of 256 bytes) or
+  // c ^ (2 (r mod 4)) (rows of an odd multiple of 128 bytes, which leaves a
+  // two-way overlap); chunks are permuted within aligned groups of 16 or 8,
+  // so a row keeps its place.
+  static constexpr int B_SWZ = Cfg::BN % 128 == 0 ? 4 : Cfg::BN % 64 == 0 ? 2 : 0;
+  __device__ __forceinline__ static int b_swz(int row) { return B_SWZ * (row & 3); }
+
+  // LDS byte offset of this lane's transpose reads of B fragment j (32
+  // columns at wn0 + 32 j), step 0: lane 4i + q of each 16-lane group points
+  // at row i, columns 4q .. 4q + 3; lanes 16-31 take the next 16 columns and
+  // lanes 32-63 rows 8-11.  The second read of a fragment is 4 rows further,
+  // step ks 16 rows further (neither changes row mod 4).
+  __device__ __forceinline__ static void tr_lane_offsets(int wn0, uint32_t (&off)[Cfg::FN]) {
     const int lane = threadIdx.x & 63;
     const int hi = lane >> 5, g = lane >> 4, sl = lane & 15;
-    return (uint32_t)(((8 * hi + (sl >> 2)) * Cfg::BN + wn0 + 16 * (g & 1) + 4 * (sl & 3)) * 2);
+    const int row = 8 * hi + (sl >> 2);
+#pragma unroll
+    for (int j = 0; j < Cfg::FN; ++j) {
+      const int col = wn0 + 32 * j + 16 * (g & 1) + 4 * (sl & 3);
+      const int chunk = (col >> 3) ^ b_swz(row);
+      off[j] = (uint32_t)((row * Cfg::BN + chunk * 8 + (col & 7)) * 2);
+    }
   }
 
-  __device__ __forceinline__ static bf16x8_t read_b_tr(const char* lb, uint32_t lane_off, int ks, int j) {
+  __device__ __forceinline__ static bf16x8_t read_b_tr(const char* lb, uint32_t lane_off, int ks) {
     typedef short v4i16 __attribute__((ext_vector_type(4)));
     typedef short v8i16 __attribute__((ext_vector_type(8)));
-    const char* p = lb + lane_off + (ks * 16 * Cfg::BN + j * 32) * 2;
+    const char* p = lb + lane_off + ks * 16 * Cfg::BN * 2;
     const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p);
     const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (__attribute__((address_space(3))) v4i16*)(p + 4 * Cfg::BN * 2));
@@ -302,8 +325,8 @@ struct GemmTile {
   }
 
   // One BK step: A from a swizzled stage, B from a row-major stage.
-  __device__ __forceinline__ static void compute_tr(const char* la, const char* lb, uint32_t tr_off,
-                                                    Acc& acc) {
+  __device__ __forceinline__ static void compute_tr(const char* la, const char* lb,
+                                                    const uint32_t (&tr_off)[Cfg::FN], Acc& acc) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int wm0 = (wave / Cfg::WN) * Cfg::WTM;
@@ -315,7 +338,7 @@ struct GemmTile {
       for (int i = 0; i < Cfg::FM; ++i)
         af[buf][i] = *(const bf16x8_t*)(la + lds_swz(wm0 + i * 32 + l32, 2 * ks + hi));
 #pragma unroll
-      for (int j = 0; j < Cfg::FN; ++j) bfr[buf][j] = read_b_tr(lb, tr_off, ks, j);
+      for (int j = 0; j < Cfg::FN; ++j) bfr[buf][j] = read_b_tr(lb, tr_off[j], ks);
     };
     rd(0, 0);
 #pragma unroll
@@ -365,15 +388,16 @@ struct GemmTile {
       if (off < 0) off = ar.stand_in();  // outside the operand: result never stored
       a_off[t] = (uint32_t)((off + lds_pos(r, lane & 7) * 8) * 2);
     }
-    // B: 16-byte chunk c = 64 blk + lane of a stage is row c / (BN/8), column
-    // 8 (c mod (BN/8)); columns at or beyond N read the operand's last 8
-    // columns instead (their results are never stored).
+    // B: 16-byte chunk c = 64 blk + lane of a stage is row c / (BN/8) at
+    // position c mod (BN/8), which holds column chunk position ^ b_swz(row);
+    // columns at or beyond N read the operand's last 8 columns instead (their
+    // results are never stored).
     uint32_t b_off[B_BPW];
 #pragma unroll
     for (int t = 0; t < B_BPW; ++t) {
       const int c = (wave + t * Cfg::NW) * 64 + lane;
       const int row = c / (Cfg::BN / 8);
-      int col = col0 + (c % (Cfg::BN / 8)) * 8;
+      int col = col0 + ((c % (Cfg::BN / 8)) ^ b_swz(row)) * 8;
       if (col >= N) col = N - 8;
       b_off[t] = (uint32_t)(((int64_t)row * ldb + col) * 2);
     }
@@ -402,7 +426,8 @@ struct GemmTile {
       }
     };
     const int wn0 = (wave % Cfg::WN) * Cfg::WTN;
-    const uint32_t tr_off = tr_lane_offset(wn0);
+    uint32_t tr_off[Cfg::FN];
+    tr_lane_offsets(wn0, tr_off);
 
     const int nk = K / Cfg::BK;
     hook.before_a(0);
