@@ -155,7 +155,7 @@ __global__ void __launch_bounds__(256) mlp_fused_kernel(const MlpFusedArgs f) {
   constexpr int L1 = D1 ? C1::LDS_DIRECT : C1::LDS_REGS;
   constexpr int L2 = D2 ? C2::LDS_DIRECT : C2::LDS_REGS;
   __shared__ __attribute__((aligned(16))) char lds[L1 > L2 ? L1 : L2];
-  const int my_xcd = (int)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & 7);  // XCC_ID
+  const int my_xcd = xcd_id();
   // The ticket goes through the first word of the tile buffer, which is free
   // between items (a tile's last LDS read precedes its pipeline's final
   // barrier; the next tile writes LDS only after the second barrier here).
@@ -164,40 +164,9 @@ __global__ void __launch_bounds__(256) mlp_fused_kernel(const MlpFusedArgs f) {
   auto fetch = [&]() -> int {
     volatile int* s_item = (volatile int*)lds;
     if (threadIdx.x < 64) {
-      // Wave 0 claims the item.  Each phase: the own XCD's queue first; if
-      // that is used up, one load per queue shows which still have tickets,
-      // and only those are tried.  A failed claim proves its queue used up,
-      // so a phase is left only once all its items are taken.
-      const int lane = threadIdx.x;
-      int item = -1;
-      for (int ph = 0; ph < 2 && item < 0; ++ph) {
-        const int n = ph == 0 ? f.n_items1 : f.n_items2;
-        const int base = ph == 0 ? 0 : f.n_items1;
-        auto claim = [&](int x) {
-          const int lo = (int)((int64_t)n * x / 8), hi = (int)((int64_t)n * (x + 1) / 8);
-          if (hi == lo) return;
-          uint32_t t = 0;
-          if (lane == 0) t = atomicAdd(f.queues + ph * 8 + x, 1u);
-          t = __builtin_amdgcn_readfirstlane(t);
-          if (t < (uint32_t)(hi - lo)) item = base + lo + (int)t;
-        };
-        claim(my_xcd);
-        if (item < 0) {
-          bool open = false;
-          if (lane < 8 && lane != my_xcd) {
-            const int lo = (int)((int64_t)n * lane / 8), hi = (int)((int64_t)n * (lane + 1) / 8);
-            const uint32_t c = __hip_atomic_load(f.queues + ph * 8 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            open = c < (uint32_t)(hi - lo);
-          }
-          uint64_t cand = __builtin_amdgcn_ballot_w64(open);
-          while (cand != 0 && item < 0) {
-            const int x = (int)__builtin_ctzll(cand);
-            cand &= cand - 1;
-            claim(x);
-          }
-        }
-      }
-      if (lane == 0) *s_item = item;
+      const int n[2] = {f.n_items1, f.n_items2};
+      const QueueItem it = xcd_queue_claim<2>(f.queues, n, my_xcd);
+      if (threadIdx.x == 0) *s_item = it.phase < 0 ? -1 : (it.phase == 0 ? 0 : f.n_items1) + it.index;
     }
     __syncthreads();
     const int v = __builtin_amdgcn_readfirstlane(*s_item);

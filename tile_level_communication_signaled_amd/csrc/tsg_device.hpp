@@ -235,6 +235,56 @@ __device__ __forceinline__ void block_wait_lines(const uint64_t* s, uint64_t tar
   acquire_lines(line_exclusive);
 }
 
+// Per-XCD phased work queues of a persistent kernel.  Phase p has n[p]
+// items, cut into 8 contiguous shares (share x = [n x / 8, n (x + 1) / 8)),
+// one ticket counter per (phase, XCD) at q[8 p + x].  The items an XCD runs
+// then form a compact block whose operands its L2 can reuse.  Called by all
+// lanes of one wave with uniform arguments; returns the phase and the index
+// in the phase (uniform), or phase -1 once every phase is used up.  Within a
+// phase the wave tries its own XCD's share first; if that is used up, one
+// load per counter shows which shares still have tickets, and only those are
+// tried.  A failed claim proves its share used up, so a wave leaves phase p
+// only once every item of phase p has been taken.
+struct QueueItem {
+  int phase, index;
+};
+template <int NP>
+__device__ __forceinline__ QueueItem xcd_queue_claim(uint32_t* q, const int (&n)[NP], int my_xcd) {
+  const int lane = __lane_id();
+  for (int ph = 0; ph < NP; ++ph) {
+    const int np = n[ph];
+    int got = -1;
+    auto claim = [&](int x) {
+      const int lo = (int)((int64_t)np * x / 8), hi = (int)((int64_t)np * (x + 1) / 8);
+      if (hi == lo) return;
+      uint32_t t = 0;
+      if (lane == 0) t = atomicAdd(q + ph * 8 + x, 1u);
+      t = __builtin_amdgcn_readfirstlane(t);
+      if (t < (uint32_t)(hi - lo)) got = lo + (int)t;
+    };
+    claim(my_xcd);
+    if (got < 0) {
+      bool open = false;
+      if (lane < 8 && lane != my_xcd) {
+        const int lo = (int)((int64_t)np * lane / 8), hi = (int)((int64_t)np * (lane + 1) / 8);
+        const uint32_t c = __hip_atomic_load(q + ph * 8 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        open = c < (uint32_t)(hi - lo);
+      }
+      uint64_t cand = __builtin_amdgcn_ballot_w64(open);
+      while (cand != 0 && got < 0) {
+        const int x = (int)__builtin_ctzll(cand);
+        cand &= cand - 1;
+        claim(x);
+      }
+    }
+    if (got >= 0) return QueueItem{ph, got};
+  }
+  return QueueItem{-1, 0};
+}
+
+// The XCD the calling wave runs on (XCC_ID hardware register).
+__device__ __forceinline__ int xcd_id() { return (int)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & 7); }
+
 // Workgroups are dispatched round-robin over the 8 XCDs, each with its own
 // L2.  Map launch index w to a logical tile index so that every XCD runs a
 // contiguous block of `per_xcd` logical tiles out of each wave of
