@@ -41,7 +41,7 @@ using namespace tsg;
 namespace {
 
 constexpr int BM = 128;                 // row padding unit and tile rows
-constexpr int BN_UP = 128;
+constexpr int BN_UP = 256;
 constexpr int BN_DN = 256;
 constexpr int kCombMaxRb = 4096;         // row blocks the combine's partner list can name
 constexpr int kRouteThreads = 256;
