@@ -324,33 +324,28 @@ struct GemmTile {
     return __builtin_bit_cast(bf16x8_t, w);
   }
 
-  // One BK step: A from a swizzled stage, B from a row-major stage.
-  __device__ __forceinline__ static void compute_tr(const char* la, const char* lb,
-                                                    const uint32_t (&tr_off)[Cfg::FN], Acc& acc) {
+  // MFMA fragments of one 16-wide k step ks of a BK step: A from a swizzled
+  // stage, B from a row-major stage through transpose reads.
+  struct Frags {
+    bf16x8_t a[Cfg::FM], b[Cfg::FN];
+  };
+  __device__ __forceinline__ static void read_frags(Frags& f, const char* la, const char* lb,
+                                                    const uint32_t (&tr_off)[Cfg::FN], int ks) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int wm0 = (wave / Cfg::WN) * Cfg::WTM;
-    const int l32 = lane & 31;
-    const int hi = lane >> 5;
-    bf16x8_t af[2][Cfg::FM], bfr[2][Cfg::FN];
-    auto rd = [&](int buf, int ks) {
 #pragma unroll
-      for (int i = 0; i < Cfg::FM; ++i)
-        af[buf][i] = *(const bf16x8_t*)(la + lds_swz(wm0 + i * 32 + l32, 2 * ks + hi));
+    for (int i = 0; i < Cfg::FM; ++i)
+      f.a[i] = *(const bf16x8_t*)(la + lds_swz(wm0 + i * 32 + (lane & 31), 2 * ks + (lane >> 5)));
 #pragma unroll
-      for (int j = 0; j < Cfg::FN; ++j) bfr[buf][j] = read_b_tr(lb, tr_off[j], ks);
-    };
-    rd(0, 0);
+    for (int j = 0; j < Cfg::FN; ++j) f.b[j] = read_b_tr(lb, tr_off[j], ks);
+  }
+  __device__ __forceinline__ static void mma(const Frags& f, Acc& acc) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      if (ks + 1 < 4) rd((ks + 1) & 1, ks + 1);
+    for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
-      for (int i = 0; i < Cfg::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < Cfg::FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][i], bfr[ks & 1][j],
-                                                               acc[i][j], 0, 0, 0);
-    }
+      for (int j = 0; j < Cfg::FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
   }
 
   // Main path (K % 128 == 0): both operands go from global memory straight
@@ -358,8 +353,9 @@ struct GemmTile {
   // the swizzled layout; B two stages, row-major, read with transpose reads.
   // Step kt: the loads of B for step kt + 1 and of A for step kt + 2 are
   // issued first (into the stages step kt - 1 vacated), then step kt is
-  // computed; the wait then leaves only the A loads just issued in flight, so
-  // everything step kt + 1 reads has landed before the barrier.
+  // computed; before its last k step, the wait leaves only the A loads just
+  // issued in flight, so everything step kt + 1 reads has landed before the
+  // barrier.
   // LDS layout: [A0 A1 A2 B0 B1], Cfg::LDS_DIRECT bytes.
   template <class ARows, class Hook = NoHook>
   __device__ __forceinline__ static void run_direct(const ARows& ar,
@@ -441,6 +437,14 @@ struct GemmTile {
       wait_vmcnt<0>();
     }
     lds_barrier();
+    // Fragments are double-buffered across the four k steps of a BK step and
+    // across BK steps: the wait and barrier that make the next stage readable
+    // come after the last fragment read of the current stage, and the first
+    // fragments of the next stage are read while the current stage's last
+    // MFMAs run, so neither the barrier nor the LDS latency of a stage's first
+    // reads leaves the matrix units idle.
+    Frags f0, f1;
+    read_frags(f0, lds_a, lds_b, tr_off, 0);
     int sa = 0;  // kt % 3
     for (int kt = 0; kt < nk; ++kt) {
       const int sa2 = sa >= 1 ? sa - 1 : 2;   // (kt + 2) % 3
@@ -449,11 +453,23 @@ struct GemmTile {
         hook.before_a((kt + 2) * Cfg::BK);
         issue_a(sa2, (kt + 2) * Cfg::BK);
       }
-      compute_tr(lds_a + sa * Cfg::A_STAGE, lds_b + (kt & 1) * Cfg::B_STAGE, tr_off, acc);
-      if (kt + 2 < nk) wait_vmcnt<Cfg::A_BPW>(); else wait_vmcnt<0>();
-      lds_barrier();
+      const char* la = lds_a + sa * Cfg::A_STAGE;
+      const char* lb = lds_b + (kt & 1) * Cfg::B_STAGE;
+      read_frags(f1, la, lb, tr_off, 1);
+      mma(f0, acc);
+      read_frags(f0, la, lb, tr_off, 2);
+      mma(f1, acc);
+      read_frags(f1, la, lb, tr_off, 3);
+      mma(f0, acc);
       sa = sa == 2 ? 0 : sa + 1;
+      if (kt + 1 < nk) {
+        if (kt + 2 < nk) wait_vmcnt<Cfg::A_BPW>(); else wait_vmcnt<0>();
+        lds_barrier();
+        read_frags(f0, lds_a + sa * Cfg::A_STAGE, lds_b + ((kt + 1) & 1) * Cfg::B_STAGE, tr_off, 0);
+      }
+      mma(f1, acc);
     }
+    lds_barrier();  // every wave is done with the stages before the LDS is reused
   }
 
   // Fallback path (any K multiple of 8): A and B staged through registers,
