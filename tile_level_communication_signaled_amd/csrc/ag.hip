@@ -80,7 +80,8 @@ struct CopyArgs {
 // slab 0 before it can start, slab 1 soon after, and so on, while later
 // slabs have time to arrive in larger pieces, which need fewer store drains and arrivals.
 // Moves unit u and arrives on its slab's signal.  Called by every thread of
-// the workgroup with the same u.
+// a workgroup of NT threads with the same u.
+template <int NT>
 __device__ __forceinline__ void copy_unit(const CopyArgs& a, int u) {
   constexpr int U = 8;  // 8-byte words in flight per thread
   const int vpr = 1 << a.vpr_log2;
@@ -116,13 +117,15 @@ __device__ __forceinline__ void copy_unit(const CopyArgs& a, int u) {
   // whole rows of a narrow slab) and writes whole lines: stores of 16 bytes
   // per lane would go out as two 8-byte halves, each instruction writing
   // every other 8 bytes.  A slab row is wpr <= 512 words; thread t moves word
-  // t mod tpr (+ 256 when the row is wider than the workgroup) of rows
+  // t mod tpr (+ NT when the row is wider than the workgroup) of rows
   // t / tpr, t / tpr + rows_p, ...  Addresses are a uniform base plus a
   // 32-bit byte offset (one register per access).
+  static_assert(NT == 256 || NT == 512, "copy workgroups of 256 or 512 threads");
+  constexpr int NT_LOG2 = NT == 256 ? 8 : 9;
   const int wpr = 2 * vpr;
-  const int tpr_log2 = min(a.vpr_log2 + 1, 8);
+  const int tpr_log2 = min(a.vpr_log2 + 1, NT_LOG2);
   const int tpr = 1 << tpr_log2;
-  const int rows_p = 256 >> tpr_log2;
+  const int rows_p = NT >> tpr_log2;
   const int rr = threadIdx.x >> tpr_log2;
   const int wwidth = 2 * width;
   const char* sb = (const char*)src;
@@ -130,7 +133,7 @@ __device__ __forceinline__ void copy_unit(const CopyArgs& a, int u) {
   const uint32_t row_bytes = (uint32_t)(a.k8 * 16);
   const uint32_t step = (uint32_t)rows_p * row_bytes;
   const int cw = threadIdx.x & (tpr - 1);
-  for (int k = 0; k < wpr; k += 256) {  // a second pass only for rows of 512 words
+  for (int k = 0; k < wpr; k += NT) {  // a second pass only for rows wider than the workgroup
     if (cw + k < wwidth) {
       const char* sk = sb + k * 8;
       char* dk = db + k * 8;
@@ -179,7 +182,7 @@ __device__ __forceinline__ void leave_queue(const CopyArgs& a) {
 // is left.  It never waits, so it always drains the queue.
 __global__ void __launch_bounds__(256) ag_copy_kernel(const CopyArgs a) {
   __shared__ int slot;
-  for (int u = claim_unit(a, &slot); u < a.n_units; u = claim_unit(a, &slot)) copy_unit(a, u);
+  for (int u = claim_unit(a, &slot); u < a.n_units; u = claim_unit(a, &slot)) copy_unit<256>(a, u);
   if (threadIdx.x == 0) leave_queue(a);
 }
 
@@ -273,11 +276,11 @@ __global__ void __launch_bounds__(Cfg::NT) ag_gemm_kernel(const AgGemmArgs args)
   const int nt = w % args.n_tiles_n;
   const int row0 = mt * Cfg::BM, col0 = nt * Cfg::BN;
   const uint64_t t0 = args.tl.buf ? wall_clock64() : 0;
-  if (Cfg::NT == 256 && (int)blockIdx.x < args.pull_wgs) {
+  if ((Cfg::NT == 256 || Cfg::NT == 512) && (int)blockIdx.x < args.pull_wgs) {
     // tile_pull_data: move one unit of the copy's queue before any wait (the
     // LDS is not in use yet, so its first word carries the ticket)
     const int u = claim_unit(args.copy, (volatile int*)lds);
-    if (u < args.copy.n_units) copy_unit(args.copy, u);
+    if (u < args.copy.n_units) copy_unit<Cfg::NT>(args.copy, u);
     if (threadIdx.x == 0) leave_queue(args.copy);
   }
   SlabWait hook;
@@ -335,6 +338,7 @@ using Cfg4 = TileCfg<256, 128, 2, 2>;
 using Cfg5 = TileCfg<128, 256, 2, 2>;
 using Cfg6 = TileCfg<64, 64, 1, 1>;
 using Cfg7 = TileCfg<128, 64, 2, 1>;
+using Cfg8 = TileCfg<256, 224, 8, 1>;
 
 struct TileShape {
   int bm, bn;
@@ -349,6 +353,7 @@ TileShape shape_of(int id) {
     case 5: return {128, 256};
     case 6: return {64, 64};
     case 7: return {128, 64};
+    case 8: return {256, 224};
     default: return {0, 0};
   }
 }
@@ -389,6 +394,7 @@ const void* gemm_fn(int id, bool bf16, int K, int* nt) {
     TSG_AG_CFG(5, Cfg5)
     TSG_AG_CFG(6, Cfg6)
     TSG_AG_CFG(7, Cfg7)
+    TSG_AG_CFG(8, Cfg8)
 #undef TSG_AG_CFG
     default: *nt = 0; return nullptr;
   }
@@ -403,13 +409,15 @@ hipError_t launch_gemm(int id, const AgGemmArgs& a, bool bf16, int grid, hipStre
     case 5: return launch_gemm_cfg<Cfg5>(a, bf16, grid, s);
     case 6: return launch_gemm_cfg<Cfg6>(a, bf16, grid, s);
     case 7: return launch_gemm_cfg<Cfg7>(a, bf16, grid, s);
+    case 8: return launch_gemm_cfg<Cfg8>(a, bf16, grid, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 int default_tile(int M, int N) {
-  // 256 x 224 when it gives whole waves of 256 tiles (e.g. 8192 x 1792)
-  if (N % 224 == 0 && M % 256 == 0 && ((M / 256) * (N / 224)) % 256 == 0) return 2;
+  // 256 x 224 (eight waves of 32 rows) when it gives whole waves of 256
+  // tiles (e.g. 8192 x 1792)
+  if (N % 224 == 0 && M % 256 == 0 && ((M / 256) * (N / 224)) % 256 == 0) return 8;
   if (M >= 2048 && N >= 1024) return 1;
   if (M >= 512 && N >= 256) return 3;
   return 6;
@@ -603,14 +611,15 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
   ca.n_units = (int)n_units;
   ca.skip_mask = o.skip_mask;
   ca.queue = ctx->d_queue + kQueueSlot;
-  // Units the GEMM pulls itself (overlap on shared CUs, tiles of 256 threads,
+  // Units the GEMM pulls itself (overlap on shared CUs, tiles of 256 or 512 threads,
   // whose workgroups move a unit the way the copy's do): by default one per
   // workgroup of the first wave of tiles, at most the first slab's units.
   const int copy_grid = (int)std::min<int64_t>(nwg, n_units);
   int pull = 0;
   int gemm_nt = 0;
   (void)gemm_fn(tile, c_dtype == TSG_BF16, K, &gemm_nt);
-  if (mode == TSG_MODE_OVERLAP && !back_to_back && o.aux_cus < 0 && o.pull_units >= 0 && gemm_nt == 256) {
+  if (mode == TSG_MODE_OVERLAP && !back_to_back && o.aux_cus < 0 && o.pull_units >= 0 &&
+      (gemm_nt == 256 || gemm_nt == 512)) {
     pull = o.pull_units > 0 ? o.pull_units : std::min(ctx->n_cus, ustart[1]);
     pull = (int)std::min<int64_t>(std::min(pull, grid_gemm), n_units);
   }
