@@ -276,12 +276,14 @@ __global__ void __launch_bounds__(Cfg::NT) ag_gemm_kernel(const AgGemmArgs args)
   const int nt = w % args.n_tiles_n;
   const int row0 = mt * Cfg::BM, col0 = nt * Cfg::BN;
   const uint64_t t0 = args.tl.buf ? wall_clock64() : 0;
-  if ((Cfg::NT == 256 || Cfg::NT == 512) && (int)blockIdx.x < args.pull_wgs) {
-    // tile_pull_data: move one unit of the copy's queue before any wait (the
-    // LDS is not in use yet, so its first word carries the ticket)
-    const int u = claim_unit(args.copy, (volatile int*)lds);
-    if (u < args.copy.n_units) copy_unit<Cfg::NT>(args.copy, u);
-    if (threadIdx.x == 0) leave_queue(args.copy);
+  if constexpr (Cfg::NT == 256 || Cfg::NT == 512) {
+    if ((int)blockIdx.x < args.pull_wgs) {
+      // tile_pull_data: move one unit of the copy's queue before any wait
+      // (the LDS is not in use yet, so its first word carries the ticket)
+      const int u = claim_unit(args.copy, (volatile int*)lds);
+      if (u < args.copy.n_units) copy_unit<Cfg::NT>(args.copy, u);
+      if (threadIdx.x == 0) leave_queue(args.copy);
+    }
   }
   SlabWait hook;
   hook.active = false;
