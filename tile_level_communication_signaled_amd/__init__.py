@@ -5,7 +5,7 @@ kernels.  Tensors are passed by device address (``tensor.data_ptr()``);
 streams by their HIP handle (``torch.cuda.current_stream().cuda_stream``).
 Anything with a ``data_ptr()`` method (a torch tensor) or a plain integer
 address is accepted.  The library must have been built
-(``python -m tile_level_communication_signaled_amd.build``); importing this
+(``python tile_level_communication_signaled_amd/build.py``); importing this
 package without it raises ImportError.
 """
 from __future__ import annotations
@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libtsg.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with "
-                      "`python -m tile_level_communication_signaled_amd.build`")
+                      "`python tile_level_communication_signaled_amd/build.py`")
 _lib = ctypes.CDLL(LIB_PATH)
 
 # status codes
