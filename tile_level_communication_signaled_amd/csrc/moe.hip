@@ -15,13 +15,13 @@
 //   1. moe_route_kernel (one workgroup): expert_counts, a stable counting sort
 //      of the pairs p = t*k + s by expert (sorted_ids, order (expert, t, s)),
 //      and the lookup tables of the padded layout: every expert's rows are
-//      padded to a multiple of BM = 128, row block rb belongs to one expert,
+//      padded to a multiple of BM = 256, row block rb belongs to one expert,
 //      row_pair[row] = pair id or -1, row_token[row] = token or -1,
 //      pair_row[p] = padded row of pair p.
 //   2. moe_producer_kernel (persistent, atomic work queue): first every "up"
-//      tile (row block rb, 128 columns of I): gather x rows through row_token,
+//      tile (row block rb, 224 columns of I): gather x rows through row_token,
 //      multiply by w_up[e], h = bf16(SiLU(u)); each arrives on the signal of
-//      its row block.  Then every "down" tile (rb, 256 columns of H): acquire
+//      its row block.  Then every "down" tile (rb, 224 columns of H): acquire
 //      the row block's signal (all up tiles of rb done), y = h w_down[e] in
 //      fp32 into the staging buffer, release the tile's ready signal.
 //   3. The combine (combine_unit), per down tile in queue order: acquire
@@ -40,9 +40,9 @@ using namespace tsg;
 
 namespace {
 
-constexpr int BM = 128;                 // row padding unit and tile rows
-constexpr int BN_UP = 256;
-constexpr int BN_DN = 256;
+constexpr int BM = 256;                 // row padding unit and tile rows
+constexpr int BN_UP = 224;
+constexpr int BN_DN = 224;
 constexpr int kCombMaxRb = 4096;         // row blocks the combine's partner list can name
 constexpr int kRouteThreads = 256;
 constexpr int kMaxExperts = 256;
@@ -50,8 +50,13 @@ constexpr size_t kSigH = size_t(1) << 19;          // h row-block signals
 constexpr size_t kSigReady = kSigH + 65536;         // ready signals of down tiles
 constexpr size_t kSigEnd = kSigReady + 262144;
 
-using CfgUp = TileCfg<BM, BN_UP, 2, 2>;
-using CfgDn = TileCfg<BM, BN_DN, 2, 2>;
+// Eight waves of 32 x 224: two waves per SIMD, 112 accumulator registers
+// each, so the persistent kernel holds both tile paths and the combine
+// without spilling.
+using CfgUp = TileCfg<BM, BN_UP, 8, 1>;
+using CfgDn = TileCfg<BM, BN_DN, 8, 1>;
+constexpr int kProdThreads = CfgUp::NT;
+static_assert(CfgDn::NT == kProdThreads, "up and down tiles share the workgroup");
 
 // Workspace layout (byte offsets, 256-aligned).
 struct Layout {
@@ -236,19 +241,19 @@ struct ProdArgs {
 
 // ---------------------------------------------------------------- combine
 
-// Combine consumer.  Unit = one down tile (128 rows x BN_DN columns of y),
+// Combine consumer.  Unit = one down tile (BM rows x BN_DN columns of y),
 // in the producer's order (row block major).  A token is combined by the
 // later of the two row blocks holding its slots, so every token is written
 // exactly once: out[t] = g0 * y(slot 0) + g1 * y(slot 1), products and sum
 // rounded in that order (an absent slot contributes 0).
-//   1. Threads 0..127 read the routing of the unit's rows (pair, partner
+//   1. Threads 0..BM-1 read the routing of the unit's rows (pair, partner
 //      row, token, gates) into LDS, and list the partner row blocks that
 //      precede this one (their tiles must be ready too), once each.
 //   2. Wave 0 reads every listed partner tile's signal in one load per 64,
 //      polls only those not yet published, and the workgroup acquires.
-//   3. Each wave takes 32 rows: eight rows at a time it issues all sixteen
-//      16-byte loads of y (both slots, this lane's 4 columns), then combines
-//      and stores them.
+//   3. Each wave takes an equal share of the rows: eight rows at a time it
+//      issues all sixteen 16-byte loads of y (both slots, this lane's 4
+//      columns), then combines and stores them.
 // Called by every thread of the workgroup with uniform (rb, nt); `scratch`
 // is kCombScratch bytes of LDS owned by the caller for the call.
 constexpr int kCombScratch = 8 * BM * 4 + 16;
@@ -319,10 +324,11 @@ __device__ __forceinline__ void combine_unit(const CombArgs& a, int rb, int nt, 
   __syncthreads();  // y is read with coherent loads: no cache invalidation
   const uint64_t t1 = a.tl.buf ? wall_clock64() : 0;
   const int col = nt * BN_DN + lane * 4;
-  const bool col_ok = col < a.H;
+  const bool col_ok = lane * 4 < BN_DN && col < a.H;
+  const int rpw = BM / (int)(blockDim.x >> 6);   // rows per wave (a multiple of 8)
 #pragma unroll 1
-  for (int g = 0; g < 4; ++g) {
-    const int j0 = wave * 32 + g * 8;
+  for (int g = 0; g < rpw / 8; ++g) {
+    const int j0 = wave * rpw + g * 8;
     float4 v0[8], v1[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -371,11 +377,10 @@ __global__ void __launch_bounds__(256) moe_combine_kernel(const CombArgs a) {
 // down tiles), which running workgroups took before it and complete without
 // waiting on later ones.
 template <bool DIRECT_UP, bool DIRECT_DN>
-__global__ void __launch_bounds__(256) moe_producer_kernel(const ProdArgs a) {
+__global__ void __launch_bounds__(kProdThreads) moe_producer_kernel(const ProdArgs a) {
   constexpr int LUP = DIRECT_UP ? CfgUp::LDS_DIRECT : CfgUp::LDS_REGS;
   constexpr int LDN = DIRECT_DN ? CfgDn::LDS_DIRECT : CfgDn::LDS_REGS;
   __shared__ __attribute__((aligned(16))) char lds[LUP > LDN ? LUP : LDN];
-  __shared__ int s_item;
   // Every value that steers a loop or branch around a barrier is made
   // wave-uniform (readfirstlane): values read from memory are otherwise
   // treated as divergent, and a divergent loop around barriers is
@@ -385,10 +390,15 @@ __global__ void __launch_bounds__(256) moe_producer_kernel(const ProdArgs a) {
   const int n_up = a.n_rb_max * a.n_up_nt;
   // Next queue item, identical in every thread.  The loop below has a single
   // back edge that always passes through this fetch (no `continue`).
+  // The ticket goes through the first word of the tile buffer, which is free
+  // between items: a tile's last LDS access precedes a barrier (the K loop's
+  // last one, or the staged epilogue's own wave-local reads, which wave 0
+  // finishes before thread 0 writes), and a combine unit ends with one.
   auto fetch = [&]() -> int {
-    if (threadIdx.x == 0) s_item = (int)(atomicAdd(a.queue, 1u) - a.queue_base);
+    volatile int* s_item = (volatile int*)lds;
+    if (threadIdx.x == 0) *s_item = (int)(atomicAdd(a.queue, 1u) - a.queue_base);
     __syncthreads();
-    const int v = __builtin_amdgcn_readfirstlane(s_item);
+    const int v = __builtin_amdgcn_readfirstlane(*s_item);
     __syncthreads();
     return v;
   };
@@ -456,7 +466,7 @@ __global__ void __launch_bounds__(256) moe_producer_kernel(const ProdArgs a) {
 
 template <bool U, bool D>
 void launch_prod(const ProdArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((moe_producer_kernel<U, D>), dim3(grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((moe_producer_kernel<U, D>), dim3(grid), dim3(kProdThreads), 0, s, a);
 }
 
 }  // namespace
