@@ -142,12 +142,12 @@ __device__ __forceinline__ void copy_unit(const CopyArgs& a, int u) {
       for (; r + (U - 1) * rows_p < nr; r += U * rows_p, off += U * step) {
         uint64_t v[U];
 #pragma unroll
-        for (int q = 0; q < U; ++q) v[q] = *(const uint64_t*)(sk + (off + q * step));
+        for (int q = 0; q < U; ++q) v[q] = __builtin_nontemporal_load((const uint64_t*)(sk + (off + q * step)));
 #pragma unroll
         for (int q = 0; q < U; ++q) store_coherent((uint64_t*)(dk + (off + q * step)), v[q]);
       }
       for (; r < nr; r += rows_p, off += step)
-        store_coherent((uint64_t*)(dk + off), *(const uint64_t*)(sk + off));
+        store_coherent((uint64_t*)(dk + off), __builtin_nontemporal_load((const uint64_t*)(sk + off)));
     }
   }
   // The piece is published without an L2 write-back: its stores went

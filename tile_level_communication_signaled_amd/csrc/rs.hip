@@ -113,6 +113,13 @@ struct RsReduceArgs {
 // Every thread re-reads exactly the elements it stored, so the two phases
 // need no synchronisation between threads.  Summation order per element:
 // peers in ascending rank order, then the local partial.
+// Streaming read of four floats that is not kept in the caches (the peers'
+// partials are read once; the L2 keeps serving the GEMM beside the reduce).
+__device__ __forceinline__ float4 nt_load4(const float* p) {
+  const f32x4_t v = __builtin_nontemporal_load((const f32x4_t*)p);
+  return make_float4(v[0], v[1], v[2], v[3]);
+}
+
 __global__ void __launch_bounds__(256) rs_reduce_kernel(const RsReduceArgs a) {
   constexpr int P_MAX = 4;  // peers per load batch (eight 16-byte loads in flight)
   const int n_units = a.n_ftm * a.n_ftn * 8;
@@ -142,8 +149,8 @@ __global__ void __launch_bounds__(256) rs_reduce_kernel(const RsReduceArgs a) {
       for (int p = 0; p < P_MAX; ++p) {
         if (p < np) {
           const float* pp = a.peers + (int64_t)(p0 + p) * a.chunk_rows * a.N;
-          if (ok0) v0[p] = *(const float4*)(pp + o0);
-          if (ok1) v1[p] = *(const float4*)(pp + o1);
+          if (ok0) v0[p] = nt_load4(pp + o0);
+          if (ok1) v1[p] = nt_load4(pp + o1);
         }
       }
 #pragma unroll
