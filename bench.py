@@ -48,6 +48,9 @@ def _parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--headline-only", action="store_true",
                    help="time only the headline overlap steps (for kernel traces)")
+    p.add_argument("--trace-path", choices=["gemm_rs", "mlp2", "moe"],
+                   help="time only this path's overlap steps (for kernel traces of that path), print one "
+                        "JSON line and exit")
     p.add_argument("--counters", action="store_true",
                    help="counter-collection run: the profiler serialises kernels, so every path runs in "
                         "compute-only mode and in comm-only mode (K steps each) instead of overlapped, then "
@@ -377,6 +380,25 @@ def main():
             label = {tsg.OVERLAP: "overlap", tsg.SERIAL: "serial"}[mode]
             out += [f"### {name}, {label}", "", _timeline_text(name, ctx.timeline()), ""]
         print("\n".join(out), flush=True)
+        ctx.close()
+        return
+
+    if args.trace_path:
+        fn, flops, _nbytes, _modes = _other_paths(torch, tsg, ctx)[args.trace_path]
+        for i in range(args.warmup):
+            fn(i, tsg.OVERLAP)
+        if ctx.check() != tsg.OK:
+            raise RuntimeError(ctx.last_error())
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            fn(i, tsg.OVERLAP)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) / args.steps * 1e3
+        if ctx.check() != tsg.OK:
+            raise RuntimeError(ctx.last_error())
+        print(json.dumps({"path": args.trace_path, "mode": "overlap", "ms_per_step": round(ms, 5),
+                          "tflops": round(flops / (ms * 1e-3) / 1e12, 2), "steps": args.steps}), flush=True)
         ctx.close()
         return
 

@@ -286,8 +286,9 @@ tsg_status mlp2_pipelined(tsg_ctx* ctx, const void* x, const void* w1, void* h,
  *   workspace device memory of at least tsg_workspace_bytes(TSG_OP_MOE, dims)
  *             bytes with dims = {T, H, I, E, k}; caller-owned, contents
  *             undefined on entry and exit.
- * Constraints: k == 2 (TSG_E_UNSUPPORTED otherwise), 1 <= E <= 256,
- * T >= 1, H % 8 == 0, I % 8 == 0, H, I >= 8.  Expert ids outside [0, E) are
+ * Constraints: k == 2 and T * k <= 65535 (TSG_E_UNSUPPORTED otherwise),
+ * 1 <= E <= 256, T >= 1, H % 8 == 0, I % 8 == 0, H, I >= 8; x, topk_ids,
+ * w_up, w_down, out and workspace 16-byte aligned (TSG_E_ALIGN).  Expert ids outside [0, E) are
  * detected on the device: the affected pairs are dropped and the call's
  * tsg_check returns TSG_E_INVALID.  Default combine partition (aux_cus): 16 CUs. */
 tsg_status moe_expert_combine(tsg_ctx* ctx, const void* x, const int32_t* topk_ids,

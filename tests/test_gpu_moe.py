@@ -159,6 +159,12 @@ def test_moe_rejects_small_workspace_and_k(env):
     args = (ctx, c.x, c.ids, c.g, c.wu, c.wd, c.out, c.counts, c.sorted, c.ws)
     assert tsg.moe_expert_combine(*args, c.wsb - 1, 64, 128, 64, 4, 2, raise_on_error=False) == tsg.E_WORKSPACE
     assert tsg.moe_expert_combine(*args, c.wsb, 64, 128, 64, 4, 3, raise_on_error=False) == tsg.E_UNSUPPORTED
+    # more routed pairs than the routing's 16-bit counts hold: rejected on the host, before any device work
+    assert tsg.moe_expert_combine(*args, c.wsb, 32768, 128, 64, 4, 2, raise_on_error=False) == tsg.E_UNSUPPORTED
+    # expert ids must be 16-byte aligned (read as vectors)
+    ids_off = c.ids.view(-1)[1:]
+    args_off = (ctx, c.x, ids_off, c.g, c.wu, c.wd, c.out, c.counts, c.sorted, c.ws)
+    assert tsg.moe_expert_combine(*args_off, c.wsb, 31, 128, 64, 4, 2, raise_on_error=False) == tsg.E_ALIGN
 
 
 def test_moe_missing_row_block_times_out_then_recovers(env):

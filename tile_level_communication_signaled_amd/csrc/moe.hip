@@ -113,9 +113,15 @@ Ws bind(char* base, const Layout& L) {
 
 // ------------------------------------------------------------------ route
 // One workgroup.  Thread j owns the contiguous pair block
-// [j*PB, (j+1)*PB); per-thread, per-expert counts live in LDS (uint16).
-// Stable: the position of pair p is offs[e] + (pairs of e in earlier blocks)
-// + (pairs of e earlier in p's own block).
+// [j*PB, (j+1)*PB) (PB a multiple of 4, read as 16-byte vectors); per-thread,
+// per-expert counts live in LDS (uint16; every count and prefix is below
+// 65536 because T*k is).  Stable: the position of pair p is offs[e] + (pairs
+// of e in earlier blocks) + (pairs of e earlier in p's own block).  The
+// prefix over blocks is a scan per expert across the workgroup: a shuffle
+// scan within each wave, then the totals of the earlier waves.
+constexpr int kRouteWaves = kRouteThreads / 64;
+constexpr int kRouteMaxPairs = 65535;
+
 struct RouteArgs {
   const int32_t* ids;
   int32_t* counts;
@@ -126,34 +132,64 @@ struct RouteArgs {
   int64_t rows_max, n_rb_max;
 };
 
+// Expert ids of pairs [p0, p1) of the block starting at 16-byte aligned p0,
+// visited in order: f(p, e).
+template <class F>
+__device__ __forceinline__ void route_block(const int32_t* __restrict__ ids, int p0, int p1, F&& f) {
+  int p = p0;
+  for (; p + 4 <= p1; p += 4) {
+    const int4 v = *(const int4*)(ids + p);
+    f(p, v.x);
+    f(p + 1, v.y);
+    f(p + 2, v.z);
+    f(p + 3, v.w);
+  }
+  for (; p < p1; ++p) f(p, ids[p]);
+}
+
 __global__ void __launch_bounds__(kRouteThreads) moe_route_kernel(const RouteArgs a) {
   __shared__ uint16_t cnt[kMaxExperts][kRouteThreads];
+  __shared__ int s_wtot[kMaxExperts][kRouteWaves];
   __shared__ int s_offs[kMaxExperts + 1], s_poffs[kMaxExperts + 1];
   __shared__ int s_bad;
   const int j = threadIdx.x;
+  const int lane = j & 63, wave = j >> 6;
   const int P = a.T * a.k, E = a.E;
-  const int PB = (P + kRouteThreads - 1) / kRouteThreads;
+  const int PB = ((P + kRouteThreads - 1) / kRouteThreads + 3) & ~3;
   const int p0 = min(P, j * PB), p1 = min(P, p0 + PB);
   for (int e = 0; e < E; ++e) cnt[e][j] = 0;
   if (j == 0) s_bad = 0;
   __syncthreads();
   int bad = 0;
-  for (int p = p0; p < p1; ++p) {
-    const int e = a.ids[p];
+  route_block(a.ids, p0, p1, [&](int, int e) {
     if (e >= 0 && e < E) cnt[e][j]++;
     else bad = 1;
-  }
+  });
   if (bad) atomicOr(&s_bad, 1);
   __syncthreads();
-  // exclusive scan over threads, one expert per thread (E <= 256 threads)
-  for (int e = j; e < E; e += kRouteThreads) {
-    int run = 0;
-    for (int i = 0; i < kRouteThreads; ++i) {
-      const int c = cnt[e][i];
-      cnt[e][i] = (uint16_t)run;
-      run += c;
+  // exclusive scan over threads, per expert: within the wave first
+  for (int e = 0; e < E; ++e) {
+    const int c = cnt[e][j];
+    int x = c;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(x, d, 64);
+      if (lane >= d) x += y;
     }
-    s_offs[e + 1] = run;  // count of expert e, scanned below
+    cnt[e][j] = (uint16_t)(x - c);
+    if (lane == 63) s_wtot[e][wave] = x;
+  }
+  __syncthreads();
+  // then the totals of the earlier waves; expert totals
+  for (int e = 0; e < E; ++e) {
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += s_wtot[e][w];
+    cnt[e][j] = (uint16_t)(cnt[e][j] + before);
+  }
+  for (int e = j; e < E; e += kRouteThreads) {
+    int tot = 0;
+    for (int w = 0; w < kRouteWaves; ++w) tot += s_wtot[e][w];
+    s_offs[e + 1] = tot;  // count of expert e, scanned below
   }
   __syncthreads();
   if (j == 0) {
@@ -190,9 +226,8 @@ __global__ void __launch_bounds__(kRouteThreads) moe_route_kernel(const RouteArg
   __syncthreads();
   for (int e = 0; e < E; ++e)
     for (int rb = s_poffs[e] / BM + j; rb < s_poffs[e + 1] / BM; rb += kRouteThreads) a.ws.rb_expert[rb] = e;
-  for (int p = p0; p < p1; ++p) {
-    const int e = a.ids[p];
-    if (e < 0 || e >= E) continue;
+  route_block(a.ids, p0, p1, [&](int p, int e) {
+    if (e < 0 || e >= E) return;
     const int rank = cnt[e][j]++;
     const int pos = s_offs[e] + rank;
     const int row = s_poffs[e] + rank;
@@ -200,7 +235,7 @@ __global__ void __launch_bounds__(kRouteThreads) moe_route_kernel(const RouteArg
     a.ws.pair_row[p] = row;
     a.ws.row_pair[row] = p;
     a.ws.row_token[row] = p / a.k;
-  }
+  });
 }
 
 // --------------------------------------------------------------- producer
@@ -487,9 +522,10 @@ tsg_status tsg_op_moe(tsg_ctx* ctx, const void* x, const int32_t* topk_ids, cons
   if (k != 2) return fail(ctx, TSG_E_UNSUPPORTED, "moe_expert_combine supports k == 2 only");
   if (T < 1 || E < 1 || E > kMaxExperts || H < 8 || I < 8 || H % 8 || I % 8)
     return fail(ctx, TSG_E_SHAPE, "moe_expert_combine: bad shape T=%d H=%d I=%d E=%d", T, H, I, E);
-  if ((int64_t)T * k > 65535 * kRouteThreads)
-    return fail(ctx, TSG_E_UNSUPPORTED, "too many routed pairs");
-  if (!aligned16(x) || !aligned16(w_up) || !aligned16(w_down) || !aligned16(out) || !aligned16(workspace))
+  if ((int64_t)T * k > kRouteMaxPairs)
+    return fail(ctx, TSG_E_UNSUPPORTED, "moe_expert_combine: T * k above %d routed pairs", kRouteMaxPairs);
+  if (!aligned16(x) || !aligned16(topk_ids) || !aligned16(w_up) || !aligned16(w_down) || !aligned16(out) ||
+      !aligned16(workspace))
     return fail(ctx, TSG_E_ALIGN, "moe_expert_combine: pointers must be 16-byte aligned");
   const Layout L = layout(T, H, I, E, k);
   if (!workspace || workspace_bytes < L.total)
