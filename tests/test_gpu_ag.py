@@ -107,6 +107,24 @@ def test_ag_ragged_shapes(env, tile):
                 assert err_ratio(c, ref, scale, bf16_out=out_bf16) <= 1.0
 
 
+@pytest.mark.parametrize("tile", [8, 2, 1])
+def test_ag_direct_path_ragged(env, tile):
+    # K a multiple of 128 (operands go straight to LDS); M and N ragged against
+    # the 256-row tiles and 224- or 256-column tiles; 3 ranks of 200 rows, so
+    # tiles straddle chunks; shared CUs (the GEMM pulls copy units) and a CU
+    # split; slabs of 128 columns
+    M, N, K, R = 600, 232, 384, 3
+    inp = ag_inputs(M, K, N, R, seed=8)
+    ref, scale = _ref(inp)
+    for rank in range(R):
+        for out_bf16 in (True, False):
+            case = AgCase(env, inp, M, N, K, R, rank, out_bf16)
+            for aux in (-1, 16):
+                full, c = case.run(opts={"tile": tile, "aux_cus": aux, "comm_tile": 128})
+                assert np.array_equal(full, inp["a"])
+                assert err_ratio(c, ref, scale, bf16_out=out_bf16) <= 1.0
+
+
 @pytest.mark.parametrize("K", [512, 320])
 def test_ag_comm_tile_slabs(env, K):
     # Chunks move as column slabs; tiles wait slab by slab inside the K loop.
