@@ -53,7 +53,7 @@ typedef enum tsg_status {
   TSG_E_ALIGN = -3,       /* pointer not 16-byte aligned                     */
   TSG_E_HIP = -4,         /* a HIP runtime call failed                       */
   TSG_E_TIMEOUT = -5,     /* a device-side signal wait exceeded its bound    */
-  TSG_E_UNSUPPORTED = -6, /* valid request this build does not implement     */
+  TSG_E_UNSUPPORTED = -6, /* valid request the library does not implement    */
   TSG_E_WORKSPACE = -7    /* workspace missing or smaller than required      */
 } tsg_status;
 
