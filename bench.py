@@ -14,7 +14,8 @@ GEMM-only and the overlap ratio (comp + comm - overlap) / comm.
 `paths` reports the same four modes for every path at its full-size
 workload: AG+GEMM, GEMM+RS (8192x1792 @ 1792x4096, 7 fp32 peer partials),
 the CTA-pipelined MLP (2048x8192 @ 8192x4096, GELU, @ 4096x8192) and MoE
-(4096 tokens, hidden 4096, 8 experts of 4096x1408 / 1408x4096, top-2 Zipf).
+(4096 tokens, hidden 4096, 8 experts of 4096x1408 / 1408x4096, top-2 Zipf),
+the latter also with its y staging in bf16.
 
 Prints one JSON line.  Only one GPU is supported.
 """
@@ -48,7 +49,7 @@ def _parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--headline-only", action="store_true",
                    help="time only the headline overlap steps (for kernel traces)")
-    p.add_argument("--trace-path", choices=["gemm_rs", "mlp2", "moe"],
+    p.add_argument("--trace-path", choices=["gemm_rs", "mlp2", "moe", "moe_bf16_staging"],
                    help="time only this path's overlap steps (for kernel traces of that path), print one "
                         "JSON line and exit")
     p.add_argument("--counters", action="store_true",
@@ -301,6 +302,16 @@ def _other_paths(torch, tsg, ctx):
     moe_flops = 4.0 * T * k * Hh * I
     moe_bytes = T * k * Hh * 2 + 2 * E * Hh * I * 2 + 2 * T * k * I * 2 + 2 * T * k * Hh * 4 + T * Hh * 4
     out["moe"] = (moe_fn, moe_flops, moe_bytes, (tsg.OVERLAP, tsg.SERIAL, tsg.COMPUTE_ONLY, tsg.COMM_ONLY))
+
+    # the same MoE workload with the y staging in bf16 (stage_dtype): the
+    # staging round trip moves half the bytes
+    def moe_bf16_fn(i, mode, opts=None):
+        o = tsg.Opts(stage_dtype=tsg.BF16) if opts is None else opts
+        o.stage_dtype = tsg.BF16
+        return moe_fn(i, mode, o)
+    moe_bf16_bytes = moe_bytes - T * k * Hh * 4
+    out["moe_bf16_staging"] = (moe_bf16_fn, moe_flops, moe_bf16_bytes,
+                               (tsg.OVERLAP, tsg.SERIAL, tsg.COMPUTE_ONLY, tsg.COMM_ONLY))
     return out
 
 
@@ -308,7 +319,8 @@ def _other_paths(torch, tsg, ctx):
 TL_KINDS = {"ag_gemm": ((1, "copy units"), (2, "GEMM tiles")),
             "gemm_rs": ((3, "GEMM tiles"), (4, "reduce units")),
             "mlp2": ((5, "GEMM1 tiles"), (6, "GEMM2 tiles")),
-            "moe": ((7, "up tiles"), (8, "down tiles"), (9, "combine units"))}
+            "moe": ((7, "up tiles"), (8, "down tiles"), (9, "combine units")),
+            "moe_bf16_staging": ((7, "up tiles"), (8, "down tiles"), (9, "combine units"))}
 
 
 def _timeline_text(name, recs, bins=24):
@@ -409,6 +421,8 @@ def main():
             ag_fn(i, tsg.COMM_ONLY)
         if args.paths == "all":
             for name, (fn, _f, _b, modes) in _other_paths(torch, tsg, ctx).items():
+                if name == "moe_bf16_staging":   # same kernel names: keep the record to one variant
+                    continue
                 for mode in (tsg.COMPUTE_ONLY, tsg.COMM_ONLY):
                     if mode in modes:
                         for i in range(args.steps):

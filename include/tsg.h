@@ -127,6 +127,11 @@ typedef struct tsg_opts {
    * 0 = the op's default (one unit per CU, at most the first slab's units),
    * -1 = none. */
   int pull_units;
+  /* MoE: element type of the y staging between the down projection and the
+   * combine.  TSG_F32 (0, default): y is kept in fp32.  TSG_BF16 (1): y is
+   * rounded to bf16 (nearest even) when stored, halving the staging traffic;
+   * out = g0 * y0 + g1 * y1 is then formed from the rounded values. */
+  int stage_dtype;
 } tsg_opts;
 
 /* ------------------------------------------------------------------ ctx */

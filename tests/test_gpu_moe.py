@@ -65,8 +65,11 @@ class MoeCase:
                 self.sorted.cpu().numpy())
 
 
-def _bound(inp, res):
-    """Per-element tolerance of out (see module docstring)."""
+def _bound(inp, res, y_bf16=False):
+    """Per-element tolerance of out (see module docstring).  With the y
+    staging in bf16, each slot's y is rounded once more before the combine:
+    its gate times one bf16 quantum of y (twice the half quantum, as the
+    device's y may lie across a power of two from the oracle's) is added."""
     x = oracle.bf16_to_f64(inp["x"])
     ids, g = inp["topk_ids"], inp["topk_w"].astype(np.float64)
     T, k = ids.shape
@@ -80,16 +83,18 @@ def _bound(inp, res):
         h = oracle.bf16_to_f64(res["h"][pairs])
         dh = 1.1 * (1e-3 * s_up + 1e-5) + 2 * bf16_half_quantum(h)
         extra[pairs] = dh @ np.abs(oracle.bf16_to_f64(inp["w_down"][e]))
+    if y_bf16:
+        extra = extra + 2 * bf16_half_quantum(res["y"])
     extra = (g.reshape(-1)[:, None] * extra).reshape(T, k, H).sum(axis=1)
     return 1e-3 * res["scale"] + 1e-5 + extra
 
 
-def _check(inp, out, counts, sorted_ids):
+def _check(inp, out, counts, sorted_ids, y_bf16=False):
     res = oracle.moe_expert_combine(inp["x"], inp["topk_ids"], inp["topk_w"], inp["w_up"], inp["w_down"])
     assert np.array_equal(counts, res["counts"])
     assert np.array_equal(sorted_ids, res["sorted_ids"])
     assert np.all(np.isfinite(out))
-    r = float(np.max(np.abs(out - res["out"]) / _bound(inp, res)))
+    r = float(np.max(np.abs(out - res["out"]) / _bound(inp, res, y_bf16)))
     return r, res
 
 
@@ -177,6 +182,27 @@ def test_moe_missing_row_block_times_out_then_recovers(env):
     assert r <= 1.0
 
 
+@pytest.mark.parametrize("T,H,I,E", [(300, 512, 256, 8), (37, 136, 200, 3)])
+def test_moe_bf16_staging(env, T, H, I, E):
+    # y staged in bf16: within the bound widened by one rounding of y per
+    # slot; identical across modes and CU splits; a bad stage type is refused
+    torch, tsg, ctx = env
+    inp = moe_inputs(T, H, I, E, k=2, seed=40 + T)
+    case = MoeCase(env, inp)
+    opt = {"stage_dtype": tsg.BF16}
+    out, counts, sorted_ids = case.run(opts=opt)
+    r, _ = _check(inp, out, counts, sorted_ids, y_bf16=True)
+    assert r <= 1.0
+    for mode in (tsg.SERIAL, tsg.COMPUTE_ONLY):
+        case.run(mode=mode, opts=opt)
+    out2, _, _ = case.run(mode=tsg.COMM_ONLY, opts=opt)
+    assert np.array_equal(out2, out)
+    out3, _, _ = case.run(opts=dict(opt, aux_cus=16))
+    assert np.array_equal(out3, out)
+    with pytest.raises(tsg.TsgError):
+        case.run(opts={"stage_dtype": 2})
+
+
 def test_moe_full_size_parity_modes_splits(env):
     torch, tsg, ctx = env
     cfg = CONFIGS["moe"]
@@ -193,3 +219,7 @@ def test_moe_full_size_parity_modes_splits(env):
     for opts in ({"aux_cus": 16}, {"aux_cus": 32}, {"aux_cus": -1}):
         out4, _, _ = case.run(opts=opts)
         assert np.array_equal(out4, out), opts
+    out5, c5, s5 = case.run(opts={"stage_dtype": tsg.BF16})
+    r5, _ = _check(inp, out5, c5, s5, y_bf16=True)
+    print(f"moe bf16 staging max err/tol {r5:.3f}")
+    assert r5 <= 1.0

@@ -51,6 +51,7 @@ class Opts(ctypes.Structure):
         ("aux_wgs", ctypes.c_int),
         ("comm_tile", ctypes.c_int),
         ("pull_units", ctypes.c_int),
+        ("stage_dtype", ctypes.c_int),
     ]
 
 

@@ -51,6 +51,7 @@ Opts resolve(const tsg_opts* o, int default_aux_cus) {
   r.aux_wgs = o ? o->aux_wgs : 0;
   r.comm_tile = o ? o->comm_tile : 0;
   r.pull_units = o ? o->pull_units : 0;
+  r.stage_dtype = o ? o->stage_dtype : TSG_F32;
   return r;
 }
 

@@ -23,7 +23,8 @@
 //      multiply by w_up[e], h = bf16(SiLU(u)); each arrives on the signal of
 //      its row block.  Then every "down" tile (rb, 224 columns of H): acquire
 //      the row block's signal (all up tiles of rb done), y = h w_down[e] in
-//      fp32 into the staging buffer, release the tile's ready signal.
+//      fp32 (bf16 with stage_dtype = TSG_BF16) into the staging buffer,
+//      release the tile's ready signal.
 //   3. The combine (combine_unit), per down tile in queue order: acquire
 //      its ready signal, and for every token whose other routed row lies in
 //      this or an earlier tile (acquiring that tile's signal too) write
@@ -249,6 +250,7 @@ struct CombArgs {
   int H, k;
   int n_dn_nt, n_rb_max;
   int wait;
+  int y_bf16;             // y staging holds bf16 (else fp32)
 };
 
 struct ProdArgs {
@@ -270,6 +272,7 @@ struct ProdArgs {
   int n_prod_items;       // up + down tiles
   CombArgs comb;          // combine units run as queue items after the down tiles
   uint32_t skip_mask;     // row blocks (mod 32) whose up tiles never arrive (test hook)
+  int y_bf16;             // y staging holds bf16 (else fp32)
   int h_l1_only;          // h rows are whole 128-byte lines: acquire invalidates L1 only
 };
 
@@ -288,10 +291,19 @@ struct ProdArgs {
 //      polls only those not yet published, and the workgroup acquires.
 //   3. Each wave takes an equal share of the rows: eight rows at a time it
 //      issues all sixteen 16-byte loads of y (both slots, this lane's 4
-//      columns), then combines and stores them.
+//      columns), then combines and stores them; with bf16 staging, sixteen
+//      rows and thirty-two 8-byte loads at a time.
 // Called by every thread of the workgroup with uniform (rb, nt); `scratch`
 // is kCombScratch bytes of LDS owned by the caller for the call.
 constexpr int kCombScratch = 8 * BM * 4 + 16;
+
+// Four bf16 values (one 8-byte word of the y staging) as floats.
+__device__ __forceinline__ float4 bf16x4_to_float4(uint64_t v) {
+  return make_float4(__uint_as_float((uint32_t)(v & 0xffffu) << 16),
+                     __uint_as_float((uint32_t)((v >> 16) & 0xffffu) << 16),
+                     __uint_as_float((uint32_t)((v >> 32) & 0xffffu) << 16),
+                     __uint_as_float((uint32_t)(v >> 48) << 16));
+}
 
 __device__ __forceinline__ void combine_unit(const CombArgs& a, int rb, int nt, char* scratch) {
   int* s_tok = (int*)scratch;
@@ -360,33 +372,60 @@ __device__ __forceinline__ void combine_unit(const CombArgs& a, int rb, int nt, 
   const uint64_t t1 = a.tl.buf ? wall_clock64() : 0;
   const int col = nt * BN_DN + lane * 4;
   const bool col_ok = lane * 4 < BN_DN && col < a.H;
-  const int rpw = BM / (int)(blockDim.x >> 6);   // rows per wave (a multiple of 8)
-#pragma unroll 1
-  for (int g = 0; g < rpw / 8; ++g) {
-    const int j0 = wave * rpw + g * 8;
-    float4 v0[8], v1[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int own = s_own[j0 + j], oth = s_oth[j0 + j];
-      v0[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-      v1[j] = v0[j];
-      if (s_tok[j0 + j] >= 0 && col_ok) {
-        if (own >= 0) v0[j] = load_coherent((const float4*)(a.ws.y + (int64_t)own * a.H + col));
-        if (oth >= 0) v1[j] = load_coherent((const float4*)(a.ws.y + (int64_t)oth * a.H + col));
-      }
+  const int rpw = BM / (int)(blockDim.x >> 6);   // rows per wave (a multiple of 16)
+  // out[t] = fl(fl(g0 y0) + fl(g1 y1)) for the row's token, four columns
+  auto emit = [&](int j, float4 y0, float4 y1) {
+    const int tok = s_tok[j];
+    if (tok >= 0 && col_ok) {
+      const float g0 = s_g0[j], g1 = s_g1[j];
+      float4 o;
+      o.x = __fadd_rn(__fmul_rn(g0, y0.x), __fmul_rn(g1, y1.x));
+      o.y = __fadd_rn(__fmul_rn(g0, y0.y), __fmul_rn(g1, y1.y));
+      o.z = __fadd_rn(__fmul_rn(g0, y0.z), __fmul_rn(g1, y1.z));
+      o.w = __fadd_rn(__fmul_rn(g0, y0.w), __fmul_rn(g1, y1.w));
+      *(float4*)(a.out + (int64_t)tok * a.H + col) = o;
     }
+  };
+  if (a.y_bf16) {
+    // bf16 staging: sixteen rows at a time, both slots' 8-byte loads issued
+    // before any is used (32 in flight, as many bytes as the fp32 form)
+    const uint16_t* yb = (const uint16_t*)a.ws.y;
+#pragma unroll 1
+    for (int g = 0; g < rpw / 16; ++g) {
+      const int j0 = wave * rpw + g * 16;
+      uint64_t w0[16], w1[16];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int tok = s_tok[j0 + j];
-      if (tok >= 0 && col_ok) {
-        const float g0 = s_g0[j0 + j], g1 = s_g1[j0 + j];
-        float4 o;
-        o.x = __fadd_rn(__fmul_rn(g0, v0[j].x), __fmul_rn(g1, v1[j].x));
-        o.y = __fadd_rn(__fmul_rn(g0, v0[j].y), __fmul_rn(g1, v1[j].y));
-        o.z = __fadd_rn(__fmul_rn(g0, v0[j].z), __fmul_rn(g1, v1[j].z));
-        o.w = __fadd_rn(__fmul_rn(g0, v0[j].w), __fmul_rn(g1, v1[j].w));
-        *(float4*)(a.out + (int64_t)tok * a.H + col) = o;
+      for (int j = 0; j < 16; ++j) {
+        const int own = s_own[j0 + j], oth = s_oth[j0 + j];
+        w0[j] = 0;
+        w1[j] = 0;
+        if (s_tok[j0 + j] >= 0 && col_ok) {
+          if (own >= 0) w0[j] = __hip_atomic_load((const uint64_t*)(yb + (int64_t)own * a.H + col),
+                                                  __ATOMIC_RELAXED, TSG_SIG_SCOPE);
+          if (oth >= 0) w1[j] = __hip_atomic_load((const uint64_t*)(yb + (int64_t)oth * a.H + col),
+                                                  __ATOMIC_RELAXED, TSG_SIG_SCOPE);
+        }
       }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) emit(j0 + j, bf16x4_to_float4(w0[j]), bf16x4_to_float4(w1[j]));
+    }
+  } else {
+#pragma unroll 1
+    for (int g = 0; g < rpw / 8; ++g) {
+      const int j0 = wave * rpw + g * 8;
+      float4 v0[8], v1[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int own = s_own[j0 + j], oth = s_oth[j0 + j];
+        v0[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+        v1[j] = v0[j];
+        if (s_tok[j0 + j] >= 0 && col_ok) {
+          if (own >= 0) v0[j] = load_coherent((const float4*)(a.ws.y + (int64_t)own * a.H + col));
+          if (oth >= 0) v1[j] = load_coherent((const float4*)(a.ws.y + (int64_t)oth * a.H + col));
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) emit(j0 + j, v0[j], v1[j]);
     }
   }
   if (a.tl.buf && threadIdx.x == 0) timeline_put(a.tl, 9, (uint32_t)(rb << 16 | nt), t0, t1, wall_clock64());
@@ -484,11 +523,17 @@ __global__ void __launch_bounds__(kProdThreads) moe_producer_kernel(const ProdAr
         const int valid = __builtin_amdgcn_readfirstlane(
             min(BM, a.ws.offs[e + 1] - a.ws.offs[e] - (rb * BM - a.ws.poffs[e])));
         const int H = a.H;
-        float* yrow = a.ws.y + (int64_t)rb * BM * H;
-        GemmTile<CfgDn>::for_each(acc, [&](int r, int c, float v) {
-          const int gc = col0 + c;
-          if (r < valid && gc < H) store_coherent(yrow + (int64_t)r * H + gc, v);
-        });
+        if (a.y_bf16) {
+          uint16_t* yb = (uint16_t*)a.ws.y + (int64_t)rb * BM * H + col0;
+          GemmTile<CfgDn>::template store_bf16_staged<sizeof(lds), true>(
+              acc, lds, yb, H, valid, H - col0, [](float v) { return v; });
+        } else {
+          float* yrow = a.ws.y + (int64_t)rb * BM * H;
+          GemmTile<CfgDn>::for_each(acc, [&](int r, int c, float v) {
+            const int gc = col0 + c;
+            if (r < valid && gc < H) store_coherent(yrow + (int64_t)r * H + gc, v);
+          });
+        }
         block_coherent_complete();
         if (threadIdx.x == 0) {
           sig_publish_coherent(a.sig_ready + (int64_t)rb * a.n_dn_nt + nt, a.sa.epoch, 1);
@@ -541,6 +586,8 @@ tsg_status tsg_op_moe(tsg_ctx* ctx, const void* x, const int32_t* topk_ids, cons
     return fail(ctx, TSG_E_UNSUPPORTED, "too many tiles for the signal pool");
 
   const Opts o = resolve(opts, -1);
+  if (o.stage_dtype != TSG_F32 && o.stage_dtype != TSG_BF16)
+    return fail(ctx, TSG_E_INVALID, "moe_expert_combine: stage_dtype must be TSG_F32 or TSG_BF16");
   TSG_HIP(ctx, hipSetDevice(ctx->device));
   hipStream_t caller = (hipStream_t)stream;
   ++ctx->epoch;
@@ -582,6 +629,7 @@ tsg_status tsg_op_moe(tsg_ctx* ctx, const void* x, const int32_t* topk_ids, cons
   pa.n_prod_items = (int)(L.n_rb_max * (n_up_nt + n_dn_nt));
   pa.n_items = pa.n_prod_items;
   pa.skip_mask = o.skip_mask;
+  pa.y_bf16 = o.stage_dtype == TSG_BF16 ? 1 : 0;
   pa.h_l1_only = ((uintptr_t)ws.h % 128 == 0 && ((int64_t)I * 2) % 128 == 0) ? 1 : 0;
 
   CombArgs ca;
@@ -595,6 +643,7 @@ tsg_status tsg_op_moe(tsg_ctx* ctx, const void* x, const int32_t* topk_ids, cons
   ca.k = k;
   ca.n_dn_nt = n_dn_nt;
   ca.n_rb_max = (int)L.n_rb_max;
+  ca.y_bf16 = pa.y_bf16;
 
   auto route = [&]() -> tsg_status {
     hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(kRouteThreads), 0, caller, ra);
