@@ -11,7 +11,8 @@ synchronisations.  The same kernels are also timed serialized (copy, then
 GEMM), GEMM-only and copy-only, giving the speedup over serial, the ratio to
 GEMM-only and the overlap ratio (comp + comm - overlap) / comm.
 
-`paths` reports the same four modes for every path at its full-size
+`paths` also holds the AllGather + GEMM with the copy paced at seven xGMI
+links' rate (arrival_gbps), and reports the same four modes for every path at its full-size
 workload: AG+GEMM, GEMM+RS (8192x1792 @ 1792x4096, 7 fp32 peer partials),
 the CTA-pipelined MLP (2048x8192 @ 8192x4096, GELU, @ 4096x8192) and MoE
 (4096 tokens, hidden 4096, 8 experts of 4096x1408 / 1408x4096, top-2 Zipf),
@@ -34,6 +35,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "overlapped TFLOP/s, % bf16 MFMA peak, speedup vs serialized copy+GEMM"
+XGMI_GBPS = 1071            # arrival pacing of the xGMI-paced AG line: 7 links x ~153 GB/s
 CSRC = os.path.join(ROOT, "tile_level_communication_signaled_amd", "csrc")
 TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -469,6 +471,17 @@ def main():
     ag["kernel_ms"] = {"gemm_in_overlap": round(k_ov[0], 5), "copy_in_overlap": round(k_ov[1], 5),
                        "gemm_alone": round(k_co[0], 5), "copy_alone": round(k_cm[1], 5)}
     paths = {"ag_gemm": ag}
+    if args.paths == "all":
+        # the same AllGather + GEMM with the arrival paced at seven peers'
+        # xGMI links (about 153 GB/s each), as a multi-GPU rank would see it
+        paced = tsg.Opts(aux_cus=args.aux_cus, tile=args.tile, arrival_gbps=XGMI_GBPS)
+        tp = Timer(torch, tsg, ctx, lambda i, mode, o=None: ag_fn(i, mode, paced)).modes(
+            (tsg.OVERLAP, tsg.SERIAL, tsg.COMPUTE_ONLY, tsg.COMM_ONLY), n)
+        paths["ag_gemm_xgmi_paced"] = _summary(
+            ag_flops, ag_gemm_bytes + ag_copy_bytes,
+            {"overlap": tp[tsg.OVERLAP], "serial": tp[tsg.SERIAL], "compute_only": tp[tsg.COMPUTE_ONLY],
+             "comm_only": tp[tsg.COMM_ONLY]})
+        paths["ag_gemm_xgmi_paced"]["arrival_gbps"] = XGMI_GBPS
 
     if args.paths == "all":
         for name, (fn, flops, nbytes, modes) in _other_paths(torch, tsg, ctx).items():

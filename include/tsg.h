@@ -132,6 +132,13 @@ typedef struct tsg_opts {
    * rounded to bf16 (nearest even) when stored, halving the staging traffic;
    * out = g0 * y0 + g1 * y1 is then formed from the rounded values. */
   int stage_dtype;
+  /* AG+GEMM: pace the arrival of the gathered data at this many GB/s (0 =
+   * as fast as the copy runs).  Copy unit u (of n, in arrival order) is
+   * published no earlier than total_bytes * (u + 1) / (n * rate) after the
+   * first unit was taken, so that one GPU's timeline follows a link-bound
+   * arrival such as seven peers over xGMI ([TD] section 3.6: AMD all-to-all
+   * links; section 3.7: arrival order).  Negative: TSG_E_INVALID. */
+  int arrival_gbps;
 } tsg_opts;
 
 /* ------------------------------------------------------------------ ctx */

@@ -125,6 +125,34 @@ def test_ag_direct_path_ragged(env, tile):
                 assert err_ratio(c, ref, scale, bf16_out=out_bf16) <= 1.0
 
 
+def test_ag_paced_arrival(env):
+    # arrival paced at 2 GB/s: the same results, and a call takes at least
+    # the gathered bytes over the rate (in every mode that copies)
+    import time
+    torch, tsg, ctx = env
+    M, N, K, R = 600, 232, 384, 3
+    inp = ag_inputs(M, K, N, R, seed=9)
+    ref, scale = _ref(inp)
+    case = AgCase(env, inp, M, N, K, R, 1, True)
+    gbps = 2
+    floor_s = M * K * 2 / (gbps * 1e9)
+    for mode in (tsg.OVERLAP, tsg.SERIAL, tsg.COMM_ONLY):
+        for aux in (-1, 16):
+            opts = {"arrival_gbps": gbps, "aux_cus": aux, "comm_tile": 128}
+            case.run(mode=mode, opts=opts)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            full, c = case.run(mode=mode, opts=opts)
+            elapsed = time.perf_counter() - t0
+            assert np.array_equal(full, inp["a"])
+            if mode != tsg.COMM_ONLY:
+                assert err_ratio(c, ref, scale, bf16_out=True) <= 1.0
+            assert elapsed >= 0.9 * floor_s, (mode, aux, elapsed, floor_s)
+    st = tsg.gemm_ag_overlap(ctx, case.loc, case.peers, case.full, case.b, case.c, tsg.BF16, M, N, K, R, 1,
+                             opts={"arrival_gbps": -1}, raise_on_error=False)
+    assert st == tsg.E_INVALID
+
+
 @pytest.mark.parametrize("K", [512, 320])
 def test_ag_comm_tile_slabs(env, K):
     # Chunks move as column slabs; tiles wait slab by slab inside the K loop.

@@ -52,6 +52,7 @@ class Opts(ctypes.Structure):
         ("comm_tile", ctypes.c_int),
         ("pull_units", ctypes.c_int),
         ("stage_dtype", ctypes.c_int),
+        ("arrival_gbps", ctypes.c_int),
     ]
 
 

@@ -38,6 +38,7 @@ constexpr int kMaxMTiles = 1024;
 constexpr size_t kSigBase = size_t(1) << 18;  // AG slab signals in the context's pool
 constexpr size_t kSigCap = size_t(1) << 18;   // slots up to the next op's region
 constexpr int kQueueSlot = 40;                // copy work queue in the context's ticket words
+constexpr size_t kPaceSlot = 8;               // arrival-pacing start time in the context's pool
 
 struct ChunkOrder {
   int8_t chunk[kMaxRanks];  // chunk copied at arrival position p (p = 0: local)
@@ -71,7 +72,31 @@ struct CopyArgs {
   // last of the n_workers claimers to leave resets both for the next call.
   uint32_t* queue;
   uint32_t n_workers;
+  // Arrival pacing (pace_ticks > 0): unit u is published no earlier than
+  // (u + 1) * pace_ticks wall-clock ticks after the first unit was taken;
+  // the taker of ticket 0 stores that time, tagged with the call's epoch,
+  // in pace_word.
+  uint64_t* pace_word;
+  float pace_ticks;
 };
+
+constexpr uint64_t kPaceClockMask = (uint64_t(1) << 48) - 1;
+
+// Time the first unit of this call was taken (one lane; bounded wait for the
+// taker of ticket 0 to publish it).
+__device__ __forceinline__ uint64_t pace_base(const CopyArgs& a) {
+  const uint64_t tag = (uint64_t)(a.sa.epoch & 0xffffu) << 48;
+  const uint64_t t0 = wall_clock64();
+  for (;;) {
+    const uint64_t v = __hip_atomic_load(a.pace_word, __ATOMIC_RELAXED, TSG_SIG_SCOPE);
+    if ((v & ~kPaceClockMask) == tag) return v & kPaceClockMask;
+    if (wall_clock64() - t0 > a.sa.spin_ticks) {
+      __hip_atomic_fetch_or(a.sa.status, ERR_TIMEOUT, __ATOMIC_RELAXED, TSG_SIG_SCOPE);
+      return t0 & kPaceClockMask;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
 
 // Work unit u -> (slab s, arrival position p, piece j), slab-major.  One unit
 // copies piece j (np[s] pieces of about equal rows) of slab s of chunk
@@ -153,6 +178,12 @@ __device__ __forceinline__ void copy_unit(const CopyArgs& a, int u) {
   // The piece is published without an L2 write-back: its stores went
   // through to the coherence point (store_coherent).
   block_coherent_complete();
+  if (a.pace_ticks > 0.f && threadIdx.x == 0) {
+    // paced arrival: not before this unit's due time (the wait is bounded by
+    // the paced duration of the whole copy)
+    const uint64_t due = (pace_base(a) + (uint64_t)((float)(u + 1) * a.pace_ticks)) & kPaceClockMask;
+    while ((int64_t)(((wall_clock64() & kPaceClockMask) - due) << 16) < 0) __builtin_amdgcn_s_sleep(8);
+  }
   const size_t si = (size_t)c * a.n_slab + s;
   if (threadIdx.x == 0 && !((a.skip_mask >> c) & 1u))
     sig_arrive_counted_coherent(a.cnt + si, a.sig + si, (uint32_t)npc, a.sa.epoch);
@@ -163,7 +194,14 @@ __device__ __forceinline__ void copy_unit(const CopyArgs& a, int u) {
 // Next unit from the queue, identical in every thread (`slot` is one int of
 // LDS owned by the caller).
 __device__ __forceinline__ int claim_unit(const CopyArgs& a, volatile int* slot) {
-  if (threadIdx.x == 0) *slot = (int)atomicAdd(a.queue, 1u);
+  if (threadIdx.x == 0) {
+    const int t = (int)atomicAdd(a.queue, 1u);
+    if (t == 0 && a.pace_ticks > 0.f)
+      __hip_atomic_store(a.pace_word,
+                         ((uint64_t)(a.sa.epoch & 0xffffu) << 48) | (wall_clock64() & kPaceClockMask),
+                         __ATOMIC_RELAXED, TSG_SIG_SCOPE);
+    *slot = t;
+  }
   __syncthreads();
   const int u = __builtin_amdgcn_readfirstlane(*slot);
   __syncthreads();
@@ -460,6 +498,7 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
   for (int p = R; p < kMaxRanks; ++p) ord.chunk[p] = 0;
 
   const Opts o = resolve(opts, -1);
+  if (o.arrival_gbps < 0) return fail(ctx, TSG_E_INVALID, "arrival_gbps must be >= 0");
   const int tile = o.tile ? o.tile : default_tile(M, N);
   const TileShape ts = shape_of(tile);
   if (!ts.bm) return fail(ctx, TSG_E_INVALID, "unknown tile id %d", tile);
@@ -613,6 +652,12 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
   ca.n_units = (int)n_units;
   ca.skip_mask = o.skip_mask;
   ca.queue = ctx->d_queue + kQueueSlot;
+  ca.pace_word = ctx->d_sig + kPaceSlot;
+  // pacing: ticks (100 MHz wall clock) per unit at the requested rate
+  ca.pace_ticks = o.arrival_gbps > 0
+                      ? (float)((double)R * chunk_rows * K * 2 / (double)n_units / (double)o.arrival_gbps *
+                                ((double)ctx->wall_khz / 1e6))
+                      : 0.f;
   // Units the GEMM pulls itself (overlap on shared CUs, tiles of 256 or 512 threads,
   // whose workgroups move a unit the way the copy's do): by default one per
   // workgroup of the first wave of tiles, at most the first slab's units.

@@ -52,6 +52,7 @@ Opts resolve(const tsg_opts* o, int default_aux_cus) {
   r.comm_tile = o ? o->comm_tile : 0;
   r.pull_units = o ? o->pull_units : 0;
   r.stage_dtype = o ? o->stage_dtype : TSG_F32;
+  r.arrival_gbps = o ? o->arrival_gbps : 0;
   return r;
 }
 
