@@ -161,11 +161,13 @@ __global__ void __launch_bounds__(256) mlp_fused_kernel(const MlpFusedArgs f) {
   // barrier; the next tile writes LDS only after the second barrier here).
   // The item is made wave-uniform (readfirstlane) and the loop has a single
   // back edge through the fetch, so its barriers stay uniform.
+  int phase = 0;  // phase of this workgroup's previous item (wave 0's copy)
   auto fetch = [&]() -> int {
     volatile int* s_item = (volatile int*)lds;
     if (threadIdx.x < 64) {
       const int n[2] = {f.n_items1, f.n_items2};
-      const QueueItem it = xcd_queue_claim<2>(f.queues, n, my_xcd);
+      const QueueItem it = xcd_queue_claim<2>(f.queues, n, my_xcd, phase);
+      if (it.phase >= 0) phase = it.phase;
       if (threadIdx.x == 0) *s_item = it.phase < 0 ? -1 : (it.phase == 0 ? 0 : f.n_items1) + it.index;
     }
     __syncthreads();

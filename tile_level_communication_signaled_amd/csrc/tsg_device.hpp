@@ -248,10 +248,12 @@ __device__ __forceinline__ void block_wait_lines(const uint64_t* s, uint64_t tar
 struct QueueItem {
   int phase, index;
 };
+// `from` is the phase of the caller's previous item (0 at first): the
+// phases before it are used up, so they are not probed again.
 template <int NP>
-__device__ __forceinline__ QueueItem xcd_queue_claim(uint32_t* q, const int (&n)[NP], int my_xcd) {
+__device__ __forceinline__ QueueItem xcd_queue_claim(uint32_t* q, const int (&n)[NP], int my_xcd, int from = 0) {
   const int lane = __lane_id();
-  for (int ph = 0; ph < NP; ++ph) {
+  for (int ph = from; ph < NP; ++ph) {
     const int np = n[ph];
     int got = -1;
     auto claim = [&](int x) {
