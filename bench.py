@@ -335,7 +335,7 @@ def _timeline_text(name, recs, bins=24):
     t0 = min(r[1] for r in rows)
     t1 = max(r[3] for r in rows)
     span = max(1, t1 - t0)
-    head = f"**{name}**: one overlapped call, span {span / 100:.1f} us.  Per bin of {span / bins / 100:.1f} us: " \
+    head = f"**{name}**: one call, span {span / 100:.1f} us.  Per bin of {span / bins / 100:.1f} us: " \
            "units active (of which waiting for a signal)."
     lines = [head, "", "| t (us) | " + " | ".join(k[1] for k in kinds) + " |",
              "|---|" + "---|" * len(kinds)]
