@@ -198,8 +198,9 @@ class Timer:
         self._check()
         return {m: sorted(v)[len(v) // 2] for m, v in got.items()}
 
-    def kernels(self, mode, n, which):
-        """Median kernel ms (library events) over n calls, per kernel slot."""
+    def kernels(self, mode, n, which, spread=None):
+        """Median kernel ms (library events) over n calls, per kernel slot;
+        with a dict `spread`, also its p10 and p90 per slot."""
         torch, ctx = self.torch, self.ctx
         kms = {k: [] for k in which}
         ctx.enable_kernel_timing(True)
@@ -210,6 +211,10 @@ class Timer:
         torch.cuda.synchronize()
         ctx.enable_kernel_timing(False)
         self._check()
+        if spread is not None:
+            for k, v in kms.items():
+                v = sorted(v)
+                spread[k] = (v[len(v) // 10], v[(9 * len(v)) // 10])
         return {k: sorted(v)[len(v) // 2] for k, v in kms.items()}
 
 
@@ -462,12 +467,15 @@ def main():
     timer = Timer(torch, tsg, ctx, ag_fn)
     n = max(5, min(args.steps, 30))
     tm = timer.modes((tsg.OVERLAP, tsg.SERIAL, tsg.COMPUTE_ONLY, tsg.COMM_ONLY), n)
-    k_ov = timer.kernels(tsg.OVERLAP, n, (0, 1))
+    k_spread = {}
+    k_ov = timer.kernels(tsg.OVERLAP, max(n, 50), (0, 1), k_spread)
     k_co = timer.kernels(tsg.COMPUTE_ONLY, n, (0,))
     k_cm = timer.kernels(tsg.COMM_ONLY, n, (1,))
     ag = _summary(ag_flops, ag_gemm_bytes + ag_copy_bytes,
                   {"overlap": tm[tsg.OVERLAP], "serial": tm[tsg.SERIAL],
                    "compute_only": tm[tsg.COMPUTE_ONLY], "comm_only": tm[tsg.COMM_ONLY]})
+    ag["kernel_ms_p10_p90"] = {"gemm_in_overlap": [round(x, 5) for x in k_spread[0]],
+                               "copy_in_overlap": [round(x, 5) for x in k_spread[1]]}
     ag["kernel_ms"] = {"gemm_in_overlap": round(k_ov[0], 5), "copy_in_overlap": round(k_ov[1], 5),
                        "gemm_alone": round(k_co[0], 5), "copy_alone": round(k_cm[1], 5)}
     paths = {"ag_gemm": ag}
