@@ -90,9 +90,10 @@ typedef struct tsg_opts {
   /* GEMM tile configuration id (BM x BN, waves), 0 = the op's default.
    * AG+GEMM: 1 = 256x256 (2x2), 2 = 256x224 (4x1), 3 = 128x128 (2x2),
    * 4 = 256x128 (2x2), 5 = 128x256 (2x2), 6 = 64x64 (1), 7 = 128x64 (2x1),
-   * 8 = 256x224 (8x1, two waves per SIMD).  GEMM+RS and the MLP (both
-   * GEMMs): 1, 3, 4, 5.  An id the op does not have is rejected with
-   * TSG_E_INVALID. */
+   * 8 = 256x224 (8x1, two waves per SIMD), 9 = 256x224 (4x2 on 16x16x32
+   * MFMA fragments, two waves per SIMD; needs K % 128 == 0, else
+   * TSG_E_UNSUPPORTED).  GEMM+RS and the MLP (both GEMMs): 1, 3, 4, 5.  An
+   * id the op does not have is rejected with TSG_E_INVALID. */
   int tile;
   /* Tile order knob.  AG+GEMM: 0 = start at the local chunk and follow the
    * arrival order; 1 = plain row-major order.  GEMM+RS: 0 = local chunk

@@ -107,7 +107,7 @@ def test_ag_ragged_shapes(env, tile):
                 assert err_ratio(c, ref, scale, bf16_out=out_bf16) <= 1.0
 
 
-@pytest.mark.parametrize("tile", [8, 2, 1])
+@pytest.mark.parametrize("tile", [8, 2, 1, 9])
 def test_ag_direct_path_ragged(env, tile):
     # K a multiple of 128 (operands go straight to LDS); M and N ragged against
     # the 256-row tiles and 224- or 256-column tiles; 3 ranks of 200 rows, so
@@ -123,6 +123,20 @@ def test_ag_direct_path_ragged(env, tile):
                 full, c = case.run(opts={"tile": tile, "aux_cus": aux, "comm_tile": 128})
                 assert np.array_equal(full, inp["a"])
                 assert err_ratio(c, ref, scale, bf16_out=out_bf16) <= 1.0
+
+
+def test_ag_tile9_needs_k_multiple_of_128(env):
+    # 16x16x32-fragment tiles load operands straight to LDS only
+    torch, tsg, ctx = env
+    M, N, K, R = 512, 224, 392, 2
+    inp = ag_inputs(M, K, N, R, seed=10)
+    case = AgCase(env, inp, M, N, K, R, 0, True)
+    st = tsg.gemm_ag_overlap(ctx, case.loc, case.peers, case.full, case.b, case.c, tsg.BF16, M, N, K, R, 0,
+                             opts={"tile": 9}, raise_on_error=False)
+    assert st == tsg.E_UNSUPPORTED
+    full, c = case.run(opts={"tile": 8})
+    ref, scale = _ref(inp)
+    assert np.array_equal(full, inp["a"]) and err_ratio(c, ref, scale, bf16_out=True) <= 1.0
 
 
 def test_ag_paced_arrival(env):

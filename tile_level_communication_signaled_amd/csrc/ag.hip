@@ -108,7 +108,7 @@ __device__ __forceinline__ uint64_t pace_base(const CopyArgs& a) {
 // a workgroup of NT threads with the same u.
 template <int NT>
 __device__ __forceinline__ void copy_unit(const CopyArgs& a, int u) {
-  constexpr int U = 8;  // 8-byte words in flight per thread
+  constexpr int U = 4;  // 8-byte words in flight per thread (8 moved data no faster)
   const int vpr = 1 << a.vpr_log2;
   const uint64_t t0 = a.tl.buf ? wall_clock64() : 0;
   int s, rem, npc;
@@ -218,7 +218,11 @@ __device__ __forceinline__ void leave_queue(const CopyArgs& a) {
 
 // Copy kernel: takes units from the queue in order (slab-major) until none
 // is left.  It never waits, so it always drains the queue.
-__global__ void __launch_bounds__(256) ag_copy_kernel(const CopyArgs a) {
+//
+// Capped at 32 registers (the attribute counts half the unified register
+// file): beside two waves of a 512-thread GEMM tile of up to 240 registers
+// each, a copy wave still fits on every SIMD.
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_num_vgpr(16))) ag_copy_kernel(const CopyArgs a) {
   __shared__ int slot;
   for (int u = claim_unit(a, &slot); u < a.n_units; u = claim_unit(a, &slot)) copy_unit<256>(a, u);
   if (threadIdx.x == 0) leave_queue(a);
@@ -379,6 +383,7 @@ using Cfg5 = TileCfg<128, 256, 2, 2>;
 using Cfg6 = TileCfg<64, 64, 1, 1>;
 using Cfg7 = TileCfg<128, 64, 2, 1>;
 using Cfg8 = TileCfg<256, 224, 8, 1>;
+using Cfg9 = TileCfg<256, 224, 4, 2, 16>;  // 16x16x32 fragments, waves of 64 x 112
 
 struct TileShape {
   int bm, bn;
@@ -394,6 +399,7 @@ TileShape shape_of(int id) {
     case 6: return {64, 64};
     case 7: return {128, 64};
     case 8: return {256, 224};
+    case 9: return {256, 224};
     default: return {0, 0};
   }
 }
@@ -435,6 +441,7 @@ const void* gemm_fn(int id, bool bf16, int K, int* nt) {
     TSG_AG_CFG(6, Cfg6)
     TSG_AG_CFG(7, Cfg7)
     TSG_AG_CFG(8, Cfg8)
+    TSG_AG_CFG(9, Cfg9)
 #undef TSG_AG_CFG
     default: *nt = 0; return nullptr;
   }
@@ -450,14 +457,16 @@ hipError_t launch_gemm(int id, const AgGemmArgs& a, bool bf16, int grid, hipStre
     case 6: return launch_gemm_cfg<Cfg6>(a, bf16, grid, s);
     case 7: return launch_gemm_cfg<Cfg7>(a, bf16, grid, s);
     case 8: return launch_gemm_cfg<Cfg8>(a, bf16, grid, s);
+    case 9: return launch_gemm_cfg<Cfg9>(a, bf16, grid, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-int default_tile(int M, int N) {
-  // 256 x 224 (eight waves of 32 rows) when it gives whole waves of 256
-  // tiles (e.g. 8192 x 1792)
-  if (N % 224 == 0 && M % 256 == 0 && ((M / 256) * (N / 224)) % 256 == 0) return 8;
+int default_tile(int M, int N, int K) {
+  // 256 x 224 when it gives whole waves of 256 tiles (e.g. 8192 x 1792):
+  // eight waves of 64 x 112 on 16x16x32 fragments where K allows, which read
+  // 31% fewer LDS bytes per MFMA than waves of 32 x 224 on 32x32x16 ones
+  if (N % 224 == 0 && M % 256 == 0 && ((M / 256) * (N / 224)) % 256 == 0) return K % 128 ? 8 : 9;
   if (M >= 2048 && N >= 1024) return 1;
   if (M >= 512 && N >= 256) return 3;
   return 6;
@@ -499,9 +508,11 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
 
   const Opts o = resolve(opts, -1);
   if (o.arrival_gbps < 0) return fail(ctx, TSG_E_INVALID, "arrival_gbps must be >= 0");
-  const int tile = o.tile ? o.tile : default_tile(M, N);
+  const int tile = o.tile ? o.tile : default_tile(M, N, K);
   const TileShape ts = shape_of(tile);
   if (!ts.bm) return fail(ctx, TSG_E_INVALID, "unknown tile id %d", tile);
+  if (tile == 9 && K % 128)
+    return fail(ctx, TSG_E_UNSUPPORTED, "tile 9 needs K a multiple of 128 (direct-to-LDS loads only)");
   const int chunk_rows = M / R;
   const int n_mt = (M + ts.bm - 1) / ts.bm, n_nt = (N + ts.bn - 1) / ts.bn;
   if (n_mt > kMaxMTiles) return fail(ctx, TSG_E_UNSUPPORTED, "M / BM exceeds %d", kMaxMTiles);

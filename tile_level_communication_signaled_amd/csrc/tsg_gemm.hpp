@@ -37,18 +37,24 @@
 // and use the matrix units ([TL] section 4.3).
 #pragma once
 
+#include <type_traits>
+
 #include "tsg_device.hpp"
 
 namespace tsg {
 
-template <int BM_, int BN_, int WM_, int WN_>
+// MF: edge of the MFMA fragments, 32 (v_mfma_f32_32x32x16_bf16, four k steps
+// of 16 per BK step) or 16 (v_mfma_f32_16x16x32_bf16, two k steps of 32).
+template <int BM_, int BN_, int WM_, int WN_, int MF_ = 32>
 struct TileCfg {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, MF = MF_;
   static constexpr int BK = 64;
   static constexpr int NW = WM * WN;
   static constexpr int NT = 64 * NW;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
-  static constexpr int FM = WTM / 32, FN = WTN / 32;
+  static constexpr int FM = WTM / MF, FN = WTN / MF;
+  static constexpr int KS = BK / (MF == 32 ? 16 : 32);  // MFMA k steps per BK step
+  static_assert(MF == 32 || MF == 16, "fragments of 32 or 16");
   static constexpr int A_STAGE = BM * BK * 2;
   static constexpr int B_STAGE = BN * BK * 2;
   static constexpr int LDS_DIRECT = 3 * A_STAGE + 2 * B_STAGE;
@@ -60,7 +66,7 @@ struct TileCfg {
   static constexpr int B_BL = BN;                   // 8x8 blocks per B stage
   static constexpr int B_PT = (B_BL + NT - 1) / NT; // blocks per thread
   static constexpr int VM_PER_STEP = A_BPW + 8 * B_PT;  // VMEM ops per thread per step
-  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
+  static_assert(WTM % MF == 0 && WTN % MF == 0, "wave tile must be a multiple of the fragment");
   static_assert(BN % 8 == 0 && BM % 8 == 0, "BM and BN must be multiples of 8");
   static_assert(LDS_REGS <= 160 * 1024, "LDS budget of one CU exceeded");
   static_assert(VM_PER_STEP < 64, "too many loads per step for one wait count");
@@ -141,7 +147,9 @@ struct NoHook {
 
 template <class Cfg>
 struct GemmTile {
-  using Acc = f32x16_t[Cfg::FM][Cfg::FN];
+  using AccV = std::conditional_t<Cfg::MF == 32, f32x16_t, f32x4_t>;
+  static constexpr int ACC_N = Cfg::MF == 32 ? 16 : 4;  // accumulator registers per fragment
+  using Acc = AccV[Cfg::FM][Cfg::FN];
 
   struct BRegs {
     u32x4_t b[Cfg::B_PT][8];
@@ -153,7 +161,7 @@ struct GemmTile {
 #pragma unroll
       for (int j = 0; j < Cfg::FN; ++j)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+        for (int v = 0; v < ACC_N; ++v) acc[i][j][v] = 0.f;
   }
 
   // Thread q of a B stage moves the 8 x 8 block at k block (q mod 8) and n
@@ -301,13 +309,17 @@ struct GemmTile {
   // at row i, columns 4q .. 4q + 3; lanes 16-31 take the next 16 columns and
   // lanes 32-63 rows 8-11.  The second read of a fragment is 4 rows further,
   // step ks 16 rows further (neither changes row mod 4).
+  // With 16-column fragments (MF = 16) the four 16-lane groups take k rows
+  // 8 g .. 8 g + 7 of the 32-wide k step (two reads of four rows) and the
+  // same 16 columns: lane l ends with column (l mod 16) and k values
+  // 8 (l / 16) .. + 7, the B operand layout of the 16x16x32 MFMA.
   __device__ __forceinline__ static void tr_lane_offsets(int wn0, uint32_t (&off)[Cfg::FN]) {
     const int lane = threadIdx.x & 63;
     const int hi = lane >> 5, g = lane >> 4, sl = lane & 15;
-    const int row = 8 * hi + (sl >> 2);
+    const int row = Cfg::MF == 32 ? 8 * hi + (sl >> 2) : 8 * g + (sl >> 2);
 #pragma unroll
     for (int j = 0; j < Cfg::FN; ++j) {
-      const int col = wn0 + 32 * j + 16 * (g & 1) + 4 * (sl & 3);
+      const int col = Cfg::MF == 32 ? wn0 + 32 * j + 16 * (g & 1) + 4 * (sl & 3) : wn0 + 16 * j + 4 * (sl & 3);
       const int chunk = (col >> 3) ^ b_swz(row);
       off[j] = (uint32_t)((row * Cfg::BN + chunk * 8 + (col & 7)) * 2);
     }
@@ -316,7 +328,7 @@ struct GemmTile {
   __device__ __forceinline__ static bf16x8_t read_b_tr(const char* lb, uint32_t lane_off, int ks) {
     typedef short v4i16 __attribute__((ext_vector_type(4)));
     typedef short v8i16 __attribute__((ext_vector_type(8)));
-    const char* p = lb + lane_off + ks * 16 * Cfg::BN * 2;
+    const char* p = lb + lane_off + ks * (Cfg::MF == 32 ? 16 : 32) * Cfg::BN * 2;
     const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p);
     const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (__attribute__((address_space(3))) v4i16*)(p + 4 * Cfg::BN * 2));
@@ -335,8 +347,12 @@ struct GemmTile {
     const int wave = threadIdx.x >> 6;
     const int wm0 = (wave / Cfg::WN) * Cfg::WTM;
 #pragma unroll
-    for (int i = 0; i < Cfg::FM; ++i)
-      f.a[i] = *(const bf16x8_t*)(la + lds_swz(wm0 + i * 32 + (lane & 31), 2 * ks + (lane >> 5)));
+    for (int i = 0; i < Cfg::FM; ++i) {
+      if constexpr (Cfg::MF == 32)
+        f.a[i] = *(const bf16x8_t*)(la + lds_swz(wm0 + i * 32 + (lane & 31), 2 * ks + (lane >> 5)));
+      else  // lane l: row (l mod 16), k chunk 4 ks + l / 16 of the BK step
+        f.a[i] = *(const bf16x8_t*)(la + lds_swz(wm0 + i * 16 + (lane & 15), 4 * ks + (lane >> 4)));
+    }
 #pragma unroll
     for (int j = 0; j < Cfg::FN; ++j) f.b[j] = read_b_tr(lb, tr_off[j], ks);
   }
@@ -344,8 +360,12 @@ struct GemmTile {
 #pragma unroll
     for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
-      for (int j = 0; j < Cfg::FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < Cfg::FN; ++j) {
+        if constexpr (Cfg::MF == 32)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+      }
   }
 
   // Main path (K % 128 == 0): both operands go from global memory straight
@@ -455,12 +475,17 @@ struct GemmTile {
       }
       const char* la = lds_a + sa * Cfg::A_STAGE;
       const char* lb = lds_b + (kt & 1) * Cfg::B_STAGE;
-      read_frags(f1, la, lb, tr_off, 1);
-      mma(f0, acc);
-      read_frags(f0, la, lb, tr_off, 2);
-      mma(f1, acc);
-      read_frags(f1, la, lb, tr_off, 3);
-      mma(f0, acc);
+      if constexpr (Cfg::KS == 4) {
+        read_frags(f1, la, lb, tr_off, 1);
+        mma(f0, acc);
+        read_frags(f0, la, lb, tr_off, 2);
+        mma(f1, acc);
+        read_frags(f1, la, lb, tr_off, 3);
+        mma(f0, acc);
+      } else {
+        read_frags(f1, la, lb, tr_off, 1);
+        mma(f0, acc);
+      }
       sa = sa == 2 ? 0 : sa + 1;
       if (kt + 1 < nk) {
         if (kt + 2 < nk) wait_vmcnt<Cfg::A_BPW>(); else wait_vmcnt<0>();
@@ -478,8 +503,11 @@ struct GemmTile {
   __device__ __forceinline__ static void run_regs(const ARows& ar, const uint16_t* __restrict__ B,
                                                   int64_t ldb, int col0, int N, int K, char* lds,
                                                   Acc& acc, Hook hook = Hook()) {
-    const int tid = threadIdx.x;
     zero(acc);
+    if constexpr (Cfg::MF != 32) {
+      return;  // 16-column fragments have the main path only (the host requires K % 128 == 0)
+    } else {
+    const int tid = threadIdx.x;
     constexpr int STAGE = Cfg::A_STAGE + Cfg::B_STAGE;
     u32x4_t ra[Cfg::A_PT];
     BRegs rb;
@@ -523,6 +551,7 @@ struct GemmTile {
       if (kt + 1 < nk) store(cur ^ 1);
       lds_barrier();
     }
+    }
   }
 
   // Visit every accumulator element: f(row_in_tile, col_in_tile, value).
@@ -538,9 +567,13 @@ struct GemmTile {
 #pragma unroll
       for (int j = 0; j < Cfg::FN; ++j)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = wm0 + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-          const int c = wn0 + j * 32 + (lane & 31);
+        for (int v = 0; v < ACC_N; ++v) {
+          // 32x32 result: lane l has column l mod 32, register v row
+          // 8 (v / 4) + 4 (l / 32) + v mod 4; 16x16: column l mod 16, row
+          // 4 (l / 16) + v
+          const int r = Cfg::MF == 32 ? wm0 + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3)
+                                      : wm0 + i * 16 + (lane >> 4) * 4 + v;
+          const int c = Cfg::MF == 32 ? wn0 + j * 32 + (lane & 31) : wn0 + j * 16 + (lane & 15);
           f(r, c, acc[i][j][v]);
         }
   }
@@ -573,16 +606,17 @@ struct GemmTile {
     const int wm0 = (wave / Cfg::WN) * Cfg::WTM;
     const int wn0 = (wave % Cfg::WN) * Cfg::WTN;
     char* reg = lds + wave * (Cfg::WTM * STRIDE);
-    char* wr = reg + ((lane >> 5) * 4) * STRIDE + (lane & 31) * 2;
+    char* wr = Cfg::MF == 32 ? reg + ((lane >> 5) * 4) * STRIDE + (lane & 31) * 2
+                             : reg + ((lane >> 4) * 4) * STRIDE + (lane & 15) * 2;
 #pragma unroll
     for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
       for (int j = 0; j < Cfg::FN; ++j)
       {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = i * 32 + (v >> 2) * 8 + (v & 3);
-          *(uint16_t*)(wr + r * STRIDE + j * 64) = (uint16_t)f32_to_bf16(f(acc[i][j][v]));
+        for (int v = 0; v < ACC_N; ++v) {
+          const int r = Cfg::MF == 32 ? i * 32 + (v >> 2) * 8 + (v & 3) : i * 16 + v;
+          *(uint16_t*)(wr + r * STRIDE + j * 2 * Cfg::MF) = (uint16_t)f32_to_bf16(f(acc[i][j][v]));
         }
         // one fragment at a time: keeps the compiler from moving every
         // accumulator into vector registers at once
