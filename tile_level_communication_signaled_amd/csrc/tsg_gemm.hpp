@@ -2,8 +2,9 @@
 //
 // One workgroup computes a BM x BN tile of C = A * B with A [M x K] and
 // B [K x N] both row-major bf16, accumulating in fp32 with
-// v_mfma_f32_32x32x16_bf16.  The K loop moves BK = 64 columns of A and rows of
-// B per step through LDS:
+// v_mfma_f32_32x32x16_bf16 (or, for tiles whose fragment size MF is 16 and
+// only on the main path, v_mfma_f32_16x16x32_bf16).  The K loop moves BK = 64
+// columns of A and rows of B per step through LDS:
 //
 //   * A is staged as BM rows x 8 chunks of 16 bytes (8 bf16 along k).  On the
 //     main path A goes straight from global memory to LDS (16-byte
@@ -301,8 +302,16 @@ struct GemmTile {
   // c ^ (2 (r mod 4)) (rows of an odd multiple of 128 bytes, which leaves a
   // two-way overlap); chunks are permuted within aligned groups of 16 or 8,
   // so a row keeps its place.
+  // With 16-column fragments one half wave reads rows 8 g .. 8 g + 3 for
+  // g = 0, 1 (32 bytes of each); rows eight apart start at the same bank
+  // whenever BN is a multiple of 16, so when the rows are otherwise
+  // unswizzled, chunk c of a row with bit 3 set is stored at c ^ 2 (32
+  // bytes over, within its aligned group of four chunks).
   static constexpr int B_SWZ = Cfg::BN % 128 == 0 ? 4 : Cfg::BN % 64 == 0 ? 2 : 0;
-  __device__ __forceinline__ static int b_swz(int row) { return B_SWZ * (row & 3); }
+  static constexpr int B_SWZ8 = (Cfg::MF == 16 && B_SWZ == 0 && Cfg::BN % 32 == 0) ? 2 : 0;
+  __device__ __forceinline__ static int b_swz(int row) {
+    return B_SWZ * (row & 3) ^ B_SWZ8 * ((row >> 3) & 1);
+  }
 
   // LDS byte offset of this lane's transpose reads of B fragment j (32
   // columns at wn0 + 32 j), step 0: lane 4i + q of each 16-lane group points
