@@ -108,7 +108,7 @@ __device__ __forceinline__ uint64_t pace_base(const CopyArgs& a) {
 // a workgroup of NT threads with the same u.
 template <int NT>
 __device__ __forceinline__ void copy_unit(const CopyArgs& a, int u) {
-  constexpr int U = 4;  // 8-byte words in flight per thread (8 moved data no faster)
+  constexpr int U = 8;  // 8-byte words in flight per thread
   const int vpr = 1 << a.vpr_log2;
   const uint64_t t0 = a.tl.buf ? wall_clock64() : 0;
   int s, rem, npc;
@@ -165,11 +165,16 @@ __device__ __forceinline__ void copy_unit(const CopyArgs& a, int u) {
       uint32_t off = (uint32_t)rr * row_bytes + (uint32_t)cw * 8u;
       int r = rr;
       for (; r + (U - 1) * rows_p < nr; r += U * rows_p, off += U * step) {
+        // addresses as base + q * step + off: eight words in flight fit in
+        // the kernel's 32 registers (the form base + (off + q * step) kept
+        // one offset register per word and did not)
         uint64_t v[U];
 #pragma unroll
-        for (int q = 0; q < U; ++q) v[q] = __builtin_nontemporal_load((const uint64_t*)(sk + (off + q * step)));
+        for (int q = 0; q < U; ++q) {
+          v[q] = __builtin_nontemporal_load((const uint64_t*)(sk + (size_t)q * step + off));
+        }
 #pragma unroll
-        for (int q = 0; q < U; ++q) store_coherent((uint64_t*)(dk + (off + q * step)), v[q]);
+        for (int q = 0; q < U; ++q) store_coherent((uint64_t*)(dk + (size_t)q * step + off), v[q]);
       }
       for (; r < nr; r += rows_p, off += step)
         store_coherent((uint64_t*)(dk + off), __builtin_nontemporal_load((const uint64_t*)(sk + off)));
