@@ -134,10 +134,25 @@ struct RouteArgs {
 };
 
 // Expert ids of pairs [p0, p1) of the block starting at 16-byte aligned p0,
-// visited in order: f(p, e).
+// visited in order: f(p, e).  Groups of eight 16-byte loads are issued
+// before any of their ids is used, so a block costs one memory round trip
+// per 32 pairs rather than one per 4.
 template <class F>
 __device__ __forceinline__ void route_block(const int32_t* __restrict__ ids, int p0, int p1, F&& f) {
+  constexpr int G = 8;
   int p = p0;
+  for (; p + 4 * G <= p1; p += 4 * G) {
+    int4 v[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) v[i] = *(const int4*)(ids + p + 4 * i);
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      f(p + 4 * i, v[i].x);
+      f(p + 4 * i + 1, v[i].y);
+      f(p + 4 * i + 2, v[i].z);
+      f(p + 4 * i + 3, v[i].w);
+    }
+  }
   for (; p + 4 <= p1; p += 4) {
     const int4 v = *(const int4*)(ids + p);
     f(p, v.x);
