@@ -12,10 +12,11 @@
 // Topk-Reduce).
 //
 // Kernels (one call):
-//   1. moe_route_kernel (one workgroup): expert_counts, a stable counting sort
-//      of the pairs p = t*k + s by expert (sorted_ids, order (expert, t, s)),
-//      and the lookup tables of the padded layout: every expert's rows are
-//      padded to a multiple of BM = 256, row block rb belongs to one expert,
+//   1. moe_route_kernel (one workgroup) and moe_place_kernel (one wave per
+//      block of pairs): expert_counts, a stable counting sort of the pairs
+//      p = t*k + s by expert (sorted_ids, order (expert, t, s)), and the
+//      lookup tables of the padded layout: every expert's rows are padded
+//      to a multiple of BM = 256, row block rb belongs to one expert,
 //      row_pair[row] = pair id or -1, row_token[row] = token or -1,
 //      pair_row[p] = padded row of pair p.
 //   2. moe_producer_kernel (persistent, atomic work queue): first every "up"
@@ -113,24 +114,39 @@ Ws bind(char* base, const Layout& L) {
 }
 
 // ------------------------------------------------------------------ route
-// One workgroup.  Thread j owns the contiguous pair block
-// [j*PB, (j+1)*PB) (PB a multiple of 4, read as 16-byte vectors); per-thread,
-// per-expert counts live in LDS (uint16; every count and prefix is below
-// 65536 because T*k is).  Stable: the position of pair p is offs[e] + (pairs
-// of e in earlier blocks) + (pairs of e earlier in p's own block).  The
-// prefix over blocks is a scan per expert across the workgroup: a shuffle
-// scan within each wave, then the totals of the earlier waves.
+// Two kernels.  The pairs are cut into blocks of PB (a multiple of 64) in
+// order.  moe_route_kernel (one workgroup, thread j counting block j)
+// counts every expert's pairs per block in LDS (uint16; every count and
+// prefix is below 65536 because T*k is), scans the counts per expert over
+// the blocks (a shuffle scan within each wave, then the totals of the
+// earlier waves), writes the expert offsets, clears the lookup tables and
+// leaves pre[e][j] = pairs of e in blocks before j.  moe_place_kernel (one
+// wave per block, spread over the CUs) then places the block's pairs 64 at
+// a time.  Stable: the position of pair p is offs[e] + pre[e][j] + (pairs
+// of e earlier in p's own block).
 constexpr int kRouteWaves = kRouteThreads / 64;
 constexpr int kRouteMaxPairs = 65535;
+__host__ __device__ constexpr int route_pb(int P) {
+  return ((P + kRouteThreads - 1) / kRouteThreads + 63) & ~63;
+}
 
 struct RouteArgs {
   const int32_t* ids;
   int32_t* counts;
   int32_t* sorted_ids;
   Ws ws;
+  int* pre;             // [E][kRouteThreads] per-block prefixes (scratch)
   uint32_t* status;
   int T, E, k;
   int64_t rows_max, n_rb_max;
+};
+
+struct PlaceArgs {
+  const int32_t* ids;
+  int32_t* sorted_ids;
+  Ws ws;
+  const int* pre;
+  int P, E, k, PB;
 };
 
 // Expert ids of pairs [p0, p1) of the block starting at 16-byte aligned p0,
@@ -171,7 +187,7 @@ __global__ void __launch_bounds__(kRouteThreads) moe_route_kernel(const RouteArg
   const int j = threadIdx.x;
   const int lane = j & 63, wave = j >> 6;
   const int P = a.T * a.k, E = a.E;
-  const int PB = ((P + kRouteThreads - 1) / kRouteThreads + 3) & ~3;
+  const int PB = route_pb(P);
   const int p0 = min(P, j * PB), p1 = min(P, p0 + PB);
   for (int e = 0; e < E; ++e) cnt[e][j] = 0;
   if (j == 0) s_bad = 0;
@@ -242,16 +258,48 @@ __global__ void __launch_bounds__(kRouteThreads) moe_route_kernel(const RouteArg
   __syncthreads();
   for (int e = 0; e < E; ++e)
     for (int rb = s_poffs[e] / BM + j; rb < s_poffs[e + 1] / BM; rb += kRouteThreads) a.ws.rb_expert[rb] = e;
-  route_block(a.ids, p0, p1, [&](int p, int e) {
-    if (e < 0 || e >= E) return;
-    const int rank = cnt[e][j]++;
-    const int pos = s_offs[e] + rank;
-    const int row = s_poffs[e] + rank;
-    a.sorted_ids[pos] = p;
-    a.ws.pair_row[p] = row;
-    a.ws.row_pair[row] = p;
-    a.ws.row_token[row] = p / a.k;
-  });
+  for (int e = 0; e < E; ++e) a.pre[e * kRouteThreads + j] = cnt[e][j];
+}
+
+// One wave per block of PB pairs.  Each group of 64 pairs is ranked per
+// expert with ballots: for each expert present, the lanes holding it learn
+// their order among them, and the block's running count of that expert
+// (in LDS) advances by their number.
+__global__ void __launch_bounds__(64) moe_place_kernel(const PlaceArgs a) {
+  __shared__ int run[kMaxExperts], s_offs[kMaxExperts], s_poffs[kMaxExperts];
+  const int j = blockIdx.x, lane = threadIdx.x;
+  for (int e = lane; e < a.E; e += 64) {
+    run[e] = a.pre[e * kRouteThreads + j];
+    s_offs[e] = a.ws.offs[e];
+    s_poffs[e] = a.ws.poffs[e];
+  }
+  __syncthreads();
+  const uint64_t below = (1ull << lane) - 1;
+  const int p_end = min(a.P, (j + 1) * a.PB);
+  for (int c0 = j * a.PB; c0 < p_end; c0 += 64) {
+    const int p = c0 + lane;
+    const int e = p < p_end ? a.ids[p] : -1;
+    const bool ok = e >= 0 && e < a.E;
+    uint64_t todo = __ballot(ok);
+    while (todo) {
+      const int l = (int)__builtin_ctzll(todo);
+      const int el = __builtin_amdgcn_readlane(e, l);
+      const uint64_t m = __ballot(ok && e == el);
+      const int base = run[el];
+      if (ok && e == el) {
+        const int rank = base + __popcll(m & below);
+        const int row = s_poffs[el] + rank;
+        a.sorted_ids[s_offs[el] + rank] = p;
+        a.ws.pair_row[p] = row;
+        a.ws.row_pair[row] = p;
+        a.ws.row_token[row] = p / a.k;
+      }
+      __syncthreads();  // every lane has read run[el] before it advances
+      if (lane == l) run[el] = base + __popcll(m);
+      __syncthreads();
+      todo &= ~m;
+    }
+  }
 }
 
 // --------------------------------------------------------------- producer
@@ -623,6 +671,18 @@ tsg_status tsg_op_moe(tsg_ctx* ctx, const void* x, const int32_t* topk_ids, cons
   ra.k = k;
   ra.rows_max = L.rows_max;
   ra.n_rb_max = L.n_rb_max;
+  // the per-block prefixes use the start of the y staging area, which only
+  // the down tiles write, after the routing (E * 1 KiB <= its size)
+  ra.pre = (int*)ws.y;
+  PlaceArgs pl;
+  pl.ids = topk_ids;
+  pl.sorted_ids = sorted_ids;
+  pl.ws = ws;
+  pl.pre = ra.pre;
+  pl.P = T * k;
+  pl.E = E;
+  pl.k = k;
+  pl.PB = route_pb(T * k);
 
   ProdArgs pa;
   pa.x = (const uint16_t*)x;
@@ -662,7 +722,10 @@ tsg_status tsg_op_moe(tsg_ctx* ctx, const void* x, const int32_t* topk_ids, cons
 
   auto route = [&]() -> tsg_status {
     hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(kRouteThreads), 0, caller, ra);
-    return check_launch(ctx, "moe_route_kernel");
+    tsg_status rs = check_launch(ctx, "moe_route_kernel");
+    if (rs != TSG_OK) return rs;
+    hipLaunchKernelGGL(moe_place_kernel, dim3((pl.P + pl.PB - 1) / pl.PB), dim3(64), 0, caller, pl);
+    return check_launch(ctx, "moe_place_kernel");
   };
   auto produce = [&](hipStream_t s, int nwg) -> tsg_status {
     // every producer workgroup ends with one failing ticket: the queue moves
