@@ -98,7 +98,8 @@ CALIB_BYTES = 1 << 30   # the plain device copy that --counters runs: 1 GiB read
 
 
 KERNELS = ("ag_gemm_kernel", "ag_copy_kernel", "rs_gemm_kernel", "rs_reduce_kernel", "mlp_gemm1_kernel",
-           "mlp_gemm2_kernel", "moe_route_kernel", "moe_producer_kernel", "moe_combine_kernel")
+           "mlp_gemm2_kernel", "moe_route_kernel", "moe_place_kernel", "moe_producer_kernel",
+           "moe_combine_kernel")
 
 
 def summarize_counters(fetch_csv: str, write_csv: str, out_path: str = TRAFFIC) -> dict:
