@@ -98,7 +98,10 @@ def _check(inp, out, counts, sorted_ids, y_bf16=False):
     return r, res
 
 
-@pytest.mark.parametrize("T,H,I,E", [(100, 256, 128, 4), (37, 136, 200, 3), (1, 64, 64, 2), (300, 512, 256, 8)])
+# (9000, ...) and (32767, ...): routed pair blocks of 128 and 256 pairs, the
+# second at the largest T * k the routing takes (65534 pairs)
+@pytest.mark.parametrize("T,H,I,E", [(100, 256, 128, 4), (37, 136, 200, 3), (1, 64, 64, 2), (300, 512, 256, 8),
+                                     (9000, 64, 72, 5), (32767, 64, 64, 8)])
 def test_moe_small(env, T, H, I, E):
     inp = moe_inputs(T, H, I, E, k=2, seed=T + E)
     out, counts, sorted_ids = MoeCase(env, inp).run()
