@@ -390,7 +390,7 @@ def main():
             for name, (fn, *_rest) in _other_paths(torch, tsg, ctx).items():
                 runs.append((name, fn, tsg.OVERLAP))
         for name, fn, mode in runs:
-            for i in range(20):
+            for i in range(200):
                 fn(i, mode)
             torch.cuda.synchronize()
             fn(0, mode, tsg.Opts(aux_cus=args.aux_cus, tile=args.tile, timeline=1))
