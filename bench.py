@@ -36,6 +36,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "overlapped TFLOP/s, % bf16 MFMA peak, speedup vs serialized copy+GEMM"
 XGMI_GBPS = 1071            # arrival pacing of the xGMI-paced AG line: 7 links x ~153 GB/s
+DMA_AUX_CUS = 32            # CUs left to the runtime's copies in the copy-engine AG line
 CSRC = os.path.join(ROOT, "tile_level_communication_signaled_amd", "csrc")
 TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -491,6 +492,18 @@ def main():
             {"overlap": tp[tsg.OVERLAP], "serial": tp[tsg.SERIAL], "compute_only": tp[tsg.COMPUTE_ONLY],
              "comm_only": tp[tsg.COMM_ONLY]})
         paths["ag_gemm_xgmi_paced"]["arrival_gbps"] = XGMI_GBPS
+        # the same AllGather + GEMM with the chunks moved by the DMA copy
+        # engines (one copy and one signal copy per chunk, one stream); the
+        # overlap runs on a CU split, which the runtime's kernel-run small
+        # copies need
+        dma = tsg.Opts(aux_cus=DMA_AUX_CUS, tile=args.tile, copy_engine=1)
+        td = Timer(torch, tsg, ctx, lambda i, mode, o=None: ag_fn(i, mode, dma)).modes(
+            (tsg.OVERLAP, tsg.SERIAL, tsg.COMPUTE_ONLY, tsg.COMM_ONLY), n)
+        paths["ag_gemm_copy_engine"] = _summary(
+            ag_flops, ag_gemm_bytes + ag_copy_bytes,
+            {"overlap": td[tsg.OVERLAP], "serial": td[tsg.SERIAL], "compute_only": td[tsg.COMPUTE_ONLY],
+             "comm_only": td[tsg.COMM_ONLY]})
+        paths["ag_gemm_copy_engine"]["aux_cus"] = DMA_AUX_CUS
 
     if args.paths == "all":
         for name, (fn, flops, nbytes, modes) in _other_paths(torch, tsg, ctx).items():

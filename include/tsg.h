@@ -140,6 +140,18 @@ typedef struct tsg_opts {
    * arrival such as seven peers over xGMI ([TD] section 3.6: AMD all-to-all
    * links; section 3.7: arrival order).  Negative: TSG_E_INVALID. */
   int arrival_gbps;
+  /* AG+GEMM: 1 = move the gathered data with the DMA copy engines instead of
+   * the CU copy kernel ([TD] section 3.6: intra-node AllGather on AMD with
+   * copy engines, whose signals are sent as a separate transfer).  Each
+   * chunk is one hipMemcpyAsync with hipMemcpyDeviceToDeviceNoCU on the op's
+   * side stream, in arrival order, followed by an 8-byte copy that sets the
+   * chunk's signal; comm_tile is ignored (one signal per chunk, [TD] section
+   * 3.2).  The GEMM pulls nothing.  The runtime still moves some of these
+   * copies (the 8-byte signal copies among them) with a kernel, so overlap
+   * mode needs a CU split (aux_cus >= 8): on shared CUs it returns
+   * TSG_E_UNSUPPORTED.  0 = the CU copy kernel (default).  Other values, or
+   * together with arrival_gbps: TSG_E_INVALID. */
+  int copy_engine;
 } tsg_opts;
 
 /* ------------------------------------------------------------------ ctx */

@@ -139,6 +139,30 @@ def test_ag_tile9_needs_k_multiple_of_128(env):
     assert np.array_equal(full, inp["a"]) and err_ratio(c, ref, scale, bf16_out=True) <= 1.0
 
 
+def test_ag_copy_engine(env):
+    # the gathered data moved by the DMA copy engines, one copy per chunk and
+    # its signal set by a following 8-byte copy: the same results in serial
+    # and comm-only mode and in overlap on a CU split (comm_tile is ignored);
+    # overlap on shared CUs is refused before anything is launched
+    torch, tsg, ctx = env
+    M, N, K, R = 600, 232, 384, 3
+    inp = ag_inputs(M, K, N, R, seed=11)
+    ref, scale = _ref(inp)
+    for rank in range(R):
+        case = AgCase(env, inp, M, N, K, R, rank, True)
+        for mode, aux in ((tsg.OVERLAP, 16), (tsg.SERIAL, -1), (tsg.SERIAL, 16), (tsg.COMM_ONLY, -1)):
+            for ct in (128, 0):
+                full, c = case.run(mode=mode, opts={"copy_engine": 1, "aux_cus": aux, "comm_tile": ct})
+                assert np.array_equal(full, inp["a"]), (rank, mode, aux, ct)
+                if mode != tsg.COMM_ONLY:
+                    assert err_ratio(c, ref, scale, bf16_out=True) <= 1.0, (rank, mode, aux, ct)
+    for bad, want in (({"copy_engine": 1, "arrival_gbps": 2}, tsg.E_INVALID), ({"copy_engine": 2}, tsg.E_INVALID),
+                      ({"copy_engine": 1}, tsg.E_UNSUPPORTED)):
+        st = tsg.gemm_ag_overlap(ctx, case.loc, case.peers, case.full, case.b, case.c, tsg.BF16, M, N, K, R, 0,
+                                 opts=bad, raise_on_error=False)
+        assert st == want, bad
+
+
 def test_ag_paced_arrival(env):
     # arrival paced at 2 GB/s: the same results, and a call takes at least
     # the gathered bytes over the rate (in every mode that copies)

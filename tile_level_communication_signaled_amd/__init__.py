@@ -53,6 +53,7 @@ class Opts(ctypes.Structure):
         ("pull_units", ctypes.c_int),
         ("stage_dtype", ctypes.c_int),
         ("arrival_gbps", ctypes.c_int),
+        ("copy_engine", ctypes.c_int),
     ]
 
 

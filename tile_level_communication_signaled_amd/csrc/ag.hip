@@ -39,6 +39,7 @@ constexpr size_t kSigBase = size_t(1) << 18;  // AG slab signals in the context'
 constexpr size_t kSigCap = size_t(1) << 18;   // slots up to the next op's region
 constexpr int kQueueSlot = 40;                // copy work queue in the context's ticket words
 constexpr size_t kPaceSlot = 8;               // arrival-pacing start time in the context's pool
+constexpr size_t kDmaSigSlot = 9;             // slab signal value the copy engines copy in
 
 struct ChunkOrder {
   int8_t chunk[kMaxRanks];  // chunk copied at arrival position p (p = 0: local)
@@ -231,6 +232,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_num_vgpr(16))) ag_c
   __shared__ int slot;
   for (int u = claim_unit(a, &slot); u < a.n_units; u = claim_unit(a, &slot)) copy_unit<256>(a, u);
   if (threadIdx.x == 0) leave_queue(a);
+}
+
+// Copy-engine arrival: the value each slab's signal takes this call, staged
+// where the 8-byte signal copies read it.
+__global__ void ag_dma_sigval_kernel(uint64_t* w, uint64_t v) {
+  if (threadIdx.x == 0) *w = v;
 }
 
 // ---------------------------------------------------------------- GEMM
@@ -513,6 +520,15 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
 
   const Opts o = resolve(opts, -1);
   if (o.arrival_gbps < 0) return fail(ctx, TSG_E_INVALID, "arrival_gbps must be >= 0");
+  if (o.copy_engine != 0 && o.copy_engine != 1) return fail(ctx, TSG_E_INVALID, "copy_engine must be 0 or 1");
+  if (o.copy_engine && o.arrival_gbps)
+    return fail(ctx, TSG_E_INVALID, "copy_engine and arrival_gbps cannot be combined");
+  // The runtime moves some device-to-device copies (the 8-byte signal copies
+  // among them) with a kernel even when asked for the copy engines; beside a
+  // GEMM that holds every CU while it waits, that kernel could not start.
+  if (o.copy_engine && mode == TSG_MODE_OVERLAP && o.aux_cus < 0)
+    return fail(ctx, TSG_E_UNSUPPORTED, "copy_engine overlap needs a CU split (aux_cus): the runtime runs small "
+                                        "device copies as kernels, which need a free CU");
   const int tile = o.tile ? o.tile : default_tile(M, N, K);
   const TileShape ts = shape_of(tile);
   if (!ts.bm) return fail(ctx, TSG_E_INVALID, "unknown tile id %d", tile);
@@ -530,6 +546,7 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
   int k_pow2 = 64;
   while (k_pow2 < K) k_pow2 *= 2;
   slab = std::min(std::min(slab, k_pow2), 2048);
+  if (o.copy_engine) slab = k_pow2;  // copy engines: one signal per chunk (one slab)
   int slab_log2 = 0;
   while ((1 << slab_log2) < slab) ++slab_log2;
   const int n_slab = (K + slab - 1) / slab;
@@ -553,7 +570,7 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
     const tsg_status ss = streams(ctx, o, &pr, (hipStream_t)stream);
     if (ss != TSG_OK) return ss;
     if (o.aux_wgs <= 0) nwg = o.aux_cus < 0 ? ctx->n_cus : pr.aux_cus * 4;
-    if (mode == TSG_MODE_OVERLAP && o.aux_cus < 0) {
+    if (mode == TSG_MODE_OVERLAP && o.aux_cus < 0 && !o.copy_engine) {  // copy engines need no CU
       int nt = 0;
       const void* fn = gemm_fn(tile, c_dtype == TSG_BF16, K, &nt);
       back_to_back = !co_resident(ctx, fn, nt, (const void*)&ag_copy_kernel, 256);
@@ -681,7 +698,7 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
   int pull = 0;
   int gemm_nt = 0;
   (void)gemm_fn(tile, c_dtype == TSG_BF16, K, &gemm_nt);
-  if (mode == TSG_MODE_OVERLAP && !back_to_back && o.aux_cus < 0 && o.pull_units >= 0 &&
+  if (mode == TSG_MODE_OVERLAP && !back_to_back && o.aux_cus < 0 && o.pull_units >= 0 && !o.copy_engine &&
       (gemm_nt == 256 || gemm_nt == 512)) {
     pull = o.pull_units > 0 ? o.pull_units : std::min(ctx->n_cus, ustart[1]);
     pull = (int)std::min<int64_t>(std::min(pull, grid_gemm), n_units);
@@ -690,7 +707,26 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
   ga.pull_wgs = 0;
   ga.copy = ca;
 
+  // Copy engines: each chunk (contiguous rows) one copy in arrival order,
+  // then its signal.  Copies on one stream run in order, so a signal lands
+  // after its data.
+  auto dma = [&](hipStream_t s) -> tsg_status {
+    time_begin(ctx, 1, s);
+    const size_t bytes = (size_t)chunk_rows * K * 2;
+    for (int p = 0; p < R; ++p) {
+      const int c = ca.ord.chunk[p];
+      const char* src = c == rank ? (const char*)a_local
+                                  : (const char*)a_peers + (size_t)(c < rank ? c : c - 1) * bytes;
+      TSG_HIP(ctx, hipMemcpyAsync((char*)a_full + (size_t)c * bytes, src, bytes, hipMemcpyDeviceToDeviceNoCU, s));
+      if (!((o.skip_mask >> c) & 1u))
+        TSG_HIP(ctx, hipMemcpyAsync(ctx->d_sig + kSigBase + (size_t)c * n_slab, ctx->d_sig + kDmaSigSlot, 8,
+                                    hipMemcpyDeviceToDeviceNoCU, s));
+    }
+    time_end(ctx, 1, s);
+    return TSG_OK;
+  };
   auto copy = [&](hipStream_t s) -> tsg_status {
+    if (o.copy_engine) return dma(s);
     time_begin(ctx, 1, s);
     hipLaunchKernelGGL(ag_copy_kernel, dim3(copy_grid), dim3(256), 0, s, ca);
     time_end(ctx, 1, s);
@@ -708,6 +744,13 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
   };
 
   tsg_status st = TSG_OK;
+  if (o.copy_engine && mode != TSG_MODE_COMPUTE_ONLY) {
+    // the signal value, staged before any copy or GEMM workgroup runs
+    hipLaunchKernelGGL(ag_dma_sigval_kernel, dim3(1), dim3(64), 0, caller, ctx->d_sig + kDmaSigSlot,
+                       ((uint64_t)ga.sa.epoch << 32) | 1u);
+    st = check_launch(ctx, "ag_dma_sigval_kernel");
+    if (st != TSG_OK) return st;
+  }
   if (back_to_back) {
     st = copy(caller);
     if (st == TSG_OK) st = gemm(caller, 1, ctx->n_cus);

@@ -53,6 +53,7 @@ Opts resolve(const tsg_opts* o, int default_aux_cus) {
   r.pull_units = o ? o->pull_units : 0;
   r.stage_dtype = o ? o->stage_dtype : TSG_F32;
   r.arrival_gbps = o ? o->arrival_gbps : 0;
+  r.copy_engine = o ? o->copy_engine : 0;
   return r;
 }
 

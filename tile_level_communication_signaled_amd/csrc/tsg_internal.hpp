@@ -72,6 +72,7 @@ struct Opts {
   int pull_units; // 0 = the op's default, -1 = none
   int stage_dtype; // MoE y staging: TSG_F32 or TSG_BF16
   int arrival_gbps; // AG arrival pacing, 0 = none
+  int copy_engine;  // AG: 1 = DMA copy engines move the data
 };
 Opts resolve(const tsg_opts* o, int default_aux_cus);
 
