@@ -144,9 +144,11 @@ typedef struct tsg_opts {
    * the CU copy kernel ([TD] section 3.6: intra-node AllGather on AMD with
    * copy engines, whose signals are sent as a separate transfer).  Each
    * chunk is one hipMemcpyAsync with hipMemcpyDeviceToDeviceNoCU on the op's
-   * side stream, in arrival order, followed by an 8-byte copy that sets the
-   * chunk's signal; comm_tile is ignored (one signal per chunk, [TD] section
-   * 3.2).  The GEMM pulls nothing.  The runtime still moves some of these
+   * side stream, in arrival order, followed by 8-byte copies that set the
+   * signals of the chunk's column slabs (comm_tile defaults to 2048 columns
+   * here; every slab of a chunk is released after the chunk's one copy, as
+   * with the one signal per chunk of [TD] section 3.2).  The GEMM pulls
+   * nothing.  The runtime still moves some of these
    * copies (the 8-byte signal copies among them) with a kernel, so overlap
    * mode needs a CU split (aux_cus >= 8): on shared CUs it returns
    * TSG_E_UNSUPPORTED.  0 = the CU copy kernel (default).  Other values, or

@@ -141,9 +141,10 @@ def test_ag_tile9_needs_k_multiple_of_128(env):
 
 def test_ag_copy_engine(env):
     # the gathered data moved by the DMA copy engines, one copy per chunk and
-    # its signal set by a following 8-byte copy: the same results in serial
-    # and comm-only mode and in overlap on a CU split (comm_tile is ignored);
-    # overlap on shared CUs is refused before anything is launched
+    # its slabs' signals set by following 8-byte copies: the same results in
+    # serial and comm-only mode and in overlap on a CU split, for slabs of 128
+    # columns and the default; overlap on shared CUs is refused before
+    # anything is launched
     torch, tsg, ctx = env
     M, N, K, R = 600, 232, 384, 3
     inp = ag_inputs(M, K, N, R, seed=11)

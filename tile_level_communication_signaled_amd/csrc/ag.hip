@@ -540,13 +540,12 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
 
   // Communication tile: slab width W (power of two, >= 64; capped at 2048
   // columns and at the first power of two >= K, which is one slab per chunk).
-  int slab = o.comm_tile ? o.comm_tile : 512;
+  int slab = o.comm_tile ? o.comm_tile : (o.copy_engine ? 2048 : 512);
   if (slab < 64 || (slab & (slab - 1)))
     return fail(ctx, TSG_E_INVALID, "comm_tile must be a power of two >= 64 (got %d)", slab);
   int k_pow2 = 64;
   while (k_pow2 < K) k_pow2 *= 2;
   slab = std::min(std::min(slab, k_pow2), 2048);
-  if (o.copy_engine) slab = k_pow2;  // copy engines: one signal per chunk (one slab)
   int slab_log2 = 0;
   while ((1 << slab_log2) < slab) ++slab_log2;
   const int n_slab = (K + slab - 1) / slab;
@@ -587,7 +586,7 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
   while (unit_vec < 8192 && unit_vec * 2 * nwg <= total_vec) unit_vec *= 2;
   const int rows_q = 256 >> vpr_log2;  // rows one pass of the workgroup moves
   auto pieces_for_rows = [&](int64_t rows) {
-    rows = std::max<int64_t>(rows, std::min(rows_q, chunk_rows));
+    rows = std::max<int64_t>(1, std::max<int64_t>(rows, std::min(rows_q, chunk_rows)));
     return (int)std::max<int64_t>(1, (chunk_rows + rows - 1) / rows);
   };
   const int np_body = pieces_for_rows(unit_vec >> vpr_log2);
@@ -708,8 +707,8 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
   ga.copy = ca;
 
   // Copy engines: each chunk (contiguous rows) one copy in arrival order,
-  // then its signal.  Copies on one stream run in order, so a signal lands
-  // after its data.
+  // then the signals of its slabs.  Copies on one stream run in order, so a
+  // signal lands after its data.
   auto dma = [&](hipStream_t s) -> tsg_status {
     time_begin(ctx, 1, s);
     const size_t bytes = (size_t)chunk_rows * K * 2;
@@ -719,8 +718,9 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
                                   : (const char*)a_peers + (size_t)(c < rank ? c : c - 1) * bytes;
       TSG_HIP(ctx, hipMemcpyAsync((char*)a_full + (size_t)c * bytes, src, bytes, hipMemcpyDeviceToDeviceNoCU, s));
       if (!((o.skip_mask >> c) & 1u))
-        TSG_HIP(ctx, hipMemcpyAsync(ctx->d_sig + kSigBase + (size_t)c * n_slab, ctx->d_sig + kDmaSigSlot, 8,
-                                    hipMemcpyDeviceToDeviceNoCU, s));
+        for (int sl = 0; sl < n_slab; ++sl)
+          TSG_HIP(ctx, hipMemcpyAsync(ctx->d_sig + kSigBase + (size_t)c * n_slab + sl, ctx->d_sig + kDmaSigSlot,
+                                      8, hipMemcpyDeviceToDeviceNoCU, s));
     }
     time_end(ctx, 1, s);
     return TSG_OK;
