@@ -52,7 +52,7 @@ def _parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--headline-only", action="store_true",
                    help="time only the headline overlap steps (for kernel traces)")
-    p.add_argument("--trace-path", choices=["gemm_rs", "mlp2", "moe", "moe_bf16_staging"],
+    p.add_argument("--trace-path", choices=["gemm_rs", "mlp2", "moe", "moe_bf16_staging", "ag_copy_engine"],
                    help="time only this path's overlap steps (for kernel traces of that path), print one "
                         "JSON line and exit")
     p.add_argument("--counters", action="store_true",
@@ -405,7 +405,11 @@ def main():
         return
 
     if args.trace_path:
-        fn, flops, _nbytes, _modes = _other_paths(torch, tsg, ctx)[args.trace_path]
+        if args.trace_path == "ag_copy_engine":
+            dma = tsg.Opts(aux_cus=DMA_AUX_CUS, tile=args.tile, copy_engine=1)
+            fn, flops = (lambda i, mode, o=None: ag_fn(i, mode, dma)), ag_flops
+        else:
+            fn, flops, _nbytes, _modes = _other_paths(torch, tsg, ctx)[args.trace_path]
         for i in range(args.warmup):
             fn(i, tsg.OVERLAP)
         if ctx.check() != tsg.OK:
