@@ -97,7 +97,11 @@ typedef struct tsg_opts {
   int tile;
   /* Tile order knob.  AG+GEMM: 0 = start at the local chunk and follow the
    * arrival order; 1 = plain row-major order.  GEMM+RS: 0 = local chunk
-   * first, 1 = local chunk last ([TD] section 3.7). */
+   * first, 1 = local chunk last ([TD] section 3.7).  MLP2 (both GEMMs):
+   * 0 = row-block-major, so GEMM1 completes row blocks one after another
+   * and GEMM2's first tiles read the first ones; 1 = groups of 8 tile rows
+   * walked column by column (operand reuse in each XCD's L2 when every tile
+   * runs at once).  Other values: TSG_E_INVALID (MLP2). */
   int order;
   /* Bound of every device-side signal wait, in milliseconds (0 = 2000). */
   uint32_t timeout_ms;
@@ -274,18 +278,26 @@ tsg_status gemm_rs_overlap(tsg_ctx* ctx, const void* x, const void* w, float* pa
  * GEMM; [TL] Table 3: a consumer tile is ready when all the producer tiles
  * it depends on are done).
  *
- * GEMM1 (producer, its own CU partition) computes h = bf16(GELU(x * w1))
- * (exact erf GELU on the fp32 accumulator, rounded to nearest even) and,
- * after each tile, releases a count on the signal of its 128-row block.
- * GEMM2 (consumer, the other partition) computes y = h * w2 (fp32), each
- * tile starting as soon as every GEMM1 tile of its row block is done.
+ * GEMM1 (producer) computes h = bf16(GELU(x * w1)) (exact erf GELU on the
+ * fp32 accumulator, rounded to nearest even) and, after each tile, counts
+ * an arrival on the signal of each 128-row block the tile covers.  GEMM2
+ * (consumer) computes y = h * w2 (fp32); each tile starts as soon as every
+ * GEMM1 tile of its row blocks is done.
  *
  *   x   bf16 [M x K1], w1 bf16 [K1 x N1], h bf16 [M x N1] (output),
  *   w2  bf16 [N1 x N2], y f32 [M x N2] (output)
  * Constraints: N1 % 8 == 0, N2 % 8 == 0, K1 % 8 == 0, all >= 8, M >= 1.
- * Default split: 64 CUs for GEMM2, 192 for GEMM1 (opts.aux_cus / main_cus).  COMPUTE_ONLY runs GEMM1 then GEMM2 on the whole GPU
- * without waits (identical to SERIAL for this op); COMM_ONLY is
- * unsupported (TSG_E_UNSUPPORTED): both halves are compute. */
+ * CU partition in OVERLAP mode:
+ *   aux_cus = 0 or -1 (default): shared CUs.  Both GEMMs run in one
+ *     persistent kernel on every CU; its workgroups take GEMM1 tiles first
+ *     and GEMM2 tiles after, from per-XCD ticket queues, and a GEMM2 tile
+ *     waits for its row blocks' signals.
+ *   aux_cus = q > 0: GEMM1 runs on main_cus CUs (default 256 - q) and GEMM2
+ *     as a persistent consumer kernel on the other q CUs, concurrently (for
+ *     example the 192/64 split: aux_cus = 64).
+ * COMPUTE_ONLY runs GEMM1 then GEMM2 on the whole GPU without waits
+ * (identical to SERIAL for this op); COMM_ONLY is unsupported
+ * (TSG_E_UNSUPPORTED): both halves are compute. */
 tsg_status mlp2_pipelined(tsg_ctx* ctx, const void* x, const void* w1, void* h,
                           const void* w2, float* y, int M, int K1, int N1, int N2,
                           const tsg_opts* opts, int mode, void* stream);
@@ -317,7 +329,15 @@ tsg_status mlp2_pipelined(tsg_ctx* ctx, const void* x, const void* w1, void* h,
  * 1 <= E <= 256, T >= 1, H % 8 == 0, I % 8 == 0, H, I >= 8; x, topk_ids,
  * w_up, w_down, out and workspace 16-byte aligned (TSG_E_ALIGN).  Expert ids outside [0, E) are
  * detected on the device: the affected pairs are dropped and the call's
- * tsg_check returns TSG_E_INVALID.  Default combine partition (aux_cus): 16 CUs. */
+ * tsg_check returns TSG_E_INVALID.
+ * CU partition in OVERLAP mode:
+ *   aux_cus = 0 or -1 (default): shared CUs.  One persistent kernel on every
+ *     CU takes the up tiles, then the down tiles, then the combine units
+ *     from one ticket queue; a combine unit waits for the ready signals of
+ *     its down tile and of the tiles holding its tokens' other slots.
+ *   aux_cus = q > 0: the producer (up and down tiles) runs on main_cus CUs
+ *     (default 256 - q) and the combine as a persistent consumer kernel on
+ *     the other q CUs, concurrently (the 16-CU consumer: aux_cus = 16). */
 tsg_status moe_expert_combine(tsg_ctx* ctx, const void* x, const int32_t* topk_ids,
                               const float* topk_w, const void* w_up, const void* w_down,
                               float* out, int32_t* expert_counts, int32_t* sorted_ids,
@@ -330,6 +350,41 @@ enum { TSG_OP_AG = 0, TSG_OP_RS = 1, TSG_OP_MLP2 = 2, TSG_OP_MOE = 3 };
 /* Workspace bytes an op needs for `dims` (TSG_OP_MOE: {T, H, I, E, k});
  * 0 for ops that need none or for invalid dims. */
 size_t tsg_workspace_bytes(int op, const int64_t* dims);
+
+/* Layout of the MoE workspace for dims = {T, H, I, E, k}, so that the
+ * intermediate results of a completed call can be read back (tests compare
+ * them with an independent reference).  out[i] receives field i, for
+ * i < n <= TSG_MOE_LAYOUT_N; region fields are byte offsets from the start
+ * of the workspace.  After moe_expert_combine has completed on its stream
+ * the regions hold ([TL] section 4.1, dynamic mapping: these are the lookup
+ * tables that map row tiles to experts and rows to pairs, filled at run
+ * time from topk_ids):
+ *   TSG_MOE_META       int32[2]: row blocks in use, routed pairs kept
+ *   TSG_MOE_OFFS       int32[E+1]: exclusive prefix sum of expert_counts
+ *   TSG_MOE_POFFS      int32[E+1]: first padded row of each expert (every
+ *                      expert's rows are padded to a multiple of BM)
+ *   TSG_MOE_RB_EXPERT  int32[RB_MAX]: expert of each BM-row block, -1 past
+ *                      the last block in use
+ *   TSG_MOE_ROW_PAIR   int32[ROWS_MAX]: pair p = t*k + s held by each padded
+ *                      row, -1 for padding rows
+ *   TSG_MOE_ROW_TOKEN  int32[ROWS_MAX]: token of each padded row, -1 for
+ *                      padding rows
+ *   TSG_MOE_PAIR_ROW   int32[T*k]: padded row of each pair
+ *   TSG_MOE_H          bf16 [ROWS_MAX x I]: bf16(SiLU(x[t] w_up[e])) of the
+ *                      pair in each row (padding rows: unspecified)
+ *   TSG_MOE_Y          [ROWS_MAX x H]: y of the pair in each row, fp32 (bf16
+ *                      with stage_dtype = TSG_BF16; padding rows:
+ *                      unspecified)
+ * TSG_MOE_TOTAL = tsg_workspace_bytes; TSG_MOE_ROWS_MAX, TSG_MOE_RB_MAX:
+ * the padded rows and row blocks the layout provides for; TSG_MOE_BM: rows
+ * per block.  Returns TSG_E_SHAPE for dims moe_expert_combine rejects,
+ * TSG_E_INVALID for a null `out` or n outside [0, TSG_MOE_LAYOUT_N]. */
+enum {
+  TSG_MOE_META = 0, TSG_MOE_OFFS, TSG_MOE_POFFS, TSG_MOE_RB_EXPERT, TSG_MOE_ROW_PAIR, TSG_MOE_ROW_TOKEN,
+  TSG_MOE_PAIR_ROW, TSG_MOE_H, TSG_MOE_Y, TSG_MOE_TOTAL, TSG_MOE_ROWS_MAX, TSG_MOE_RB_MAX, TSG_MOE_BM,
+  TSG_MOE_LAYOUT_N
+};
+tsg_status tsg_moe_workspace_layout(const int64_t* dims, int64_t* out, int n);
 
 #ifdef __cplusplus
 }

@@ -67,3 +67,23 @@ def test_opts_struct_layout_matches_header(tmp_path):
 def test_workspace_query_is_host_only():
     import tile_level_communication_signaled_amd as tsg
     assert tsg.workspace_bytes(tsg.OP_AG, [1, 1, 1, 1, 1]) == 0
+
+
+@pytest.mark.skipif(not os.path.exists(LIB), reason="library not built")
+def test_moe_workspace_layout_is_consistent():
+    # host-only query: regions in order, 256-byte aligned, each large enough
+    # for what the header says it holds, and the total equal to the size query
+    import tile_level_communication_signaled_amd as tsg
+    T, H, I, E, k = 4096, 4096, 1408, 8, 2
+    L = tsg.moe_workspace_layout([T, H, I, E, k])
+    assert L["total"] == tsg.workspace_bytes(tsg.OP_MOE, [T, H, I, E, k])
+    assert L["rows_max"] == L["rb_max"] * L["bm"]
+    assert L["rows_max"] >= T * k + E * (L["bm"] - 1)
+    sizes = {"meta": 8, "offs": 4 * (E + 1), "poffs": 4 * (E + 1), "rb_expert": 4 * L["rb_max"],
+             "row_pair": 4 * L["rows_max"], "row_token": 4 * L["rows_max"], "pair_row": 4 * T * k,
+             "h": 2 * L["rows_max"] * I, "y": 4 * L["rows_max"] * H}
+    order = ["meta", "offs", "poffs", "rb_expert", "row_pair", "row_token", "pair_row", "h", "y"]
+    for a, b in zip(order, order[1:] + ["total"]):
+        assert L[a] % 256 == 0 and L[a] + sizes[a] <= L[b], (a, b)
+    with pytest.raises(tsg.TsgError):
+        tsg.moe_workspace_layout([T, H, I, E, 3])

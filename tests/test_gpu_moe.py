@@ -1,15 +1,27 @@
 """MoE expert compute + overlapped gate-weighted combine on the GPU against
 the oracle.
 
-Routing bookkeeping (expert_counts, sorted_ids) must match bit for bit.  out is
-pre-filled with NaN, so a token never combined, or combined from a tile read
-before its ready signal, shows up as a non-finite element.
+Before every call out is filled with NaN, and the whole workspace (routing
+tables, h, y staging) with 0xFF bytes (NaN in bf16 and fp32, -1 in int32): a
+down tile that read h before its row block's signal, or a combine that read y
+before its tile's ready signal, yields a non-finite element.
 
-Bound on out: the GEMM bound on the down projection with the oracle's h,
-1e-3 * sum_s g_s sum_k |h_sk w_down_kj| + 1e-5, plus the effect of the largest
-difference the device's h may have from the oracle's: per element of h,
-1.1 * (1e-3 * sum |x w_up| + 1e-5) (|SiLU'| <= 1.1) plus one bf16 quantum,
-carried through |w_down| and the gates."""
+Checked after each call:
+  * expert_counts and sorted_ids bit for bit;
+  * the device's lookup tables, read through tsg_moe_workspace_layout, bit
+    for bit: the expert of each row block against oracle.moe_tile_table, the
+    expert offsets, and the row of each pair and the pair of each row
+    implied by the oracle's stable routing order and padded offsets;
+  * the device's h (per pair, through the pair -> row table) against the
+    oracle's h: u differs by at most the GEMM bound 1e-3 * sum_k |x w_up| +
+    1e-5, SiLU changes that by at most |SiLU'| <= 1.1 times, and the two
+    roundings to bf16 add at most one bf16 quantum;
+  * out against the oracle's out under the GEMM bound of the down projection,
+    1e-3 * sum_s g_s sum_k |h_sk w_down_kj| + 1e-5, plus the device's actual
+    h difference carried through |w_down| and the gates,
+    sum_s g_s sum_k |h_gpu - h_ref|_sk |w_down_kj| (with bf16 y staging, also
+    the gate times one bf16 quantum of y per slot).
+The ratio under the plain per-element GEMM bound (no h term) is printed too."""
 import numpy as np
 import pytest
 
@@ -34,6 +46,7 @@ class MoeCase:
     def __init__(self, env, inp):
         torch, tsg, ctx = env
         self.env = env
+        self.inp = inp
         T, H = inp["x"].shape
         E, _, I = inp["w_up"].shape
         self.T, self.H, self.I, self.E, self.k = T, H, I, E, inp["topk_ids"].shape[1]
@@ -45,17 +58,24 @@ class MoeCase:
         self.out = torch.empty((T, H), dtype=torch.float32, device="cuda")
         self.counts = torch.empty((E,), dtype=torch.int32, device="cuda")
         self.sorted = torch.empty((T * self.k,), dtype=torch.int32, device="cuda")
-        self.wsb = tsg.workspace_bytes(tsg.OP_MOE, [T, H, I, E, self.k])
+        dims = [T, H, I, E, self.k]
+        self.wsb = tsg.workspace_bytes(tsg.OP_MOE, dims)
         assert self.wsb > 0
+        self.lay = tsg.moe_workspace_layout(dims)
+        assert self.lay["total"] == self.wsb
         self.ws = torch.empty((self.wsb,), dtype=torch.uint8, device="cuda")
 
     def run(self, mode=None, opts=None, expect=0, poison=True):
+        """One call; outputs poisoned first, and the workspace too except in
+        COMM_ONLY mode, whose combine reads the staging a previous call left."""
         torch, tsg, ctx = self.env
         mode = tsg.OVERLAP if mode is None else mode
         if poison:
             self.out.fill_(float("nan"))
             self.counts.fill_(-7)
             self.sorted.fill_(-7)
+            if mode != tsg.COMM_ONLY:
+                self.ws.fill_(0xFF)
         tsg.moe_expert_combine(ctx, self.x, self.ids, self.g, self.wu, self.wd, self.out, self.counts,
                                self.sorted, self.ws, self.wsb, self.T, self.H, self.I, self.E, self.k,
                                opts=opts, mode=mode)
@@ -64,38 +84,83 @@ class MoeCase:
         return (self.out.cpu().numpy().astype(np.float64), self.counts.cpu().numpy(),
                 self.sorted.cpu().numpy())
 
+    def tables(self):
+        """The device's routing tables and h from the workspace of the last call."""
+        L, E, P = self.lay, self.E, self.T * self.k
+        ws = self.ws.cpu().numpy()
 
-def _bound(inp, res, y_bf16=False):
-    """Per-element tolerance of out (see module docstring).  With the y
-    staging in bf16, each slot's y is rounded once more before the combine:
-    its gate times one bf16 quantum of y (twice the half quantum, as the
-    device's y may lie across a power of two from the oracle's) is added."""
-    x = oracle.bf16_to_f64(inp["x"])
-    ids, g = inp["topk_ids"], inp["topk_w"].astype(np.float64)
-    T, k = ids.shape
-    H = inp["w_down"].shape[2]
-    extra = np.zeros((T * k, H))
-    for e in range(inp["w_up"].shape[0]):
-        pairs = np.nonzero(ids.reshape(-1) == e)[0]
-        if pairs.size == 0:
-            continue
-        s_up = np.abs(x[pairs // k]) @ np.abs(oracle.bf16_to_f64(inp["w_up"][e]))
-        h = oracle.bf16_to_f64(res["h"][pairs])
-        dh = 1.1 * (1e-3 * s_up + 1e-5) + 2 * bf16_half_quantum(h)
-        extra[pairs] = dh @ np.abs(oracle.bf16_to_f64(inp["w_down"][e]))
-    if y_bf16:
-        extra = extra + 2 * bf16_half_quantum(res["y"])
-    extra = (g.reshape(-1)[:, None] * extra).reshape(T, k, H).sum(axis=1)
-    return 1e-3 * res["scale"] + 1e-5 + extra
+        def i32(field, n):
+            o = L[field]
+            return ws[o:o + 4 * n].view(np.int32).copy()
+        rows = L["rows_max"]
+        h = ws[L["h"]:L["h"] + rows * self.I * 2].view(np.uint16).reshape(rows, self.I)
+        return dict(meta=i32("meta", 2), offs=i32("offs", E + 1), poffs=i32("poffs", E + 1),
+                    rb_expert=i32("rb_expert", L["rb_max"]), row_pair=i32("row_pair", rows),
+                    row_token=i32("row_token", rows), pair_row=i32("pair_row", P), h=h)
 
 
-def _check(inp, out, counts, sorted_ids, y_bf16=False):
+def _check_tables(case, res):
+    """Bit-exact lookup tables: the oracle's tile table and the row <-> pair
+    maps its stable order implies."""
+    tb = case.tables()
+    L, k, P = case.lay, case.k, case.T * case.k
+    counts, offsets, sorted_ids = oracle.moe_route(case.inp["topk_ids"], case.E)
+    poff, tiles = oracle.moe_tile_table(counts, L["bm"])
+    n_rb = len(tiles)
+    assert tb["meta"][0] == n_rb and tb["meta"][1] == P, tb["meta"]
+    assert np.array_equal(tb["offs"], offsets)
+    assert np.array_equal(tb["poffs"], poff)
+    assert np.array_equal(tb["rb_expert"][:n_rb], np.array([t[0] for t in tiles], dtype=np.int32))
+    assert np.all(tb["rb_expert"][n_rb:] == -1)
+    pair_row = np.empty(P, dtype=np.int64)
+    for e in range(case.E):
+        pairs = sorted_ids[offsets[e]:offsets[e + 1]]
+        pair_row[pairs] = poff[e] + np.arange(pairs.size)
+    assert np.array_equal(tb["pair_row"], pair_row)
+    row_pair = np.full(L["rows_max"], -1, dtype=np.int64)
+    row_pair[pair_row] = np.arange(P)
+    assert np.array_equal(tb["row_pair"], row_pair)
+    assert np.array_equal(tb["row_token"], np.where(row_pair >= 0, row_pair // k, -1))
+    return tb["h"][pair_row]
+
+
+def _check(case, out, counts, sorted_ids, y_bf16=False, label=""):
+    """Full check of one call; returns (max err/tol of out, of h, of out under
+    the plain GEMM bound)."""
+    inp = case.inp
     res = oracle.moe_expert_combine(inp["x"], inp["topk_ids"], inp["topk_w"], inp["w_up"], inp["w_down"])
     assert np.array_equal(counts, res["counts"])
     assert np.array_equal(sorted_ids, res["sorted_ids"])
+    h_dev = _check_tables(case, res)
+    x = oracle.bf16_to_f64(inp["x"])
+    ids, g = inp["topk_ids"], inp["topk_w"].astype(np.float64)
+    T, k = ids.shape
+    H = case.H
+    hg, hr = oracle.bf16_to_f64(h_dev), oracle.bf16_to_f64(res["h"])
+    assert np.all(np.isfinite(hg))
+    flat = ids.reshape(-1)
+    rh, prop = 0.0, np.zeros((T * k, H))
+    for e in range(case.E):
+        pairs = np.nonzero(flat == e)[0]
+        if pairs.size == 0:
+            continue
+        s_up = np.abs(x[pairs // k]) @ np.abs(oracle.bf16_to_f64(inp["w_up"][e]))
+        tol_h = 1.1 * (1e-3 * s_up + 1e-5) + 2 * bf16_half_quantum(hr[pairs]) + 1e-7
+        rh = max(rh, float(np.max(np.abs(hg[pairs] - hr[pairs]) / tol_h)))
+        prop[pairs] = np.abs(hg[pairs] - hr[pairs]) @ np.abs(oracle.bf16_to_f64(inp["w_down"][e]))
+    if y_bf16:
+        prop = prop + 2 * bf16_half_quantum(res["y"])
+    extra = (g.reshape(-1)[:, None] * prop).reshape(T, k, H).sum(axis=1)
+    plain = 1e-3 * res["scale"] + 1e-5
     assert np.all(np.isfinite(out))
-    r = float(np.max(np.abs(out - res["out"]) / _bound(inp, res, y_bf16)))
-    return r, res
+    err = np.abs(out - res["out"])
+    r = float(np.max(err / (plain + extra)))
+    r_plain = float(np.max(err / plain))
+    if label:
+        print(f"moe {label}: max err/tol {r:.4f} (h {rh:.4f}; plain GEMM bound {r_plain:.4f}), "
+              f"expert counts {counts.tolist()}")
+    assert rh <= 1.0, rh
+    return r, rh, r_plain
 
 
 # (9000, ...) and (32767, ...): routed pair blocks of 128 and 256 pairs, the
@@ -104,8 +169,9 @@ def _check(inp, out, counts, sorted_ids, y_bf16=False):
                                      (9000, 64, 72, 5), (32767, 64, 64, 8)])
 def test_moe_small(env, T, H, I, E):
     inp = moe_inputs(T, H, I, E, k=2, seed=T + E)
-    out, counts, sorted_ids = MoeCase(env, inp).run()
-    r, _ = _check(inp, out, counts, sorted_ids)
+    case = MoeCase(env, inp)
+    out, counts, sorted_ids = case.run()
+    r, _, _ = _check(case, out, counts, sorted_ids)
     assert r <= 1.0, r
 
 
@@ -118,7 +184,7 @@ def test_moe_skewed_routing_single_expert_heavy(env):
     inp["topk_ids"] = ids
     case = MoeCase(env, inp)
     out, counts, sorted_ids = case.run()
-    r, _ = _check(inp, out, counts, sorted_ids)
+    r, _, _ = _check(case, out, counts, sorted_ids)
     assert r <= 1.0
     assert counts[0] == T
 
@@ -129,8 +195,9 @@ def test_moe_zero_gate_slot_is_ignored_bit_exactly(env):
     g = np.zeros_like(inp["topk_w"])
     g[:, 0] = 1.0
     inp["topk_w"] = g
-    out1, c1, s1 = MoeCase(env, inp).run()
-    r, _ = _check(inp, out1, c1, s1)
+    case1 = MoeCase(env, inp)
+    out1, c1, s1 = case1.run()
+    r, _, _ = _check(case1, out1, c1, s1)
     assert r <= 1.0
     # move every second slot to another expert: with gate 0 the output cannot change
     ids = inp["topk_ids"].copy()
@@ -146,8 +213,9 @@ def test_moe_identical_experts(env):
     inp = moe_inputs(T, H, I, E, k=2, seed=33)
     inp["w_up"] = np.repeat(inp["w_up"][:1], E, axis=0)
     inp["w_down"] = np.repeat(inp["w_down"][:1], E, axis=0)
-    out, counts, sorted_ids = MoeCase(env, inp).run()
-    r, res = _check(inp, out, counts, sorted_ids)
+    case = MoeCase(env, inp)
+    out, counts, sorted_ids = case.run()
+    r, _, _ = _check(case, out, counts, sorted_ids)
     assert r <= 1.0
 
 
@@ -181,7 +249,7 @@ def test_moe_missing_row_block_times_out_then_recovers(env):
     case = MoeCase(env, inp)
     case.run(opts={"debug_skip_mask": 1 << 1, "timeout_ms": 20}, expect=tsg.E_TIMEOUT)
     out, counts, sorted_ids = case.run()
-    r, _ = _check(inp, out, counts, sorted_ids)
+    r, _, _ = _check(case, out, counts, sorted_ids)
     assert r <= 1.0
 
 
@@ -194,7 +262,7 @@ def test_moe_bf16_staging(env, T, H, I, E):
     case = MoeCase(env, inp)
     opt = {"stage_dtype": tsg.BF16}
     out, counts, sorted_ids = case.run(opts=opt)
-    r, _ = _check(inp, out, counts, sorted_ids, y_bf16=True)
+    r, _, _ = _check(case, out, counts, sorted_ids, y_bf16=True)
     assert r <= 1.0
     for mode in (tsg.SERIAL, tsg.COMPUTE_ONLY):
         case.run(mode=mode, opts=opt)
@@ -207,22 +275,27 @@ def test_moe_bf16_staging(env, T, H, I, E):
 
 
 def test_moe_full_size_parity_modes_splits(env):
+    # the Zipf-routed workload at full size: the shared-CU default and the
+    # 16-CU combine consumer each checked in full against the oracle
     torch, tsg, ctx = env
     cfg = CONFIGS["moe"]
     inp = moe_inputs(cfg["T"], cfg["H"], cfg["I"], cfg["E"], k=cfg["k"], seed=cfg["seed"], zipf=cfg["zipf"])
     case = MoeCase(env, inp)
     out, counts, sorted_ids = case.run()
-    r, _ = _check(inp, out, counts, sorted_ids)
-    print(f"moe max err/tol {r:.3f}, expert counts {counts.tolist()}")
+    r, _, _ = _check(case, out, counts, sorted_ids, label="overlap, shared CUs")
     assert r <= 1.0
+    out16, c16, s16 = case.run(opts={"aux_cus": 16})
+    r16, _, _ = _check(case, out16, c16, s16, label="overlap, 16-CU combine consumer")
+    assert r16 <= 1.0
+    assert np.array_equal(out16, out)
     out2, c2, s2 = case.run(mode=tsg.SERIAL)
     assert np.array_equal(out2, out) and np.array_equal(c2, counts) and np.array_equal(s2, sorted_ids)
+    # the combine alone, over the staging the serial call left
     out3, _, _ = case.run(mode=tsg.COMM_ONLY)
     assert np.array_equal(out3, out)
-    for opts in ({"aux_cus": 16}, {"aux_cus": 32}, {"aux_cus": -1}):
+    for opts in ({"aux_cus": 32}, {"aux_cus": -1}):
         out4, _, _ = case.run(opts=opts)
         assert np.array_equal(out4, out), opts
     out5, c5, s5 = case.run(opts={"stage_dtype": tsg.BF16})
-    r5, _ = _check(inp, out5, c5, s5, y_bf16=True)
-    print(f"moe bf16 staging max err/tol {r5:.3f}")
+    r5, _, _ = _check(case, out5, c5, s5, y_bf16=True, label="bf16 y staging")
     assert r5 <= 1.0

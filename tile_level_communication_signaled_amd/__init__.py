@@ -10,8 +10,11 @@ package without it raises ImportError.
 """
 from __future__ import annotations
 
+import atexit
 import ctypes
 import os
+import sys
+import weakref
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtsg.so")
@@ -35,8 +38,13 @@ OP_AG, OP_RS, OP_MLP2, OP_MOE = 0, 1, 2, 3
 EXPORTS = (
     "tsg_ctx_create", "tsg_ctx_destroy", "tsg_last_error", "tsg_check", "tsg_device_info",
     "tsg_enable_kernel_timing", "tsg_kernel_ms", "tsg_timeline", "tsg_workspace_bytes",
+    "tsg_moe_workspace_layout",
     "gemm_ag_overlap", "gemm_rs_overlap", "mlp2_pipelined", "moe_expert_combine",
 )
+
+# fields of tsg_moe_workspace_layout, in order
+MOE_LAYOUT_FIELDS = ("meta", "offs", "poffs", "rb_expert", "row_pair", "row_token", "pair_row", "h", "y",
+                     "total", "rows_max", "rb_max", "bm")
 
 
 class Opts(ctypes.Structure):
@@ -71,13 +79,15 @@ _lib.tsg_kernel_ms.argtypes = [_vp, _i, _P(ctypes.c_float)]
 _lib.tsg_timeline.argtypes = [_vp, _P(ctypes.c_uint64), _sz, _P(_sz)]
 _lib.tsg_workspace_bytes.argtypes = [_i, _P(ctypes.c_int64)]
 _lib.tsg_workspace_bytes.restype = _sz
+_lib.tsg_moe_workspace_layout.argtypes = [_P(ctypes.c_int64), _P(ctypes.c_int64), _i]
 _lib.gemm_ag_overlap.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _P(_i), _P(Opts), _i, _vp]
 _lib.gemm_rs_overlap.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _P(Opts), _i, _vp]
 _lib.mlp2_pipelined.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _P(Opts), _i, _vp]
 _lib.moe_expert_combine.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                                     _i, _i, _i, _i, _i, _P(Opts), _i, _vp]
 for _f in ("tsg_ctx_create", "tsg_check", "tsg_device_info", "tsg_enable_kernel_timing", "tsg_kernel_ms",
-           "tsg_timeline", "gemm_ag_overlap", "gemm_rs_overlap", "mlp2_pipelined", "moe_expert_combine"):
+           "tsg_timeline", "tsg_moe_workspace_layout", "gemm_ag_overlap", "gemm_rs_overlap", "mlp2_pipelined",
+           "moe_expert_combine"):
     getattr(_lib, _f).restype = _i
 
 
@@ -112,8 +122,28 @@ def _opts(o):
     return ctypes.byref(Opts(**o))
 
 
+# Contexts still open, closed by _close_all() at interpreter exit.  A context
+# owns HIP streams (CU-masked ones among them) and events; destroying them
+# must happen while the HIP runtime is fully alive.  Left to garbage
+# collection, a context can be destroyed during interpreter finalisation,
+# after a profiler's or the runtime's own exit handlers have started to tear
+# down the state those handles refer to.
+_LIVE = weakref.WeakSet()
+
+
+def _close_all():
+    for ctx in list(_LIVE):
+        ctx.close()
+
+
+atexit.register(_close_all)
+
+
 class Context:
-    """Owns one library context (signal words, side streams, timeline)."""
+    """Owns one library context (signal words, side streams, timeline).
+
+    Closed by close(), when collected, or at the latest from an atexit hook,
+    before the interpreter (and with it the HIP runtime) shuts down."""
 
     def __init__(self, device: int = 0):
         h = _vp()
@@ -121,6 +151,7 @@ class Context:
         if st != OK:
             raise TsgError(st, f"tsg_ctx_create(device={device}) failed")
         self._h = h
+        _LIVE.add(self)
 
     @property
     def handle(self):
@@ -130,8 +161,13 @@ class Context:
         if getattr(self, "_h", None):
             _lib.tsg_ctx_destroy(self._h)
             self._h = None
+        _LIVE.discard(self)
 
     def __del__(self):
+        # During interpreter shutdown the atexit hook has already closed every
+        # context; a collection this late must not call into the runtime.
+        if sys.is_finalizing():
+            return
         try:
             self.close()
         except Exception:
@@ -173,6 +209,18 @@ class Context:
 def workspace_bytes(op: int, dims) -> int:
     arr = (ctypes.c_int64 * len(dims))(*dims)
     return _lib.tsg_workspace_bytes(op, arr)
+
+
+def moe_workspace_layout(dims) -> dict:
+    """Regions of the MoE workspace for dims (T, H, I, E, k): byte offsets of
+    meta, offs, poffs, rb_expert, row_pair, row_token, pair_row, h and y, the
+    total size, and rows_max, rb_max and bm (see tsg_moe_workspace_layout)."""
+    arr = (ctypes.c_int64 * 5)(*dims)
+    out = (ctypes.c_int64 * len(MOE_LAYOUT_FIELDS))()
+    st = _lib.tsg_moe_workspace_layout(arr, out, len(MOE_LAYOUT_FIELDS))
+    if st != OK:
+        raise TsgError(st, f"no MoE workspace layout for dims {tuple(dims)}")
+    return dict(zip(MOE_LAYOUT_FIELDS, out))
 
 
 def gemm_ag_overlap(ctx: Context, a_local, a_peers, a_full, b, c, c_dtype, M, N, K, R, rank,

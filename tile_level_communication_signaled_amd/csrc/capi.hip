@@ -340,6 +340,11 @@ size_t tsg_workspace_bytes(int op, const int64_t* dims) {
   return 0;
 }
 
+tsg_status tsg_moe_workspace_layout(const int64_t* dims, int64_t* out, int n) {
+  if (!out || n < 0 || n > TSG_MOE_LAYOUT_N) return TSG_E_INVALID;
+  return tsg_moe_layout_fields(dims, out, n) ? TSG_OK : TSG_E_SHAPE;
+}
+
 tsg_status gemm_ag_overlap(tsg_ctx* ctx, const void* a_local, const void* a_peers, void* a_full,
                            const void* b, void* c, int c_dtype, int M, int N, int K, int R,
                            int rank, const int* arrival_order, const tsg_opts* opts, int mode,

@@ -6,9 +6,10 @@
 // producer CTAs it depends on are done; shown on a 2-layer GEMM that stands
 // for the MLP.  Here both GEMMs run on one GPU:
 //
-//   GEMM1 (producer): H = bf16(GELU(X W1)), tiles visited 128-row block by
-//     row block.  After storing a tile, one lane arrives on the signal of each
-//     128-row block the tile covers ("TileLink: Generating Efficient
+//   GEMM1 (producer): H = bf16(GELU(X W1)), tiles visited row block by row
+//     block (by default; a grouped order is an option).  After storing a
+//     tile, one lane arrives on the signal of each 128-row block the tile
+//     covers ("TileLink: Generating Efficient
 //     Compute-Communication Overlapping Kernels using Tile-Centric Primitives",
 //     Table 3: a consumer tile is ready once all the producer tiles it depends
 //     on are done -- here the N1 / BN1 tiles of that row block).
@@ -93,8 +94,9 @@ struct Mlp2Args {
   uint32_t arrivals;
 };
 
-// Persistent: workgroup g computes tiles g, g + G, ... in row-block-major
-// order, so the first tiles need the first row blocks GEMM1 completes.
+// Persistent: workgroup g computes tiles g, g + G, ... of the tile order
+// (row-block-major by default, so the first tiles need the first row blocks
+// GEMM1 completes).
 template <class Cfg, bool DIRECT>
 __global__ void __launch_bounds__(Cfg::NT) mlp_gemm2_kernel(const Mlp2Args a) {
   __shared__ __attribute__((aligned(16))) char lds[DIRECT ? Cfg::LDS_DIRECT : Cfg::LDS_REGS];
@@ -131,9 +133,9 @@ __global__ void __launch_bounds__(Cfg::NT) mlp_gemm2_kernel(const Mlp2Args a) {
 
 // Both GEMMs in one persistent kernel (overlap mode on shared CUs).
 // Items are GEMM1 tiles (phase 1), then GEMM2 tiles (phase 2), each set in
-// grouped tile order and cut into 8 contiguous shares, one per XCD, so that
-// the tiles an XCD runs form a compact block of the tile grid whose operands
-// its L2 can reuse.  A workgroup reads its XCD (XCC_ID) and takes tickets
+// the op's tile order and cut into 8 contiguous shares, one per XCD (with the
+// grouped order the tiles an XCD runs form a compact block of the tile grid
+// whose operands its L2 can reuse).  A workgroup reads its XCD (XCC_ID) and takes tickets
 // from its XCD's phase-1 queue, then from the other XCDs' phase-1 queues,
 // and only then from the phase-2 queues, its own first.  A GEMM2 tile
 // acquires the signals of its row blocks before its K loop.  No item waits
@@ -334,7 +336,14 @@ tsg_status tsg_op_mlp2(tsg_ctx* ctx, const void* x, const void* w1, void* h, con
   const Opts o = resolve(opts, -1);
   const bool small = M < 1024 || N1 < 1024 || N2 < 1024;
   const int tile1 = o.tile ? o.tile : (small ? 3 : 5);  // 128 x 256 for GEMM1
-  const int tile2 = o.tile ? o.tile : (small ? 3 : (o.order == 5 ? 5 : 1));  // 256 x 256 for GEMM2
+  const int tile2 = o.tile ? o.tile : (small ? 3 : 1);  // 256 x 256 for GEMM2
+  if (o.order != 0 && o.order != 1) return fail(ctx, TSG_E_INVALID, "mlp2_pipelined: order must be 0 or 1");
+  // Tile order of both GEMMs: 0 = row-block-major (a GEMM2 tile needs whole
+  // row blocks of H, so GEMM1 finishes them one after another and GEMM2's
+  // first tiles read the first ones); 1 = groups of 8 tile rows walked
+  // column by column, which keeps an XCD's operands in its L2 when all
+  // tiles run at once.
+  const int group = o.order == 1 ? 8 : 1;
   const TileShape s1 = shape_of(tile1), s2 = shape_of(tile2);
   if (!s1.bm || !s2.bm) return fail(ctx, TSG_E_INVALID, "tile id %d is not available for mlp2_pipelined", o.tile);
 
@@ -358,7 +367,7 @@ tsg_status tsg_op_mlp2(tsg_ctx* ctx, const void* x, const void* w1, void* h, con
   a1.N1 = N1;
   a1.n_tiles_n = n_nt1;
   a1.n_tiles_m = n_mt1;
-  a1.group = 8;
+  a1.group = group;
   a1.arrivals = (uint32_t)n_nt1;
   a1.skip_mask = o.skip_mask;
   Mlp2Args a2;
@@ -373,7 +382,7 @@ tsg_status tsg_op_mlp2(tsg_ctx* ctx, const void* x, const void* w1, void* h, con
   a2.N2 = N2;
   a2.n_tiles_n = n_nt2;
   a2.n_tiles = n_mt2 * n_nt2;
-  a2.group = 8;
+  a2.group = group;
   a2.arrivals = (uint32_t)n_nt1;
   a2.l1_only = ((uintptr_t)h % 128 == 0 && ((int64_t)N1 * 2) % 128 == 0) ? 1 : 0;
   if (o.timeline) TSG_HIP(ctx, hipMemsetAsync(ctx->d_timeline_n, 0, sizeof(uint32_t), caller));

@@ -324,8 +324,7 @@ struct ProdArgs {
   uint64_t* sig_h;
   uint32_t* cnt_h;
   uint64_t* sig_ready;
-  uint32_t* queue;
-  uint32_t queue_base;
+  uint32_t* queue;        // ticket counter, then the exit counter (both zero between calls)
   SyncArgs sa;
   Timeline tl;
   int T, H, I;
@@ -533,7 +532,7 @@ __global__ void __launch_bounds__(kProdThreads) moe_producer_kernel(const ProdAr
   // finishes before thread 0 writes), and a combine unit ends with one.
   auto fetch = [&]() -> int {
     volatile int* s_item = (volatile int*)lds;
-    if (threadIdx.x == 0) *s_item = (int)(atomicAdd(a.queue, 1u) - a.queue_base);
+    if (threadIdx.x == 0) *s_item = (int)atomicAdd(a.queue, 1u);
     __syncthreads();
     const int v = __builtin_amdgcn_readfirstlane(*s_item);
     __syncthreads();
@@ -605,6 +604,13 @@ __global__ void __launch_bounds__(kProdThreads) moe_producer_kernel(const ProdAr
       }
     }
   }
+  // Every workgroup leaves after its failing ticket, so once the last one has
+  // left no claim of this call is outstanding: it resets both counters for
+  // the next call.  A launch that never ran leaves them at zero.
+  if (threadIdx.x == 0 && atomicAdd(a.queue + 1, 1u) == gridDim.x - 1) {
+    __hip_atomic_store(a.queue, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(a.queue + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 template <bool U, bool D>
@@ -617,6 +623,18 @@ void launch_prod(const ProdArgs& a, int grid, hipStream_t s) {
 size_t tsg_moe_workspace(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k) {
   if (T < 1 || H < 8 || I < 8 || E < 1 || E > kMaxExperts || k != 2) return 0;
   return layout(T, H, I, E, k).total;
+}
+
+bool tsg_moe_layout_fields(const int64_t* d, int64_t* out, int n) {
+  if (!d || !out || n < 0 || tsg_moe_workspace(d[0], d[1], d[2], d[3], d[4]) == 0) return false;
+  const Layout L = layout(d[0], d[1], d[2], d[3], d[4]);
+  const int64_t f[TSG_MOE_LAYOUT_N] = {(int64_t)L.meta,     (int64_t)L.offs,     (int64_t)L.poffs,
+                                       (int64_t)L.rb_expert, (int64_t)L.row_pair, (int64_t)L.row_token,
+                                       (int64_t)L.pair_row,  (int64_t)L.h,        (int64_t)L.y,
+                                       (int64_t)L.total,     L.rows_max,          L.n_rb_max,
+                                       (int64_t)BM};
+  for (int i = 0; i < n && i < TSG_MOE_LAYOUT_N; ++i) out[i] = f[i];
+  return true;
 }
 
 tsg_status tsg_op_moe(tsg_ctx* ctx, const void* x, const int32_t* topk_ids, const float* topk_w,
@@ -728,10 +746,6 @@ tsg_status tsg_op_moe(tsg_ctx* ctx, const void* x, const int32_t* topk_ids, cons
     return check_launch(ctx, "moe_place_kernel");
   };
   auto produce = [&](hipStream_t s, int nwg) -> tsg_status {
-    // every producer workgroup ends with one failing ticket: the queue moves
-    // by n_items + nwg per call, tracked here so no reset pass is needed
-    pa.queue_base = (uint32_t)ctx->queue_base[0];
-    ctx->queue_base[0] += (uint64_t)pa.n_items + (uint64_t)nwg;
     const bool du = H % (2 * CfgUp::BK) == 0, dd = I % (2 * CfgDn::BK) == 0;
     time_begin(ctx, 0, s);
     if (du && dd) launch_prod<true, true>(pa, nwg, s);

@@ -22,8 +22,7 @@ struct tsg_ctx {
   uint32_t* d_cnt = nullptr;   // arrival counters, one per signal word (zero between calls)
   size_t n_sig = 0;
   uint32_t* d_status = nullptr;  // sticky device error bits
-  uint32_t* d_queue = nullptr;   // work-queue tickets of persistent kernels
-  uint64_t queue_base[4] = {0, 0, 0, 0};
+  uint32_t* d_queue = nullptr;   // work-queue tickets of persistent kernels (zero between calls)
 
   uint64_t* d_timeline = nullptr;
   uint32_t* d_timeline_n = nullptr;
@@ -121,4 +120,5 @@ tsg_status tsg_op_moe(tsg_ctx*, const void*, const int32_t*, const float*, const
                       const void*, float*, int32_t*, int32_t*, void*, size_t, int, int, int, int,
                       int, const tsg_opts*, int, void*);
 size_t tsg_moe_workspace(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k);
+bool tsg_moe_layout_fields(const int64_t* dims, int64_t* out, int n);
 tsg_status tsg_probe_xcd(tsg_ctx* ctx);
