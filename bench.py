@@ -36,7 +36,6 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "overlapped TFLOP/s, % bf16 MFMA peak, speedup vs serialized copy+GEMM"
 XGMI_GBPS = 1071            # arrival pacing of the xGMI-paced AG line: 7 links x ~153 GB/s
-DMA_AUX_CUS = 32            # CUs left to the runtime's copies in the copy-engine AG line
 CSRC = os.path.join(ROOT, "tile_level_communication_signaled_amd", "csrc")
 TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -143,27 +142,95 @@ def summarize_counters(fetch_csv: str, write_csv: str, out_path: str = TRAFFIC) 
     return rec
 
 
-def _cpu_baseline(inp, M, N, K, R):
-    """The oracle as it stands, on this host's cores: full AG + GEMM in float64."""
-    import numpy as np
-    import oracle
-    from synth.gen import split_chunks
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 0) for i in threadpool_info()] + [1])
+        return max([i.get("num_threads", 0) for i in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
-    loc, peers = split_chunks(inp["a"], R, 0)
+        return os.cpu_count() or 1
+
+
+def _time_host(fn, budget_s: float, min_runs: int = 3):
+    """Median seconds of fn() over repeated runs: at least min_runs, and more
+    until about budget_s seconds have passed."""
+    import numpy as np
     times = []
-    t_end = time.perf_counter() + 10.0   # about ten seconds of host work, at least three runs
-    while len(times) < 3 or time.perf_counter() < t_end:
+    t_end = time.perf_counter() + budget_s
+    while len(times) < min_runs or time.perf_counter() < t_end:
         t0 = time.perf_counter()
-        oracle.ag_gemm(loc, peers, inp["b"], R, 0)
+        fn()
         times.append(time.perf_counter() - t0)
-    t = float(np.median(times))
-    return {"value": round(2.0 * M * N * K / t / 1e12, 4), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"the full workload (AllGather + {M}x{N}x{K} GEMM, float64 numpy on the host), "
-                      f"median of {len(times)} runs of {t:.3f} s"}
+    return float(np.median(times)), len(times)
+
+
+def _cpu_baselines(ag_host, budget_s: float = 8.0) -> dict:
+    """The oracle as it stands, timed on this host's cores for every workload
+    (float64 numpy, the BLAS's own threads), in the unit of each path's GPU
+    line; the tiny AllGather+GEMM also on one thread.  Bounded samples: every
+    entry runs the whole workload, repeated for about its time budget."""
+    import oracle
+    from synth import CONFIGS, ag_inputs, mlp2_inputs, moe_inputs, rs_inputs
+    from synth.gen import split_chunks
+    cores, model = _blas_threads(), _cpu_model()
+    out = {}
+
+    def entry(flops, t, runs, what, threads=cores):
+        return {"value": round(flops / t / 1e12, 4), "unit": "TFLOP/s", "ms": round(t * 1e3, 3),
+                "cores": int(threads), "cpu": model, "kind": "oracle",
+                "sample": f"{what}, float64 numpy on the host, median of {runs} runs"}
+
+    c1 = CONFIGS["tiny_ag"]
+    M, N, K, R = c1["M"], c1["N"], c1["K"], c1["R"]
+    inp = ag_inputs(M, K, N, R, rank=0, seed=c1["seed"], dist="uniform")
+    loc, peers = split_chunks(inp["a"], R, 0)
+    f1 = lambda: oracle.ag_gemm(loc, peers, inp["b"], R, 0)
+    t, n = _time_host(f1, 2.0)
+    out["tiny_ag"] = entry(2.0 * M * N * K, t, n, f"AllGather + {M}x{N}x{K} GEMM, R={R}")
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            t, n = _time_host(f1, 2.0)
+        out["tiny_ag_1thread"] = entry(2.0 * M * N * K, t, n, f"AllGather + {M}x{N}x{K} GEMM, R={R}", 1)
+    except Exception:  # pragma: no cover
+        pass
+
+    c2 = CONFIGS["llama_ag"]
+    M, N, K, R = c2["M"], c2["N"], c2["K"], c2["R"]
+    loc, peers = split_chunks(ag_host["a"], R, 0)
+    t, n = _time_host(lambda: oracle.ag_gemm(loc, peers, ag_host["b"], R, 0), budget_s)
+    out["llama_ag"] = entry(2.0 * M * N * K, t, n, f"the full workload (AllGather + {M}x{N}x{K} GEMM, R={R})")
+
+    c3 = CONFIGS["gemm_rs"]
+    M, N, K, R = c3["M"], c3["N"], c3["K"], c3["R"]
+    inp = rs_inputs(M, K, N, R, rank=0, seed=c3["seed"])
+    t, n = _time_host(lambda: oracle.gemm_rs(inp["x"], inp["w"], inp["peer_partials"], R, 0), budget_s / 2, 2)
+    out["gemm_rs"] = entry(2.0 * M * N * K, t, n, f"the full workload ({M}x{N}x{K} GEMM + reduce of {R} chunks)")
+
+    c4 = CONFIGS["mlp2"]
+    M, K1, N1, N2 = c4["M"], c4["K1"], c4["N1"], c4["N2"]
+    inp = mlp2_inputs(M, K1, N1, N2, seed=c4["seed"])
+    t, n = _time_host(lambda: oracle.mlp2(inp["x"], inp["w1"], inp["w2"]), budget_s / 2, 2)
+    out["mlp2"] = entry(2.0 * M * N1 * K1 + 2.0 * M * N2 * N1, t, n,
+                        f"the full workload ({M}x{K1} @ {K1}x{N1}, GELU, @ {N1}x{N2})")
+
+    c5 = CONFIGS["moe"]
+    T, Hh, I, E, k = c5["T"], c5["H"], c5["I"], c5["E"], c5["k"]
+    inp = moe_inputs(T, Hh, I, E, k=k, seed=c5["seed"], zipf=c5["zipf"])
+    t, n = _time_host(lambda: oracle.moe_expert_combine(inp["x"], inp["topk_ids"], inp["topk_w"], inp["w_up"],
+                                                        inp["w_down"]), budget_s / 2, 2)
+    out["moe"] = entry(4.0 * T * k * Hh * I, t, n,
+                       f"the full workload ({T} tokens, top-{k} of {E} experts {Hh}x{I} / {I}x{Hh}, combine)")
+    return out
 
 
 class Timer:
@@ -199,6 +266,27 @@ class Timer:
                 got[m].append((time.perf_counter() - t0) / n * 1e3)
         self._check()
         return {m: sorted(v)[len(v) // 2] for m, v in got.items()}
+
+    def per_call(self, modes, n, warmup=3):
+        """Per-call device time of each mode from events recorded on the
+        caller's stream around each call (fork to join), n calls back to
+        back: {mode: (p10, p50, p90) in ms}."""
+        torch = self.torch
+        out = {}
+        for m in modes:
+            for i in range(warmup):
+                self.fn(i, m)
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+            torch.cuda.synchronize()
+            for i, (a, b) in enumerate(evs):
+                a.record()
+                self.fn(i, m)
+                b.record()
+            torch.cuda.synchronize()
+            v = sorted(a.elapsed_time(b) for a, b in evs)
+            out[m] = (v[len(v) // 10], v[len(v) // 2], v[(9 * len(v)) // 10])
+        self._check()
+        return out
 
     def kernels(self, mode, n, which, spread=None):
         """Median kernel ms (library events) over n calls, per kernel slot;
@@ -236,6 +324,27 @@ def _summary(flops, hbm_bytes, t):
     }
     if cm:
         out["overlap_ratio"] = round((co + cm - ov) / cm, 4)
+    return out
+
+
+def _path_line(tsg, timer, flops, nbytes, modes, n):
+    """One path's line: back-to-back ms per call of each mode (median of
+    interleaved rounds), the rates and ratios of _summary, and the per-call
+    p10 / p50 / p90 of each mode."""
+    names = {tsg.OVERLAP: "overlap", tsg.SERIAL: "serial", tsg.COMPUTE_ONLY: "compute_only",
+             tsg.COMM_ONLY: "comm_only"}
+    tm = timer.modes(modes, n)
+    pc = timer.per_call(modes, max(n, 20))
+    t = {"overlap": tm.get(tsg.OVERLAP), "serial": tm.get(tsg.SERIAL),
+         "compute_only": tm.get(tsg.COMPUTE_ONLY), "comm_only": tm.get(tsg.COMM_ONLY)}
+    if t["serial"] is None or t["compute_only"] is None:
+        ov = t["overlap"]
+        out = {"ms": {"overlap": round(ov, 5)}, "tflops": round(flops / (ov * 1e-3) / 1e12, 2),
+               "pct_bf16_peak": round(100.0 * flops / (ov * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+               "hbm_GBps_algorithmic": round(nbytes / (ov * 1e-3) / 1e9, 1)}
+    else:
+        out = _summary(flops, nbytes, t)
+    out["ms_per_call_p10_p50_p90"] = {names[m]: [round(x, 5) for x in pc[m]] for m in modes}
     return out
 
 
@@ -324,6 +433,32 @@ def _other_paths(torch, tsg, ctx):
     return out
 
 
+def _tiny_line(torch, tsg, ctx, n):
+    """The tiny AllGather + GEMM (4 ranks, 256x128x256, fp32 out): a latency
+    line in microseconds per call for each mode, with per-call p10 / p50 /
+    p90; TFLOP/s is nominal at this size."""
+    import numpy as np
+    from synth import CONFIGS, ag_inputs
+    from synth.gen import split_chunks
+    c = CONFIGS["tiny_ag"]
+    M, N, K, R = c["M"], c["N"], c["K"], c["R"]
+    inp = ag_inputs(M, K, N, R, rank=0, seed=c["seed"], dist="uniform")
+    loc, peers = split_chunks(inp["a"], R, 0)
+    dl = torch.from_numpy(loc.view(np.int16)).cuda()
+    dp = torch.from_numpy(peers.view(np.int16)).cuda()
+    db = torch.from_numpy(inp["b"].view(np.int16)).cuda()
+    full = torch.empty((M, K), dtype=torch.int16, device="cuda")
+    cc = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    fn = lambda i, mode, o=None: tsg.gemm_ag_overlap(ctx, dl, dp, full, db, cc, tsg.F32, M, N, K, R, 0, mode=mode)
+    line = _path_line(tsg, Timer(torch, tsg, ctx, fn), 2.0 * M * N * K, 2 * (M * K + K * N) + 4 * M * N,
+                      (tsg.OVERLAP, tsg.SERIAL, tsg.COMPUTE_ONLY, tsg.COMM_ONLY), max(n, 50))
+    line["us"] = {k: (None if v is None else round(v * 1e3, 2)) for k, v in line.pop("ms").items()}
+    line["us_per_call_p10_p50_p90"] = {k: [round(x * 1e3, 2) for x in v]
+                                       for k, v in line.pop("ms_per_call_p10_p50_p90").items()}
+    line["workload"] = f"AllGather+GEMM, A {M}x{K} bf16 in {R} row chunks, B {K}x{N} bf16, fp32 out"
+    return line
+
+
 # Timeline record kinds (tsg_timeline): producer / consumer units of each path.
 TL_KINDS = {"ag_gemm": ((1, "copy units"), (2, "GEMM tiles")),
             "gemm_rs": ((3, "GEMM tiles"), (4, "reduce units")),
@@ -406,7 +541,7 @@ def main():
 
     if args.trace_path:
         if args.trace_path == "ag_copy_engine":
-            dma = tsg.Opts(aux_cus=DMA_AUX_CUS, tile=args.tile, copy_engine=1)
+            dma = tsg.Opts(aux_cus=args.aux_cus, tile=args.tile, copy_engine=1)
             fn, flops = (lambda i, mode, o=None: ag_fn(i, mode, dma)), ag_flops
         else:
             fn, flops, _nbytes, _modes = _other_paths(torch, tsg, ctx)[args.trace_path]
@@ -472,49 +607,56 @@ def main():
 
     timer = Timer(torch, tsg, ctx, ag_fn)
     n = max(5, min(args.steps, 30))
-    tm = timer.modes((tsg.OVERLAP, tsg.SERIAL, tsg.COMPUTE_ONLY, tsg.COMM_ONLY), n)
+    ALL = (tsg.OVERLAP, tsg.SERIAL, tsg.COMPUTE_ONLY, tsg.COMM_ONLY)
+    ag = _path_line(tsg, timer, ag_flops, ag_gemm_bytes + ag_copy_bytes, ALL, n)
     k_spread = {}
     k_ov = timer.kernels(tsg.OVERLAP, max(n, 50), (0, 1), k_spread)
     k_co = timer.kernels(tsg.COMPUTE_ONLY, n, (0,))
     k_cm = timer.kernels(tsg.COMM_ONLY, n, (1,))
-    ag = _summary(ag_flops, ag_gemm_bytes + ag_copy_bytes,
-                  {"overlap": tm[tsg.OVERLAP], "serial": tm[tsg.SERIAL],
-                   "compute_only": tm[tsg.COMPUTE_ONLY], "comm_only": tm[tsg.COMM_ONLY]})
     ag["kernel_ms_p10_p90"] = {"gemm_in_overlap": [round(x, 5) for x in k_spread[0]],
                                "copy_in_overlap": [round(x, 5) for x in k_spread[1]]}
     ag["kernel_ms"] = {"gemm_in_overlap": round(k_ov[0], 5), "copy_in_overlap": round(k_ov[1], 5),
                        "gemm_alone": round(k_co[0], 5), "copy_alone": round(k_cm[1], 5)}
     paths = {"ag_gemm": ag}
     if args.paths == "all":
+        # the tiny AllGather + GEMM: a latency line, in microseconds
+        paths["tiny_ag"] = _tiny_line(torch, tsg, ctx, n)
         # the same AllGather + GEMM with the arrival paced at seven peers'
         # xGMI links (about 153 GB/s each), as a multi-GPU rank would see it
         paced = tsg.Opts(aux_cus=args.aux_cus, tile=args.tile, arrival_gbps=XGMI_GBPS)
-        tp = Timer(torch, tsg, ctx, lambda i, mode, o=None: ag_fn(i, mode, paced)).modes(
-            (tsg.OVERLAP, tsg.SERIAL, tsg.COMPUTE_ONLY, tsg.COMM_ONLY), n)
-        paths["ag_gemm_xgmi_paced"] = _summary(
-            ag_flops, ag_gemm_bytes + ag_copy_bytes,
-            {"overlap": tp[tsg.OVERLAP], "serial": tp[tsg.SERIAL], "compute_only": tp[tsg.COMPUTE_ONLY],
-             "comm_only": tp[tsg.COMM_ONLY]})
+        paths["ag_gemm_xgmi_paced"] = _path_line(
+            tsg, Timer(torch, tsg, ctx, lambda i, mode, o=None: ag_fn(i, mode, paced)), ag_flops,
+            ag_gemm_bytes + ag_copy_bytes, ALL, n)
         paths["ag_gemm_xgmi_paced"]["arrival_gbps"] = XGMI_GBPS
         # the same AllGather + GEMM with the chunks moved by the DMA copy
-        # engines (one copy and one signal copy per chunk, one stream); the
-        # overlap runs on a CU split, which the runtime's kernel-run small
-        # copies need
-        dma = tsg.Opts(aux_cus=DMA_AUX_CUS, tile=args.tile, copy_engine=1)
-        td = Timer(torch, tsg, ctx, lambda i, mode, o=None: ag_fn(i, mode, dma)).modes(
-            (tsg.OVERLAP, tsg.SERIAL, tsg.COMPUTE_ONLY, tsg.COMM_ONLY), n)
-        paths["ag_gemm_copy_engine"] = _summary(
-            ag_flops, ag_gemm_bytes + ag_copy_bytes,
-            {"overlap": td[tsg.OVERLAP], "serial": td[tsg.SERIAL], "compute_only": td[tsg.COMPUTE_ONLY],
-             "comm_only": td[tsg.COMM_ONLY]})
-        paths["ag_gemm_copy_engine"]["aux_cus"] = DMA_AUX_CUS
+        # engines (one stream per peer chunk)
+        dma = tsg.Opts(aux_cus=args.aux_cus, tile=args.tile, copy_engine=1)
+        paths["ag_gemm_copy_engine"] = _path_line(
+            tsg, Timer(torch, tsg, ctx, lambda i, mode, o=None: ag_fn(i, mode, dma)), ag_flops,
+            ag_gemm_bytes + ag_copy_bytes, ALL, n)
 
     if args.paths == "all":
-        for name, (fn, flops, nbytes, modes) in _other_paths(torch, tsg, ctx).items():
-            tm = Timer(torch, tsg, ctx, fn).modes(modes, n)
-            paths[name] = _summary(flops, nbytes,
-                                   {"overlap": tm[tsg.OVERLAP], "serial": tm[tsg.SERIAL],
-                                    "compute_only": tm[tsg.COMPUTE_ONLY], "comm_only": tm.get(tsg.COMM_ONLY)})
+        other = _other_paths(torch, tsg, ctx)
+        for name, (fn, flops, nbytes, modes) in other.items():
+            paths[name] = _path_line(tsg, Timer(torch, tsg, ctx, fn), flops, nbytes, modes, n)
+        # The CU splits the configurations name, beside the shared-CU
+        # defaults: the two-GEMM MLP with GEMM1 / GEMM2 on 128/128 ... 224/32
+        # CUs, and the MoE combine as a persistent consumer on 16 CUs.
+        fn, flops, nbytes, _m = other["mlp2"]
+        sweep = {}
+        for q in (128, 96, 64, 32):
+            o = tsg.Opts(aux_cus=q)
+            sweep[f"{256 - q}/{q}"] = _path_line(
+                tsg, Timer(torch, tsg, ctx, lambda i, mode, o_=None, o=o: fn(i, mode, o)), flops, nbytes,
+                (tsg.OVERLAP,), n)
+        og = tsg.Opts(order=1)
+        sweep["shared, grouped order"] = _path_line(
+            tsg, Timer(torch, tsg, ctx, lambda i, mode, o_=None: fn(i, mode, og)), flops, nbytes, (tsg.OVERLAP,), n)
+        paths["mlp2_cu_splits"] = sweep
+        fn, flops, nbytes, _m = other["moe"]
+        o16 = tsg.Opts(aux_cus=16)
+        paths["moe_combine_16cu"] = _path_line(
+            tsg, Timer(torch, tsg, ctx, lambda i, mode, o_=None: fn(i, mode, o16)), flops, nbytes, (tsg.OVERLAP,), n)
 
     tflops = ag_flops / (ms_step * 1e-3) / 1e12
     achieved = ag_flops / (k_ov[0] * 1e-3) / 1e12
@@ -546,7 +688,11 @@ def main():
         "paths": paths,
     }
     if not args.no_cpu:
-        out["cpu_baseline"] = _cpu_baseline(ag_host, M, N, K, R)
+        cb = _cpu_baselines(ag_host)
+        head = dict(cb["llama_ag"])
+        head.pop("ms", None)
+        out["cpu_baseline"] = head
+        out["cpu_baselines"] = cb
     print(json.dumps(out), flush=True)
     ctx.close()
 

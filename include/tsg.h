@@ -105,9 +105,11 @@ typedef struct tsg_opts {
   int order;
   /* Bound of every device-side signal wait, in milliseconds (0 = 2000). */
   uint32_t timeout_ms;
-  /* Test hook: bit c set = the signal of chunk / row-block / tile group c
-   * is never published in this call, so its consumers time out (the call
-   * then reports TSG_E_TIMEOUT from tsg_check).  0 in normal use. */
+  /* Test hook: bit c set = the signals of AG channel c (the chunk when
+   * channels = 1), RS chunk c, MLP or MoE row block c (mod 32) are never
+   * published in this call, so its consumers
+   * time out (the call then reports TSG_E_TIMEOUT from tsg_check).  0 in
+   * normal use. */
   uint32_t debug_skip_mask;
   /* Nonzero: record per-tile device timestamps into the context's timeline
    * buffer (tsg_timeline). */
@@ -146,18 +148,28 @@ typedef struct tsg_opts {
   int arrival_gbps;
   /* AG+GEMM: 1 = move the gathered data with the DMA copy engines instead of
    * the CU copy kernel ([TD] section 3.6: intra-node AllGather on AMD with
-   * copy engines, whose signals are sent as a separate transfer).  Each
-   * chunk is one hipMemcpyAsync with hipMemcpyDeviceToDeviceNoCU on the op's
-   * side stream, in arrival order, followed by 8-byte copies that set the
-   * signals of the chunk's column slabs (comm_tile defaults to 2048 columns
-   * here; every slab of a chunk is released after the chunk's one copy, as
-   * with the one signal per chunk of [TD] section 3.2).  The GEMM pulls
-   * nothing.  The runtime still moves some of these
-   * copies (the 8-byte signal copies among them) with a kernel, so overlap
-   * mode needs a CU split (aux_cus >= 8): on shared CUs it returns
-   * TSG_E_UNSUPPORTED.  0 = the CU copy kernel (default).  Other values, or
+   * copy engines, transfers issued on several streams at once, each signal
+   * sent as a separate data transfer).  Each chunk gets a stream of its own;
+   * on it every channel of the chunk is one hipMemcpyAsync with
+   * hipMemcpyDeviceToDeviceNoCU, followed by an 8-byte NoCU copy of the
+   * call's signal value (kept in an allocation of its own, so that the
+   * runtime hands it to a DMA engine, not to a kernel) into the channel's
+   * signal word.  comm_tile does not apply (one slab: whole rows), the GEMM
+   * pulls nothing, and no CU runs any part of the transfer, so overlap runs
+   * on shared CUs.  0 = the CU copy kernel (default).  Other values, or
    * together with arrival_gbps: TSG_E_INVALID. */
   int copy_engine;
+  /* AG+GEMM: channels per rank C ([TL] section 4.1, static mapping:
+   * M_per_channel = M / (R C) rows, channel of row r = floor(r /
+   * M_per_channel)).  Every (channel, column slab) has its own signal, and
+   * a GEMM tile waits for the signals of every channel its rows span.  The
+   * copy moves channel 0 of every chunk (in arrival order), then channel 1,
+   * and so on, so that each step brings a sub-chunk from every peer ([TD]
+   * section 3.7, Figure 8).  debug_skip_mask bit g then names global
+   * channel g = chunk * C + channel.  0 = 1.  C must divide M / R, leave at
+   * least 8 rows per channel (else TSG_E_SHAPE) and be at most 64
+   * (else TSG_E_INVALID). */
+  int channels;
 } tsg_opts;
 
 /* ------------------------------------------------------------------ ctx */

@@ -46,10 +46,11 @@ def test_binding_exports_match_header():
 def test_opts_struct_layout_matches_header(tmp_path):
     src = tmp_path / "sz.c"
     src.write_text('#include "tsg.h"\n#include <stdio.h>\n#include <stddef.h>\n'
-                   'int main(void){printf("%zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(tsg_opts), '
+                   'int main(void){printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(tsg_opts), '
                    'offsetof(tsg_opts, timeout_ms), offsetof(tsg_opts, timeline), offsetof(tsg_opts, comm_tile), '
                    'offsetof(tsg_opts, pull_units), offsetof(tsg_opts, stage_dtype), '
-                   'offsetof(tsg_opts, arrival_gbps), offsetof(tsg_opts, copy_engine));return 0;}\n')
+                   'offsetof(tsg_opts, arrival_gbps), offsetof(tsg_opts, copy_engine), '
+                   'offsetof(tsg_opts, channels));return 0;}\n')
     exe = tmp_path / "sz"
     subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
     got = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()
@@ -60,7 +61,7 @@ def test_opts_struct_layout_matches_header(tmp_path):
     assert [int(v) for v in got] == [ctypes.sizeof(tsg.Opts), tsg.Opts.timeout_ms.offset, tsg.Opts.timeline.offset,
                                       tsg.Opts.comm_tile.offset, tsg.Opts.pull_units.offset,
                                       tsg.Opts.stage_dtype.offset, tsg.Opts.arrival_gbps.offset,
-                                      tsg.Opts.copy_engine.offset]
+                                      tsg.Opts.copy_engine.offset, tsg.Opts.channels.offset]
 
 
 @pytest.mark.skipif(not os.path.exists(LIB), reason="library not built")

@@ -140,28 +140,100 @@ def test_ag_tile9_needs_k_multiple_of_128(env):
 
 
 def test_ag_copy_engine(env):
-    # the gathered data moved by the DMA copy engines, one copy per chunk and
-    # its slabs' signals set by following 8-byte copies: the same results in
-    # serial and comm-only mode and in overlap on a CU split, for slabs of 128
-    # columns and the default; overlap on shared CUs is refused before
-    # anything is launched
+    # the gathered data moved by the DMA copy engines, one stream per chunk,
+    # each channel followed by an 8-byte copy of its signal: bit-identical
+    # results in overlap (shared CUs and a CU split), serial and comm-only
+    # mode, for one and two channels per rank, every rank
     torch, tsg, ctx = env
     M, N, K, R = 600, 232, 384, 3
     inp = ag_inputs(M, K, N, R, seed=11)
     ref, scale = _ref(inp)
+    first = None
     for rank in range(R):
         case = AgCase(env, inp, M, N, K, R, rank, True)
-        for mode, aux in ((tsg.OVERLAP, 16), (tsg.SERIAL, -1), (tsg.SERIAL, 16), (tsg.COMM_ONLY, -1)):
-            for ct in (128, 0):
-                full, c = case.run(mode=mode, opts={"copy_engine": 1, "aux_cus": aux, "comm_tile": ct})
-                assert np.array_equal(full, inp["a"]), (rank, mode, aux, ct)
+        for mode, aux in ((tsg.OVERLAP, -1), (tsg.OVERLAP, 16), (tsg.SERIAL, -1), (tsg.COMM_ONLY, -1)):
+            for ch in (1, 2):
+                full, c = case.run(mode=mode, opts={"copy_engine": 1, "aux_cus": aux, "channels": ch})
+                assert np.array_equal(full, inp["a"]), (rank, mode, aux, ch)
                 if mode != tsg.COMM_ONLY:
-                    assert err_ratio(c, ref, scale, bf16_out=True) <= 1.0, (rank, mode, aux, ct)
-    for bad, want in (({"copy_engine": 1, "arrival_gbps": 2}, tsg.E_INVALID), ({"copy_engine": 2}, tsg.E_INVALID),
-                      ({"copy_engine": 1}, tsg.E_UNSUPPORTED)):
+                    assert err_ratio(c, ref, scale, bf16_out=True) <= 1.0, (rank, mode, aux, ch)
+                    first = c if first is None else first
+                    assert np.array_equal(c, first), (rank, mode, aux, ch)
+    for bad, want in (({"copy_engine": 1, "arrival_gbps": 2}, tsg.E_INVALID), ({"copy_engine": 2}, tsg.E_INVALID)):
         st = tsg.gemm_ag_overlap(ctx, case.loc, case.peers, case.full, case.b, case.c, tsg.BF16, M, N, K, R, 0,
                                  opts=bad, raise_on_error=False)
         assert st == want, bad
+
+
+@pytest.mark.parametrize("tile", [3, 1, 6])
+def test_ag_channels_bit_exact(env, tile):
+    # C channels per rank ([TL] section 4.1): 200-row chunks cut into 2, 4
+    # and 8 channels (100, 50, 25 rows), so 128- and 256-row tiles span
+    # several channels whose edges fall inside tiles; every rank, overlap and
+    # serial, CU copy and copy engines: the same bits as one channel
+    torch, tsg, ctx = env
+    M, N, K, R = 600, 256, 256, 3
+    inp = ag_inputs(M, K, N, R, seed=21)
+    ref, scale = _ref(inp)
+    for rank in range(R):
+        case = AgCase(env, inp, M, N, K, R, rank, False)
+        _, base = case.run(opts={"tile": tile})
+        assert err_ratio(base, ref, scale) <= 1.0
+        for C in (2, 4, 8):
+            for mode in (tsg.OVERLAP, tsg.SERIAL):
+                for ce in (0, 1):
+                    opts = {"tile": tile, "channels": C, "copy_engine": ce, "comm_tile": 0 if ce else 64}
+                    full, c = case.run(mode=mode, opts=opts)
+                    assert np.array_equal(full, inp["a"]), (rank, C, mode, ce)
+                    assert np.array_equal(c, base), (rank, C, mode, ce)
+
+
+def test_ag_channels_rejected(env):
+    torch, tsg, ctx = env
+    M, N, K, R = 600, 64, 128, 3
+    case = AgCase(env, ag_inputs(M, K, N, R, seed=22), M, N, K, R, 0, False)
+    for C, want in ((3, tsg.E_INVALID), (65, tsg.E_INVALID), (-1, tsg.E_INVALID), (40, tsg.E_SHAPE)):
+        st = tsg.gemm_ag_overlap(ctx, case.loc, case.peers, case.full, case.b, case.c, tsg.F32, M, N, K, R, 0,
+                                 opts={"channels": C}, raise_on_error=False)
+        assert st == want, C
+
+
+@pytest.mark.parametrize("copy_engine", [0, 1])
+def test_ag_channel_mapping_matches_static_map(env, copy_engine):
+    # The signals a GEMM tile waits for are those of the channels its rows
+    # belong to under TileLink's static mapping (oracle.static_map_ag, pinned
+    # by tests/golden/static_mapping.txt).  For each global channel g the
+    # signal of g alone is withheld (20 ms bound); the device timeline then
+    # shows which tiles waited out the bound: exactly the non-local tiles
+    # whose rows map to channel g.  M 384, R 4, C 2: 48-row channels, 64-row
+    # tiles that straddle channel and chunk edges.
+    torch, tsg, ctx = env
+    M, N, K, R, C, rank = 384, 64, 128, 4, 2, 1
+    inp = ag_inputs(M, K, N, R, seed=23)
+    case = AgCase(env, inp, M, N, K, R, rank, False)
+    BM = 64
+    n_mt = M // BM
+    spans = []
+    for mt in range(n_mt):
+        rows = range(mt * BM, (mt + 1) * BM)
+        maps = [oracle.static_map_ag(r, 1, M, R, C) for r in rows]
+        local = all(m[2] == rank for m in maps)
+        spans.append(set() if local else {m[3] for m in maps})
+    # one plain call first: the first copy-engine call after the set of copy
+    # streams has grown can take milliseconds longer (runtime engine set-up)
+    case.run(opts={"channels": C, "tile": 6, "copy_engine": copy_engine})
+    for g in range(R * C):
+        want = {mt for mt in range(n_mt) if g in spans[mt]}
+        opts = {"channels": C, "tile": 6, "copy_engine": copy_engine, "debug_skip_mask": 1 << g,
+                "timeout_ms": 20, "timeline": 1, "comm_tile": 0 if copy_engine else 128}
+        case.run(opts=opts, expect=tsg.E_TIMEOUT if want else tsg.OK)
+        recs = [r for r in ctx.timeline() if (r[0] >> 56) == 2]
+        assert len(recs) == n_mt
+        waited = {(r[0] & 0xFFFFFFFF) >> 16 for r in recs if r[2] - r[1] > 1_000_000}   # > 10 ms at 100 MHz
+        assert waited == want, (g, waited, want)
+    full, c = case.run(opts={"channels": C, "tile": 6, "copy_engine": copy_engine})
+    ref, scale = _ref(inp)
+    assert np.array_equal(full, inp["a"]) and err_ratio(c, ref, scale) <= 1.0
 
 
 def test_ag_paced_arrival(env):

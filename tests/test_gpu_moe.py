@@ -282,11 +282,13 @@ def test_moe_full_size_parity_modes_splits(env):
     inp = moe_inputs(cfg["T"], cfg["H"], cfg["I"], cfg["E"], k=cfg["k"], seed=cfg["seed"], zipf=cfg["zipf"])
     case = MoeCase(env, inp)
     out, counts, sorted_ids = case.run()
-    r, _, _ = _check(case, out, counts, sorted_ids, label="overlap, shared CUs")
-    assert r <= 1.0
+    r, _, r_plain = _check(case, out, counts, sorted_ids, label="overlap, shared CUs")
+    # with fp32 staging the output also meets the plain per-element GEMM
+    # bound of the down projection, with no allowance for h differences
+    assert r <= 1.0 and r_plain <= 1.0
     out16, c16, s16 = case.run(opts={"aux_cus": 16})
-    r16, _, _ = _check(case, out16, c16, s16, label="overlap, 16-CU combine consumer")
-    assert r16 <= 1.0
+    r16, _, r16_plain = _check(case, out16, c16, s16, label="overlap, 16-CU combine consumer")
+    assert r16 <= 1.0 and r16_plain <= 1.0
     assert np.array_equal(out16, out)
     out2, c2, s2 = case.run(mode=tsg.SERIAL)
     assert np.array_equal(out2, out) and np.array_equal(c2, counts) and np.array_equal(s2, sorted_ids)

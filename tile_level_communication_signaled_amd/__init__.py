@@ -62,6 +62,7 @@ class Opts(ctypes.Structure):
         ("stage_dtype", ctypes.c_int),
         ("arrival_gbps", ctypes.c_int),
         ("copy_engine", ctypes.c_int),
+        ("channels", ctypes.c_int),
     ]
 
 
@@ -163,10 +164,11 @@ class Context:
             self._h = None
         _LIVE.discard(self)
 
-    def __del__(self):
+    def __del__(self, _finalizing=sys.is_finalizing):
         # During interpreter shutdown the atexit hook has already closed every
-        # context; a collection this late must not call into the runtime.
-        if sys.is_finalizing():
+        # context; a collection this late must not call into the runtime (nor
+        # rely on module globals, which may already be cleared).
+        if _finalizing():
             return
         try:
             self.close()

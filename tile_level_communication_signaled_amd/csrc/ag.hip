@@ -23,9 +23,20 @@
 // of every chunk its rows span, and then, just before it issues the loads of
 // the first K step of slab s, for slab s.  The signal of slab s + 1 is read
 // as soon as slab s has been passed, so when the copy runs ahead the wait
-// costs no round trip.  The chunk a row belongs to is the static rank mapping
-// of the TileLink page, section 4.1 (rank = floor(row / M_per_rank)), with
-// one channel per rank.
+// costs no round trip.  The signal a row belongs to is the static mapping of
+// the TileLink page, section 4.1: each rank's chunk is cut into C channels of
+// M / (R C) rows, and row r belongs to channel floor(r / M_per_channel) of
+// rank floor(r / M_per_rank).  Each (channel, slab) has its own signal.  The
+// copy moves, for each slab, channel 0 of every chunk in arrival order, then
+// channel 1, and so on: sub-chunks arrive from all peers at each step (the
+// Triton-distributed page, section 3.7, the full-mesh swizzle of Figure 8).
+//
+// Copy-engine arrival (opts.copy_engine): the same signals are set by the DMA
+// engines instead of a kernel (the Triton-distributed page, section 3.6: AMD
+// intra-node AllGather with copy engines on several streams at once, the
+// signal sent as a separate data transfer).  One stream per chunk copies the
+// chunk channel by channel, each channel followed by an 8-byte copy of the
+// call's signal value into that channel's signal word.
 #include "tsg_gemm.hpp"
 #include "tsg_internal.hpp"
 
@@ -39,7 +50,7 @@ constexpr size_t kSigBase = size_t(1) << 18;  // AG slab signals in the context'
 constexpr size_t kSigCap = size_t(1) << 18;   // slots up to the next op's region
 constexpr int kQueueSlot = 40;                // copy work queue in the context's ticket words
 constexpr size_t kPaceSlot = 8;               // arrival-pacing start time in the context's pool
-constexpr size_t kDmaSigSlot = 9;             // slab signal value the copy engines copy in
+constexpr int kMaxChannels = 64;               // channels per rank
 
 struct ChunkOrder {
   int8_t chunk[kMaxRanks];  // chunk copied at arrival position p (p = 0: local)
@@ -59,11 +70,12 @@ struct CopyArgs {
   ChunkOrder ord;
   int64_t k8;              // vectors per row (K / 8)
   int chunk_rows, R, rank;
+  int C, ch_rows;          // channels per chunk, rows per channel
   int n_slab;              // slabs per chunk
   int vpr_log2;            // log2(vectors per slab row), <= 8: slab width W = 8 << vpr_log2
-  // Pieces per chunk of slab s: np[s] for s < kHead, np[kHead] for the rest;
-  // the units of slab s < kHead start at ustart[s], those of the rest at
-  // ustart[kHead].
+  // Pieces per channel of slab s: np[s] for s < kHead, np[kHead] for the
+  // rest; the units of slab s < kHead start at ustart[s], those of the rest
+  // at ustart[kHead].
   int np[kHead + 1];
   int ustart[kHead + 1];
   int n_units;
@@ -99,14 +111,16 @@ __device__ __forceinline__ uint64_t pace_base(const CopyArgs& a) {
   }
 }
 
-// Work unit u -> (slab s, arrival position p, piece j), slab-major.  One unit
-// copies piece j (np[s] pieces of about equal rows) of slab s of chunk
-// ord[p], then arrives on that slab's signal.  The first slabs are cut into
+// Work unit u -> (slab s, channel ch, arrival position p, piece j), in that
+// order of significance: slab-major, then channel 0 of every chunk in
+// arrival order, then channel 1, and so on.  One unit copies piece j (np[s]
+// pieces of about equal rows) of channel ch of slab s of chunk ord[p], then
+// arrives on that (channel, slab) signal.  The first slabs are cut into
 // more pieces so that many workgroups share them: every GEMM tile needs
 // slab 0 before it can start, slab 1 soon after, and so on, while later
-// slabs have time to arrive in larger pieces, which need fewer store drains and arrivals.
-// Moves unit u and arrives on its slab's signal.  Called by every thread of
-// a workgroup of NT threads with the same u.
+// slabs have time to arrive in larger pieces, which need fewer store drains
+// and arrivals.  Called by every thread of a workgroup of NT threads with
+// the same u.
 template <int NT>
 __device__ __forceinline__ void copy_unit(const CopyArgs& a, int u) {
   constexpr int U = 8;  // 8-byte words in flight per thread
@@ -116,7 +130,7 @@ __device__ __forceinline__ void copy_unit(const CopyArgs& a, int u) {
   if (u >= a.ustart[kHead]) {
     npc = a.np[kHead];
     const int v = u - a.ustart[kHead];
-    const int per = a.R * npc;
+    const int per = a.R * a.C * npc;
     s = kHead + v / per;
     rem = v - (s - kHead) * per;
   } else {
@@ -125,12 +139,14 @@ __device__ __forceinline__ void copy_unit(const CopyArgs& a, int u) {
     npc = a.np[s];
     rem = u - a.ustart[s];
   }
-  const int p = rem / npc;
-  const int j = rem - p * npc;
+  const int cp = rem / npc;          // ch * R + p
+  const int j = rem - cp * npc;
+  const int ch = cp / a.R;
+  const int p = cp - ch * a.R;
   const int c = a.ord.chunk[p];
-  const int rp = (a.chunk_rows + npc - 1) / npc;
-  const int r0 = j * rp;
-  const int nr = min(rp, a.chunk_rows - r0);
+  const int rp = (a.ch_rows + npc - 1) / npc;
+  const int r0 = ch * a.ch_rows + j * rp;
+  const int nr = min(rp, (ch + 1) * a.ch_rows - r0);
   const int64_t col0 = (int64_t)s * vpr;
   const int width = (int)min((int64_t)vpr, a.k8 - col0);
   const int64_t chunk_vec = (int64_t)a.chunk_rows * a.k8;
@@ -190,11 +206,12 @@ __device__ __forceinline__ void copy_unit(const CopyArgs& a, int u) {
     const uint64_t due = (pace_base(a) + (uint64_t)((float)(u + 1) * a.pace_ticks)) & kPaceClockMask;
     while ((int64_t)(((wall_clock64() & kPaceClockMask) - due) << 16) < 0) __builtin_amdgcn_s_sleep(8);
   }
-  const size_t si = (size_t)c * a.n_slab + s;
-  if (threadIdx.x == 0 && !((a.skip_mask >> c) & 1u))
+  const int g = c * a.C + ch;         // global channel id
+  const size_t si = (size_t)g * a.n_slab + s;
+  if (threadIdx.x == 0 && !(g < 32 && ((a.skip_mask >> g) & 1u)))
     sig_arrive_counted_coherent(a.cnt + si, a.sig + si, (uint32_t)npc, a.sa.epoch);
   if (threadIdx.x == 0 && a.tl.buf)
-    timeline_put(a.tl, 1, (uint32_t)(c << 24 | s << 12 | (j & 0xfff)), t0, t0, wall_clock64());
+    timeline_put(a.tl, 1, (uint32_t)(c << 24 | s << 12 | ((ch * npc + j) & 0xfff)), t0, t0, wall_clock64());
 }
 
 // Next unit from the queue, identical in every thread (`slot` is one int of
@@ -234,10 +251,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_num_vgpr(16))) ag_c
   if (threadIdx.x == 0) leave_queue(a);
 }
 
-// Copy-engine arrival: the value each slab's signal takes this call, staged
-// where the 8-byte signal copies read it.
-__global__ void ag_dma_sigval_kernel(uint64_t* w, uint64_t v) {
-  if (threadIdx.x == 0) *w = v;
+// Copy-engine arrival: entry i of the signal-value ring holds {base + i | 1},
+// the value a channel signal takes in the call whose epoch is base + i.  The
+// DMA engines copy the call's entry into each channel's signal word.
+__global__ void ag_dma_ring_kernel(uint64_t* ring, int n, uint32_t base) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
+    ring[i] = sig_target(base + (uint32_t)i, 1u);
 }
 
 // ---------------------------------------------------------------- GEMM
@@ -251,6 +270,7 @@ struct AgGemmArgs {
   Timeline tl;
   int M, N, K;
   int chunk_rows;
+  int ch_rows;            // rows per channel: row r waits on channel r / ch_rows
   int rank;
   int n_tiles_n;
   int wait;               // 0: no waits (compute-only)
@@ -266,7 +286,7 @@ struct AgGemmArgs {
 
 // Slab waits inside the K loop, per wave.  Slabs below `ready_until` are
 // known complete and already acquired.  Reaching slab s >= ready_until, the
-// wave polls a window of signals in one load: lane l reads chunk
+// wave polls a window of signals in one load: lane l reads channel
 // c_lo + l mod n_span at slab s + l / n_span.  The window's complete prefix
 // becomes ready; if slab s itself is incomplete the wave polls it until it
 // is.  One acquire then covers every slab of the prefix.  As the copy runs
@@ -345,20 +365,22 @@ __global__ void __launch_bounds__(Cfg::NT) ag_gemm_kernel(const AgGemmArgs args)
   const int last = min(row0 + Cfg::BM, args.M) - 1;
   const int c_lo = row0 / args.chunk_rows, c_hi = last / args.chunk_rows;
   // A tile inside the local chunk reads it where it already is and waits for
-  // nothing; every other tile reads the gathered buffer behind its signals.
+  // nothing; every other tile reads the gathered buffer behind the signals
+  // of the channels its rows span.
   const bool local = c_lo == args.rank && c_hi == args.rank;
   if (args.wait && !local) {
+    const int g_lo = row0 / args.ch_rows, g_hi = last / args.ch_rows;
     hook.sig = args.sig;
     hook.sa = args.sa;
     hook.target = sig_target(args.sa.epoch, args.arrivals);
     hook.n_slab = args.n_slab;
     hook.slab_log2 = args.slab_log2;
-    hook.c_lo = c_lo;
-    hook.n_span = c_hi - c_lo + 1;
+    hook.c_lo = g_lo;
+    hook.n_span = g_hi - g_lo + 1;
     hook.active = args.n_slab > 1;
     hook.l1_only = args.l1_only != 0;
     hook.ready_until = 1;
-    for (int c = c_lo; c <= c_hi; ++c) block_poll_ge(args.sig + (size_t)c * args.n_slab, hook.target, args.sa);
+    for (int g = g_lo; g <= g_hi; ++g) block_poll_ge(args.sig + (size_t)g * args.n_slab, hook.target, args.sa);
     acquire_lines(hook.l1_only);
   }
   const uint64_t t1 = args.tl.buf ? wall_clock64() : 0;
@@ -523,35 +545,38 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
   if (o.copy_engine != 0 && o.copy_engine != 1) return fail(ctx, TSG_E_INVALID, "copy_engine must be 0 or 1");
   if (o.copy_engine && o.arrival_gbps)
     return fail(ctx, TSG_E_INVALID, "copy_engine and arrival_gbps cannot be combined");
-  // The runtime moves some device-to-device copies (the 8-byte signal copies
-  // among them) with a kernel even when asked for the copy engines; beside a
-  // GEMM that holds every CU while it waits, that kernel could not start.
-  if (o.copy_engine && mode == TSG_MODE_OVERLAP && o.aux_cus < 0)
-    return fail(ctx, TSG_E_UNSUPPORTED, "copy_engine overlap needs a CU split (aux_cus): the runtime runs small "
-                                        "device copies as kernels, which need a free CU");
   const int tile = o.tile ? o.tile : default_tile(M, N, K);
   const TileShape ts = shape_of(tile);
   if (!ts.bm) return fail(ctx, TSG_E_INVALID, "unknown tile id %d", tile);
   if (tile == 9 && K % 128)
     return fail(ctx, TSG_E_UNSUPPORTED, "tile 9 needs K a multiple of 128 (direct-to-LDS loads only)");
   const int chunk_rows = M / R;
+  // Channels ([TL] section 4.1): C signals per rank, M / (R C) rows each.
+  const int C = o.channels > 0 ? o.channels : 1;
+  if (o.channels < 0 || C > kMaxChannels || chunk_rows % C)
+    return fail(ctx, TSG_E_INVALID, "channels must be in [1, %d] and divide the %d rows per rank", kMaxChannels,
+                chunk_rows);
+  const int ch_rows = chunk_rows / C;
+  if (C > 1 && ch_rows < 8)
+    return fail(ctx, TSG_E_SHAPE, "channels of %d rows: at least 8 rows per channel are needed", ch_rows);
   const int n_mt = (M + ts.bm - 1) / ts.bm, n_nt = (N + ts.bn - 1) / ts.bn;
   if (n_mt > kMaxMTiles) return fail(ctx, TSG_E_UNSUPPORTED, "M / BM exceeds %d", kMaxMTiles);
 
   // Communication tile: slab width W (power of two, >= 64; capped at 2048
   // columns and at the first power of two >= K, which is one slab per chunk).
-  int slab = o.comm_tile ? o.comm_tile : (o.copy_engine ? 2048 : 512);
+  // The copy engines move whole channels: one slab.
+  int slab = o.comm_tile ? o.comm_tile : 512;
   if (slab < 64 || (slab & (slab - 1)))
     return fail(ctx, TSG_E_INVALID, "comm_tile must be a power of two >= 64 (got %d)", slab);
   int k_pow2 = 64;
   while (k_pow2 < K) k_pow2 *= 2;
-  slab = std::min(std::min(slab, k_pow2), 2048);
+  slab = o.copy_engine ? k_pow2 : std::min(std::min(slab, k_pow2), 2048);
   int slab_log2 = 0;
   while ((1 << slab_log2) < slab) ++slab_log2;
   const int n_slab = (K + slab - 1) / slab;
-  if ((size_t)R * n_slab > kSigCap)
-    return fail(ctx, TSG_E_UNSUPPORTED, "R * ceil(K / comm_tile) exceeds %zu signals", kSigCap);
-  const int vpr_log2 = slab_log2 - 3;
+  if ((size_t)R * C * n_slab > kSigCap)
+    return fail(ctx, TSG_E_UNSUPPORTED, "R * channels * ceil(K / comm_tile) exceeds %zu signals", kSigCap);
+  const int vpr_log2 = std::min(slab_log2, 11) - 3;
   TSG_HIP(ctx, hipSetDevice(ctx->device));
 
   // Copy workgroups and streams.  Overlap: in shared mode one workgroup per
@@ -561,19 +586,24 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
   // In shared mode the GEMM runs on the caller's stream and the copy on a
   // side stream; their workgroups must be able to share a CU, or a GEMM that
   // fills every CU first would leave the copy no room while it waits for the
-  // copy.  Otherwise the two run back to back.
+  // copy.  Otherwise the two run back to back.  The copy engines need no CU.
   Pair pr{(hipStream_t)stream, (hipStream_t)stream, ctx->n_cus, 0};
   int nwg = o.aux_wgs > 0 ? o.aux_wgs : ctx->n_cus * 2;
-  bool back_to_back = mode == TSG_MODE_SERIAL;
-  if (mode == TSG_MODE_OVERLAP || mode == TSG_MODE_COMM_ONLY) {
+  bool back_to_back = mode == TSG_MODE_SERIAL && !o.copy_engine;
+  if (!o.copy_engine && (mode == TSG_MODE_OVERLAP || mode == TSG_MODE_COMM_ONLY)) {
     const tsg_status ss = streams(ctx, o, &pr, (hipStream_t)stream);
     if (ss != TSG_OK) return ss;
     if (o.aux_wgs <= 0) nwg = o.aux_cus < 0 ? ctx->n_cus : pr.aux_cus * 4;
-    if (mode == TSG_MODE_OVERLAP && o.aux_cus < 0 && !o.copy_engine) {  // copy engines need no CU
+    if (mode == TSG_MODE_OVERLAP && o.aux_cus < 0) {
       int nt = 0;
       const void* fn = gemm_fn(tile, c_dtype == TSG_BF16, K, &nt);
       back_to_back = !co_resident(ctx, fn, nt, (const void*)&ag_copy_kernel, 256);
     }
+  }
+  if (o.copy_engine && mode == TSG_MODE_OVERLAP && o.aux_cus >= 0) {
+    // the GEMM on its CU share; the copies on the DMA streams
+    const tsg_status ss = streams(ctx, o, &pr, (hipStream_t)stream);
+    if (ss != TSG_OK) return ss;
   }
   // Pieces: every piece ends with the workgroup draining its stores to the
   // coherence point before it arrives, which idles it for a memory round trip,
@@ -581,13 +611,14 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
   // volume over the workgroups, between 32 KB and 128 KB).  Slab 0, which
   // every tile waits for first, is cut so that all workgroups share it; each
   // following head slab gets half as many pieces, down to the body size.
+  // Pieces never straddle channels: np counts pieces per channel.
   const int64_t total_vec = (int64_t)R * chunk_rows * (K / 8);
   int64_t unit_vec = 2048;
   while (unit_vec < 8192 && unit_vec * 2 * nwg <= total_vec) unit_vec *= 2;
   const int rows_q = 256 >> vpr_log2;  // rows one pass of the workgroup moves
   auto pieces_for_rows = [&](int64_t rows) {
-    rows = std::max<int64_t>(1, std::max<int64_t>(rows, std::min(rows_q, chunk_rows)));
-    return (int)std::max<int64_t>(1, (chunk_rows + rows - 1) / rows);
+    rows = std::max<int64_t>(1, std::max<int64_t>(rows, std::min(rows_q, ch_rows)));
+    return (int)std::max<int64_t>(1, (ch_rows + rows - 1) / rows);
   };
   const int np_body = pieces_for_rows(unit_vec >> vpr_log2);
   int np[kHead + 1];
@@ -598,21 +629,21 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
   }
   np[kHead] = np_body;
   for (int h = 0; h <= kHead; ++h) {  // no empty piece: every piece arrives once
-    const int rp = (chunk_rows + np[h] - 1) / np[h];
-    np[h] = (chunk_rows + rp - 1) / rp;
+    const int rp = (ch_rows + np[h] - 1) / np[h];
+    np[h] = (ch_rows + rp - 1) / rp;
   }
   int64_t rows_max = 0;
-  for (int h = 0; h <= kHead; ++h) rows_max = std::max<int64_t>(rows_max, (chunk_rows + np[h] - 1) / np[h]);
+  for (int h = 0; h <= kHead; ++h) rows_max = std::max<int64_t>(rows_max, (ch_rows + np[h] - 1) / np[h]);
   if (rows_max * K * 2 >= (int64_t)1 << 31)
     return fail(ctx, TSG_E_UNSUPPORTED, "gemm_ag_overlap: K too large for the copy's 32-bit offsets");
   int ustart[kHead + 1];
   int64_t n_units = 0;
   for (int h = 0; h < kHead; ++h) {
     ustart[h] = (int)n_units;
-    if (h < n_slab) n_units += (int64_t)R * np[h];
+    if (h < n_slab) n_units += (int64_t)R * C * np[h];
   }
   ustart[kHead] = (int)n_units;
-  n_units += (int64_t)std::max(0, n_slab - kHead) * R * np[kHead];
+  n_units += (int64_t)std::max(0, n_slab - kHead) * R * C * np[kHead];
   if (n_units >= ((int64_t)1 << 30)) return fail(ctx, TSG_E_UNSUPPORTED, "gemm_ag_overlap: too many copy units");
 
   hipStream_t caller = (hipStream_t)stream;
@@ -632,19 +663,33 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
   ga.N = N;
   ga.K = K;
   ga.chunk_rows = chunk_rows;
+  ga.ch_rows = ch_rows;
   ga.n_tiles_n = n_nt;
-  ga.arrivals = 1;  // any completed count: a slab signal is only published once complete
+  ga.arrivals = 1;  // any completed count: a signal is only published once complete
   ga.n_slab = n_slab;
   ga.slab_log2 = slab_log2;
   ga.l1_only = ((uintptr_t)a_full % 128 == 0 && K % 64 == 0) ? 1 : 0;
-  // M-tile order: by the arrival position of the last chunk a tile spans,
+
+  // The copy moves the peers' chunks in arrival order and the local chunk
+  // last: tiles inside the local chunk read it in place, so only the
+  // gathered buffer's own content (and tiles straddling it) waits for it.
+  ChunkOrder co;
+  int copy_pos[kMaxRanks];
+  for (int p = 0; p < kMaxRanks; ++p) co.chunk[p] = 0;
+  for (int p = 1; p < R; ++p) co.chunk[p - 1] = ord.chunk[p];
+  co.chunk[R - 1] = (int8_t)rank;
+  for (int p = 0; p < R; ++p) copy_pos[co.chunk[p]] = p;
+  // M-tile order: tiles inside the local chunk first, then by the copy step
+  // (channel-major, then arrival position) of the last channel a tile spans,
   // ties by row (order knob 1 = plain row order).
   {
     std::vector<std::pair<int, int>> key(n_mt);
     for (int m = 0; m < n_mt; ++m) {
       const int lo = m * ts.bm, hi = std::min(M, lo + ts.bm) - 1;
-      int ready = 0;
-      for (int cc = lo / chunk_rows; cc <= hi / chunk_rows; ++cc) ready = std::max(ready, pos_of[cc]);
+      int ready = -1;
+      if (!(lo / chunk_rows == rank && hi / chunk_rows == rank))
+        for (int g = lo / ch_rows; g <= hi / ch_rows; ++g)
+          ready = std::max(ready, (g % C) * R + copy_pos[g / C]);
       key[m] = {o.order == 1 ? 0 : ready, m};
     }
     std::sort(key.begin(), key.end());
@@ -661,20 +706,13 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
   ca.cnt = ctx->d_cnt + kSigBase;
   ca.sa = ga.sa;
   ca.tl = ga.tl;
-  // The copy moves the peers' chunks in arrival order and the local chunk
-  // last: tiles inside the local chunk read it in place, so only the
-  // gathered buffer's own content (and tiles straddling it) waits for it.
-  {
-    ChunkOrder co;
-    for (int p = 0; p < kMaxRanks; ++p) co.chunk[p] = 0;
-    for (int p = 1; p < R; ++p) co.chunk[p - 1] = ord.chunk[p];
-    co.chunk[R - 1] = (int8_t)rank;
-    ca.ord = co;
-  }
+  ca.ord = co;
   ca.k8 = K / 8;
   ca.chunk_rows = chunk_rows;
   ca.R = R;
   ca.rank = rank;
+  ca.C = C;
+  ca.ch_rows = ch_rows;
   ca.n_slab = n_slab;
   ca.vpr_log2 = vpr_log2;
   for (int h = 0; h <= kHead; ++h) {
@@ -706,32 +744,6 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
   ga.pull_wgs = 0;
   ga.copy = ca;
 
-  // Copy engines: each chunk (contiguous rows) one copy in arrival order,
-  // then the signals of its slabs.  Copies on one stream run in order, so a
-  // signal lands after its data.
-  auto dma = [&](hipStream_t s) -> tsg_status {
-    time_begin(ctx, 1, s);
-    const size_t bytes = (size_t)chunk_rows * K * 2;
-    for (int p = 0; p < R; ++p) {
-      const int c = ca.ord.chunk[p];
-      const char* src = c == rank ? (const char*)a_local
-                                  : (const char*)a_peers + (size_t)(c < rank ? c : c - 1) * bytes;
-      TSG_HIP(ctx, hipMemcpyAsync((char*)a_full + (size_t)c * bytes, src, bytes, hipMemcpyDeviceToDeviceNoCU, s));
-      if (!((o.skip_mask >> c) & 1u))
-        for (int sl = 0; sl < n_slab; ++sl)
-          TSG_HIP(ctx, hipMemcpyAsync(ctx->d_sig + kSigBase + (size_t)c * n_slab + sl, ctx->d_sig + kDmaSigSlot,
-                                      8, hipMemcpyDeviceToDeviceNoCU, s));
-    }
-    time_end(ctx, 1, s);
-    return TSG_OK;
-  };
-  auto copy = [&](hipStream_t s) -> tsg_status {
-    if (o.copy_engine) return dma(s);
-    time_begin(ctx, 1, s);
-    hipLaunchKernelGGL(ag_copy_kernel, dim3(copy_grid), dim3(256), 0, s, ca);
-    time_end(ctx, 1, s);
-    return check_launch(ctx, "ag_copy_kernel");
-  };
   auto gemm = [&](hipStream_t s, int wait, int cus) -> tsg_status {
     ga.wait = wait;
     ga.pull_wgs = wait ? pull : 0;
@@ -743,14 +755,95 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
     return TSG_OK;
   };
 
-  tsg_status st = TSG_OK;
-  if (o.copy_engine && mode != TSG_MODE_COMPUTE_ONLY) {
-    // the signal value, staged before any copy or GEMM workgroup runs
-    hipLaunchKernelGGL(ag_dma_sigval_kernel, dim3(1), dim3(64), 0, caller, ctx->d_sig + kDmaSigSlot,
-                       ((uint64_t)ga.sa.epoch << 32) | 1u);
-    st = check_launch(ctx, "ag_dma_sigval_kernel");
-    if (st != TSG_OK) return st;
+  if (o.copy_engine) {
+    // ---- copy engines: one stream per chunk, fork from / join to `caller`
+    if (mode == TSG_MODE_COMPUTE_ONLY) return gemm(caller, 0, ctx->n_cus);
+    // The call's signal value comes from the ring, which lives in an
+    // allocation of its own: a device copy within one allocation is run as
+    // a kernel by the runtime, a copy between two allocations by a DMA
+    // engine.  The ring is refilled (a short kernel ahead of the fork) once
+    // the epochs it covers are used up.
+    const uint32_t e = ga.sa.epoch;
+    hipStream_t ds[kMaxRanks];
+    for (int p = 0; p < R; ++p) {
+      tsg_status st = dma_stream(ctx, p, &ds[p]);
+      if (st != TSG_OK) return st;
+    }
+    hipStream_t join_s = nullptr;
+    {
+      tsg_status st = dma_stream(ctx, kMaxRanks, &join_s);
+      if (st != TSG_OK) return st;
+    }
+    if (!ctx->dma_ring_valid || e < ctx->dma_ring_base || e - ctx->dma_ring_base >= (uint32_t)tsg_ctx::kDmaRing) {
+      hipLaunchKernelGGL(ag_dma_ring_kernel, dim3(64), dim3(256), 0, caller, ctx->d_dma_ring,
+                         (int)tsg_ctx::kDmaRing, e);
+      tsg_status st = check_launch(ctx, "ag_dma_ring_kernel");
+      if (st != TSG_OK) return st;
+      ctx->dma_ring_base = e;
+      ctx->dma_ring_valid = true;
+    }
+    const uint64_t* val = ctx->d_dma_ring + (e - ctx->dma_ring_base);
+    // Fork, then every copy, then the GEMM: the copies are all queued on
+    // the engines' streams before the GEMM is queued, so that none of them
+    // can be ordered behind the GEMM whose tiles wait for it.
+    TSG_HIP(ctx, hipEventRecord(ctx->ev_fork, caller));
+    hipStream_t gs = caller;
+    if (mode == TSG_MODE_OVERLAP && pr.main != caller) {
+      gs = pr.main;  // the GEMM on its CU share
+      TSG_HIP(ctx, hipStreamWaitEvent(gs, ctx->ev_fork, 0));
+    }
+    TSG_HIP(ctx, hipStreamWaitEvent(join_s, ctx->ev_fork, 0));
+    for (int p = 0; p < R; ++p) TSG_HIP(ctx, hipStreamWaitEvent(ds[p], ctx->ev_fork, 0));
+    time_begin(ctx, 1, join_s);
+    const size_t ch_bytes = (size_t)ch_rows * K * 2;
+    const size_t chunk_bytes = (size_t)chunk_rows * K * 2;
+    for (int p = 0; p < R; ++p) {
+      const int cc = co.chunk[p];
+      const char* src = cc == rank ? (const char*)a_local
+                                   : (const char*)a_peers + (size_t)(cc < rank ? cc : cc - 1) * chunk_bytes;
+      char* dst = (char*)a_full + (size_t)cc * chunk_bytes;
+      for (int ch = 0; ch < C; ++ch) {
+        // copies on one stream complete in order: the signal lands after
+        // the channel's data
+        TSG_HIP(ctx, hipMemcpyAsync(dst + ch * ch_bytes, src + ch * ch_bytes, ch_bytes,
+                                    hipMemcpyDeviceToDeviceNoCU, ds[p]));
+        const int g = cc * C + ch;
+        if (!(g < 32 && ((o.skip_mask >> g) & 1u)))
+          TSG_HIP(ctx, hipMemcpyAsync(ctx->d_sig + kSigBase + (size_t)g * n_slab, val, sizeof(uint64_t),
+                                      hipMemcpyDeviceToDeviceNoCU, ds[p]));
+      }
+      TSG_HIP(ctx, hipEventRecord(ctx->ev_dma[p], ds[p]));
+      TSG_HIP(ctx, hipStreamWaitEvent(join_s, ctx->ev_dma[p], 0));
+    }
+    time_end(ctx, 1, join_s);
+    TSG_HIP(ctx, hipEventRecord(ctx->ev_join[1], join_s));
+    if (mode == TSG_MODE_OVERLAP) {
+      // GEMM last: dispatched at once, its tiles wait for the channels the
+      // engines deliver.
+      tsg_status st = gemm(gs, 1, gs == caller ? ctx->n_cus : pr.main_cus);
+      if (st != TSG_OK) return st;
+    }
+    if (mode == TSG_MODE_SERIAL) {
+      // the whole gather first, then the GEMM (its waits already satisfied)
+      TSG_HIP(ctx, hipStreamWaitEvent(caller, ctx->ev_join[1], 0));
+      return gemm(caller, 1, ctx->n_cus);
+    }
+    if (gs != caller) {
+      TSG_HIP(ctx, hipEventRecord(ctx->ev_join[0], gs));
+      TSG_HIP(ctx, hipStreamWaitEvent(caller, ctx->ev_join[0], 0));
+    }
+    TSG_HIP(ctx, hipStreamWaitEvent(caller, ctx->ev_join[1], 0));
+    return TSG_OK;
   }
+
+  auto copy = [&](hipStream_t s) -> tsg_status {
+    time_begin(ctx, 1, s);
+    hipLaunchKernelGGL(ag_copy_kernel, dim3(copy_grid), dim3(256), 0, s, ca);
+    time_end(ctx, 1, s);
+    return check_launch(ctx, "ag_copy_kernel");
+  };
+
+  tsg_status st = TSG_OK;
   if (back_to_back) {
     st = copy(caller);
     if (st == TSG_OK) st = gemm(caller, 1, ctx->n_cus);

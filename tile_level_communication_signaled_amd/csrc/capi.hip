@@ -54,7 +54,29 @@ Opts resolve(const tsg_opts* o, int default_aux_cus) {
   r.stage_dtype = o ? o->stage_dtype : TSG_F32;
   r.arrival_gbps = o ? o->arrival_gbps : 0;
   r.copy_engine = o ? o->copy_engine : 0;
+  r.channels = o ? o->channels : 0;
   return r;
+}
+
+tsg_status dma_stream(tsg_ctx* ctx, int i, hipStream_t* s) {
+  if (i < 0 || i >= tsg_ctx::kDmaStreams) return fail(ctx, TSG_E_INVALID, "copy-engine stream %d", i);
+  if (!ctx->dma[i]) {
+    if (!ctx->d_dma_ring) {
+      TSG_HIP(ctx, hipMalloc(&ctx->d_dma_ring, (size_t)tsg_ctx::kDmaRing * sizeof(uint64_t)));
+      ctx->dma_ring_valid = false;
+    }
+    TSG_HIP(ctx, hipStreamCreateWithFlags(&ctx->dma[i], hipStreamNonBlocking));
+    TSG_HIP(ctx, hipEventCreateWithFlags(&ctx->ev_dma[i], hipEventDisableTiming));
+    // The first DMA copy on a new stream takes milliseconds (the runtime
+    // sets up its engine queue).  Pay it here, with one 8-byte copy into an
+    // unused word of the status buffer, rather than inside the first call's
+    // signal waits.
+    TSG_HIP(ctx, hipMemcpyAsync(ctx->d_status + 8, ctx->d_dma_ring, sizeof(uint64_t), hipMemcpyDeviceToDeviceNoCU,
+                                ctx->dma[i]));
+    TSG_HIP(ctx, hipStreamSynchronize(ctx->dma[i]));
+  }
+  *s = ctx->dma[i];
+  return TSG_OK;
 }
 
 static tsg_status unmasked(tsg_ctx* ctx, int i, hipStream_t* s) {
@@ -257,6 +279,11 @@ void tsg_ctx_destroy(tsg_ctx* c) {
   for (auto& kv : c->masked) (void)hipStreamDestroy(kv.second);
   for (int i = 0; i < 2; ++i)
     if (c->side[i]) (void)hipStreamDestroy(c->side[i]);
+  for (int i = 0; i < tsg_ctx::kDmaStreams; ++i) {
+    if (c->dma[i]) (void)hipStreamDestroy(c->dma[i]);
+    if (c->ev_dma[i]) (void)hipEventDestroy(c->ev_dma[i]);
+  }
+  if (c->d_dma_ring) (void)hipFree(c->d_dma_ring);
   if (c->ev_fork) (void)hipEventDestroy(c->ev_fork);
   for (int i = 0; i < 2; ++i) {
     if (c->ev_join[i]) (void)hipEventDestroy(c->ev_join[i]);
@@ -281,6 +308,8 @@ tsg_status tsg_check(tsg_ctx* ctx, void* stream) {
   for (auto& kv : ctx->masked) TSG_HIP(ctx, hipStreamSynchronize(kv.second));
   for (int i = 0; i < 2; ++i)
     if (ctx->side[i]) TSG_HIP(ctx, hipStreamSynchronize(ctx->side[i]));
+  for (int i = 0; i < tsg_ctx::kDmaStreams; ++i)
+    if (ctx->dma[i]) TSG_HIP(ctx, hipStreamSynchronize(ctx->dma[i]));
   uint32_t st = 0;
   TSG_HIP(ctx, hipMemcpy(&st, ctx->d_status, sizeof st, hipMemcpyDeviceToHost));
   if (st) {

@@ -31,6 +31,15 @@ struct tsg_ctx {
   // side streams keyed by CU mask (empty key: unmasked streams 0 / 1)
   std::map<std::vector<uint32_t>, hipStream_t> masked;
   hipStream_t side[2] = {nullptr, nullptr};
+  // Copy-engine streams of the AllGather (one per chunk, then a join
+  // stream), their events, and the ring of signal values the engines copy.
+  static constexpr int kDmaStreams = 33;
+  static constexpr int kDmaRing = 1 << 16;
+  hipStream_t dma[kDmaStreams] = {};
+  hipEvent_t ev_dma[kDmaStreams] = {};
+  uint64_t* d_dma_ring = nullptr;
+  uint32_t dma_ring_base = 0;
+  bool dma_ring_valid = false;
   hipEvent_t ev_fork = nullptr;
   hipEvent_t ev_join[2] = {nullptr, nullptr};
   hipEvent_t ev_k[2][2] = {{nullptr, nullptr}, {nullptr, nullptr}};
@@ -72,6 +81,7 @@ struct Opts {
   int stage_dtype; // MoE y staging: TSG_F32 or TSG_BF16
   int arrival_gbps; // AG arrival pacing, 0 = none
   int copy_engine;  // AG: 1 = DMA copy engines move the data
+  int channels;     // AG: signals per rank (0 = 1)
 };
 Opts resolve(const tsg_opts* o, int default_aux_cus);
 
@@ -86,6 +96,10 @@ struct Pair {
   int aux_cus;
 };
 tsg_status streams(tsg_ctx* ctx, const Opts& o, Pair* out, hipStream_t caller = nullptr);
+
+// Copy-engine stream i (0 <= i < tsg_ctx::kDmaStreams) and its event,
+// created on first use.
+tsg_status dma_stream(tsg_ctx* ctx, int i, hipStream_t* s);
 
 // True when one workgroup of kernel `a` (nt_a threads) and one of kernel `b`
 // fit on one CU together: registers of their waves on each SIMD and LDS.
