@@ -357,6 +357,27 @@ tsg_status moe_expert_combine(tsg_ctx* ctx, const void* x, const int32_t* topk_i
                               int T, int H, int I, int E, int k,
                               const tsg_opts* opts, int mode, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * moe_expert_combine with the workspace taken from the library's own static
+ * device buffer of TSG_MOE_NOALLOC_BYTES (64 MiB) instead of an argument.
+ * Every other argument, the results and the errors are those of
+ * moe_expert_combine.  The call allocates nothing (no hipMalloc, hipFree,
+ * stream creation or memset) and queues its work on `stream` only, so it
+ * supports shared CUs only: aux_cus > 0 or opts.timeline != 0 give
+ * TSG_E_UNSUPPORTED.  Dims whose workspace (tsg_workspace_bytes) exceeds the
+ * buffer give TSG_E_WORKSPACE, before anything is queued.  The buffer is
+ * one per GPU, set up by tsg_ctx_create and held until the process ends;
+ * every call on that GPU shares it (each call rebuilds all of its content),
+ * so calls that overlap in time on one GPU (different streams or contexts)
+ * race and must not be issued. */
+#define TSG_MOE_NOALLOC_BYTES (64u << 20)
+tsg_status moe_expert_combine_noalloc(tsg_ctx* ctx, const void* x, const int32_t* topk_ids,
+                                      const float* topk_w, const void* w_up, const void* w_down,
+                                      float* out, int32_t* expert_counts, int32_t* sorted_ids,
+                                      int T, int H, int I, int E, int k,
+                                      const tsg_opts* opts, int mode, void* stream);
+
 enum { TSG_OP_AG = 0, TSG_OP_RS = 1, TSG_OP_MLP2 = 2, TSG_OP_MOE = 3 };
 
 /* Workspace bytes an op needs for `dims` (TSG_OP_MOE: {T, H, I, E, k});

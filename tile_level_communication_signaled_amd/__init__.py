@@ -40,7 +40,9 @@ EXPORTS = (
     "tsg_enable_kernel_timing", "tsg_kernel_ms", "tsg_timeline", "tsg_workspace_bytes",
     "tsg_moe_workspace_layout",
     "gemm_ag_overlap", "gemm_rs_overlap", "mlp2_pipelined", "moe_expert_combine",
+    "moe_expert_combine_noalloc",
 )
+MOE_NOALLOC_BYTES = 64 << 20   # the static workspace of moe_expert_combine_noalloc, per GPU
 
 # fields of tsg_moe_workspace_layout, in order
 MOE_LAYOUT_FIELDS = ("meta", "offs", "poffs", "rb_expert", "row_pair", "row_token", "pair_row", "h", "y",
@@ -86,9 +88,11 @@ _lib.gemm_rs_overlap.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _
 _lib.mlp2_pipelined.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _P(Opts), _i, _vp]
 _lib.moe_expert_combine.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                                     _i, _i, _i, _i, _i, _P(Opts), _i, _vp]
+_lib.moe_expert_combine_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                            _i, _i, _i, _i, _i, _P(Opts), _i, _vp]
 for _f in ("tsg_ctx_create", "tsg_check", "tsg_device_info", "tsg_enable_kernel_timing", "tsg_kernel_ms",
            "tsg_timeline", "tsg_moe_workspace_layout", "gemm_ag_overlap", "gemm_rs_overlap", "mlp2_pipelined",
-           "moe_expert_combine"):
+           "moe_expert_combine", "moe_expert_combine_noalloc"):
     getattr(_lib, _f).restype = _i
 
 
@@ -255,4 +259,14 @@ def moe_expert_combine(ctx: Context, x, topk_ids, topk_w, w_up, w_down, out, exp
     st = _lib.moe_expert_combine(ctx.handle, _ptr(x), _ptr(topk_ids), _ptr(topk_w), _ptr(w_up), _ptr(w_down),
                                  _ptr(out), _ptr(expert_counts), _ptr(sorted_ids), _ptr(workspace),
                                  workspace_bytes_, T, H, I, E, k, _opts(opts), mode, _stream(stream))
+    return ctx._raise(st) if raise_on_error else st
+
+
+def moe_expert_combine_noalloc(ctx: Context, x, topk_ids, topk_w, w_up, w_down, out, expert_counts, sorted_ids,
+                               T, H, I, E, k, opts=None, mode=OVERLAP, stream=None, raise_on_error=True):
+    """moe_expert_combine with its workspace in the library's static device
+    buffer (MOE_NOALLOC_BYTES per GPU): the call allocates nothing."""
+    st = _lib.moe_expert_combine_noalloc(ctx.handle, _ptr(x), _ptr(topk_ids), _ptr(topk_w), _ptr(w_up),
+                                         _ptr(w_down), _ptr(out), _ptr(expert_counts), _ptr(sorted_ids),
+                                         T, H, I, E, k, _opts(opts), mode, _stream(stream))
     return ctx._raise(st) if raise_on_error else st

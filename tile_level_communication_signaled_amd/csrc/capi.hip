@@ -264,7 +264,7 @@ tsg_status tsg_ctx_create(int device, tsg_ctx** out) {
   if (e == hipSuccess) e = hipDeviceSynchronize();
   c->n_sig = kSignals;
   c->timeline_cap = kTimelineCap;
-  if (e != hipSuccess) {
+  if (e != hipSuccess || tsg_moe_scratch_init(c) != TSG_OK) {
     tsg_ctx_destroy(c);
     return TSG_E_HIP;
   }
@@ -408,7 +408,18 @@ tsg_status moe_expert_combine(tsg_ctx* ctx, const void* x, const int32_t* topk_i
   if (!ctx) return TSG_E_INVALID;
   ctx->err.clear();
   return tsg_op_moe(ctx, x, topk_ids, topk_w, w_up, w_down, out, expert_counts, sorted_ids,
-                    workspace, workspace_bytes, T, H, I, E, k, opts, mode, stream);
+                    workspace, workspace_bytes, T, H, I, E, k, opts, mode, stream, false);
+}
+
+tsg_status moe_expert_combine_noalloc(tsg_ctx* ctx, const void* x, const int32_t* topk_ids,
+                                      const float* topk_w, const void* w_up, const void* w_down,
+                                      float* out, int32_t* expert_counts, int32_t* sorted_ids, int T,
+                                      int H, int I, int E, int k, const tsg_opts* opts, int mode,
+                                      void* stream) {
+  if (!ctx) return TSG_E_INVALID;
+  ctx->err.clear();
+  return tsg_op_moe(ctx, x, topk_ids, topk_w, w_up, w_down, out, expert_counts, sorted_ids, nullptr, 0,
+                    T, H, I, E, k, opts, mode, stream, true);
 }
 
 }  // extern "C"

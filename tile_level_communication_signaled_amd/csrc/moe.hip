@@ -35,6 +35,8 @@
 //      queue items of the producer itself, after the down tiles, so they run
 //      on any CU as soon as their tiles are ready; with a CU split they run
 //      in moe_combine_kernel, a persistent consumer on its own partition.
+#include <mutex>
+
 #include "tsg_gemm.hpp"
 #include "tsg_internal.hpp"
 
@@ -620,6 +622,32 @@ void launch_prod(const ProdArgs& a, int grid, hipStream_t s) {
 
 }  // namespace
 
+// Workspace of moe_expert_combine_noalloc: a static device array, one copy
+// per GPU, held until the process ends.  Host code never uses the array's
+// name as an address (on the host it is a stand-in, not device memory): its
+// device address is looked up once per device, below, and kept.
+namespace {
+static __device__ __align__(256) char scratch[TSG_MOE_NOALLOC_BYTES];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};
+}  // namespace
+
+tsg_status tsg_moe_scratch_init(tsg_ctx* ctx) {
+  if (ctx->device < 0 || ctx->device >= 64) return tsgh::fail(ctx, TSG_E_UNSUPPORTED, "device index above 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[ctx->device]) {
+    // called with ctx->device current (tsg_ctx_create)
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return tsgh::hip_fail(ctx, e, "hipGetSymbolAddress(scratch)");
+    if (!ptr || ((uintptr_t)ptr & 255u))
+      return tsgh::fail(ctx, TSG_E_HIP, "scratch buffer at an unexpected address %p", ptr);
+    g_scratch_ptr[ctx->device] = ptr;
+  }
+  ctx->d_noalloc_ws = g_scratch_ptr[ctx->device];
+  return TSG_OK;
+}
+
 size_t tsg_moe_workspace(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k) {
   if (T < 1 || H < 8 || I < 8 || E < 1 || E > kMaxExperts || k != 2) return 0;
   return layout(T, H, I, E, k).total;
@@ -640,8 +668,14 @@ bool tsg_moe_layout_fields(const int64_t* d, int64_t* out, int n) {
 tsg_status tsg_op_moe(tsg_ctx* ctx, const void* x, const int32_t* topk_ids, const float* topk_w,
                       const void* w_up, const void* w_down, float* out, int32_t* expert_counts,
                       int32_t* sorted_ids, void* workspace, size_t workspace_bytes, int T, int H,
-                      int I, int E, int k, const tsg_opts* opts, int mode, void* stream) {
+                      int I, int E, int k, const tsg_opts* opts, int mode, void* stream, bool noalloc) {
   using namespace tsgh;
+  if (noalloc) {
+    // the library's static buffer stands in for the workspace argument
+    workspace = ctx->d_noalloc_ws;
+    workspace_bytes = TSG_MOE_NOALLOC_BYTES;
+    if (!workspace) return fail(ctx, TSG_E_HIP, "moe_expert_combine_noalloc: no scratch buffer on this device");
+  }
   if (!x || !topk_ids || !topk_w || !w_up || !w_down || !out || !expert_counts || !sorted_ids)
     return fail(ctx, TSG_E_INVALID, "moe_expert_combine: null pointer");
   if (mode < TSG_MODE_OVERLAP || mode > TSG_MODE_COMM_ONLY) return fail(ctx, TSG_E_INVALID, "bad mode");
@@ -654,6 +688,10 @@ tsg_status tsg_op_moe(tsg_ctx* ctx, const void* x, const int32_t* topk_ids, cons
       !aligned16(workspace))
     return fail(ctx, TSG_E_ALIGN, "moe_expert_combine: pointers must be 16-byte aligned");
   const Layout L = layout(T, H, I, E, k);
+  if (noalloc && L.total > workspace_bytes)
+    return fail(ctx, TSG_E_WORKSPACE,
+                "moe_expert_combine_noalloc: these dims need %zu bytes of workspace, above the %zu-byte static buffer",
+                L.total, workspace_bytes);
   if (!workspace || workspace_bytes < L.total)
     return fail(ctx, TSG_E_WORKSPACE, "workspace of %zu bytes needed", L.total);
   if ((int64_t)T * H * 2 >= (int64_t(1) << 32) || (int64_t)H * I * 2 >= (int64_t(1) << 32) ||
@@ -669,6 +707,10 @@ tsg_status tsg_op_moe(tsg_ctx* ctx, const void* x, const int32_t* topk_ids, cons
   const Opts o = resolve(opts, -1);
   if (o.stage_dtype != TSG_F32 && o.stage_dtype != TSG_BF16)
     return fail(ctx, TSG_E_INVALID, "moe_expert_combine: stage_dtype must be TSG_F32 or TSG_BF16");
+  // Everything on the caller's stream: no stream is created and no memset
+  // is recorded (the timeline counter would need one).
+  if (noalloc && (o.aux_cus > 0 || o.timeline))
+    return fail(ctx, TSG_E_UNSUPPORTED, "moe_expert_combine_noalloc runs on shared CUs without a timeline");
   TSG_HIP(ctx, hipSetDevice(ctx->device));
   hipStream_t caller = (hipStream_t)stream;
   ++ctx->epoch;
@@ -778,6 +820,7 @@ tsg_status tsg_op_moe(tsg_ctx* ctx, const void* x, const int32_t* topk_ids, cons
     if (st == TSG_OK && mode == TSG_MODE_SERIAL) st = combine(caller, ctx->n_cus * 2, 1);
     return st;
   }
+  if (noalloc) return combine(caller, ctx->n_cus * 2, 0);  // COMM_ONLY on the caller's stream
   Pair pr;
   st = streams(ctx, o, &pr);
   if (st != TSG_OK) return st;

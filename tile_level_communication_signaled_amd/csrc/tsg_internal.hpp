@@ -38,6 +38,7 @@ struct tsg_ctx {
   hipStream_t dma[kDmaStreams] = {};
   hipEvent_t ev_dma[kDmaStreams] = {};
   uint64_t* d_dma_ring = nullptr;
+  void* d_noalloc_ws = nullptr;  // device address of the MoE no-alloc workspace (static)
   uint32_t dma_ring_base = 0;
   bool dma_ring_valid = false;
   hipEvent_t ev_fork = nullptr;
@@ -132,7 +133,10 @@ tsg_status tsg_op_mlp2(tsg_ctx*, const void*, const void*, void*, const void*, f
                        int, int, const tsg_opts*, int, void*);
 tsg_status tsg_op_moe(tsg_ctx*, const void*, const int32_t*, const float*, const void*,
                       const void*, float*, int32_t*, int32_t*, void*, size_t, int, int, int, int,
-                      int, const tsg_opts*, int, void*);
+                      int, const tsg_opts*, int, void*, bool noalloc);
+// Looks up (once per device) the device address of the MoE no-alloc
+// workspace and stores it in ctx->d_noalloc_ws; ctx->device must be current.
+tsg_status tsg_moe_scratch_init(tsg_ctx* ctx);
 size_t tsg_moe_workspace(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k);
 bool tsg_moe_layout_fields(const int64_t* dims, int64_t* out, int n);
 tsg_status tsg_probe_xcd(tsg_ctx* ctx);
