@@ -12,8 +12,8 @@
 // Topk-Reduce).
 //
 // Kernels (one call):
-//   1. moe_route_kernel (one workgroup) and moe_place_kernel (one wave per
-//      block of pairs): expert_counts, a stable counting sort of the pairs
+//   1. moe_count_kernel and moe_place_kernel (one workgroup per 256 pairs):
+//      expert_counts, a stable counting sort of the pairs
 //      p = t*k + s by expert (sorted_ids, order (expert, t, s)), and the
 //      lookup tables of the padded layout: every expert's rows are padded
 //      to a multiple of BM = 256, row block rb belongs to one expert,
@@ -48,7 +48,6 @@ constexpr int BM = 256;                 // row padding unit and tile rows
 constexpr int BN_UP = 224;
 constexpr int BN_DN = 224;
 constexpr int kCombMaxRb = 4096;         // row blocks the combine's partner list can name
-constexpr int kRouteThreads = 256;
 constexpr int kMaxExperts = 256;
 constexpr size_t kSigH = size_t(1) << 19;          // h row-block signals
 constexpr size_t kSigReady = kSigH + 65536;         // ready signals of down tiles
@@ -116,192 +115,165 @@ Ws bind(char* base, const Layout& L) {
 }
 
 // ------------------------------------------------------------------ route
-// Two kernels.  The pairs are cut into blocks of PB (a multiple of 64) in
-// order.  moe_route_kernel (one workgroup, thread j counting block j)
-// counts every expert's pairs per block in LDS (uint16; every count and
-// prefix is below 65536 because T*k is), scans the counts per expert over
-// the blocks (a shuffle scan within each wave, then the totals of the
-// earlier waves), writes the expert offsets, clears the lookup tables and
-// leaves pre[e][j] = pairs of e in blocks before j.  moe_place_kernel (one
-// wave per block, spread over the CUs) then places the block's pairs 64 at
-// a time.  Stable: the position of pair p is offs[e] + pre[e][j] + (pairs
-// of e earlier in p's own block).
+// Two kernels over blocks of 256 pairs, one pair per thread (P = T k <=
+// 65535 pairs, so at most 256 blocks).
+//   moe_count_kernel: each block counts its pairs per expert (wave ballots
+//     into LDS) and stores the G x E block counts.
+//   moe_place_kernel: each block loads all G x E counts into LDS and takes
+//     from them the expert totals, offsets, padded offsets and its own
+//     per-expert prefix over the earlier blocks.  A pair's rank among its
+//     block's pairs of the same expert (wave ballots, then the earlier
+//     waves' counts) then gives its place: position offs[e] + pre_b[e] +
+//     rank in sorted_ids, row poffs[e] + pre_b[e] + rank.  The same kernel
+//     marks padding rows, unused rows and the sorted_ids of dropped pairs
+//     with -1; block 0 writes the counts, offsets and row-block table.
+// Stable: pairs of one expert keep their order, so sorted_ids is ordered by
+// (expert, token, slot).
+constexpr int kRouteThreads = 256;
 constexpr int kRouteWaves = kRouteThreads / 64;
 constexpr int kRouteMaxPairs = 65535;
-__host__ __device__ constexpr int route_pb(int P) {
-  return ((P + kRouteThreads - 1) / kRouteThreads + 63) & ~63;
-}
+constexpr int kRouteLdsCounts = 4096;  // G x E counts kept in LDS (larger: read from memory)
 
 struct RouteArgs {
   const int32_t* ids;
   int32_t* counts;
   int32_t* sorted_ids;
   Ws ws;
-  int* pre;             // [E][kRouteThreads] per-block prefixes (scratch)
+  int* blk;             // [G][E] per-block counts (scratch)
   uint32_t* status;
-  int T, E, k;
+  int P, E, k, G;
   int64_t rows_max, n_rb_max;
 };
 
-struct PlaceArgs {
-  const int32_t* ids;
-  int32_t* sorted_ids;
-  Ws ws;
-  const int* pre;
-  int P, E, k, PB;
-};
-
-// Expert ids of pairs [p0, p1) of the block starting at 16-byte aligned p0,
-// visited in order: f(p, e).  Groups of eight 16-byte loads are issued
-// before any of their ids is used, so a block costs one memory round trip
-// per 32 pairs rather than one per 4.
-template <class F>
-__device__ __forceinline__ void route_block(const int32_t* __restrict__ ids, int p0, int p1, F&& f) {
-  constexpr int G = 8;
-  int p = p0;
-  for (; p + 4 * G <= p1; p += 4 * G) {
-    int4 v[G];
-#pragma unroll
-    for (int i = 0; i < G; ++i) v[i] = *(const int4*)(ids + p + 4 * i);
-#pragma unroll
-    for (int i = 0; i < G; ++i) {
-      f(p + 4 * i, v[i].x);
-      f(p + 4 * i + 1, v[i].y);
-      f(p + 4 * i + 2, v[i].z);
-      f(p + 4 * i + 3, v[i].w);
-    }
+// Padded offsets in LDS -> expert of padded row r (binary search), or -1
+// past the last expert's rows.
+__device__ __forceinline__ int expert_of_row(const int* s_poffs, int E, int64_t r) {
+  if (r >= s_poffs[E]) return -1;
+  int lo = 0, hi = E - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (s_poffs[mid] <= r) lo = mid; else hi = mid - 1;
   }
-  for (; p + 4 <= p1; p += 4) {
-    const int4 v = *(const int4*)(ids + p);
-    f(p, v.x);
-    f(p + 1, v.y);
-    f(p + 2, v.z);
-    f(p + 3, v.w);
-  }
-  for (; p < p1; ++p) f(p, ids[p]);
+  return lo;
 }
 
-__global__ void __launch_bounds__(kRouteThreads) moe_route_kernel(const RouteArgs a) {
-  __shared__ uint16_t cnt[kMaxExperts][kRouteThreads];
-  __shared__ int s_wtot[kMaxExperts][kRouteWaves];
-  __shared__ int s_offs[kMaxExperts + 1], s_poffs[kMaxExperts + 1];
-  __shared__ int s_bad;
-  const int j = threadIdx.x;
-  const int lane = j & 63, wave = j >> 6;
-  const int P = a.T * a.k, E = a.E;
-  const int PB = route_pb(P);
-  const int p0 = min(P, j * PB), p1 = min(P, p0 + PB);
-  for (int e = 0; e < E; ++e) cnt[e][j] = 0;
-  if (j == 0) s_bad = 0;
+// Ranks each lane's expert id among the lanes of its wave with the same id
+// (lower lanes first) and stores the count of every id present into cnt[id]
+// (LDS).  Lanes with ok == false take part in no group.
+__device__ __forceinline__ int wave_rank(int e, bool ok, int* cnt) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t below = (1ull << lane) - 1;
+  int rank = 0;
+  uint64_t todo = __ballot(ok);
+  while (todo) {
+    const int l = (int)__builtin_ctzll(todo);
+    const int el = __builtin_amdgcn_readlane(e, l);
+    const uint64_t m = __ballot(ok && e == el);
+    if (ok && e == el) rank = __popcll(m & below);
+    if (lane == l) cnt[el] = __popcll(m);
+    todo &= ~m;
+  }
+  return rank;
+}
+
+__global__ void __launch_bounds__(kRouteThreads) moe_count_kernel(const RouteArgs a) {
+  __shared__ int s_cnt[kRouteWaves][kMaxExperts];
+  const int b = blockIdx.x, t = threadIdx.x, wave = t >> 6;
+  const int E = a.E;
+  for (int i = t; i < kRouteWaves * kMaxExperts; i += kRouteThreads) (&s_cnt[0][0])[i] = 0;
   __syncthreads();
-  int bad = 0;
-  route_block(a.ids, p0, p1, [&](int, int e) {
-    if (e >= 0 && e < E) cnt[e][j]++;
-    else bad = 1;
-  });
-  if (bad) atomicOr(&s_bad, 1);
+  const int p = b * kRouteThreads + t;
+  const int e = p < a.P ? a.ids[p] : 0;
+  const bool ok = p < a.P && e >= 0 && e < E;
+  (void)wave_rank(e, ok, s_cnt[wave]);
+  if (__ballot(p < a.P && !ok) && (t & 63) == 0)
+    __hip_atomic_fetch_or(a.status, ERR_BAD_EXPERT, __ATOMIC_RELAXED, TSG_SIG_SCOPE);
   __syncthreads();
-  // exclusive scan over threads, per expert: within the wave first
-  for (int e = 0; e < E; ++e) {
-    const int c = cnt[e][j];
-    int x = c;
+  for (int x = t; x < E; x += kRouteThreads) {
+    int c = 0;
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int y = __shfl_up(x, d, 64);
-      if (lane >= d) x += y;
+    for (int w = 0; w < kRouteWaves; ++w) c += s_cnt[w][x];
+    a.blk[(int64_t)b * E + x] = c;
+  }
+}
+
+__global__ void __launch_bounds__(kRouteThreads) moe_place_kernel(const RouteArgs a) {
+  __shared__ int s_cnt[kRouteWaves][kMaxExperts];
+  __shared__ int s_blk[kRouteLdsCounts];
+  __shared__ int s_offs[kMaxExperts + 1], s_poffs[kMaxExperts + 1], s_pre[kMaxExperts];
+  const int b = blockIdx.x, t = threadIdx.x, wave = t >> 6;
+  const int E = a.E, G = a.G;
+  const bool in_lds = G * E <= kRouteLdsCounts;
+  const int p = b * kRouteThreads + t;
+  const int e = p < a.P ? a.ids[p] : 0;
+  if (in_lds)
+    for (int i = t; i < G * E; i += kRouteThreads) s_blk[i] = a.blk[i];
+  for (int i = t; i < kRouteWaves * kMaxExperts; i += kRouteThreads) (&s_cnt[0][0])[i] = 0;
+  __syncthreads();
+  // per expert: prefix over the blocks before b, and the total
+  for (int x = t; x < E; x += kRouteThreads) {
+    int pre = 0, tot = 0;
+    for (int bb = 0; bb < G; ++bb) {
+      const int c = in_lds ? s_blk[bb * E + x] : a.blk[(int64_t)bb * E + x];
+      pre += bb < b ? c : 0;
+      tot += c;
     }
-    cnt[e][j] = (uint16_t)(x - c);
-    if (lane == 63) s_wtot[e][wave] = x;
+    s_pre[x] = pre;
+    s_offs[x + 1] = tot;  // scanned below
   }
   __syncthreads();
-  // then the totals of the earlier waves; expert totals
-  for (int e = 0; e < E; ++e) {
-    int before = 0;
-    for (int w = 0; w < wave; ++w) before += s_wtot[e][w];
-    cnt[e][j] = (uint16_t)(cnt[e][j] + before);
-  }
-  for (int e = j; e < E; e += kRouteThreads) {
-    int tot = 0;
-    for (int w = 0; w < kRouteWaves; ++w) tot += s_wtot[e][w];
-    s_offs[e + 1] = tot;  // count of expert e, scanned below
-  }
-  __syncthreads();
-  if (j == 0) {
+  if (t == 0) {
     int o = 0, po = 0;
-    for (int e = 0; e < E; ++e) {
-      const int c = s_offs[e + 1];
-      a.counts[e] = c;
-      s_offs[e] = o;
-      s_poffs[e] = po;
+    for (int x = 0; x < E; ++x) {
+      const int c = s_offs[x + 1];
+      s_offs[x] = o;
+      s_poffs[x] = po;
       o += c;
       po += (c + BM - 1) / BM * BM;
     }
     s_offs[E] = o;
     s_poffs[E] = po;
-    a.ws.meta[0] = po / BM;
-    a.ws.meta[1] = o;
-    for (int e = 0; e <= E; ++e) {
-      a.ws.offs[e] = s_offs[e];
-      a.ws.poffs[e] = s_poffs[e];
+  }
+  __syncthreads();
+  if (b == 0) {
+    for (int x = t; x <= E; x += kRouteThreads) {
+      if (x < E) a.counts[x] = s_offs[x + 1] - s_offs[x];
+      a.ws.offs[x] = s_offs[x];
+      a.ws.poffs[x] = s_poffs[x];
     }
-    if (s_bad) __hip_atomic_fetch_or(a.status, ERR_BAD_EXPERT, __ATOMIC_RELAXED, TSG_SIG_SCOPE);
+    if (t == 0) {
+      a.ws.meta[0] = s_poffs[E] / BM;
+      a.ws.meta[1] = s_offs[E];
+    }
+    for (int64_t rb = t; rb < a.n_rb_max; rb += kRouteThreads)
+      a.ws.rb_expert[rb] = expert_of_row(s_poffs, E, rb * BM);
   }
+  const bool ok = p < a.P && e >= 0 && e < E;
+  int rank = wave_rank(e, ok, s_cnt[wave]);
   __syncthreads();
-  // row tables default to "no pair"; pairs dropped for a bad id keep -1
-  for (int64_t r = j; r < a.rows_max; r += kRouteThreads) {
-    a.ws.row_pair[r] = -1;
-    a.ws.row_token[r] = -1;
+  if (ok) {
+    for (int w = 0; w < wave; ++w) rank += s_cnt[w][e];
+    rank += s_pre[e];
+    const int row = s_poffs[e] + rank;
+    a.sorted_ids[s_offs[e] + rank] = p;
+    a.ws.pair_row[p] = row;
+    a.ws.row_pair[row] = p;
+    a.ws.row_token[row] = p / a.k;
+  } else if (p < a.P) {
+    a.ws.pair_row[p] = -1;  // dropped pair (bad expert id)
   }
-  for (int p = j; p < P; p += kRouteThreads) {
-    a.sorted_ids[p] = -1;
-    a.ws.pair_row[p] = -1;
-  }
-  for (int64_t rb = j; rb < a.n_rb_max; rb += kRouteThreads) a.ws.rb_expert[rb] = -1;
-  __syncthreads();
-  for (int e = 0; e < E; ++e)
-    for (int rb = s_poffs[e] / BM + j; rb < s_poffs[e + 1] / BM; rb += kRouteThreads) a.ws.rb_expert[rb] = e;
-  for (int e = 0; e < E; ++e) a.pre[e * kRouteThreads + j] = cnt[e][j];
-}
-
-// One wave per block of PB pairs.  Each group of 64 pairs is ranked per
-// expert with ballots: for each expert present, the lanes holding it learn
-// their order among them, and the block's running count of that expert
-// (in LDS) advances by their number.
-__global__ void __launch_bounds__(64) moe_place_kernel(const PlaceArgs a) {
-  __shared__ int run[kMaxExperts], s_offs[kMaxExperts], s_poffs[kMaxExperts];
-  const int j = blockIdx.x, lane = threadIdx.x;
-  for (int e = lane; e < a.E; e += 64) {
-    run[e] = a.pre[e * kRouteThreads + j];
-    s_offs[e] = a.ws.offs[e];
-    s_poffs[e] = a.ws.poffs[e];
-  }
-  __syncthreads();
-  const uint64_t below = (1ull << lane) - 1;
-  const int p_end = min(a.P, (j + 1) * a.PB);
-  for (int c0 = j * a.PB; c0 < p_end; c0 += 64) {
-    const int p = c0 + lane;
-    const int e = p < p_end ? a.ids[p] : -1;
-    const bool ok = e >= 0 && e < a.E;
-    uint64_t todo = __ballot(ok);
-    while (todo) {
-      const int l = (int)__builtin_ctzll(todo);
-      const int el = __builtin_amdgcn_readlane(e, l);
-      const uint64_t m = __ballot(ok && e == el);
-      const int base = run[el];
-      if (ok && e == el) {
-        const int rank = base + __popcll(m & below);
-        const int row = s_poffs[el] + rank;
-        a.sorted_ids[s_offs[el] + rank] = p;
-        a.ws.pair_row[p] = row;
-        a.ws.row_pair[row] = p;
-        a.ws.row_token[row] = p / a.k;
-      }
-      __syncthreads();  // every lane has read run[el] before it advances
-      if (lane == l) run[el] = base + __popcll(m);
-      __syncthreads();
-      todo &= ~m;
+  // rows that hold no pair: padding after each expert's pairs, and rows
+  // past the last expert's
+  const int64_t stride = (int64_t)G * kRouteThreads;
+  for (int64_t r = p; r < a.rows_max; r += stride) {
+    const int x = expert_of_row(s_poffs, E, r);
+    if (x < 0 || r - s_poffs[x] >= s_offs[x + 1] - s_offs[x]) {
+      a.ws.row_pair[r] = -1;
+      a.ws.row_token[r] = -1;
     }
   }
+  // sorted_ids past the kept pairs (only when pairs were dropped)
+  for (int64_t q = (int64_t)s_offs[E] + p; q < a.P; q += stride) a.sorted_ids[q] = -1;
 }
 
 // --------------------------------------------------------------- producer
@@ -726,23 +698,15 @@ tsg_status tsg_op_moe(tsg_ctx* ctx, const void* x, const int32_t* topk_ids, cons
   ra.sorted_ids = sorted_ids;
   ra.ws = ws;
   ra.status = ctx->d_status;
-  ra.T = T;
+  ra.P = T * k;
   ra.E = E;
   ra.k = k;
+  ra.G = (ra.P + kRouteThreads - 1) / kRouteThreads;
   ra.rows_max = L.rows_max;
   ra.n_rb_max = L.n_rb_max;
-  // the per-block prefixes use the start of the y staging area, which only
-  // the down tiles write, after the routing (E * 1 KiB <= its size)
-  ra.pre = (int*)ws.y;
-  PlaceArgs pl;
-  pl.ids = topk_ids;
-  pl.sorted_ids = sorted_ids;
-  pl.ws = ws;
-  pl.pre = ra.pre;
-  pl.P = T * k;
-  pl.E = E;
-  pl.k = k;
-  pl.PB = route_pb(T * k);
+  // the per-block counts use the start of the y staging area, which only
+  // the down tiles write, after the routing (G E ints, far below its size)
+  ra.blk = (int*)ws.y;
 
   ProdArgs pa;
   pa.x = (const uint16_t*)x;
@@ -781,10 +745,10 @@ tsg_status tsg_op_moe(tsg_ctx* ctx, const void* x, const int32_t* topk_ids, cons
   ca.y_bf16 = pa.y_bf16;
 
   auto route = [&]() -> tsg_status {
-    hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(kRouteThreads), 0, caller, ra);
-    tsg_status rs = check_launch(ctx, "moe_route_kernel");
+    hipLaunchKernelGGL(moe_count_kernel, dim3(ra.G), dim3(kRouteThreads), 0, caller, ra);
+    tsg_status rs = check_launch(ctx, "moe_count_kernel");
     if (rs != TSG_OK) return rs;
-    hipLaunchKernelGGL(moe_place_kernel, dim3((pl.P + pl.PB - 1) / pl.PB), dim3(64), 0, caller, pl);
+    hipLaunchKernelGGL(moe_place_kernel, dim3(ra.G), dim3(kRouteThreads), 0, caller, ra);
     return check_launch(ctx, "moe_place_kernel");
   };
   auto produce = [&](hipStream_t s, int nwg) -> tsg_status {
