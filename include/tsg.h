@@ -214,7 +214,8 @@ tsg_status tsg_kernel_ms(tsg_ctx* ctx, int which, float* ms);
  * of the workgroup.  kind / id: 1 AG copy unit (chunk<<24 | slab<<12 |
  * piece), 2 AG GEMM tile, 3 RS GEMM tile, 4 RS reduce tile, 5 MLP GEMM1
  * tile, 6 MLP GEMM2 tile (m_tile<<16 | n_tile for tiles), 7 MoE up tile,
- * 8 MoE down tile, 9 MoE combine unit (row_block<<16 | n_tile). */
+ * 8 MoE down tile, 9 MoE combine unit (row_block<<16 | n_tile), 10 MoE
+ * gather-side up tile (row_block<<16 | n_tile). */
 tsg_status tsg_timeline(tsg_ctx* ctx, uint64_t* out, size_t cap, size_t* n);
 
 /* ------------------------------------------------------------- AG+GEMM */
@@ -357,6 +358,63 @@ tsg_status moe_expert_combine(tsg_ctx* ctx, const void* x, const int32_t* topk_i
                               int T, int H, int I, int E, int k,
                               const tsg_opts* opts, int mode, void* stream);
 
+/* ------------------------------------------------- AllGather + MoE gather */
+
+/* AllGather + Gather + grouped GEMM: the gather side of a tensor-parallel MoE
+ * layer at one rank's share ([TL] section 5, Figure 5: AllGather + MoE,
+ * whose dynamic routing makes the shape, rank and channel mapping of every
+ * tile a lookup table filled at run time, through which the tile's loads
+ * gather its tokens; [TL] section 7.2, MoE layer, first part: AG + Gather +
+ * GroupGEMM; [TD] section 3.2, Algorithm 2: pull-mode AllGather, local chunk
+ * first).
+ *
+ * The T tokens are sharded over R ranks along T: chunk c = tokens
+ * [c T/R, (c+1) T/R) belongs to rank c.  A copy standing in for the peers'
+ * arrival (the AllGather + GEMM path's copy units: column slabs of each
+ * chunk, the local chunk first, then the peers in arrival order, each slab
+ * signalled once complete) fills x_full.  For every routed pair
+ * p = t*k + s with e = topk_ids[t][s]:
+ *     h[p] = bf16(SiLU(x_full[t] * w_up[e]))
+ * (fp32 accumulation, SiLU(u) = u / (1 + e^-u), rounded to nearest even).
+ * Row tiles of the grouped GEMM are 256 rows of one expert's pairs (each
+ * expert's rows padded to a multiple of 256).  Every row block's set of
+ * source ranks is filled into a lookup table by the routing, and its tiles
+ * wait for exactly those chunks' signals; the blocks are visited in order
+ * of the arrival position of the last chunk they need (ties by block), the
+ * runtime counterpart of the AllGather GEMM's swizzle.
+ *
+ *   x_local  bf16 [T/R x H]             this rank's tokens (input)
+ *   x_peers  bf16 [(R-1) x T/R x H]     the other ranks' tokens, ascending
+ *                                       rank order skipping `rank` (input)
+ *   x_full   bf16 [T x H]               gathered tokens (output)
+ *   topk_ids int32 [T x k]              routing of all T tokens (input)
+ *   w_up     bf16 [E x H x I]           this rank's shard of every expert's
+ *                                       up projection (input)
+ *   h        bf16 [T*k x I]             output, in pair order
+ *   expert_counts int32 [E], sorted_ids int32 [T*k]: outputs, as in
+ *            moe_expert_combine
+ *   workspace: at least tsg_workspace_bytes(TSG_OP_MOE_AG, {T, H, I, E, k})
+ *            bytes, caller-owned, contents undefined on entry and exit.
+ *   arrival_order: as in gemm_ag_overlap.
+ * Modes: OVERLAP runs one persistent kernel whose workgroups take the copy
+ * units first and then the tiles from one queue (a tile only waits for
+ * copy units, all taken before it by workgroups that never wait); SERIAL
+ * runs the copy, then the tiles; COMPUTE_ONLY the tiles without waits
+ * (x_full must hold the tokens already); COMM_ONLY the copy alone.  Shared
+ * CUs only (aux_cus > 0: TSG_E_UNSUPPORTED).  comm_tile sets the slab width
+ * (default 2048 columns); debug_skip_mask bit c withholds chunk c's signals.
+ * Constraints: k == 2, T * k <= 65535, 1 <= R <= 32, T % R == 0,
+ * 1 <= E <= 256, H % 8 == 0, I % 8 == 0, H, I >= 8, 16-byte aligned
+ * pointers.  Expert ids outside [0, E) are dropped and reported by
+ * tsg_check as TSG_E_INVALID. */
+tsg_status moe_ag_group_gemm(tsg_ctx* ctx, const void* x_local, const void* x_peers, void* x_full,
+                             const int32_t* topk_ids, const void* w_up, void* h,
+                             int32_t* expert_counts, int32_t* sorted_ids,
+                             void* workspace, size_t workspace_bytes,
+                             int T, int H, int I, int E, int k, int R, int rank,
+                             const int* arrival_order, const tsg_opts* opts, int mode,
+                             void* stream);
+
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc):
  * moe_expert_combine with the workspace taken from the library's own static
@@ -378,10 +436,10 @@ tsg_status moe_expert_combine_noalloc(tsg_ctx* ctx, const void* x, const int32_t
                                       int T, int H, int I, int E, int k,
                                       const tsg_opts* opts, int mode, void* stream);
 
-enum { TSG_OP_AG = 0, TSG_OP_RS = 1, TSG_OP_MLP2 = 2, TSG_OP_MOE = 3 };
+enum { TSG_OP_AG = 0, TSG_OP_RS = 1, TSG_OP_MLP2 = 2, TSG_OP_MOE = 3, TSG_OP_MOE_AG = 4 };
 
-/* Workspace bytes an op needs for `dims` (TSG_OP_MOE: {T, H, I, E, k});
- * 0 for ops that need none or for invalid dims. */
+/* Workspace bytes an op needs for `dims` (TSG_OP_MOE and TSG_OP_MOE_AG:
+ * {T, H, I, E, k}); 0 for ops that need none or for invalid dims. */
 size_t tsg_workspace_bytes(int op, const int64_t* dims);
 
 /* Layout of the MoE workspace for dims = {T, H, I, E, k}, so that the

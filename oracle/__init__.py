@@ -38,5 +38,6 @@ from .paths import (  # noqa: F401
     moe_route,
     moe_tile_table,
     moe_expert_combine,
+    moe_ag_up,
     overlap_ratio,
 )

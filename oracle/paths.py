@@ -203,6 +203,38 @@ def moe_expert_combine(x_bits, topk_ids, topk_w, w_up_bits, w_down_bits):
     return dict(out=out, h=h_bits, y=y, scale=scale, counts=counts, sorted_ids=sorted_ids)
 
 
+def moe_ag_up(a_local, a_peers, R: int, rank: int, topk_ids, w_up_bits):
+    """Gather side of a tensor-parallel MoE layer ([TL] section 5, AllGather
+    + MoE; [TL] section 7.2, the MoE layer's first part, AG + Gather +
+    GroupGEMM).  The token chunks of all R ranks are gathered along the token
+    dimension (ag_gather, [TD] Algorithm 2); then every routed pair p = t*k +
+    s with e = topk_ids[t, s] takes
+
+        h[p] = bf16(SiLU(x_t W_up[e])),
+
+    the gathered token's row times this rank's shard of the expert's up
+    projection, rounded once to bf16.  Returns dict(x_full bits, h bits
+    [T*k x I] in pair order, scale [T*k x I] = sum_k |x_tk W_up[e]_kj| for the
+    error bound, counts, sorted_ids)."""
+    x_full = ag_gather(a_local, a_peers, R, rank)
+    x = bf16_to_f64(x_full)
+    ids = np.asarray(topk_ids, dtype=np.int64)
+    T, k = ids.shape
+    E, _, I = w_up_bits.shape
+    counts, offsets, sorted_ids = moe_route(ids, E)
+    h = np.zeros((T * k, I), dtype=np.uint16)
+    scale = np.zeros((T * k, I), dtype=np.float64)
+    for e in range(E):
+        pairs = sorted_ids[offsets[e]:offsets[e + 1]].astype(np.int64)
+        if pairs.size == 0:
+            continue
+        xe = x[pairs // k]
+        we = bf16_to_f64(w_up_bits[e])
+        h[pairs] = f64_to_bf16_bits(silu(xe @ we))
+        scale[pairs] = np.abs(xe) @ np.abs(we)
+    return dict(x_full=x_full, h=h, scale=scale, counts=counts, sorted_ids=sorted_ids)
+
+
 def overlap_ratio(comp_only: float, comm_only: float, overlap: float) -> float:
     """Fraction of communication time hidden by overlap ([TL] section 7.2):
     (comp_only + comm_only - overlap) / comm_only."""

@@ -255,3 +255,47 @@ def test_overlap_ratio_closed_form():
     assert oracle.overlap_ratio(10.0, 4.0, 12.0) == 0.5
     assert oracle.overlap_ratio(10.0, 4.0, 14.0) == 0.0
     assert oracle.overlap_ratio(10.0, 4.0, 10.0) == 1.0
+
+
+def test_moe_ag_up_brute_force_tiny():
+    # the gather side written out with Python loops: the gathered token rows
+    # are the ranks' chunks in rank order, and each pair's h is the rounded
+    # SiLU of its token row times its expert's up projection (math.exp)
+    R, rank = 3, 1
+    T, H, I, E, k = 6, 8, 5, 3, 2
+    inp = moe_inputs(T=T, H=H, I=I, E=E, k=k, seed=61)
+    loc, peers = split_chunks(inp["x"], R, rank)
+    res = oracle.moe_ag_up(loc, peers, R, rank, inp["topk_ids"], inp["w_up"])
+    assert np.array_equal(res["x_full"], inp["x"])
+    x = bf16_to_f64(inp["x"])
+    w = bf16_to_f64(inp["w_up"])
+    for t in range(T):
+        for s in range(k):
+            e = int(inp["topk_ids"][t, s])
+            for j in range(I):
+                u = 0.0
+                a = 0.0
+                for kk in range(H):
+                    u += x[t, kk] * w[e, kk, j]
+                    a += abs(x[t, kk] * w[e, kk, j])
+                want = _bits([u / (1.0 + math.exp(-u))])[0] if abs(u) < 80 else None
+                got = int(res["h"][t * k + s, j])
+                if want is not None:
+                    # one rounding of the float64 value: equal unless the two
+                    # sums straddle a bf16 rounding boundary
+                    assert abs(bf16_to_f64(np.uint16(got)) - bf16_to_f64(np.uint16(want))) <= \
+                        2.0 ** (math.frexp(abs(u / (1.0 + math.exp(-u))) or 1.0)[1] - 8), (t, s, j)
+                assert math.isclose(res["scale"][t * k + s, j], a, rel_tol=1e-12, abs_tol=1e-300)
+
+
+def test_moe_ag_up_matches_expert_path_and_rank_invariance():
+    # the same h as the expert-compute path's for the gathered tokens, and
+    # the same result whatever rank gathers
+    R = 4
+    inp = moe_inputs(T=32, H=16, I=24, E=5, k=2, seed=62)
+    ref = oracle.moe_expert_combine(inp["x"], inp["topk_ids"], inp["topk_w"], inp["w_up"], inp["w_down"])
+    for rank in range(R):
+        loc, peers = split_chunks(inp["x"], R, rank)
+        res = oracle.moe_ag_up(loc, peers, R, rank, inp["topk_ids"], inp["w_up"])
+        assert np.array_equal(res["h"], ref["h"])
+        assert np.array_equal(res["counts"], ref["counts"]) and np.array_equal(res["sorted_ids"], ref["sorted_ids"])

@@ -33,14 +33,14 @@ OVERLAP, SERIAL, COMPUTE_ONLY, COMM_ONLY = 0, 1, 2, 3
 # dtypes
 F32, BF16 = 0, 1
 # ops (workspace sizing)
-OP_AG, OP_RS, OP_MLP2, OP_MOE = 0, 1, 2, 3
+OP_AG, OP_RS, OP_MLP2, OP_MOE, OP_MOE_AG = 0, 1, 2, 3, 4
 
 EXPORTS = (
     "tsg_ctx_create", "tsg_ctx_destroy", "tsg_last_error", "tsg_check", "tsg_device_info",
     "tsg_enable_kernel_timing", "tsg_kernel_ms", "tsg_timeline", "tsg_workspace_bytes",
     "tsg_moe_workspace_layout",
     "gemm_ag_overlap", "gemm_rs_overlap", "mlp2_pipelined", "moe_expert_combine",
-    "moe_expert_combine_noalloc",
+    "moe_expert_combine_noalloc", "moe_ag_group_gemm",
 )
 MOE_NOALLOC_BYTES = 64 << 20   # the static workspace of moe_expert_combine_noalloc, per GPU
 
@@ -88,11 +88,13 @@ _lib.gemm_rs_overlap.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _
 _lib.mlp2_pipelined.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _P(Opts), _i, _vp]
 _lib.moe_expert_combine.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                                     _i, _i, _i, _i, _i, _P(Opts), _i, _vp]
+_lib.moe_ag_group_gemm.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
+                                   _i, _i, _i, _i, _i, _i, _i, _P(_i), _P(Opts), _i, _vp]
 _lib.moe_expert_combine_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                             _i, _i, _i, _i, _i, _P(Opts), _i, _vp]
 for _f in ("tsg_ctx_create", "tsg_check", "tsg_device_info", "tsg_enable_kernel_timing", "tsg_kernel_ms",
            "tsg_timeline", "tsg_moe_workspace_layout", "gemm_ag_overlap", "gemm_rs_overlap", "mlp2_pipelined",
-           "moe_expert_combine", "moe_expert_combine_noalloc"):
+           "moe_expert_combine", "moe_expert_combine_noalloc", "moe_ag_group_gemm"):
     getattr(_lib, _f).restype = _i
 
 
@@ -269,4 +271,17 @@ def moe_expert_combine_noalloc(ctx: Context, x, topk_ids, topk_w, w_up, w_down, 
     st = _lib.moe_expert_combine_noalloc(ctx.handle, _ptr(x), _ptr(topk_ids), _ptr(topk_w), _ptr(w_up),
                                          _ptr(w_down), _ptr(out), _ptr(expert_counts), _ptr(sorted_ids),
                                          T, H, I, E, k, _opts(opts), mode, _stream(stream))
+    return ctx._raise(st) if raise_on_error else st
+
+
+def moe_ag_group_gemm(ctx: Context, x_local, x_peers, x_full, topk_ids, w_up, h, expert_counts, sorted_ids,
+                      workspace, workspace_bytes_, T, H, I, E, k, R, rank, arrival_order=None, opts=None,
+                      mode=OVERLAP, stream=None, raise_on_error=True):
+    order = None
+    if arrival_order is not None:
+        order = (_i * len(arrival_order))(*arrival_order)
+    st = _lib.moe_ag_group_gemm(ctx.handle, _ptr(x_local), _ptr(x_peers), _ptr(x_full), _ptr(topk_ids),
+                                _ptr(w_up), _ptr(h), _ptr(expert_counts), _ptr(sorted_ids), _ptr(workspace),
+                                workspace_bytes_, T, H, I, E, k, R, rank, order, _opts(opts), mode,
+                                _stream(stream))
     return ctx._raise(st) if raise_on_error else st

@@ -366,6 +366,7 @@ tsg_status tsg_timeline(tsg_ctx* ctx, uint64_t* out, size_t cap, size_t* n) {
 
 size_t tsg_workspace_bytes(int op, const int64_t* dims) {
   if (op == TSG_OP_MOE && dims) return tsg_moe_workspace(dims[0], dims[1], dims[2], dims[3], dims[4]);
+  if (op == TSG_OP_MOE_AG && dims) return tsg_moe_ag_workspace(dims[0], dims[1], dims[2], dims[3], dims[4]);
   return 0;
 }
 
@@ -409,6 +410,17 @@ tsg_status moe_expert_combine(tsg_ctx* ctx, const void* x, const int32_t* topk_i
   ctx->err.clear();
   return tsg_op_moe(ctx, x, topk_ids, topk_w, w_up, w_down, out, expert_counts, sorted_ids,
                     workspace, workspace_bytes, T, H, I, E, k, opts, mode, stream, false);
+}
+
+tsg_status moe_ag_group_gemm(tsg_ctx* ctx, const void* x_local, const void* x_peers, void* x_full,
+                             const int32_t* topk_ids, const void* w_up, void* h, int32_t* expert_counts,
+                             int32_t* sorted_ids, void* workspace, size_t workspace_bytes, int T, int H, int I,
+                             int E, int k, int R, int rank, const int* arrival_order, const tsg_opts* opts,
+                             int mode, void* stream) {
+  if (!ctx) return TSG_E_INVALID;
+  ctx->err.clear();
+  return tsg_op_moe_ag(ctx, x_local, x_peers, x_full, topk_ids, w_up, h, expert_counts, sorted_ids, workspace,
+                       workspace_bytes, T, H, I, E, k, R, rank, arrival_order, opts, mode, stream);
 }
 
 tsg_status moe_expert_combine_noalloc(tsg_ctx* ctx, const void* x, const int32_t* topk_ids,

@@ -127,16 +127,20 @@ struct ARowsLinear {
   __device__ __forceinline__ int64_t stand_in() const { return (int64_t)(M - 1) * ld; }
 };
 
-// Gathered rows: idx[r] is the source row index (or < 0 for no row).
+// Gathered rows: idx[r] is the source row index (or < 0 for no row).  Rows
+// with no source read row `stand` of the operand instead (their results are
+// never stored); when the operand is written while the tile runs, `stand`
+// must be a row the tile waited for.
 struct ARowsGather {
   const uint16_t* base;
   int64_t ld;
   const int* idx;
+  int stand = 0;
   __device__ __forceinline__ int64_t row(int r) const {
     const int g = idx[r];
     return g >= 0 ? (int64_t)g * ld : (int64_t)-1;
   }
-  __device__ __forceinline__ int64_t stand_in() const { return 0; }
+  __device__ __forceinline__ int64_t stand_in() const { return (int64_t)stand * ld; }
 };
 
 // Called with the first K column k0 of every step, in increasing order, just
@@ -600,20 +604,22 @@ struct GemmTile {
   // LDS_BYTES is the size of the caller's LDS array.  COHERENT: the stores go
   // through to the coherence point (store_coherent), for data a consumer in
   // the same kernel reads after a signal.
-  template <int LDS_BYTES, bool COHERENT, class F>
-  __device__ __forceinline__ static void store_bf16_staged(const Acc& acc, char* lds, uint16_t* C,
-                                                          int64_t ldc, int rows, int cols, F&& f) {
-    constexpr int PAD = Cfg::NW * Cfg::WTM * (Cfg::WTN * 2 + 32) <= LDS_BYTES ? 32 : 0;
-    constexpr int STRIDE = Cfg::WTN * 2 + PAD;
+  // Row stride of a wave's staging region: padded by 32 bytes when the LDS
+  // allows, so that the two row groups of a fragment write different banks.
+  template <int LDS_BYTES>
+  static constexpr int stage_stride() {
+    return Cfg::WTN * 2 + (Cfg::NW * Cfg::WTM * (Cfg::WTN * 2 + 32) <= LDS_BYTES ? 32 : 0);
+  }
+
+  // Rounds f(value) of this wave's results to bf16 into its own LDS region
+  // (row-major, stage_stride bytes per row) and returns the region, after
+  // the wave's writes have completed.
+  template <int LDS_BYTES, class F>
+  __device__ __forceinline__ static char* stage_bf16(const Acc& acc, char* lds, F&& f) {
+    constexpr int STRIDE = stage_stride<LDS_BYTES>();
     static_assert(Cfg::NW * Cfg::WTM * STRIDE <= LDS_BYTES, "staged tile does not fit the LDS");
-    constexpr int VPR = Cfg::WTN / 8;          // 16-byte pieces per row
-    constexpr int TOT = Cfg::WTM * VPR;
-    static_assert(TOT % 64 == 0, "pieces must fill whole wave passes");
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm0 = (wave / Cfg::WN) * Cfg::WTM;
-    const int wn0 = (wave % Cfg::WN) * Cfg::WTN;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
     char* reg = lds + wave * (Cfg::WTM * STRIDE);
     char* wr = Cfg::MF == 32 ? reg + ((lane >> 5) * 4) * STRIDE + (lane & 31) * 2
                              : reg + ((lane >> 4) * 4) * STRIDE + (lane & 15) * 2;
@@ -634,6 +640,49 @@ struct GemmTile {
     // The region is this wave's alone: its LDS writes complete before its
     // reads, and the clobber keeps the compiler from reordering them.
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    return reg;
+  }
+
+  // bf16 epilogue with scattered rows: tile row r is stored to row
+  // dst_row[r] of C (ldc elements per row; the row is skipped when
+  // dst_row[r] < 0), its first `cols` columns (a multiple of 8) as 16-byte
+  // pieces.  Called by every thread after the K loop, whose last barrier
+  // freed the LDS.
+  template <int LDS_BYTES, class F>
+  __device__ __forceinline__ static void store_bf16_rows(const Acc& acc, char* lds, uint16_t* C, int64_t ldc,
+                                                        const int* __restrict__ dst_row, int cols, F&& f) {
+    constexpr int STRIDE = stage_stride<LDS_BYTES>();
+    constexpr int VPR = Cfg::WTN / 8;
+    constexpr int TOT = Cfg::WTM * VPR;
+    static_assert(TOT % 64 == 0, "pieces must fill whole wave passes");
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wm0 = (wave / Cfg::WN) * Cfg::WTM;
+    const int wn0 = (wave % Cfg::WN) * Cfg::WTN;
+    const char* reg = stage_bf16<LDS_BYTES>(acc, lds, f);
+#pragma unroll 4
+    for (int it = 0; it < TOT / 64; ++it) {
+      const int idx = it * 64 + lane;
+      const int r = idx / VPR, q = idx - r * VPR;
+      const u32x4_t v = *(const u32x4_t*)(reg + r * STRIDE + q * 16);
+      const int dr = dst_row[wm0 + r];
+      if (dr >= 0 && wn0 + q * 8 < cols) *(u32x4_t*)(C + (int64_t)dr * ldc + wn0 + q * 8) = v;
+    }
+  }
+
+  template <int LDS_BYTES, bool COHERENT, class F>
+  __device__ __forceinline__ static void store_bf16_staged(const Acc& acc, char* lds, uint16_t* C,
+                                                          int64_t ldc, int rows, int cols, F&& f) {
+    constexpr int STRIDE = stage_stride<LDS_BYTES>();
+    constexpr int VPR = Cfg::WTN / 8;          // 16-byte pieces per row
+    constexpr int TOT = Cfg::WTM * VPR;
+    static_assert(TOT % 64 == 0, "pieces must fill whole wave passes");
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm0 = (wave / Cfg::WN) * Cfg::WTM;
+    const int wn0 = (wave % Cfg::WN) * Cfg::WTN;
+    const char* reg = stage_bf16<LDS_BYTES>(acc, lds, f);
     uint16_t* dst0 = C + (int64_t)wm0 * ldc + wn0;
     if (COHERENT) {
       // 8-byte pieces: each store instruction of the wave then writes

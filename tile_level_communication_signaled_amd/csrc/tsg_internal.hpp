@@ -131,6 +131,10 @@ tsg_status tsg_op_rs(tsg_ctx*, const void*, const void*, float*, const float*, f
                      int, int, int, const tsg_opts*, int, void*);
 tsg_status tsg_op_mlp2(tsg_ctx*, const void*, const void*, void*, const void*, float*, int, int,
                        int, int, const tsg_opts*, int, void*);
+tsg_status tsg_op_moe_ag(tsg_ctx*, const void*, const void*, void*, const int32_t*, const void*, void*, int32_t*,
+                         int32_t*, void*, size_t, int, int, int, int, int, int, int, const int*,
+                         const tsg_opts*, int, void*);
+size_t tsg_moe_ag_workspace(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k);
 tsg_status tsg_op_moe(tsg_ctx*, const void*, const int32_t*, const float*, const void*,
                       const void*, float*, int32_t*, int32_t*, void*, size_t, int, int, int, int,
                       int, const tsg_opts*, int, void*, bool noalloc);
@@ -138,5 +142,10 @@ tsg_status tsg_op_moe(tsg_ctx*, const void*, const int32_t*, const float*, const
 // workspace and stores it in ctx->d_noalloc_ws; ctx->device must be current.
 tsg_status tsg_moe_scratch_init(tsg_ctx* ctx);
 size_t tsg_moe_workspace(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k);
+// Piece plan of the AllGather copy (tsg_copy.hpp): pieces per channel of the
+// head slabs and the body (np[5]), first unit of each (ustart[5]) and the
+// unit count; false if the copy's offsets or unit count would overflow.
+bool copy_plan(int R, int C, int chunk_rows, int K, int n_slab, int vpr_log2, int nwg, int* np, int* ustart,
+               int64_t* n_units);
 bool tsg_moe_layout_fields(const int64_t* dims, int64_t* out, int n);
 tsg_status tsg_probe_xcd(tsg_ctx* ctx);
