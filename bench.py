@@ -51,7 +51,7 @@ def _parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--headline-only", action="store_true",
                    help="time only the headline overlap steps (for kernel traces)")
-    p.add_argument("--trace-path", choices=["gemm_rs", "mlp2", "moe", "moe_bf16_staging", "ag_copy_engine"],
+    p.add_argument("--trace-path", choices=["gemm_rs", "mlp2", "moe", "moe_bf16_staging", "moe_ag", "ag_copy_engine"],
                    help="time only this path's overlap steps (for kernel traces of that path), print one "
                         "JSON line and exit")
     p.add_argument("--counters", action="store_true",
@@ -98,8 +98,8 @@ CALIB_BYTES = 1 << 30   # the plain device copy that --counters runs: 1 GiB read
 
 
 KERNELS = ("ag_gemm_kernel", "ag_copy_kernel", "rs_gemm_kernel", "rs_reduce_kernel", "mlp_gemm1_kernel",
-           "mlp_gemm2_kernel", "moe_route_kernel", "moe_place_kernel", "moe_producer_kernel",
-           "moe_combine_kernel")
+           "mlp_gemm2_kernel", "mlp_fused_kernel", "moe_count_kernel", "moe_place_kernel", "moe_producer_kernel",
+           "moe_combine_kernel", "moe_ag_order_kernel", "moe_ag_kernel")
 
 
 def summarize_counters(fetch_csv: str, write_csv: str, out_path: str = TRAFFIC) -> dict:
@@ -421,6 +421,24 @@ def _other_paths(torch, tsg, ctx):
     moe_bytes = T * k * Hh * 2 + 2 * E * Hh * I * 2 + 2 * T * k * I * 2 + 2 * T * k * Hh * 4 + T * Hh * 4
     out["moe"] = (moe_fn, moe_flops, moe_bytes, (tsg.OVERLAP, tsg.SERIAL, tsg.COMPUTE_ONLY, tsg.COMM_ONLY))
 
+    # the gather side of the same MoE layer at tensor parallelism 8: the
+    # 4096 tokens gathered from 8 ranks of 512, then gathered per expert and
+    # multiplied by this rank's up-projection shards, SiLU, h in pair order
+    from synth.gen import split_chunks
+    R6 = 8
+    loc6, peers6 = split_chunks(inp["x"], R6, 0)
+    dl6, dp6 = dv(loc6), dv(peers6)
+    full6 = torch.empty((T, Hh), dtype=torch.int16, device="cuda")
+    h6 = torch.empty((T * k, I), dtype=torch.int16, device="cuda")
+    wsb6 = tsg.workspace_bytes(tsg.OP_MOE_AG, [T, Hh, I, E, k])
+    ws6 = torch.empty((wsb6,), dtype=torch.uint8, device="cuda")
+    moe_ag_fn = lambda i, mode, opts=None: tsg.moe_ag_group_gemm(ctx, dl6, dp6, full6, ids, wu, h6, cnt, srt, ws6,
+                                                                 wsb6, T, Hh, I, E, k, R6, 0, opts=opts, mode=mode)
+    moe_ag_flops = 2.0 * T * k * Hh * I
+    moe_ag_bytes = 3 * T * Hh * 2 + E * Hh * I * 2 + T * k * I * 2
+    out["moe_ag"] = (moe_ag_fn, moe_ag_flops, moe_ag_bytes,
+                     (tsg.OVERLAP, tsg.SERIAL, tsg.COMPUTE_ONLY, tsg.COMM_ONLY))
+
     # the same MoE workload with the y staging in bf16 (stage_dtype): the
     # staging round trip moves half the bytes
     def moe_bf16_fn(i, mode, opts=None):
@@ -464,6 +482,7 @@ TL_KINDS = {"ag_gemm": ((1, "copy units"), (2, "GEMM tiles")),
             "gemm_rs": ((3, "GEMM tiles"), (4, "reduce units")),
             "mlp2": ((5, "GEMM1 tiles"), (6, "GEMM2 tiles")),
             "moe": ((7, "up tiles"), (8, "down tiles"), (9, "combine units")),
+            "moe_ag": ((10, "up tiles"),),
             "moe_bf16_staging": ((7, "up tiles"), (8, "down tiles"), (9, "combine units"))}
 
 

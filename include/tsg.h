@@ -215,7 +215,8 @@ tsg_status tsg_kernel_ms(tsg_ctx* ctx, int which, float* ms);
  * piece), 2 AG GEMM tile, 3 RS GEMM tile, 4 RS reduce tile, 5 MLP GEMM1
  * tile, 6 MLP GEMM2 tile (m_tile<<16 | n_tile for tiles), 7 MoE up tile,
  * 8 MoE down tile, 9 MoE combine unit (row_block<<16 | n_tile), 10 MoE
- * gather-side up tile (row_block<<16 | n_tile). */
+ * gather-side up tile (row_block<<16 | n_tile), 11 attention tile
+ * (head<<16 | query block). */
 tsg_status tsg_timeline(tsg_ctx* ctx, uint64_t* out, size_t cap, size_t* n);
 
 /* ------------------------------------------------------------- AG+GEMM */
@@ -414,6 +415,50 @@ tsg_status moe_ag_group_gemm(tsg_ctx* ctx, const void* x_local, const void* x_pe
                              int T, int H, int I, int E, int k, int R, int rank,
                              const int* arrival_order, const tsg_opts* opts, int mode,
                              void* stream);
+
+/* ------------------------------------------------ AllGather KV + attention */
+
+/* AllGather of the key/value context + self-attention, sequence parallel,
+ * one rank's share ([TL] section 2.1: the context is sharded across ranks
+ * and gathered before the attention; [TL] section 5, Figure 6: AllGather
+ * KV + self-attention, the communication tile being one rank's share of the
+ * sequence and the computation tile a different one, with tile-centric
+ * mapping keeping the barriers between them; [TL] section 7.2: two batched
+ * GEMMs and a softmax fused as in Flash-Attention).
+ *
+ * The S tokens are sharded over R ranks along the sequence: chunk c = rows
+ * [c S/R, (c+1) S/R) belongs to rank c.  A copy standing in for the peers'
+ * arrival (the AllGather copy's units over K, then V, each viewed as an
+ * [S x heads*head_dim] matrix: column slabs of comm_tile columns, default
+ * one head, of each chunk; peers in arrival order, the own chunk last; each
+ * (chunk, slab) signalled once complete) fills k_full and v_full.  For
+ * every head h and local query q (no mask):
+ *     out[q, h] = sum_j softmax_j(q[q, h] . K[j, h] / sqrt(head_dim)) V[j, h]
+ * over all S keys j, with fp32 scores and accumulators, probabilities
+ * rounded to bf16 for the second product, and out rounded to bf16.  A tile
+ * (one head, 128 queries) takes the chunks in arrival order, its own chunk
+ * first, read in place from k_local / v_local; before a peer chunk it waits
+ * for the K and V signals of the slabs holding its head.
+ *
+ *   q        bf16 [S/R x heads x head_dim]   this rank's queries (input)
+ *   k_local, v_local  bf16 [S/R x heads x head_dim]   (input)
+ *   k_peers, v_peers  bf16 [(R-1) x S/R x heads x head_dim], ascending rank
+ *            order skipping `rank` (input)
+ *   k_full, v_full    bf16 [S x heads x head_dim]   gathered (output)
+ *   out      bf16 [S/R x heads x head_dim]   (output)
+ *   arrival_order: as in gemm_ag_overlap.
+ * Modes: OVERLAP runs one persistent kernel whose workgroups take the copy
+ * units first and then the tiles from one queue; SERIAL the copy, then the
+ * tiles; COMPUTE_ONLY the tiles without waits (k_full / v_full must hold
+ * the context already); COMM_ONLY the copy alone.  Shared CUs only (aux_cus
+ * > 0: TSG_E_UNSUPPORTED).  debug_skip_mask bit c withholds chunk c's
+ * signals.  Constraints: head_dim == 128 (else TSG_E_UNSUPPORTED),
+ * 1 <= R <= 32, S a positive multiple of 64 R, heads >= 1, comm_tile a power
+ * of two in [64, 2048] or 0, 16-byte aligned pointers. */
+tsg_status ag_kv_attention(tsg_ctx* ctx, const void* q, const void* k_local, const void* k_peers,
+                           const void* v_local, const void* v_peers, void* k_full, void* v_full,
+                           void* out, int S, int heads, int head_dim, int R, int rank,
+                           const int* arrival_order, const tsg_opts* opts, int mode, void* stream);
 
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc):

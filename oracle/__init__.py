@@ -39,5 +39,7 @@ from .paths import (  # noqa: F401
     moe_tile_table,
     moe_expert_combine,
     moe_ag_up,
+    attention,
+    ag_kv_attention,
     overlap_ratio,
 )

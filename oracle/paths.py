@@ -235,6 +235,44 @@ def moe_ag_up(a_local, a_peers, R: int, rank: int, topk_ids, w_up_bits):
     return dict(x_full=x_full, h=h, scale=scale, counts=counts, sorted_ids=sorted_ids)
 
 
+def attention(q_bits, k_bits, v_bits):
+    """Self-attention of queries q [Sq x heads x D] over keys and values
+    [S x heads x D] (bf16 bits), per head, with no mask ([TL] section 7.2: two
+    batched GEMMs and a softmax): out[i, h] = sum_j P_ij V[j, h] with
+    P_ij = exp(s_ij - max_j s_ij) / sum_j exp(s_ij - max_j s_ij) and
+    s_ij = q[i, h] . K[j, h] / sqrt(D).  Returns dict(out float64
+    [Sq x heads x D], pv_abs = sum_j P_ij |V[j, h]| for the error bound,
+    qk_abs_max = max_j sum_d |q[i, h, d] K[j, h, d]| per (i, h))."""
+    q = bf16_to_f64(q_bits)
+    k = bf16_to_f64(k_bits)
+    v = bf16_to_f64(v_bits)
+    Sq, H, D = q.shape
+    out = np.empty((Sq, H, D))
+    pv_abs = np.empty((Sq, H, D))
+    qk_abs_max = np.empty((Sq, H))
+    for h in range(H):
+        s = (q[:, h, :] @ k[:, h, :].T) / np.sqrt(D)
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        p = p / p.sum(axis=1, keepdims=True)
+        out[:, h, :] = p @ v[:, h, :]
+        pv_abs[:, h, :] = p @ np.abs(v[:, h, :])
+        qk_abs_max[:, h] = (np.abs(q[:, h, :]) @ np.abs(k[:, h, :]).T).max(axis=1)
+    return dict(out=out, pv_abs=pv_abs, qk_abs_max=qk_abs_max)
+
+
+def ag_kv_attention(q_bits, k_local, k_peers, v_local, v_peers, R: int, rank: int):
+    """Sequence-parallel self-attention of one rank ([TL] section 2.1; [TL]
+    section 5, AllGather KV + self-attention): the key and value shards of
+    all R ranks are gathered along the sequence (ag_gather, [TD] Algorithm
+    2), then this rank's queries attend over the whole gathered context.
+    Returns dict(k_full, v_full bits, and attention()'s fields)."""
+    k_full = ag_gather(k_local, k_peers, R, rank)
+    v_full = ag_gather(v_local, v_peers, R, rank)
+    res = attention(q_bits, k_full, v_full)
+    res.update(k_full=k_full, v_full=v_full)
+    return res
+
+
 def overlap_ratio(comp_only: float, comm_only: float, overlap: float) -> float:
     """Fraction of communication time hidden by overlap ([TL] section 7.2):
     (comp_only + comm_only - overlap) / comm_only."""

@@ -299,3 +299,47 @@ def test_moe_ag_up_matches_expert_path_and_rank_invariance():
         res = oracle.moe_ag_up(loc, peers, R, rank, inp["topk_ids"], inp["w_up"])
         assert np.array_equal(res["h"], ref["h"])
         assert np.array_equal(res["counts"], ref["counts"]) and np.array_equal(res["sorted_ids"], ref["sorted_ids"])
+
+
+def test_attention_brute_force_tiny():
+    # softmax attention written out with Python loops and math.exp
+    rng = np.random.default_rng(63)
+    Sq, S, H, D = 3, 5, 2, 4
+    q = _bits(rng.standard_normal((Sq, H, D)))
+    k = _bits(rng.standard_normal((S, H, D)))
+    v = _bits(rng.standard_normal((S, H, D)))
+    res = oracle.attention(q, k, v)
+    qf, kf, vf = bf16_to_f64(q), bf16_to_f64(k), bf16_to_f64(v)
+    for i in range(Sq):
+        for h in range(H):
+            s = [sum(qf[i, h, d] * kf[j, h, d] for d in range(D)) / math.sqrt(D) for j in range(S)]
+            mx = max(s)
+            w = [math.exp(x - mx) for x in s]
+            tot = sum(w)
+            for d in range(D):
+                want = sum(w[j] / tot * vf[j, h, d] for j in range(S))
+                assert math.isclose(res["out"][i, h, d], want, rel_tol=1e-12, abs_tol=1e-14)
+                pv = sum(w[j] / tot * abs(vf[j, h, d]) for j in range(S))
+                assert math.isclose(res["pv_abs"][i, h, d], pv, rel_tol=1e-12, abs_tol=1e-14)
+
+
+def test_attention_special_cases_and_gather():
+    rng = np.random.default_rng(64)
+    S, H, D, R = 8, 2, 4, 4
+    q = _bits(rng.standard_normal((2, H, D)))
+    k = _bits(rng.standard_normal((S, H, D)))
+    v = _bits(rng.standard_normal((S, H, D)))
+    # one key: the output is its value row
+    one = oracle.attention(q, k[:1], v[:1])
+    assert np.allclose(one["out"], np.broadcast_to(bf16_to_f64(v[:1]), one["out"].shape), rtol=0, atol=0)
+    # zero queries: uniform weights, the mean of the value rows
+    z = oracle.attention(np.zeros_like(q), k, v)
+    assert np.allclose(z["out"], bf16_to_f64(v).mean(axis=0)[None], rtol=1e-14, atol=1e-15)
+    # the gathered context does not depend on the rank that gathers it
+    base = oracle.attention(q, k, v)["out"]
+    for rank in range(R):
+        kl, kp = split_chunks(k, R, rank)
+        vl, vp = split_chunks(v, R, rank)
+        res = oracle.ag_kv_attention(q, kl, kp, vl, vp, R, rank)
+        assert np.array_equal(res["k_full"], k) and np.array_equal(res["v_full"], v)
+        assert np.array_equal(res["out"], base)

@@ -40,7 +40,7 @@ EXPORTS = (
     "tsg_enable_kernel_timing", "tsg_kernel_ms", "tsg_timeline", "tsg_workspace_bytes",
     "tsg_moe_workspace_layout",
     "gemm_ag_overlap", "gemm_rs_overlap", "mlp2_pipelined", "moe_expert_combine",
-    "moe_expert_combine_noalloc", "moe_ag_group_gemm",
+    "moe_expert_combine_noalloc", "moe_ag_group_gemm", "ag_kv_attention",
 )
 MOE_NOALLOC_BYTES = 64 << 20   # the static workspace of moe_expert_combine_noalloc, per GPU
 
@@ -90,11 +90,13 @@ _lib.moe_expert_combine.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                     _i, _i, _i, _i, _i, _P(Opts), _i, _vp]
 _lib.moe_ag_group_gemm.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                                    _i, _i, _i, _i, _i, _i, _i, _P(_i), _P(Opts), _i, _vp]
+_lib.ag_kv_attention.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _P(_i),
+                                 _P(Opts), _i, _vp]
 _lib.moe_expert_combine_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                             _i, _i, _i, _i, _i, _P(Opts), _i, _vp]
 for _f in ("tsg_ctx_create", "tsg_check", "tsg_device_info", "tsg_enable_kernel_timing", "tsg_kernel_ms",
            "tsg_timeline", "tsg_moe_workspace_layout", "gemm_ag_overlap", "gemm_rs_overlap", "mlp2_pipelined",
-           "moe_expert_combine", "moe_expert_combine_noalloc", "moe_ag_group_gemm"):
+           "moe_expert_combine", "moe_expert_combine_noalloc", "moe_ag_group_gemm", "ag_kv_attention"):
     getattr(_lib, _f).restype = _i
 
 
@@ -284,4 +286,15 @@ def moe_ag_group_gemm(ctx: Context, x_local, x_peers, x_full, topk_ids, w_up, h,
                                 _ptr(w_up), _ptr(h), _ptr(expert_counts), _ptr(sorted_ids), _ptr(workspace),
                                 workspace_bytes_, T, H, I, E, k, R, rank, order, _opts(opts), mode,
                                 _stream(stream))
+    return ctx._raise(st) if raise_on_error else st
+
+
+def ag_kv_attention(ctx: Context, q, k_local, k_peers, v_local, v_peers, k_full, v_full, out, S, heads, head_dim,
+                    R, rank, arrival_order=None, opts=None, mode=OVERLAP, stream=None, raise_on_error=True):
+    order = None
+    if arrival_order is not None:
+        order = (_i * len(arrival_order))(*arrival_order)
+    st = _lib.ag_kv_attention(ctx.handle, _ptr(q), _ptr(k_local), _ptr(k_peers), _ptr(v_local), _ptr(v_peers),
+                              _ptr(k_full), _ptr(v_full), _ptr(out), S, heads, head_dim, R, rank, order,
+                              _opts(opts), mode, _stream(stream))
     return ctx._raise(st) if raise_on_error else st

@@ -423,6 +423,16 @@ tsg_status moe_ag_group_gemm(tsg_ctx* ctx, const void* x_local, const void* x_pe
                        workspace_bytes, T, H, I, E, k, R, rank, arrival_order, opts, mode, stream);
 }
 
+tsg_status ag_kv_attention(tsg_ctx* ctx, const void* q, const void* k_local, const void* k_peers,
+                           const void* v_local, const void* v_peers, void* k_full, void* v_full, void* out, int S,
+                           int heads, int head_dim, int R, int rank, const int* arrival_order,
+                           const tsg_opts* opts, int mode, void* stream) {
+  if (!ctx) return TSG_E_INVALID;
+  ctx->err.clear();
+  return tsg_op_attn(ctx, q, k_local, k_peers, v_local, v_peers, k_full, v_full, out, S, heads, head_dim, R, rank,
+                     arrival_order, opts, mode, stream);
+}
+
 tsg_status moe_expert_combine_noalloc(tsg_ctx* ctx, const void* x, const int32_t* topk_ids,
                                       const float* topk_w, const void* w_up, const void* w_down,
                                       float* out, int32_t* expert_counts, int32_t* sorted_ids, int T,

@@ -135,6 +135,8 @@ tsg_status tsg_op_moe_ag(tsg_ctx*, const void*, const void*, void*, const int32_
                          int32_t*, void*, size_t, int, int, int, int, int, int, int, const int*,
                          const tsg_opts*, int, void*);
 size_t tsg_moe_ag_workspace(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k);
+tsg_status tsg_op_attn(tsg_ctx*, const void*, const void*, const void*, const void*, const void*, void*, void*,
+                       void*, int, int, int, int, int, const int*, const tsg_opts*, int, void*);
 tsg_status tsg_op_moe(tsg_ctx*, const void*, const int32_t*, const float*, const void*,
                       const void*, float*, int32_t*, int32_t*, void*, size_t, int, int, int, int,
                       int, const tsg_opts*, int, void*, bool noalloc);
