@@ -51,7 +51,8 @@ def _parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--headline-only", action="store_true",
                    help="time only the headline overlap steps (for kernel traces)")
-    p.add_argument("--trace-path", choices=["gemm_rs", "mlp2", "moe", "moe_bf16_staging", "moe_ag", "ag_copy_engine"],
+    p.add_argument("--trace-path", choices=["gemm_rs", "mlp2", "moe", "moe_bf16_staging", "moe_ag", "ag_kv_attention",
+                                            "ag_copy_engine"],
                    help="time only this path's overlap steps (for kernel traces of that path), print one "
                         "JSON line and exit")
     p.add_argument("--counters", action="store_true",
@@ -99,7 +100,7 @@ CALIB_BYTES = 1 << 30   # the plain device copy that --counters runs: 1 GiB read
 
 KERNELS = ("ag_gemm_kernel", "ag_copy_kernel", "rs_gemm_kernel", "rs_reduce_kernel", "mlp_gemm1_kernel",
            "mlp_gemm2_kernel", "mlp_fused_kernel", "moe_count_kernel", "moe_place_kernel", "moe_producer_kernel",
-           "moe_combine_kernel", "moe_ag_order_kernel", "moe_ag_kernel")
+           "moe_combine_kernel", "moe_ag_order_kernel", "moe_ag_kernel", "ag_attn_kernel")
 
 
 def summarize_counters(fetch_csv: str, write_csv: str, out_path: str = TRAFFIC) -> dict:
@@ -439,6 +440,25 @@ def _other_paths(torch, tsg, ctx):
     out["moe_ag"] = (moe_ag_fn, moe_ag_flops, moe_ag_bytes,
                      (tsg.OVERLAP, tsg.SERIAL, tsg.COMPUTE_ONLY, tsg.COMM_ONLY))
 
+    # sequence-parallel self-attention with the KV context gathered: 16k
+    # tokens, 32 heads of 128, one rank's share of 8 (2048 queries)
+    S7, heads7, R7 = 16384, 32, 8
+    sl7 = S7 // R7
+    rng7 = np.random.default_rng(7)
+    mk7 = lambda shape: torch.from_numpy(rng7.standard_normal(shape, dtype=np.float32)).to(torch.bfloat16).cuda()
+    q7 = mk7((sl7, heads7, 128))
+    kl7, vl7 = mk7((sl7, heads7, 128)), mk7((sl7, heads7, 128))
+    kp7, vp7 = mk7((R7 - 1, sl7, heads7, 128)), mk7((R7 - 1, sl7, heads7, 128))
+    kf7 = torch.empty((S7, heads7, 128), dtype=torch.bfloat16, device="cuda")
+    vf7 = torch.empty_like(kf7)
+    o7 = torch.empty_like(q7)
+    attn_fn = lambda i, mode, opts=None: tsg.ag_kv_attention(ctx, q7, kl7, kp7, vl7, vp7, kf7, vf7, o7, S7, heads7,
+                                                             128, R7, 0, opts=opts, mode=mode)
+    attn_flops = 4.0 * sl7 * S7 * 128 * heads7
+    attn_bytes = 4 * S7 * heads7 * 128 * 2 + 2 * sl7 * heads7 * 128 * 2
+    out["ag_kv_attention"] = (attn_fn, attn_flops, attn_bytes,
+                              (tsg.OVERLAP, tsg.SERIAL, tsg.COMPUTE_ONLY, tsg.COMM_ONLY))
+
     # the same MoE workload with the y staging in bf16 (stage_dtype): the
     # staging round trip moves half the bytes
     def moe_bf16_fn(i, mode, opts=None):
@@ -483,6 +503,7 @@ TL_KINDS = {"ag_gemm": ((1, "copy units"), (2, "GEMM tiles")),
             "mlp2": ((5, "GEMM1 tiles"), (6, "GEMM2 tiles")),
             "moe": ((7, "up tiles"), (8, "down tiles"), (9, "combine units")),
             "moe_ag": ((10, "up tiles"),),
+            "ag_kv_attention": ((11, "attention tiles"),),
             "moe_bf16_staging": ((7, "up tiles"), (8, "down tiles"), (9, "combine units"))}
 
 

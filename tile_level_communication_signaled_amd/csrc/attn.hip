@@ -25,11 +25,12 @@
 // order, its own chunk first, read in place from k_local / v_local without
 // waiting; before a peer chunk it waits for the K and V signals of the slabs
 // holding its head's columns.  Inside a chunk, 64 keys at a time:
-//   S = Q K^T (v_mfma_f32_32x32x16_bf16; Q fragments in registers, K staged
-//   in LDS), online softmax per query row (running max and sum, exp2 of the
-//   scaled scores), P rounded to bf16 through a per-wave LDS region, then
-//   O += P V (V staged in LDS and read with transpose reads).  The next
-//   block's K and V are loaded into registers while this one is computed.
+//   S^T = K Q^T (v_mfma_f32_32x32x16_bf16; Q fragments in registers, K
+//   staged in LDS), online softmax per query (running max and sum, exp2 of
+//   the scaled scores), then O^T += V^T P^T with P^T taken from the S^T
+//   registers rounded to bf16 and V staged in LDS and read with transpose
+//   reads.  The next block's K and V are loaded into registers while this
+//   one is computed.
 // out = O / (row sum), rounded to bf16.
 #include "tsg_copy.hpp"
 #include "tsg_gemm.hpp"
@@ -47,17 +48,18 @@ constexpr size_t kSigBase = (size_t(1) << 17) + 65536;  // K then V slab signals
 constexpr size_t kSigCap = 65536;
 constexpr int kQueueSlot = 52;
 
-// V blocks are staged as the B operand of a GEMM whose k dimension is the
-// key (64 rows) and whose n dimension is the head dimension (128 columns):
-// the transpose reads of the GEMM engine then hand out P V's B fragments.
+// V blocks are staged like a B stage of the GEMM engine (64 key rows of 128
+// head-dimension columns, row-major, 16-byte chunks permuted per row by
+// b_swz so that transpose reads are free of bank conflicts).
 using CfgV = TileCfg<BQ, D, 4, 1>;
 using TileV = GemmTile<CfgV>;
 
 constexpr int K_BYTES = BKV * D * 2;     // 16 KB, two halves of 64 columns
 constexpr int V_BYTES = BKV * D * 2;     // 16 KB
-constexpr int P_BYTES = 32 * BKV * 2;    // per wave, 4 KB
-constexpr int LDS_BYTES = K_BYTES + V_BYTES + 4 * P_BYTES;
+constexpr int STAGE_BYTES = K_BYTES + V_BYTES;
+constexpr int LDS_BYTES = 2 * STAGE_BYTES;  // two stages: block b + 1 lands while block b is computed
 static_assert(CfgV::B_STAGE == V_BYTES, "V block is one B stage");
+static_assert(BKV == 64 && D == 128, "the load-block mapping below assumes 64 x 128 blocks");
 
 struct AttnArgs {
   const uint16_t* q;
@@ -83,86 +85,145 @@ struct AttnArgs {
   float scale_log2;       // log2(e) / sqrt(D)
 };
 
-// Global -> register loads of one 64-key block of K or V (64 rows x 256 B):
-// 1024 pieces of 16 B, four per thread; piece i = t + 256 it is row i / 16,
-// 16-byte column chunk i % 16.
-struct BlockRegs {
-  u32x4_t k[4], v[4];
+// A 64-key block of K or V is 16 KB of LDS, moved from global memory by
+// global_load_lds (16 bytes a lane, 1 KB a wave instruction, no registers):
+// load block t = w + 4 i (i = 0..3) of wave w.  Lane l fills byte 16 l of the
+// load block, which fixes the global piece it fetches:
+//   K: two halves of 64 columns in the engine's A-stage layout (rows of 128
+//      bytes, chunk c of row r at position lds_pos(r, c), its own inverse);
+//      load block t is rows 8 (t mod 8) .. + 7 of half t / 8, and lane l
+//      takes row 8 (t mod 8) + l / 8, logical chunk lds_pos(row, l mod 8);
+//   V: one B stage, row-major, column chunk c of row r at position
+//      c ^ b_swz(r); load block t is rows 4 t .. 4 t + 3, and lane l takes
+//      row 4 t + l / 16, column chunk (l mod 16) ^ b_swz(row).
+// The offsets are in bytes from the block's first row in global memory.
+struct LoadOffsets {
+  uint32_t k[4], v[4];
 };
 
-__device__ __forceinline__ void load_block(BlockRegs& br, const uint16_t* kb, const uint16_t* vb, int64_t ld) {
+__device__ __forceinline__ void load_offsets(LoadOffsets& lo, int64_t ld) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int i = threadIdx.x + NT * it;
-    const int r = i >> 4, gc = i & 15;
-    br.k[it] = *(const u32x4_t*)(kb + (int64_t)r * ld + gc * 8);
-    br.v[it] = *(const u32x4_t*)(vb + (int64_t)r * ld + gc * 8);
+  for (int i = 0; i < 4; ++i) {
+    const int t = wave + 4 * i;
+    const int kr = 8 * (t & 7) + (lane >> 3);
+    const int kcol = 64 * (t >> 3) + 8 * (int)lds_pos(kr, lane & 7);
+    lo.k[i] = (uint32_t)((kr * ld + kcol) * 2);
+    const int vr = 4 * t + (lane >> 4);
+    const int vcol = 8 * ((lane & 15) ^ TileV::b_swz(vr));
+    lo.v[i] = (uint32_t)((vr * ld + vcol) * 2);
   }
 }
 
-// Register -> LDS.  K: two halves of 64 columns, each in the engine's A-stage
-// layout (rows of 128 bytes, chunk c of row r at position c ^ (r / 2 mod 8)).
-// V: one B stage, row-major, chunk c of row r at position c ^ b_swz(r).
-__device__ __forceinline__ void store_block(const BlockRegs& br, char* lk, char* lv) {
+// Issue the loads of one block (its first rows at kb and vb) into a stage.
+__device__ __forceinline__ void issue_block(const LoadOffsets& lo, const uint16_t* kb, const uint16_t* vb,
+                                            char* stage) {
+  const int wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int i = threadIdx.x + NT * it;
-    const int r = i >> 4, gc = i & 15;
-    *(u32x4_t*)(lk + (gc >> 3) * (BKV * 128) + lds_swz(r, gc & 7)) = br.k[it];
-    *(u32x4_t*)(lv + r * (D * 2) + ((gc ^ TileV::b_swz(r)) << 4)) = br.v[it];
+  for (int i = 0; i < 4; ++i) {
+    const int t = wave + 4 * i;
+    __builtin_amdgcn_global_load_lds((const void*)((const char*)kb + lo.k[i]),
+                                     (__attribute__((address_space(3))) void*)(stage + t * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)((const char*)vb + lo.v[i]),
+                                     (__attribute__((address_space(3))) void*)(stage + K_BYTES + t * 1024),
+                                     16, 0, 0);
   }
 }
 
-__device__ __forceinline__ float wave_half_max(float x) {
+// LDS byte offset of this lane's transpose reads of V for the A operand of
+// O^T += V^T P^T: lane l takes column d = 32 j + (l mod 32) of V and, in a
+// 16-key step, the keys 4 (l / 32) + 0..3 (first read) and 8 + 4 (l / 32)
+// + 0..3 (second read, 8 rows further) -- the same keys, in the same order,
+// as the scores this lane holds in registers 0..7 (or 8..15) of S^T, which
+// makes those registers the B operand P^T directly.  In each group of 16
+// lanes, lane 4 i + q points at row i, columns 4 q .. 4 q + 3 of a 4-row,
+// 16-column block.
+__device__ __forceinline__ void v_lane_offsets(uint32_t (&off)[D / 32]) {
+  const int lane = threadIdx.x & 63;
+  const int hi = lane >> 5, g = lane >> 4, sl = lane & 15;
+  const int row = 4 * hi + (sl >> 2);
 #pragma unroll
-  for (int o = 1; o < 32; o <<= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-  return x;
-}
-__device__ __forceinline__ float wave_half_sum(float x) {
-#pragma unroll
-  for (int o = 1; o < 32; o <<= 1) x += __shfl_xor(x, o, 64);
-  return x;
+  for (int j = 0; j < D / 32; ++j) {
+    const int col = 32 * j + 16 * (g & 1) + 4 * (sl & 3);
+    const int chunk = (col >> 3) ^ TileV::b_swz(row);
+    off[j] = (uint32_t)((row * D + chunk * 8 + (col & 7)) * 2);
+  }
 }
 
-// One attention tile: head h, queries [qb * BQ, qb * BQ + BQ) of this rank.
+__device__ __forceinline__ bf16x8_t read_v(const char* lv, uint32_t off, int kk) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  const char* p = lv + off + kk * 16 * D * 2;
+  const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p);
+  const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p + 8 * D * 2));
+  const v8i16 w = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8_t, w);
+}
+
+// Eight fp32 values as the bf16x8 operand, rounded to nearest even
+// (v_cvt_pk_bf16_f32, two values per instruction).
+__device__ __forceinline__ bf16x8_t pack_bf16x8(const f32x16_t& x, int base) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f32x2 f = {x[base + 2 * i], x[base + 2 * i + 1]};
+    w[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+  }
+  const u32x4_t v = {w[0], w[1], w[2], w[3]};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// Rescale threshold of the running maximum, in log2 units: the reference
+// maximum m of a query moves only when a block's maximum exceeds it by more
+// than this, so that exp2(score - m) stays below 2^8 and the rescale of O
+// and l is skipped for most blocks (softmax does not depend on m).
+constexpr float kRescaleLog2 = 8.0f;
+
+// One attention tile: head h, queries [qb * BQ, qb * BQ + BQ) of this rank;
+// wave w owns queries qb * BQ + 32 w .. + 31, one per lane pair (l, l + 32).
+// Transposed products: S^T = K Q^T and O^T += V^T P^T, so that a lane holds
+// scores and outputs of a single query (its l mod 32): the softmax max and
+// sum reduce in registers and across the two lane halves only, the running
+// rescale is per lane, and the probabilities go from the S^T accumulators
+// straight into the B operand of the second product.
 // Returns the wall-clock ticks spent waiting for signals.
 __device__ __forceinline__ uint64_t attn_tile(const AttnArgs& a, int h, int qb, char* lds) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int hi = lane >> 5, l32 = lane & 31;
-  char* lk = lds;
-  char* lv = lds + K_BYTES;
-  char* lp = lds + K_BYTES + V_BYTES + wave * P_BYTES;
   const int64_t ld = (int64_t)a.heads * D;  // elements per token row
+  const int qrow = qb * BQ + wave * 32 + l32;
 
-  // Q fragments: lane row = wave * 32 + l32, k16 step ks: columns 16 ks + 8 hi .. + 7
+  // Q^T fragments (B operand): lane column = query qrow, k16 step ks:
+  // head-dimension 16 ks + 8 hi .. + 7
   bf16x8_t qa[D / 16];
   {
-    int row = qb * BQ + wave * 32 + l32;
-    if (row >= a.S_loc) row = a.S_loc - 1;  // never stored
+    const int row = qrow < a.S_loc ? qrow : a.S_loc - 1;  // never stored
     const uint16_t* qr = a.q + (int64_t)row * ld + h * D + 8 * hi;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) qa[ks] = *(const bf16x8_t*)(qr + 16 * ks);
   }
+  // O^T: fragment j holds head-dimension rows 32 j + 8 (v / 4) + 4 hi +
+  // v mod 4 (register v) of this lane's query
   f32x16_t o[D / 32];
 #pragma unroll
   for (int j = 0; j < D / 32; ++j)
 #pragma unroll
     for (int v = 0; v < 16; ++v) o[j][v] = 0.f;
-  // per lane: 16 query rows (8 (v / 4) + 4 hi + v mod 4), running max (in
-  // log2 units) and sum
-  float m[16], l[16];
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    m[v] = -INFINITY;
-    l[v] = 0.f;
-  }
-  uint32_t tr_off[CfgV::FN];
-  TileV::tr_lane_offsets(0, tr_off);
+  float m = -INFINITY, l = 0.f;  // reference max (log2 units) and sum of this lane's query
+  uint32_t v_off[D / 32];
+  v_lane_offsets(v_off);
   const int s_lo = (h * D) >> a.slab_log2, s_hi = (h * D + D - 1) >> a.slab_log2;
   const int n_blk = a.S_loc / BKV;
   uint64_t waited = 0;
 
-  for (int p = 0; p < a.R; ++p) {
+  LoadOffsets lo;
+  load_offsets(lo, ld);
+  // chunk base pointers (this head's columns) of arrival position p; before
+  // a peer chunk's first block is loaded, the K and V signals of the slabs
+  // holding the head's columns are waited for
+  auto chunk_base = [&](int p, const uint16_t*& kc, const uint16_t*& vc) {
     const int c = a.order[p];
     const bool own = c == a.rank;
     if (!own && a.wait) {
@@ -175,75 +236,100 @@ __device__ __forceinline__ uint64_t attn_tile(const AttnArgs& a, int h, int qb, 
       acquire_lines(a.l1_only != 0);
       waited += wall_clock64() - t;
     }
-    const uint16_t* kc = own ? a.k_local : a.k_full + (int64_t)c * a.S_loc * ld;
-    const uint16_t* vc = own ? a.v_local : a.v_full + (int64_t)c * a.S_loc * ld;
-    kc += h * D;
-    vc += h * D;
-    BlockRegs br;
-    load_block(br, kc, vc, ld);
-    for (int b = 0; b < n_blk; ++b) {
-      __syncthreads();  // the previous block's LDS reads are done
-      store_block(br, lk, lv);
-      __syncthreads();
-      if (b + 1 < n_blk) load_block(br, kc + (int64_t)(b + 1) * BKV * ld, vc + (int64_t)(b + 1) * BKV * ld, ld);
-      // S = Q K^T, two fragments of 32 keys
-      f32x16_t s[2];
+    kc = (own ? a.k_local : a.k_full + (int64_t)c * a.S_loc * ld) + h * D;
+    vc = (own ? a.v_local : a.v_full + (int64_t)c * a.S_loc * ld) + h * D;
+  };
+  const uint16_t *kc, *vc;
+  chunk_base(0, kc, vc);
+  issue_block(lo, kc, vc, lds);
+  // blocks g = p n_blk + b in arrival order; block g is in stage g mod 2
+  const int n_all = a.R * n_blk;
+  for (int g = 0, b = 0, p = 0; g < n_all; ++g) {
+    // block g has landed (this wave's loads, then every wave's), and every
+    // wave is done reading the other stage (block g - 1)
+    wait_vmcnt<0>();
+    lds_barrier();
+    const char* lk = lds + (g & 1) * STAGE_BYTES;
+    const char* lv = lk + K_BYTES;
+    if (++b == n_blk) {
+      b = 0;
+      if (++p < a.R) chunk_base(p, kc, vc);
+    }
+    if (g + 1 < n_all)
+      issue_block(lo, kc + (int64_t)b * BKV * ld, vc + (int64_t)b * BKV * ld, lds + ((g + 1) & 1) * STAGE_BYTES);
+    // S^T = K Q^T: fragment j holds keys 32 j + 8 (v / 4) + 4 hi + v mod 4
+    f32x16_t s[2];
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) s[j][v] = 0.f;
+      for (int v = 0; v < 16; ++v) s[j][v] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const char* half = lk + (ks >> 2) * (BKV * 128);
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const char* half = lk + (ks >> 2) * (BKV * 128);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const bf16x8_t kb = *(const bf16x8_t*)(half + lds_swz(32 * j + l32, 2 * (ks & 3) + hi));
-          s[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kb, s[j], 0, 0, 0);
-        }
+      for (int j = 0; j < 2; ++j) {
+        const bf16x8_t kf = *(const bf16x8_t*)(half + lds_swz(32 * j + l32, 2 * (ks & 3) + hi));
+        s[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qa[ks], s[j], 0, 0, 0);
       }
-      // online softmax over the block's 64 keys, per query row
+    }
+    // online softmax of this lane's query over the block's 64 keys: 32 in
+    // this lane, 32 in lane l ^ 32 (scores in log2 units: raw x scale)
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[j][v]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * a.scale_log2;
+    if (__any(mx > m + kRescaleLog2)) {  // wave-uniform
+      const float mn = fmaxf(m, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m - mn);
+      l *= alpha;
+      m = mn;
+#pragma unroll
+      for (int j = 0; j < D / 32; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[j][v] *= alpha;
+    }
+    float sum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const float x0 = s[0][v] * a.scale_log2, x1 = s[1][v] * a.scale_log2;
-        const float mn = fmaxf(m[v], wave_half_max(fmaxf(x0, x1)));
-        const float alpha = exp2f(m[v] - mn);
-        const float p0 = exp2f(x0 - mn), p1 = exp2f(x1 - mn);
-        l[v] = l[v] * alpha + wave_half_sum(p0 + p1);
-        m[v] = mn;
-#pragma unroll
-        for (int j = 0; j < D / 32; ++j) o[j][v] *= alpha;
-        // P in bf16, row r of the wave's region, keys l32 and 32 + l32
-        const int r = 8 * (v >> 2) + 4 * hi + (v & 3);
-        *(uint16_t*)(lp + lds_swz(r, l32 >> 3) + (l32 & 7) * 2) = (uint16_t)f32_to_bf16(p0);
-        *(uint16_t*)(lp + lds_swz(r, 4 + (l32 >> 3)) + (l32 & 7) * 2) = (uint16_t)f32_to_bf16(p1);
+        s[j][v] = __builtin_amdgcn_exp2f(fmaf(s[j][v], a.scale_log2, -m));
+        sum += s[j][v];
       }
-      // the wave's P region is its own: its writes complete before its reads
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      // O += P V, four k16 steps of 16 keys
+    l += sum + __shfl_xor(sum, 32, 64);
+    // O^T += V^T P^T, four 16-key steps: P^T from registers 8 (kk mod 2)
+    // .. + 7 of S^T fragment kk / 2, rounded to bf16
 #pragma unroll
-      for (int kk = 0; kk < BKV / 16; ++kk) {
-        const bf16x8_t pa = *(const bf16x8_t*)(lp + lds_swz(l32, 2 * kk + hi));
+    for (int kk = 0; kk < BKV / 16; ++kk) {
+      const bf16x8_t pb = pack_bf16x8(s[kk >> 1], 8 * (kk & 1));
 #pragma unroll
-        for (int j = 0; j < D / 32; ++j)
-          o[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, TileV::read_b_tr(lv, tr_off[j], kk), o[j], 0, 0, 0);
-      }
+      for (int j = 0; j < D / 32; ++j)
+        o[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_v(lv, v_off[j], kk), pb, o[j], 0, 0, 0);
     }
   }
-  // out = O / l, bf16
+  lds_barrier();  // every wave is done with the stages before the LDS is reused
+  // out = O / l in bf16: four consecutive head-dimension values per
+  // (fragment, register group), one 8-byte store each
+  if (qrow < a.S_loc) {
+    const float inv = 1.0f / l;
+    uint16_t* orow = a.out + (int64_t)qrow * ld + h * D + 4 * hi;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int row = qb * BQ + wave * 32 + 8 * (v >> 2) + 4 * hi + (v & 3);
-    if (row < a.S_loc) {
-      const float inv = 1.0f / l[v];
-      uint16_t* orow = a.out + (int64_t)row * ld + h * D + l32;
+    for (int j = 0; j < D / 32; ++j)
 #pragma unroll
-      for (int j = 0; j < D / 32; ++j) orow[32 * j] = (uint16_t)f32_to_bf16(o[j][v] * inv);
-    }
+      for (int g = 0; g < 4; ++g) {
+        const uint64_t w = (uint64_t)f32_to_bf16(o[j][4 * g] * inv) |
+                           ((uint64_t)f32_to_bf16(o[j][4 * g + 1] * inv) << 16) |
+                           ((uint64_t)f32_to_bf16(o[j][4 * g + 2] * inv) << 32) |
+                           ((uint64_t)f32_to_bf16(o[j][4 * g + 3] * inv) << 48);
+        *(uint64_t*)(orow + 32 * j + 8 * g) = w;
+      }
   }
   return waited;
 }
 
-__global__ void __launch_bounds__(NT) ag_attn_kernel(const AttnArgs a) {
+__global__ void __launch_bounds__(NT, 2) ag_attn_kernel(const AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
   const int n_items = a.n_copy_k + a.n_copy_v + a.n_tiles;
   // Next item, identical in every thread; the ticket goes through the first
@@ -326,7 +412,9 @@ tsg_status tsg_op_attn(tsg_ctx* ctx, const void* q, const void* k_local, const v
   const int n_slab = (HD + slab - 1) / slab;
   if ((size_t)2 * R * n_slab > kSigCap) return fail(ctx, TSG_E_UNSUPPORTED, "too many slab signals");
   const int S_loc = S / R;
-  const int nwg = ctx->n_cus;  // one workgroup per CU (its registers allow one wave per SIMD)
+  // two workgroups per CU: with at most 256 registers a wave, two waves share
+  // each SIMD, so one's softmax runs while the other's MFMAs do
+  const int nwg = 2 * ctx->n_cus;
   int np[kHead + 1], ustart[kHead + 1];
   int64_t n_units = 0;
   if (!copy_plan(R, 1, S_loc, HD, n_slab, slab_log2 - 3, nwg, np, ustart, &n_units))
