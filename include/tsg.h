@@ -132,7 +132,9 @@ typedef struct tsg_opts {
    * so compute need not wait for the copy kernel to be scheduled.  Units not
    * taken by the GEMM are moved by the copy kernel from the same queue.
    * 0 = the op's default (one unit per CU, at most the first slab's units),
-   * -1 = none. */
+   * -1 = none.  AllGather KV + attention, overlapped: > 0 = the attention
+   * workgroups take every copy unit from their own queue before the tiles;
+   * 0 or -1 = a copy kernel runs beside them. */
   int pull_units;
   /* MoE: element type of the y staging between the down projection and the
    * combine.  TSG_F32 (0, default): y is kept in fp32.  TSG_BF16 (1): y is
@@ -447,8 +449,13 @@ tsg_status moe_ag_group_gemm(tsg_ctx* ctx, const void* x_local, const void* x_pe
  *   k_full, v_full    bf16 [S x heads x head_dim]   gathered (output)
  *   out      bf16 [S/R x heads x head_dim]   (output)
  *   arrival_order: as in gemm_ag_overlap.
- * Modes: OVERLAP runs one persistent kernel whose workgroups take the copy
- * units first and then the tiles from one queue; SERIAL the copy, then the
+ * Modes: OVERLAP runs the copy as a small kernel beside the attention
+ * kernel on the same CUs (a copy wave per SIMD next to two attention
+ * waves), moving the units arrival position by position (K and V of every
+ * slab of the first peer, then of the next), while the tiles start on their
+ * own chunks; with opts.pull_units > 0 (or where the two kernels cannot share
+ * a CU) it runs one persistent kernel whose workgroups take the copy units
+ * first and then the tiles from one queue.  SERIAL runs the copy, then the
  * tiles; COMPUTE_ONLY the tiles without waits (k_full / v_full must hold
  * the context already); COMM_ONLY the copy alone.  Shared CUs only (aux_cus
  * > 0: TSG_E_UNSUPPORTED).  debug_skip_mask bit c withholds chunk c's

@@ -115,6 +115,11 @@ def test_attention_modes_orders_slabs(env):
     for mode in (tsg.SERIAL, tsg.COMPUTE_ONLY):
         _, _, o2 = case.run(mode=mode)
         assert np.array_equal(o2, out), mode
+    # overlapped with the copy units in the attention kernel's own queue
+    # instead of a copy kernel beside it: the same bits
+    kf2, vf2, o2 = case.run(opts={"pull_units": 1})
+    assert np.array_equal(o2, out)
+    assert np.array_equal(kf2, inp["k"]) and np.array_equal(vf2, inp["v"])
     kf3, vf3, _ = case.run(mode=tsg.COMM_ONLY)
     assert np.array_equal(kf3, inp["k"]) and np.array_equal(vf3, inp["v"])
     # another arrival order changes the order in which a tile accumulates
@@ -166,13 +171,17 @@ def test_attention_waits_for_its_chunks(env):
     inp = _inputs(S, heads, seed=83)
     case = Case(env, inp, S, heads, R, rank)
     case.run()
-    for c in range(R):
-        expect = tsg.OK if c == rank else tsg.E_TIMEOUT
-        case.run(opts={"debug_skip_mask": 1 << c, "timeout_ms": 20, "timeline": 1}, expect=expect)
-        recs = [r for r in ctx.timeline() if (r[0] >> 56) == 11]
-        assert len(recs) == heads * ((S // R + 127) // 128)
-        long = sum(1 for r in recs if r[2] - r[1] > 1_000_000)
-        assert long == (0 if c == rank else len(recs)), (c, long)
+    # both overlapped forms: copy kernel beside the tiles, copy units in
+    # the attention kernel's queue
+    for pull in (0, 1):
+        for c in range(R):
+            expect = tsg.OK if c == rank else tsg.E_TIMEOUT
+            case.run(opts={"debug_skip_mask": 1 << c, "timeout_ms": 20, "timeline": 1, "pull_units": pull},
+                     expect=expect)
+            recs = [r for r in ctx.timeline() if (r[0] >> 56) == 11]
+            assert len(recs) == heads * ((S // R + 127) // 128)
+            long = sum(1 for r in recs if r[2] - r[1] > 1_000_000)
+            assert long == (0 if c == rank else len(recs)), (pull, c, long)
     kf, vf, out = case.run()
     _check(case, kf, vf, out)
 

@@ -17,20 +17,23 @@
 //     out[q, h] = sum_j softmax_j(Q[q, h] . K[j, h] / sqrt(D)) V[j, h]
 // over all S keys j (no mask).
 //
-// One persistent kernel, one ticket queue: first the copy units that stand
-// in for the peers' arrival (the AllGather copy's units over K, then V, as
-// [S x heads D] matrices: column slabs of each chunk, peers in arrival order,
-// the local chunk last, every (chunk, slab) counted on its signal), then the
-// attention tiles (head, 128 queries).  A tile takes the chunks in arrival
-// order, its own chunk first, read in place from k_local / v_local without
-// waiting; before a peer chunk it waits for the K and V signals of the slabs
-// holding its head's columns.  Inside a chunk, 64 keys at a time:
+// The copy that stands in for the peers' arrival is the AllGather copy's
+// units over K and V as [S x heads D] matrices: column slabs of each chunk,
+// peers in arrival order, the local chunk last, every (chunk, slab) counted
+// on its signal.  Overlapped, it runs as a small kernel of its own beside the
+// attention kernel, on the same CUs (one copy wave per SIMD fits beside two
+// attention waves), arrival position by position; or, with opts.pull_units > 0, as the first items of the attention
+// kernel's own ticket queue.  The attention tiles (head, 128 queries) take
+// the chunks in arrival order, their own chunk first, read in place from
+// k_local / v_local without waiting; before a peer chunk a tile waits for the
+// K and V signals of the slabs holding its head's columns.  Inside a chunk,
+// 64 keys at a time:
 //   S^T = K Q^T (v_mfma_f32_32x32x16_bf16; Q fragments in registers, K
 //   staged in LDS), online softmax per query (running max and sum, exp2 of
 //   the scaled scores), then O^T += V^T P^T with P^T taken from the S^T
 //   registers rounded to bf16 and V staged in LDS and read with transpose
-//   reads.  The next block's K and V are loaded into registers while this
-//   one is computed.
+//   reads.  The next block's K and V are loaded into the other LDS stage
+//   while this one is computed.
 // out = O / (row sum), rounded to bf16.
 #include "tsg_copy.hpp"
 #include "tsg_gemm.hpp"
@@ -46,7 +49,8 @@ constexpr int BKV = 64;     // keys per block
 constexpr int NT = 256;
 constexpr size_t kSigBase = (size_t(1) << 17) + 65536;  // K then V slab signals in the context's pool
 constexpr size_t kSigCap = 65536;
-constexpr int kQueueSlot = 52;
+constexpr int kQueueSlot = 64;       // attention kernel: 2 phases x 8 XCD tickets, exit counter
+constexpr int kCopyQueueSlot = 54;   // copy kernel: ticket, exit counter
 
 // V blocks are staged like a B stage of the GEMM engine (64 key rows of 128
 // head-dimension columns, row-major, 16-byte chunks permuted per row by
@@ -70,7 +74,7 @@ struct AttnArgs {
   uint16_t* out;
   const uint64_t* sig_k;  // chunk c, slab s at c * n_slab + s
   const uint64_t* sig_v;
-  uint32_t* queue;        // ticket, exit counter (zero between calls)
+  uint32_t* queue;        // 2 phases x 8 XCD ticket counters, exit counter (zero between calls)
   SyncArgs sa;
   Timeline tl;
   CopyArgs copy_k, copy_v;
@@ -329,28 +333,42 @@ __device__ __forceinline__ uint64_t attn_tile(const AttnArgs& a, int h, int qb, 
   return waited;
 }
 
+// Items come from per-XCD phased queues: phase 0 the copy units (K, then
+// V), phase 1 the tiles, head-major (tile t = head t / n_qb, query block
+// t mod n_qb), so that each XCD runs a contiguous share of heads and the
+// query blocks of a head, which stream the same keys and values, share its
+// L2.
 __global__ void __launch_bounds__(NT, 2) ag_attn_kernel(const AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
-  const int n_items = a.n_copy_k + a.n_copy_v + a.n_tiles;
-  // Next item, identical in every thread; the ticket goes through the first
-  // word of the LDS, which is free between items (every item ends with a
-  // barrier).
-  auto fetch = [&]() -> int {
+  const int n_ph[2] = {a.n_copy_k + a.n_copy_v, a.n_tiles};
+  const int my_xcd = xcd_id();
+  int phase = 0;
+  // Next item, identical in every thread: wave 0 claims it and passes it on
+  // through the first words of the LDS, which are free between items (every
+  // item ends with a barrier).
+  auto fetch = [&]() -> QueueItem {
     volatile int* s_item = (volatile int*)lds;
-    if (threadIdx.x == 0) *s_item = (int)atomicAdd(a.queue, 1u);
+    if (threadIdx.x < 64) {
+      const QueueItem it = xcd_queue_claim<2>(a.queue, n_ph, my_xcd, phase);
+      if (threadIdx.x == 0) {
+        s_item[0] = it.phase;
+        s_item[1] = it.index;
+      }
+    }
     __syncthreads();
-    const int v = __builtin_amdgcn_readfirstlane(*s_item);
+    const QueueItem it{__builtin_amdgcn_readfirstlane(s_item[0]), __builtin_amdgcn_readfirstlane(s_item[1])};
     __syncthreads();
-    return v;
+    return it;
   };
-  for (int item = fetch(); item < n_items; item = fetch()) {
-    if (item < a.n_copy_k) {
-      copy_unit<NT>(a.copy_k, item);
-    } else if (item < a.n_copy_k + a.n_copy_v) {
-      copy_unit<NT>(a.copy_v, item - a.n_copy_k);
+  for (QueueItem it = fetch(); it.phase >= 0; it = fetch()) {
+    phase = it.phase;
+    if (it.phase == 0) {
+      if (it.index < a.n_copy_k)
+        copy_unit<NT>(a.copy_k, it.index);
+      else
+        copy_unit<NT>(a.copy_v, it.index - a.n_copy_k);
     } else {
-      const int t = item - a.n_copy_k - a.n_copy_v;
-      const int h = t / a.n_qb, qb = t - h * a.n_qb;
+      const int h = it.index / a.n_qb, qb = it.index - h * a.n_qb;
       const uint64_t t0 = a.tl.buf ? wall_clock64() : 0;
       const uint64_t waited = attn_tile(a, h, qb, lds);
       if (a.tl.buf && threadIdx.x == 0)
@@ -359,10 +377,37 @@ __global__ void __launch_bounds__(NT, 2) ag_attn_kernel(const AttnArgs a) {
     __syncthreads();
   }
   // the last workgroup to leave resets the ticket and exit counters
-  if (threadIdx.x == 0 && atomicAdd(a.queue + 1, 1u) == gridDim.x - 1) {
-    __hip_atomic_store(a.queue, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(a.queue + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0 && atomicAdd(a.queue + 16, 1u) == gridDim.x - 1)
+    for (int i = 0; i <= 16; ++i) __hip_atomic_store(a.queue + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Copy kernel of the overlapped form: units from its own queue, arrival
+// position by position (all slabs of the first peer's K and V, then the
+// next peer's, ...), until none is left.  It never
+// waits, so it always drains the queue.  Capped at 48 registers (the
+// attribute counts half the unified register file): one copy wave fits on
+// each SIMD beside two attention waves of 200.
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_num_vgpr(24)))
+    ag_attn_copy_kernel(const CopyArgs ck, const CopyArgs cv) {
+  __shared__ int slot;
+  // every slab has npc pieces a chunk, and unit u = (s R + p) npc + j;
+  // ticket w takes arrival position p = (w / 2) / (n_slab npc) first, then
+  // slab, piece, and K (w even) or V (w odd)
+  const int npc = ck.np[kHead];
+  const int per_pos = ck.n_slab * npc;
+  const int n = ck.n_units + cv.n_units;
+  for (int w = claim_unit(ck, &slot); w < n; w = claim_unit(ck, &slot)) {
+    const int w2 = w >> 1;
+    const int p = w2 / per_pos;
+    const int r = w2 - p * per_pos;
+    const int sl = r / npc;
+    const int u = (sl * ck.R + p) * npc + (r - sl * npc);
+    if (w & 1)
+      copy_unit<256>(cv, u);
+    else
+      copy_unit<256>(ck, u);
   }
+  if (threadIdx.x == 0) leave_queue(ck);
 }
 
 }  // namespace
@@ -419,6 +464,16 @@ tsg_status tsg_op_attn(tsg_ctx* ctx, const void* q, const void* k_local, const v
   int64_t n_units = 0;
   if (!copy_plan(R, 1, S_loc, HD, n_slab, slab_log2 - 3, nwg, np, ustart, &n_units))
     return fail(ctx, TSG_E_UNSUPPORTED, "ag_kv_attention: the copy's offsets would overflow");
+  // one piece count for every slab (every tile needs whole chunks of its
+  // head, so no slab comes first): unit u = (s R + p) npc + j
+  {
+    const int npc = np[kHead];
+    for (int i = 0; i <= kHead; ++i) {
+      np[i] = npc;
+      ustart[i] = std::min(i, n_slab) * R * npc;
+    }
+    n_units = (int64_t)n_slab * R * npc;
+  }
 
   TSG_HIP(ctx, hipSetDevice(ctx->device));
   hipStream_t caller = (hipStream_t)stream;
@@ -434,7 +489,7 @@ tsg_status tsg_op_attn(tsg_ctx* ctx, const void* q, const void* k_local, const v
   ck.sig = ctx->d_sig + kSigBase;
   ck.cnt = ctx->d_cnt + kSigBase;
   ck.sa = sa;
-  ck.tl = Timeline{nullptr, nullptr, 0};
+  ck.tl = timeline(ctx, o);  // copy units: kind 1
   for (int p = 0; p < kMaxRanks; ++p) ck.ord.chunk[p] = 0;
   for (int p = 1; p < R; ++p) ck.ord.chunk[p - 1] = ord[p];
   ck.ord.chunk[R - 1] = (int8_t)rank;
@@ -489,23 +544,47 @@ tsg_status tsg_op_attn(tsg_ctx* ctx, const void* q, const void* k_local, const v
   ka.scale_log2 = 1.4426950408889634f / sqrtf((float)D);
   const int n_tiles = heads * ka.n_qb;
 
-  auto launch = [&](int n_copy, int tiles, int wait, int which) -> tsg_status {
+  auto launch = [&](hipStream_t st, int n_copy, int tiles, int wait, int which) -> tsg_status {
     ka.n_copy_k = n_copy;
     ka.n_copy_v = n_copy;
     ka.n_tiles = tiles;
     ka.wait = wait;
-    time_begin(ctx, which, caller);
-    hipLaunchKernelGGL(ag_attn_kernel, dim3(nwg), dim3(NT), 0, caller, ka);
-    time_end(ctx, which, caller);
+    time_begin(ctx, which, st);
+    hipLaunchKernelGGL(ag_attn_kernel, dim3(nwg), dim3(NT), 0, st, ka);
+    time_end(ctx, which, st);
     return check_launch(ctx, "ag_attn_kernel");
   };
+  // Overlapped with a copy kernel of its own on the same CUs: two attention
+  // workgroups (one of 2 NT threads, for the register count) and one copy
+  // workgroup must fit on a CU together.
+  static_assert(2 * LDS_BYTES + 1024 <= 160 * 1024, "two attention workgroups and a copy workgroup share a CU");
+  const bool side_copy = mode == TSG_MODE_OVERLAP && o.pull_units <= 0 &&
+                         co_resident(ctx, (const void*)ag_attn_kernel, 2 * NT, (const void*)ag_attn_copy_kernel, 256);
   switch (mode) {
-    case TSG_MODE_OVERLAP: return launch((int)n_units, n_tiles, 1, 0);
-    case TSG_MODE_SERIAL: {
-      tsg_status st = launch((int)n_units, 0, 0, 1);
-      return st != TSG_OK ? st : launch(0, n_tiles, 1, 0);
+    case TSG_MODE_OVERLAP: {
+      if (!side_copy) return launch(caller, (int)n_units, n_tiles, 1, 0);
+      Pair pr;
+      tsg_status st = streams(ctx, o, &pr, caller);
+      if (st == TSG_OK) st = fork(ctx, caller, pr);
+      if (st != TSG_OK) return st;
+      // the copy first, so that its workgroups are dispatched while the
+      // attention workgroups start on their own chunks
+      const int copy_grid = o.aux_wgs > 0 ? std::min(o.aux_wgs, 4 * ctx->n_cus) : ctx->n_cus;
+      ck.queue = ctx->d_queue + kCopyQueueSlot;
+      ck.n_workers = (uint32_t)copy_grid;
+      time_begin(ctx, 1, pr.aux);
+      hipLaunchKernelGGL(ag_attn_copy_kernel, dim3(copy_grid), dim3(256), 0, pr.aux, ck, cv);
+      time_end(ctx, 1, pr.aux);
+      st = check_launch(ctx, "ag_attn_copy_kernel");
+      if (st == TSG_OK) st = launch(pr.main, 0, n_tiles, 1, 0);
+      if (st != TSG_OK) return st;
+      return join(ctx, caller, pr);
     }
-    case TSG_MODE_COMPUTE_ONLY: return launch(0, n_tiles, 0, 0);
-    default: return launch((int)n_units, 0, 0, 1);
+    case TSG_MODE_SERIAL: {
+      tsg_status st = launch(caller, (int)n_units, 0, 0, 1);
+      return st != TSG_OK ? st : launch(caller, 0, n_tiles, 1, 0);
+    }
+    case TSG_MODE_COMPUTE_ONLY: return launch(caller, 0, n_tiles, 0, 0);
+    default: return launch(caller, (int)n_units, 0, 0, 1);
   }
 }

@@ -251,8 +251,8 @@ tsg_status tsg_ctx_create(int device, tsg_ctx** out) {
   if (e == hipSuccess) e = hipMemset(c->d_cnt, 0, kSignals * sizeof(uint32_t));
   if (e == hipSuccess) e = hipMalloc(&c->d_status, 64);
   if (e == hipSuccess) e = hipMemset(c->d_status, 0, 64);
-  if (e == hipSuccess) e = hipMalloc(&c->d_queue, 64 * sizeof(uint32_t));
-  if (e == hipSuccess) e = hipMemset(c->d_queue, 0, 64 * sizeof(uint32_t));
+  if (e == hipSuccess) e = hipMalloc(&c->d_queue, 128 * sizeof(uint32_t));
+  if (e == hipSuccess) e = hipMemset(c->d_queue, 0, 128 * sizeof(uint32_t));
   if (e == hipSuccess) e = hipMalloc(&c->d_timeline, (size_t)kTimelineCap * 4 * sizeof(uint64_t));
   if (e == hipSuccess) e = hipMalloc(&c->d_timeline_n, 64);
   if (e == hipSuccess) e = hipMemset(c->d_timeline_n, 0, 64);
