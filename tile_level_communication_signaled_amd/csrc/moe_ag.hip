@@ -22,16 +22,20 @@
 //      whose tokens arrive first run first -- the tile order follows the
 //      arrival order, as in the AllGather GEMM's swizzle, but read from the
 //      runtime tables.
-//   3. moe_ag_kernel (persistent, one ticket queue): first the copy units
-//      that stand in for the peers' arrival (the AllGather copy's units:
-//      column slabs of each chunk, the local chunk first, counted signals),
-//      then the up tiles in that order.  A tile waits for every slab signal
+//   3. moe_ag_kernel (persistent, per-XCD phased queues): first the copy
+//      units that stand in for the peers' arrival (the AllGather copy's
+//      units: column slabs of each chunk, the local chunk first, counted
+//      signals), then the up tiles in that order, all column tiles of a row
+//      block together; each XCD takes a contiguous share of the tiles, so
+//      the column tiles of a row block, which gather the same tokens, and
+//      the blocks of one expert, which read the same weights, meet in its
+//      L2.  A tile waits for every slab signal
 //      of every chunk in its block's rank mask, gathers its tokens' rows of
 //      x_full through the row -> token table, multiplies them by w_up[e]
 //      (bf16 MFMA, fp32 accumulation), applies SiLU and stores bf16 rows to
 //      h in pair order through the row -> pair table.  Copy units never
-//      wait and every tile waits only for copy units, which running
-//      workgroups took before it: the queue always drains.
+//      wait, and a workgroup reaches the tiles only once every copy unit
+//      has been taken by a running workgroup: the queues always drain.
 #include "tsg_copy.hpp"
 #include "tsg_gemm.hpp"
 #include "tsg_internal.hpp"
@@ -44,12 +48,18 @@ namespace {
 constexpr int BM = 256;  // row block: tile rows and the per-expert padding unit
 constexpr int BN = 224;
 constexpr int kMaxRowBlocks = 4096;
+static_assert(kMaxRowBlocks <= kRouteMaskBlocks, "the placement kernel gathers every block's rank mask in LDS");
 constexpr size_t kSigBase = size_t(1) << 17;  // chunk slab signals in the context's pool
 constexpr size_t kSigCap = size_t(1) << 16;
-constexpr int kQueueSlot = 48;                // ticket, exit counter; then the copy's own pair
+constexpr int kQueueSlot = 96;                // 2 phases x 8 XCD tickets, exit counter
 
-using Cfg = TileCfg<BM, BN, 8, 1>;
-constexpr int kThreads = Cfg::NT;
+// Main path (H a multiple of 128): 16x16x32 fragments, four by two waves of
+// 64 x 112; otherwise the register-staged path with 32x32x16 fragments,
+// eight waves of 32 x 224.
+template <bool DIRECT>
+using CfgOf = std::conditional_t<DIRECT, TileCfg<BM, BN, 4, 2, 16>, TileCfg<BM, BN, 8, 1>>;
+constexpr int kThreads = CfgOf<true>::NT;
+static_assert(CfgOf<false>::NT == kThreads, "both paths use one workgroup size");
 
 struct Layout {
   size_t meta, offs, poffs, rb_expert, row_pair, row_token, pair_row, blk, rb_mask, rb_order, total;
@@ -125,7 +135,7 @@ struct AgMoeArgs {
   const uint32_t* rb_mask;
   const int* rb_order;
   const uint64_t* sig;    // slab signals of the chunks, c * n_slab + s
-  uint32_t* queue;        // ticket, exit counter (zero between calls)
+  uint32_t* queue;        // 2 phases x 8 XCD ticket counters, exit counter (zero between calls)
   SyncArgs sa;
   Timeline tl;
   CopyArgs copy;
@@ -140,28 +150,39 @@ struct AgMoeArgs {
 
 template <bool DIRECT>
 __global__ void __launch_bounds__(kThreads) moe_ag_kernel(const AgMoeArgs a) {
+  using Cfg = CfgOf<DIRECT>;
   __shared__ __attribute__((aligned(16))) char lds[DIRECT ? Cfg::LDS_DIRECT : Cfg::LDS_REGS];
   const int n_rb = __builtin_amdgcn_readfirstlane(a.tab.meta[0]);
-  const int n_items = a.n_copy + a.n_tiles;
-  // Next item, identical in every thread; the loop's single back edge goes
-  // through this fetch.  The ticket travels through the first word of the
-  // tile buffer, which is free between items (a tile's last LDS access
-  // precedes a barrier: the K loop's last one, or the staged epilogue's
-  // wave-local reads, which wave 0 finishes before thread 0 writes).
-  auto fetch = [&]() -> int {
+  // tiles of the row blocks in use (n_tiles is the bound for n_rb_max blocks)
+  const int n_ph[2] = {a.n_copy, a.n_tiles > 0 ? min(n_rb * a.n_nt, a.n_tiles) : 0};
+  const int my_xcd = xcd_id();
+  int phase = 0;
+  // Next item, identical in every thread: wave 0 claims it and passes it on
+  // through the first words of the tile buffer, which are free between items
+  // (a tile's last LDS access precedes a barrier: the K loop's last one, or
+  // the staged epilogue's wave-local reads, which wave 0 finishes before
+  // its lane 0 writes).
+  auto fetch = [&]() -> QueueItem {
     volatile int* s_item = (volatile int*)lds;
-    if (threadIdx.x == 0) *s_item = (int)atomicAdd(a.queue, 1u);
+    if (threadIdx.x < 64) {
+      const QueueItem it = xcd_queue_claim<2>(a.queue, n_ph, my_xcd, phase);
+      if (threadIdx.x == 0) {
+        s_item[0] = it.phase;
+        s_item[1] = it.index;
+      }
+    }
     __syncthreads();
-    const int v = __builtin_amdgcn_readfirstlane(*s_item);
+    const QueueItem it{__builtin_amdgcn_readfirstlane(s_item[0]), __builtin_amdgcn_readfirstlane(s_item[1])};
     __syncthreads();
-    return v;
+    return it;
   };
-  for (int item = fetch(); item < n_items; item = fetch()) {
-    if (item < a.n_copy) {
-      copy_unit<kThreads>(a.copy, item);
+  for (QueueItem it = fetch(); it.phase >= 0; it = fetch()) {
+    phase = it.phase;
+    if (it.phase == 0) {
+      copy_unit<kThreads>(a.copy, it.index);
       __syncthreads();
     } else {
-      const int ti = item - a.n_copy;
+      const int ti = it.index;
       const int ord = ti / a.n_nt, nt = ti - ord * a.n_nt;
       if (ord < n_rb) {
         const uint64_t t0 = a.tl.buf ? wall_clock64() : 0;
@@ -200,10 +221,8 @@ __global__ void __launch_bounds__(kThreads) moe_ag_kernel(const AgMoeArgs a) {
     }
   }
   // the last workgroup to leave resets the ticket and exit counters
-  if (threadIdx.x == 0 && atomicAdd(a.queue + 1, 1u) == gridDim.x - 1) {
-    __hip_atomic_store(a.queue, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(a.queue + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  if (threadIdx.x == 0 && atomicAdd(a.queue + 16, 1u) == gridDim.x - 1)
+    for (int i = 0; i <= 16; ++i) __hip_atomic_store(a.queue + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace
@@ -343,7 +362,7 @@ tsg_status tsg_op_moe_ag(tsg_ctx* ctx, const void* x_local, const void* x_peers,
   }
   ca.n_units = (int)n_units;
   ca.skip_mask = o.skip_mask;
-  ca.queue = ctx->d_queue + kQueueSlot + 2;  // not used: units come from the kernel's own queue
+  ca.queue = nullptr;  // not used: units come from the kernel's own queues
   ca.n_workers = 0;
   ca.pace_word = nullptr;
   ca.pace_ticks = 0.f;
@@ -365,7 +384,7 @@ tsg_status tsg_op_moe_ag(tsg_ctx* ctx, const void* x_local, const void* x_peers,
   ka.I = I;
   ka.n_slab = n_slab;
   ka.l1_only = ((uintptr_t)x_full % 128 == 0 && H % 64 == 0 && slab >= 64) ? 1 : 0;
-  const bool direct = H % (2 * Cfg::BK) == 0;
+  const bool direct = H % (2 * CfgOf<true>::BK) == 0;
 
   auto launch = [&](int n_copy, int n_tiles, int wait, int which) -> tsg_status {
     ka.n_copy = n_copy;

@@ -43,6 +43,7 @@ constexpr int kRouteThreads = 256;
 constexpr int kRouteWaves = kRouteThreads / 64;
 constexpr int kRouteMaxPairs = 65535;
 constexpr int kRouteLdsCounts = 4096;  // G x E counts kept in LDS (larger: read from memory)
+constexpr int kRouteMaskBlocks = 4096; // row blocks whose rank masks a block gathers in LDS
 
 struct RouteArgs {
   const int32_t* ids;
@@ -54,7 +55,11 @@ struct RouteArgs {
   int P, E, k, G;
   int64_t rows_max, n_rb_max;
   // Optional (AllGather + MoE): rb_mask[rb] receives bit c for every chunk c
-  // = token / tokens_per_rank that a row of block rb gathers from.
+  // = token / tokens_per_rank that a row of block rb gathers from.  Each
+  // placement block ORs its pairs' bits in LDS first and then ORs every
+  // nonzero word into rb_mask once (n_rb_max <= kRouteMaskBlocks): a block's
+  // pairs of one expert fill consecutive rows, so it touches few row blocks,
+  // and the global atomics per word drop from one per pair to one per block.
   uint32_t* rb_mask;
   int tokens_per_rank;
 };
@@ -119,9 +124,13 @@ __global__ void __launch_bounds__(kRouteThreads) moe_place_kernel(const RouteArg
   __shared__ int s_cnt[kRouteWaves][kMaxExperts];
   __shared__ int s_blk[kRouteLdsCounts];
   __shared__ int s_offs[kMaxExperts + 1], s_poffs[kMaxExperts + 1], s_pre[kMaxExperts];
+  __shared__ uint32_t s_mask[kRouteMaskBlocks];
   const int b = blockIdx.x, t = threadIdx.x, wave = t >> 6;
   const int E = a.E, G = a.G;
   const bool in_lds = G * E <= kRouteLdsCounts;
+  const bool mask_lds = a.rb_mask && a.n_rb_max <= kRouteMaskBlocks;
+  if (mask_lds)
+    for (int i = t; i < a.n_rb_max; i += kRouteThreads) s_mask[i] = 0u;
   const int p = b * kRouteThreads + t;
   const int e = p < a.P ? a.ids[p] : 0;
   if (in_lds)
@@ -177,9 +186,20 @@ __global__ void __launch_bounds__(kRouteThreads) moe_place_kernel(const RouteArg
     a.ws.pair_row[p] = row;
     a.ws.row_pair[row] = p;
     a.ws.row_token[row] = p / a.k;
-    if (a.rb_mask) atomicOr(a.rb_mask + row / BM, 1u << ((p / a.k) / a.tokens_per_rank));
+    if (a.rb_mask) {
+      const uint32_t bit = 1u << ((p / a.k) / a.tokens_per_rank);
+      if (mask_lds)
+        atomicOr(s_mask + row / BM, bit);
+      else
+        atomicOr(a.rb_mask + row / BM, bit);
+    }
   } else if (p < a.P) {
     a.ws.pair_row[p] = -1;  // dropped pair (bad expert id)
+  }
+  if (mask_lds) {
+    __syncthreads();
+    for (int i = t; i < a.n_rb_max; i += kRouteThreads)
+      if (s_mask[i]) atomicOr(a.rb_mask + i, s_mask[i]);
   }
   // rows that hold no pair: padding after each expert's pairs, and rows
   // past the last expert's
