@@ -375,6 +375,54 @@ def _path_ag(torch, tsg, ctx, cfg, n, opts, seed_sets=2):
     return fn, flops, gemm_bytes, copy_bytes, host
 
 
+def _moe_remote_first(torch, tsg, ctx, fn, flops, nbytes, n, ep_ranks=8, ep_rank=7):
+    """The MoE expert compute + combine with remote-critical tiles first
+    (tokens from 8 source ranks, this rank 7) beside the plain order: the
+    overlapped time of each, and from one call's device timeline of each, when
+    the last down tile of a remote-critical row block published its ready
+    signal (from then on every remote-bound output could be on its way), the
+    mean of those tiles' ready times, and when the last tile of all was
+    ready, in microseconds from the call's first record.
+    The blocks are classed by the source-rank masks the call left in the
+    workspace."""
+    import numpy as np
+    ws, dims = fn.workspace
+    lay = tsg.moe_workspace_layout(dims)
+    prio = tsg.Opts(ep_ranks=ep_ranks, ep_rank=ep_rank)
+    out = {"ep_ranks": ep_ranks, "ep_rank": ep_rank}
+    for label, opts in (("plain", tsg.Opts()), ("remote_first", prio)):
+        line = _path_line(tsg, Timer(torch, tsg, ctx, lambda i, mode, o_=None, o=opts: fn(i, mode, o)), flops,
+                          nbytes, (tsg.OVERLAP,), n)
+        tl = tsg.Opts(timeline=1, ep_ranks=opts.ep_ranks, ep_rank=opts.ep_rank)
+        fn(0, tsg.OVERLAP, tl)
+        if ctx.check() != tsg.OK:
+            raise RuntimeError(ctx.last_error())
+        recs = np.array(ctx.timeline(), dtype=np.uint64)
+        if label == "plain":
+            # the masks: one more call with the order on, timeline off
+            fn(0, tsg.OVERLAP, prio)
+            if ctx.check() != tsg.OK:
+                raise RuntimeError(ctx.last_error())
+        w = ws.cpu().numpy()
+        n_rb = int(w[lay["meta"]:lay["meta"] + 4].view(np.int32)[0])
+        mask = w[lay["rb_mask"]:lay["rb_mask"] + 4 * n_rb].view(np.uint32)
+        remote = (mask & ~np.uint32(1 << ep_rank)) != 0
+        kind = (recs[:, 0] >> np.uint64(56)).astype(np.int64)
+        rb = ((recs[:, 0] & np.uint64(0xFFFFFFFF)) >> np.uint64(16)).astype(np.int64)
+        t0 = recs[:, 1].astype(np.int64).min()
+        end = recs[:, 3].astype(np.int64)
+        down = kind == 8
+        rem = down & np.isin(rb, np.nonzero(remote)[0])
+        # device wall clock: 100 ticks per microsecond
+        line["remote_tiles_ready_us"] = round(float(end[rem].max() - t0) / 100.0, 2)
+        line["remote_tiles_mean_ready_us"] = round(float((end[rem] - t0).mean()) / 100.0, 2)
+        line["all_tiles_ready_us"] = round(float(end[down].max() - t0) / 100.0, 2)
+        line["call_us"] = round(float(end.max() - t0) / 100.0, 2)
+        out["remote_blocks"], out["blocks"] = int(remote.sum()), n_rb
+        out[label] = line
+    return out
+
+
 def _other_paths(torch, tsg, ctx):
     """The GEMM+RS, MLP and MoE paths at full size: name -> (fn(i, mode,
     opts=None), flops, algorithmic HBM bytes, modes the path has)."""
@@ -416,8 +464,9 @@ def _other_paths(torch, tsg, ctx):
     srt = torch.empty((T * k,), dtype=torch.int32, device="cuda")
     wsb = tsg.workspace_bytes(tsg.OP_MOE, [T, Hh, I, E, k])
     ws = torch.empty((wsb,), dtype=torch.uint8, device="cuda")
-    moe_fn = lambda i, mode, opts=None: tsg.moe_expert_combine(ctx, mx, ids, g, wu, wd, mo, cnt, srt, ws, wsb,
-                                                               T, Hh, I, E, k, opts=opts, mode=mode)
+    def moe_fn(i, mode, opts=None):
+        tsg.moe_expert_combine(ctx, mx, ids, g, wu, wd, mo, cnt, srt, ws, wsb, T, Hh, I, E, k, opts=opts, mode=mode)
+    moe_fn.workspace = (ws, [T, Hh, I, E, k])   # read back by the remote-critical line
     moe_flops = 4.0 * T * k * Hh * I
     moe_bytes = T * k * Hh * 2 + 2 * E * Hh * I * 2 + 2 * T * k * I * 2 + 2 * T * k * Hh * 4 + T * Hh * 4
     out["moe"] = (moe_fn, moe_flops, moe_bytes, (tsg.OVERLAP, tsg.SERIAL, tsg.COMPUTE_ONLY, tsg.COMM_ONLY))
@@ -697,6 +746,7 @@ def main():
         o16 = tsg.Opts(aux_cus=16)
         paths["moe_combine_16cu"] = _path_line(
             tsg, Timer(torch, tsg, ctx, lambda i, mode, o_=None: fn(i, mode, o16)), flops, nbytes, (tsg.OVERLAP,), n)
+        paths["moe_remote_first"] = _moe_remote_first(torch, tsg, ctx, fn, flops, nbytes, n)
 
     tflops = ag_flops / (ms_step * 1e-3) / 1e12
     achieved = ag_flops / (k_ov[0] * 1e-3) / 1e12

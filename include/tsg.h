@@ -172,6 +172,20 @@ typedef struct tsg_opts {
    * least 8 rows per channel (else TSG_E_SHAPE) and be at most 64
    * (else TSG_E_INVALID). */
   int channels;
+  /* MoE expert compute + combine: remote-critical tiles first (the MoE
+   * overlap page's producer, which covers all local experts and takes the
+   * tiles whose outputs go back to other ranks first, so that their return
+   * transfers start earliest).  The T tokens come from ep_ranks source
+   * ranks in contiguous blocks of T / ep_ranks; this rank is ep_rank.  A row
+   * block holding a pair of a token from another rank is remote-critical:
+   * the producer takes the up tiles, then the down tiles, then the combine
+   * units of those blocks before the others' (stable), and the table of the
+   * order is readable in the workspace (TSG_MOE_RB_ORDER).  Results are
+   * bit-identical to the plain row-block order.  0 = plain order (default);
+   * otherwise 1 <= ep_ranks <= 32, T % ep_ranks == 0 and 0 <= ep_rank <
+   * ep_ranks (else TSG_E_INVALID). */
+  int ep_ranks;
+  int ep_rank;
 } tsg_opts;
 
 /* ------------------------------------------------------------------ ctx */
@@ -518,6 +532,14 @@ size_t tsg_workspace_bytes(int op, const int64_t* dims);
  *   TSG_MOE_Y          [ROWS_MAX x H]: y of the pair in each row, fp32 (bf16
  *                      with stage_dtype = TSG_BF16; padding rows:
  *                      unspecified)
+ *   TSG_MOE_RB_ORDER   int32[RB_MAX]: with opts.ep_ranks > 0, the row blocks
+ *                      in use in the order the producer takes them
+ *                      (remote-critical first, each group by block index;
+ *                      entries past the blocks in use unspecified); not
+ *                      written otherwise
+ *   TSG_MOE_RB_MASK    uint32[RB_MAX]: with opts.ep_ranks > 0, bit c of
+ *                      entry rb set when a row of block rb holds a token of
+ *                      source rank c; not written otherwise
  * TSG_MOE_TOTAL = tsg_workspace_bytes; TSG_MOE_ROWS_MAX, TSG_MOE_RB_MAX:
  * the padded rows and row blocks the layout provides for; TSG_MOE_BM: rows
  * per block.  Returns TSG_E_SHAPE for dims moe_expert_combine rejects,
@@ -525,7 +547,7 @@ size_t tsg_workspace_bytes(int op, const int64_t* dims);
 enum {
   TSG_MOE_META = 0, TSG_MOE_OFFS, TSG_MOE_POFFS, TSG_MOE_RB_EXPERT, TSG_MOE_ROW_PAIR, TSG_MOE_ROW_TOKEN,
   TSG_MOE_PAIR_ROW, TSG_MOE_H, TSG_MOE_Y, TSG_MOE_TOTAL, TSG_MOE_ROWS_MAX, TSG_MOE_RB_MAX, TSG_MOE_BM,
-  TSG_MOE_LAYOUT_N
+  TSG_MOE_RB_ORDER, TSG_MOE_RB_MASK, TSG_MOE_LAYOUT_N
 };
 tsg_status tsg_moe_workspace_layout(const int64_t* dims, int64_t* out, int n);
 

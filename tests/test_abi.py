@@ -46,11 +46,12 @@ def test_binding_exports_match_header():
 def test_opts_struct_layout_matches_header(tmp_path):
     src = tmp_path / "sz.c"
     src.write_text('#include "tsg.h"\n#include <stdio.h>\n#include <stddef.h>\n'
-                   'int main(void){printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(tsg_opts), '
+                   'int main(void){printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(tsg_opts), '
                    'offsetof(tsg_opts, timeout_ms), offsetof(tsg_opts, timeline), offsetof(tsg_opts, comm_tile), '
                    'offsetof(tsg_opts, pull_units), offsetof(tsg_opts, stage_dtype), '
                    'offsetof(tsg_opts, arrival_gbps), offsetof(tsg_opts, copy_engine), '
-                   'offsetof(tsg_opts, channels));return 0;}\n')
+                   'offsetof(tsg_opts, channels), offsetof(tsg_opts, ep_ranks), offsetof(tsg_opts, ep_rank));'
+                   'return 0;}\n')
     exe = tmp_path / "sz"
     subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
     got = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()
@@ -61,7 +62,8 @@ def test_opts_struct_layout_matches_header(tmp_path):
     assert [int(v) for v in got] == [ctypes.sizeof(tsg.Opts), tsg.Opts.timeout_ms.offset, tsg.Opts.timeline.offset,
                                       tsg.Opts.comm_tile.offset, tsg.Opts.pull_units.offset,
                                       tsg.Opts.stage_dtype.offset, tsg.Opts.arrival_gbps.offset,
-                                      tsg.Opts.copy_engine.offset, tsg.Opts.channels.offset]
+                                      tsg.Opts.copy_engine.offset, tsg.Opts.channels.offset,
+                                      tsg.Opts.ep_ranks.offset, tsg.Opts.ep_rank.offset]
 
 
 @pytest.mark.skipif(not os.path.exists(LIB), reason="library not built")
@@ -82,8 +84,10 @@ def test_moe_workspace_layout_is_consistent():
     assert L["rows_max"] >= T * k + E * (L["bm"] - 1)
     sizes = {"meta": 8, "offs": 4 * (E + 1), "poffs": 4 * (E + 1), "rb_expert": 4 * L["rb_max"],
              "row_pair": 4 * L["rows_max"], "row_token": 4 * L["rows_max"], "pair_row": 4 * T * k,
-             "h": 2 * L["rows_max"] * I, "y": 4 * L["rows_max"] * H}
-    order = ["meta", "offs", "poffs", "rb_expert", "row_pair", "row_token", "pair_row", "h", "y"]
+             "rb_mask": 4 * L["rb_max"], "rb_order": 4 * L["rb_max"], "h": 2 * L["rows_max"] * I,
+             "y": 4 * L["rows_max"] * H}
+    order = ["meta", "offs", "poffs", "rb_expert", "row_pair", "row_token", "pair_row", "rb_mask", "rb_order", "h",
+             "y"]
     for a, b in zip(order, order[1:] + ["total"]):
         assert L[a] % 256 == 0 and L[a] + sizes[a] <= L[b], (a, b)
     with pytest.raises(tsg.TsgError):

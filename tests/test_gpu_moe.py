@@ -301,3 +301,82 @@ def test_moe_full_size_parity_modes_splits(env):
     out5, c5, s5 = case.run(opts={"stage_dtype": tsg.BF16})
     r5, _, _ = _check(case, out5, c5, s5, y_bf16=True, label="bf16 y staging")
     assert r5 <= 1.0
+
+
+def _remote_first_order(inp, E, bm, ep_ranks, ep_rank):
+    """Row blocks in remote-critical order, from the oracle's routing: the
+    blocks holding a pair of a token from another source rank (tokens of rank
+    c are [c T / ep_ranks, (c + 1) T / ep_ranks)), then the others, each group
+    by block index."""
+    ids = inp["topk_ids"]
+    T, k = ids.shape
+    counts, offsets, sorted_ids = oracle.moe_route(ids, E)
+    poff, tiles = oracle.moe_tile_table(counts, bm)
+    remote = []
+    for e, lo, n in tiles:
+        pairs = sorted_ids[offsets[e] + (lo - poff[e]):offsets[e] + (lo - poff[e]) + n]
+        remote.append(bool(np.any((pairs // k) // (T // ep_ranks) != ep_rank)))
+    first = [rb for rb, r in enumerate(remote) if r]
+    return np.array(first + [rb for rb, r in enumerate(remote) if not r], dtype=np.int32), remote
+
+
+def test_moe_remote_critical_order(env):
+    # opts.ep_ranks / ep_rank: the producer takes the row blocks holding a
+    # token of another rank first.  The tokens of rank 1 go to experts 0 and 1
+    # only and the others' to experts 2 and 3, so both kinds of block exist.
+    # The device's order table is the oracle's, and every output is
+    # bit-identical to the plain order's, in every mode and CU split.
+    torch, tsg, ctx = env
+    T, H, I, E, R, rank = 1024, 256, 128, 4, 4, 1
+    inp = moe_inputs(T, H, I, E, k=2, seed=37)
+    tpr = T // R
+    rng = np.random.default_rng(38)
+    ids = np.empty((T, 2), dtype=np.int32)
+    for t in range(T):
+        pool = [0, 1] if t // tpr == rank else [2, 3]
+        ids[t] = rng.permutation(pool)
+    inp["topk_ids"] = ids
+    case = MoeCase(env, inp)
+    out, counts, sorted_ids = case.run()
+    _check(case, out, counts, sorted_ids)
+    want, remote = _remote_first_order(inp, E, case.lay["bm"], R, rank)
+    assert any(remote) and not all(remote)
+    prio = {"ep_ranks": R, "ep_rank": rank}
+    for mode, opts in ((tsg.OVERLAP, prio), (tsg.OVERLAP, dict(prio, aux_cus=16)), (tsg.SERIAL, prio),
+                       (tsg.COMPUTE_ONLY, prio)):
+        o2, c2, s2 = case.run(mode=mode, opts=opts)
+        assert np.array_equal(c2, counts) and np.array_equal(s2, sorted_ids)
+        n_rb = int(case.tables()["meta"][0])
+        L = case.lay
+        got = case.ws.cpu().numpy()[L["rb_order"]:L["rb_order"] + 4 * n_rb].view(np.int32)
+        assert np.array_equal(got, want), (mode, opts)
+        if mode != tsg.COMPUTE_ONLY:
+            assert np.array_equal(o2, out), (mode, opts)
+    # the combine alone over the staging of the last call: plain order
+    o3, _, _ = case.run(mode=tsg.COMM_ONLY, opts=prio)
+    assert np.array_equal(o3, out)
+    for bad in ({"ep_ranks": 3, "ep_rank": 0}, {"ep_ranks": 4, "ep_rank": 4}, {"ep_ranks": 33, "ep_rank": 0},
+                {"ep_ranks": -1, "ep_rank": 0}):
+        with pytest.raises(tsg.TsgError):
+            case.run(opts=bad)
+
+
+def test_moe_remote_critical_order_full_size(env):
+    # the Zipf-routed workload with 8 source ranks: each expert's rows are in
+    # token order, so a row block spans few source ranks and some hold only
+    # this rank's tokens; the order table matches the oracle's and out is
+    # bit-identical to the plain order's
+    torch, tsg, ctx = env
+    cfg = CONFIGS["moe"]
+    inp = moe_inputs(cfg["T"], cfg["H"], cfg["I"], cfg["E"], k=cfg["k"], seed=cfg["seed"], zipf=cfg["zipf"])
+    case = MoeCase(env, inp)
+    out, counts, sorted_ids = case.run()
+    for rank in (0, 7):
+        want, remote = _remote_first_order(inp, cfg["E"], case.lay["bm"], 8, rank)
+        o2, _, _ = case.run(opts={"ep_ranks": 8, "ep_rank": rank})
+        assert np.array_equal(o2, out)
+        n_rb = len(want)
+        L = case.lay
+        got = case.ws.cpu().numpy()[L["rb_order"]:L["rb_order"] + 4 * n_rb].view(np.int32)
+        assert np.array_equal(got, want), rank
+        print(f"rank {rank}: {sum(remote)} of {n_rb} row blocks remote-critical")

@@ -46,7 +46,7 @@ MOE_NOALLOC_BYTES = 64 << 20   # the static workspace of moe_expert_combine_noal
 
 # fields of tsg_moe_workspace_layout, in order
 MOE_LAYOUT_FIELDS = ("meta", "offs", "poffs", "rb_expert", "row_pair", "row_token", "pair_row", "h", "y",
-                     "total", "rows_max", "rb_max", "bm")
+                     "total", "rows_max", "rb_max", "bm", "rb_order", "rb_mask")
 
 
 class Opts(ctypes.Structure):
@@ -65,6 +65,8 @@ class Opts(ctypes.Structure):
         ("arrival_gbps", ctypes.c_int),
         ("copy_engine", ctypes.c_int),
         ("channels", ctypes.c_int),
+        ("ep_ranks", ctypes.c_int),
+        ("ep_rank", ctypes.c_int),
     ]
 
 

@@ -55,6 +55,8 @@ Opts resolve(const tsg_opts* o, int default_aux_cus) {
   r.arrival_gbps = o ? o->arrival_gbps : 0;
   r.copy_engine = o ? o->copy_engine : 0;
   r.channels = o ? o->channels : 0;
+  r.ep_ranks = o ? o->ep_ranks : 0;
+  r.ep_rank = o ? o->ep_rank : 0;
   return r;
 }
 

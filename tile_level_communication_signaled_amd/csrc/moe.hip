@@ -63,7 +63,7 @@ static_assert(CfgDn::NT == kProdThreads, "up and down tiles share the workgroup"
 
 // Workspace layout (byte offsets, 256-aligned).
 struct Layout {
-  size_t meta, offs, poffs, rb_expert, row_pair, row_token, pair_row, h, y, total;
+  size_t meta, offs, poffs, rb_expert, row_pair, row_token, pair_row, rb_mask, rb_order, h, y, total;
   int64_t n_rb_max, rows_max;
 };
 
@@ -82,6 +82,8 @@ Layout layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k) {
   L.row_pair = o;  o += up256(L.rows_max * 4);
   L.row_token = o; o += up256(L.rows_max * 4);
   L.pair_row = o;  o += up256(pairs * 4);
+  L.rb_mask = o;   o += up256(L.n_rb_max * 4);
+  L.rb_order = o;  o += up256(L.n_rb_max * 4);
   L.h = o;         o += up256(L.rows_max * I * 2);
   L.y = o;         o += up256(L.rows_max * H * 4);
   L.total = o;
@@ -89,6 +91,8 @@ Layout layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k) {
 }
 
 struct Ws : MoeTables {
+  uint32_t* rb_mask;  // source ranks of each row block's tokens (remote-critical order only)
+  int* rb_order;      // row blocks in producer order (remote-critical order only)
   uint16_t* h;
   float* y;
 };
@@ -102,6 +106,8 @@ Ws bind(char* base, const Layout& L) {
   w.row_pair = (int*)(base + L.row_pair);
   w.row_token = (int*)(base + L.row_token);
   w.pair_row = (int*)(base + L.pair_row);
+  w.rb_mask = (uint32_t*)(base + L.rb_mask);
+  w.rb_order = (int*)(base + L.rb_order);
   w.h = (uint16_t*)(base + L.h);
   w.y = (float*)(base + L.y);
   return w;
@@ -153,6 +159,7 @@ struct CombArgs {
   int n_dn_nt, n_rb_max;
   int wait;
   int y_bf16;             // y staging holds bf16 (else fp32)
+  const int* rb_order;    // row block at each position of the producer order (null: identity)
 };
 
 struct ProdArgs {
@@ -175,6 +182,7 @@ struct ProdArgs {
   uint32_t skip_mask;     // row blocks (mod 32) whose up tiles never arrive (test hook)
   int y_bf16;             // y staging holds bf16 (else fp32)
   int h_l1_only;          // h rows are whole 128-byte lines: acquire invalidates L1 only
+  const int* rb_order;    // row block at each position of the tile order (null: identity)
 };
 
 
@@ -182,9 +190,12 @@ struct ProdArgs {
 
 // Combine consumer.  Unit = one down tile (BM rows x BN_DN columns of y),
 // in the producer's order (row block major).  A token is combined by the
-// later of the two row blocks holding its slots, so every token is written
-// exactly once: out[t] = g0 * y(slot 0) + g1 * y(slot 1), products and sum
-// rounded in that order (an absent slot contributes 0).
+// higher-numbered of the two row blocks holding its slots (when both slots
+// sit in one block, both rows write the same value): out[t] = g0 * y(slot
+// 0) + g1 * y(slot 1), products and sum rounded in that order (an absent
+// slot contributes 0).  The units come after every down tile in the
+// producer's queue, so the partner tiles a unit waits for were taken
+// before it, whatever the order of the row blocks.
 //   1. Threads 0..BM-1 read the routing of the unit's rows (pair, partner
 //      row, token, gates) into LDS, and list the partner row blocks that
 //      precede this one (their tiles must be ready too), once each.
@@ -340,17 +351,18 @@ __global__ void __launch_bounds__(256) moe_combine_kernel(const CombArgs a) {
   const int n_rb = __builtin_amdgcn_readfirstlane(a.ws.meta[0]);
   const int n_units = a.n_rb_max * a.n_dn_nt;
   for (int u = blockIdx.x; u < n_units; u += gridDim.x) {
-    const int rb = u / a.n_dn_nt, nt = u % a.n_dn_nt;
-    if (rb >= n_rb) break;                   // units are rb-major: the rest are empty too
+    const int ord = u / a.n_dn_nt, nt = u % a.n_dn_nt;
+    if (ord >= n_rb) break;                  // units are rb-major: the rest are empty too
+    const int rb = a.rb_order ? __builtin_amdgcn_readfirstlane(a.rb_order[ord]) : ord;
     combine_unit(a, rb, nt, scratch);
   }
 }
 
 // Persistent producer: up tiles, then down tiles, then (fused mode) the
-// combine units, all from one ticket queue.  Every item waits only for
-// earlier items (down tiles for their row block's up tiles, combine units for
-// down tiles), which running workgroups took before it and complete without
-// waiting on later ones.
+// combine units, all from one ticket queue, row blocks in the tile order
+// (plain, or remote-critical blocks first).  Every item waits only for earlier items (down tiles for their row
+// block's up tiles, combine units for down tiles), which running workgroups
+// took before it and complete without waiting on later ones.
 template <bool DIRECT_UP, bool DIRECT_DN>
 __global__ void __launch_bounds__(kProdThreads) moe_producer_kernel(const ProdArgs a) {
   constexpr int LUP = DIRECT_UP ? CfgUp::LDS_DIRECT : CfgUp::LDS_REGS;
@@ -379,15 +391,18 @@ __global__ void __launch_bounds__(kProdThreads) moe_producer_kernel(const ProdAr
   };
   for (int item = fetch(); item < a.n_items; item = fetch()) {
     const uint64_t t0 = a.tl.buf ? wall_clock64() : 0;
+    // item -> (kind, position ord in the tile order, column tile); then
+    // ord -> row block (positions past the blocks in use stay past them)
+    const bool comb = item >= a.n_prod_items;
+    const bool up = item < n_up;
+    const int j = comb ? item - a.n_prod_items : up ? item : item - n_up;
+    const int ntc = up ? a.n_up_nt : a.n_dn_nt;
+    const int ord = j / ntc, nt = j - ord * ntc;
+    const int rb = a.rb_order && ord < n_rb ? __builtin_amdgcn_readfirstlane(a.rb_order[ord]) : ord;
     // no `continue`: the loop keeps a single back edge through the fetch
-    if (item >= a.n_prod_items) {            // combine unit (fused mode)
-      const int cu = item - a.n_prod_items;
-      const int rb = cu / a.n_dn_nt, nt = cu % a.n_dn_nt;
+    if (comb) {                              // combine unit (fused mode)
       if (rb < n_rb) combine_unit(a.comb, rb, nt, lds);
     } else {
-      const bool up = item < n_up;
-      const int rb = up ? item / a.n_up_nt : (item - n_up) / a.n_dn_nt;
-      const int nt = up ? item % a.n_up_nt : (item - n_up) % a.n_dn_nt;
       if (rb < n_rb && up) {
         const int e = __builtin_amdgcn_readfirstlane(a.ws.rb_expert[rb]);
         const int col0 = nt * BN_UP;
@@ -493,7 +508,7 @@ bool tsg_moe_layout_fields(const int64_t* d, int64_t* out, int n) {
                                        (int64_t)L.rb_expert, (int64_t)L.row_pair, (int64_t)L.row_token,
                                        (int64_t)L.pair_row,  (int64_t)L.h,        (int64_t)L.y,
                                        (int64_t)L.total,     L.rows_max,          L.n_rb_max,
-                                       (int64_t)BM};
+                                       (int64_t)BM,          (int64_t)L.rb_order, (int64_t)L.rb_mask};
   for (int i = 0; i < n && i < TSG_MOE_LAYOUT_N; ++i) out[i] = f[i];
   return true;
 }
@@ -540,6 +555,14 @@ tsg_status tsg_op_moe(tsg_ctx* ctx, const void* x, const int32_t* topk_ids, cons
   const Opts o = resolve(opts, -1);
   if (o.stage_dtype != TSG_F32 && o.stage_dtype != TSG_BF16)
     return fail(ctx, TSG_E_INVALID, "moe_expert_combine: stage_dtype must be TSG_F32 or TSG_BF16");
+  if (o.ep_ranks < 0 || o.ep_ranks > kRouteMaxRanks ||
+      (o.ep_ranks > 0 && (T % o.ep_ranks || o.ep_rank < 0 || o.ep_rank >= o.ep_ranks)))
+    return fail(ctx, TSG_E_INVALID,
+                "moe_expert_combine: need 0 <= ep_ranks <= %d, T a multiple of ep_ranks and 0 <= ep_rank < ep_ranks "
+                "(T=%d ep_ranks=%d ep_rank=%d)", kRouteMaxRanks, T, o.ep_ranks, o.ep_rank);
+  if (o.ep_ranks > 0 && L.n_rb_max > kRouteMaskBlocks)
+    return fail(ctx, TSG_E_UNSUPPORTED, "moe_expert_combine: remote-critical order supports %d row blocks",
+                kRouteMaskBlocks);
   // Everything on the caller's stream: no stream is created and no memset
   // is recorded (the timeline counter would need one).
   if (noalloc && (o.aux_cus > 0 || o.timeline))
@@ -565,8 +588,18 @@ tsg_status tsg_op_moe(tsg_ctx* ctx, const void* x, const int32_t* topk_ids, cons
   ra.G = (ra.P + kRouteThreads - 1) / kRouteThreads;
   ra.rows_max = L.rows_max;
   ra.n_rb_max = L.n_rb_max;
-  ra.rb_mask = nullptr;
-  ra.tokens_per_rank = 1;
+  // remote-critical order: each row block's source ranks, then the order
+  // (blocks with a token of another rank first)
+  const bool prio = o.ep_ranks > 0;
+  ra.rb_mask = prio ? ws.rb_mask : nullptr;
+  ra.tokens_per_rank = prio ? T / o.ep_ranks : 1;
+  RbOrderArgs oa;
+  oa.meta = ws.meta;
+  oa.rb_mask = ws.rb_mask;
+  oa.rb_order = ws.rb_order;
+  for (int c = 0; c < kRouteMaxRanks; ++c) oa.key_of[c] = c == o.ep_rank ? 1 : 0;
+  oa.R = prio ? o.ep_ranks : 1;
+  oa.min_key = 1;
   // the per-block counts use the start of the y staging area, which only
   // the down tiles write, after the routing (G E ints, far below its size)
   ra.blk = (int*)ws.y;
@@ -593,6 +626,7 @@ tsg_status tsg_op_moe(tsg_ctx* ctx, const void* x, const int32_t* topk_ids, cons
   pa.skip_mask = o.skip_mask;
   pa.y_bf16 = o.stage_dtype == TSG_BF16 ? 1 : 0;
   pa.h_l1_only = ((uintptr_t)ws.h % 128 == 0 && ((int64_t)I * 2) % 128 == 0) ? 1 : 0;
+  pa.rb_order = prio ? ws.rb_order : nullptr;
 
   CombArgs ca;
   ca.topk_w = topk_w;
@@ -606,13 +640,19 @@ tsg_status tsg_op_moe(tsg_ctx* ctx, const void* x, const int32_t* topk_ids, cons
   ca.n_dn_nt = n_dn_nt;
   ca.n_rb_max = (int)L.n_rb_max;
   ca.y_bf16 = pa.y_bf16;
+  // comm-only runs on the previous call's tables, whose order may not exist:
+  // the combine's results do not depend on its order
+  ca.rb_order = mode == TSG_MODE_COMM_ONLY ? nullptr : pa.rb_order;
 
   auto route = [&]() -> tsg_status {
     hipLaunchKernelGGL(moe_count_kernel<BM>, dim3(ra.G), dim3(kRouteThreads), 0, caller, ra);
     tsg_status rs = check_launch(ctx, "moe_count_kernel");
     if (rs != TSG_OK) return rs;
     hipLaunchKernelGGL(moe_place_kernel<BM>, dim3(ra.G), dim3(kRouteThreads), 0, caller, ra);
-    return check_launch(ctx, "moe_place_kernel");
+    rs = check_launch(ctx, "moe_place_kernel");
+    if (rs != TSG_OK || !prio) return rs;
+    hipLaunchKernelGGL(moe_rb_order_kernel<>, dim3(1), dim3(256), 0, caller, oa);
+    return check_launch(ctx, "moe_rb_order_kernel");
   };
   auto produce = [&](hipStream_t s, int nwg) -> tsg_status {
     const bool du = H % (2 * CfgUp::BK) == 0, dd = I % (2 * CfgDn::BK) == 0;

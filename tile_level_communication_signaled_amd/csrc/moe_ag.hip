@@ -17,7 +17,7 @@
 //      path): expert_counts, sorted_ids and the padded row tables, plus the
 //      rank mask of every row block (bit c: a row of the block gathers a
 //      token of chunk c) -- the dynamic rank mapping f_R of the block.
-//   2. moe_ag_order_kernel (one workgroup): orders the row blocks by the
+//   2. moe_rb_order_kernel (one workgroup): orders the row blocks by the
 //      arrival position of the last chunk they need (stable), so tiles
 //      whose tokens arrive first run first -- the tile order follows the
 //      arrival order, as in the AllGather GEMM's swizzle, but read from the
@@ -87,44 +87,6 @@ Layout layout(int64_t T, int64_t E, int64_t k) {
   L.rb_order = o;  o += up256(L.n_rb_max * 4);
   L.total = o;
   return L;
-}
-
-// Row blocks in order of the arrival position of the last chunk each needs
-// (pos_of[c]: arrival position of chunk c), ties by block index.  One
-// workgroup; at most kMaxRowBlocks blocks.
-struct OrderArgs {
-  const int* meta;
-  const uint32_t* rb_mask;
-  int* rb_order;
-  int pos_of[kMaxRanks];
-  int R;
-};
-
-__global__ void __launch_bounds__(256) moe_ag_order_kernel(const OrderArgs a) {
-  __shared__ int s_hist[kMaxRanks + 1];
-  __shared__ int s_key[kMaxRowBlocks];
-  const int n_rb = a.meta[0];
-  const int t = threadIdx.x;
-  if (t <= kMaxRanks) s_hist[t] = 0;
-  __syncthreads();
-  for (int rb = t; rb < n_rb; rb += 256) {
-    const uint32_t m = a.rb_mask[rb];
-    int key = 0;
-    for (int c = 0; c < a.R; ++c)
-      if ((m >> c) & 1u) key = max(key, a.pos_of[c]);
-    s_key[rb] = key;
-    atomicAdd(&s_hist[key], 1);
-  }
-  __syncthreads();
-  if (t == 0) {  // exclusive scan over the keys, then a stable placement
-    int run = 0;
-    for (int key = 0; key < a.R; ++key) {
-      const int c = s_hist[key];
-      s_hist[key] = run;
-      run += c;
-    }
-    for (int rb = 0; rb < n_rb; ++rb) a.rb_order[s_hist[s_key[rb]]++] = rb;
-  }
 }
 
 struct AgMoeArgs {
@@ -332,11 +294,12 @@ tsg_status tsg_op_moe_ag(tsg_ctx* ctx, const void* x_local, const void* x_peers,
   ra.rb_mask = rb_mask;
   ra.tokens_per_rank = chunk_rows;
 
-  OrderArgs oa;
+  RbOrderArgs oa;
   oa.meta = tab.meta;
   oa.rb_mask = rb_mask;
   oa.rb_order = rb_order;
-  for (int i = 0; i < kMaxRanks; ++i) oa.pos_of[i] = pos_of[i] < 0 ? 0 : pos_of[i];
+  for (int i = 0; i < kRouteMaxRanks; ++i) oa.key_of[i] = i < kMaxRanks && pos_of[i] >= 0 ? pos_of[i] : 0;
+  oa.min_key = 0;
   oa.R = R;
 
   CopyArgs ca;
@@ -405,8 +368,8 @@ tsg_status tsg_op_moe_ag(tsg_ctx* ctx, const void* x_local, const void* x_peers,
     if (st != TSG_OK) return st;
     hipLaunchKernelGGL(moe_place_kernel<BM>, dim3(ra.G), dim3(256), 0, caller, ra);
     if ((st = check_launch(ctx, "moe_place_kernel")) != TSG_OK) return st;
-    hipLaunchKernelGGL(moe_ag_order_kernel, dim3(1), dim3(256), 0, caller, oa);
-    if ((st = check_launch(ctx, "moe_ag_order_kernel")) != TSG_OK) return st;
+    hipLaunchKernelGGL(moe_rb_order_kernel<>, dim3(1), dim3(256), 0, caller, oa);
+    if ((st = check_launch(ctx, "moe_rb_order_kernel")) != TSG_OK) return st;
   }
   switch (mode) {
     case TSG_MODE_OVERLAP: return launch((int)n_units, n_tiles, 1, 0);

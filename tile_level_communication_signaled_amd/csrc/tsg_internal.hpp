@@ -83,6 +83,8 @@ struct Opts {
   int arrival_gbps; // AG arrival pacing, 0 = none
   int copy_engine;  // AG: 1 = DMA copy engines move the data
   int channels;     // AG: signals per rank (0 = 1)
+  int ep_ranks;     // MoE: source ranks of the tokens (0 = plain tile order)
+  int ep_rank;      // MoE: this rank among them
 };
 Opts resolve(const tsg_opts* o, int default_aux_cus);
 

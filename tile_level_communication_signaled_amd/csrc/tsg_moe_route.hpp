@@ -215,4 +215,54 @@ __global__ void __launch_bounds__(kRouteThreads) moe_place_kernel(const RouteArg
   for (int64_t q = (int64_t)s_offs[E] + p; q < a.P; q += stride) a.sorted_ids[q] = -1;
 }
 
+// ------------------------------------------------------------ block order
+// The row blocks in use (meta[0] of them), ordered by a key taken from each
+// block's rank mask: key(rb) = the largest (smallest, with min_key) of
+// key_of[c] over the ranks c in rb_mask[rb], ties by block index (a stable
+// counting sort).  The AllGather + MoE path keys a block by the arrival
+// position of the last chunk it gathers from; the expert-compute path puts
+// the blocks holding any token of another rank first.  One workgroup; at
+// most kRouteMaskBlocks blocks, keys in [0, kRouteMaxRanks).
+constexpr int kRouteMaxRanks = 32;
+
+struct RbOrderArgs {
+  const int* meta;
+  const uint32_t* rb_mask;
+  int* rb_order;
+  int key_of[kRouteMaxRanks];
+  int R;
+  int min_key;
+};
+
+// (a template, like the routing kernels, so that every translation unit
+// including this header may instantiate it)
+template <int MAX_BLOCKS = kRouteMaskBlocks>
+__global__ void __launch_bounds__(256) moe_rb_order_kernel(const RbOrderArgs a) {
+  __shared__ int s_hist[kRouteMaxRanks + 1];
+  __shared__ int s_key[MAX_BLOCKS];
+  const int n_rb = min(a.meta[0], MAX_BLOCKS);
+  const int t = threadIdx.x;
+  if (t <= kRouteMaxRanks) s_hist[t] = 0;
+  __syncthreads();
+  for (int rb = t; rb < n_rb; rb += 256) {
+    const uint32_t m = a.rb_mask[rb];
+    int key = a.min_key ? kRouteMaxRanks - 1 : 0;
+    for (int c = 0; c < a.R; ++c)
+      if ((m >> c) & 1u) key = a.min_key ? min(key, a.key_of[c]) : max(key, a.key_of[c]);
+    key = min(max(key, 0), kRouteMaxRanks - 1);
+    s_key[rb] = key;
+    atomicAdd(&s_hist[key], 1);
+  }
+  __syncthreads();
+  if (t == 0) {  // exclusive scan over the keys, then a stable placement
+    int run = 0;
+    for (int key = 0; key < kRouteMaxRanks; ++key) {
+      const int c = s_hist[key];
+      s_hist[key] = run;
+      run += c;
+    }
+    for (int rb = 0; rb < n_rb; ++rb) a.rb_order[s_hist[s_key[rb]]++] = rb;
+  }
+}
+
 }  // namespace tsg
