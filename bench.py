@@ -100,7 +100,7 @@ CALIB_BYTES = 1 << 30   # the plain device copy that --counters runs: 1 GiB read
 
 KERNELS = ("ag_gemm_kernel", "ag_copy_kernel", "rs_gemm_kernel", "rs_reduce_kernel", "mlp_gemm1_kernel",
            "mlp_gemm2_kernel", "mlp_fused_kernel", "moe_count_kernel", "moe_place_kernel", "moe_producer_kernel",
-           "moe_combine_kernel", "moe_ag_order_kernel", "moe_ag_kernel", "ag_attn_kernel")
+           "moe_combine_kernel", "moe_rb_order_kernel", "moe_ag_kernel", "ag_attn_kernel", "ag_attn_copy_kernel")
 
 
 def summarize_counters(fetch_csv: str, write_csv: str, out_path: str = TRAFFIC) -> dict:
@@ -661,6 +661,10 @@ def main():
                 if name == "moe_bf16_staging":   # same kernel names: keep the record to one variant
                     continue
                 for mode in (tsg.COMPUTE_ONLY, tsg.COMM_ONLY):
+                    # the gather-side and attention kernels run their copy
+                    # alone under their own names: compute-only launches only
+                    if mode == tsg.COMM_ONLY and name in ("moe_ag", "ag_kv_attention"):
+                        continue
                     if mode in modes:
                         for i in range(args.steps):
                             fn(i, mode)

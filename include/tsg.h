@@ -131,8 +131,10 @@ typedef struct tsg_opts {
    * the consumer pulls the head of the data ([TL] Table 3, tile_pull_data),
    * so compute need not wait for the copy kernel to be scheduled.  Units not
    * taken by the GEMM are moved by the copy kernel from the same queue.
-   * 0 = the op's default (one unit per CU, at most the first slab's units),
-   * -1 = none.  AllGather KV + attention, overlapped: > 0 = the attention
+   * 0 = the op's default (one unit per CU, at most the first slab's units;
+   * when the whole copy is at most 1 MiB, every unit: each GEMM workgroup
+   * takes units until none is left, and no copy kernel or second stream is
+   * used), -1 = none.  AllGather KV + attention, overlapped: > 0 = the attention
    * workgroups take every copy unit from their own queue before the tiles;
    * 0 or -1 = a copy kernel runs beside them. */
   int pull_units;

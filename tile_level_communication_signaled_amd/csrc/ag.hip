@@ -50,6 +50,7 @@ constexpr size_t kSigCap = size_t(1) << 18;   // slots up to the next op's regio
 constexpr int kQueueSlot = 40;                // copy work queue in the context's ticket words
 constexpr size_t kPaceSlot = 8;               // arrival-pacing start time in the context's pool
 constexpr int kMaxChannels = 64;               // channels per rank
+constexpr int64_t kPullAllBytes = 1 << 20;     // overlap: copies up to this size run inside the GEMM
 
 // Copy kernel: takes units from the queue in order (slab-major) until none
 // is left.  It never waits, so it always drains the queue.
@@ -92,6 +93,7 @@ struct AgGemmArgs {
   int l1_only;            // slabs never share a 128-byte line
   int per_xcd;            // resident tiles per XCD (0 = no XCD remap)
   int pull_wgs;           // workgroups 0 .. pull_wgs - 1 first move one copy unit each
+  int pull_all;           // ... or every unit left in the queue (the whole copy; no copy kernel)
   CopyArgs copy;
   uint16_t mt_order[kMaxMTiles];
 };
@@ -162,14 +164,14 @@ __global__ void __launch_bounds__(Cfg::NT) ag_gemm_kernel(const AgGemmArgs args)
   const int nt = w % args.n_tiles_n;
   const int row0 = mt * Cfg::BM, col0 = nt * Cfg::BN;
   const uint64_t t0 = args.tl.buf ? wall_clock64() : 0;
-  if constexpr (Cfg::NT == 256 || Cfg::NT == 512) {
-    if ((int)blockIdx.x < args.pull_wgs) {
-      // tile_pull_data: move one unit of the copy's queue before any wait
-      // (the LDS is not in use yet, so its first word carries the ticket)
-      const int u = claim_unit(args.copy, (volatile int*)lds);
-      if (u < args.copy.n_units) copy_unit<Cfg::NT>(args.copy, u);
-      if (threadIdx.x == 0) leave_queue(args.copy);
-    }
+  if ((int)blockIdx.x < args.pull_wgs) {
+    // tile_pull_data: move one unit of the copy's queue before any wait, or
+    // with pull_all every unit left (the LDS is not in use yet, so its first
+    // word carries the ticket)
+    for (int u = claim_unit(args.copy, (volatile int*)lds); u < args.copy.n_units;
+         u = args.pull_all ? claim_unit(args.copy, (volatile int*)lds) : args.copy.n_units)
+      copy_unit<Cfg::NT>(args.copy, u);
+    if (threadIdx.x == 0) leave_queue(args.copy);
   }
   SlabWait hook;
   hook.active = false;
@@ -464,6 +466,15 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
     const tsg_status ss = streams(ctx, o, &pr, (hipStream_t)stream);
     if (ss != TSG_OK) return ss;
   }
+  // A copy of at most kPullAllBytes (every chunk together) is moved by the
+  // GEMM's own workgroups, each taking units until none is left before its
+  // first wait: one launch on the caller's stream, no copy kernel and no
+  // second stream, whose fork and join would cost more than such a copy.
+  // Every unit is then taken by a running workgroup before any waits, so the
+  // queue drains whatever the grid.  The units are sized for the GEMM's grid.
+  const bool pull_all = mode == TSG_MODE_OVERLAP && o.aux_cus < 0 && o.pull_units == 0 && !o.copy_engine &&
+                        o.arrival_gbps == 0 && (int64_t)R * chunk_rows * K * 2 <= kPullAllBytes;
+  if (pull_all) nwg = n_mt * n_nt;
   int np[kHead + 1], ustart[kHead + 1];
   int64_t n_units = 0;
   if (!copy_plan(R, C, chunk_rows, K, n_slab, vpr_log2, nwg, np, ustart, &n_units))
@@ -558,13 +569,16 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
   int pull = 0;
   int gemm_nt = 0;
   (void)gemm_fn(tile, c_dtype == TSG_BF16, K, &gemm_nt);
-  if (mode == TSG_MODE_OVERLAP && !back_to_back && o.aux_cus < 0 && o.pull_units >= 0 && !o.copy_engine &&
-      (gemm_nt == 256 || gemm_nt == 512)) {
+  if (pull_all) {
+    pull = grid_gemm;
+  } else if (mode == TSG_MODE_OVERLAP && !back_to_back && o.aux_cus < 0 && o.pull_units >= 0 && !o.copy_engine &&
+             (gemm_nt == 256 || gemm_nt == 512)) {
     pull = o.pull_units > 0 ? o.pull_units : std::min(ctx->n_cus, ustart[1]);
     pull = (int)std::min<int64_t>(std::min(pull, grid_gemm), n_units);
   }
-  ca.n_workers = (uint32_t)(copy_grid + pull);
+  ca.n_workers = (uint32_t)(pull_all ? pull : copy_grid + pull);
   ga.pull_wgs = 0;
+  ga.pull_all = pull_all ? 1 : 0;
   ga.copy = ca;
 
   auto gemm = [&](hipStream_t s, int wait, int cus) -> tsg_status {
@@ -667,6 +681,7 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
   };
 
   tsg_status st = TSG_OK;
+  if (pull_all) return gemm(caller, 1, ctx->n_cus);
   if (back_to_back) {
     st = copy(caller);
     if (st == TSG_OK) st = gemm(caller, 1, ctx->n_cus);

@@ -128,8 +128,8 @@ __device__ __forceinline__ void copy_unit(const CopyArgs& a, int u) {
   // t mod tpr (+ NT when the row is wider than the workgroup) of rows
   // t / tpr, t / tpr + rows_p, ...  Addresses are a uniform base plus a
   // 32-bit byte offset (one register per access).
-  static_assert(NT == 256 || NT == 512, "copy workgroups of 256 or 512 threads");
-  constexpr int NT_LOG2 = NT == 256 ? 8 : 9;
+  static_assert(NT == 64 || NT == 128 || NT == 256 || NT == 512, "copy workgroups of 64 to 512 threads");
+  constexpr int NT_LOG2 = NT == 64 ? 6 : NT == 128 ? 7 : NT == 256 ? 8 : 9;
   const int wpr = 2 * vpr;
   const int tpr_log2 = min(a.vpr_log2 + 1, NT_LOG2);
   const int tpr = 1 << tpr_log2;
