@@ -155,10 +155,10 @@ typedef struct tsg_opts {
    * copy engines, transfers issued on several streams at once, each signal
    * sent as a separate data transfer).  Each chunk gets a stream of its own;
    * on it every channel of the chunk is one hipMemcpyAsync with
-   * hipMemcpyDeviceToDeviceNoCU, followed by an 8-byte NoCU copy of the
-   * call's signal value (kept in an allocation of its own, so that the
-   * runtime hands it to a DMA engine, not to a kernel) into the channel's
-   * signal word.  comm_tile does not apply (one slab: whole rows), the GEMM
+   * hipMemcpyDeviceToDeviceNoCU, followed by a 64 KB NoCU copy that ends
+   * with the call's signal value into the channel's 64 KB signal block,
+   * whose last word the GEMM polls (the runtime runs device copies below
+   * 64 KB as kernels on the CUs, larger ones on the DMA engines).  comm_tile does not apply (one slab: whole rows), the GEMM
    * pulls nothing, and no CU runs any part of the transfer, so overlap runs
    * on shared CUs.  0 = the CU copy kernel (default).  Other values, or
    * together with arrival_gbps: TSG_E_INVALID. */

@@ -31,12 +31,13 @@
 // channel 1, and so on: sub-chunks arrive from all peers at each step (the
 // Triton-distributed page, section 3.7, the full-mesh swizzle of Figure 8).
 //
-// Copy-engine arrival (opts.copy_engine): the same signals are set by the DMA
+// Copy-engine arrival (opts.copy_engine): the signals are set by the DMA
 // engines instead of a kernel (the Triton-distributed page, section 3.6: AMD
 // intra-node AllGather with copy engines on several streams at once, the
 // signal sent as a separate data transfer).  One stream per chunk copies the
-// chunk channel by channel, each channel followed by an 8-byte copy of the
-// call's signal value into that channel's signal word.
+// chunk channel by channel, each channel followed by a copy that sets the
+// channel's signal: 64 KB, because the runtime runs smaller device copies as
+// kernels on the CUs, ending with the call's signal value.
 #include "tsg_copy.hpp"
 #include "tsg_gemm.hpp"
 #include "tsg_internal.hpp"
@@ -66,7 +67,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_num_vgpr(16))) ag_c
 
 // Copy-engine arrival: entry i of the signal-value ring holds {base + i | 1},
 // the value a channel signal takes in the call whose epoch is base + i.  The
-// DMA engines copy the call's entry into each channel's signal word.
+// DMA engines copy the 64 KB window of the ring that ends with the call's
+// entry into each channel's signal block, whose last word is its signal.
 __global__ void ag_dma_ring_kernel(uint64_t* ring, int n, uint32_t base) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
     ring[i] = sig_target(base + (uint32_t)i, 1u);
@@ -78,7 +80,8 @@ struct AgGemmArgs {
   const uint16_t* a_local;  // the local chunk, read in place by tiles inside it
   const uint16_t* b;
   void* c;
-  uint64_t* sig;          // slab signals, c * n_slab + s
+  uint64_t* sig;          // slab signals: channel g, slab s at g * sig_stride + s
+  int sig_stride;         // words between consecutive channels' signals (n_slab, or a signal block)
   SyncArgs sa;
   Timeline tl;
   int M, N, K;
@@ -122,6 +125,7 @@ struct SlabWait {
   uint64_t target;
   uint64_t waited;  // ticks spent polling inside the K loop (timeline only)
   int n_slab, slab_log2, c_lo, n_span;
+  int sig_stride;   // words between consecutive channels' signals
   int ready_until;
   bool active;
   bool l1_only;     // slabs are line-aligned: the acquire only invalidates L1
@@ -136,7 +140,7 @@ struct SlabWait {
     const bool valid = lane < win * n_span && ls < n_slab;
     uint64_t v = ~0ull;
     if (valid)
-      v = __hip_atomic_load(sig + (size_t)(c_lo + lane % n_span) * n_slab + ls, __ATOMIC_RELAXED,
+      v = __hip_atomic_load(sig + (size_t)(c_lo + lane % n_span) * sig_stride + ls, __ATOMIC_RELAXED,
                             TSG_SIG_SCOPE);
     const uint64_t bad = __builtin_amdgcn_ballot_w64(v < target);
     if (bad == 0) {
@@ -147,7 +151,7 @@ struct SlabWait {
         ready_until = s + f / n_span;
       } else {
         const uint64_t t = wall_clock64();
-        for (int i = 0; i < n_span; ++i) wave_poll_ge(sig + (size_t)(c_lo + i) * n_slab + s, target, sa);
+        for (int i = 0; i < n_span; ++i) wave_poll_ge(sig + (size_t)(c_lo + i) * sig_stride + s, target, sa);
         waited += wall_clock64() - t;
         ready_until = s + 1;
       }
@@ -188,13 +192,14 @@ __global__ void __launch_bounds__(Cfg::NT) ag_gemm_kernel(const AgGemmArgs args)
     hook.sa = args.sa;
     hook.target = sig_target(args.sa.epoch, args.arrivals);
     hook.n_slab = args.n_slab;
+    hook.sig_stride = args.sig_stride;
     hook.slab_log2 = args.slab_log2;
     hook.c_lo = g_lo;
     hook.n_span = g_hi - g_lo + 1;
     hook.active = args.n_slab > 1;
     hook.l1_only = args.l1_only != 0;
     hook.ready_until = 1;
-    for (int g = g_lo; g <= g_hi; ++g) block_poll_ge(args.sig + (size_t)g * args.n_slab, hook.target, args.sa);
+    for (int g = g_lo; g <= g_hi; ++g) block_poll_ge(args.sig + (size_t)g * args.sig_stride, hook.target, args.sa);
     acquire_lines(hook.l1_only);
   }
   const uint64_t t1 = args.tl.buf ? wall_clock64() : 0;
@@ -501,6 +506,7 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
   ga.n_tiles_n = n_nt;
   ga.arrivals = 1;  // any completed count: a signal is only published once complete
   ga.n_slab = n_slab;
+  ga.sig_stride = n_slab;
   ga.slab_log2 = slab_log2;
   ga.l1_only = ((uintptr_t)a_full % 128 == 0 && K % 64 == 0) ? 1 : 0;
 
@@ -595,10 +601,12 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
   if (o.copy_engine) {
     // ---- copy engines: one stream per chunk, fork from / join to `caller`
     if (mode == TSG_MODE_COMPUTE_ONLY) return gemm(caller, 0, ctx->n_cus);
-    // The call's signal value comes from the ring, which lives in an
-    // allocation of its own: a device copy within one allocation is run as
-    // a kernel by the runtime, a copy between two allocations by a DMA
-    // engine.  The ring is refilled (a short kernel ahead of the fork) once
+    // The runtime runs device copies below 64 KB as blit kernels on the
+    // CUs and larger ones on the DMA engines, so each signal is a 64 KB copy
+    // too: the window of the ring of signal values that ends with this
+    // call's entry, into the channel's signal block, whose last word is what
+    // the GEMM polls (the window's other words land in the block's unread
+    // part).  The ring is refilled (a short kernel ahead of the fork) once
     // the epochs it covers are used up.
     const uint32_t e = ga.sa.epoch;
     hipStream_t ds[kMaxRanks];
@@ -611,15 +619,22 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
       tsg_status st = dma_stream(ctx, kMaxRanks, &join_s);
       if (st != TSG_OK) return st;
     }
+    {
+      tsg_status st = dma_sig_blocks(ctx, R * C);
+      if (st != TSG_OK) return st;
+    }
+    uint64_t* const ring = ctx->d_dma_ring + tsg_ctx::kDmaRingPad;
     if (!ctx->dma_ring_valid || e < ctx->dma_ring_base || e - ctx->dma_ring_base >= (uint32_t)tsg_ctx::kDmaRing) {
-      hipLaunchKernelGGL(ag_dma_ring_kernel, dim3(64), dim3(256), 0, caller, ctx->d_dma_ring,
-                         (int)tsg_ctx::kDmaRing, e);
+      hipLaunchKernelGGL(ag_dma_ring_kernel, dim3(64), dim3(256), 0, caller, ring, (int)tsg_ctx::kDmaRing, e);
       tsg_status st = check_launch(ctx, "ag_dma_ring_kernel");
       if (st != TSG_OK) return st;
       ctx->dma_ring_base = e;
       ctx->dma_ring_valid = true;
     }
-    const uint64_t* val = ctx->d_dma_ring + (e - ctx->dma_ring_base);
+    // the window of the ring that ends with this call's entry
+    const char* win = (const char*)(ring + (e - ctx->dma_ring_base) + 1) - tsg_ctx::kDmaSigBytes;
+    ga.sig = (uint64_t*)((char*)ctx->d_dma_sig + tsg_ctx::kDmaSigBytes) - 1;
+    ga.sig_stride = (int)(tsg_ctx::kDmaSigBytes / sizeof(uint64_t));
     // Fork, then every copy, then the GEMM: the copies are all queued on
     // the engines' streams before the GEMM is queued, so that none of them
     // can be ordered behind the GEMM whose tiles wait for it.
@@ -641,13 +656,13 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
       char* dst = (char*)a_full + (size_t)cc * chunk_bytes;
       for (int ch = 0; ch < C; ++ch) {
         // copies on one stream complete in order: the signal lands after
-        // the channel's data
+        // the channel's data (both run on the engines: 64 KB and more)
         TSG_HIP(ctx, hipMemcpyAsync(dst + ch * ch_bytes, src + ch * ch_bytes, ch_bytes,
                                     hipMemcpyDeviceToDeviceNoCU, ds[p]));
         const int g = cc * C + ch;
         if (!(g < 32 && ((o.skip_mask >> g) & 1u)))
-          TSG_HIP(ctx, hipMemcpyAsync(ctx->d_sig + kSigBase + (size_t)g * n_slab, val, sizeof(uint64_t),
-                                      hipMemcpyDeviceToDeviceNoCU, ds[p]));
+          TSG_HIP(ctx, hipMemcpyAsync((char*)ctx->d_dma_sig + (size_t)g * tsg_ctx::kDmaSigBytes, win,
+                                      tsg_ctx::kDmaSigBytes, hipMemcpyDeviceToDeviceNoCU, ds[p]));
       }
       TSG_HIP(ctx, hipEventRecord(ctx->ev_dma[p], ds[p]));
       TSG_HIP(ctx, hipStreamWaitEvent(join_s, ctx->ev_dma[p], 0));

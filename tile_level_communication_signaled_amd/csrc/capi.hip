@@ -64,20 +64,40 @@ tsg_status dma_stream(tsg_ctx* ctx, int i, hipStream_t* s) {
   if (i < 0 || i >= tsg_ctx::kDmaStreams) return fail(ctx, TSG_E_INVALID, "copy-engine stream %d", i);
   if (!ctx->dma[i]) {
     if (!ctx->d_dma_ring) {
-      TSG_HIP(ctx, hipMalloc(&ctx->d_dma_ring, (size_t)tsg_ctx::kDmaRing * sizeof(uint64_t)));
+      TSG_HIP(ctx, hipMalloc(&ctx->d_dma_ring,
+                             (size_t)(tsg_ctx::kDmaRingPad + tsg_ctx::kDmaRing) * sizeof(uint64_t)));
+      TSG_HIP(ctx, hipMemset(ctx->d_dma_ring, 0,
+                             (size_t)(tsg_ctx::kDmaRingPad + tsg_ctx::kDmaRing) * sizeof(uint64_t)));
       ctx->dma_ring_valid = false;
     }
+    tsg_status st = dma_sig_blocks(ctx, 1);
+    if (st != TSG_OK) return st;
     TSG_HIP(ctx, hipStreamCreateWithFlags(&ctx->dma[i], hipStreamNonBlocking));
     TSG_HIP(ctx, hipEventCreateWithFlags(&ctx->ev_dma[i], hipEventDisableTiming));
-    // The first DMA copy on a new stream takes milliseconds (the runtime
-    // sets up its engine queue).  Pay it here, with one 8-byte copy into an
-    // unused word of the status buffer, rather than inside the first call's
-    // signal waits.
-    TSG_HIP(ctx, hipMemcpyAsync(ctx->d_status + 8, ctx->d_dma_ring, sizeof(uint64_t), hipMemcpyDeviceToDeviceNoCU,
-                                ctx->dma[i]));
+    // The first engine copy on a new stream takes milliseconds (the runtime
+    // sets up its engine queue).  Pay it here, with one signal-sized copy of
+    // the ring's zero padding into the first signal block (zero there
+    // already), rather than inside the first call's signal waits.
+    TSG_HIP(ctx, hipMemcpyAsync(ctx->d_dma_sig, ctx->d_dma_ring, tsg_ctx::kDmaSigBytes,
+                                hipMemcpyDeviceToDeviceNoCU, ctx->dma[i]));
     TSG_HIP(ctx, hipStreamSynchronize(ctx->dma[i]));
   }
   *s = ctx->dma[i];
+  return TSG_OK;
+}
+
+tsg_status dma_sig_blocks(tsg_ctx* ctx, int n) {
+  if (n <= ctx->dma_sig_blocks) return TSG_OK;
+  const int cap = (n + 63) / 64 * 64;
+  if (ctx->d_dma_sig) {
+    TSG_HIP(ctx, hipDeviceSynchronize());
+    TSG_HIP(ctx, hipFree(ctx->d_dma_sig));
+    ctx->d_dma_sig = nullptr;
+    ctx->dma_sig_blocks = 0;
+  }
+  TSG_HIP(ctx, hipMalloc(&ctx->d_dma_sig, (size_t)cap * tsg_ctx::kDmaSigBytes));
+  TSG_HIP(ctx, hipMemset(ctx->d_dma_sig, 0, (size_t)cap * tsg_ctx::kDmaSigBytes));
+  ctx->dma_sig_blocks = cap;
   return TSG_OK;
 }
 
@@ -286,6 +306,7 @@ void tsg_ctx_destroy(tsg_ctx* c) {
     if (c->ev_dma[i]) (void)hipEventDestroy(c->ev_dma[i]);
   }
   if (c->d_dma_ring) (void)hipFree(c->d_dma_ring);
+  if (c->d_dma_sig) (void)hipFree(c->d_dma_sig);
   if (c->ev_fork) (void)hipEventDestroy(c->ev_fork);
   for (int i = 0; i < 2; ++i) {
     if (c->ev_join[i]) (void)hipEventDestroy(c->ev_join[i]);

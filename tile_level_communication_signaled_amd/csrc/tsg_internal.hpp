@@ -33,11 +33,19 @@ struct tsg_ctx {
   hipStream_t side[2] = {nullptr, nullptr};
   // Copy-engine streams of the AllGather (one per chunk, then a join
   // stream), their events, and the ring of signal values the engines copy.
+  // The runtime runs device copies below 64 KB as blit kernels, so a signal
+  // travels as a 64 KB copy: the window of the ring that ends at the call's
+  // value (the ring has kDmaRingPad words ahead of its entries), into a
+  // 64 KB signal block whose last word is the signal the GEMM polls.
   static constexpr int kDmaStreams = 33;
   static constexpr int kDmaRing = 1 << 16;
+  static constexpr size_t kDmaSigBytes = size_t(64) << 10;
+  static constexpr int kDmaRingPad = (int)(kDmaSigBytes / 8);
   hipStream_t dma[kDmaStreams] = {};
   hipEvent_t ev_dma[kDmaStreams] = {};
-  uint64_t* d_dma_ring = nullptr;
+  uint64_t* d_dma_ring = nullptr;  // kDmaRingPad + kDmaRing words; entries from kDmaRingPad on
+  void* d_dma_sig = nullptr;       // signal blocks of kDmaSigBytes (zeroed when allocated)
+  int dma_sig_blocks = 0;
   void* d_noalloc_ws = nullptr;  // device address of the MoE no-alloc workspace (static)
   uint32_t dma_ring_base = 0;
   bool dma_ring_valid = false;
@@ -103,6 +111,9 @@ tsg_status streams(tsg_ctx* ctx, const Opts& o, Pair* out, hipStream_t caller = 
 // Copy-engine stream i (0 <= i < tsg_ctx::kDmaStreams) and its event,
 // created on first use.
 tsg_status dma_stream(tsg_ctx* ctx, int i, hipStream_t* s);
+// At least n zeroed signal blocks in ctx->d_dma_sig (reallocated, after a
+// device synchronisation, when fewer exist).
+tsg_status dma_sig_blocks(tsg_ctx* ctx, int n);
 
 // True when one workgroup of kernel `a` (nt_a threads) and one of kernel `b`
 // fit on one CU together: registers of their waves on each SIMD and LDS.
