@@ -619,6 +619,13 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
       tsg_status st = dma_stream(ctx, kMaxRanks, &join_s);
       if (st != TSG_OK) return st;
     }
+    // A copy below 64 KB runs as a kernel on the CUs; beside a GEMM that
+    // holds every CU it could not start while the tiles wait for it.
+    if (mode == TSG_MODE_OVERLAP && o.aux_cus < 0 && grid_gemm >= ctx->n_cus &&
+        (size_t)ch_rows * K * 2 < tsg_ctx::kDmaSigBytes)
+      return fail(ctx, TSG_E_UNSUPPORTED,
+                  "copy engines beside a GEMM on every CU need channel copies of at least 64 KB "
+                  "(rows per channel x K x 2 bytes); use fewer channels or a CU split");
     {
       tsg_status st = dma_sig_blocks(ctx, R * C);
       if (st != TSG_OK) return st;
@@ -649,21 +656,28 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
     time_begin(ctx, 1, join_s);
     const size_t ch_bytes = (size_t)ch_rows * K * 2;
     const size_t chunk_bytes = (size_t)chunk_rows * K * 2;
+    // Copy (arrival position p, channel ch) goes to stream (p C + ch) mod
+    // R: with one channel, one stream per chunk; with C = R channels,
+    // stream j takes channel j of every chunk in arrival order, so that a
+    // whole chunk lands at each step, moved by every engine at once.
     for (int p = 0; p < R; ++p) {
       const int cc = co.chunk[p];
       const char* src = cc == rank ? (const char*)a_local
                                    : (const char*)a_peers + (size_t)(cc < rank ? cc : cc - 1) * chunk_bytes;
       char* dst = (char*)a_full + (size_t)cc * chunk_bytes;
       for (int ch = 0; ch < C; ++ch) {
+        hipStream_t st = ds[(p * C + ch) % R];
         // copies on one stream complete in order: the signal lands after
         // the channel's data (both run on the engines: 64 KB and more)
         TSG_HIP(ctx, hipMemcpyAsync(dst + ch * ch_bytes, src + ch * ch_bytes, ch_bytes,
-                                    hipMemcpyDeviceToDeviceNoCU, ds[p]));
+                                    hipMemcpyDeviceToDeviceNoCU, st));
         const int g = cc * C + ch;
         if (!(g < 32 && ((o.skip_mask >> g) & 1u)))
           TSG_HIP(ctx, hipMemcpyAsync((char*)ctx->d_dma_sig + (size_t)g * tsg_ctx::kDmaSigBytes, win,
-                                      tsg_ctx::kDmaSigBytes, hipMemcpyDeviceToDeviceNoCU, ds[p]));
+                                      tsg_ctx::kDmaSigBytes, hipMemcpyDeviceToDeviceNoCU, st));
       }
+    }
+    for (int p = 0; p < R; ++p) {
       TSG_HIP(ctx, hipEventRecord(ctx->ev_dma[p], ds[p]));
       TSG_HIP(ctx, hipStreamWaitEvent(join_s, ctx->ev_dma[p], 0));
     }
