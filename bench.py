@@ -63,6 +63,10 @@ def _parse():
     p.add_argument("--timeline", action="store_true",
                    help="print each path's device timeline of one overlapped call (units active and "
                         "waiting per time bin) as markdown, and exit")
+    p.add_argument("--summarize-mfma", metavar="CSV",
+                   help="no GPU: turn the counter_collection.csv of a rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES "
+                        "GRBM_GUI_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_BUSY_CYCLES SQ_LDS_BANK_CONFLICT "
+                        "SQ_LDS_IDX_ACTIVE run of --counters into a markdown table per kernel and exit")
     p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="no GPU: turn the counter_collection.csv files of two rocprofv3 --pmc runs of "
                         "--counters (FETCH_SIZE, then WRITE_SIZE) into the traffic record and exit")
@@ -141,6 +145,38 @@ def summarize_counters(fetch_csv: str, write_csv: str, out_path: str = TRAFFIC) 
         json.dump(rec, f, indent=1)
         f.write("\n")
     return rec
+
+
+def summarize_mfma(csv_path: str) -> str:
+    """Markdown table per kernel from one rocprofv3 --pmc run of --counters:
+    active cycles = GRBM_GUI_ACTIVE summed over the 8 XCDs / 8 (the
+    dispatch's duration in GPU clocks), MFMA utilisation =
+    SQ_VALU_MFMA_BUSY_CYCLES / (active cycles x 1024 SIMDs), MFMA GFLOP =
+    SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512, LDS conflict % = SQ_LDS_BANK_CONFLICT
+    / SQ_LDS_IDX_ACTIVE; means over each kernel's dispatches."""
+    import csv
+    per = {}
+    for r in csv.DictReader(open(csv_path)):
+        short = next((k for k in KERNELS if k in r["Kernel_Name"]), None)
+        if short is None:
+            continue
+        d = per.setdefault(short, {}).setdefault(r["Dispatch_Id"], {})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    lines = ["| kernel | launches | active cycles | MFMA busy cycles | MFMA util % | MFMA GFLOP | LDS conflict % |",
+             "|---|---|---|---|---|---|---|"]
+    for short in KERNELS:
+        if short not in per:
+            continue
+        ds = list(per[short].values())
+        mean = lambda key: sum(d.get(key, 0.0) for d in ds) / len(ds)
+        active = mean("GRBM_GUI_ACTIVE") / 8
+        busy = mean("SQ_VALU_MFMA_BUSY_CYCLES")
+        util = 100.0 * busy / (active * 1024) if active else 0.0
+        gflop = mean("SQ_INSTS_VALU_MFMA_MOPS_BF16") * 512 / 1e9
+        lds = mean("SQ_LDS_IDX_ACTIVE")
+        conf = 100.0 * mean("SQ_LDS_BANK_CONFLICT") / lds if lds else 0.0
+        lines.append(f"| {short} | {len(ds)} | {active:,.0f} | {busy:,.0f} | {util:.1f} | {gflop:.2f} | {conf:.2f} |")
+    return "\n".join(lines)
 
 
 def _cpu_model() -> str:
@@ -231,6 +267,32 @@ def _cpu_baselines(ag_host, budget_s: float = 8.0) -> dict:
                                                         inp["w_down"]), budget_s / 2, 2)
     out["moe"] = entry(4.0 * T * k * Hh * I, t, n,
                        f"the full workload ({T} tokens, top-{k} of {E} experts {Hh}x{I} / {I}x{Hh}, combine)")
+
+    # the gather side of the same layer: 4096 tokens from 8 ranks, gather,
+    # up projection, SiLU
+    R6 = 8
+    loc6, peers6 = split_chunks(inp["x"], R6, 0)
+    t, n = _time_host(lambda: oracle.moe_ag_up(loc6, peers6, R6, 0, inp["topk_ids"], inp["w_up"]), budget_s / 2, 2)
+    out["moe_ag"] = entry(2.0 * T * k * Hh * I, t, n,
+                          f"the full workload (AllGather of {T} tokens from {R6} ranks, gather, "
+                          f"top-{k} of {E} experts {Hh}x{I}, SiLU)")
+
+    # AllGather KV + attention: 2048 queries over the 16384-token context;
+    # the sample is 4 of the 32 heads (the oracle's cost is per head), with
+    # the rate scaled to the sample's own FLOPs
+    import numpy as np
+    from synth import f32_to_bf16_bits
+    S7, R7, D7, h7 = 16384, 8, 128, 4
+    sl7 = S7 // R7
+    rng = np.random.default_rng(7)
+    mk = lambda shape: f32_to_bf16_bits(rng.standard_normal(shape).astype(np.float32))
+    q7, kf7, vf7 = mk((sl7, h7, D7)), mk((S7, h7, D7)), mk((S7, h7, D7))
+    kl7, kp7 = split_chunks(kf7, R7, 0)
+    vl7, vp7 = split_chunks(vf7, R7, 0)
+    t, n = _time_host(lambda: oracle.ag_kv_attention(q7, kl7, kp7, vl7, vp7, R7, 0), budget_s / 2, 2)
+    out["ag_kv_attention"] = entry(4.0 * sl7 * S7 * D7 * h7, t, n,
+                                   f"{h7} of the 32 heads ({sl7} queries over the gathered {S7}-token context, "
+                                   f"D={D7}, {R7} ranks)")
     return out
 
 
@@ -551,8 +613,8 @@ TL_KINDS = {"ag_gemm": ((1, "copy units"), (2, "GEMM tiles")),
             "gemm_rs": ((3, "GEMM tiles"), (4, "reduce units")),
             "mlp2": ((5, "GEMM1 tiles"), (6, "GEMM2 tiles")),
             "moe": ((7, "up tiles"), (8, "down tiles"), (9, "combine units")),
-            "moe_ag": ((10, "up tiles"),),
-            "ag_kv_attention": ((11, "attention tiles"),),
+            "moe_ag": ((1, "copy units"), (10, "up tiles")),
+            "ag_kv_attention": ((1, "copy units"), (11, "attention tiles")),
             "moe_bf16_staging": ((7, "up tiles"), (8, "down tiles"), (9, "combine units"))}
 
 
@@ -585,6 +647,9 @@ def main():
     args = _parse()
     if args.summarize_counters:
         print(json.dumps(summarize_counters(*args.summarize_counters)))
+        return
+    if args.summarize_mfma:
+        print(summarize_mfma(args.summarize_mfma))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this library has no multi-GPU path "

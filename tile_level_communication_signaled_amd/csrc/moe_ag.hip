@@ -309,7 +309,7 @@ tsg_status tsg_op_moe_ag(tsg_ctx* ctx, const void* x_local, const void* x_peers,
   ca.sig = ctx->d_sig + kSigBase;
   ca.cnt = ctx->d_cnt + kSigBase;
   ca.sa = sa;
-  ca.tl = Timeline{nullptr, nullptr, 0};
+  ca.tl = tl;  // copy units: kind 1
   ca.ord = co;
   ca.k8 = H / 8;
   ca.chunk_rows = chunk_rows;
