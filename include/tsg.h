@@ -92,7 +92,11 @@ typedef struct tsg_opts {
    * 4 = 256x128 (2x2), 5 = 128x256 (2x2), 6 = 64x64 (1), 7 = 128x64 (2x1),
    * 8 = 256x224 (8x1, two waves per SIMD), 9 = 256x224 (4x2 on 16x16x32
    * MFMA fragments, two waves per SIMD; needs K % 128 == 0, else
-   * TSG_E_UNSUPPORTED).  GEMM+RS and the MLP (both GEMMs): 1, 3, 4, 5.  An
+   * TSG_E_UNSUPPORTED).  GEMM+RS: 1, 3, 4, 5, and 6 = 256x256 (4x2 on
+   * 16x16x32 fragments, two waves per SIMD; needs K % 128 == 0, else
+   * TSG_E_UNSUPPORTED; its GEMM is the fastest alone, but a reduce
+   * workgroup cannot share its CU, so overlap on shared CUs runs the two
+   * kernels back to back).  The MLP (both GEMMs): 1, 3, 4, 5.  An
    * id the op does not have is rejected with TSG_E_INVALID. */
   int tile;
   /* Tile order knob.  AG+GEMM: 0 = start at the local chunk and follow the

@@ -55,7 +55,7 @@ def _ref(inp, R, rank):
     return P, out, sP, s_out
 
 
-@pytest.mark.parametrize("tile", [3, 1, 4])
+@pytest.mark.parametrize("tile", [3, 1, 4, 6])
 def test_rs_small_all_ranks(env, tile):
     M, N, K, R = 512, 256, 128, 4
     inp = rs_inputs(M, K, N, R, seed=3)
@@ -132,3 +132,19 @@ def test_rs_full_size_parity_and_modes(env):
         assert np.array_equal(gP4, gP) and np.array_equal(gout4, gout)
     gP5, gout5 = case.run(opts={"order": 1})
     assert np.array_equal(gP5, gP) and np.array_equal(gout5, gout)
+    # the eight-wave 16x16x32 tile: another accumulation order, checked
+    # against the oracle; overlap and serial give the same bits
+    gP6, gout6 = case.run(opts={"tile": 6})
+    assert err_ratio(gP6, P, sP) <= 1.0 and err_ratio(gout6, out, s_out) <= 1.0
+    gP7, gout7 = case.run(mode=tsg.SERIAL, opts={"tile": 6})
+    assert np.array_equal(gP7, gP6) and np.array_equal(gout7, gout6)
+
+
+def test_rs_tile6_needs_k_multiple_of_128(env):
+    torch, tsg, ctx = env
+    M, N, K, R = 512, 256, 192, 4
+    inp = rs_inputs(M, K, N, R, rank=0, seed=9)
+    case = RsCase(env, inp, M, N, K, R, 0)
+    st = tsg.gemm_rs_overlap(ctx, case.x, case.w, case.partial, case.peers, case.out, M, N, K, R, 0, opts={"tile": 6},
+                             raise_on_error=False)
+    assert st == tsg.E_UNSUPPORTED

@@ -113,40 +113,6 @@ Ws bind(char* base, const Layout& L) {
   return w;
 }
 
-// fp32 y of a down tile: element (r, c) of the tile goes to y_tile[r * H +
-// c] for r < valid and c < cols, one coherent 4-byte store each.  A store's
-// address is the tile's wave-uniform base plus a 32-bit per-lane offset,
-// built fragment by fragment from an offset the compiler cannot see through
-// (the empty asm), so that it computes at most one fragment's offsets ahead:
-// the 112 addresses of a lane computed in advance made the producer spill.
-template <class Cfg>
-__device__ __forceinline__ void store_y_f32(const typename GemmTile<Cfg>::Acc& acc, float* y_tile, int H, int valid,
-                                            int cols) {
-  constexpr int ACC_N = Cfg::MF == 32 ? 16 : 4;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm0 = (wave / Cfg::WN) * Cfg::WTM, wn0 = (wave % Cfg::WN) * Cfg::WTN;
-  // 32x32 result: lane l has column l mod 32 and rows 4 (l / 32) + 8 (v /
-  // 4) + v mod 4; 16x16: column l mod 16, rows 4 (l / 16) + v
-  const int r_l = Cfg::MF == 32 ? (lane >> 5) * 4 : (lane >> 4) * 4;
-  const int c_l = Cfg::MF == 32 ? (lane & 31) : (lane & 15);
-  const char* base = (const char*)y_tile;
-  const uint32_t row_b = (uint32_t)H * 4u;
-#pragma unroll
-  for (int i = 0; i < Cfg::FM; ++i)
-#pragma unroll
-    for (int j = 0; j < Cfg::FN; ++j) {
-      const int r0 = wm0 + i * Cfg::MF + r_l, c = wn0 + j * Cfg::MF + c_l;
-      uint32_t off = (uint32_t)r0 * row_b + (uint32_t)c * 4u;
-      asm volatile("" : "+v"(off));
-#pragma unroll
-      for (int v = 0; v < ACC_N; ++v) {
-        const int dr = Cfg::MF == 32 ? (v >> 2) * 8 + (v & 3) : v;
-        if (r0 + dr < valid && c < cols)
-          store_coherent((float*)(base + off + (uint32_t)dr * row_b), acc[i][j][v]);
-      }
-    }
-}
-
 // --------------------------------------------------------------- producer
 struct CombArgs {
   const float* topk_w;
@@ -444,7 +410,7 @@ __global__ void __launch_bounds__(kProdThreads) moe_producer_kernel(const ProdAr
           GemmTile<CfgDn>::template store_bf16_staged<sizeof(lds), true>(
               acc, lds, yb, H, valid, H - col0, [](float v) { return v; });
         } else {
-          store_y_f32<CfgDn>(acc, a.ws.y + (int64_t)rb * BM * H + col0, H, valid, H - col0);
+          GemmTile<CfgDn>::store_f32_coherent(acc, a.ws.y + (int64_t)rb * BM * H + col0, H, valid, H - col0);
         }
         block_coherent_complete();
         if (threadIdx.x == 0) {

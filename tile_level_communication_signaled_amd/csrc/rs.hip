@@ -62,11 +62,7 @@ __global__ void __launch_bounds__(Cfg::NT) rs_gemm_kernel(const RsGemmArgs args)
   else
     GemmTile<Cfg>::run_regs(ar, args.w, args.N, col0, args.N, args.K, lds, acc);
   const int M = args.M, N = args.N;
-  float* P = args.partial;
-  GemmTile<Cfg>::for_each(acc, [&](int r, int c, float v) {
-    const int gr = row0 + r, gc = col0 + c;
-    if (gr < M && gc < N) store_coherent(P + (int64_t)gr * N + gc, v);
-  });
+  GemmTile<Cfg>::store_f32_coherent(acc, args.partial + (int64_t)row0 * N + col0, N, M - row0, N - col0);
   // producer_tile_notify: the tile's stores went through to the coherence
   // point; once every wave has them acknowledged, one store per covered
   // 128 x 128 signal publishes it (no L2 write-back).
@@ -192,6 +188,7 @@ using Cfg1 = TileCfg<256, 256, 2, 2>;
 using Cfg3 = TileCfg<128, 128, 2, 2>;
 using Cfg4 = TileCfg<256, 128, 2, 2>;
 using Cfg5 = TileCfg<128, 256, 2, 2>;
+using Cfg6 = TileCfg<256, 256, 4, 2, 16>;  // 16x16x32 fragments, eight waves of 64 x 128
 
 struct TileShape {
   int bm, bn;
@@ -203,6 +200,7 @@ TileShape shape_of(int id) {
     case 3: return {128, 128};
     case 4: return {256, 128};
     case 5: return {128, 256};
+    case 6: return {256, 256};
     default: return {0, 0};
   }
 }
@@ -227,6 +225,7 @@ const void* gemm_fn(int id, bool direct) {
     case 3: return fn_cfg<Cfg3>(direct);
     case 4: return fn_cfg<Cfg4>(direct);
     case 5: return fn_cfg<Cfg5>(direct);
+    case 6: return fn_cfg<Cfg6>(direct);
     default: return nullptr;
   }
 }
@@ -237,6 +236,7 @@ hipError_t launch_gemm(int id, const RsGemmArgs& a, int grid, hipStream_t s) {
     case 3: return launch_cfg<Cfg3>(a, grid, s);
     case 4: return launch_cfg<Cfg4>(a, grid, s);
     case 5: return launch_cfg<Cfg5>(a, grid, s);
+    case 6: return launch_cfg<Cfg6>(a, grid, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -266,6 +266,8 @@ tsg_status tsg_op_rs(tsg_ctx* ctx, const void* x, const void* w, float* partial,
   const int tile = o.tile ? o.tile : ((M >= 2048 && N >= 1024) ? 1 : 3);
   const TileShape ts = shape_of(tile);
   if (!ts.bm) return fail(ctx, TSG_E_INVALID, "tile id %d is not available for gemm_rs_overlap", tile);
+  if (tile == 6 && K % 128)
+    return fail(ctx, TSG_E_UNSUPPORTED, "tile 6 needs K a multiple of 128 (direct-to-LDS loads only)");
   const int chunk_rows = M / R;
   const int n_mt = (M + ts.bm - 1) / ts.bm, n_nt = (N + ts.bn - 1) / ts.bn;
   if (n_mt > kMaxMTiles) return fail(ctx, TSG_E_UNSUPPORTED, "M / BM exceeds %d", kMaxMTiles);

@@ -591,6 +591,39 @@ struct GemmTile {
         }
   }
 
+  // fp32 epilogue with coherent stores: element (r, c) of the tile goes to
+  // C[r * ldc + c] for r < rows and c < cols, one 4-byte store each.  A
+  // store's address is the tile's wave-uniform base plus a 32-bit per-lane
+  // offset, built fragment by fragment from an offset the compiler cannot
+  // see through (the empty asm), so that it computes at most one fragment's
+  // offsets ahead: all of a lane's 64-bit addresses computed in advance made
+  // persistent kernels spill.
+  __device__ __forceinline__ static void store_f32_coherent(const Acc& acc, float* C, int64_t ldc, int rows,
+                                                            int cols) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm0 = (wave / Cfg::WN) * Cfg::WTM, wn0 = (wave % Cfg::WN) * Cfg::WTN;
+    // 32x32 result: lane l has column l mod 32 and rows 4 (l / 32) + 8 (v /
+    // 4) + v mod 4; 16x16: column l mod 16, rows 4 (l / 16) + v
+    const int r_l = Cfg::MF == 32 ? (lane >> 5) * 4 : (lane >> 4) * 4;
+    const int c_l = Cfg::MF == 32 ? (lane & 31) : (lane & 15);
+    const char* base = (const char*)C;
+    const uint32_t row_b = (uint32_t)ldc * 4u;
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < Cfg::FN; ++j) {
+        const int r0 = wm0 + i * Cfg::MF + r_l, c = wn0 + j * Cfg::MF + c_l;
+        uint32_t off = (uint32_t)r0 * row_b + (uint32_t)c * 4u;
+        asm volatile("" : "+v"(off));
+#pragma unroll
+        for (int v = 0; v < ACC_N; ++v) {
+          const int dr = Cfg::MF == 32 ? (v >> 2) * 8 + (v & 3) : v;
+          if (r0 + dr < rows && c < cols)
+            store_coherent((float*)(base + off + (uint32_t)dr * row_b), acc[i][j][v]);
+        }
+      }
+  }
+
   // bf16 epilogue through LDS.  C points at the tile's first element, with
   // ldc elements per row; ldc and the address are multiples of 8 elements,
   // and only the first `rows` rows and `cols` columns of the tile are stored
