@@ -96,8 +96,14 @@ typedef struct tsg_opts {
    * 16x16x32 fragments, two waves per SIMD; needs K % 128 == 0, else
    * TSG_E_UNSUPPORTED; its GEMM is the fastest alone, but a reduce
    * workgroup cannot share its CU, so overlap on shared CUs runs the two
-   * kernels back to back).  The MLP (both GEMMs): 1, 3, 4, 5.  An
-   * id the op does not have is rejected with TSG_E_INVALID. */
+   * kernels back to back).  The MLP: 1, 3, 4, 5 (the same tile for both
+   * GEMMs), 6 = the pair of 16x16x32 eight-wave tiles 128x256 (2x4) for
+   * GEMM1 and 256x256 (4x2) for GEMM2, 7 = 128x256 (2x4 on 16x16x32) for
+   * both; 6 and 7 need K1 and N1 multiples of 128, else TSG_E_UNSUPPORTED.
+   * The MLP's default is 6 when M, N1 and N2 are all at least 1024 and K1
+   * and N1 are multiples of 128, 128x256 then 256x256 on 2x2 waves of
+   * 32x32x16 for other shapes of that size, and 3 below it.  An id the op
+   * does not have is rejected with TSG_E_INVALID. */
   int tile;
   /* Tile order knob.  AG+GEMM: 0 = start at the local chunk and follow the
    * arrival order; 1 = plain row-major order.  GEMM+RS: 0 = local chunk

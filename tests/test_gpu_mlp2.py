@@ -40,9 +40,13 @@ def _run(env, inp, M, K1, N1, N2, mode=None, opts=None, expect=0):
     return bf16_from_dev(h), y.cpu().numpy().astype(np.float64)
 
 
-def _check(inp, h_gpu, y_gpu):
+def _ref(inp):
     z, h_ref, y_ref = oracle.mlp2(inp["x"], inp["w1"], inp["w2"])
-    s1 = oracle.gemm_abs(inp["x"], inp["w1"])
+    return h_ref, y_ref, oracle.gemm_abs(inp["x"], inp["w1"])
+
+
+def _check(inp, h_gpu, y_gpu, ref=None):
+    h_ref, y_ref, s1 = ref if ref is not None else _ref(inp)
     hg, hr = oracle.bf16_to_f64(h_gpu), oracle.bf16_to_f64(h_ref)
     tol_h = 1.13 * (1e-3 * s1 + 1e-5) + 2 * bf16_half_quantum(hr) + 1e-7
     assert np.all(np.isfinite(hg))
@@ -55,7 +59,7 @@ def _check(inp, h_gpu, y_gpu):
     return rh, ry
 
 
-@pytest.mark.parametrize("tile", [3, 5, 1])
+@pytest.mark.parametrize("tile", [3, 5, 1, 6, 7])
 def test_mlp2_small_ragged(env, tile):
     M, K1, N1, N2 = 300, 256, 384, 200
     inp = mlp2_inputs(M, K1, N1, N2, seed=11)
@@ -67,6 +71,27 @@ def test_mlp2_small_ragged(env, tile):
 def test_mlp2_k_not_multiple_of_128(env):
     M, K1, N1, N2 = 256, 200, 136, 264
     inp = mlp2_inputs(M, K1, N1, N2, seed=12)
+    h, y = _run(env, inp, M, K1, N1, N2)
+    rh, ry = _check(inp, h, y)
+    assert rh <= 1.0 and ry <= 1.0, (rh, ry)
+
+
+def test_mlp2_eight_wave_tiles_need_k_multiple_of_128(env):
+    torch, tsg, ctx = env
+    M, K1, N1, N2 = 256, 200, 256, 256
+    inp = mlp2_inputs(M, K1, N1, N2, seed=16)
+    x, w1, w2 = to_dev(inp["x"], torch), to_dev(inp["w1"], torch), to_dev(inp["w2"], torch)
+    h = torch.empty((M, N1), dtype=torch.int16, device="cuda")
+    y = torch.empty((M, N2), dtype=torch.float32, device="cuda")
+    for tile in (6, 7):
+        st = tsg.mlp2_pipelined(ctx, x, w1, h, w2, y, M, K1, N1, N2, opts={"tile": tile}, raise_on_error=False)
+        assert st == tsg.E_UNSUPPORTED
+
+
+def test_mlp2_large_k_not_multiple_of_128_default(env):
+    # at this size the default takes the 32x32x16 tiles, because K1 % 128 != 0
+    M, K1, N1, N2 = 1024, 1000, 1024, 1024
+    inp = mlp2_inputs(M, K1, N1, N2, seed=17)
     h, y = _run(env, inp, M, K1, N1, N2)
     rh, ry = _check(inp, h, y)
     assert rh <= 1.0 and ry <= 1.0, (rh, ry)
@@ -106,10 +131,15 @@ def test_mlp2_full_size_parity_modes_splits(env):
     cfg = CONFIGS["mlp2"]
     M, K1, N1, N2 = cfg["M"], cfg["K1"], cfg["N1"], cfg["N2"]
     inp = mlp2_inputs(M, K1, N1, N2, seed=cfg["seed"])
+    ref = _ref(inp)
     h, y = _run(env, inp, M, K1, N1, N2)
-    rh, ry = _check(inp, h, y)
+    rh, ry = _check(inp, h, y, ref)
     print(f"mlp2 max err/tol H {rh:.3f} Y {ry:.3f}")
     assert rh <= 1.0 and ry <= 1.0
+    # the 32x32x16 pair (another accumulation order) against the oracle too
+    h5, y5 = _run(env, inp, M, K1, N1, N2, opts={"tile": 5})
+    rh5, ry5 = _check(inp, h5, y5, ref)
+    assert rh5 <= 1.0 and ry5 <= 1.0, (rh5, ry5)
     for mode in (tsg.SERIAL, tsg.COMPUTE_ONLY):
         h2, y2 = _run(env, inp, M, K1, N1, N2, mode=mode)
         assert np.array_equal(h2, h) and np.array_equal(y2, y)

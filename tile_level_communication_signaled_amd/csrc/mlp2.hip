@@ -120,12 +120,7 @@ __global__ void __launch_bounds__(Cfg::NT) mlp_gemm2_kernel(const Mlp2Args a) {
       GemmTile<Cfg>::run_direct(ar, a.w2, a.N2, col0, a.N2, a.N1, lds, acc);
     else
       GemmTile<Cfg>::run_regs(ar, a.w2, a.N2, col0, a.N2, a.N1, lds, acc);
-    const int M = a.M, N2 = a.N2;
-    float* Y = a.y;
-    GemmTile<Cfg>::for_each(acc, [&](int r, int c, float v) {
-      const int gr = row0 + r, gc = col0 + c;
-      if (gr < M && gc < N2) Y[(int64_t)gr * N2 + gc] = v;
-    });
+    GemmTile<Cfg>::template store_f32<false>(acc, a.y + (int64_t)row0 * a.N2 + col0, a.N2, a.M - row0, a.N2 - col0);
     if (a.tl.buf && threadIdx.x == 0) timeline_put(a.tl, 6, (uint32_t)(mt << 16 | nt), t0, t1, wall_clock64());
     __syncthreads();  // LDS of this tile fully consumed before the next one
   }
@@ -152,8 +147,8 @@ struct MlpFusedArgs {
 };
 
 template <class C1, bool D1, class C2, bool D2>
-__global__ void __launch_bounds__(256) mlp_fused_kernel(const MlpFusedArgs f) {
-  static_assert(C1::NT == 256 && C2::NT == 256, "both tiles use 2 x 2 waves");
+__global__ void __launch_bounds__(C1::NT) mlp_fused_kernel(const MlpFusedArgs f) {
+  static_assert(C1::NT == C2::NT, "both tiles use the same number of waves");
   constexpr int L1 = D1 ? C1::LDS_DIRECT : C1::LDS_REGS;
   constexpr int L2 = D2 ? C2::LDS_DIRECT : C2::LDS_REGS;
   __shared__ __attribute__((aligned(16))) char lds[L1 > L2 ? L1 : L2];
@@ -216,12 +211,7 @@ __global__ void __launch_bounds__(256) mlp_fused_kernel(const MlpFusedArgs f) {
         GemmTile<C2>::run_direct(ar, b.w2, b.N2, col0, b.N2, b.N1, lds, acc);
       else
         GemmTile<C2>::run_regs(ar, b.w2, b.N2, col0, b.N2, b.N1, lds, acc);
-      const int M = b.M, N2 = b.N2;
-      float* Y = b.y;
-      GemmTile<C2>::for_each(acc, [&](int r, int c, float v) {
-        const int gr = row0 + r, gc = col0 + c;
-        if (gr < M && gc < N2) Y[(int64_t)gr * N2 + gc] = v;
-      });
+      GemmTile<C2>::template store_f32<false>(acc, b.y + (int64_t)row0 * b.N2 + col0, b.N2, b.M - row0, b.N2 - col0);
       if (b.tl.buf && threadIdx.x == 0) timeline_put(b.tl, 6, (uint32_t)(mt << 16 | nt), t0, t1, wall_clock64());
     }
   }
@@ -234,30 +224,45 @@ using Cfg1 = TileCfg<256, 256, 2, 2>;
 using Cfg3 = TileCfg<128, 128, 2, 2>;
 using Cfg4 = TileCfg<256, 128, 2, 2>;
 using Cfg5 = TileCfg<128, 256, 2, 2>;
+// 16x16x32 fragments, eight waves (two per SIMD): 256 x 256 as 4 x 2 waves of
+// 64 x 128, and 128 x 256 as 2 x 4 waves of 64 x 64.  Direct-to-LDS loads
+// only, so the K of each GEMM must be a multiple of 128.
+using Cfg6 = TileCfg<256, 256, 4, 2, 16>;
+using Cfg7 = TileCfg<128, 256, 2, 4, 16>;
+
+template <class T>
+constexpr bool is_mf16() { return T::MF == 16; }
 
 template <class C1, class C2>
 hipError_t launch_fused_cfg(const MlpFusedArgs& f, int grid, hipStream_t s) {
   const bool d1 = f.g1.K1 % (2 * C1::BK) == 0, d2 = f.g2.N1 % (2 * C2::BK) == 0;
-  if (d1 && d2)
-    hipLaunchKernelGGL((mlp_fused_kernel<C1, true, C2, true>), dim3(grid), dim3(256), 0, s, f);
+  constexpr int NT = C1::NT;
+  if constexpr (is_mf16<C1>() || is_mf16<C2>()) {
+    if (!d1 || !d2) return hipErrorInvalidValue;  // the host rejects these shapes first
+    hipLaunchKernelGGL((mlp_fused_kernel<C1, true, C2, true>), dim3(grid), dim3(NT), 0, s, f);
+  } else if (d1 && d2)
+    hipLaunchKernelGGL((mlp_fused_kernel<C1, true, C2, true>), dim3(grid), dim3(NT), 0, s, f);
   else if (d1)
-    hipLaunchKernelGGL((mlp_fused_kernel<C1, true, C2, false>), dim3(grid), dim3(256), 0, s, f);
+    hipLaunchKernelGGL((mlp_fused_kernel<C1, true, C2, false>), dim3(grid), dim3(NT), 0, s, f);
   else if (d2)
-    hipLaunchKernelGGL((mlp_fused_kernel<C1, false, C2, true>), dim3(grid), dim3(256), 0, s, f);
+    hipLaunchKernelGGL((mlp_fused_kernel<C1, false, C2, true>), dim3(grid), dim3(NT), 0, s, f);
   else
-    hipLaunchKernelGGL((mlp_fused_kernel<C1, false, C2, false>), dim3(grid), dim3(256), 0, s, f);
+    hipLaunchKernelGGL((mlp_fused_kernel<C1, false, C2, false>), dim3(grid), dim3(NT), 0, s, f);
   return hipGetLastError();
 }
 
 // Tile pairs the fused kernel is built for: (GEMM1 tile, GEMM2 tile).
 bool fused_supported(int t1, int t2) {
-  return (t1 == 5 && t2 == 1) || (t1 == 5 && t2 == 5) || (t1 == 3 && t2 == 3);
+  return (t1 == 5 && t2 == 1) || (t1 == 5 && t2 == 5) || (t1 == 3 && t2 == 3) || (t1 == 7 && t2 == 6) ||
+         (t1 == 7 && t2 == 7);
 }
 
 hipError_t launch_fused(int t1, int t2, const MlpFusedArgs& f, int grid, hipStream_t s) {
   if (t1 == 5 && t2 == 1) return launch_fused_cfg<Cfg5, Cfg1>(f, grid, s);
   if (t1 == 5 && t2 == 5) return launch_fused_cfg<Cfg5, Cfg5>(f, grid, s);
   if (t1 == 3 && t2 == 3) return launch_fused_cfg<Cfg3, Cfg3>(f, grid, s);
+  if (t1 == 7 && t2 == 6) return launch_fused_cfg<Cfg7, Cfg6>(f, grid, s);
+  if (t1 == 7 && t2 == 7) return launch_fused_cfg<Cfg7, Cfg7>(f, grid, s);
   return hipErrorInvalidValue;
 }
 
@@ -271,12 +276,15 @@ TileShape shape_of(int id) {
     case 3: return {128, 128};
     case 4: return {256, 128};
     case 5: return {128, 256};
+    case 6: return {256, 256};
+    case 7: return {128, 256};
     default: return {0, 0};
   }
 }
 
 template <class Cfg>
 hipError_t launch1_cfg(const Mlp1Args& a, int grid, hipStream_t s) {
+  if (is_mf16<Cfg>() && a.K1 % (2 * Cfg::BK)) return hipErrorInvalidValue;  // rejected by the host first
   if (a.K1 % (2 * Cfg::BK) == 0)
     hipLaunchKernelGGL((mlp_gemm1_kernel<Cfg, true>), dim3(grid), dim3(Cfg::NT), 0, s, a);
   else
@@ -286,6 +294,7 @@ hipError_t launch1_cfg(const Mlp1Args& a, int grid, hipStream_t s) {
 
 template <class Cfg>
 hipError_t launch2_cfg(const Mlp2Args& a, int grid, hipStream_t s) {
+  if (is_mf16<Cfg>() && a.N1 % (2 * Cfg::BK)) return hipErrorInvalidValue;  // rejected by the host first
   if (a.N1 % (2 * Cfg::BK) == 0)
     hipLaunchKernelGGL((mlp_gemm2_kernel<Cfg, true>), dim3(grid), dim3(Cfg::NT), 0, s, a);
   else
@@ -299,6 +308,8 @@ hipError_t launch1(int id, const Mlp1Args& a, int grid, hipStream_t s) {
     case 3: return launch1_cfg<Cfg3>(a, grid, s);
     case 4: return launch1_cfg<Cfg4>(a, grid, s);
     case 5: return launch1_cfg<Cfg5>(a, grid, s);
+    case 6: return launch1_cfg<Cfg6>(a, grid, s);
+    case 7: return launch1_cfg<Cfg7>(a, grid, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -309,6 +320,8 @@ hipError_t launch2(int id, const Mlp2Args& a, int grid, hipStream_t s) {
     case 3: return launch2_cfg<Cfg3>(a, grid, s);
     case 4: return launch2_cfg<Cfg4>(a, grid, s);
     case 5: return launch2_cfg<Cfg5>(a, grid, s);
+    case 6: return launch2_cfg<Cfg6>(a, grid, s);
+    case 7: return launch2_cfg<Cfg7>(a, grid, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -335,8 +348,13 @@ tsg_status tsg_op_mlp2(tsg_ctx* ctx, const void* x, const void* w1, void* h, con
 
   const Opts o = resolve(opts, -1);
   const bool small = M < 1024 || N1 < 1024 || N2 < 1024;
-  const int tile1 = o.tile ? o.tile : (small ? 3 : 5);  // 128 x 256 for GEMM1
-  const int tile2 = o.tile ? o.tile : (small ? 3 : 1);  // 256 x 256 for GEMM2
+  // Tile 6 names a pair of eight-wave tiles on 16x16x32 fragments: 128 x 256
+  // (2 x 4 waves) for GEMM1 and 256 x 256 (4 x 2 waves) for GEMM2.  It is the
+  // default when both K dimensions allow direct-to-LDS loads; otherwise
+  // GEMM1 takes 128 x 256 and GEMM2 256 x 256 on four waves of 32x32x16.
+  const bool eight = !small && K1 % 128 == 0 && N1 % 128 == 0;
+  const int tile1 = o.tile == 6 ? 7 : o.tile ? o.tile : small ? 3 : eight ? 7 : 5;
+  const int tile2 = o.tile ? o.tile : small ? 3 : eight ? 6 : 1;
   if (o.order != 0 && o.order != 1) return fail(ctx, TSG_E_INVALID, "mlp2_pipelined: order must be 0 or 1");
   // Tile order of both GEMMs: 0 = row-block-major (a GEMM2 tile needs whole
   // row blocks of H, so GEMM1 finishes them one after another and GEMM2's
@@ -346,6 +364,8 @@ tsg_status tsg_op_mlp2(tsg_ctx* ctx, const void* x, const void* w1, void* h, con
   const int group = o.order == 1 ? 8 : 1;
   const TileShape s1 = shape_of(tile1), s2 = shape_of(tile2);
   if (!s1.bm || !s2.bm) return fail(ctx, TSG_E_INVALID, "tile id %d is not available for mlp2_pipelined", o.tile);
+  if ((tile1 >= 6 && K1 % 128) || (tile2 >= 6 && N1 % 128))
+    return fail(ctx, TSG_E_UNSUPPORTED, "tile %d needs K1 and N1 multiples of 128 (direct-to-LDS loads only)", o.tile);
 
   TSG_HIP(ctx, hipSetDevice(ctx->device));
   hipStream_t caller = (hipStream_t)stream;

@@ -410,7 +410,7 @@ __global__ void __launch_bounds__(kProdThreads) moe_producer_kernel(const ProdAr
           GemmTile<CfgDn>::template store_bf16_staged<sizeof(lds), true>(
               acc, lds, yb, H, valid, H - col0, [](float v) { return v; });
         } else {
-          GemmTile<CfgDn>::store_f32_coherent(acc, a.ws.y + (int64_t)rb * BM * H + col0, H, valid, H - col0);
+          GemmTile<CfgDn>::store_f32<true>(acc, a.ws.y + (int64_t)rb * BM * H + col0, H, valid, H - col0);
         }
         block_coherent_complete();
         if (threadIdx.x == 0) {

@@ -62,7 +62,7 @@ __global__ void __launch_bounds__(Cfg::NT) rs_gemm_kernel(const RsGemmArgs args)
   else
     GemmTile<Cfg>::run_regs(ar, args.w, args.N, col0, args.N, args.K, lds, acc);
   const int M = args.M, N = args.N;
-  GemmTile<Cfg>::store_f32_coherent(acc, args.partial + (int64_t)row0 * N + col0, N, M - row0, N - col0);
+  GemmTile<Cfg>::template store_f32<true>(acc, args.partial + (int64_t)row0 * N + col0, N, M - row0, N - col0);
   // producer_tile_notify: the tile's stores went through to the coherence
   // point; once every wave has them acknowledged, one store per covered
   // 128 x 128 signal publishes it (no L2 write-back).

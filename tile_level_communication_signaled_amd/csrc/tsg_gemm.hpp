@@ -73,6 +73,14 @@ struct TileCfg {
   static_assert(VM_PER_STEP < 64, "too many loads per step for one wait count");
 };
 
+// threadIdx.x through an empty asm: values derived from it are recomputed
+// where they are used instead of being hoisted out of enclosing loops.
+__device__ __forceinline__ int opaque_tid() {
+  int t = (int)threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
 // Physical 16-byte position of logical chunk `chunk` of LDS row `row`.  A
 // row is 128 bytes; with 64 banks of 4 bytes, the 16 lanes served together by
 // a 16-byte access hit distinct banks iff their (row parity, position) pairs
@@ -326,8 +334,7 @@ struct GemmTile {
   // 8 g .. 8 g + 7 of the 32-wide k step (two reads of four rows) and the
   // same 16 columns: lane l ends with column (l mod 16) and k values
   // 8 (l / 16) .. + 7, the B operand layout of the 16x16x32 MFMA.
-  __device__ __forceinline__ static void tr_lane_offsets(int wn0, uint32_t (&off)[Cfg::FN]) {
-    const int lane = threadIdx.x & 63;
+  __device__ __forceinline__ static void tr_lane_offsets(int wn0, int lane, uint32_t (&off)[Cfg::FN]) {
     const int hi = lane >> 5, g = lane >> 4, sl = lane & 15;
     const int row = Cfg::MF == 32 ? 8 * hi + (sl >> 2) : 8 * g + (sl >> 2);
 #pragma unroll
@@ -355,10 +362,8 @@ struct GemmTile {
     bf16x8_t a[Cfg::FM], b[Cfg::FN];
   };
   __device__ __forceinline__ static void read_frags(Frags& f, const char* la, const char* lb,
-                                                    const uint32_t (&tr_off)[Cfg::FN], int ks) {
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int wm0 = (wave / Cfg::WN) * Cfg::WTM;
+                                                    const uint32_t (&tr_off)[Cfg::FN], int ks, int lane,
+                                                    int wm0) {
 #pragma unroll
     for (int i = 0; i < Cfg::FM; ++i) {
       if constexpr (Cfg::MF == 32)
@@ -398,8 +403,14 @@ struct GemmTile {
     static_assert(Cfg::B_STAGE % 1024 == 0, "a B stage must be whole 1 KB load blocks");
     constexpr int B_BLK = Cfg::B_STAGE / 1024;
     constexpr int B_BPW = (B_BLK + Cfg::NW - 1) / Cfg::NW;
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    // The lane's offsets are derived from a thread index the compiler cannot
+    // see through, so they are computed per call: in a persistent kernel they
+    // would otherwise be hoisted out of the tile loop and stay live across
+    // every other kind of tile the kernel runs.
+    const int tid = opaque_tid();
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm0 = (wave / Cfg::WN) * Cfg::WTM;
     char* const lds_a = lds;
     char* const lds_b = lds + 3 * Cfg::A_STAGE;
     zero(acc);
@@ -456,7 +467,7 @@ struct GemmTile {
     };
     const int wn0 = (wave % Cfg::WN) * Cfg::WTN;
     uint32_t tr_off[Cfg::FN];
-    tr_lane_offsets(wn0, tr_off);
+    tr_lane_offsets(wn0, lane, tr_off);
 
     const int nk = K / Cfg::BK;
     hook.before_a(0);
@@ -477,7 +488,7 @@ struct GemmTile {
     // MFMAs run, so neither the barrier nor the LDS latency of a stage's first
     // reads leaves the matrix units idle.
     Frags f0, f1;
-    read_frags(f0, lds_a, lds_b, tr_off, 0);
+    read_frags(f0, lds_a, lds_b, tr_off, 0, lane, wm0);
     int sa = 0;  // kt % 3
     for (int kt = 0; kt < nk; ++kt) {
       const int sa2 = sa >= 1 ? sa - 1 : 2;   // (kt + 2) % 3
@@ -489,21 +500,21 @@ struct GemmTile {
       const char* la = lds_a + sa * Cfg::A_STAGE;
       const char* lb = lds_b + (kt & 1) * Cfg::B_STAGE;
       if constexpr (Cfg::KS == 4) {
-        read_frags(f1, la, lb, tr_off, 1);
+        read_frags(f1, la, lb, tr_off, 1, lane, wm0);
         mma(f0, acc);
-        read_frags(f0, la, lb, tr_off, 2);
+        read_frags(f0, la, lb, tr_off, 2, lane, wm0);
         mma(f1, acc);
-        read_frags(f1, la, lb, tr_off, 3);
+        read_frags(f1, la, lb, tr_off, 3, lane, wm0);
         mma(f0, acc);
       } else {
-        read_frags(f1, la, lb, tr_off, 1);
+        read_frags(f1, la, lb, tr_off, 1, lane, wm0);
         mma(f0, acc);
       }
       sa = sa == 2 ? 0 : sa + 1;
       if (kt + 1 < nk) {
         if (kt + 2 < nk) wait_vmcnt<Cfg::A_BPW>(); else wait_vmcnt<0>();
         lds_barrier();
-        read_frags(f0, lds_a + sa * Cfg::A_STAGE, lds_b + ((kt + 1) & 1) * Cfg::B_STAGE, tr_off, 0);
+        read_frags(f0, lds_a + sa * Cfg::A_STAGE, lds_b + ((kt + 1) & 1) * Cfg::B_STAGE, tr_off, 0, lane, wm0);
       }
       mma(f1, acc);
     }
@@ -591,16 +602,18 @@ struct GemmTile {
         }
   }
 
-  // fp32 epilogue with coherent stores: element (r, c) of the tile goes to
-  // C[r * ldc + c] for r < rows and c < cols, one 4-byte store each.  A
+  // fp32 epilogue: element (r, c) of the tile goes to C[r * ldc + c] for
+  // r < rows and c < cols, one 4-byte store each (COHERENT: stores that
+  // write through to memory, for data a concurrent kernel reads).  A
   // store's address is the tile's wave-uniform base plus a 32-bit per-lane
   // offset, built fragment by fragment from an offset the compiler cannot
   // see through (the empty asm), so that it computes at most one fragment's
   // offsets ahead: all of a lane's 64-bit addresses computed in advance made
   // persistent kernels spill.
-  __device__ __forceinline__ static void store_f32_coherent(const Acc& acc, float* C, int64_t ldc, int rows,
-                                                            int cols) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  template <bool COHERENT = true>
+  __device__ __forceinline__ static void store_f32(const Acc& acc, float* C, int64_t ldc, int rows, int cols) {
+    const int tid = opaque_tid();
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm0 = (wave / Cfg::WN) * Cfg::WTM, wn0 = (wave % Cfg::WN) * Cfg::WTN;
     // 32x32 result: lane l has column l mod 32 and rows 4 (l / 32) + 8 (v /
     // 4) + v mod 4; 16x16: column l mod 16, rows 4 (l / 16) + v
@@ -618,9 +631,17 @@ struct GemmTile {
 #pragma unroll
         for (int v = 0; v < ACC_N; ++v) {
           const int dr = Cfg::MF == 32 ? (v >> 2) * 8 + (v & 3) : v;
-          if (r0 + dr < rows && c < cols)
-            store_coherent((float*)(base + off + (uint32_t)dr * row_b), acc[i][j][v]);
+          if (r0 + dr < rows && c < cols) {
+            float* p = (float*)(base + off + (uint32_t)dr * row_b);
+            if (COHERENT)
+              store_coherent(p, acc[i][j][v]);
+            else
+              *p = acc[i][j][v];
+          }
         }
+        // one fragment at a time (plain stores could otherwise be batched
+        // with every address live at once)
+        if (!COHERENT) __builtin_amdgcn_sched_barrier(0);
       }
   }
 
@@ -651,8 +672,9 @@ struct GemmTile {
   __device__ __forceinline__ static char* stage_bf16(const Acc& acc, char* lds, F&& f) {
     constexpr int STRIDE = stage_stride<LDS_BYTES>();
     static_assert(Cfg::NW * Cfg::WTM * STRIDE <= LDS_BYTES, "staged tile does not fit the LDS");
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int tid = opaque_tid();
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     char* reg = lds + wave * (Cfg::WTM * STRIDE);
     char* wr = Cfg::MF == 32 ? reg + ((lane >> 5) * 4) * STRIDE + (lane & 31) * 2
                              : reg + ((lane >> 4) * 4) * STRIDE + (lane & 15) * 2;
@@ -688,8 +710,9 @@ struct GemmTile {
     constexpr int VPR = Cfg::WTN / 8;
     constexpr int TOT = Cfg::WTM * VPR;
     static_assert(TOT % 64 == 0, "pieces must fill whole wave passes");
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int tid = opaque_tid();
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm0 = (wave / Cfg::WN) * Cfg::WTM;
     const int wn0 = (wave % Cfg::WN) * Cfg::WTN;
     const char* reg = stage_bf16<LDS_BYTES>(acc, lds, f);
@@ -710,9 +733,9 @@ struct GemmTile {
     constexpr int VPR = Cfg::WTN / 8;          // 16-byte pieces per row
     constexpr int TOT = Cfg::WTM * VPR;
     static_assert(TOT % 64 == 0, "pieces must fill whole wave passes");
-    const int tid = threadIdx.x;
+    const int tid = opaque_tid();
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm0 = (wave / Cfg::WN) * Cfg::WTM;
     const int wn0 = (wave % Cfg::WN) * Cfg::WTN;
     const char* reg = stage_bf16<LDS_BYTES>(acc, lds, f);
