@@ -53,13 +53,15 @@ constexpr size_t kSigH = size_t(1) << 19;          // h row-block signals
 constexpr size_t kSigReady = kSigH + 65536;         // ready signals of down tiles
 constexpr size_t kSigEnd = kSigReady + 262144;
 
-// Eight waves of 32 x 224: two waves per SIMD, 112 accumulator registers
-// each, so the persistent kernel holds both tile paths and the combine
-// without spilling.
-using CfgUp = TileCfg<BM, BN_UP, 8, 1>;
-using CfgDn = TileCfg<BM, BN_DN, 8, 1>;
-constexpr int kProdThreads = CfgUp::NT;
-static_assert(CfgDn::NT == kProdThreads, "up and down tiles share the workgroup");
+// Eight waves, two per SIMD, 112 accumulator registers each: with
+// direct-to-LDS loads (K a multiple of 128) 4 x 2 waves of 64 x 112 on
+// 16x16x32 fragments, else 8 x 1 waves of 32 x 224 on 32x32x16 (the register
+// path).  The persistent kernel holds both tile paths and the combine.
+template <bool DIRECT>
+using CfgOf = std::conditional_t<DIRECT, TileCfg<BM, BN_UP, 4, 2, 16>, TileCfg<BM, BN_UP, 8, 1>>;
+static_assert(BN_UP == BN_DN, "up and down tiles share one shape");
+constexpr int kProdThreads = CfgOf<true>::NT;
+static_assert(CfgOf<false>::NT == kProdThreads, "both layouts use eight waves");
 
 // Workspace layout (byte offsets, 256-aligned).
 struct Layout {
@@ -331,6 +333,8 @@ __global__ void __launch_bounds__(256) moe_combine_kernel(const CombArgs a) {
 // took before it and complete without waiting on later ones.
 template <bool DIRECT_UP, bool DIRECT_DN>
 __global__ void __launch_bounds__(kProdThreads) moe_producer_kernel(const ProdArgs a) {
+  using CfgUp = CfgOf<DIRECT_UP>;
+  using CfgDn = CfgOf<DIRECT_DN>;
   constexpr int LUP = DIRECT_UP ? CfgUp::LDS_DIRECT : CfgUp::LDS_REGS;
   constexpr int LDN = DIRECT_DN ? CfgDn::LDS_DIRECT : CfgDn::LDS_REGS;
   __shared__ __attribute__((aligned(16))) char lds[LUP > LDN ? LUP : LDN];
@@ -372,11 +376,14 @@ __global__ void __launch_bounds__(kProdThreads) moe_producer_kernel(const ProdAr
       if (rb < n_rb && up) {
         const int e = __builtin_amdgcn_readfirstlane(a.ws.rb_expert[rb]);
         const int col0 = nt * BN_UP;
+        // rows past the expert's last pair are padding
+        const int valid = __builtin_amdgcn_readfirstlane(
+            min(BM, a.ws.offs[e + 1] - a.ws.offs[e] - (rb * BM - a.ws.poffs[e])));
         typename GemmTile<CfgUp>::Acc acc;
         const ARowsGather ar{a.x, a.H, a.ws.row_token + (int64_t)rb * BM};
         const uint16_t* B = a.w_up + (int64_t)e * a.H * a.I;
         if (DIRECT_UP)
-          GemmTile<CfgUp>::run_direct(ar, B, a.I, col0, a.I, a.H, lds, acc);
+          GemmTile<CfgUp>::run_direct(ar, B, a.I, col0, a.I, a.H, lds, acc, NoHook(), valid);
         else
           GemmTile<CfgUp>::run_regs(ar, B, a.I, col0, a.I, a.H, lds, acc);
         // h = bf16(SiLU(u)), SiLU(u) = u / (1 + e^-u)
@@ -394,23 +401,24 @@ __global__ void __launch_bounds__(kProdThreads) moe_producer_kernel(const ProdAr
         const int col0 = nt * BN_DN;
         block_wait_lines(a.sig_h + rb, sig_target(a.sa.epoch, (uint32_t)a.n_up_nt), a.sa, a.h_l1_only != 0);
         const uint64_t t1 = a.tl.buf ? wall_clock64() : 0;
+        // rows past the expert's last pair are padding: not computed (whole
+        // waves of them) and not stored
+        const int valid = __builtin_amdgcn_readfirstlane(
+            min(BM, a.ws.offs[e + 1] - a.ws.offs[e] - (rb * BM - a.ws.poffs[e])));
         typename GemmTile<CfgDn>::Acc acc;
         const ARowsLinear ar{a.ws.h, a.I, rb * BM, a.n_rb_max * BM};
         const uint16_t* B = a.w_down + (int64_t)e * a.I * a.H;
         if (DIRECT_DN)
-          GemmTile<CfgDn>::run_direct(ar, B, a.H, col0, a.H, a.I, lds, acc);
+          GemmTile<CfgDn>::run_direct(ar, B, a.H, col0, a.H, a.I, lds, acc, NoHook(), valid);
         else
           GemmTile<CfgDn>::run_regs(ar, B, a.H, col0, a.H, a.I, lds, acc);
-        // rows past the expert's last pair are padding: not stored
-        const int valid = __builtin_amdgcn_readfirstlane(
-            min(BM, a.ws.offs[e + 1] - a.ws.offs[e] - (rb * BM - a.ws.poffs[e])));
         const int H = a.H;
         if (a.y_bf16) {
           uint16_t* yb = (uint16_t*)a.ws.y + (int64_t)rb * BM * H + col0;
           GemmTile<CfgDn>::template store_bf16_staged<sizeof(lds), true>(
               acc, lds, yb, H, valid, H - col0, [](float v) { return v; });
         } else {
-          GemmTile<CfgDn>::store_f32<true>(acc, a.ws.y + (int64_t)rb * BM * H + col0, H, valid, H - col0);
+          GemmTile<CfgDn>::template store_f32<true>(acc, a.ws.y + (int64_t)rb * BM * H + col0, H, valid, H - col0);
         }
         block_coherent_complete();
         if (threadIdx.x == 0) {
@@ -621,7 +629,7 @@ tsg_status tsg_op_moe(tsg_ctx* ctx, const void* x, const int32_t* topk_ids, cons
     return check_launch(ctx, "moe_rb_order_kernel");
   };
   auto produce = [&](hipStream_t s, int nwg) -> tsg_status {
-    const bool du = H % (2 * CfgUp::BK) == 0, dd = I % (2 * CfgDn::BK) == 0;
+    const bool du = H % 128 == 0, dd = I % 128 == 0;
     time_begin(ctx, 0, s);
     if (du && dd) launch_prod<true, true>(pa, nwg, s);
     else if (du) launch_prod<true, false>(pa, nwg, s);

@@ -168,8 +168,12 @@ __global__ void __launch_bounds__(kThreads) moe_ag_kernel(const AgMoeArgs a) {
         const int first = __builtin_amdgcn_readfirstlane(a.tab.row_token[(int64_t)rb * BM]);
         const ARowsGather ar{a.x_full, a.H, a.tab.row_token + (int64_t)rb * BM, first};
         const uint16_t* B = a.w_up + (int64_t)e * a.H * a.I;
+        // rows past the expert's last pair are padding (whole waves of them
+        // skip their matrix work)
+        const int valid = __builtin_amdgcn_readfirstlane(
+            min(BM, a.tab.offs[e + 1] - a.tab.offs[e] - (rb * BM - a.tab.poffs[e])));
         if (DIRECT)
-          GemmTile<Cfg>::run_direct(ar, B, a.I, col0, a.I, a.H, lds, acc);
+          GemmTile<Cfg>::run_direct(ar, B, a.I, col0, a.I, a.H, lds, acc, NoHook(), valid);
         else
           GemmTile<Cfg>::run_regs(ar, B, a.I, col0, a.I, a.H, lds, acc);
         // h[pair] = bf16(SiLU(u)), SiLU(u) = u / (1 + e^-u), rows scattered

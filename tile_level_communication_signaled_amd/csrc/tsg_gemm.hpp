@@ -399,7 +399,7 @@ struct GemmTile {
   __device__ __forceinline__ static void run_direct(const ARows& ar,
                                                     const uint16_t* __restrict__ B, int64_t ldb,
                                                     int col0, int N, int K, char* lds, Acc& acc,
-                                                    Hook hook = Hook()) {
+                                                    Hook hook = Hook(), int rows_active = Cfg::BM) {
     static_assert(Cfg::B_STAGE % 1024 == 0, "a B stage must be whole 1 KB load blocks");
     constexpr int B_BLK = Cfg::B_STAGE / 1024;
     constexpr int B_BPW = (B_BLK + Cfg::NW - 1) / Cfg::NW;
@@ -487,8 +487,20 @@ struct GemmTile {
     // fragments of the next stage are read while the current stage's last
     // MFMAs run, so neither the barrier nor the LDS latency of a stage's first
     // reads leaves the matrix units idle.
+    // A wave whose rows all lie at or past rows_active (padding rows of the
+    // tile, wave-uniform) keeps its loads, waits and barriers but skips its
+    // fragment reads and MFMAs; its accumulators stay zero.  With two waves
+    // per SIMD from different row halves (4 x 2 waves), a tile with at most
+    // half its rows in use then takes about half the matrix time.
+    const bool on = rows_active >= Cfg::BM || wm0 < rows_active;  // folds to true for the default
+    auto rd = [&](Frags& f, const char* la, const char* lb, int ks) {
+      if (on) read_frags(f, la, lb, tr_off, ks, lane, wm0);
+    };
+    auto mm = [&](const Frags& f) {
+      if (on) mma(f, acc);
+    };
     Frags f0, f1;
-    read_frags(f0, lds_a, lds_b, tr_off, 0, lane, wm0);
+    rd(f0, lds_a, lds_b, 0);
     int sa = 0;  // kt % 3
     for (int kt = 0; kt < nk; ++kt) {
       const int sa2 = sa >= 1 ? sa - 1 : 2;   // (kt + 2) % 3
@@ -500,23 +512,23 @@ struct GemmTile {
       const char* la = lds_a + sa * Cfg::A_STAGE;
       const char* lb = lds_b + (kt & 1) * Cfg::B_STAGE;
       if constexpr (Cfg::KS == 4) {
-        read_frags(f1, la, lb, tr_off, 1, lane, wm0);
-        mma(f0, acc);
-        read_frags(f0, la, lb, tr_off, 2, lane, wm0);
-        mma(f1, acc);
-        read_frags(f1, la, lb, tr_off, 3, lane, wm0);
-        mma(f0, acc);
+        rd(f1, la, lb, 1);
+        mm(f0);
+        rd(f0, la, lb, 2);
+        mm(f1);
+        rd(f1, la, lb, 3);
+        mm(f0);
       } else {
-        read_frags(f1, la, lb, tr_off, 1, lane, wm0);
-        mma(f0, acc);
+        rd(f1, la, lb, 1);
+        mm(f0);
       }
       sa = sa == 2 ? 0 : sa + 1;
       if (kt + 1 < nk) {
         if (kt + 2 < nk) wait_vmcnt<Cfg::A_BPW>(); else wait_vmcnt<0>();
         lds_barrier();
-        read_frags(f0, lds_a + sa * Cfg::A_STAGE, lds_b + ((kt + 1) & 1) * Cfg::B_STAGE, tr_off, 0, lane, wm0);
+        rd(f0, lds_a + sa * Cfg::A_STAGE, lds_b + ((kt + 1) & 1) * Cfg::B_STAGE, 0);
       }
-      mma(f1, acc);
+      mm(f1);
     }
     lds_barrier();  // every wave is done with the stages before the LDS is reused
   }
