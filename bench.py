@@ -63,6 +63,10 @@ def _parse():
     p.add_argument("--timeline", action="store_true",
                    help="print each path's device timeline of one overlapped call (units active and "
                         "waiting per time bin) as markdown, and exit")
+    p.add_argument("--library-gemms", action="store_true",
+                   help="time torch.matmul (hipBLASLt) on the plain GEMMs of the AllGather, ReduceScatter and "
+                        "MLP paths beside this library's compute-only calls of those paths, print a markdown "
+                        "table and exit (a comparison only: no path calls the library)")
     p.add_argument("--summarize-mfma", metavar="CSV",
                    help="no GPU: turn the counter_collection.csv of a rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES "
                         "GRBM_GUI_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_BUSY_CYCLES SQ_LDS_BANK_CONFLICT "
@@ -643,6 +647,55 @@ def _timeline_text(name, recs, bins=24):
     return "\n".join(lines)
 
 
+def _library_gemms(torch, tsg, ctx, ag_fn):
+    """hipBLASLt (torch.matmul, bf16 operands) on the same GEMM shapes as the
+    AG, RS and MLP paths, beside this library's compute-only calls of those
+    paths (the same GEMMs; the MLP call also applies GELU between them).
+    Each figure is the best of 3 rounds of 100 back-to-back calls."""
+    from synth import CONFIGS
+    other = _other_paths(torch, tsg, ctx)
+
+    def best(fn, n=100):
+        ts = []
+        for _ in range(3):
+            for i in range(20):
+                fn(i)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(n):
+                fn(i)
+            torch.cuda.synchronize()
+            ts.append((time.perf_counter() - t0) / n * 1e3)
+        return min(ts)
+
+    def lib(M, N, K, out32):
+        a = torch.randn(M, K, device="cuda", dtype=torch.bfloat16)
+        b = torch.randn(K, N, device="cuda", dtype=torch.bfloat16)
+        if out32:
+            return best(lambda i: torch.mm(a, b, out_dtype=torch.float32))
+        return best(lambda i: torch.matmul(a, b))
+
+    ag, rs, mlp = CONFIGS["llama_ag"], CONFIGS["gemm_rs"], CONFIGS["mlp2"]
+    rows = []
+    t_ag = best(lambda i: ag_fn(i, tsg.COMPUTE_ONLY))
+    l_ag = lib(ag["M"], ag["N"], ag["K"], False)
+    rows.append(("AG GEMM %dx%dx%d, bf16 out" % (ag["M"], ag["N"], ag["K"]), 2.0 * ag["M"] * ag["N"] * ag["K"],
+                 l_ag, t_ag))
+    t_rs = best(lambda i: other["gemm_rs"][0](i, tsg.COMPUTE_ONLY))
+    l_rs = lib(rs["M"], rs["N"], rs["K"], True)
+    rows.append(("RS GEMM %dx%dx%d, fp32 out" % (rs["M"], rs["N"], rs["K"]), 2.0 * rs["M"] * rs["N"] * rs["K"],
+                 l_rs, t_rs))
+    M, K1, N1, N2 = mlp["M"], mlp["K1"], mlp["N1"], mlp["N2"]
+    t_mlp = best(lambda i: other["mlp2"][0](i, tsg.COMPUTE_ONLY))
+    l_mlp = lib(M, N1, K1, False) + lib(M, N2, N1, True)
+    rows.append(("MLP %dx%d -> %d -> %d (two GEMMs; bf16 H, fp32 Y)" % (M, K1, N1, N2),
+                 2.0 * M * N1 * K1 + 2.0 * M * N2 * N1, l_mlp, t_mlp))
+    out = ["| GEMM | hipBLASLt ms | TFLOP/s | this library, compute only, ms | TFLOP/s |", "|---|---|---|---|---|"]
+    for name, fl, lt, tt in rows:
+        out.append(f"| {name} | {lt:.4f} | {fl / lt / 1e9:.0f} | {tt:.4f} | {fl / tt / 1e9:.0f} |")
+    return "\n".join(out)
+
+
 def main():
     args = _parse()
     if args.summarize_counters:
@@ -690,6 +743,11 @@ def main():
             label = {tsg.OVERLAP: "overlap", tsg.SERIAL: "serial"}[mode]
             out += [f"### {name}, {label}", "", _timeline_text(name, ctx.timeline()), ""]
         print("\n".join(out), flush=True)
+        ctx.close()
+        return
+
+    if args.library_gemms:
+        print(_library_gemms(torch, tsg, ctx, ag_fn), flush=True)
         ctx.close()
         return
 

@@ -470,8 +470,8 @@ struct GemmTile {
     tr_lane_offsets(wn0, lane, tr_off);
 
     const int nk = K / Cfg::BK;
+    issue_b(0, 0);  // B never waits for a signal: its first stage loads during the A wait
     hook.before_a(0);
-    issue_b(0, 0);
     issue_a(0, 0);
     if (nk > 1) {
       hook.before_a(Cfg::BK);
