@@ -214,18 +214,20 @@ hipError_t launch_cfg(const RsGemmArgs& a, int grid, hipStream_t s) {
   return hipGetLastError();
 }
 
+// The GEMM kernel of a tile id and its workgroup size (threads).
 template <class Cfg>
-const void* fn_cfg(bool direct) {
+const void* fn_cfg(bool direct, int* nt) {
+  *nt = Cfg::NT;
   return direct ? (const void*)&rs_gemm_kernel<Cfg, true> : (const void*)&rs_gemm_kernel<Cfg, false>;
 }
 
-const void* gemm_fn(int id, bool direct) {
+const void* gemm_fn(int id, bool direct, int* nt) {
   switch (id) {
-    case 1: return fn_cfg<Cfg1>(direct);
-    case 3: return fn_cfg<Cfg3>(direct);
-    case 4: return fn_cfg<Cfg4>(direct);
-    case 5: return fn_cfg<Cfg5>(direct);
-    case 6: return fn_cfg<Cfg6>(direct);
+    case 1: return fn_cfg<Cfg1>(direct, nt);
+    case 3: return fn_cfg<Cfg3>(direct, nt);
+    case 4: return fn_cfg<Cfg4>(direct, nt);
+    case 5: return fn_cfg<Cfg5>(direct, nt);
+    case 6: return fn_cfg<Cfg6>(direct, nt);
     default: return nullptr;
   }
 }
@@ -351,8 +353,12 @@ tsg_status tsg_op_rs(tsg_ctx* ctx, const void* x, const void* w, float* partial,
   // share a CU they run back to back instead.
   bool back_to_back = mode == TSG_MODE_SERIAL;
   if (mode == TSG_MODE_OVERLAP && o.aux_cus < 0) {
+    // (a reduce workgroup placed where the GEMM's next tile cannot then fit
+    // would wait for that tile until its time-out)
     const bool direct = K % 128 == 0;
-    back_to_back = !co_resident(ctx, gemm_fn(tile, direct), 256 /* 2 x 2 waves */, (const void*)&rs_reduce_kernel, 256);
+    int gemm_nt = 0;
+    const void* fn = gemm_fn(tile, direct, &gemm_nt);
+    back_to_back = !co_resident(ctx, fn, gemm_nt, (const void*)&rs_reduce_kernel, 256);
   }
   if (back_to_back) {
     st = gemm(caller, ctx->n_cus);

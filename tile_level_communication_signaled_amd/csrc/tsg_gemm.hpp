@@ -316,11 +316,13 @@ struct GemmTile {
   // so a row keeps its place.
   // With 16-column fragments one half wave reads rows 8 g .. 8 g + 3 for
   // g = 0, 1 (32 bytes of each); rows eight apart start at the same bank
-  // whenever BN is a multiple of 16, so when the rows are otherwise
-  // unswizzled, chunk c of a row with bit 3 set is stored at c ^ 2 (32
-  // bytes over, within its aligned group of four chunks).
+  // whenever BN is a multiple of 16, and (r mod 4) does not tell them
+  // apart, so chunk c of a row with bit 3 set is moved by a further XOR
+  // with 2 (32 bytes over, within its aligned group of four chunks): with
+  // rows of a multiple of 256 bytes the half wave's eight rows then take
+  // the sixteen 16-byte slots of one 256-byte bank cycle once each.
   static constexpr int B_SWZ = Cfg::BN % 128 == 0 ? 4 : Cfg::BN % 64 == 0 ? 2 : 0;
-  static constexpr int B_SWZ8 = (Cfg::MF == 16 && B_SWZ == 0 && Cfg::BN % 32 == 0) ? 2 : 0;
+  static constexpr int B_SWZ8 = (Cfg::MF == 16 && B_SWZ != 2 && Cfg::BN % 32 == 0) ? 2 : 0;
   __device__ __forceinline__ static int b_swz(int row) {
     return B_SWZ * (row & 3) ^ B_SWZ8 * ((row >> 3) & 1);
   }
