@@ -65,8 +65,9 @@ def _parse():
                         "waiting per time bin) as markdown, and exit")
     p.add_argument("--library-gemms", action="store_true",
                    help="time torch.matmul (hipBLASLt) on the plain GEMMs of the AllGather, ReduceScatter and "
-                        "MLP paths beside this library's compute-only calls of those paths, print a markdown "
-                        "table and exit (a comparison only: no path calls the library)")
+                        "MLP paths, and torch's scaled_dot_product_attention (flash and memory-efficient "
+                        "backends only) on the attention workload, beside this library's compute-only calls of "
+                        "those paths; print a markdown table and exit (a comparison only: no path calls them)")
     p.add_argument("--summarize-mfma", metavar="CSV",
                    help="no GPU: turn the counter_collection.csv of a rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES "
                         "GRBM_GUI_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_BUSY_CYCLES SQ_LDS_BANK_CONFLICT "
@@ -644,6 +645,32 @@ def _timeline_text(name, recs, bins=24):
             wt = sum(1 for r in rows if r[0] == kind and r[1] < hi and r[2] >= lo and r[2] > r[1])
             cells.append(f"{act} ({wt})" if wt else f"{act}")
         lines.append(f"| {(lo - t0) / 100:.1f} | " + " | ".join(cells) + " |")
+    # per kind: when its units ran, how long they waited for signals and how
+    # long they ran once their data was there
+    import numpy as np
+    lines += ["", "| units | count | start (us) | wait median / max (us) | run after the wait, median / p90 (us) "
+                  "| end (us) |", "|---|---|---|---|---|---|"]
+    for kind, label in kinds:
+        rr = [r for r in rows if r[0] == kind]
+        if not rr:
+            continue
+        st = np.array([(r[1] - t0) / 100 for r in rr])
+        wt = np.array([(r[2] - r[1]) / 100 for r in rr])
+        ru = np.array([(r[3] - r[2]) / 100 for r in rr])
+        en = np.array([(r[3] - t0) / 100 for r in rr])
+        lines.append(f"| {label} | {len(rr)} | {st.min():.1f}-{st.max():.1f} | {np.median(wt):.1f} / {wt.max():.1f} "
+                     f"| {np.median(ru):.1f} / {np.percentile(ru, 90):.1f} | {en.min():.1f}-{en.max():.1f} |")
+    if name == "ag_gemm":
+        # copy units carry (chunk << 24 | slab << 12 | piece): when each of the
+        # first column slabs was complete in every chunk
+        done = {}
+        for r0 in recs:
+            if int(r0[0]) >> 56 == 1:
+                sl = (int(r0[0]) >> 12) & 0xfff
+                done[sl] = max(done.get(sl, 0), (r0[3] - t0) / 100)
+        if done:
+            lines += ["", "Column slab complete in every chunk (us): " +
+                      ", ".join(f"slab {k}: {v:.1f}" for k, v in sorted(done.items())[:8]) + "."]
     return "\n".join(lines)
 
 
@@ -690,9 +717,30 @@ def _library_gemms(torch, tsg, ctx, ag_fn):
     l_mlp = lib(M, N1, K1, False) + lib(M, N2, N1, True)
     rows.append(("MLP %dx%d -> %d -> %d (two GEMMs; bf16 H, fp32 Y)" % (M, K1, N1, N2),
                  2.0 * M * N1 * K1 + 2.0 * M * N2 * N1, l_mlp, t_mlp))
-    out = ["| GEMM | hipBLASLt ms | TFLOP/s | this library, compute only, ms | TFLOP/s |", "|---|---|---|---|---|"]
+    # attention: 2048 queries (one rank's share) over 16384 keys, 32 heads of
+    # 128, bf16; torch's fused backends only (its math path is never used)
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    import torch.nn.functional as F
+    S, Hh, D, sl = 16384, 32, 128, 2048
+    q = torch.randn(1, Hh, sl, D, device="cuda", dtype=torch.bfloat16)
+    k = torch.randn(1, Hh, S, D, device="cuda", dtype=torch.bfloat16)
+    v = torch.randn(1, Hh, S, D, device="cuda", dtype=torch.bfloat16)
+    t_at = best(lambda i: other["ag_kv_attention"][0](i, tsg.COMPUTE_ONLY), 30)
+    l_at = None
+    for be in (SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION):
+        try:
+            with sdpa_kernel([be]):
+                t = best(lambda i: F.scaled_dot_product_attention(q, k, v), 30)
+            l_at = t if l_at is None else min(l_at, t)
+        except RuntimeError:
+            pass
+    out = ["| operation | library ms | TFLOP/s | this library, compute only, ms | TFLOP/s |", "|---|---|---|---|---|"]
     for name, fl, lt, tt in rows:
-        out.append(f"| {name} | {lt:.4f} | {fl / lt / 1e9:.0f} | {tt:.4f} | {fl / tt / 1e9:.0f} |")
+        out.append(f"| {name}: hipBLASLt | {lt:.4f} | {fl / lt / 1e9:.0f} | {tt:.4f} | {fl / tt / 1e9:.0f} |")
+    fl_at = 4.0 * sl * S * D * Hh
+    if l_at is not None:
+        out.append(f"| attention {sl} queries x {S} keys x {Hh} heads of {D}: torch SDPA (flash / memory-efficient) "
+                   f"| {l_at:.4f} | {fl_at / l_at / 1e9:.0f} | {t_at:.4f} | {fl_at / t_at / 1e9:.0f} |")
     return "\n".join(out)
 
 
@@ -728,7 +776,7 @@ def main():
         # One overlapped call per path with device timestamps (after warm-up);
         # AG also serialized, for comparison.
         out = ["Device timelines (`python3 bench.py --timeline`), one call each.", ""]
-        runs = [("ag_gemm", ag_fn, tsg.OVERLAP), ("ag_gemm", ag_fn, tsg.SERIAL)]
+        runs = [("ag_gemm", ag_fn, tsg.OVERLAP), ("ag_gemm", ag_fn, tsg.SERIAL), ("ag_gemm", ag_fn, tsg.COMPUTE_ONLY)]
         if args.paths == "all":
             for name, (fn, *_rest) in _other_paths(torch, tsg, ctx).items():
                 runs.append((name, fn, tsg.OVERLAP))
@@ -740,7 +788,7 @@ def main():
             torch.cuda.synchronize()
             if ctx.check() != tsg.OK:
                 raise RuntimeError(ctx.last_error())
-            label = {tsg.OVERLAP: "overlap", tsg.SERIAL: "serial"}[mode]
+            label = {tsg.OVERLAP: "overlap", tsg.SERIAL: "serial", tsg.COMPUTE_ONLY: "compute only"}[mode]
             out += [f"### {name}, {label}", "", _timeline_text(name, ctx.timeline()), ""]
         print("\n".join(out), flush=True)
         ctx.close()
