@@ -407,7 +407,8 @@ def _path_line(tsg, timer, flops, nbytes, modes, n):
          "compute_only": tm.get(tsg.COMPUTE_ONLY), "comm_only": tm.get(tsg.COMM_ONLY)}
     if t["serial"] is None or t["compute_only"] is None:
         ov = t["overlap"]
-        out = {"ms": {"overlap": round(ov, 5)}, "tflops": round(flops / (ov * 1e-3) / 1e12, 2),
+        out = {"ms": {k: round(v, 5) for k, v in t.items() if v is not None},
+               "tflops": round(flops / (ov * 1e-3) / 1e12, 2),
                "pct_bf16_peak": round(100.0 * flops / (ov * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
                "hbm_GBps_algorithmic": round(nbytes / (ov * 1e-3) / 1e9, 1)}
     else:
@@ -917,6 +918,13 @@ def main():
         sweep["shared, grouped order"] = _path_line(
             tsg, Timer(torch, tsg, ctx, lambda i, mode, o_=None: fn(i, mode, og)), flops, nbytes, (tsg.OVERLAP,), n)
         paths["mlp2_cu_splits"] = sweep
+        # the GEMM+RS eight-wave tile (16x16x32 fragments): faster alone, but
+        # its workgroups fill their CUs, so overlap runs back to back
+        fn, flops, nbytes, _m = other["gemm_rs"]
+        o6 = tsg.Opts(tile=6)
+        paths["gemm_rs_tile6"] = _path_line(
+            tsg, Timer(torch, tsg, ctx, lambda i, mode, o_=None: fn(i, mode, o6)), flops, nbytes,
+            (tsg.OVERLAP, tsg.COMPUTE_ONLY), n)
         fn, flops, nbytes, _m = other["moe"]
         o16 = tsg.Opts(aux_cus=16)
         paths["moe_combine_16cu"] = _path_line(
