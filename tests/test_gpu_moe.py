@@ -164,9 +164,11 @@ def _check(case, out, counts, sorted_ids, y_bf16=False, label=""):
 
 
 # (9000, ...) and (32767, ...): routed pair blocks of 128 and 256 pairs, the
-# second at the largest T * k the routing takes (65534 pairs)
+# second at the largest T * k the routing takes (65534 pairs); 16 to 40
+# experts: more groups of pairs per wave in the counting and placement.
 @pytest.mark.parametrize("T,H,I,E", [(100, 256, 128, 4), (37, 136, 200, 3), (1, 64, 64, 2), (300, 512, 256, 8),
-                                     (9000, 64, 72, 5), (32767, 64, 64, 8)])
+                                     (9000, 64, 72, 5), (32767, 64, 64, 8), (300, 256, 128, 24),
+                                     (2000, 64, 64, 40), (700, 64, 64, 16)])
 def test_moe_small(env, T, H, I, E):
     inp = moe_inputs(T, H, I, E, k=2, seed=T + E)
     case = MoeCase(env, inp)
