@@ -69,7 +69,10 @@ typedef enum tsg_mode {
                                 wait pre-satisfied; outputs hold valid values
                                 only if the data they read is already present  */
   TSG_MODE_COMM_ONLY = 3     /* the copy / reduce / combine kernel alone, with
-                                the same launch shape as in overlap mode      */
+                                the grid of overlap mode; on shared CUs it
+                                runs on `stream` itself (no side stream), and
+                                the GEMM+RS reduce then takes one pass per
+                                unit, as when it follows the GEMM             */
 } tsg_mode;
 
 typedef enum tsg_dtype { TSG_F32 = 0, TSG_BF16 = 1 } tsg_dtype;

@@ -717,6 +717,8 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
     return st;
   }
   if (mode == TSG_MODE_COMPUTE_ONLY) return gemm(caller, 0, ctx->n_cus);
+  // the copy alone on shared CUs has nothing to overlap with: no fork
+  if (mode == TSG_MODE_COMM_ONLY && o.aux_cus < 0) return copy(caller);
 
   st = fork(ctx, caller, pr);
   if (st != TSG_OK) return st;

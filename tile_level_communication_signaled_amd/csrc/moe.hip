@@ -661,7 +661,10 @@ tsg_status tsg_op_moe(tsg_ctx* ctx, const void* x, const int32_t* topk_ids, cons
     if (st == TSG_OK && mode == TSG_MODE_SERIAL) st = combine(caller, ctx->n_cus * 2, 1);
     return st;
   }
-  if (noalloc) return combine(caller, ctx->n_cus * 2, 0);  // COMM_ONLY on the caller's stream
+  // Here the mode is COMM_ONLY, or OVERLAP on a CU split.  The combine alone
+  // on shared CUs (always so in the no-alloc form) has nothing to overlap
+  // with, so it runs on the caller's stream.
+  if (o.aux_cus < 0) return combine(caller, o.aux_wgs > 0 ? o.aux_wgs : ctx->n_cus * 2, 0);
   Pair pr;
   st = streams(ctx, o, &pr);
   if (st != TSG_OK) return st;

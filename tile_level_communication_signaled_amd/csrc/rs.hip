@@ -106,6 +106,10 @@ struct RsReduceArgs {
 //   acquire the tile's done signal, then out += the local partial.
 // Phase 1 depends on nothing the GEMM computes, so it runs beside the
 // GEMM's first tiles; only the last third of the traffic waits for them.
+// When no GEMM runs beside the reduce (back to back, or the reduce alone),
+// each unit is done in one pass instead: acquire its tile's signal (already
+// complete), load the peers and the local partial together and store out
+// once, which saves writing and re-reading out; the additions are the same.
 // Every thread re-reads exactly the elements it stored, so the two phases
 // need no synchronisation between threads.  Summation order per element:
 // peers in ascending rank order, then the local partial.
@@ -116,8 +120,13 @@ __device__ __forceinline__ float4 nt_load4(const float* p) {
   return make_float4(v[0], v[1], v[2], v[3]);
 }
 
+// P_MAX peers per load batch (2 P_MAX 16-byte loads in flight per thread):
+// 4 beside the GEMM (the registers a reduce wave has next to a GEMM wave), 8
+// when the reduce runs on CUs of its own or after the GEMM (seven peers in
+// one batch: one memory round trip per unit).  The summation order is the
+// same for both.
+template <int P_MAX, bool ONE_PASS>
 __global__ void __launch_bounds__(256) rs_reduce_kernel(const RsReduceArgs a) {
-  constexpr int P_MAX = 4;  // peers per load batch (eight 16-byte loads in flight)
   const int n_units = a.n_ftm * a.n_ftn * 8;
   const int c0 = a.rank * a.chunk_rows, c1 = c0 + a.chunk_rows;
   const int cx = threadIdx.x & 31;
@@ -129,6 +138,47 @@ __global__ void __launch_bounds__(256) rs_reduce_kernel(const RsReduceArgs a) {
     col = ftn * kFlagTile + cx * 4;
     r0 = ftm * kFlagTile + part * 16 + ry;
   };
+  if constexpr (ONE_PASS) {
+    for (int u = blockIdx.x; u < n_units; u += gridDim.x) {
+      int ftm, ftn, r0, col;
+      where(u, ftm, ftn, r0, col);
+      const int r1 = r0 + 8;
+      const bool ok0 = col < a.N && r0 >= c0 && r0 < c1;
+      const bool ok1 = col < a.N && r1 >= c0 && r1 < c1;
+      const uint64_t t0 = a.tl.buf ? wall_clock64() : 0;
+      if (a.wait) block_poll_ge(a.flags + (int64_t)ftm * a.n_ftn + ftn, sig_target(a.sa.epoch, 1), a.sa);
+      const uint64_t t1 = a.tl.buf ? wall_clock64() : 0;
+      float4 q0, q1;
+      if (ok0) q0 = load_coherent((const float4*)(a.partial + (int64_t)r0 * a.N + col));
+      if (ok1) q1 = load_coherent((const float4*)(a.partial + (int64_t)r1 * a.N + col));
+      float4 s0 = make_float4(0.f, 0.f, 0.f, 0.f), s1 = s0;
+      const uint32_t o0 = (uint32_t)((r0 - c0) * a.N + col), o1 = o0 + 8u * (uint32_t)a.N;
+      for (int p0 = 0; p0 < a.R - 1; p0 += P_MAX) {
+        const int np = min(P_MAX, a.R - 1 - p0);
+        float4 v0[P_MAX], v1[P_MAX];
+#pragma unroll
+        for (int p = 0; p < P_MAX; ++p) {
+          if (p < np) {
+            const float* pp = a.peers + (int64_t)(p0 + p) * a.chunk_rows * a.N;
+            if (ok0) v0[p] = nt_load4(pp + o0);
+            if (ok1) v1[p] = nt_load4(pp + o1);
+          }
+        }
+#pragma unroll
+        for (int p = 0; p < P_MAX; ++p) {
+          if (p < np) {
+            if (ok0) { s0.x += v0[p].x; s0.y += v0[p].y; s0.z += v0[p].z; s0.w += v0[p].w; }
+            if (ok1) { s1.x += v1[p].x; s1.y += v1[p].y; s1.z += v1[p].z; s1.w += v1[p].w; }
+          }
+        }
+      }
+      if (ok0) *(float4*)(a.out + o0) = make_float4(s0.x + q0.x, s0.y + q0.y, s0.z + q0.z, s0.w + q0.w);
+      if (ok1) *(float4*)(a.out + o1) = make_float4(s1.x + q1.x, s1.y + q1.y, s1.z + q1.z, s1.w + q1.w);
+      if (a.tl.buf && threadIdx.x == 0 && (u & 7) == 0)
+        timeline_put(a.tl, 4, (uint32_t)(ftm << 16 | ftn), t0, t1, wall_clock64());
+    }
+    return;
+  }
   for (int u = blockIdx.x; u < n_units; u += gridDim.x) {
     int ftm, ftn, r0, col;
     where(u, ftm, ftn, r0, col);
@@ -338,10 +388,17 @@ tsg_status tsg_op_rs(tsg_ctx* ctx, const void* x, const void* w, float* partial,
     if (e != hipSuccess) return hip_fail(ctx, e, "rs_gemm_kernel");
     return TSG_OK;
   };
-  auto reduce = [&](hipStream_t s, int nwg, int wait) -> tsg_status {
+  // beside: the GEMM runs at the same time (on the same or other CUs)
+  auto reduce = [&](hipStream_t s, int nwg, int wait, bool beside) -> tsg_status {
     ra.wait = wait;
+    const dim3 grid(std::max(1, std::min(nwg, 8 * n_red_tiles)));
     time_begin(ctx, 1, s);
-    hipLaunchKernelGGL(rs_reduce_kernel, dim3(std::max(1, std::min(nwg, 8 * n_red_tiles))), dim3(256), 0, s, ra);
+    if (beside && o.aux_cus < 0)  // sharing every CU with the GEMM: fewer registers
+      hipLaunchKernelGGL((rs_reduce_kernel<4, false>), grid, dim3(256), 0, s, ra);
+    else if (beside)
+      hipLaunchKernelGGL((rs_reduce_kernel<8, false>), grid, dim3(256), 0, s, ra);
+    else
+      hipLaunchKernelGGL((rs_reduce_kernel<8, true>), grid, dim3(256), 0, s, ra);
     time_end(ctx, 1, s);
     return check_launch(ctx, "rs_reduce_kernel");
   };
@@ -358,14 +415,17 @@ tsg_status tsg_op_rs(tsg_ctx* ctx, const void* x, const void* w, float* partial,
     const bool direct = K % 128 == 0;
     int gemm_nt = 0;
     const void* fn = gemm_fn(tile, direct, &gemm_nt);
-    back_to_back = !co_resident(ctx, fn, gemm_nt, (const void*)&rs_reduce_kernel, 256);
+    back_to_back = !co_resident(ctx, fn, gemm_nt, (const void*)&rs_reduce_kernel<4, false>, 256);
   }
   if (back_to_back) {
     st = gemm(caller, ctx->n_cus);
-    if (st == TSG_OK) st = reduce(caller, o.aux_wgs > 0 ? o.aux_wgs : ctx->n_cus * 2, 1);
+    if (st == TSG_OK) st = reduce(caller, o.aux_wgs > 0 ? o.aux_wgs : ctx->n_cus * 2, 1, false);
     return st;
   }
 
+  // the reduce alone on shared CUs has nothing to overlap with: no fork
+  if (mode == TSG_MODE_COMM_ONLY && o.aux_cus < 0)
+    return reduce(caller, o.aux_wgs > 0 ? o.aux_wgs : 2 * ctx->n_cus, 0, false);
   Pair pr;
   st = streams(ctx, o, &pr, caller);
   if (st != TSG_OK) return st;
@@ -374,7 +434,7 @@ tsg_status tsg_op_rs(tsg_ctx* ctx, const void* x, const void* w, float* partial,
   if (st != TSG_OK) return st;
   // Producer (GEMM) first, consumer (reduce) second: the GEMM never waits.
   if (mode == TSG_MODE_OVERLAP) st = gemm(pr.main, pr.main_cus);
-  if (st == TSG_OK) st = reduce(pr.aux, nwg, mode == TSG_MODE_OVERLAP ? 1 : 0);
+  if (st == TSG_OK) st = reduce(pr.aux, nwg, mode == TSG_MODE_OVERLAP ? 1 : 0, mode == TSG_MODE_OVERLAP);
   tsg_status sj = join(ctx, caller, pr);
   return st != TSG_OK ? st : sj;
 }
