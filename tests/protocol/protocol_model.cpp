@@ -202,11 +202,12 @@ void check_decode() {
   std::printf("ok unit_decode\n");
 }
 
-// One call of the AllGather protocol: copy workers and pulling consumers
-// claim units from one ticket counter; every unit "moves" its rows (writes
-// the call's epoch into each row word of its piece) and arrives on its
-// (channel, slab) signal; consumer tiles wait for their channels' signals
-// and check every row word they cover.  The last claimer to leave resets
+// One call of the AllGather protocol: pulling consumer j moves unit j
+// directly (no ticket), and the copy workers claim the other units from one
+// ticket counter (ticket t is unit n_pull + t); every unit "moves" its rows
+// (writes the call's epoch into each row word of its piece) and arrives on
+// its (channel, slab) signal; consumer tiles wait for their channels' signals
+// and check every row word they cover.  The last copy worker to leave resets
 // the ticket and exit counters.
 struct AgCall {
   AgShape a;
@@ -219,7 +220,8 @@ void ag_call(Signals& S, std::vector<std::atomic<uint32_t>>& rows, std::atomic<u
              std::vector<std::atomic<int>>& moved, const AgCall& c, uint32_t epoch, uint64_t seed,
              uint32_t withheld, int bound_ms) {
   const AgShape& a = c.a;
-  const int R = a.R, C = a.C, n_workers = c.n_copy + c.n_pull;
+  const int R = a.R, C = a.C, n_workers = c.n_copy;
+  const int n_pull = std::min(c.n_pull, a.n_units);  // units taken without a ticket
   for (auto& m : moved) m.store(0);
   auto move_unit = [&](int u) {
     const Unit x = decode(a, u);
@@ -247,7 +249,7 @@ void ag_call(Signals& S, std::vector<std::atomic<uint32_t>>& rows, std::atomic<u
   run_threads(c.n_copy + c.n_pull, seed, [&](int w) {
     if (w < c.n_copy) {  // copy kernel workgroup: claim until none is left
       for (;;) {
-        const int u = (int)queue[0].fetch_add(1, std::memory_order_relaxed);
+        const int u = n_pull + (int)queue[0].fetch_add(1, std::memory_order_relaxed);
         if (u >= a.n_units) break;
         jitter(30);
         move_unit(u);
@@ -255,10 +257,9 @@ void ag_call(Signals& S, std::vector<std::atomic<uint32_t>>& rows, std::atomic<u
       leave();
       return;
     }
-    // GEMM workgroup: pull one unit, then compute tiles
-    const int u = (int)queue[0].fetch_add(1, std::memory_order_relaxed);
-    if (u < a.n_units) move_unit(u);
-    leave();
+    // GEMM workgroup j: move unit j, then compute tiles
+    const int j = w - c.n_copy;
+    if (j < n_pull) move_unit(j);
     for (int t = tile_next.fetch_add(1); t < n_tiles; t = tile_next.fetch_add(1)) {
       const int lo = t * BM, hi = std::min(M, lo + BM) - 1;
       bool ok = true;

@@ -169,13 +169,20 @@ __global__ void __launch_bounds__(Cfg::NT) ag_gemm_kernel(const AgGemmArgs args)
   const int row0 = mt * Cfg::BM, col0 = nt * Cfg::BN;
   const uint64_t t0 = args.tl.buf ? wall_clock64() : 0;
   if ((int)blockIdx.x < args.pull_wgs) {
-    // tile_pull_data: move one unit of the copy's queue before any wait, or
-    // with pull_all every unit left (the LDS is not in use yet, so its first
-    // word carries the ticket)
-    for (int u = claim_unit(args.copy, (volatile int*)lds); u < args.copy.n_units;
-         u = args.pull_all ? claim_unit(args.copy, (volatile int*)lds) : args.copy.n_units)
-      copy_unit<Cfg::NT>(args.copy, u);
-    if (threadIdx.x == 0) leave_queue(args.copy);
+    // tile_pull_data: move copy units before any wait.  Workgroup b moves
+    // unit b (the first slab's pieces, taken without a ticket: the copy
+    // kernel's queue starts after them), or with pull_all every unit left in
+    // the queue (the LDS is not in use yet, so its first word carries the
+    // ticket).
+    if (args.pull_all) {
+      for (int u = claim_unit(args.copy, (volatile int*)lds); u < args.copy.n_units;
+           u = claim_unit(args.copy, (volatile int*)lds))
+        copy_unit<Cfg::NT>(args.copy, u);
+      if (threadIdx.x == 0) leave_queue(args.copy);
+    } else if ((int)blockIdx.x < args.copy.n_units) {
+      if (blockIdx.x == 0 && threadIdx.x == 0) pace_start(args.copy);
+      copy_unit<Cfg::NT>(args.copy, (int)blockIdx.x);
+    }
   }
   SlabWait hook;
   hook.active = false;
@@ -582,7 +589,11 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
     pull = o.pull_units > 0 ? o.pull_units : std::min(ctx->n_cus, ustart[1]);
     pull = (int)std::min<int64_t>(std::min(pull, grid_gemm), n_units);
   }
-  ca.n_workers = (uint32_t)(pull_all ? pull : copy_grid + pull);
+  // Units 0 .. pull - 1 are moved by GEMM workgroups 0 .. pull - 1 directly
+  // (no ticket: at the start every workgroup of the GPU would claim from the
+  // one counter at once); the copy kernel's queue hands out the rest.
+  ca.unit_base = (!pull_all && pull > 0) ? pull : 0;
+  ca.n_workers = (uint32_t)(pull_all ? pull : copy_grid);
   ga.pull_wgs = 0;
   ga.pull_all = pull_all ? 1 : 0;
   ga.copy = ca;

@@ -511,6 +511,7 @@ tsg_status tsg_op_attn(tsg_ctx* ctx, const void* q, const void* k_local, const v
   ck.n_workers = 0;
   ck.pace_word = nullptr;
   ck.pace_ticks = 0.f;
+  ck.unit_base = 0;
   CopyArgs cv = ck;
   cv.a_local = (const u32x4_t*)v_local;
   cv.a_peers = (const u32x4_t*)v_peers;

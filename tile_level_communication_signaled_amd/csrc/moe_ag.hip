@@ -333,6 +333,7 @@ tsg_status tsg_op_moe_ag(tsg_ctx* ctx, const void* x_local, const void* x_peers,
   ca.n_workers = 0;
   ca.pace_word = nullptr;
   ca.pace_ticks = 0.f;
+  ca.unit_base = 0;
 
   AgMoeArgs ka;
   ka.x_full = (const uint16_t*)x_full;

@@ -51,6 +51,7 @@ struct CopyArgs {
   // last of the n_workers claimers to leave resets both for the next call.
   uint32_t* queue;
   uint32_t n_workers;
+  int unit_base;           // ticket t of the queue is unit unit_base + t (units below are taken statically)
   // Arrival pacing (pace_ticks > 0): unit u is published no earlier than
   // (u + 1) * pace_ticks wall-clock ticks after the first unit was taken;
   // the taker of ticket 0 stores that time, tagged with the call's epoch,
@@ -62,7 +63,7 @@ struct CopyArgs {
 constexpr uint64_t kPaceClockMask = (uint64_t(1) << 48) - 1;
 
 // Time the first unit of this call was taken (one lane; bounded wait for the
-// taker of ticket 0 to publish it).
+// taker of unit 0 to publish it).
 __device__ __forceinline__ uint64_t pace_base(const CopyArgs& a) {
   const uint64_t tag = (uint64_t)(a.sa.epoch & 0xffffu) << 48;
   const uint64_t t0 = wall_clock64();
@@ -180,16 +181,21 @@ __device__ __forceinline__ void copy_unit(const CopyArgs& a, int u) {
     timeline_put(a.tl, 1, (uint32_t)(c << 24 | s << 12 | ((ch * npc + j) & 0xfff)), t0, t0, wall_clock64());
 }
 
+// Paced arrival: the taker of unit 0 records when the copy started (one lane).
+__device__ __forceinline__ void pace_start(const CopyArgs& a) {
+  if (a.pace_ticks > 0.f)
+    __hip_atomic_store(a.pace_word,
+                       ((uint64_t)(a.sa.epoch & 0xffffu) << 48) | (wall_clock64() & kPaceClockMask),
+                       __ATOMIC_RELAXED, TSG_SIG_SCOPE);
+}
+
 // Next unit from the queue, identical in every thread (`slot` is one int of
 // LDS owned by the caller).
 __device__ __forceinline__ int claim_unit(const CopyArgs& a, volatile int* slot) {
   if (threadIdx.x == 0) {
     const int t = (int)atomicAdd(a.queue, 1u);
-    if (t == 0 && a.pace_ticks > 0.f)
-      __hip_atomic_store(a.pace_word,
-                         ((uint64_t)(a.sa.epoch & 0xffffu) << 48) | (wall_clock64() & kPaceClockMask),
-                         __ATOMIC_RELAXED, TSG_SIG_SCOPE);
-    *slot = t;
+    if (t + a.unit_base == 0) pace_start(a);
+    *slot = t + a.unit_base;
   }
   __syncthreads();
   const int u = __builtin_amdgcn_readfirstlane(*slot);
