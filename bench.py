@@ -785,6 +785,9 @@ def main():
             for i in range(200):
                 fn(i, mode)
             torch.cuda.synchronize()
+            # the recorded call follows another call on the stream without a
+            # host synchronisation, as in the timed loops
+            fn(1, mode)
             fn(0, mode, tsg.Opts(aux_cus=args.aux_cus, tile=args.tile, timeline=1))
             torch.cuda.synchronize()
             if ctx.check() != tsg.OK:
