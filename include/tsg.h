@@ -25,7 +25,8 @@
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Calls are asynchronous and stream-ordered: work forks from `stream` to
  *     the context's side streams and joins back before the call returns, so
- *     later work on `stream` sees every output.
+ *     later work on `stream` sees every output (gemm_ag_overlap in overlap
+ *     mode on shared CUs joins through its GEMM instead: see there).
  *   - Return value: TSG_OK or a negative tsg_status.  Argument errors are
  *     detected before anything is enqueued; the message is available from
  *     tsg_last_error().  Device-side errors (a signal wait that exceeded its
@@ -279,7 +280,17 @@ tsg_status tsg_timeline(tsg_ctx* ctx, uint64_t* out, size_t cap, size_t* n);
  *                  rank+1, rank+2, ... (mod R)
  * Constraints: 1 <= R <= 32, 0 <= rank < R, M % R == 0, M >= R,
  * N % 8 == 0, K % 8 == 0, N, K >= 8 (else TSG_E_SHAPE).
- * COMPUTE_ONLY expects a_full to hold the gathered peer chunks already. */
+ * COMPUTE_ONLY expects a_full to hold the gathered peer chunks already.
+ *
+ * Overlap on shared CUs (opts.aux_cus < 0, no timeline, no debug skip mask),
+ * with a copy kernel beside the GEMM: `stream` waits for the GEMM only, not
+ * for the copy kernel on the side stream.  The GEMM ends only after it has
+ * observed every chunk's arrival (tiles inside the local chunk wait for it
+ * after their stores), so a_full and c are complete, and a_local and a_peers
+ * no longer read, when `stream` passes the call; the copy kernel's
+ * workgroups may still be leaving its work queue (context-internal words).
+ * After a device-side error the copy may still run: tsg_check() waits for
+ * the side streams before it reports. */
 tsg_status gemm_ag_overlap(tsg_ctx* ctx, const void* a_local, const void* a_peers,
                            void* a_full, const void* b, void* c, int c_dtype,
                            int M, int N, int K, int R, int rank,

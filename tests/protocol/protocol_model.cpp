@@ -25,14 +25,21 @@
 //     gets a phase-1 item while a phase-0 item is still unclaimed, so GEMM2
 //     tiles (which wait for GEMM1 row blocks) never starve the producers;
 //   * a withheld signal ends in a bounded wait that sets the error word, and
-//     later waits of that call return at once.
+//     later waits of that call return at once;
+//   * when the last GEMM workgroup of an AllGather call ends (the caller's
+//     stream does not wait for the copy kernel), every row of every chunk,
+//     the local chunk's included, holds the call's data and every arrival
+//     counter is back at zero, while copy workgroups may still be leaving
+//     their queue.
 // Usage: protocol_model [iterations] [seed]; prints one "ok <scenario>" line
 // per scenario and exits 0, or prints "FAIL ..." and exits 1.
 // Built with -DMUTATION=m (m > 0) the model plants one mistake in its own
 // restatement of the protocol, so that a test can show the checks catch it:
 //   1: the last arriver does not reset the arrival counter;
 //   2: a counted signal is published by its first arriver;
-//   3: the last claimer to leave does not reset the ticket counter.
+//   3: the last claimer to leave does not reset the ticket counter;
+//   4: AllGather tiles inside the local chunk do not wait for its arrival at
+//      their end.
 #ifndef MUTATION
 #define MUTATION 0
 #endif
@@ -207,13 +214,15 @@ void check_decode() {
 // ticket counter (ticket t is unit n_pull + t); every unit "moves" its rows
 // (writes the call's epoch into each row word of its piece) and arrives on
 // its (channel, slab) signal; consumer tiles wait for their channels' signals
-// and check every row word they cover.  The last copy worker to leave resets
-// the ticket and exit counters.
+// and check every row word they cover.  Tiles inside the local chunk (the
+// last arrival position, moved last and slowly here) read it in place and
+// wait for its signals only after computing.  The last copy worker to leave
+// resets the ticket and exit counters.
 struct AgCall {
   AgShape a;
   int chunk_rows, ch_rows;
-  int n_copy, n_pull;
-  std::vector<int> order;  // chunk at arrival position p
+  int n_copy, n_gemm, n_pull;  // n_pull <= n_gemm GEMM workgroups pull a unit each
+  std::vector<int> order;      // chunk at arrival position p; the last is the local chunk
 };
 
 void ag_call(Signals& S, std::vector<std::atomic<uint32_t>>& rows, std::atomic<uint32_t> (&queue)[2],
@@ -226,6 +235,7 @@ void ag_call(Signals& S, std::vector<std::atomic<uint32_t>>& rows, std::atomic<u
   auto move_unit = [&](int u) {
     const Unit x = decode(a, u);
     const int chunk = c.order[x.p];
+    if (x.p == R - 1) std::this_thread::sleep_for(std::chrono::microseconds(50));
     const int rp = (c.ch_rows + x.npc - 1) / x.npc;
     const int r0 = x.ch * c.ch_rows + x.j * rp;
     const int nr = std::min(rp, (x.ch + 1) * c.ch_rows - r0);
@@ -245,8 +255,9 @@ void ag_call(Signals& S, std::vector<std::atomic<uint32_t>>& rows, std::atomic<u
   const int M = R * c.chunk_rows;
   const int BM = std::max(8, c.ch_rows / 2 + 3);  // tiles straddle channel edges
   const int n_tiles = (M + BM - 1) / BM;
-  std::atomic<int> tile_next{0};
-  run_threads(c.n_copy + c.n_pull, seed, [&](int w) {
+  std::atomic<int> tile_next{0}, gemm_done{0};
+  const int local = c.order[R - 1];
+  run_threads(c.n_copy + c.n_gemm, seed, [&](int w) {
     if (w < c.n_copy) {  // copy kernel workgroup: claim until none is left
       for (;;) {
         const int u = n_pull + (int)queue[0].fetch_add(1, std::memory_order_relaxed);
@@ -262,15 +273,34 @@ void ag_call(Signals& S, std::vector<std::atomic<uint32_t>>& rows, std::atomic<u
     if (j < n_pull) move_unit(j);
     for (int t = tile_next.fetch_add(1); t < n_tiles; t = tile_next.fetch_add(1)) {
       const int lo = t * BM, hi = std::min(M, lo + BM) - 1;
-      bool ok = true;
-      for (int s = 0; s < a.n_slab && ok; ++s)
-        for (int g = lo / c.ch_rows; g <= hi / c.ch_rows; ++g)
-          ok = ok && wait_ge(S, (size_t)g * a.n_slab + s, target(epoch, 1), bound_ms);
-      if (!ok) continue;  // timed out: the call reports an error
+      auto wait_all = [&] {
+        bool ok = true;
+        for (int s = 0; s < a.n_slab && ok; ++s)
+          for (int g = lo / c.ch_rows; g <= hi / c.ch_rows; ++g)
+            ok = ok && wait_ge(S, (size_t)g * a.n_slab + s, target(epoch, 1), bound_ms);
+        return ok;
+      };
+      if (lo / c.chunk_rows == local && hi / c.chunk_rows == local) {
+        jitter(20);  // computes from the local shard in place
+        if (MUTATION != 4) wait_all();
+        continue;
+      }
+      if (!wait_all()) continue;  // timed out: the call reports an error
       for (int r = lo; r <= hi; ++r)
         for (int s = 0; s < a.n_slab; ++s)
           CHECK(rows[(size_t)r * a.n_slab + s].load(std::memory_order_relaxed) == epoch,
                 "tile %d read row %d slab %d before its data (epoch %u)", t, r, s, epoch);
+    }
+    // The GEMM's end is where the caller's stream moves on: the gathered
+    // buffer must be whole and the counters free for the next call's pulls.
+    if (gemm_done.fetch_add(1, std::memory_order_acq_rel) == c.n_gemm - 1 && !withheld) {
+      for (size_t i = 0; i < rows.size(); ++i)
+        CHECK(rows[i].load(std::memory_order_relaxed) == epoch, "row word %zu incomplete when the GEMM ended",
+              i);
+      for (int g = 0; g < R * C; ++g)
+        for (int s = 0; s < a.n_slab; ++s)
+          CHECK(S.cnt[(size_t)g * a.n_slab + s].load(std::memory_order_relaxed) == 0,
+                "counter (%d,%d) not reset when the GEMM ended", g, s);
     }
   });
   if (!withheld) {
@@ -305,6 +335,7 @@ void scenario_ag(int iters, uint64_t seed) {
     c.chunk_rows = ch_rows * C;
     c.n_copy = 1 + (int)(rng() % 6);
     c.n_pull = (int)(rng() % 4);
+    c.n_gemm = std::max(1, c.n_pull) + (int)(rng() % 2);
     c.order.resize(R);
     for (int p = 0; p < R; ++p) c.order[p] = p;
     std::shuffle(c.order.begin(), c.order.end(), rng);  // any arrival permutation
@@ -328,6 +359,7 @@ void scenario_ag(int iters, uint64_t seed) {
     c.chunk_rows = ch_rows * C;
     c.n_copy = 3;
     c.n_pull = 2;
+    c.n_gemm = 2;
     c.order = {2, 0, 1};
     std::vector<std::atomic<uint32_t>> rows((size_t)R * c.chunk_rows * 2);
     for (auto& r : rows) r.store(0);

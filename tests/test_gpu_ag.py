@@ -21,8 +21,12 @@ def env():
     import torch
     import tile_level_communication_signaled_amd as tsg
     ctx = tsg.Context(0)
+    # a dedicated stream, as the benchmark uses: on the null stream the GEMM
+    # runs on a side stream too and every call joins
+    torch.cuda.set_stream(torch.cuda.Stream())
     yield torch, tsg, ctx
     torch.cuda.synchronize()
+    torch.cuda.set_stream(torch.cuda.default_stream())
     ctx.close()
 
 
@@ -340,6 +344,76 @@ def test_ag_comm_only_and_serial_fill_gathered_buffer(env):
     assert np.array_equal(full, inp["a"])
     full, c = case.run(mode=tsg.SERIAL, opts={"comm_tile": 64, "aux_wgs": 5})
     assert np.array_equal(full, inp["a"]) and err_ratio(c, ref, scale) <= 1.0
+
+
+def _launch(case, mode=None, opts=None):
+    """Poison the outputs and enqueue one call, with no synchronisation."""
+    torch, tsg, ctx = case.env
+    case.full.fill_(NAN_BF16)
+    case.c.fill_(NAN_BF16 if case.out_bf16 else float("nan"))
+    tsg.gemm_ag_overlap(ctx, case.loc, case.peers, case.full, case.b, case.c,
+                        tsg.BF16 if case.out_bf16 else tsg.F32, case.M, case.N, case.K, case.R, case.rank,
+                        opts=opts, mode=tsg.OVERLAP if mode is None else mode)
+
+
+def _result(case):
+    full = bf16_from_dev(case.full)
+    c = oracle.bf16_to_f64(bf16_from_dev(case.c)) if case.out_bf16 else case.c.cpu().numpy().astype(np.float64)
+    return full, c
+
+
+def test_ag_overlap_joined_through_the_gemm(env):
+    # Overlap on shared CUs: the caller's stream waits for the GEMM only, and
+    # the copy kernel's workgroups may still be leaving their work queue when
+    # the next call starts.  Calls of every other launch form follow with no
+    # synchronisation in between; each must find its queue words at zero and
+    # leave every output whole, and a stream synchronisation alone must show
+    # the whole gathered buffer (the local chunk included).
+    torch, tsg, ctx = env
+    M, N, K, R = 2048, 448, 1024, 8          # a 4 MiB copy: a copy kernel runs beside the GEMM
+    inps = [ag_inputs(M, K, N, R, seed=40 + i) for i in range(6)]
+    refs = [_ref(x) for x in inps]
+    cases = [AgCase(env, x, M, N, K, R, 0, out_bf16=True) for x in inps]
+    tcfg = CONFIGS["tiny_ag"]
+    tinp = ag_inputs(tcfg["M"], tcfg["K"], tcfg["N"], tcfg["R"], seed=46, dist="uniform")
+    tiny = AgCase(env, tinp, tcfg["M"], tcfg["N"], tcfg["K"], tcfg["R"], 0, out_bf16=False)
+    for i in range(12):                      # back to back on two buffer sets
+        _launch(cases[i % 2])
+    torch.cuda.current_stream().synchronize()
+    for j in range(2):
+        full, c = _result(cases[j])
+        assert np.array_equal(full, inps[j]["a"]) and err_ratio(c, *refs[j]) <= 1.0, j
+    _launch(cases[0])                                     # detached
+    _launch(cases[1], mode=tsg.COMM_ONLY)                 # copy on the caller's stream
+    _launch(cases[2])                                     # detached
+    _launch(cases[3], mode=tsg.SERIAL)                    # copy, then GEMM
+    _launch(cases[4], opts={"aux_cus": 16})               # CU split, joined
+    _launch(tiny)                                         # the GEMM moves the whole copy
+    _launch(cases[5])                                     # detached
+    torch.cuda.current_stream().synchronize()
+    for j in (0, 1, 2, 3, 4, 5):
+        full, c = _result(cases[j])
+        assert np.array_equal(full, inps[j]["a"]), j
+        if j != 1:
+            assert err_ratio(c, *refs[j]) <= 1.0, j
+    full, c = _result(tiny)
+    assert np.array_equal(full, tinp["a"]) and err_ratio(c, *_ref(tinp)) <= 1.0
+    assert ctx.check() == tsg.OK, ctx.last_error()
+    # the same after the copy queue has been used by all of them
+    full, c = cases[0].run()
+    assert np.array_equal(full, inps[0]["a"]) and err_ratio(c, *refs[0]) <= 1.0
+
+
+def test_ag_overlap_on_the_null_stream(env):
+    # from the null stream the GEMM runs on a side stream too, and the call
+    # joins both back
+    torch, tsg, ctx = env
+    M, N, K, R = 2048, 448, 1024, 8
+    inp = ag_inputs(M, K, N, R, seed=47)
+    with torch.cuda.stream(torch.cuda.default_stream()):
+        case = AgCase(env, inp, M, N, K, R, 3, out_bf16=False)
+        full, c = case.run()
+    assert np.array_equal(full, inp["a"]) and err_ratio(c, *_ref(inp)) <= 1.0
 
 
 def test_ag_rejects_bad_comm_tile(env):

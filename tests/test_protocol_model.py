@@ -47,7 +47,7 @@ def test_protocol_model_thread_sanitizer(tmp_path):
     assert "WARNING: ThreadSanitizer" not in r.stderr, r.stderr[-3000:]
 
 
-@pytest.mark.parametrize("mutation", [1, 2, 3])
+@pytest.mark.parametrize("mutation", [1, 2, 3, 4])
 def test_protocol_model_catches_planted_mistakes(tmp_path, mutation):
     exe = _build(tmp_path, f"model_m{mutation}", f"-DMUTATION={mutation}")
     r = _run(exe, 40, 4)

@@ -48,7 +48,9 @@ namespace {
 constexpr int kMaxMTiles = 1024;
 constexpr size_t kSigBase = size_t(1) << 18;  // AG slab signals in the context's pool
 constexpr size_t kSigCap = size_t(1) << 18;   // slots up to the next op's region
-constexpr int kQueueSlot = 40;                // copy work queue in the context's ticket words
+constexpr int kQueueSlot = 40;                // copy work queue in the context's ticket words: a
+                                              // copy the caller's stream does not wait for (on the
+                                              // side stream only) uses words 40-41, every other 42-43
 constexpr size_t kPaceSlot = 8;               // arrival-pacing start time in the context's pool
 constexpr int kMaxChannels = 64;               // channels per rank
 constexpr int64_t kPullAllBytes = 1 << 20;     // overlap: copies up to this size run inside the GEMM
@@ -97,6 +99,7 @@ struct AgGemmArgs {
   int per_xcd;            // resident tiles per XCD (0 = no XCD remap)
   int pull_wgs;           // workgroups 0 .. pull_wgs - 1 first move one copy unit each
   int pull_all;           // ... or every unit left in the queue (the whole copy; no copy kernel)
+  int wait_local_end;     // tiles inside the local chunk wait for its arrival after their stores
   CopyArgs copy;
   uint16_t mt_order[kMaxMTiles];
 };
@@ -229,6 +232,24 @@ __global__ void __launch_bounds__(Cfg::NT) ag_gemm_kernel(const AgGemmArgs args)
       const int gr = row0 + r, gc = col0 + c;
       if (gr < M && gc < N) C[(int64_t)gr * N + gc] = v;
     });
+  }
+  // When the caller's stream does not wait for the copy kernel, the GEMM's
+  // end must imply that every chunk has arrived.  The tiles that read a
+  // remote channel waited for it; the local chunk, moved last and read in
+  // place, is waited for here by the tiles inside it (one load per lane,
+  // long complete in practice), so the gathered buffer is whole when the
+  // GEMM is.
+  if (args.wait_local_end && local && threadIdx.x < 64) {
+    const int g_lo = row0 / args.ch_rows;
+    const int n = (last / args.ch_rows - g_lo + 1) * args.n_slab;
+    const uint64_t target = sig_target(args.sa.epoch, args.arrivals);
+    auto at = [&](int i) { return args.sig + (size_t)(g_lo + i / args.n_slab) * args.sig_stride + i % args.n_slab; };
+    for (int base = 0; base < n; base += 64) {
+      const int i = base + (int)__lane_id();
+      const uint64_t v = i < n ? __hip_atomic_load(at(i), __ATOMIC_RELAXED, TSG_SIG_SCOPE) : ~0ull;
+      for (uint64_t bad = __builtin_amdgcn_ballot_w64(v < target); bad; bad &= bad - 1)
+        wave_poll_ge(at(base + (int)__builtin_ctzll(bad)), target, args.sa);
+    }
   }
   if (args.tl.buf && threadIdx.x == 0)
     timeline_put(args.tl, 2, (uint32_t)(mt << 16 | nt), t0, t1 + hook.waited, wall_clock64());
@@ -568,7 +589,17 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
   }
   ca.n_units = (int)n_units;
   ca.skip_mask = o.skip_mask;
-  ca.queue = ctx->d_queue + kQueueSlot;
+  // Overlap on shared CUs: the caller's stream waits for the GEMM alone (a
+  // join would put a barrier packet between consecutive GEMMs on its queue,
+  // about 4 us per call).  The GEMM observes every arrival, the local
+  // chunk's at the end of the tiles inside it, so the gathered buffer and C
+  // are whole when the stream passes the call; the copy kernel's workgroups
+  // may then still be leaving their work queue, whose words no other launch
+  // uses than later copies on the same side stream.  With a timeline the
+  // copy's rows are written after its arrivals, so the call joins.
+  const bool detached = mode == TSG_MODE_OVERLAP && o.aux_cus < 0 && pr.main == caller && !pull_all &&
+                        !back_to_back && !o.copy_engine && !o.timeline && o.skip_mask == 0;
+  ca.queue = ctx->d_queue + kQueueSlot + (detached ? 0 : 2);
   ca.pace_word = ctx->d_sig + kPaceSlot;
   // pacing: ticks (100 MHz wall clock) per unit at the requested rate
   ca.pace_ticks = o.arrival_gbps > 0
@@ -596,6 +627,7 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
   ca.n_workers = (uint32_t)(pull_all ? pull : copy_grid);
   ga.pull_wgs = 0;
   ga.pull_all = pull_all ? 1 : 0;
+  ga.wait_local_end = detached ? 1 : 0;
   ga.copy = ca;
 
   auto gemm = [&](hipStream_t s, int wait, int cus) -> tsg_status {
@@ -743,6 +775,7 @@ tsg_status tsg_op_ag(tsg_ctx* ctx, const void* a_local, const void* a_peers, voi
     // copy's workgroups join it on the same CUs.
     st = gemm(pr.main, 1, pr.main_cus);
     if (st == TSG_OK) st = copy(pr.aux);
+    if (detached) return st;
   } else {
     st = copy(pr.aux);
     if (st == TSG_OK && mode == TSG_MODE_OVERLAP) st = gemm(pr.main, 1, pr.main_cus);

@@ -130,6 +130,9 @@ __device__ __forceinline__ void sig_arrive_counted_coherent(uint32_t* cnt, uint6
   const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, TSG_SIG_SCOPE);
   if (old == n - 1) {
     __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, TSG_SIG_SCOPE);
+    // the reset is acknowledged before the signal: whoever has seen the
+    // signal (and a launch ordered after it) finds the counter at zero
+    __builtin_amdgcn_s_waitcnt(0);
     __hip_atomic_store(s, sig_target(epoch, n), __ATOMIC_RELAXED, TSG_SIG_SCOPE);
   }
 }
