@@ -80,7 +80,7 @@ def _parse():
 
 # Sources the AllGather + GEMM kernels are compiled from: a traffic record
 # measured on other code does not apply.
-AG_SOURCES = ("ag.hip", "tsg_gemm.hpp", "tsg_device.hpp")
+AG_SOURCES = ("ag.hip", "tsg_gemm.hpp", "tsg_device.hpp", "tsg_copy.hpp")
 
 
 def source_hash() -> str:

@@ -177,6 +177,27 @@ def test_moe_small(env, T, H, I, E):
     assert r <= 1.0, r
 
 
+def test_moe_back_to_back_calls_alternating_routings(env):
+    # Calls back to back without a synchronisation, alternating two routings
+    # (the larger with 256 blocks of pairs) on one context: each must leave
+    # its own tables, h and out, whatever the previous call left in the
+    # context's signals and queue.
+    torch, tsg, ctx = env
+    cases = [MoeCase(env, moe_inputs(T, 64, 64, E, k=2, seed=50 + T)) for T, E in ((32767, 8), (700, 16))]
+    for c in cases:
+        c.out.fill_(float("nan"))
+        c.ws.fill_(0xFF)
+    for i in range(8):
+        c = cases[i % 2]
+        tsg.moe_expert_combine(ctx, c.x, c.ids, c.g, c.wu, c.wd, c.out, c.counts, c.sorted, c.ws, c.wsb,
+                               c.T, c.H, c.I, c.E, c.k, mode=tsg.OVERLAP)
+    assert ctx.check() == tsg.OK, ctx.last_error()
+    for c in cases:
+        out = c.out.cpu().numpy().astype(np.float64)
+        r, _, _ = _check(c, out, c.counts.cpu().numpy(), c.sorted.cpu().numpy())
+        assert r <= 1.0, r
+
+
 def test_moe_skewed_routing_single_expert_heavy(env):
     T, H, I, E = 512, 256, 128, 8
     inp = moe_inputs(T, H, I, E, k=2, seed=31)
