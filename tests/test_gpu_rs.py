@@ -18,8 +18,12 @@ def env():
     import torch
     import tile_level_communication_signaled_amd as tsg
     ctx = tsg.Context(0)
+    # a dedicated stream, as the benchmark uses (the null stream is covered
+    # by its own test)
+    torch.cuda.set_stream(torch.cuda.Stream())
     yield torch, tsg, ctx
     torch.cuda.synchronize()
+    torch.cuda.set_stream(torch.cuda.default_stream())
     ctx.close()
 
 
@@ -138,6 +142,17 @@ def test_rs_full_size_parity_and_modes(env):
     assert err_ratio(gP6, P, sP) <= 1.0 and err_ratio(gout6, out, s_out) <= 1.0
     gP7, gout7 = case.run(mode=tsg.SERIAL, opts={"tile": 6})
     assert np.array_equal(gP7, gP6) and np.array_equal(gout7, gout6)
+
+
+def test_rs_overlap_on_the_null_stream(env):
+    torch, tsg, ctx = env
+    M, N, K, R = 1024, 512, 256, 4
+    inp = rs_inputs(M, K, N, R, rank=1, seed=66)
+    P, out, sP, s_out = _ref(inp, R, 1)
+    with torch.cuda.stream(torch.cuda.default_stream()):
+        case = RsCase(env, inp, M, N, K, R, 1)
+        gP, gout = case.run()
+    assert err_ratio(gP, P, sP) <= 1.0 and err_ratio(gout, out, s_out) <= 1.0
 
 
 def test_rs_tile6_needs_k_multiple_of_128(env):
