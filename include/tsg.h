@@ -25,8 +25,9 @@
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Calls are asynchronous and stream-ordered: work forks from `stream` to
  *     the context's side streams and joins back before the call returns, so
- *     later work on `stream` sees every output (gemm_ag_overlap in overlap
- *     mode on shared CUs joins through its GEMM instead: see there).
+ *     later work on `stream` sees every output (gemm_ag_overlap and
+ *     gemm_rs_overlap in overlap mode on shared CUs join through their GEMM
+ *     instead: see there).
  *   - Return value: TSG_OK or a negative tsg_status.  Argument errors are
  *     detected before anything is enqueued; the message is available from
  *     tsg_last_error().  Device-side errors (a signal wait that exceeded its
@@ -282,9 +283,10 @@ tsg_status tsg_timeline(tsg_ctx* ctx, uint64_t* out, size_t cap, size_t* n);
  * N % 8 == 0, K % 8 == 0, N, K >= 8 (else TSG_E_SHAPE).
  * COMPUTE_ONLY expects a_full to hold the gathered peer chunks already.
  *
- * Overlap on shared CUs (opts.aux_cus < 0, no timeline, no debug skip mask),
- * with a copy kernel beside the GEMM: `stream` waits for the GEMM only, not
- * for the copy kernel on the side stream.  The GEMM ends only after it has
+ * Overlap on shared CUs (opts.aux_cus < 0, no timeline, no debug skip mask)
+ * from a non-null `stream`, with a copy kernel beside the GEMM: `stream`
+ * waits for the GEMM only, not for the copy kernel on the side stream.  The
+ * GEMM ends only after it has
  * observed every chunk's arrival (tiles inside the local chunk wait for it
  * after their stores), so a_full and c are complete, and a_local and a_peers
  * no longer read, when `stream` passes the call; the copy kernel's
@@ -321,7 +323,15 @@ tsg_status gemm_ag_overlap(tsg_ctx* ctx, const void* a_local, const void* a_peer
  *                                               rank order skipping `rank`
  *   out            f32  [M/R x N]               (output)
  * Constraints: 1 <= R <= 32, 0 <= rank < R, M % R == 0, N % 8 == 0,
- * K % 8 == 0, N, K >= 8.  COMM_ONLY expects `partial` to be computed already. */
+ * K % 8 == 0, N, K >= 8.  COMM_ONLY expects `partial` to be computed already.
+ *
+ * Overlap on shared CUs (opts.aux_cus < 0, no timeline, no debug skip mask)
+ * from a non-null `stream`, with the reduce beside the GEMM: `stream` waits
+ * for the GEMM only.  The reduce stores out coherently and signals its end,
+ * and the GEMM's last workgroup waits for that signal, so `partial` and `out`
+ * are complete, and `peer_partials` no longer read, when `stream` passes the
+ * call.  After a device-side error the reduce may still run: tsg_check()
+ * waits for the side streams before it reports. */
 tsg_status gemm_rs_overlap(tsg_ctx* ctx, const void* x, const void* w, float* partial,
                            const float* peer_partials, float* out,
                            int M, int N, int K, int R, int rank,

@@ -144,6 +144,51 @@ def test_rs_full_size_parity_and_modes(env):
     assert np.array_equal(gP7, gP6) and np.array_equal(gout7, gout6)
 
 
+def _launch(case, mode=None, opts=None):
+    """Poison the outputs and enqueue one call, with no synchronisation."""
+    torch, tsg, ctx = case.env
+    mode = tsg.OVERLAP if mode is None else mode
+    case.out.fill_(float("nan"))
+    if mode != tsg.COMM_ONLY:
+        case.partial.fill_(float("nan"))
+    tsg.gemm_rs_overlap(ctx, case.x, case.w, case.partial, case.peers, case.out, case.M, case.N, case.K,
+                        case.R, case.rank, opts=opts, mode=mode)
+
+
+def test_rs_overlap_joined_through_the_gemm(env):
+    # Overlap on shared CUs: the caller's stream waits for the GEMM only,
+    # whose last workgroup waits for the reduce's end signal; the reduce
+    # stores its final out coherently.  Calls of every launch form follow
+    # with no synchronisation in between, and a stream synchronisation alone
+    # must show every output whole.
+    torch, tsg, ctx = env
+    M, N, K, R = 2048, 1024, 512, 8
+    inps = [rs_inputs(M, K, N, R, rank=r, seed=60 + r) for r in range(6)]
+    refs = [_ref(x, R, r) for r, x in enumerate(inps)]
+    cases = [RsCase(env, x, M, N, K, R, r) for r, x in enumerate(inps)]
+
+    def check(j):
+        P, out, sP, s_out = refs[j]
+        gP = cases[j].partial.cpu().numpy().astype(np.float64)
+        gout = cases[j].out.cpu().numpy().astype(np.float64)
+        assert err_ratio(gP, P, sP) <= 1.0 and err_ratio(gout, out, s_out) <= 1.0, j
+    for i in range(12):                      # back to back on two buffer sets
+        _launch(cases[i % 2])
+    torch.cuda.current_stream().synchronize()
+    check(0)
+    check(1)
+    _launch(cases[0])                                    # detached
+    _launch(cases[1], mode=tsg.SERIAL)                   # GEMM, then the reduce
+    _launch(cases[2])                                    # detached
+    _launch(cases[3], opts={"aux_cus": 16})              # CU split, joined
+    _launch(cases[4], opts={"tile": 6})                  # back to back (no room beside tile 6)
+    _launch(cases[5])                                    # detached
+    torch.cuda.current_stream().synchronize()
+    for j in range(6):
+        check(j)
+    assert ctx.check() == tsg.OK, ctx.last_error()
+
+
 def test_rs_overlap_on_the_null_stream(env):
     torch, tsg, ctx = env
     M, N, K, R = 1024, 512, 256, 4

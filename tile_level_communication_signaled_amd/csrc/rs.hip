@@ -28,6 +28,7 @@ constexpr int kMaxRanks = 32;
 constexpr int kMaxMTiles = 1024;
 constexpr size_t kSigBase = 4096;      // RS signals start here in the context's pool
 constexpr int kFlagTile = 128;         // signal granularity (rows and columns)
+constexpr size_t kDoneSlot = 24;       // the reduce's completion signal in the context's pool
 
 struct RsGemmArgs {
   const uint16_t* x;
@@ -43,6 +44,8 @@ struct RsGemmArgs {
   int per_xcd;
   int chunk_rows;
   uint32_t skip_mask;    // chunks whose signals are not published (test hook)
+  const uint64_t* reduce_done;  // non-null: the last workgroup waits for the reduce's end
+  uint32_t reduce_n;            // ... signalled as {epoch | reduce_n}
   uint16_t mt_order[kMaxMTiles];
 };
 
@@ -81,6 +84,11 @@ __global__ void __launch_bounds__(Cfg::NT) rs_gemm_kernel(const RsGemmArgs args)
     }
     if (args.tl.buf) timeline_put(args.tl, 3, (uint32_t)(mt << 16 | nt), t0, t0, wall_clock64());
   }
+  // When the caller's stream does not wait for the reduce kernel, the
+  // GEMM's end must imply the reduce's: the workgroup dispatched last waits
+  // for the reduce's completion signal.
+  if (args.reduce_done && blockIdx.x == gridDim.x - 1 && threadIdx.x < 64)
+    wave_poll_ge(args.reduce_done, sig_target(args.sa.epoch, args.reduce_n), args.sa);
 }
 
 struct RsReduceArgs {
@@ -95,7 +103,29 @@ struct RsReduceArgs {
   int n_ftn;
   int ftm0, n_ftm;       // signal rows covering the local chunk
   int wait;
+  uint64_t* done_sig;    // DETACHED: every workgroup arrives here at its end
+  uint32_t* done_cnt;
 };
+
+// Coherent store of one row segment of 128 floats held as a float4 per lane
+// by each 32-lane half of the wave, in 8-byte stores laid out so that every
+// store instruction writes whole 128-byte lines: store i of lane l (l within
+// its half) writes floats 64 i + 2 l and 64 i + 2 l + 1, which lane
+// 16 i + l / 2 of the half holds.  A lane writes only a valid lane's floats.
+// Every lane of the wave executes it.
+__device__ __forceinline__ void store_segment_coherent(float* seg, float4 v, bool ok) {
+  const int lane = __lane_id(), l = lane & 31, half = lane & 32;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int src = half | (16 * i + (l >> 1));
+    const float x = __shfl(v.x, src), y = __shfl(v.y, src), z = __shfl(v.z, src), w = __shfl(v.w, src);
+    const int src_ok = __shfl((int)ok, src);
+    const float lo = (l & 1) ? z : x, hi = (l & 1) ? w : y;
+    if (src_ok)
+      store_coherent((uint64_t*)(seg + 64 * i + 2 * l),
+                     (uint64_t)__float_as_uint(lo) | ((uint64_t)__float_as_uint(hi) << 32));
+  }
+}
 
 // Work unit: 16 rows x 128 columns of one 128 x 128 signal tile of the
 // local chunk; thread (ry, cx) owns rows ry and ry + 8 at float4 column cx.
@@ -125,8 +155,13 @@ __device__ __forceinline__ float4 nt_load4(const float* p) {
 // when the reduce runs on CUs of its own or after the GEMM (seven peers in
 // one batch: one memory round trip per unit).  The summation order is the
 // same for both.
-template <int P_MAX, bool ONE_PASS>
+// DETACHED (two phases): phase 2 stores out coherently, and every workgroup
+// arrives on done_sig at its end, for a GEMM that waits for the reduce.
+// Phase 2 then rewrites every line phase 1 left in this XCD's L2, so a later
+// write-back of those lines carries the same values.
+template <int P_MAX, bool ONE_PASS, bool DETACHED = false>
 __global__ void __launch_bounds__(256) rs_reduce_kernel(const RsReduceArgs a) {
+  static_assert(!DETACHED || !ONE_PASS, "a detached reduce runs in two phases");
   const int n_units = a.n_ftm * a.n_ftn * 8;
   const int c0 = a.rank * a.chunk_rows, c1 = c0 + a.chunk_rows;
   const int cx = threadIdx.x & 31;
@@ -227,10 +262,22 @@ __global__ void __launch_bounds__(256) rs_reduce_kernel(const RsReduceArgs a) {
     float* d1 = a.out + (int64_t)(r1 - c0) * a.N + col;
     if (ok0) { q0 = load_coherent((const float4*)(a.partial + (int64_t)r0 * a.N + col)); o0 = *(const float4*)d0; }
     if (ok1) { q1 = load_coherent((const float4*)(a.partial + (int64_t)r1 * a.N + col)); o1 = *(const float4*)d1; }
-    if (ok0) *(float4*)d0 = make_float4(o0.x + q0.x, o0.y + q0.y, o0.z + q0.z, o0.w + q0.w);
-    if (ok1) *(float4*)d1 = make_float4(o1.x + q1.x, o1.y + q1.y, o1.z + q1.z, o1.w + q1.w);
+    if constexpr (DETACHED) {
+      const int seg = ftn * kFlagTile;  // first column of the half-wave's 128
+      store_segment_coherent(a.out + (int64_t)(r0 - c0) * a.N + seg,
+                             make_float4(o0.x + q0.x, o0.y + q0.y, o0.z + q0.z, o0.w + q0.w), ok0);
+      store_segment_coherent(a.out + (int64_t)(r1 - c0) * a.N + seg,
+                             make_float4(o1.x + q1.x, o1.y + q1.y, o1.z + q1.z, o1.w + q1.w), ok1);
+    } else {
+      if (ok0) *(float4*)d0 = make_float4(o0.x + q0.x, o0.y + q0.y, o0.z + q0.z, o0.w + q0.w);
+      if (ok1) *(float4*)d1 = make_float4(o1.x + q1.x, o1.y + q1.y, o1.z + q1.z, o1.w + q1.w);
+    }
     if (a.tl.buf && threadIdx.x == 0 && (u & 7) == 0)
       timeline_put(a.tl, 4, (uint32_t)(ftm << 16 | ftn), t0, t1, wall_clock64());
+  }
+  if constexpr (DETACHED) {
+    block_coherent_complete();
+    if (threadIdx.x == 0) sig_arrive_counted_coherent(a.done_cnt, a.done_sig, gridDim.x, a.sa.epoch);
   }
 }
 
@@ -348,6 +395,8 @@ tsg_status tsg_op_rs(tsg_ctx* ctx, const void* x, const void* w, float* partial,
   ga.n_ftn = n_ftn;
   ga.chunk_rows = chunk_rows;
   ga.skip_mask = o.skip_mask;
+  ga.reduce_done = nullptr;
+  ga.reduce_n = 0;
   // M-tile order: by the position of the tile's first chunk in the order
   // local, rank+1, rank+2, ... (order 0) or rank+1, ..., local last (order 1).
   {
@@ -377,6 +426,8 @@ tsg_status tsg_op_rs(tsg_ctx* ctx, const void* x, const void* w, float* partial,
   ra.n_ftn = n_ftn;
   ra.ftm0 = (rank * chunk_rows) / kFlagTile;
   ra.n_ftm = ((rank + 1) * chunk_rows - 1) / kFlagTile - ra.ftm0 + 1;
+  ra.done_sig = ctx->d_sig + kDoneSlot;
+  ra.done_cnt = ctx->d_cnt + kDoneSlot;
   const int n_red_tiles = ra.n_ftm * n_ftn;
   if (o.timeline) TSG_HIP(ctx, hipMemsetAsync(ctx->d_timeline_n, 0, sizeof(uint32_t), caller));
 
@@ -389,11 +440,14 @@ tsg_status tsg_op_rs(tsg_ctx* ctx, const void* x, const void* w, float* partial,
     return TSG_OK;
   };
   // beside: the GEMM runs at the same time (on the same or other CUs)
-  auto reduce = [&](hipStream_t s, int nwg, int wait, bool beside) -> tsg_status {
+  auto red_grid = [&](int nwg) { return std::max(1, std::min(nwg, 8 * n_red_tiles)); };
+  auto reduce = [&](hipStream_t s, int nwg, int wait, bool beside, bool detached = false) -> tsg_status {
     ra.wait = wait;
-    const dim3 grid(std::max(1, std::min(nwg, 8 * n_red_tiles)));
+    const dim3 grid(red_grid(nwg));
     time_begin(ctx, 1, s);
-    if (beside && o.aux_cus < 0)  // sharing every CU with the GEMM: fewer registers
+    if (detached)
+      hipLaunchKernelGGL((rs_reduce_kernel<4, false, true>), grid, dim3(256), 0, s, ra);
+    else if (beside && o.aux_cus < 0)  // sharing every CU with the GEMM: fewer registers
       hipLaunchKernelGGL((rs_reduce_kernel<4, false>), grid, dim3(256), 0, s, ra);
     else if (beside)
       hipLaunchKernelGGL((rs_reduce_kernel<8, false>), grid, dim3(256), 0, s, ra);
@@ -408,6 +462,15 @@ tsg_status tsg_op_rs(tsg_ctx* ctx, const void* x, const void* w, float* partial,
   // In shared mode the GEMM runs on the caller's stream and the reduce on a
   // side stream, one workgroup per CU beside the GEMM's; when the two cannot
   // share a CU they run back to back instead.
+  // Overlap on shared CUs from a stream of the caller's own: the caller's
+  // stream waits for the GEMM alone (a join would put a barrier packet
+  // between consecutive GEMMs on its queue).  The reduce stores its final
+  // out coherently and signals its end, and the GEMM's last workgroup waits
+  // for that signal, so out and the partial are whole when the stream passes
+  // the call.  With a timeline (written after the reduce's stores) or a
+  // debug skip mask the call joins.
+  bool detached = mode == TSG_MODE_OVERLAP && o.aux_cus < 0 && caller != nullptr && !o.timeline &&
+                  o.skip_mask == 0;
   bool back_to_back = mode == TSG_MODE_SERIAL;
   if (mode == TSG_MODE_OVERLAP && o.aux_cus < 0) {
     // (a reduce workgroup placed where the GEMM's next tile cannot then fit
@@ -415,7 +478,10 @@ tsg_status tsg_op_rs(tsg_ctx* ctx, const void* x, const void* w, float* partial,
     const bool direct = K % 128 == 0;
     int gemm_nt = 0;
     const void* fn = gemm_fn(tile, direct, &gemm_nt);
-    back_to_back = !co_resident(ctx, fn, gemm_nt, (const void*)&rs_reduce_kernel<4, false>, 256);
+    const void* red = detached ? (const void*)&rs_reduce_kernel<4, false, true>
+                               : (const void*)&rs_reduce_kernel<4, false>;
+    back_to_back = !co_resident(ctx, fn, gemm_nt, red, 256);
+    detached = detached && !back_to_back;
   }
   if (back_to_back) {
     st = gemm(caller, ctx->n_cus);
@@ -432,9 +498,15 @@ tsg_status tsg_op_rs(tsg_ctx* ctx, const void* x, const void* w, float* partial,
   const int nwg = o.aux_wgs > 0 ? o.aux_wgs : (o.aux_cus < 0 ? 2 * ctx->n_cus : pr.aux_cus * 2);
   st = fork(ctx, caller, pr);
   if (st != TSG_OK) return st;
-  // Producer (GEMM) first, consumer (reduce) second: the GEMM never waits.
+  if (detached) {
+    ga.reduce_done = ra.done_sig;
+    ga.reduce_n = (uint32_t)red_grid(nwg);
+  }
+  // Producer (GEMM) first, consumer (reduce) second: the GEMM waits for the
+  // reduce only in its last workgroup, at its end.
   if (mode == TSG_MODE_OVERLAP) st = gemm(pr.main, pr.main_cus);
-  if (st == TSG_OK) st = reduce(pr.aux, nwg, mode == TSG_MODE_OVERLAP ? 1 : 0, mode == TSG_MODE_OVERLAP);
+  if (st == TSG_OK) st = reduce(pr.aux, nwg, mode == TSG_MODE_OVERLAP ? 1 : 0, mode == TSG_MODE_OVERLAP, detached);
+  if (detached) return st;
   tsg_status sj = join(ctx, caller, pr);
   return st != TSG_OK ? st : sj;
 }
