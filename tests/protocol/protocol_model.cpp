@@ -30,7 +30,10 @@
 //     stream does not wait for the copy kernel), every row of every chunk,
 //     the local chunk's included, holds the call's data and every arrival
 //     counter is back at zero, while copy workgroups may still be leaving
-//     their queue.
+//     their queue;
+//   * when the last GEMM workgroup of a GEMM + ReduceScatter call ends (the
+//     caller's stream does not wait for the reduce kernel), every output
+//     word holds its final value (the peers' sum plus the local partial).
 // Usage: protocol_model [iterations] [seed]; prints one "ok <scenario>" line
 // per scenario and exits 0, or prints "FAIL ..." and exits 1.
 // Built with -DMUTATION=m (m > 0) the model plants one mistake in its own
@@ -39,7 +42,9 @@
 //   2: a counted signal is published by its first arriver;
 //   3: the last claimer to leave does not reset the ticket counter;
 //   4: AllGather tiles inside the local chunk do not wait for its arrival at
-//      their end.
+//      their end;
+//   5: the last GEMM + ReduceScatter GEMM workgroup does not wait for the
+//      reduce's end signal.
 #ifndef MUTATION
 #define MUTATION 0
 #endif
@@ -552,6 +557,57 @@ void scenario_epochs(uint64_t seed) {
 
 }  // namespace
 
+// ------------------------------------------------- GEMM + ReduceScatter
+// One call: GEMM workers take tiles from a counter, write the tile's partial
+// words (the call's epoch) and publish its flag; the worker dispatched last
+// then waits for the reduce's end signal.  Reduce workers own output words:
+// phase 1 writes the peers' sum (2 e), phase 2 waits for the word's tile
+// flag, reads the partial and writes 2 e + 1; then each arrives on the end
+// signal (slowly, so that a GEMM that did not wait would end first).  When
+// the last GEMM worker ends, every output word must be final.
+void scenario_rs(int iters, uint64_t seed) {
+  std::mt19937_64 rng(seed);
+  uint32_t epoch = 1000;
+  for (int it = 0; it < iters; ++it) {
+    const int n_tiles = 1 + (int)(rng() % 12), per_tile = 1 + (int)(rng() % 4);
+    const int n_gemm = 1 + (int)(rng() % 4), n_red = 1 + (int)(rng() % 4);
+    Signals S((size_t)n_tiles + 1);  // tile flags, then the reduce's end signal
+    const size_t done = (size_t)n_tiles;
+    std::vector<std::atomic<uint32_t>> partial((size_t)n_tiles * per_tile), out((size_t)n_tiles * per_tile);
+    for (auto& x : partial) x.store(0);
+    for (auto& x : out) x.store(0);
+    ++epoch;
+    std::atomic<int> tile_next{0}, gemm_left{n_gemm};
+    run_threads(n_gemm + n_red, seed + (uint64_t)it, [&](int w) {
+      if (w < n_gemm) {
+        for (int t = tile_next.fetch_add(1); t < n_tiles; t = tile_next.fetch_add(1)) {
+          jitter(20);
+          for (int i = 0; i < per_tile; ++i) partial[(size_t)t * per_tile + i].store(epoch, std::memory_order_relaxed);
+          S.sig[t].store(target(epoch, 1), std::memory_order_release);
+        }
+        if (w == n_gemm - 1 && MUTATION != 5) wait_ge(S, done, target(epoch, (uint32_t)n_red), 5000);
+        if (gemm_left.fetch_sub(1, std::memory_order_acq_rel) == 1)
+          for (size_t i = 0; i < out.size(); ++i)
+            CHECK(out[i].load(std::memory_order_relaxed) == 2 * epoch + 1,
+                  "output word %zu not final when the GEMM ended (epoch %u)", i, epoch);
+        return;
+      }
+      const int r = w - n_gemm;
+      for (size_t i = (size_t)r; i < out.size(); i += (size_t)n_red) out[i].store(2 * epoch, std::memory_order_relaxed);
+      for (size_t i = (size_t)r; i < out.size(); i += (size_t)n_red) {
+        if (!wait_ge(S, i / (size_t)per_tile, target(epoch, 1), 5000)) continue;
+        CHECK(partial[i].load(std::memory_order_relaxed) == epoch, "partial word %zu read before its flag", i);
+        out[i].store(out[i].load(std::memory_order_relaxed) + 1, std::memory_order_relaxed);
+      }
+      std::this_thread::sleep_for(std::chrono::microseconds(200));
+      arrive_counted(S, done, (uint32_t)n_red, epoch);
+    });
+    CHECK(S.status.load() == 0, "rs call timed out");
+    CHECK(S.cnt[done].load() == 0, "end-signal counter left at %u", S.cnt[done].load());
+  }
+  std::printf("ok rs_end_signal_joins_through_the_gemm (%d calls)\n", iters);
+}
+
 int main(int argc, char** argv) {
   const int iters = argc > 1 ? std::atoi(argv[1]) : 200;
   const uint64_t seed = argc > 2 ? std::strtoull(argv[2], nullptr, 10) : 12345;
@@ -560,6 +616,7 @@ int main(int argc, char** argv) {
   scenario_ag(iters, seed);
   scenario_xcd_queues(iters, seed + 1);
   scenario_moe(iters, seed + 2);
+  scenario_rs(iters / 2, seed + 3);
   if (g_fail) {
     std::printf("FAIL: %d checks failed\n", g_fail);
     return 1;

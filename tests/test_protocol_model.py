@@ -33,7 +33,7 @@ def test_protocol_model(tmp_path):
         assert r.returncode == 0, r.stdout[-2000:]
         for name in ("unit_decode", "epoch_tagging", "ag_queue_counted_arrival_epochs",
                      "ag_withheld_signal_timeout_and_recovery", "xcd_phased_queues_mlp_dependencies",
-                     "moe_queue_reset_and_failed_launch"):
+                     "moe_queue_reset_and_failed_launch", "rs_end_signal_joins_through_the_gemm"):
             assert f"ok {name}" in r.stdout, (name, r.stdout[-2000:])
 
 
@@ -47,7 +47,7 @@ def test_protocol_model_thread_sanitizer(tmp_path):
     assert "WARNING: ThreadSanitizer" not in r.stderr, r.stderr[-3000:]
 
 
-@pytest.mark.parametrize("mutation", [1, 2, 3, 4])
+@pytest.mark.parametrize("mutation", [1, 2, 3, 4, 5])
 def test_protocol_model_catches_planted_mistakes(tmp_path, mutation):
     exe = _build(tmp_path, f"model_m{mutation}", f"-DMUTATION={mutation}")
     r = _run(exe, 40, 4)
