@@ -141,11 +141,12 @@ typedef struct tsg_opts {
    * power of two (one signal per chunk when K <= 2048). */
   int comm_tile;
   /* AG+GEMM, shared CUs: copy units (pieces of the first column slabs, in
-   * the copy's order) that the GEMM's first workgroups take from the copy's
-   * work queue and move themselves at their start, before their first wait:
-   * the consumer pulls the head of the data ([TL] Table 3, tile_pull_data),
-   * so compute need not wait for the copy kernel to be scheduled.  Units not
-   * taken by the GEMM are moved by the copy kernel from the same queue.
+   * the copy's order) that the GEMM's workgroups move themselves at their
+   * start, before their first wait: workgroup b moves unit b, for b below
+   * min(pull_units, GEMM grid, units).  The consumer pulls the head of the
+   * data ([TL] Table 3, tile_pull_data), so compute need not wait for the
+   * copy kernel to be scheduled; the copy kernel's queue hands out the units
+   * after them.
    * 0 = the op's default (one unit per CU, at most the first slab's units;
    * when the whole copy is at most 1 MiB, every unit: each GEMM workgroup
    * takes units until none is left, and no copy kernel or second stream is
