@@ -25,9 +25,9 @@
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Calls are asynchronous and stream-ordered: work forks from `stream` to
  *     the context's side streams and joins back before the call returns, so
- *     later work on `stream` sees every output (gemm_ag_overlap and
- *     gemm_rs_overlap in overlap mode on shared CUs join through their GEMM
- *     instead: see there).
+ *     later work on `stream` sees every output (gemm_ag_overlap,
+ *     gemm_rs_overlap and ag_kv_attention in overlap mode on shared CUs join
+ *     through their compute kernel instead: see there).
  *   - Return value: TSG_OK or a negative tsg_status.  Argument errors are
  *     detected before anything is enqueued; the message is available from
  *     tsg_last_error().  Device-side errors (a signal wait that exceeded its
@@ -512,7 +512,14 @@ tsg_status moe_ag_group_gemm(tsg_ctx* ctx, const void* x_local, const void* x_pe
  * > 0: TSG_E_UNSUPPORTED).  debug_skip_mask bit c withholds chunk c's
  * signals.  Constraints: head_dim == 128 (else TSG_E_UNSUPPORTED),
  * 1 <= R <= 32, S a positive multiple of 64 R, heads >= 1, comm_tile a power
- * of two in [64, 2048] or 0, 16-byte aligned pointers. */
+ * of two in [64, 2048] or 0, 16-byte aligned pointers.
+ *
+ * With the copy kernel beside the tiles, from a non-null `stream` and with no
+ * timeline or debug skip mask, `stream` waits for the attention kernel only:
+ * its tiles wait for their head's own-chunk slabs after their stores, so
+ * k_full, v_full and out are complete, and the local and peer chunks no
+ * longer read, when `stream` passes the call; the copy kernel's workgroups
+ * may still be leaving its work queue (context-internal words). */
 tsg_status ag_kv_attention(tsg_ctx* ctx, const void* q, const void* k_local, const void* k_peers,
                            const void* v_local, const void* v_peers, void* k_full, void* v_full,
                            void* out, int S, int heads, int head_dim, int R, int rank,

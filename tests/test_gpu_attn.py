@@ -36,8 +36,12 @@ def env():
     import torch
     import tile_level_communication_signaled_amd as tsg
     ctx = tsg.Context(0)
+    # a dedicated stream, as the benchmark uses (the null stream, on which
+    # every call joins, is covered by its own test)
+    torch.cuda.set_stream(torch.cuda.Stream())
     yield torch, tsg, ctx
     torch.cuda.synchronize()
+    torch.cuda.set_stream(torch.cuda.default_stream())
     ctx.close()
 
 
@@ -141,6 +145,48 @@ def test_attention_modes_orders_slabs(env):
     st = tsg.ag_kv_attention(ctx, case.q, case.kl, case.kp, case.vl, case.vp, case.kf, case.vf, case.out, 1000,
                              heads, D, R, rank, raise_on_error=False)
     assert st == tsg.E_SHAPE
+
+
+def test_attention_joined_through_the_attention_kernel(env):
+    # Overlapped with a copy kernel beside it, the caller's stream waits for
+    # the attention kernel only; its tiles wait for their head's own-chunk
+    # slabs after their stores.  Calls back to back with no synchronisation,
+    # alternating two cases, then the other launch forms, must leave every
+    # output whole when the stream alone is synchronised.
+    torch, tsg, ctx = env
+    S, heads, R = 1024, 4, 4
+    inps = [_inputs(S, heads, seed=90 + i) for i in range(4)]
+    cases = [Case(env, x, S, heads, R, i % R) for i, x in enumerate(inps)]
+
+    def launch(c, mode=None, opts=None):
+        c.kf.fill_(NAN_BF16)
+        c.vf.fill_(NAN_BF16)
+        c.out.fill_(-1)
+        tsg.ag_kv_attention(ctx, c.q, c.kl, c.kp, c.vl, c.vp, c.kf, c.vf, c.out, S, heads, D, R, c.rank,
+                            opts=opts, mode=tsg.OVERLAP if mode is None else mode)
+    for i in range(8):
+        launch(cases[i % 2])
+    torch.cuda.current_stream().synchronize()
+    for c in cases[:2]:
+        _check(c, bf16_from_dev(c.kf), bf16_from_dev(c.vf), bf16_from_dev(c.out))
+    launch(cases[0])                           # detached
+    launch(cases[1], mode=tsg.SERIAL)          # copy units, then tiles, one kernel
+    launch(cases[2], opts={"pull_units": 1})   # copy units in the attention kernel's own queue
+    launch(cases[3])                           # detached
+    torch.cuda.current_stream().synchronize()
+    for c in cases:
+        _check(c, bf16_from_dev(c.kf), bf16_from_dev(c.vf), bf16_from_dev(c.out))
+    assert ctx.check() == tsg.OK, ctx.last_error()
+
+
+def test_attention_on_the_null_stream(env):
+    torch, tsg, ctx = env
+    S, heads, R = 512, 2, 4
+    inp = _inputs(S, heads, seed=95)
+    with torch.cuda.stream(torch.cuda.default_stream()):
+        case = Case(env, inp, S, heads, R, 2)
+        kf, vf, out = case.run()
+    _check(case, kf, vf, out)
 
 
 def test_attention_special_cases(env):

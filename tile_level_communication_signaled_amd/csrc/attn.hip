@@ -50,7 +50,7 @@ constexpr int NT = 256;
 constexpr size_t kSigBase = (size_t(1) << 17) + 65536;  // K then V slab signals in the context's pool
 constexpr size_t kSigCap = 65536;
 constexpr int kQueueSlot = 64;       // attention kernel: 2 phases x 8 XCD tickets, exit counter
-constexpr int kCopyQueueSlot = 54;   // copy kernel: ticket, exit counter
+constexpr int kCopyQueueSlot = 54;   // copy kernel: ticket, exit counter (56-57: a copy the call joins)
 
 // V blocks are staged like a B stage of the GEMM engine (64 key rows of 128
 // head-dimension columns, row-major, 16-byte chunks permuted per row by
@@ -85,6 +85,7 @@ struct AttnArgs {
   int8_t order[kMaxRanks];  // chunk at arrival position p (p = 0: own chunk)
   int n_slab, slab_log2;
   int wait;
+  int wait_own_end;       // after its stores a tile waits for its own chunk's K and V slabs
   int l1_only;
   float scale_log2;       // log2(e) / sqrt(D)
 };
@@ -330,6 +331,17 @@ __device__ __forceinline__ uint64_t attn_tile(const AttnArgs& a, int h, int qb, 
         *(uint64_t*)(orow + 32 * j + 8 * g) = w;
       }
   }
+  // When the caller's stream does not wait for the copy kernel, the
+  // attention kernel's end must imply the whole gather: a tile waited for
+  // every peer chunk of its head, and the own chunk, moved last and read in
+  // place, is waited for here (long complete in practice).
+  if (a.wait_own_end) {
+    const uint64_t target = sig_target(a.sa.epoch, 1);
+    for (int s = s_lo; s <= s_hi; ++s) {
+      block_poll_ge(a.sig_k + (size_t)a.rank * a.n_slab + s, target, a.sa);
+      block_poll_ge(a.sig_v + (size_t)a.rank * a.n_slab + s, target, a.sa);
+    }
+  }
   return waited;
 }
 
@@ -541,6 +553,7 @@ tsg_status tsg_op_attn(tsg_ctx* ctx, const void* q, const void* k_local, const v
   for (int p = 0; p < kMaxRanks; ++p) ka.order[p] = ord[p];
   ka.n_slab = n_slab;
   ka.slab_log2 = slab_log2;
+  ka.wait_own_end = 0;
   ka.l1_only = ((uintptr_t)k_full % 128 == 0 && (uintptr_t)v_full % 128 == 0 && slab >= 64) ? 1 : 0;
   ka.scale_log2 = 1.4426950408889634f / sqrtf((float)D);
   const int n_tiles = heads * ka.n_qb;
@@ -568,17 +581,27 @@ tsg_status tsg_op_attn(tsg_ctx* ctx, const void* q, const void* k_local, const v
       tsg_status st = streams(ctx, o, &pr, caller);
       if (st == TSG_OK) st = fork(ctx, caller, pr);
       if (st != TSG_OK) return st;
+      // On shared CUs the caller's stream waits for the attention kernel
+      // alone (a join would put a barrier packet between consecutive calls'
+      // kernels on its queue): its tiles wait for their head's own-chunk
+      // slabs after their stores, so its end implies every arrival, and the
+      // copy kernel's workgroups may then still be leaving their queue,
+      // whose words only later such copies on the same side stream use.
+      // With a timeline (copy rows are written after the arrivals) or a
+      // debug skip mask the call joins.
+      const bool detached = o.aux_cus < 0 && pr.main == caller && !o.timeline && o.skip_mask == 0;
+      ka.wait_own_end = detached ? 1 : 0;
       // the copy first, so that its workgroups are dispatched while the
       // attention workgroups start on their own chunks
       const int copy_grid = o.aux_wgs > 0 ? std::min(o.aux_wgs, 4 * ctx->n_cus) : ctx->n_cus;
-      ck.queue = ctx->d_queue + kCopyQueueSlot;
+      ck.queue = ctx->d_queue + kCopyQueueSlot + (detached ? 0 : 2);
       ck.n_workers = (uint32_t)copy_grid;
       time_begin(ctx, 1, pr.aux);
       hipLaunchKernelGGL(ag_attn_copy_kernel, dim3(copy_grid), dim3(256), 0, pr.aux, ck, cv);
       time_end(ctx, 1, pr.aux);
       st = check_launch(ctx, "ag_attn_copy_kernel");
       if (st == TSG_OK) st = launch(pr.main, 0, n_tiles, 1, 0);
-      if (st != TSG_OK) return st;
+      if (st != TSG_OK || detached) return st;
       return join(ctx, caller, pr);
     }
     case TSG_MODE_SERIAL: {
