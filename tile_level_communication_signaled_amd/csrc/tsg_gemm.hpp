@@ -153,7 +153,9 @@ struct ARowsGather {
 
 // Called with the first K column k0 of every step, in increasing order, just
 // before that step's A loads are issued: a consumer whose A arrives in column
-// slabs waits there for the slab's signal.
+// slabs waits there for the slab's signal.  The K loops take the hook by
+// reference, so state it keeps (the time spent waiting) is the caller's
+// after the loop.
 struct NoHook {
   __device__ __forceinline__ void before_a(int) {}
 };
@@ -401,7 +403,7 @@ struct GemmTile {
   __device__ __forceinline__ static void run_direct(const ARows& ar,
                                                     const uint16_t* __restrict__ B, int64_t ldb,
                                                     int col0, int N, int K, char* lds, Acc& acc,
-                                                    Hook hook = Hook(), int rows_active = Cfg::BM) {
+                                                    Hook&& hook = Hook(), int rows_active = Cfg::BM) {
     static_assert(Cfg::B_STAGE % 1024 == 0, "a B stage must be whole 1 KB load blocks");
     constexpr int B_BLK = Cfg::B_STAGE / 1024;
     constexpr int B_BPW = (B_BLK + Cfg::NW - 1) / Cfg::NW;
@@ -540,7 +542,7 @@ struct GemmTile {
   template <class ARows, class Hook = NoHook>
   __device__ __forceinline__ static void run_regs(const ARows& ar, const uint16_t* __restrict__ B,
                                                   int64_t ldb, int col0, int N, int K, char* lds,
-                                                  Acc& acc, Hook hook = Hook()) {
+                                                  Acc& acc, Hook&& hook = Hook()) {
     zero(acc);
     if constexpr (Cfg::MF != 32) {
       return;  // 16-column fragments have the main path only (the host requires K % 128 == 0)
