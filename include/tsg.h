@@ -287,11 +287,11 @@ tsg_status tsg_timeline(tsg_ctx* ctx, uint64_t* out, size_t cap, size_t* n);
  * Overlap on shared CUs (opts.aux_cus < 0, no timeline, no debug skip mask)
  * from a non-null `stream`, with a copy kernel beside the GEMM: `stream`
  * waits for the GEMM only, not for the copy kernel on the side stream.  The
- * GEMM ends only after it has
- * observed every chunk's arrival (tiles inside the local chunk wait for it
- * after their stores), so a_full and c are complete, and a_local and a_peers
- * no longer read, when `stream` passes the call; the copy kernel's
- * workgroups may still be leaving its work queue (context-internal words).
+ * GEMM ends only after it has observed every chunk's arrival (tiles inside
+ * the local chunk wait for it after their stores), so a_full and c are
+ * complete, and a_local and a_peers no longer read, when `stream` passes the
+ * call; the copy kernel's workgroups may still be leaving its work queue
+ * (context-internal words).
  * After a device-side error the copy may still run: tsg_check() waits for
  * the side streams before it reports. */
 tsg_status gemm_ag_overlap(tsg_ctx* ctx, const void* a_local, const void* a_peers,
